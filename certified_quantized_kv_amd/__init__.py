@@ -1,0 +1,257 @@
+"""Python binding of libkvq (certified quantized-KV decode attention on MI355X).
+
+Argument marshalling only: every step of the decode path runs in the HIP
+kernels of libkvq.so, built in-tree by ``certified_quantized_kv_amd/build.py``.
+Importing this package without the built library raises ImportError; there is
+no CPU fallback.  PyTorch is used for device memory and streams.
+
+Method: "Runtime-Certified Bounded-Error Quantized Attention" (gist.science
+technical summary), Méthodologie §1-§3; see include/kvq.h for the C ABI.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvq.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                      "(hipcc --offload-arch=gfx950) first")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+P = ctypes.c_void_p
+I32 = ctypes.c_int32
+I64 = ctypes.c_int64
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("n_layers", I32), ("max_batch", I32), ("n_q_heads", I32), ("n_kv_heads", I32),
+                ("head_dim", I32), ("max_tokens", I32), ("tau_cov_ppm", I32),
+                ("rho_min_ppm", I32), ("widen_rounds", I32), ("layer_frac_ppm", I32),
+                ("eps_key", ctypes.c_double), ("v_tol", ctypes.c_double),
+                ("flags", ctypes.c_uint32)]
+
+
+class StepStats(ctypes.Structure):
+    _fields_ = [("promoted_key_blocks", I64), ("promoted_value_blocks", I64),
+                ("dense_kv_heads", I64), ("h2d_bytes", I64), ("key_rounds", I32),
+                ("host_syncs", I32), ("level_count", I32 * 5), ("ms_score", ctypes.c_float),
+                ("ms_select", ctypes.c_float), ("ms_promote", ctypes.c_float),
+                ("ms_decode", ctypes.c_float), ("ms_total", ctypes.c_float)]
+
+    def as_dict(self):
+        d = {k: getattr(self, k) for k, _ in self._fields_}
+        d["level_count"] = list(self.level_count)
+        return d
+
+
+FLAG_FORCE_DENSE = 1
+FLAG_TIMING = 2
+
+TR = dict(shat=1, sp=2, mhat=3, Lhat=4, delta=5, m16=6, L16=7, What=8, pi=9, Wt=10, W16=11,
+          k0=12, ssize=13, ssd=14, ekey64=15, eval64=16, hflags=17, U=18, V=19, vh=20)
+_TR_DTYPE = dict(shat=np.float32, sp=np.float32, mhat=np.float32, Lhat=np.uint32,
+                 delta=np.float32, m16=np.float32, L16=np.uint32, What=np.uint32, pi=np.uint32,
+                 Wt=np.uint32, W16=np.uint32, k0=np.int32, ssize=np.int32, ssd=np.uint64,
+                 ekey64=np.float64, eval64=np.float64, hflags=np.uint32, U=np.uint8, V=np.uint8,
+                 vh=np.uint8)
+
+_SIGS = {
+    "kvq_default_config": (None, [P, I32, I32, I32, I32, I32, I32]),
+    "kvq_create": (I32, [P, P]),
+    "kvq_destroy": (None, [P]),
+    "kvq_append": (I32, [P, I32, I32, P, P, P, P, P]),
+    "kvq_decode_step": (I32, [P, I32, I32, P, P, P, P, P, P, P, P]),
+    "kvq_reset_seq": (I32, [P, I32]),
+    "kvq_seq_len": (I64, [P, I32, I32]),
+    "kvq_strerror": (ctypes.c_char_p, [I32]),
+    "kvq_last_error": (ctypes.c_char_p, [P]),
+    "kvq_tier1_bytes_per_token": (ctypes.c_double, [I32]),
+    "kvq_device_bytes": (I64, [P]),
+    "kvq_host_pinned_bytes": (I64, [P]),
+    "kvq_tier1_export_bytes": (I64, [P, I32, I32]),
+    "kvq_export_tier1": (I32, [P, I32, I32, I32, P, ctypes.c_size_t]),
+    "kvq_trace_bytes": (I64, [P, I32, I32]),
+    "kvq_export_trace": (I32, [P, I32, I32, P, ctypes.c_size_t]),
+    "kvq_selftest_exp2k": (I32, [P, P, I64, P]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+EXPORTED = tuple(_SIGS)
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"kvq status {status} ({_lib.kvq_strerror(status).decode()}): {msg}")
+        self.status = status
+
+
+def tier1_bytes_per_token(head_dim):
+    return _lib.kvq_tier1_bytes_per_token(head_dim)
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t, dtype, name):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _i32(seq):
+    arr = (I32 * len(seq))(*[int(x) for x in seq])
+    return arr
+
+
+def exp2k(x):
+    """The library's decision exponential on a float32 CUDA tensor (test hook)."""
+    import torch
+    y = torch.empty_like(x)
+    st = _lib.kvq_selftest_exp2k(_dev(x, torch.float32, "x"), _dev(y, torch.float32, "y"),
+                                 x.numel(), _stream())
+    if st != 0:
+        raise KvqError(st, "exp2k")
+    return y
+
+
+class Context:
+    """A tiered quantized KV cache on the current device (kvq_create)."""
+
+    def __init__(self, n_layers, max_batch, n_q_heads, n_kv_heads, head_dim, max_tokens,
+                 tau_cov_ppm=995_000, eps_key=1e-3, v_tol=0.25, rho_min_ppm=900_000,
+                 widen_rounds=2, layer_frac_ppm=500_000, force_dense=False, timing=False):
+        cfg = Config()
+        _lib.kvq_default_config(ctypes.byref(cfg), n_layers, max_batch, n_q_heads, n_kv_heads,
+                                head_dim, max_tokens)
+        cfg.tau_cov_ppm = tau_cov_ppm
+        cfg.eps_key = eps_key
+        cfg.v_tol = v_tol
+        cfg.rho_min_ppm = rho_min_ppm
+        cfg.widen_rounds = widen_rounds
+        cfg.layer_frac_ppm = layer_frac_ppm
+        cfg.flags = (FLAG_FORCE_DENSE if force_dense else 0) | (FLAG_TIMING if timing else 0)
+        self.cfg = cfg
+        self._ctx = ctypes.c_void_p()
+        st = _lib.kvq_create(ctypes.byref(cfg), ctypes.byref(self._ctx))
+        if st != 0:
+            raise KvqError(st, "kvq_create")
+        self.Hq, self.Hkv, self.d = n_q_heads, n_kv_heads, head_dim
+
+    def _check(self, st, what):
+        if st != 0:
+            raise KvqError(st, f"{what}: {_lib.kvq_last_error(self._ctx).decode()}")
+
+    def close(self):
+        if self._ctx:
+            _lib.kvq_destroy(self._ctx)
+            self._ctx = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def device_bytes(self):
+        return _lib.kvq_device_bytes(self._ctx)
+
+    @property
+    def host_pinned_bytes(self):
+        return _lib.kvq_host_pinned_bytes(self._ctx)
+
+    def seq_len(self, layer, seq):
+        return _lib.kvq_seq_len(self._ctx, layer, seq)
+
+    def reset_seq(self, seq):
+        self._check(_lib.kvq_reset_seq(self._ctx, seq), "kvq_reset_seq")
+
+    def append(self, layer, seq_ids, n_new, k, v):
+        """k, v: fp16 CUDA tensors [sum(n_new), n_kv_heads, head_dim]."""
+        import torch
+        n = len(seq_ids)
+        kp = _dev(k, torch.float16, "k")
+        vp = _dev(v, torch.float16, "v")
+        if k.shape != v.shape or k.dim() != 3 or k.shape[0] != sum(n_new) or \
+                k.shape[1] != self.Hkv or k.shape[2] != self.d:
+            raise ValueError(f"k/v shape {tuple(k.shape)} does not match the call")
+        self._check(_lib.kvq_append(self._ctx, layer, n, _i32(seq_ids), _i32(n_new), kp, vp,
+                                    _stream()), "kvq_append")
+
+    def decode_step(self, layer, seq_ids, q, out=None, e_key=None, e_val=None, level=None,
+                    stats=False):
+        """q: fp16 CUDA tensor [n, n_q_heads, head_dim].  Returns
+        (out f32 [n,Hq,d], e_key f32 [n,Hq], e_val f32 [n,Hq], level int8 [n,Hq], stats)."""
+        import torch
+        n = len(seq_ids)
+        if q.shape != (n, self.Hq, self.d):
+            raise ValueError(f"q shape {tuple(q.shape)} != {(n, self.Hq, self.d)}")
+        dev = q.device
+        out = torch.empty((n, self.Hq, self.d), dtype=torch.float32, device=dev) if out is None else out
+        e_key = torch.empty((n, self.Hq), dtype=torch.float32, device=dev) if e_key is None else e_key
+        e_val = torch.empty((n, self.Hq), dtype=torch.float32, device=dev) if e_val is None else e_val
+        level = torch.empty((n, self.Hq), dtype=torch.int8, device=dev) if level is None else level
+        ss = StepStats() if stats else None
+        st = _lib.kvq_decode_step(self._ctx, layer, n, _i32(seq_ids), _dev(q, torch.float16, "q"),
+                                  _dev(out, torch.float32, "out"), _dev(e_key, torch.float32, "e_key"),
+                                  _dev(e_val, torch.float32, "e_val"), _dev(level, torch.int8, "level"),
+                                  ctypes.byref(ss) if ss is not None else None, _stream())
+        self._check(st, "kvq_decode_step")
+        return out, e_key, e_val, level, (ss.as_dict() if ss is not None else None)
+
+    def export_tier1(self, layer, seq, g):
+        """Tier 1 of one (layer, slot, KV head) in plain layouts (numpy)."""
+        nbytes = _lib.kvq_tier1_export_bytes(self._ctx, layer, seq)
+        if nbytes < 0:
+            raise KvqError(int(nbytes), "kvq_tier1_export_bytes")
+        buf = np.empty(nbytes, np.uint8)
+        self._check(_lib.kvq_export_tier1(self._ctx, layer, seq, g, buf.ctypes.data_as(P), nbytes),
+                    "kvq_export_tier1")
+        T = self.seq_len(layer, seq)
+        NB = (T + 63) // 64
+        d = self.d
+        out = {}
+        o = 0
+
+        def take(name, count, dtype, shape):
+            nonlocal o
+            nb = count * np.dtype(dtype).itemsize
+            out[name] = buf[o:o + nb].view(dtype).reshape(shape).copy()
+            o += nb
+        take("kcode", T * d, np.uint8, (T, d))
+        take("kscale", NB * d, np.uint16, (NB, d))
+        take("koff", NB * d, np.uint16, (NB, d))
+        take("eta", NB, np.float32, (NB,))
+        take("vcode", T * d, np.uint8, (T, d))
+        take("vscale", T * (d // 32), np.uint16, (T, d // 32))
+        take("voff", T * (d // 32), np.uint16, (T, d // 32))
+        take("vmin", d, np.float32, (d,))
+        take("vmax", d, np.float32, (d,))
+        assert o == nbytes
+        out["T"], out["d"] = T, d
+        return out
+
+    def export_trace(self, which, seq):
+        """One per-step array of the last decode step for slot `seq` (numpy)."""
+        code = TR[which]
+        nbytes = _lib.kvq_trace_bytes(self._ctx, code, seq)
+        if nbytes < 0:
+            raise KvqError(int(nbytes), "kvq_trace_bytes")
+        arr = np.empty(nbytes // np.dtype(_TR_DTYPE[which]).itemsize, _TR_DTYPE[which])
+        self._check(_lib.kvq_export_trace(self._ctx, code, seq, arr.ctypes.data_as(P), nbytes),
+                    "kvq_export_trace")
+        return arr

@@ -1,0 +1,678 @@
+// kvq_api.hip -- the C ABI (include/kvq.h): context, tiers, and the host
+// orchestration of one certified decode step.
+//
+// Decode step ("Runtime-Certified Bounded-Error Quantized Attention",
+// Méthodologie §1-§3), all on the caller's stream except the promotion
+// copies, which run on the context's copy stream and are joined by events:
+//   1. q' (log2 units); INT8 scoring pass with per-block Delta' and (m, L);
+//   2. per query head top-K* selection; per KV head union -> key runs;
+//   3. host round trip: runs of FP16 key blocks are copied from pinned tier 2
+//      to the device staging buffer (hipMemcpyAsync, side stream);
+//   4. FP16 scoring of the new blocks; controller round (ranking check,
+//      E_key, rung 1 widening, and for groups that stop: rung 3, rung 2);
+//      repeat 3-4 while some group widened (at most widen_rounds + 1 rounds);
+//   5. value runs copied (rung 2); rung 4 and the per-head outputs; whole KV
+//      heads copied for groups with a dense head;
+//   6. split-K decode (mixed and dense) and the combine.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+using namespace kvq;
+
+struct kvq_ctx {
+  kvq_config cfg;
+  Shape s;
+  Thresh th;
+  Tier1 t;
+  Step w;
+  uint16_t *t2k_host = nullptr, *t2v_host = nullptr;
+  std::vector<int64_t> T;     // [slot][layer]
+  std::vector<void *> dallocs;
+  hipStream_t cstream = nullptr;
+  hipEvent_t ev_start = nullptr, ev_copy = nullptr;
+  hipEvent_t ev_t[6] = {};
+  unsigned long long *plan_host = nullptr;
+  size_t plan_cap = 0;
+  size_t plan_words = 0;
+  int last_n = 0, last_layer = -1;
+  int last_slot[MAX_CALL] = {}, last_T[MAX_CALL] = {};
+  std::string err;
+  int64_t dev_bytes = 0, host_bytes = 0;
+  int device = 0;
+};
+
+namespace {
+
+kvq_status fail(kvq_ctx *c, kvq_status st, const std::string &msg) {
+  if (c) c->err = msg;
+  return st;
+}
+
+#define HIPCK(ctx, expr)                                                             \
+  do {                                                                               \
+    hipError_t e_ = (expr);                                                          \
+    if (e_ != hipSuccess)                                                            \
+      return fail(ctx, KVQ_EHIP, std::string(#expr) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+template <class P>
+hipError_t dalloc(kvq_ctx *c, P **p, size_t bytes) {
+  void *q = nullptr;
+  hipError_t e = hipMalloc(&q, bytes ? bytes : 16);
+  if (e != hipSuccess) return e;
+  c->dallocs.push_back(q);
+  c->dev_bytes += (int64_t)bytes;
+  *p = (P *)q;
+  return hipSuccess;
+}
+
+void free_all(kvq_ctx *c) {
+  if (!c) return;
+  (void)hipDeviceSynchronize();
+  for (void *p : c->dallocs) (void)hipFree(p);
+  c->dallocs.clear();
+  if (c->t2k_host) (void)hipHostFree(c->t2k_host);
+  if (c->t2v_host) (void)hipHostFree(c->t2v_host);
+  if (c->plan_host) (void)hipHostFree(c->plan_host);
+  if (c->cstream) (void)hipStreamDestroy(c->cstream);
+  if (c->ev_start) (void)hipEventDestroy(c->ev_start);
+  if (c->ev_copy) (void)hipEventDestroy(c->ev_copy);
+  for (auto &e : c->ev_t)
+    if (e) (void)hipEventDestroy(e);
+}
+
+bool valid_seqs(const kvq_ctx *c, int n, const int32_t *ids) {
+  if (n < 1 || n > c->cfg.max_batch || n > MAX_CALL || !ids) return false;
+  for (int a = 0; a < n; ++a) {
+    if (ids[a] < 0 || ids[a] >= c->cfg.max_batch) return false;
+    for (int b = 0; b < a; ++b)
+      if (ids[a] == ids[b]) return false;
+  }
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+void kvq_default_config(kvq_config *cfg, int32_t n_layers, int32_t max_batch, int32_t n_q_heads,
+                        int32_t n_kv_heads, int32_t head_dim, int32_t max_tokens) {
+  if (!cfg) return;
+  memset(cfg, 0, sizeof(*cfg));
+  cfg->n_layers = n_layers;
+  cfg->max_batch = max_batch;
+  cfg->n_q_heads = n_q_heads;
+  cfg->n_kv_heads = n_kv_heads;
+  cfg->head_dim = head_dim;
+  cfg->max_tokens = max_tokens;
+  cfg->tau_cov_ppm = 995000;
+  cfg->rho_min_ppm = 900000;
+  cfg->widen_rounds = 2;
+  cfg->layer_frac_ppm = 500000;
+  cfg->eps_key = 1e-3;
+  cfg->v_tol = 0.25;
+  cfg->flags = 0u;
+}
+
+const char *kvq_strerror(kvq_status s) {
+  switch (s) {
+    case KVQ_OK: return "ok";
+    case KVQ_EINVAL: return "invalid argument";
+    case KVQ_ENOMEM_DEVICE: return "device allocation failed";
+    case KVQ_ENOMEM_HOST: return "pinned host allocation failed";
+    case KVQ_ECAPACITY: return "sequence capacity exceeded";
+    case KVQ_ESTATE: return "invalid state (empty sequence or bad layer)";
+    case KVQ_EHIP: return "HIP runtime error";
+    case KVQ_ENOTIMPL: return "not implemented";
+    default: return "unknown status";
+  }
+}
+
+const char *kvq_last_error(const kvq_ctx *ctx) { return ctx ? ctx->err.c_str() : ""; }
+
+double kvq_tier1_bytes_per_token(int32_t d) {
+  // K codes d + K meta 4d/64 + V codes d/2 + V meta 4d/32 + eta 4/64
+  return (double)d + 4.0 * d / 64.0 + d / 2.0 + 4.0 * d / 32.0 + 4.0 / 64.0;
+}
+
+int64_t kvq_device_bytes(const kvq_ctx *ctx) { return ctx ? ctx->dev_bytes : -1; }
+int64_t kvq_host_pinned_bytes(const kvq_ctx *ctx) { return ctx ? ctx->host_bytes : -1; }
+
+kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out) {
+  if (!cfg || !out) return KVQ_EINVAL;
+  const kvq_config &c = *cfg;
+  if (c.n_layers < 1 || c.max_batch < 1 || c.n_q_heads < 1 || c.n_kv_heads < 1 ||
+      c.n_q_heads % c.n_kv_heads != 0 || (c.head_dim != 64 && c.head_dim != 128) ||
+      c.max_tokens < 1 || (c.max_tokens + BLOCK - 1) / BLOCK > MAX_NB)
+    return KVQ_EINVAL;
+  const int G = c.n_q_heads / c.n_kv_heads;
+  if (G != 1 && G != 2 && G != 4) return KVQ_EINVAL;
+  if (c.tau_cov_ppm < 1 || c.tau_cov_ppm > 1000000 || c.rho_min_ppm < -1000000 ||
+      c.rho_min_ppm > 1000000 || c.widen_rounds < 0 || c.widen_rounds > 12 ||
+      c.layer_frac_ppm < 0 || c.layer_frac_ppm > 1000000 || !(c.eps_key >= 0.0) ||
+      !(c.v_tol >= 0.0))
+    return KVQ_EINVAL;
+
+  kvq_ctx *x = new (std::nothrow) kvq_ctx();
+  if (!x) return KVQ_ENOMEM_HOST;
+  x->cfg = c;
+  (void)hipGetDevice(&x->device);
+  Shape &s = x->s;
+  s.L = c.n_layers;
+  s.Hq = c.n_q_heads;
+  s.Hkv = c.n_kv_heads;
+  s.G = G;
+  s.d = c.head_dim;
+  s.NBmax = (c.max_tokens + BLOCK - 1) / BLOCK;
+  s.Tmax = s.NBmax * BLOCK;
+  s.runmax = s.NBmax / 2 + 1;
+  s.nchmax = (s.NBmax + DEC_CB - 1) / DEC_CB;
+  s.B = c.max_batch;
+  x->th.tau_ppm = c.tau_cov_ppm;
+  x->th.rho_ppm = c.rho_min_ppm;
+  x->th.R1 = c.widen_rounds;
+  x->th.frac_ppm = c.layer_frac_ppm;
+  x->th.eps_key = c.eps_key;
+  x->th.v_tol = c.v_tol;
+  x->th.force_dense = (c.flags & KVQ_FLAG_FORCE_DENSE) ? 1 : 0;
+  x->T.assign((size_t)c.max_batch * c.n_layers, 0);
+
+  const size_t NU = (size_t)c.max_batch * c.n_layers * c.n_kv_heads;
+  const size_t d = s.d, NBm = s.NBmax, Tm = s.Tmax;
+  Tier1 &t = x->t;
+  Step &w = x->w;
+  const size_t B = s.B, Hq = s.Hq, Hkv = s.Hkv;
+  hipError_t e = hipSuccess;
+#define DA(p, n)                                  \
+  if (e == hipSuccess) e = dalloc(x, &(p), (n)); \
+  else (void)0
+  DA(t.kcodes, NU * NBm * BLOCK * d);
+  DA(t.kmeta, NU * NBm * d * 4);
+  DA(t.vcodes, NU * Tm * d / 2);
+  DA(t.vmeta, NU * Tm * (d / VGROUP) * 4);
+  DA(t.eta, NU * NBm * 4);
+  DA(t.vmin, NU * d * 4);
+  DA(t.vmax, NU * d * 4);
+  DA(t.openk, NU * BLOCK * d * 2);
+  DA(w.qp, B * Hq * d * 4);
+  DA(w.shat, B * Hq * Tm * 4);
+  DA(w.sp, B * Hq * Tm * 4);
+  DA(w.mhat, B * Hq * NBm * 4);
+  DA(w.delta, B * Hq * NBm * 4);
+  DA(w.m16, B * Hq * NBm * 4);
+  DA(w.Lhat, B * Hq * NBm * 4);
+  DA(w.L16, B * Hq * NBm * 4);
+  DA(w.What, B * Hq * NBm * 4);
+  DA(w.pi, B * Hq * NBm * 4);
+  DA(w.Wt, B * Hq * NBm * 4);
+  DA(w.W16, B * Hq * NBm * 4);
+  DA(w.vh, B * Hq * NBm);
+  DA(w.k0, B * Hq * 4);
+  DA(w.ssize, B * Hq * 4);
+  DA(w.ssd, B * Hq * 8);
+  DA(w.ekey64, B * Hq * 8);
+  DA(w.eval64, B * Hq * 8);
+  DA(w.hflags, B * Hq * 4);
+  DA(w.hlevel, B * Hq);
+  DA(w.U, B * Hkv * NBm);
+  DA(w.Knew, B * Hkv * NBm);
+  DA(w.V, B * Hkv * NBm);
+  DA(w.Vnew, B * Hkv * NBm);
+  DA(w.gstat, B * Hkv * 4);
+  DA(w.runs, B * Hkv * 2 * (size_t)s.runmax * 4);
+  DA(w.nruns, B * Hkv * 2 * 4);
+  x->plan_words = 4 + B * Hkv * 2 * (size_t)s.runmax;
+  DA(w.plan, x->plan_words * 8);
+  DA(w.stage_k, B * Hkv * Tm * d * 2);
+  DA(w.stage_v, B * Hkv * Tm * d * 2);
+  DA(w.part, B * Hkv * (size_t)s.nchmax * G * (d + 2) * 4);
+  DA(w.partd, B * Hkv * (size_t)s.nchmax * G * (d + 2) * 4);
+  DA(w.gdense, B * Hkv);
+#undef DA
+  if (e != hipSuccess) {
+    x->err = std::string("device allocation: ") + hipGetErrorString(e);
+    free_all(x);
+    delete x;
+    (void)hipGetLastError();
+    return KVQ_ENOMEM_DEVICE;
+  }
+  const size_t t2bytes = NU * Tm * d * 2;
+  if (hipHostMalloc((void **)&x->t2k_host, t2bytes, hipHostMallocMapped) != hipSuccess ||
+      hipHostMalloc((void **)&x->t2v_host, t2bytes, hipHostMallocMapped) != hipSuccess) {
+    free_all(x);
+    delete x;
+    (void)hipGetLastError();
+    return KVQ_ENOMEM_HOST;
+  }
+  x->host_bytes = (int64_t)(2 * t2bytes);
+  void *dk = nullptr, *dv = nullptr;
+  e = hipHostGetDevicePointer(&dk, x->t2k_host, 0);
+  if (e == hipSuccess) e = hipHostGetDevicePointer(&dv, x->t2v_host, 0);
+  x->plan_cap = 4096;
+  if (e == hipSuccess) e = hipHostMalloc((void **)&x->plan_host, (4 + x->plan_cap) * 8, 0);
+  if (e == hipSuccess) e = hipStreamCreateWithFlags(&x->cstream, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&x->ev_start, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&x->ev_copy, hipEventDisableTiming);
+  for (auto &ev : x->ev_t)
+    if (e == hipSuccess) e = hipEventCreate(&ev);
+  if (e == hipSuccess) e = hipMemsetD32(reinterpret_cast<hipDeviceptr_t>(t.vmin), 0xff800000u, NU * d);
+  if (e == hipSuccess) e = hipMemsetD32(reinterpret_cast<hipDeviceptr_t>(t.vmax), 0x007fffffu, NU * d);
+  if (e == hipSuccess) e = hipMemset(t.eta, 0, NU * NBm * 4);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    x->err = hipGetErrorString(e);
+    free_all(x);
+    delete x;
+    (void)hipGetLastError();
+    return KVQ_EHIP;
+  }
+  t.t2k = (uint16_t *)dk;
+  t.t2v = (uint16_t *)dv;
+  *out = x;
+  return KVQ_OK;
+}
+
+void kvq_destroy(kvq_ctx *ctx) {
+  if (!ctx) return;
+  free_all(ctx);
+  delete ctx;
+}
+
+int64_t kvq_seq_len(const kvq_ctx *ctx, int32_t layer, int32_t seq) {
+  if (!ctx || layer < 0 || layer >= ctx->cfg.n_layers || seq < 0 || seq >= ctx->cfg.max_batch)
+    return KVQ_EINVAL;
+  return ctx->T[(size_t)seq * ctx->cfg.n_layers + layer];
+}
+
+kvq_status kvq_reset_seq(kvq_ctx *ctx, int32_t seq) {
+  if (!ctx || seq < 0 || seq >= ctx->cfg.max_batch) return KVQ_EINVAL;
+  const Shape &s = ctx->s;
+  for (int l = 0; l < s.L; ++l) {
+    ctx->T[(size_t)seq * s.L + l] = 0;
+    const size_t u0 = unit_of(s, seq, l, 0);
+    HIPCK(ctx, hipMemsetD32(reinterpret_cast<hipDeviceptr_t>(ctx->t.vmin + u0 * s.d), 0xff800000u,
+                            (size_t)s.Hkv * s.d));
+    HIPCK(ctx, hipMemsetD32(reinterpret_cast<hipDeviceptr_t>(ctx->t.vmax + u0 * s.d), 0x007fffffu,
+                            (size_t)s.Hkv * s.d));
+  }
+  HIPCK(ctx, hipDeviceSynchronize());
+  return KVQ_OK;
+}
+
+kvq_status kvq_append(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t *seq_ids,
+                      const int32_t *n_new, const void *k, const void *v, void *stream) {
+  if (!ctx) return KVQ_EINVAL;
+  if (layer < 0 || layer >= ctx->cfg.n_layers) return fail(ctx, KVQ_ESTATE, "bad layer");
+  if (!valid_seqs(ctx, n, seq_ids) || !n_new) return fail(ctx, KVQ_EINVAL, "bad sequence list");
+  const Shape &s = ctx->s;
+  AppendArgs a;
+  memset(&a, 0, sizeof(a));
+  a.n = n;
+  a.layer = layer;
+  int64_t off = 0;
+  int max_blk = 0;
+  for (int i = 0; i < n; ++i) {
+    if (n_new[i] < 0) return fail(ctx, KVQ_EINVAL, "negative token count");
+    const int64_t Told = ctx->T[(size_t)seq_ids[i] * s.L + layer];
+    if (Told + n_new[i] > ctx->cfg.max_tokens) return fail(ctx, KVQ_ECAPACITY, "capacity exceeded");
+    a.slot[i] = seq_ids[i];
+    a.T_old[i] = (int)Told;
+    a.n_new[i] = n_new[i];
+    a.in_off[i] = (int)off;
+    a.n_blk[i] = n_new[i] > 0 ? (int)((Told + n_new[i] - 1) / BLOCK - Told / BLOCK + 1) : 0;
+    max_blk = std::max(max_blk, a.n_blk[i]);
+    off += n_new[i];
+  }
+  if (off > 0 && (!k || !v)) return fail(ctx, KVQ_EINVAL, "null k/v");
+  if (off > 0) {
+    HIPCK(ctx, launch_append(s, ctx->t, a, (const uint16_t *)k, (const uint16_t *)v, max_blk,
+                             (hipStream_t)stream));
+  }
+  for (int i = 0; i < n; ++i) ctx->T[(size_t)seq_ids[i] * s.L + layer] += n_new[i];
+  return KVQ_OK;
+}
+
+namespace {
+
+struct Plan {
+  int64_t nk = 0, nv = 0;
+  uint32_t flags = 0;
+  std::vector<unsigned long long> ent;
+};
+
+kvq_status read_plan(kvq_ctx *c, hipStream_t st, Plan &p) {
+  const size_t first = std::min(c->plan_cap, c->plan_words - 4);
+  HIPCK(c, hipMemcpyAsync(c->plan_host, c->w.plan, (4 + first) * 8, hipMemcpyDeviceToHost, st));
+  HIPCK(c, hipStreamSynchronize(st));
+  p.nk = (int64_t)c->plan_host[0];
+  p.nv = (int64_t)c->plan_host[1];
+  p.flags = (uint32_t)c->plan_host[2];
+  const size_t tot = (size_t)(p.nk + p.nv);
+  p.ent.assign(c->plan_host + 4, c->plan_host + 4 + std::min(tot, first));
+  if (tot > first) {
+    p.ent.resize(tot);
+    HIPCK(c, hipMemcpy(p.ent.data() + first, c->w.plan + 4 + first, (tot - first) * 8,
+                       hipMemcpyDeviceToHost));
+  }
+  return KVQ_OK;
+}
+
+// Issues the copies of a plan on the copy stream; returns bytes and blocks.
+kvq_status issue_copies(kvq_ctx *c, const SeqTab &tab, int layer, const Plan &p, int64_t &bytes,
+                        int64_t &kblocks, int64_t &vblocks) {
+  const Shape &s = c->s;
+  const size_t blk_bytes = (size_t)BLOCK * s.d * 2;
+  for (const unsigned long long e : p.ent) {
+    const int len = (int)(e & 0xffffu), start = (int)((e >> 16) & 0xffffu);
+    const int ig = (int)((e >> 32) & 0xffffu), kind = (int)((e >> 48) & 1u);
+    const int i = ig / s.Hkv, g = ig % s.Hkv;
+    const size_t u = unit_of(s, tab.slot[i], layer, g);
+    const size_t srow = u * s.Tmax + (size_t)start * BLOCK;
+    const size_t drow = (size_t)ig * s.Tmax + (size_t)start * BLOCK;
+    uint16_t *dst = (kind ? c->w.stage_v : c->w.stage_k) + drow * s.d;
+    const uint16_t *src = (kind ? c->t2v_host : c->t2k_host) + srow * s.d;
+    HIPCK(c, hipMemcpyAsync(dst, src, (size_t)len * blk_bytes, hipMemcpyHostToDevice, c->cstream));
+    bytes += (int64_t)len * (int64_t)blk_bytes;
+    (kind ? vblocks : kblocks) += len;
+  }
+  return KVQ_OK;
+}
+
+}  // namespace
+
+kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t *seq_ids,
+                           const void *q, float *out, float *e_key, float *e_val, int8_t *level,
+                           kvq_step_stats *stats, void *stream) {
+  if (!ctx) return KVQ_EINVAL;
+  if (layer < 0 || layer >= ctx->cfg.n_layers) return fail(ctx, KVQ_ESTATE, "bad layer");
+  if (!valid_seqs(ctx, n, seq_ids)) return fail(ctx, KVQ_EINVAL, "bad sequence list");
+  if (!q || !out || !e_key || !e_val || !level) return fail(ctx, KVQ_EINVAL, "null output");
+  const Shape &s = ctx->s;
+  SeqTab tab;
+  memset(&tab, 0, sizeof(tab));
+  tab.n = n;
+  int maxNB = 0;
+  for (int i = 0; i < n; ++i) {
+    const int64_t T = ctx->T[(size_t)seq_ids[i] * s.L + layer];
+    if (T < 1) return fail(ctx, KVQ_ESTATE, "decode on an empty sequence");
+    tab.slot[i] = seq_ids[i];
+    tab.T[i] = (int)T;
+    maxNB = std::max(maxNB, (int)((T + BLOCK - 1) / BLOCK));
+  }
+  hipStream_t st = (hipStream_t)stream;
+  const bool timing = (ctx->cfg.flags & KVQ_FLAG_TIMING) != 0;
+  Step &w = ctx->w;
+  const size_t NBm = s.NBmax;
+  int64_t h2d = 0, kblk = 0, vblk = 0, dense_heads = 0;
+  int syncs = 0, rounds = 0;
+  if (timing) HIPCK(ctx, hipEventRecord(ctx->ev_t[0], st));
+
+  HIPCK(ctx, hipMemsetAsync(w.U, 0, (size_t)n * s.Hkv * NBm, st));
+  HIPCK(ctx, hipMemsetAsync(w.Knew, 0, (size_t)n * s.Hkv * NBm, st));
+  HIPCK(ctx, hipMemsetAsync(w.V, 0, (size_t)n * s.Hkv * NBm, st));
+  HIPCK(ctx, hipMemsetAsync(w.Vnew, 0, (size_t)n * s.Hkv * NBm, st));
+  HIPCK(ctx, hipMemsetAsync(w.vh, 0, (size_t)n * s.Hq * NBm, st));
+  HIPCK(ctx, hipMemsetAsync(w.gstat, 0, (size_t)n * s.Hkv * 4, st));
+  HIPCK(ctx, hipMemsetAsync(w.hflags, 0, (size_t)n * s.Hq * 4, st));
+  HIPCK(ctx, hipMemsetAsync(w.nruns, 0, (size_t)n * s.Hkv * 2 * 4, st));
+  HIPCK(ctx, hipMemsetAsync(w.ekey64, 0, (size_t)n * s.Hq * 8, st));
+  HIPCK(ctx, hipMemsetAsync(w.eval64, 0, (size_t)n * s.Hq * 8, st));
+  // staging may still be read by the previous step's kernels, and tier 2 was
+  // written by earlier appends on this stream: copies wait for both
+  HIPCK(ctx, hipEventRecord(ctx->ev_start, st));
+  HIPCK(ctx, hipStreamWaitEvent(ctx->cstream, ctx->ev_start, 0));
+
+  const float C = (float)(1.4426950408889634 / sqrt((double)s.d));
+  HIPCK(ctx, launch_qprep(s, w, n, (const uint16_t *)q, C, st));
+  HIPCK(ctx, launch_score_int8(s, ctx->t, w, tab, layer, maxNB, st));
+  if (timing) HIPCK(ctx, hipEventRecord(ctx->ev_t[1], st));
+  HIPCK(ctx, launch_select(s, w, tab, ctx->th.tau_ppm, maxNB, st));
+  HIPCK(ctx, launch_plan_keys(s, w, tab, maxNB, st));
+  HIPCK(ctx, launch_gather_plan(s, w, n, st));
+  if (timing) HIPCK(ctx, hipEventRecord(ctx->ev_t[2], st));
+  Plan plan;
+  kvq_status rs = read_plan(ctx, st, plan);
+  if (rs != KVQ_OK) return rs;
+  ++syncs;
+  for (int round = 0;; ++round) {
+    const bool new_keys = plan.nk > 0;
+    if (!plan.ent.empty()) {
+      rs = issue_copies(ctx, tab, layer, plan, h2d, kblk, vblk);
+      if (rs != KVQ_OK) return rs;
+      HIPCK(ctx, hipEventRecord(ctx->ev_copy, ctx->cstream));
+      HIPCK(ctx, hipStreamWaitEvent(st, ctx->ev_copy, 0));
+    }
+    if (round > 0 && !(plan.flags & 1u)) break;      // every group final
+    if (round > ctx->th.R1) return fail(ctx, KVQ_EHIP, "controller did not finish its rounds");
+    if (new_keys) HIPCK(ctx, launch_score_fp16(s, w, tab, maxNB, st));
+    HIPCK(ctx, launch_control(s, ctx->t, w, tab, layer, ctx->th, round, maxNB, st));
+    HIPCK(ctx, launch_gather_plan(s, w, n, st));
+    rs = read_plan(ctx, st, plan);
+    if (rs != KVQ_OK) return rs;
+    ++syncs;
+    rounds = round + 1;
+    if (!(plan.flags & 1u) && plan.ent.empty()) break;
+  }
+  HIPCK(ctx, launch_finalize(s, w, tab, ctx->th, e_key, e_val, level, st));
+  const bool maybe_dense = ctx->th.force_dense || (plan.flags & 2u);
+  std::vector<uint8_t> gd;
+  if (maybe_dense) {
+    gd.resize((size_t)n * s.Hkv);
+    HIPCK(ctx, hipMemcpyAsync(gd.data(), w.gdense, gd.size(), hipMemcpyDeviceToHost, st));
+    HIPCK(ctx, hipStreamSynchronize(st));
+    ++syncs;
+    bool any = false;
+    for (int i = 0; i < n; ++i)
+      for (int g = 0; g < s.Hkv; ++g) {
+        if (!gd[(size_t)i * s.Hkv + g]) continue;
+        any = true;
+        ++dense_heads;
+        const size_t u = unit_of(s, tab.slot[i], layer, g);
+        const size_t ig = (size_t)i * s.Hkv + g;
+        const size_t bytes = (size_t)((tab.T[i] + BLOCK - 1) / BLOCK) * BLOCK * s.d * 2;
+        HIPCK(ctx, hipMemcpyAsync(w.stage_k + ig * s.Tmax * s.d, ctx->t2k_host + u * s.Tmax * s.d,
+                                  bytes, hipMemcpyHostToDevice, ctx->cstream));
+        HIPCK(ctx, hipMemcpyAsync(w.stage_v + ig * s.Tmax * s.d, ctx->t2v_host + u * s.Tmax * s.d,
+                                  bytes, hipMemcpyHostToDevice, ctx->cstream));
+        h2d += 2 * (int64_t)bytes;
+      }
+    if (any) {
+      HIPCK(ctx, hipEventRecord(ctx->ev_copy, ctx->cstream));
+      HIPCK(ctx, hipStreamWaitEvent(st, ctx->ev_copy, 0));
+      HIPCK(ctx, launch_decode(s, ctx->t, w, tab, layer, maxNB, true, st));
+    }
+  }
+  if (timing) HIPCK(ctx, hipEventRecord(ctx->ev_t[3], st));
+  HIPCK(ctx, launch_decode(s, ctx->t, w, tab, layer, maxNB, false, st));
+  HIPCK(ctx, launch_combine(s, w, tab, out, st));
+  if (timing) HIPCK(ctx, hipEventRecord(ctx->ev_t[4], st));
+
+  ctx->last_n = n;
+  ctx->last_layer = layer;
+  for (int i = 0; i < n; ++i) {
+    ctx->last_slot[i] = tab.slot[i];
+    ctx->last_T[i] = tab.T[i];
+  }
+  if (stats) {
+    memset(stats, 0, sizeof(*stats));
+    stats->promoted_key_blocks = kblk;
+    stats->promoted_value_blocks = vblk;
+    stats->dense_kv_heads = dense_heads;
+    stats->h2d_bytes = h2d;
+    stats->key_rounds = rounds;
+    stats->host_syncs = syncs;
+    std::vector<int8_t> lv((size_t)n * s.Hq);
+    HIPCK(ctx, hipMemcpyAsync(lv.data(), level, lv.size(), hipMemcpyDeviceToHost, st));
+    HIPCK(ctx, hipStreamSynchronize(st));
+    for (int8_t x : lv)
+      if (x >= 0 && x <= 4) stats->level_count[(int)x]++;
+    if (timing) {
+      float a = 0;
+      HIPCK(ctx, hipEventElapsedTime(&a, ctx->ev_t[0], ctx->ev_t[1]));
+      stats->ms_score = a;
+      HIPCK(ctx, hipEventElapsedTime(&a, ctx->ev_t[1], ctx->ev_t[2]));
+      stats->ms_select = a;
+      HIPCK(ctx, hipEventElapsedTime(&a, ctx->ev_t[2], ctx->ev_t[3]));
+      stats->ms_promote = a;
+      HIPCK(ctx, hipEventElapsedTime(&a, ctx->ev_t[3], ctx->ev_t[4]));
+      stats->ms_decode = a;
+      HIPCK(ctx, hipEventElapsedTime(&a, ctx->ev_t[0], ctx->ev_t[4]));
+      stats->ms_total = a;
+    }
+  }
+  return KVQ_OK;
+}
+
+// ---- test and debug exports -----------------------------------------------------
+
+int64_t kvq_tier1_export_bytes(const kvq_ctx *ctx, int32_t layer, int32_t seq) {
+  if (!ctx || layer < 0 || layer >= ctx->cfg.n_layers || seq < 0 || seq >= ctx->cfg.max_batch)
+    return KVQ_EINVAL;
+  const int64_t T = ctx->T[(size_t)seq * ctx->cfg.n_layers + layer];
+  const int64_t NB = (T + BLOCK - 1) / BLOCK, d = ctx->s.d;
+  return T * d + NB * d * 2 * 2 + NB * 4 + T * d + T * (d / 32) * 2 * 2 + d * 4 * 2;
+}
+
+kvq_status kvq_export_tier1(kvq_ctx *ctx, int32_t layer, int32_t seq, int32_t g, void *host_dst,
+                            size_t bytes) {
+  if (!ctx || !host_dst) return KVQ_EINVAL;
+  const int64_t need = kvq_tier1_export_bytes(ctx, layer, seq);
+  if (need < 0 || (size_t)need != bytes || g < 0 || g >= ctx->s.Hkv)
+    return fail(ctx, KVQ_EINVAL, "bad export request");
+  const Shape &s = ctx->s;
+  const int T = (int)ctx->T[(size_t)seq * s.L + layer];
+  const int NB = (T + BLOCK - 1) / BLOCK, d = s.d;
+  const size_t u = unit_of(s, seq, layer, g);
+  HIPCK(ctx, hipDeviceSynchronize());
+  uint8_t *p = (uint8_t *)host_dst;
+  if (T > 0) {
+    uint8_t *tmp = nullptr;
+    HIPCK(ctx, hipMalloc(&tmp, (size_t)T * d));
+    hipError_t e = launch_export_kcodes(s, ctx->t, u, T, tmp, nullptr);
+    if (e == hipSuccess) e = hipMemcpy(p, tmp, (size_t)T * d, hipMemcpyDeviceToHost);
+    if (e == hipSuccess) e = launch_export_vcodes(s, ctx->t, u, T, tmp, nullptr);
+    if (e == hipSuccess)
+      e = hipMemcpy(p + (size_t)T * d + (size_t)NB * d * 4 + (size_t)NB * 4, tmp, (size_t)T * d,
+                    hipMemcpyDeviceToHost);
+    (void)hipFree(tmp);
+    HIPCK(ctx, e);
+  }
+  std::vector<uint32_t> km((size_t)NB * d), vm((size_t)T * (d / 32)), mn(d), mx(d);
+  HIPCK(ctx, hipMemcpy(km.data(), ctx->t.kmeta + u * s.NBmax * d, km.size() * 4, hipMemcpyDeviceToHost));
+  HIPCK(ctx, hipMemcpy(vm.data(), ctx->t.vmeta + u * s.Tmax * (d / 32), vm.size() * 4,
+                       hipMemcpyDeviceToHost));
+  HIPCK(ctx, hipMemcpy(mn.data(), ctx->t.vmin + u * d, (size_t)d * 4, hipMemcpyDeviceToHost));
+  HIPCK(ctx, hipMemcpy(mx.data(), ctx->t.vmax + u * d, (size_t)d * 4, hipMemcpyDeviceToHost));
+  uint8_t *q = p + (size_t)T * d;
+  uint16_t *ks = (uint16_t *)q, *ko = ks + (size_t)NB * d;
+  for (size_t k = 0; k < km.size(); ++k) {
+    ks[k] = (uint16_t)(km[k] & 0xffffu);
+    ko[k] = (uint16_t)(km[k] >> 16);
+  }
+  q += (size_t)NB * d * 4;
+  HIPCK(ctx, hipMemcpy(q, ctx->t.eta + u * s.NBmax, (size_t)NB * 4, hipMemcpyDeviceToHost));
+  q += (size_t)NB * 4 + (size_t)T * d;
+  uint16_t *vs = (uint16_t *)q, *vo = vs + vm.size();
+  for (size_t k = 0; k < vm.size(); ++k) {
+    vs[k] = (uint16_t)(vm[k] & 0xffffu);
+    vo[k] = (uint16_t)(vm[k] >> 16);
+  }
+  q += vm.size() * 4;
+  float *fmn = (float *)q, *fmx = fmn + d;
+  auto unord = [](uint32_t x) {
+    uint32_t b = (x & 0x80000000u) ? (x & 0x7fffffffu) : ~x;
+    float f;
+    memcpy(&f, &b, 4);
+    return f;
+  };
+  for (int c = 0; c < d; ++c) {
+    fmn[c] = unord(mn[c]);
+    fmx[c] = unord(mx[c]);
+  }
+  return KVQ_OK;
+}
+
+int64_t kvq_trace_bytes(const kvq_ctx *ctx, int32_t which, int32_t seq) {
+  if (!ctx) return KVQ_EINVAL;
+  int i = -1;
+  for (int k = 0; k < ctx->last_n; ++k)
+    if (ctx->last_slot[k] == seq) i = k;
+  if (i < 0) return KVQ_ESTATE;
+  const int64_t T = ctx->last_T[i], NB = (T + BLOCK - 1) / BLOCK;
+  const int64_t Hq = ctx->s.Hq, Hkv = ctx->s.Hkv;
+  switch (which) {
+    case KVQ_TR_SHAT: case KVQ_TR_SP: return Hq * T * 4;
+    case KVQ_TR_MHAT: case KVQ_TR_LHAT: case KVQ_TR_DELTA: case KVQ_TR_M16: case KVQ_TR_L16:
+    case KVQ_TR_WHAT: case KVQ_TR_PI: case KVQ_TR_WT: case KVQ_TR_W16: return Hq * NB * 4;
+    case KVQ_TR_K0: case KVQ_TR_SSIZE: case KVQ_TR_HFLAGS: return Hq * 4;
+    case KVQ_TR_SSD: case KVQ_TR_EKEY64: case KVQ_TR_EVAL64: return Hq * 8;
+    case KVQ_TR_U: case KVQ_TR_V: return Hkv * NB;
+    case KVQ_TR_VH: return Hq * NB;
+    default: return KVQ_EINVAL;
+  }
+}
+
+kvq_status kvq_export_trace(kvq_ctx *ctx, int32_t which, int32_t seq, void *host_dst, size_t bytes) {
+  const int64_t need = kvq_trace_bytes(ctx, which, seq);
+  if (need < 0) return (kvq_status)need;
+  if (!host_dst || (size_t)need != bytes) return fail(ctx, KVQ_EINVAL, "bad trace request");
+  int i = 0;
+  for (int k = 0; k < ctx->last_n; ++k)
+    if (ctx->last_slot[k] == seq) i = k;
+  const Shape &s = ctx->s;
+  const Step &w = ctx->w;
+  const int64_t T = ctx->last_T[i], NB = (T + BLOCK - 1) / BLOCK;
+  HIPCK(ctx, hipDeviceSynchronize());
+  uint8_t *dst = (uint8_t *)host_dst;
+  auto rows = [&](const void *base, size_t elem, int nrows, size_t row_elems, size_t stride) -> hipError_t {
+    for (int r = 0; r < nrows; ++r) {
+      hipError_t e = hipMemcpy(dst + (size_t)r * row_elems * elem,
+                               (const uint8_t *)base + ((size_t)i * nrows + r) * stride * elem,
+                               row_elems * elem, hipMemcpyDeviceToHost);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  };
+  hipError_t e = hipSuccess;
+  switch (which) {
+    case KVQ_TR_SHAT: e = rows(w.shat, 4, s.Hq, T, s.Tmax); break;
+    case KVQ_TR_SP: e = rows(w.sp, 4, s.Hq, T, s.Tmax); break;
+    case KVQ_TR_MHAT: e = rows(w.mhat, 4, s.Hq, NB, s.NBmax); break;
+    case KVQ_TR_LHAT: e = rows(w.Lhat, 4, s.Hq, NB, s.NBmax); break;
+    case KVQ_TR_DELTA: e = rows(w.delta, 4, s.Hq, NB, s.NBmax); break;
+    case KVQ_TR_M16: e = rows(w.m16, 4, s.Hq, NB, s.NBmax); break;
+    case KVQ_TR_L16: e = rows(w.L16, 4, s.Hq, NB, s.NBmax); break;
+    case KVQ_TR_WHAT: e = rows(w.What, 4, s.Hq, NB, s.NBmax); break;
+    case KVQ_TR_PI: e = rows(w.pi, 4, s.Hq, NB, s.NBmax); break;
+    case KVQ_TR_WT: e = rows(w.Wt, 4, s.Hq, NB, s.NBmax); break;
+    case KVQ_TR_W16: e = rows(w.W16, 4, s.Hq, NB, s.NBmax); break;
+    case KVQ_TR_K0: e = rows(w.k0, 4, 1, s.Hq, s.Hq); break;
+    case KVQ_TR_SSIZE: e = rows(w.ssize, 4, 1, s.Hq, s.Hq); break;
+    case KVQ_TR_HFLAGS: e = rows(w.hflags, 4, 1, s.Hq, s.Hq); break;
+    case KVQ_TR_SSD: e = rows(w.ssd, 8, 1, s.Hq, s.Hq); break;
+    case KVQ_TR_EKEY64: e = rows(w.ekey64, 8, 1, s.Hq, s.Hq); break;
+    case KVQ_TR_EVAL64: e = rows(w.eval64, 8, 1, s.Hq, s.Hq); break;
+    case KVQ_TR_U: e = rows(w.U, 1, s.Hkv, NB, s.NBmax); break;
+    case KVQ_TR_V: e = rows(w.V, 1, s.Hkv, NB, s.NBmax); break;
+    case KVQ_TR_VH: e = rows(w.vh, 1, s.Hq, NB, s.NBmax); break;
+    default: return KVQ_EINVAL;
+  }
+  HIPCK(ctx, e);
+  return KVQ_OK;
+}
+
+kvq_status kvq_selftest_exp2k(const float *x, float *y, int64_t n, void *stream) {
+  if (!x || !y || n < 0) return KVQ_EINVAL;
+  if (n == 0) return KVQ_OK;
+  return launch_exp2k(x, y, n, (hipStream_t)stream) == hipSuccess ? KVQ_OK : KVQ_EHIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,400 @@
+// kvq_control.hip -- ranking-consistency check, the two bounds and the
+// fallback ladder ("Runtime-Certified Bounded-Error Quantized Attention":
+// Méthodologie §2 for E_key / E_val, Méthodologie §3 for the ranking check
+// and the four rungs, Contributions clés for deterministic recovery).
+//
+// One workgroup per (sequence, KV head) runs one controller round for the
+// group's query heads.  Readings (the page names the rungs, not triggers):
+//   * ranking check: Spearman correlation between the INT8 order of the
+//     promoted set S_h (positions in pi) and its FP16 order (W16 descending,
+//     index ascending) must reach rho_min:
+//       6e6 * sum d^2 <= (1e6 - rho_ppm) * n (n^2 - 1)     (exact integers);
+//   * E_key, bound on TV(p_dense, p_used) with tail T = blocks outside U_g:
+//       W+ = (Wt + 65)(1 + 2^-12), W- = Wt (1 - 2^-12)          (fp64, exact)
+//       g+ = fl32(exp2k(D') - 1)(1 + 2^-16) + 2^-20, g- = fl32(1 - exp2k(-D'))(...)
+//       E_key = min(1, sum_T ceil(W+ g+) / (sum_b floor(W-) - sum_T ceil(W+ g-)))
+//     (1 if a tail block has D' > 20 or the denominator is <= 0);
+//   * E_val = sum_{b not in V_g} ceil(W+ eta_b) / sum_b floor(W-);
+//   * rung 1: a consistent head with E_key > eps_key doubles |S_h| along pi
+//     while rounds remain; rung 3: ranking failure, or E_key > eps_key after
+//     the last round; rung 2: a head with E_val > v_tol promotes the values of
+//     blocks by contribution ceil(W+ eta_b) (descending, index ascending)
+//     until E_val <= v_tol; V_g = union of the heads' choices;
+//   * rung 4 (k_finalize): more than layer_frac of a sequence's heads at rung 3.
+// Every sum is an integer, so no reduction order can change a decision.
+#include "kvq_device.h"
+#include "kvq_internal.h"
+#include "kvq_blockops.h"
+
+namespace kvq {
+
+
+constexpr int CTL_NT = 1024;
+constexpr double W_UP = 1.0 + 0x1p-12;
+constexpr double W_DN = 1.0 - 0x1p-12;
+
+struct CtlShared {
+  unsigned long long u64[3][CTL_NT / 64];
+  float f32[CTL_NT / 64];
+  int i32[CTL_NT / 64];
+  int flag;
+  int wid;
+};
+
+__device__ unsigned long long block_sum_u64(unsigned long long v, unsigned long long *buf) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  if ((threadIdx.x & 63) == 0) buf[threadIdx.x >> 6] = v;
+  __syncthreads();
+  unsigned long long r = 0ull;
+  for (int k = 0; k < (int)(blockDim.x >> 6); ++k) r += buf[k];
+  __syncthreads();
+  return r;
+}
+
+__device__ float block_max_f32(float v, float *buf) {
+  v = bfly_max<64>(v);
+  if ((threadIdx.x & 63) == 0) buf[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = buf[0];
+  for (int k = 1; k < (int)(blockDim.x >> 6); ++k) r = fmaxf(r, buf[k]);
+  __syncthreads();
+  return r;
+}
+
+__device__ int block_or_i32(int v, int *buf) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v |= __shfl_xor(v, o, 64);
+  if ((threadIdx.x & 63) == 0) buf[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int r = 0;
+  for (int k = 0; k < (int)(blockDim.x >> 6); ++k) r |= buf[k];
+  __syncthreads();
+  return r;
+}
+
+__device__ int block_min_i32(int v, int *buf) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
+  if ((threadIdx.x & 63) == 0) buf[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int r = buf[0];
+  for (int k = 1; k < (int)(blockDim.x >> 6); ++k) r = min(r, buf[k]);
+  __syncthreads();
+  return r;
+}
+
+// Evaluates one head on the current U: mixed weights Wt, FP16 weights W16
+// over S_h, ranking verdict and E_key.
+__device__ void evaluate_head(const Shape &s, const Step &w, const Thresh &th, int i, int g, int hq,
+                              int NB, unsigned long long *keys, uint16_t *pos, CtlShared &sh) {
+  const size_t base = ((size_t)i * s.Hq + hq) * s.NBmax;
+  const uint8_t *U = w.U + ((size_t)i * s.Hkv + g) * s.NBmax;
+  // mixed weights
+  float mloc = -INFINITY;
+  for (int b = threadIdx.x; b < NB; b += CTL_NT)
+    mloc = fmaxf(mloc, U[b] ? w.m16[base + b] : w.mhat[base + b]);
+  const float Mt = block_max_f32(mloc, sh.f32);
+  unsigned long long den = 0ull, num = 0ull, sub = 0ull;
+  int cap = 0;
+  for (int b = threadIdx.x; b < NB; b += CTL_NT) {
+    const bool pr = U[b] != 0;
+    const float mb = pr ? w.m16[base + b] : w.mhat[base + b];
+    const uint32_t Lb = pr ? w.L16[base + b] : w.Lhat[base + b];
+    const uint32_t Wt = (uint32_t)floorf((float)Lb * exp2k(mb - Mt));
+    w.Wt[base + b] = Wt;
+    const double Wp = (double)(Wt + 65u) * W_UP;
+    const double Wm = (double)Wt * W_DN;
+    den += (unsigned long long)floor(Wm);
+    if (!pr) {
+      const float dl = w.delta[base + b];
+      if (dl > 20.0f) {
+        cap = 1;
+      } else {
+        const float up = exp2k(dl) - 1.0f;
+        const float dn = 1.0f - exp2k(-dl);
+        const double gp = (double)up * (1.0 + 0x1p-16) + 0x1p-20;
+        const double gm = (double)dn * (1.0 + 0x1p-16) + 0x1p-20;
+        num += (unsigned long long)ceil(Wp * gp);
+        sub += (unsigned long long)ceil(Wp * gm);
+      }
+    }
+  }
+  den = block_sum_u64(den, sh.u64[0]);
+  num = block_sum_u64(num, sh.u64[1]);
+  sub = block_sum_u64(sub, sh.u64[2]);
+  cap = block_or_i32(cap, sh.i32);
+  double ek;
+  if (cap) {
+    ek = 1.0;
+  } else {
+    const long long D = (long long)den - (long long)sub;
+    ek = (D <= 0) ? 1.0 : fmin(1.0, (double)num / (double)D);
+  }
+
+  // ranking over S_h = pi[0 .. n)
+  const int n = w.ssize[(size_t)i * s.Hq + hq];
+  const uint32_t *pi = w.pi + base;
+  float m16loc = -INFINITY;
+  for (int k = threadIdx.x; k < n; k += CTL_NT) m16loc = fmaxf(m16loc, w.m16[base + pi[k]]);
+  const float M16 = block_max_f32(m16loc, sh.f32);
+  for (int b = threadIdx.x; b < NB; b += CTL_NT) w.W16[base + b] = 0u;
+  __syncthreads();
+  const int n2 = pow2_at_least(n);
+  for (int k = threadIdx.x; k < n2; k += CTL_NT) {
+    unsigned long long key = 0ull;
+    if (k < n) {
+      const uint32_t b = pi[k];
+      const uint32_t W16 = (uint32_t)floorf((float)w.L16[base + b] * exp2k(w.m16[base + b] - M16));
+      w.W16[base + b] = W16;
+      key = ((unsigned long long)W16 << 32) | (unsigned long long)(0xffffffffu - b);
+      pos[b] = (uint16_t)k;
+    }
+    keys[k] = key;
+  }
+  __syncthreads();
+  bitonic_desc<CTL_NT>(keys, n2);
+  unsigned long long ssd = 0ull;
+  for (int j = threadIdx.x; j < n; j += CTL_NT) {
+    const uint32_t b = 0xffffffffu - (uint32_t)(keys[j] & 0xffffffffull);
+    const long long dd = (long long)pos[b] - (long long)j;
+    ssd += (unsigned long long)(dd * dd);
+  }
+  ssd = block_sum_u64(ssd, sh.u64[0]);
+  if (threadIdx.x == 0) {
+    const unsigned long long nn = (unsigned long long)n;
+    const bool ok = (n <= 1) ||
+                    (6000000ull * ssd <= (unsigned long long)(1000000 - th.rho_ppm) * nn * (nn * nn - 1ull));
+    w.ssd[(size_t)i * s.Hq + hq] = ssd;
+    w.ekey64[(size_t)i * s.Hq + hq] = ek;
+    uint32_t f = w.hflags[(size_t)i * s.Hq + hq];
+    f = ok ? (f | 1u) : ((f & ~1u) | 4u);
+    w.hflags[(size_t)i * s.Hq + hq] = f;
+  }
+  __syncthreads();
+}
+
+// Rung 2 for one head: greedy value promotion; returns via vh / V flags.
+__device__ void value_rung(const Shape &s, const Tier1 &t, const Step &w, const Thresh &th, int i,
+                           int g, int hq, int NB, size_t unit, unsigned long long *keys,
+                           CtlShared &sh) {
+  const size_t base = ((size_t)i * s.Hq + hq) * s.NBmax;
+  const float *eta = t.eta + unit * s.NBmax;
+  unsigned long long numv = 0ull, denv = 0ull;
+  for (int b = threadIdx.x; b < NB; b += CTL_NT) {
+    const uint32_t Wt = w.Wt[base + b];
+    numv += (unsigned long long)ceil((double)(Wt + 65u) * W_UP * (double)eta[b]);
+    denv += (unsigned long long)floor((double)Wt * W_DN);
+  }
+  numv = block_sum_u64(numv, sh.u64[0]);
+  denv = block_sum_u64(denv, sh.u64[1]);
+  if (!((double)numv / (double)denv > th.v_tol)) return;
+  const int n2 = pow2_at_least(NB);
+  for (int b = threadIdx.x; b < n2; b += CTL_NT) {
+    unsigned long long key = 0ull;
+    if (b < NB) {
+      const uint32_t Wt = w.Wt[base + b];
+      const unsigned long long c =
+          (unsigned long long)ceil((double)(Wt + 65u) * W_UP * (double)eta[b]);
+      key = (c << 12) | (unsigned long long)(4095 - b);
+    }
+    keys[b] = key;
+  }
+  __syncthreads();
+  bitonic_desc<CTL_NT>(keys, n2);
+  // prefix sums of the sorted contributions (4 per thread, NB <= 4096)
+  constexpr int PER = MAX_NB / CTL_NT;
+  unsigned long long loc[PER];
+  unsigned long long run = 0ull;
+  for (int k = 0; k < PER; ++k) {
+    const int p = threadIdx.x * PER + k;
+    if (p < NB) run += keys[p] >> 12;
+    loc[k] = run;
+  }
+  __shared__ unsigned long long part[CTL_NT + 1];
+  part[threadIdx.x + 1] = run;
+  if (threadIdx.x == 0) part[0] = 0ull;
+  __syncthreads();
+  for (int o = 1; o < CTL_NT; o <<= 1) {
+    unsigned long long v = 0ull;
+    if ((int)threadIdx.x >= o) v = part[threadIdx.x + 1 - o];
+    __syncthreads();
+    part[threadIdx.x + 1] += v;
+    __syncthreads();
+  }
+  const unsigned long long off = part[threadIdx.x];
+  int kmin = NB;
+  for (int k = 0; k < PER; ++k) {
+    const int p = threadIdx.x * PER + k;
+    if (p >= NB) break;
+    const unsigned long long rem = numv - (off + loc[k]);
+    if ((double)rem / (double)denv <= th.v_tol) {
+      kmin = min(kmin, p + 1);
+      break;
+    }
+  }
+  kmin = block_min_i32(kmin, sh.i32);
+  uint8_t *vh = w.vh + base;
+  uint8_t *V = w.V + ((size_t)i * s.Hkv + g) * s.NBmax;
+  for (int p = threadIdx.x; p < kmin; p += CTL_NT) {
+    const int b = 4095 - (int)(keys[p] & 4095ull);
+    vh[b] = 1;
+    V[b] = 1;   // benign race across heads: every writer stores 1
+  }
+  if (threadIdx.x == 0) w.hflags[(size_t)i * s.Hq + hq] |= 8u;   // bit3: V_h non-empty
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(CTL_NT) void k_control(Shape s, Tier1 t, Step w, SeqTab tab, int layer,
+                                                    Thresh th, int round) {
+  extern __shared__ unsigned long long keys[];
+  __shared__ uint16_t pos[MAX_NB];
+  __shared__ CtlShared sh;
+  __shared__ int tmp[17];
+  const int i = blockIdx.y, g = blockIdx.x;
+  uint32_t *gs = w.gstat + (size_t)i * s.Hkv + g;
+  if (*gs & 1u) {                             // group already final: nothing new to copy
+    if (threadIdx.x == 0) {
+      w.nruns[((size_t)i * s.Hkv + g) * 2 + 0] = 0u;
+      w.nruns[((size_t)i * s.Hkv + g) * 2 + 1] = 0u;
+    }
+    return;
+  }
+  const int T = tab.T[i], NB = (T + BLOCK - 1) / BLOCK;
+  const size_t unit = unit_of(s, tab.slot[i], layer, g);
+  if (threadIdx.x == 0) w.nruns[((size_t)i * s.Hkv + g) * 2 + 0] = 0u;
+  for (int hh = 0; hh < s.G; ++hh) {
+    const int hq = g * s.G + hh;
+    if (w.hflags[(size_t)i * s.Hq + hq] & 4u) continue;      // failed earlier
+    evaluate_head(s, w, th, i, g, hq, NB, keys, pos, sh);
+  }
+  // rung 1
+  if (threadIdx.x == 0) {
+    int any = 0;
+    if (round < th.R1) {
+      for (int hh = 0; hh < s.G; ++hh) {
+        const size_t o = (size_t)i * s.Hq + g * s.G + hh;
+        const uint32_t f = w.hflags[o];
+        if (f & 4u) continue;
+        if (w.ekey64[o] > th.eps_key && w.ssize[o] < NB) {
+          w.ssize[o] = min(NB, 2 * w.ssize[o]);
+          w.hflags[o] = f | 2u;
+          any = 1;
+        }
+      }
+    }
+    sh.wid = any;
+  }
+  __syncthreads();
+  if (sh.wid) {
+    plan_group_keys(s, w, i, g, NB);
+    return;
+  }
+  // final round of this group: rung 3 for heads still above eps_key
+  if (threadIdx.x == 0) {
+    for (int hh = 0; hh < s.G; ++hh) {
+      const size_t o = (size_t)i * s.Hq + g * s.G + hh;
+      if (!(w.hflags[o] & 4u) && w.ekey64[o] > th.eps_key) w.hflags[o] |= 4u;
+    }
+  }
+  __syncthreads();
+  // rung 2
+  for (int hh = 0; hh < s.G; ++hh) {
+    const int hq = g * s.G + hh;
+    if (w.hflags[(size_t)i * s.Hq + hq] & 4u) continue;
+    value_rung(s, t, w, th, i, g, hq, NB, unit, keys, sh);
+  }
+  __syncthreads();
+  // E_val on the group's V and the levels
+  const uint8_t *V = w.V + ((size_t)i * s.Hkv + g) * s.NBmax;
+  const float *eta = t.eta + unit * s.NBmax;
+  int any3 = 0;
+  for (int hh = 0; hh < s.G; ++hh) {
+    const int hq = g * s.G + hh;
+    const size_t o = (size_t)i * s.Hq + hq;
+    const uint32_t f = w.hflags[o];
+    if (f & 4u) {
+      if (threadIdx.x == 0) {
+        w.hlevel[o] = 3;
+        w.eval64[o] = 0.0;
+      }
+      any3 = 1;
+      continue;
+    }
+    const size_t base = o * s.NBmax;
+    unsigned long long numv = 0ull, denv = 0ull;
+    for (int b = threadIdx.x; b < NB; b += CTL_NT) {
+      const uint32_t Wt = w.Wt[base + b];
+      if (!V[b]) numv += (unsigned long long)ceil((double)(Wt + 65u) * W_UP * (double)eta[b]);
+      denv += (unsigned long long)floor((double)Wt * W_DN);
+    }
+    numv = block_sum_u64(numv, sh.u64[0]);
+    denv = block_sum_u64(denv, sh.u64[1]);
+    if (threadIdx.x == 0) {
+      w.eval64[o] = (double)numv / (double)denv;
+      w.hlevel[o] = (f & 8u) ? 2 : ((f & 2u) ? 1 : 0);
+    }
+  }
+  // value promotions to copy
+  uint8_t *Vn = w.Vnew + ((size_t)i * s.Hkv + g) * s.NBmax;
+  for (int b = threadIdx.x; b < NB; b += CTL_NT) Vn[b] = V[b];
+  __syncthreads();
+  uint32_t *runs = w.runs + (((size_t)i * s.Hkv + g) * 2 + 1) * s.runmax;
+  const int nr = build_runs(Vn, NB, runs, tmp);
+  if (threadIdx.x == 0) {
+    w.nruns[((size_t)i * s.Hkv + g) * 2 + 1] = (uint32_t)nr;
+    *gs = 1u | (any3 ? 2u : 0u);
+    uint32_t *fl = w.hflags + (size_t)i * s.Hq + g * s.G;
+    for (int hh = 0; hh < s.G; ++hh) fl[hh] = (fl[hh] & 0xffu) | ((uint32_t)round << 8);
+  }
+}
+
+hipError_t launch_control(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,
+                          int layer, const Thresh &th, int round, int maxNB, hipStream_t st) {
+  const int n2 = pow2_at_least(maxNB);
+  hipLaunchKernelGGL(k_control, dim3(s.Hkv, tab.n), dim3(CTL_NT), n2 * sizeof(unsigned long long),
+                     st, s, t, w, tab, layer, th, round);
+  return hipGetLastError();
+}
+
+// ---- rung 4 and the per-head outputs ---------------------------------------------
+__device__ __forceinline__ float f32_up(double x) {
+  float f = (float)x;
+  if ((double)f < x) f = __uint_as_float(__float_as_uint(f) + 1u);   // x >= 0
+  return f;
+}
+
+__global__ void k_finalize(Shape s, Step w, SeqTab tab, Thresh th, float *e_key, float *e_val,
+                           int8_t *level) {
+  const int i = blockIdx.x;
+  __shared__ int n3;
+  if (threadIdx.x == 0) n3 = 0;
+  __syncthreads();
+  for (int h = threadIdx.x; h < s.Hq; h += blockDim.x)
+    if (w.hlevel[(size_t)i * s.Hq + h] == 3) atomicAdd(&n3, 1);
+  __syncthreads();
+  const bool all4 = th.force_dense ||
+                    1000000ull * (unsigned long long)n3 > (unsigned long long)th.frac_ppm * s.Hq;
+  for (int h = threadIdx.x; h < s.Hq; h += blockDim.x) {
+    const size_t o = (size_t)i * s.Hq + h;
+    const int lv = all4 ? 4 : w.hlevel[o];
+    w.hlevel[o] = (int8_t)lv;
+    level[o] = (int8_t)lv;
+    e_key[o] = (lv >= 3) ? 0.0f : f32_up(w.ekey64[o]);
+    e_val[o] = (lv >= 3) ? 0.0f : f32_up(w.eval64[o]);
+  }
+  __syncthreads();
+  for (int g = threadIdx.x; g < s.Hkv; g += blockDim.x) {
+    uint8_t dn = 0;
+    for (int hh = 0; hh < s.G; ++hh) dn |= (w.hlevel[(size_t)i * s.Hq + g * s.G + hh] >= 3);
+    w.gdense[(size_t)i * s.Hkv + g] = dn;
+  }
+}
+
+hipError_t launch_finalize(const Shape &s, const Step &w, const SeqTab &tab, const Thresh &th,
+                           float *e_key, float *e_val, int8_t *level, hipStream_t st) {
+  hipLaunchKernelGGL(k_finalize, dim3(tab.n), dim3(64), 0, st, s, w, tab, th, e_key, e_val, level);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -1,0 +1,118 @@
+// kvq_internal.h -- context layout and kernel argument blocks of libkvq.
+//
+// Layout of everything the library keeps in device memory (tier 1 and the
+// per-step scratch) and of tier 2 in pinned host memory.  A "unit" is one
+// (slot, layer, KV head); u = (slot * n_layers + layer) * n_kv_heads + g.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string>
+
+#include "../../include/kvq.h"
+
+namespace kvq {
+
+constexpr int MAX_CALL = KVQ_MAX_CALL_SEQS;
+constexpr int MAX_NB = 4096;        // blocks per sequence (262144 tokens)
+constexpr int DEC_CB = 16;          // blocks per split-K chunk of the decode kernels
+
+// Tier 1, per unit (device memory):
+//   kcodes [NBmax][64*d] u8   block-local MFMA operand order: the 16 bytes at
+//                             ((ks*4 + nt)*64 + l)*16 are the codes of token
+//                             nt*16 + l%16, channels ks*64 + 16*(l/16) + 0..15
+//   kmeta  [NBmax][d]    u32  binary16 scale (low half), offset (high half)
+//   vcodes [Tmax][d/2]   u8   channel 2c in the low nibble, 2c+1 in the high
+//   vmeta  [Tmax][d/32]  u32  binary16 scale (low), offset (high) per group
+//   eta    [NBmax]       f32  per-block value error annotation
+//   vmin/vmax [d]        u32  order-mapped floats, running over all tokens
+//   openk  [64][d]       u16  FP16 keys of the open (partial) block
+// Tier 2, per unit (pinned host, device-mapped): t2k/t2v [Tmax][d] fp16.
+struct Tier1 {
+  uint8_t *kcodes;
+  uint32_t *kmeta;
+  uint8_t *vcodes;
+  uint32_t *vmeta;
+  float *eta;
+  uint32_t *vmin, *vmax;
+  uint16_t *openk;
+  uint16_t *t2k, *t2v;     // device-mapped pointers to pinned host memory
+};
+
+// Per-step scratch, indexed by the position i of a sequence in the call.
+struct Step {
+  float *qp;                       // [B][Hq][d]
+  float *shat, *sp;                // [B][Hq][Tmax]
+  float *mhat, *delta, *m16;       // [B][Hq][NBmax]
+  uint32_t *Lhat, *L16, *What, *pi, *Wt, *W16;
+  uint8_t *vh;                     // [B][Hq][NBmax]
+  int32_t *k0, *ssize;             // [B][Hq]
+  unsigned long long *ssd;         // [B][Hq]
+  double *ekey64, *eval64;         // [B][Hq]
+  uint32_t *hflags;                // [B][Hq]
+  int8_t *hlevel;                  // [B][Hq]
+  uint8_t *U, *Knew, *V, *Vnew;    // [B][Hkv][NBmax]
+  uint32_t *gstat;                 // [B][Hkv] bit0 done, bit1 any rung 3
+  uint32_t *runs;                  // [B][Hkv][2][RUNMAX] start | len << 16
+  uint32_t *nruns;                 // [B][Hkv][2]
+  unsigned long long *plan;        // compacted runs for the host
+  uint16_t *stage_k, *stage_v;     // [B][Hkv][Tmax][d]
+  float *part, *partd;             // [B][Hkv][NCH][G][d + 2]
+  uint8_t *gdense;                 // [B][Hkv]
+};
+
+struct SeqTab {
+  int n;
+  int slot[MAX_CALL];
+  int T[MAX_CALL];
+};
+
+struct Shape {
+  int L, Hq, Hkv, G, d, Tmax, NBmax, runmax, nchmax, B;
+};
+
+struct Thresh {
+  int tau_ppm, rho_ppm, R1, frac_ppm;
+  double eps_key, v_tol;
+  int force_dense;
+};
+
+// Layout helpers (host and device).
+__host__ __device__ inline size_t unit_of(const Shape &s, int slot, int layer, int g) {
+  return ((size_t)slot * s.L + layer) * s.Hkv + g;
+}
+
+// ---- launchers (each in its own .hip file) ---------------------------------
+
+struct AppendArgs {
+  int n, layer;
+  int slot[MAX_CALL], T_old[MAX_CALL], n_new[MAX_CALL], in_off[MAX_CALL], n_blk[MAX_CALL];
+};
+hipError_t launch_append(const Shape &s, const Tier1 &t, const AppendArgs &a, const uint16_t *k,
+                         const uint16_t *v, int max_blk, hipStream_t st);
+
+hipError_t launch_qprep(const Shape &s, const Step &w, int n, const uint16_t *q, float C,
+                        hipStream_t st);
+hipError_t launch_score_int8(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,
+                             int layer, int maxNB, hipStream_t st);
+hipError_t launch_select(const Shape &s, const Step &w, const SeqTab &tab, int tau_ppm, int maxNB,
+                         hipStream_t st);
+hipError_t launch_plan_keys(const Shape &s, const Step &w, const SeqTab &tab, int maxNB,
+                            hipStream_t st);
+hipError_t launch_score_fp16(const Shape &s, const Step &w, const SeqTab &tab, int maxNB,
+                             hipStream_t st);
+hipError_t launch_control(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,
+                          int layer, const Thresh &th, int round, int maxNB, hipStream_t st);
+hipError_t launch_gather_plan(const Shape &s, const Step &w, int n, hipStream_t st);
+hipError_t launch_finalize(const Shape &s, const Step &w, const SeqTab &tab, const Thresh &th,
+                           float *e_key, float *e_val, int8_t *level, hipStream_t st);
+hipError_t launch_decode(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,
+                         int layer, int maxNB, bool dense, hipStream_t st);
+hipError_t launch_combine(const Shape &s, const Step &w, const SeqTab &tab, float *out,
+                          hipStream_t st);
+hipError_t launch_exp2k(const float *x, float *y, int64_t n, hipStream_t st);
+hipError_t launch_export_kcodes(const Shape &s, const Tier1 &t, size_t u, int T, uint8_t *dst,
+                                hipStream_t st);
+hipError_t launch_export_vcodes(const Shape &s, const Tier1 &t, size_t u, int T, uint8_t *dst,
+                                hipStream_t st);
+
+}  // namespace kvq

@@ -1,0 +1,280 @@
+// kvq_score.hip -- the INT8 scoring pass and the FP16 scoring of promoted
+// blocks ("Runtime-Certified Bounded-Error Quantized Attention",
+// Méthodologie §3: a lightweight pass over the INT8 keys estimates per-block
+// attention mass; Méthodologie §2: the per-token score perturbation Delta
+// that bounds the key error, from quantization scales and query values).
+//
+// Scores are in log2 units: q'_c = fl32(q_c * fl32(log2(e) / sqrt(d))).
+//
+// INT8 score of token t in block b for query head h (exact integer core):
+//   a_c = fl32(q'_c s_bc),  e = ilogb(max_c |a_c|) - 21,  A_c = rint(a_c 2^-e)
+//   D_t = sum_c A_c (code_tc - 128)        (exact; any order)
+//   beta = dot of q' with fl32(off + 128 s) in the fixed order below
+//   shat_t = fmaf(fl32(D_t), 2^e, beta)
+// The four query heads of a KV head share the block's codes, so the core is
+// a real contraction: 16 rows (4 heads x 3 signed-byte limbs of A, + 1 zero
+// row each) x 64 channels x 16 tokens per v_mfma_i32_16x16x64_i8.  Limbs:
+// A = L2 2^16 + L1 2^8 + L0 with L0, L1 in [-128, 127]; each limb's dot
+// product is exact in int32, and D_t is recombined in int64.
+//
+// Fixed order of per-block channel sums (beta and Delta'): lane (h, j) of a
+// wave owns channels [j d/16, (j+1) d/16) of head h, runs an fma chain over
+// them from 0, then the 16 lanes of the head fold in half (xor 8, 4, 2, 1).
+//
+// Delta'_b (bound on |shat_t - s'_t|, s' the FP16-key score below):
+//   K'_c = max(|off_c|, |fmaf(256, s_c, off_c)|)
+//   t_c  = fmaf(d 2^-22, K'_c, s_c / 2)
+//   Delta' = fl32(fl32(sum_c |q'_c| t_c + R) (1 + 2^-15)), R = 64 d 2^e
+// (s_c/2: quantization half-step; d 2^-22 K': fp32 evaluation of both score
+// chains; R: rounding of A; the last factor: evaluation of Delta' itself.)
+//
+// FP16-key score (promoted blocks): s'_t = fma chain over c ascending of
+// q'_c * k_tc from 0.  Block ingredients of any score row x:
+//   m_b = max_t x_t,   L_b = sum_t floor(2^24 exp2k(fl32(x_t - m_b)))  (exact).
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+__global__ void k_qprep(int total, const uint16_t *__restrict__ q, float C, float *__restrict__ qp) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx < total) qp[idx] = h2f(q[idx]) * C;
+}
+
+hipError_t launch_qprep(const Shape &s, const Step &w, int n, const uint16_t *q, float C,
+                        hipStream_t st) {
+  const int total = n * s.Hq * s.d;
+  hipLaunchKernelGGL(k_qprep, dim3((total + 255) / 256), dim3(256), 0, st, total, q, C, w.qp);
+  return hipGetLastError();
+}
+
+// Wave-level LDS hand-off between lanes of one wave.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+constexpr int S8_BLOCKS_PER_WG = 16;   // 4 waves x 4 blocks
+
+template <int D>
+__global__ __launch_bounds__(256) void k_score_int8(Shape s, Tier1 t, Step w, SeqTab tab, int layer) {
+  constexpr int CW = D / 16;            // channels per lane-chunk
+  constexpr int NKS = D / 64;           // MFMA k-steps per block
+  constexpr int AST = D + 16;           // LDS row stride of the A operand (bank spread)
+  const int i = blockIdx.z, g = blockIdx.y;
+  const int T = tab.T[i], NB = (T + BLOCK - 1) / BLOCK;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int h = lane >> 4, jc = lane & 15;
+  const bool hv = h < s.G;
+  const int hq = g * s.G + (hv ? h : 0);
+  const size_t u = unit_of(s, tab.slot[i], layer, g);
+
+  __shared__ __align__(16) int8_t As[4][16][AST];
+
+  float qv[CW];
+  {
+    const float *qsrc = w.qp + ((size_t)i * s.Hq + hq) * D + jc * CW;
+#pragma unroll
+    for (int k = 0; k < CW; ++k) qv[k] = qsrc[k];
+  }
+
+  const int b_first = blockIdx.x * S8_BLOCKS_PER_WG + wave;
+  const int b_end = min(NB, (int)(blockIdx.x + 1) * S8_BLOCKS_PER_WG);
+  for (int b = b_first; b < b_end; b += 4) {
+    const int n = min(BLOCK, T - b * BLOCK);
+    const uint8_t *kc = t.kcodes + (u * s.NBmax + b) * (size_t)(BLOCK * D);
+    v4i Bv[NKS][4];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        Bv[ks][nt] = *(const v4i *)(kc + ((size_t)((ks * 4 + nt) * 64 + lane)) * 16);
+
+    // ---- prologue: exponent, limbs of A, beta and Delta' per head -----------
+    const uint32_t *km = t.kmeta + (u * s.NBmax + b) * D + jc * CW;
+    float sv[CW], ov[CW], a[CW];
+    float am = 0.0f;
+#pragma unroll
+    for (int k = 0; k < CW; ++k) {
+      const uint32_t m = km[k];
+      sv[k] = h2f((uint16_t)(m & 0xffffu));
+      ov[k] = h2f((uint16_t)(m >> 16));
+      a[k] = qv[k] * sv[k];
+      am = fmaxf(am, fabsf(a[k]));
+    }
+    am = bfly_max<16>(am);
+    const bool zero = !(am > 0.0f);
+    const int e = zero ? 0 : ilogb_f(am) - 21;
+    uint32_t l0w[CW / 4], l1w[CW / 4], l2w[CW / 4];
+#pragma unroll
+    for (int k = 0; k < CW / 4; ++k) l0w[k] = l1w[k] = l2w[k] = 0u;
+    float pb = 0.0f, pd = 0.0f;
+#pragma unroll
+    for (int k = 0; k < CW; ++k) {
+      const int A = (int)rintf(ldexpf(a[k], -e));
+      const int L0 = ((A + 128) & 255) - 128;
+      const int A1 = (A - L0) >> 8;
+      const int L1 = ((A1 + 128) & 255) - 128;
+      const int L2 = (A1 - L1) >> 8;
+      l0w[k / 4] |= ((uint32_t)L0 & 255u) << (8 * (k % 4));
+      l1w[k / 4] |= ((uint32_t)L1 & 255u) << (8 * (k % 4));
+      l2w[k / 4] |= ((uint32_t)L2 & 255u) << (8 * (k % 4));
+      const float uu = fmaf(128.0f, sv[k], ov[k]);
+      pb = fmaf(qv[k], uu, pb);
+      const float kp = fmaxf(fabsf(ov[k]), fabsf(fmaf(256.0f, sv[k], ov[k])));
+      const float tt = fmaf((float)D * 0x1p-22f, kp, 0.5f * sv[k]);
+      pd = fmaf(fabsf(qv[k]), tt, pd);
+    }
+    pb = bfly_sum<16>(pb);
+    pd = bfly_sum<16>(pd);
+    {
+      int8_t *row = &As[wave][h * 4][jc * CW];
+#pragma unroll
+      for (int k = 0; k < CW / 4; ++k) {
+        const uint32_t z = 0u;
+        ((uint32_t *)(row + 0 * AST))[k] = hv ? l0w[k] : z;
+        ((uint32_t *)(row + 1 * AST))[k] = hv ? l1w[k] : z;
+        ((uint32_t *)(row + 2 * AST))[k] = hv ? l2w[k] : z;
+        ((uint32_t *)(row + 3 * AST))[k] = z;
+      }
+    }
+    if (hv && jc == 0) {
+      const float R = zero ? 0.0f : ldexpf(64.0f * (float)D, e);
+      w.delta[((size_t)i * s.Hq + hq) * s.NBmax + b] = (pd + R) * (1.0f + 0x1p-15f);
+    }
+    wave_lds_sync();
+
+    // ---- exact integer core on the matrix cores -------------------------------
+    v4i acc[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[nt] = (v4i){0, 0, 0, 0};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const v4i Aop = *(const v4i *)&As[wave][lane & 15][ks * 64 + 16 * (lane >> 4)];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        v4i Bop = Bv[ks][nt] ^ (v4i){(int)0x80808080, (int)0x80808080, (int)0x80808080,
+                                     (int)0x80808080};
+        acc[nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aop, Bop, acc[nt], 0, 0, 0);
+      }
+    }
+
+    // ---- scores and block ingredients (lane: head lane/16, token lane%16) -----
+    const float sc = ldexpf(1.0f, e);
+    float x[4];
+    float mx = -INFINITY;
+    float *dst = w.shat + ((size_t)i * s.Hq + hq) * s.Tmax + (size_t)b * BLOCK;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const long long Dv = ((long long)acc[nt][2] << 16) + ((long long)acc[nt][1] << 8) +
+                           (long long)acc[nt][0];
+      x[nt] = fmaf(i64_to_f32(Dv), sc, pb);
+      const int tok = nt * 16 + jc;
+      if (tok < n) {
+        mx = fmaxf(mx, x[nt]);
+        if (hv) dst[tok] = x[nt];
+      }
+    }
+    mx = bfly_max<16>(mx);
+    uint32_t Ls = 0u;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+      if (nt * 16 + jc < n) Ls += (uint32_t)floorf(0x1p24f * exp2k(x[nt] - mx));
+    Ls = bfly_sum_u32<16>(Ls);
+    if (hv && jc == 0) {
+      const size_t o = ((size_t)i * s.Hq + hq) * s.NBmax + b;
+      w.mhat[o] = mx;
+      w.Lhat[o] = Ls;
+    }
+    wave_lds_sync();
+  }
+}
+
+hipError_t launch_score_int8(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,
+                             int layer, int maxNB, hipStream_t st) {
+  dim3 grid((maxNB + S8_BLOCKS_PER_WG - 1) / S8_BLOCKS_PER_WG, s.Hkv, tab.n);
+  if (s.d == 128)
+    hipLaunchKernelGGL(k_score_int8<128>, grid, dim3(256), 0, st, s, t, w, tab, layer);
+  else
+    hipLaunchKernelGGL(k_score_int8<64>, grid, dim3(256), 0, st, s, t, w, tab, layer);
+  return hipGetLastError();
+}
+
+// ---- FP16-key scores of blocks promoted this round ------------------------------
+// One workgroup per (sequence, KV head, block); wave h = query head of the
+// group, lane = token.  Each lane runs the canonical fma chain over channels.
+template <int D>
+__global__ __launch_bounds__(256) void k_score_fp16(Shape s, Step w, SeqTab tab) {
+  constexpr int KST = D + 2;            // LDS row stride (halves): 4-byte bank spread
+  const int i = blockIdx.z, g = blockIdx.y, b = blockIdx.x;
+  const int T = tab.T[i], NB = (T + BLOCK - 1) / BLOCK;
+  if (b >= NB) return;
+  uint8_t *flag = w.Knew + ((size_t)i * s.Hkv + g) * s.NBmax + b;
+  if (*flag == 0) return;
+  const int n = min(BLOCK, T - b * BLOCK);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __shared__ __align__(16) uint16_t sk[BLOCK * KST];
+  __shared__ float sq[4][D];
+
+  const uint16_t *src = w.stage_k + (((size_t)i * s.Hkv + g) * s.Tmax + (size_t)b * BLOCK) * D;
+  for (int idx = threadIdx.x; idx < BLOCK * D / 2; idx += 256) {
+    const int r = idx / (D / 2), c2 = (idx % (D / 2)) * 2;
+    uint32_t v = 0u;
+    if (r < n) v = *(const uint32_t *)(src + (size_t)r * D + c2);
+    *(uint32_t *)&sk[r * KST + c2] = v;
+  }
+  for (int idx = threadIdx.x; idx < s.G * D; idx += 256) {
+    const int hh = idx / D, c = idx % D;
+    sq[hh][c] = w.qp[((size_t)i * s.Hq + g * s.G + hh) * D + c];
+  }
+  __syncthreads();
+  if (wave < s.G) {
+    const int hq = g * s.G + wave;
+    float acc = 0.0f;
+    const uint16_t *row = &sk[lane * KST];
+#pragma unroll 8
+    for (int c = 0; c < D; c += 2) {
+      const uint32_t kk = *(const uint32_t *)&row[c];
+      acc = fmaf(sq[wave][c], h2f((uint16_t)(kk & 0xffffu)), acc);
+      acc = fmaf(sq[wave][c + 1], h2f((uint16_t)(kk >> 16)), acc);
+    }
+    const bool valid = lane < n;
+    if (valid) w.sp[((size_t)i * s.Hq + hq) * s.Tmax + (size_t)b * BLOCK + lane] = acc;
+    const float mx = bfly_max<64>(valid ? acc : -INFINITY);
+    uint32_t L = valid ? (uint32_t)floorf(0x1p24f * exp2k(acc - mx)) : 0u;
+    L = bfly_sum_u32<64>(L);
+    if (lane == 0) {
+      const size_t o = ((size_t)i * s.Hq + hq) * s.NBmax + b;
+      w.m16[o] = mx;
+      w.L16[o] = L;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) *flag = 0;
+}
+
+hipError_t launch_score_fp16(const Shape &s, const Step &w, const SeqTab &tab, int maxNB,
+                             hipStream_t st) {
+  dim3 grid(maxNB, s.Hkv, tab.n);
+  if (s.d == 128)
+    hipLaunchKernelGGL(k_score_fp16<128>, grid, dim3(256), 0, st, s, w, tab);
+  else
+    hipLaunchKernelGGL(k_score_fp16<64>, grid, dim3(256), 0, st, s, w, tab);
+  return hipGetLastError();
+}
+
+// ---- test hook: the decision exponential on a vector ------------------------------
+__global__ void k_exp2k(const float *x, float *y, int64_t n) {
+  for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < n;
+       idx += (int64_t)gridDim.x * blockDim.x)
+    y[idx] = exp2k(x[idx]);
+}
+hipError_t launch_exp2k(const float *x, float *y, int64_t n, hipStream_t st) {
+  hipLaunchKernelGGL(k_exp2k, dim3(1024), dim3(256), 0, st, x, y, n);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

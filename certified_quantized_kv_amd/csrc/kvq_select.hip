@@ -1,0 +1,167 @@
+// kvq_select.hip -- top-K* coverage selection and promotion planning
+// ("Runtime-Certified Bounded-Error Quantized Attention", Méthodologie §3:
+// the top-K* blocks covering tau_cov of the estimated mass get FP16 keys).
+//
+// Per query head: fixed-point INT8 block weights
+//   What_b = floor(fl32(fl32(Lhat_b) exp2k(fl32(mhat_b - max_b mhat_b))))  (< 2^31)
+// are sorted by (What descending, block index ascending) in LDS (bitonic
+// sort of 64-bit keys What << 32 | ~b), prefix-summed in 64-bit integers, and
+//   K* = min k >= 1 with 10^6 sum_{i<k} What_pi(i) >= tau_ppm sum_b What_b.
+// Integer sums make the result independent of reduction order.
+// Promotion is per KV head: U_g = union of the group's top-K* sets; blocks
+// new to U_g are listed as runs of consecutive blocks for the host copies.
+#include "kvq_device.h"
+#include "kvq_internal.h"
+#include "kvq_blockops.h"
+
+namespace kvq {
+
+constexpr int SEL_NT = 1024;
+
+__global__ __launch_bounds__(SEL_NT) void k_select(Shape s, Step w, SeqTab tab, int tau_ppm) {
+  extern __shared__ unsigned long long keys[];
+  __shared__ float red[SEL_NT / 64];
+  __shared__ unsigned long long part[SEL_NT + 1];
+  const int i = blockIdx.y, hq = blockIdx.x;
+  const int T = tab.T[i], NB = (T + BLOCK - 1) / BLOCK;
+  int n2 = 1;
+  while (n2 < NB) n2 <<= 1;
+  const size_t base = ((size_t)i * s.Hq + hq) * s.NBmax;
+
+  float m = -INFINITY;
+  for (int b = threadIdx.x; b < NB; b += SEL_NT) m = fmaxf(m, w.mhat[base + b]);
+  m = bfly_max<64>(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  float M = red[0];
+  for (int k = 1; k < SEL_NT / 64; ++k) M = fmaxf(M, red[k]);
+
+  for (int b = threadIdx.x; b < n2; b += SEL_NT) {
+    unsigned long long key = 0ull;
+    if (b < NB) {
+      const uint32_t W = (uint32_t)floorf((float)w.Lhat[base + b] * exp2k(w.mhat[base + b] - M));
+      w.What[base + b] = W;
+      key = ((unsigned long long)W << 32) | (unsigned long long)(0xffffffffu - (uint32_t)b);
+    }
+    keys[b] = key;
+  }
+  __syncthreads();
+  bitonic_desc<SEL_NT>(keys, n2);
+
+  // pi, then inclusive prefix sums of the sorted weights (4 per thread)
+  constexpr int PER = MAX_NB / SEL_NT;
+  unsigned long long loc[PER];
+  unsigned long long run = 0ull;
+  for (int k = 0; k < PER; ++k) {
+    const int p = threadIdx.x * PER + k;
+    unsigned long long W = 0ull;
+    if (p < NB) {
+      const unsigned long long key = keys[p];
+      w.pi[base + p] = 0xffffffffu - (uint32_t)(key & 0xffffffffull);
+      W = key >> 32;
+    }
+    run += W;
+    loc[k] = run;
+  }
+  part[threadIdx.x + 1] = run;
+  if (threadIdx.x == 0) part[0] = 0ull;
+  __syncthreads();
+  for (int o = 1; o < SEL_NT; o <<= 1) {           // inclusive scan of part[1..]
+    unsigned long long v = 0ull;
+    if (threadIdx.x >= o) v = part[threadIdx.x + 1 - o];
+    __syncthreads();
+    part[threadIdx.x + 1] += v;
+    __syncthreads();
+  }
+  const unsigned long long total = part[SEL_NT];
+  const unsigned long long need = (unsigned long long)tau_ppm * total;
+  const unsigned long long off = part[threadIdx.x];
+  for (int k = 0; k < PER; ++k) {
+    const int p = threadIdx.x * PER + k;         // K* candidate p + 1
+    if (p >= NB) break;
+    const unsigned long long pre = off + loc[k];
+    const unsigned long long prev = (k == 0) ? off : off + loc[k - 1];
+    const bool ok = 1000000ull * pre >= need;
+    const bool ok_prev = (p == 0) ? false : (1000000ull * prev >= need);
+    if (ok && !ok_prev) {
+      w.k0[(size_t)i * s.Hq + hq] = p + 1;
+      w.ssize[(size_t)i * s.Hq + hq] = p + 1;
+    }
+  }
+}
+
+hipError_t launch_select(const Shape &s, const Step &w, const SeqTab &tab, int tau_ppm, int maxNB,
+                         hipStream_t st) {
+  int n2 = 1;
+  while (n2 < maxNB) n2 <<= 1;
+  hipLaunchKernelGGL(k_select, dim3(s.Hq, tab.n), dim3(SEL_NT), n2 * sizeof(unsigned long long),
+                     st, s, w, tab, tau_ppm);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void k_plan_keys(Shape s, Step w, SeqTab tab) {
+  const int i = blockIdx.y, g = blockIdx.x;
+  const int NB = (tab.T[i] + BLOCK - 1) / BLOCK;
+  plan_group_keys(s, w, i, g, NB);
+}
+
+hipError_t launch_plan_keys(const Shape &s, const Step &w, const SeqTab &tab, int maxNB,
+                            hipStream_t st) {
+  (void)maxNB;
+  hipLaunchKernelGGL(k_plan_keys, dim3(s.Hkv, tab.n), dim3(256), 0, st, s, w, tab);
+  return hipGetLastError();
+}
+
+// Compacts every group's runs into plan[]: plan[0] = #K runs, plan[1] = #V
+// runs, plan[2] = flags (bit0: a group is still widening, bit1: some head is
+// at rung 3), then the K entries followed by the V entries, each
+// len | start << 16 | ig << 32 | kind << 48 with ig = i * Hkv + g.
+__global__ __launch_bounds__(1024) void k_gather_plan(Shape s, Step w, int n) {
+  __shared__ int tmp[17];
+  __shared__ uint32_t s_flags;
+  if (threadIdx.x == 0) s_flags = 0u;
+  __syncthreads();
+  const int G2 = n * s.Hkv;
+  int base = 0, nk = 0;
+  for (int kind = 0; kind < 2; ++kind) {
+    for (int c0 = 0; c0 < G2; c0 += blockDim.x) {
+      const int ig = c0 + threadIdx.x;
+      const int cnt = (ig < G2) ? (int)w.nruns[(size_t)ig * 2 + kind] : 0;
+      int total;
+      const int pos = block_excl_scan(cnt, tmp, total);
+      if (ig < G2) {
+        const uint32_t *runs = w.runs + ((size_t)ig * 2 + kind) * s.runmax;
+        for (int k = 0; k < cnt; ++k) {
+          const uint32_t r = runs[k];
+          w.plan[4 + base + pos + k] = (unsigned long long)(r >> 16) |
+                                       ((unsigned long long)(r & 0xffffu) << 16) |
+                                       ((unsigned long long)ig << 32) |
+                                       ((unsigned long long)kind << 48);
+        }
+        if (kind == 0) {
+          const uint32_t gs = w.gstat[ig];
+          uint32_t f = 0u;
+          if (!(gs & 1u)) f |= 1u;
+          if (gs & 2u) f |= 2u;
+          if (f) atomicOr(&s_flags, f);
+        }
+      }
+      base += total;
+    }
+    if (kind == 0) nk = base;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    w.plan[0] = (unsigned long long)nk;
+    w.plan[1] = (unsigned long long)(base - nk);
+    w.plan[2] = (unsigned long long)s_flags;
+    w.plan[3] = 0ull;
+  }
+}
+
+hipError_t launch_gather_plan(const Shape &s, const Step &w, int n, hipStream_t st) {
+  hipLaunchKernelGGL(k_gather_plan, dim3(1), dim3(1024), 0, st, s, w, n);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

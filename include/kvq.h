@@ -1,0 +1,209 @@
+/*
+ * kvq.h -- C ABI of the certified quantized-KV decode-attention library
+ * (libkvq.so, HIP on AMD Instinct MI355X / gfx950).
+ *
+ * Method: "Runtime-Certified Bounded-Error Quantized Attention" (gist.science
+ * technical summary; French section names are used in citations):
+ *   Méthodologie §1  tier 1 in device memory (INT8 keys per channel, INT4
+ *                    values per group, scale/offset, per-block error
+ *                    annotations); tier 2 = FP16 ground truth in pinned host
+ *                    memory; fallback to exact dense attention per head/layer.
+ *   Méthodologie §2  per-head, per-step bounds E_key (total variation via the
+ *                    per-token score perturbation) and E_val (mass-weighted
+ *                    per-block value error), computed without touching FP16.
+ *   Méthodologie §3  INT8 scoring pass -> per-block mass -> top-K* blocks
+ *                    covering tau_cov promoted to FP16 keys; INT8 vs FP16
+ *                    ranking-consistency check; ladder: widen coverage,
+ *                    promote values, per-head dense, per-layer dense.
+ *
+ * Conventions shared by every call:
+ *   - Pointers marked (device) are HIP device pointers, (host) are host
+ *     pointers.  Arrays are dense, row-major, no padding.
+ *   - fp16 data is IEEE binary16 passed as 16-bit words.
+ *   - Work is ordered on the caller's `stream` (a hipStream_t passed as
+ *     void*; NULL = the null stream).  A call returns once its work is
+ *     enqueued; device outputs are valid after the caller synchronises
+ *     `stream`.  kvq_decode_step synchronises `stream` internally (it reads
+ *     promotion lists and ladder decisions back to issue host->device copies)
+ *     and may block the calling thread for that long.
+ *   - A context is not thread-safe: use it from one host thread at a time.
+ *   - No call throws.  On error the outputs are unspecified; the context
+ *     stays usable unless the status is KVQ_EHIP.  kvq_last_error() gives the
+ *     message of the last failing call on that context.
+ *   - Block size is 64 tokens; value groups are 32 consecutive channels of a
+ *     token.  head_dim must be 64 or 128; n_q_heads / n_kv_heads must be 1,
+ *     2 or 4.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t kvq_status;
+#define KVQ_OK              0
+#define KVQ_EINVAL         -1   /* bad shape, pointer or threshold          */
+#define KVQ_ENOMEM_DEVICE  -2   /* device allocation failed                  */
+#define KVQ_ENOMEM_HOST    -3   /* pinned host allocation failed (tier 2)    */
+#define KVQ_ECAPACITY      -4   /* append past max_tokens                    */
+#define KVQ_ESTATE         -5   /* decode on an empty sequence, bad layer    */
+#define KVQ_EHIP           -6   /* a HIP runtime error (see kvq_last_error)  */
+#define KVQ_ENOTIMPL       -7
+
+#define KVQ_BLOCK_TOKENS   64
+#define KVQ_VALUE_GROUP    32
+#define KVQ_MAX_CALL_SEQS  64   /* sequences per append/decode call          */
+
+/* flags */
+#define KVQ_FLAG_FORCE_DENSE  1u  /* every head at level 4 (exact dense path) */
+#define KVQ_FLAG_TIMING       2u  /* fill kvq_step_stats phase times          */
+
+typedef struct kvq_config {
+    int32_t n_layers;        /* layers held by the context                      */
+    int32_t max_batch;       /* sequence slots 0 .. max_batch-1                 */
+    int32_t n_q_heads;       /* query heads per layer                           */
+    int32_t n_kv_heads;      /* KV heads per layer (query head h uses KV head
+                                h / (n_q_heads / n_kv_heads))                   */
+    int32_t head_dim;        /* 64 or 128                                        */
+    int32_t max_tokens;      /* capacity per (slot, layer)                       */
+    /* thresholds (Méthodologie §3; only tau_cov = 0.995 is the page's example) */
+    int32_t tau_cov_ppm;     /* coverage of estimated block mass, ppm (995000)  */
+    int32_t rho_min_ppm;     /* Spearman threshold of the ranking check (900000)*/
+    int32_t widen_rounds;    /* rounds of rung 1 (2)                             */
+    int32_t layer_frac_ppm;  /* rung 4 when more than this share of a layer's
+                                query heads is at rung 3, ppm (500000)          */
+    double eps_key;          /* E_key tolerance (1e-3)                           */
+    double v_tol;            /* E_val tolerance (0.25)                           */
+    uint32_t flags;          /* KVQ_FLAG_*                                       */
+} kvq_config;
+
+/* Fills cfg with the defaults above for the given shape. */
+void kvq_default_config(kvq_config *cfg, int32_t n_layers, int32_t max_batch,
+                        int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                        int32_t max_tokens);
+
+typedef struct kvq_ctx kvq_ctx;
+
+/* Creates a context on the current HIP device: allocates tier 1 (device),
+ * tier 2 (pinned host, 2 * n_layers * max_batch * n_kv_heads * max_tokens *
+ * head_dim * 2 bytes) and per-step scratch.  *out is set on success only. */
+kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out);
+
+/* Frees everything the context owns (synchronises the device first). */
+void kvq_destroy(kvq_ctx *ctx);
+
+/* Appends tokens to sequences at one layer (Méthodologie §1: quantize into
+ * tier 1, keep the FP16 originals in tier 2).
+ *   seq_ids (host) [n_seqs]   distinct slots in [0, max_batch)
+ *   n_new   (host) [n_seqs]   tokens appended per sequence (>= 0)
+ *   k, v    (device) fp16 [sum(n_new)][n_kv_heads][head_dim], sequence i's
+ *           tokens first in call order (post-RoPE keys).
+ * Re-quantizes the open (partial) last block over its valid tokens, so tier 1
+ * depends only on the token stream.  The caller's k/v may be reused once
+ * `stream` has passed this call.  KVQ_ECAPACITY if a sequence would exceed
+ * max_tokens (nothing is appended then). */
+kvq_status kvq_append(kvq_ctx *ctx, int32_t layer, int32_t n_seqs, const int32_t *seq_ids,
+                      const int32_t *n_new, const void *k, const void *v, void *stream);
+
+typedef struct kvq_step_stats {
+    int64_t promoted_key_blocks;   /* FP16 key blocks copied host->device       */
+    int64_t promoted_value_blocks; /* FP16 value blocks copied (rung 2)          */
+    int64_t dense_kv_heads;        /* KV heads copied whole for rungs 3/4        */
+    int64_t h2d_bytes;             /* bytes copied host->device                  */
+    int32_t key_rounds;            /* evaluation rounds of the controller         */
+    int32_t host_syncs;            /* host round-trips taken                      */
+    int32_t level_count[5];        /* heads per ladder level                      */
+    float ms_score;                /* phase times (KVQ_FLAG_TIMING), milliseconds */
+    float ms_select;
+    float ms_promote;              /* copies + FP16 scoring + controller rounds   */
+    float ms_decode;
+    float ms_total;
+} kvq_step_stats;
+
+/* One decode step at one layer (Méthodologie §2-§3): attends over every
+ * cached token of each sequence (append the step's token first).
+ *   seq_ids (host)   [n_seqs] distinct slots, each with >= 1 token at `layer`
+ *   q       (device) fp16 [n_seqs][n_q_heads][head_dim]
+ *   out     (device) f32  [n_seqs][n_q_heads][head_dim]
+ *   e_key   (device) f32  [n_seqs][n_q_heads]  bound on TV(p_dense, p_used)
+ *   e_val   (device) f32  [n_seqs][n_q_heads]  bound on the value error,
+ *           inf-norm over channels; both 0 for heads at levels 3/4 (exact)
+ *   level   (device) int8 [n_seqs][n_q_heads]  0 = certified as selected,
+ *           1 = coverage widened, 2 = values promoted, 3 = head dense,
+ *           4 = layer dense
+ *   stats   (host, nullable) filled before return.
+ * Softmax scale is 1/sqrt(head_dim).  With value ranges R_v (per KV head,
+ * max over channels of max - min), |out - out_dense|_inf <= R_v * e_key + e_val
+ * for levels 0-2, up to fp32 accumulation. */
+kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n_seqs, const int32_t *seq_ids,
+                           const void *q, float *out, float *e_key, float *e_val, int8_t *level,
+                           kvq_step_stats *stats, void *stream);
+
+/* Forgets every token of a slot at every layer. */
+kvq_status kvq_reset_seq(kvq_ctx *ctx, int32_t seq_id);
+
+/* Tokens currently held by (slot, layer), or a negative status. */
+int64_t kvq_seq_len(const kvq_ctx *ctx, int32_t layer, int32_t seq_id);
+
+const char *kvq_strerror(kvq_status s);
+const char *kvq_last_error(const kvq_ctx *ctx);
+
+/* Device bytes of tier 1 per (token, KV head), and the context's totals. */
+double kvq_tier1_bytes_per_token(int32_t head_dim);
+int64_t kvq_device_bytes(const kvq_ctx *ctx);
+int64_t kvq_host_pinned_bytes(const kvq_ctx *ctx);
+
+/* ---- test and debug exports (parity checks; synchronise the device) ----- */
+
+/* Tier 1 of one (layer, slot, KV head) in plain layouts, written to host_dst
+ * as consecutive arrays (T = current length, NB = ceil(T/64), d = head_dim):
+ *   kcode  u8  [T][d]          vcode  u8  [T][d] (one code per byte)
+ *   kscale u16 [NB][d]         vscale u16 [T][d/32]
+ *   koff   u16 [NB][d]         voff   u16 [T][d/32]
+ *   eta    f32 [NB]            vmin   f32 [d]      vmax f32 [d]
+ * `bytes` must equal kvq_tier1_export_bytes(ctx, layer, seq_id). */
+int64_t kvq_tier1_export_bytes(const kvq_ctx *ctx, int32_t layer, int32_t seq_id);
+kvq_status kvq_export_tier1(kvq_ctx *ctx, int32_t layer, int32_t seq_id, int32_t kv_head,
+                            void *host_dst, size_t bytes);
+
+/* Per-step internals of the last kvq_decode_step for one slot (the arrays of
+ * that call; NB = ceil(T/64) of that step, Hq = n_q_heads, Hkv = n_kv_heads).
+ * `which` selects one array; shapes are [Hq][T] (scores), [Hq][NB] (block
+ * arrays), [Hq] (head arrays), [Hkv][NB] (group block flags). */
+#define KVQ_TR_SHAT      1   /* f32 [Hq][T]   INT8 scores (log2 units)              */
+#define KVQ_TR_SP        2   /* f32 [Hq][T]   FP16 scores, valid on promoted blocks */
+#define KVQ_TR_MHAT      3   /* f32 [Hq][NB]                                         */
+#define KVQ_TR_LHAT      4   /* u32 [Hq][NB]                                         */
+#define KVQ_TR_DELTA     5   /* f32 [Hq][NB]  score-perturbation bound Delta'        */
+#define KVQ_TR_M16       6   /* f32 [Hq][NB]  valid on promoted blocks               */
+#define KVQ_TR_L16       7   /* u32 [Hq][NB]  valid on promoted blocks               */
+#define KVQ_TR_WHAT      8   /* u32 [Hq][NB]  INT8 block weights                     */
+#define KVQ_TR_PI        9   /* u32 [Hq][NB]  blocks by (WHAT desc, index asc)       */
+#define KVQ_TR_WT       10   /* u32 [Hq][NB]  final mixed weights                    */
+#define KVQ_TR_W16      11   /* u32 [Hq][NB]  final FP16 weights over S_h            */
+#define KVQ_TR_K0       12   /* i32 [Hq]      K* of the first round                  */
+#define KVQ_TR_SSIZE    13   /* i32 [Hq]      final |S_h|                            */
+#define KVQ_TR_SSD      14   /* u64 [Hq]      sum of squared rank differences        */
+#define KVQ_TR_EKEY64   15   /* f64 [Hq]      E_key before rounding                  */
+#define KVQ_TR_EVAL64   16   /* f64 [Hq]      E_val before rounding                  */
+#define KVQ_TR_HFLAGS   17   /* u32 [Hq]      bit0 consistent, bit1 widened, bit2
+                                                failed (rung 3), bits 8..15 rounds   */
+#define KVQ_TR_U        18   /* u8 [Hkv][NB]  FP16 keys used (union of S_h)          */
+#define KVQ_TR_V        19   /* u8 [Hkv][NB]  FP16 values used (union of V_h)        */
+#define KVQ_TR_VH       20   /* u8 [Hq][NB]   the head's own value promotions        */
+int64_t kvq_trace_bytes(const kvq_ctx *ctx, int32_t which, int32_t seq_id);
+kvq_status kvq_export_trace(kvq_ctx *ctx, int32_t which, int32_t seq_id, void *host_dst,
+                            size_t bytes);
+
+/* Runs the library's base-2 exponential (the one every decision uses) on n
+ * device floats.  For tests. */
+kvq_status kvq_selftest_exp2k(const float *x, float *y, int64_t n, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVQ_H */
