@@ -38,9 +38,11 @@ class Config(ctypes.Structure):
 class StepStats(ctypes.Structure):
     _fields_ = [("promoted_key_blocks", I64), ("promoted_value_blocks", I64),
                 ("dense_kv_heads", I64), ("h2d_bytes", I64), ("key_rounds", I32),
-                ("host_syncs", I32), ("level_count", I32 * 5), ("ms_score", ctypes.c_float),
-                ("ms_select", ctypes.c_float), ("ms_promote", ctypes.c_float),
-                ("ms_decode", ctypes.c_float), ("ms_total", ctypes.c_float)]
+                ("host_syncs", I32), ("level_count", I32 * 5),
+                ("ms_score_int8", ctypes.c_float), ("ms_select", ctypes.c_float),
+                ("ms_score_fp16", ctypes.c_float), ("ms_control", ctypes.c_float),
+                ("ms_copy", ctypes.c_float), ("ms_decode", ctypes.c_float),
+                ("ms_dense", ctypes.c_float), ("ms_total", ctypes.c_float)]
 
     def as_dict(self):
         d = {k: getattr(self, k) for k, _ in self._fields_}

@@ -38,7 +38,7 @@ struct kvq_ctx {
   std::vector<void *> dallocs;
   hipStream_t cstream = nullptr;
   hipEvent_t ev_start = nullptr, ev_copy = nullptr;
-  hipEvent_t ev_t[6] = {};
+  hipEvent_t ev_t[48] = {};
   unsigned long long *plan_host = nullptr;
   size_t plan_cap = 0;
   size_t plan_words = 0;
@@ -98,6 +98,37 @@ bool valid_seqs(const kvq_ctx *c, int n, const int32_t *ids) {
   }
   return true;
 }
+
+// Kernel timing: pairs of events around a launch, summed per category.
+enum TimeCat { TC_SCORE8, TC_SELECT, TC_SCORE16, TC_CONTROL, TC_COPY, TC_DECODE, TC_DENSE, TC_TOTAL, TC_N };
+struct Timer {
+  kvq_ctx *c;
+  bool on;
+  int used = 0;
+  int cat[24];
+  hipError_t begin(int k, hipStream_t st) {
+    if (!on || used >= 24) return hipSuccess;
+    cat[used] = k;
+    return hipEventRecord(c->ev_t[2 * used], st);
+  }
+  hipError_t end(hipStream_t st) {
+    if (!on || used >= 24) return hipSuccess;
+    hipError_t e = hipEventRecord(c->ev_t[2 * used + 1], st);
+    ++used;
+    return e;
+  }
+  hipError_t collect(float *ms) {
+    for (int k = 0; k < TC_N; ++k) ms[k] = 0.0f;
+    for (int u = 0; u < used; ++u) {
+      float a = 0.0f;
+      hipError_t e = hipEventSynchronize(c->ev_t[2 * u + 1]);
+      if (e == hipSuccess) e = hipEventElapsedTime(&a, c->ev_t[2 * u], c->ev_t[2 * u + 1]);
+      if (e != hipSuccess) return e;
+      ms[cat[u]] += a;
+    }
+    return hipSuccess;
+  }
+};
 
 }  // namespace
 
@@ -196,7 +227,7 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out) {
   else (void)0
   DA(t.kcodes, NU * NBm * BLOCK * d);
   DA(t.kmeta, NU * NBm * d * 4);
-  DA(t.vcodes, NU * Tm * d / 2);
+  DA(t.vcodes, NU * NBm * 32 * d);
   DA(t.vmeta, NU * Tm * (d / VGROUP) * 4);
   DA(t.eta, NU * NBm * 4);
   DA(t.vmin, NU * d * 4);
@@ -413,7 +444,8 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
   const size_t NBm = s.NBmax;
   int64_t h2d = 0, kblk = 0, vblk = 0, dense_heads = 0;
   int syncs = 0, rounds = 0;
-  if (timing) HIPCK(ctx, hipEventRecord(ctx->ev_t[0], st));
+  Timer tm{ctx, timing};
+  if (timing) HIPCK(ctx, hipEventRecord(ctx->ev_t[46], st));
 
   HIPCK(ctx, hipMemsetAsync(w.U, 0, (size_t)n * s.Hkv * NBm, st));
   HIPCK(ctx, hipMemsetAsync(w.Knew, 0, (size_t)n * s.Hkv * NBm, st));
@@ -432,12 +464,14 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
 
   const float C = (float)(1.4426950408889634 / sqrt((double)s.d));
   HIPCK(ctx, launch_qprep(s, w, n, (const uint16_t *)q, C, st));
+  HIPCK(ctx, tm.begin(TC_SCORE8, st));
   HIPCK(ctx, launch_score_int8(s, ctx->t, w, tab, layer, maxNB, st));
-  if (timing) HIPCK(ctx, hipEventRecord(ctx->ev_t[1], st));
+  HIPCK(ctx, tm.end(st));
+  HIPCK(ctx, tm.begin(TC_SELECT, st));
   HIPCK(ctx, launch_select(s, w, tab, ctx->th.tau_ppm, maxNB, st));
   HIPCK(ctx, launch_plan_keys(s, w, tab, maxNB, st));
   HIPCK(ctx, launch_gather_plan(s, w, n, st));
-  if (timing) HIPCK(ctx, hipEventRecord(ctx->ev_t[2], st));
+  HIPCK(ctx, tm.end(st));
   Plan plan;
   kvq_status rs = read_plan(ctx, st, plan);
   if (rs != KVQ_OK) return rs;
@@ -445,15 +479,23 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
   for (int round = 0;; ++round) {
     const bool new_keys = plan.nk > 0;
     if (!plan.ent.empty()) {
+      HIPCK(ctx, tm.begin(TC_COPY, ctx->cstream));
       rs = issue_copies(ctx, tab, layer, plan, h2d, kblk, vblk);
       if (rs != KVQ_OK) return rs;
+      HIPCK(ctx, tm.end(ctx->cstream));
       HIPCK(ctx, hipEventRecord(ctx->ev_copy, ctx->cstream));
       HIPCK(ctx, hipStreamWaitEvent(st, ctx->ev_copy, 0));
     }
     if (round > 0 && !(plan.flags & 1u)) break;      // every group final
     if (round > ctx->th.R1) return fail(ctx, KVQ_EHIP, "controller did not finish its rounds");
-    if (new_keys) HIPCK(ctx, launch_score_fp16(s, w, tab, maxNB, st));
+    if (new_keys) {
+      HIPCK(ctx, tm.begin(TC_SCORE16, st));
+      HIPCK(ctx, launch_score_fp16(s, w, tab, maxNB, st));
+      HIPCK(ctx, tm.end(st));
+    }
+    HIPCK(ctx, tm.begin(TC_CONTROL, st));
     HIPCK(ctx, launch_control(s, ctx->t, w, tab, layer, ctx->th, round, maxNB, st));
+    HIPCK(ctx, tm.end(st));
     HIPCK(ctx, launch_gather_plan(s, w, n, st));
     rs = read_plan(ctx, st, plan);
     if (rs != KVQ_OK) return rs;
@@ -478,22 +520,27 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
         const size_t u = unit_of(s, tab.slot[i], layer, g);
         const size_t ig = (size_t)i * s.Hkv + g;
         const size_t bytes = (size_t)((tab.T[i] + BLOCK - 1) / BLOCK) * BLOCK * s.d * 2;
+        HIPCK(ctx, tm.begin(TC_COPY, ctx->cstream));
         HIPCK(ctx, hipMemcpyAsync(w.stage_k + ig * s.Tmax * s.d, ctx->t2k_host + u * s.Tmax * s.d,
                                   bytes, hipMemcpyHostToDevice, ctx->cstream));
         HIPCK(ctx, hipMemcpyAsync(w.stage_v + ig * s.Tmax * s.d, ctx->t2v_host + u * s.Tmax * s.d,
                                   bytes, hipMemcpyHostToDevice, ctx->cstream));
+        HIPCK(ctx, tm.end(ctx->cstream));
         h2d += 2 * (int64_t)bytes;
       }
     if (any) {
       HIPCK(ctx, hipEventRecord(ctx->ev_copy, ctx->cstream));
       HIPCK(ctx, hipStreamWaitEvent(st, ctx->ev_copy, 0));
+      HIPCK(ctx, tm.begin(TC_DENSE, st));
       HIPCK(ctx, launch_decode(s, ctx->t, w, tab, layer, maxNB, true, st));
+      HIPCK(ctx, tm.end(st));
     }
   }
-  if (timing) HIPCK(ctx, hipEventRecord(ctx->ev_t[3], st));
+  HIPCK(ctx, tm.begin(TC_DECODE, st));
   HIPCK(ctx, launch_decode(s, ctx->t, w, tab, layer, maxNB, false, st));
   HIPCK(ctx, launch_combine(s, w, tab, out, st));
-  if (timing) HIPCK(ctx, hipEventRecord(ctx->ev_t[4], st));
+  HIPCK(ctx, tm.end(st));
+  if (timing) HIPCK(ctx, hipEventRecord(ctx->ev_t[47], st));
 
   ctx->last_n = n;
   ctx->last_layer = layer;
@@ -515,16 +562,18 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
     for (int8_t x : lv)
       if (x >= 0 && x <= 4) stats->level_count[(int)x]++;
     if (timing) {
-      float a = 0;
-      HIPCK(ctx, hipEventElapsedTime(&a, ctx->ev_t[0], ctx->ev_t[1]));
-      stats->ms_score = a;
-      HIPCK(ctx, hipEventElapsedTime(&a, ctx->ev_t[1], ctx->ev_t[2]));
-      stats->ms_select = a;
-      HIPCK(ctx, hipEventElapsedTime(&a, ctx->ev_t[2], ctx->ev_t[3]));
-      stats->ms_promote = a;
-      HIPCK(ctx, hipEventElapsedTime(&a, ctx->ev_t[3], ctx->ev_t[4]));
-      stats->ms_decode = a;
-      HIPCK(ctx, hipEventElapsedTime(&a, ctx->ev_t[0], ctx->ev_t[4]));
+      float ms[TC_N];
+      HIPCK(ctx, tm.collect(ms));
+      stats->ms_score_int8 = ms[TC_SCORE8];
+      stats->ms_select = ms[TC_SELECT];
+      stats->ms_score_fp16 = ms[TC_SCORE16];
+      stats->ms_control = ms[TC_CONTROL];
+      stats->ms_copy = ms[TC_COPY];
+      stats->ms_decode = ms[TC_DECODE];
+      stats->ms_dense = ms[TC_DENSE];
+      float a = 0.0f;
+      HIPCK(ctx, hipEventSynchronize(ctx->ev_t[47]));
+      HIPCK(ctx, hipEventElapsedTime(&a, ctx->ev_t[46], ctx->ev_t[47]));
       stats->ms_total = a;
     }
   }

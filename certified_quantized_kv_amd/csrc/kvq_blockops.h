@@ -41,22 +41,33 @@ __device__ inline int block_excl_scan(int v, int *tmp, int &total) {
 }
 
 // Runs of consecutive set flags (flags[0..NB)) -> runs[k] = start | len << 16.
+// Starts and (exclusive) ends are compacted separately, in increasing order,
+// so the k-th start pairs with the k-th end; the two halves of runs[k] are
+// written by different threads, then joined.
 __device__ inline int build_runs(const uint8_t *flags, int NB, uint32_t *runs, int *tmp) {
-  int base = 0;
+  uint16_t *half = reinterpret_cast<uint16_t *>(runs);
+  int base_s = 0, base_e = 0;
   for (int c0 = 0; c0 < NB; c0 += blockDim.x) {
     const int b = c0 + threadIdx.x;
     const bool on = b < NB && flags[b];
     const bool start = on && (b == 0 || !flags[b - 1]);
-    int total;
-    const int pos = block_excl_scan(start ? 1 : 0, tmp, total);
-    if (start) {
-      int e = b + 1;
-      while (e < NB && flags[e]) ++e;
-      runs[base + pos] = (uint32_t)b | ((uint32_t)(e - b) << 16);
-    }
-    base += total;
+    const bool end = on && (b == NB - 1 || !flags[b + 1]);
+    int ts, te;
+    const int ps = block_excl_scan(start ? 1 : 0, tmp, ts);
+    const int pe = block_excl_scan(end ? 1 : 0, tmp, te);
+    if (start) half[2 * (base_s + ps)] = (uint16_t)b;
+    if (end) half[2 * (base_e + pe) + 1] = (uint16_t)(b + 1);
+    base_s += ts;
+    base_e += te;
   }
-  return base;
+  __syncthreads();
+  for (int k = threadIdx.x; k < base_s; k += blockDim.x) {
+    const uint32_t r = runs[k];
+    const uint32_t st = r & 0xffffu, en = r >> 16;
+    runs[k] = st | ((en - st) << 16);
+  }
+  __syncthreads();
+  return base_s;
 }
 
 template <int NT>

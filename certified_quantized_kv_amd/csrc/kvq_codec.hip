@@ -40,6 +40,7 @@ __global__ __launch_bounds__(256) void k_append(Shape s, Tier1 t, AppendArgs a,
   __shared__ __align__(16) uint16_t kb[BLOCK][D];
   __shared__ __align__(16) uint16_t vb[BLOCK][D];
   __shared__ __align__(16) uint8_t cb[BLOCK][D];
+  __shared__ __align__(16) uint8_t cv[BLOCK][D];
   __shared__ uint32_t s_err;
   if (tid == 0) s_err = 0u;
 
@@ -110,7 +111,6 @@ __global__ __launch_bounds__(256) void k_append(Shape s, Tier1 t, AppendArgs a,
     const uint16_t sh = (rng > 0.0f) ? ru16(rng / 15.0f) : (uint16_t)0;
     const uint16_t oh = f2h(lo + 0.0f);
     const float sf = h2f(sh), of = h2f(oh);
-    uint32_t packed[4] = {0u, 0u, 0u, 0u};
     for (int x = 0; x < VGROUP; ++x) {
       const float y = h2f(gv[x]);
       float qv = 0.0f;
@@ -118,13 +118,11 @@ __global__ __launch_bounds__(256) void k_append(Shape s, Tier1 t, AppendArgs a,
         qv = rintf((y - of) / sf);
         qv = fminf(fmaxf(qv, 0.0f), 15.0f);
       }
-      packed[x / 8] |= (uint32_t)qv << (4 * (x % 8));
+      cv[r][jg * VGROUP + x] = (uint8_t)qv;
       const float err = fabsf(y - fmaf(sf, qv, of));
       myerr = fmaxf(myerr, err);
     }
     const size_t row = u * s.Tmax + t0 + r;
-    *(uint4 *)(t.vcodes + row * (D / 2) + jg * (VGROUP / 2)) =
-        make_uint4(packed[0], packed[1], packed[2], packed[3]);
     t.vmeta[row * NG + jg] = (uint32_t)sh | ((uint32_t)oh << 16);
   }
   if (myerr > 0.0f) atomicMax(&s_err, __float_as_uint(myerr));
@@ -136,6 +134,26 @@ __global__ __launch_bounds__(256) void k_append(Shape s, Tier1 t, AppendArgs a,
     const int ks = q / 256, nt = (q / 64) % 4, l = q % 64;
     const int r = nt * 16 + (l % 16), c0 = ks * 64 + 16 * (l / 16);
     *(uint4 *)(kdst + (size_t)q * 16) = *(const uint4 *)&cb[r][c0];
+  }
+  // ---- value codes in MFMA operand order (old rows' nibbles kept) --------------
+  uint32_t *vdst = (uint32_t *)(t.vcodes + (u * s.NBmax + b) * (size_t)(32 * D));
+  for (int q = tid; q < 8 * D; q += 256) {
+    const int nt = q >> 7, l = (q >> 1) & 63, qq = q & 1;
+    const int c = nt * 16 + (l & 15), rb = 16 * (l >> 4) + 8 * qq;
+    const uint32_t old = (r_new > 0) ? vdst[q] : 0u;
+    uint32_t word = 0u;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi) {
+        const int r = rb + 4 * hi + m, sh = 8 * m + 4 * hi;
+        uint32_t nib = 0u;
+        if (r < r_new) nib = (old >> sh) & 15u;
+        else if (r < n) nib = cv[r][c];
+        word |= nib << sh;
+      }
+    }
+    vdst[q] = word;
   }
   // ---- tier 2 (new rows) and the open block's FP16 keys ------------------------
   for (int idx = tid; idx < (n - r_new) * (D / 8); idx += 256) {
@@ -186,8 +204,10 @@ __global__ void k_export_vcodes(Shape s, Tier1 t, size_t u, int T, uint8_t *dst)
   for (size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x; idx < total;
        idx += (size_t)gridDim.x * blockDim.x) {
     const int tok = (int)(idx / d), c = (int)(idx % d);
-    const uint8_t byte = t.vcodes[(u * s.Tmax + tok) * (size_t)(d / 2) + c / 2];
-    dst[idx] = (c & 1) ? (byte >> 4) : (byte & 15);
+    int byte, shift;
+    vnib(tok % BLOCK, c, byte, shift);
+    const uint8_t v = t.vcodes[(u * s.NBmax + tok / BLOCK) * (size_t)(32 * d) + byte];
+    dst[idx] = (v >> shift) & 15;
   }
 }
 

@@ -19,28 +19,15 @@
 
 namespace kvq {
 
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// Scores of a chunk -> per-head p = 2^(x - M_h) in LDS, M_h and l_h = sum p.
 template <int D, bool DENSE>
-__global__ __launch_bounds__(256) void k_decode(Shape s, Tier1 t, Step w, SeqTab tab, int layer) {
-  constexpr int CT = DEC_CB * BLOCK;              // tokens per chunk
-  constexpr int CPL = D / 64;                     // channels per lane
-  const int i = blockIdx.z, g = blockIdx.y, ch = blockIdx.x;
-  const int T = tab.T[i], NB = (T + BLOCK - 1) / BLOCK;
-  const int b0 = ch * DEC_CB;
-  if (b0 >= NB) return;
-  const size_t ig = (size_t)i * s.Hkv + g;
-  if (DENSE && !w.gdense[ig]) return;
+__device__ __forceinline__ void chunk_softmax(const Shape &s, const Step &w, int i, int g, size_t ig,
+                                              int t0, int nt, const uint8_t *U, float (*ps)[DEC_CB * BLOCK],
+                                              float *sM, float *sL) {
   const int G = s.G;
-  const int t0 = b0 * BLOCK, nt = min(T, (b0 + DEC_CB) * BLOCK) - t0;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const size_t u = unit_of(s, tab.slot[i], layer, g);
-  const uint8_t *U = w.U + ig * s.NBmax;
-  const uint8_t *V = w.V + ig * s.NBmax;
-
-  __shared__ float ps[4][CT];
-  __shared__ float red[4][4][D];
-  __shared__ float sM[4], sL[4];
-
-  // ---- scores ------------------------------------------------------------------
   for (int idx = threadIdx.x; idx < G * nt; idx += 256) {
     const int h = idx / nt, tt = idx % nt;
     const int tok = t0 + tt;
@@ -76,8 +63,26 @@ __global__ __launch_bounds__(256) void k_decode(Shape s, Tier1 t, Step w, SeqTab
     }
   }
   __syncthreads();
+}
 
-  // ---- P.V ---------------------------------------------------------------------
+// Dense fallback: FP16 keys and values throughout (VALU).
+template <int D>
+__global__ __launch_bounds__(256) void k_decode_dense(Shape s, Tier1 t, Step w, SeqTab tab, int layer) {
+  constexpr int CT = DEC_CB * BLOCK;
+  constexpr int CPL = D / 64;
+  const int i = blockIdx.z, g = blockIdx.y, ch = blockIdx.x;
+  const int T = tab.T[i], NB = (T + BLOCK - 1) / BLOCK;
+  const int b0 = ch * DEC_CB;
+  if (b0 >= NB) return;
+  const size_t ig = (size_t)i * s.Hkv + g;
+  if (!w.gdense[ig]) return;
+  const int G = s.G;
+  const int t0 = b0 * BLOCK, nt = min(T, (b0 + DEC_CB) * BLOCK) - t0;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __shared__ float ps[4][CT];
+  __shared__ float red[4][4][D];
+  __shared__ float sM[4], sL[4];
+  chunk_softmax<D, true>(s, w, i, g, ig, t0, nt, w.U + ig * s.NBmax, ps, sM, sL);
   float o[4][CPL];
 #pragma unroll
   for (int h = 0; h < 4; ++h)
@@ -86,45 +91,31 @@ __global__ __launch_bounds__(256) void k_decode(Shape s, Tier1 t, Step w, SeqTab
   const int per = (nt + 3) / 4;
   const int ta = wave * per, tb = min(nt, ta + per);
   const uint16_t *sv = w.stage_v + ig * s.Tmax * D;
+#pragma unroll 4
   for (int tt = ta; tt < tb; ++tt) {
     const int tok = t0 + tt;
     float v[CPL];
-    if (DENSE || V[tok / BLOCK]) {
-      if (CPL == 2) {
-        const uint32_t pr = *(const uint32_t *)(sv + (size_t)tok * D + 2 * lane);
-        v[0] = h2f((uint16_t)(pr & 0xffffu));
-        v[CPL - 1] = h2f((uint16_t)(pr >> 16));
-      } else {
-        v[0] = h2f(sv[(size_t)tok * D + lane]);
-      }
+    if (CPL == 2) {
+      const uint32_t pr = *(const uint32_t *)(sv + (size_t)tok * D + 2 * lane);
+      v[0] = h2f((uint16_t)(pr & 0xffffu));
+      v[CPL - 1] = h2f((uint16_t)(pr >> 16));
     } else {
-      const size_t row = u * s.Tmax + tok;
-      const int c0 = CPL * lane;
-      const uint32_t meta = t.vmeta[row * (D / VGROUP) + c0 / VGROUP];
-      const float sc = h2f((uint16_t)(meta & 0xffffu)), of = h2f((uint16_t)(meta >> 16));
-      const uint8_t byte = t.vcodes[row * (D / 2) + c0 / 2];
-      if (CPL == 2) {
-        v[0] = fmaf(sc, (float)(byte & 15), of);
-        v[CPL - 1] = fmaf(sc, (float)(byte >> 4), of);
-      } else {
-        v[0] = fmaf(sc, (float)((lane & 1) ? (byte >> 4) : (byte & 15)), of);
-      }
+      v[0] = h2f(sv[(size_t)tok * D + lane]);
     }
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
+    for (int h = 0; h < 4; ++h)
       if (h < G) {
         const float p = ps[h][tt];
 #pragma unroll
         for (int k = 0; k < CPL; ++k) o[h][k] = fmaf(p, v[k], o[h][k]);
       }
-    }
   }
 #pragma unroll
   for (int h = 0; h < 4; ++h)
 #pragma unroll
     for (int k = 0; k < CPL; ++k) red[wave][h][CPL * lane + k] = o[h][k];
   __syncthreads();
-  float *part = (DENSE ? w.partd : w.part) + ((ig * s.nchmax + ch) * G) * (size_t)(D + 2);
+  float *part = w.partd + ((ig * s.nchmax + ch) * G) * (size_t)(D + 2);
   for (int idx = threadIdx.x; idx < G * D; idx += 256) {
     const int h = idx / D, c = idx % D;
     part[(size_t)h * (D + 2) + c] = red[0][h][c] + red[1][h][c] + red[2][h][c] + red[3][h][c];
@@ -135,46 +126,188 @@ __global__ __launch_bounds__(256) void k_decode(Shape s, Tier1 t, Step w, SeqTab
   }
 }
 
+// Mixed decode.  Per block, sum_t p_ht v_tc with v = off_tj + s_tj code_tc
+// splits into sum_t p_ht off_tj (VALU, per group) and the contraction
+// sum_t (p_ht s_tj) code_tc on the matrix cores: A = fixed-point p*s as four
+// unsigned 7-bit limbs (rows: head x limb, k: 64 tokens), B = the INT4 codes
+// (k: tokens, n: 16 channels), one v_mfma_i32_16x16x64_i8 per 16 channels.
+// Wave w owns the channel tiles of one value group, so A is built by the
+// wave that uses it (p*s < 2^(e + 28), e from the block's largest scale).
+template <int D>
+__global__ __launch_bounds__(256) void k_decode_mixed(Shape s, Tier1 t, Step w, SeqTab tab, int layer) {
+  constexpr int CT = DEC_CB * BLOCK;
+  constexpr int NTW = D / 64;                    // 16-channel tiles per wave
+  constexpr int AST = 80;                        // LDS row stride of A (bank spread)
+  const int i = blockIdx.z, g = blockIdx.y, ch = blockIdx.x;
+  const int T = tab.T[i], NB = (T + BLOCK - 1) / BLOCK;
+  const int b0 = ch * DEC_CB;
+  if (b0 >= NB) return;
+  const size_t ig = (size_t)i * s.Hkv + g;
+  const int G = s.G;
+  const int t0 = b0 * BLOCK, nt = min(T, (b0 + DEC_CB) * BLOCK) - t0;
+  const int b1 = (t0 + nt + BLOCK - 1) / BLOCK;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int hl = lane >> 4;                      // head of this lane in the MFMA output
+  const int j = (wave * NTW * 16) / VGROUP;      // value group of this wave's tiles
+  const size_t u = unit_of(s, tab.slot[i], layer, g);
+  const uint8_t *U = w.U + ig * s.NBmax;
+  const uint8_t *V = w.V + ig * s.NBmax;
+
+  __shared__ float ps[4][CT];
+  __shared__ __align__(16) int8_t As[4][16 * AST];
+  __shared__ float sM[4], sL[4];
+  chunk_softmax<D, false>(s, w, i, g, ig, t0, nt, U, ps, sM, sL);
+
+  float acc[NTW];
+#pragma unroll
+  for (int k = 0; k < NTW; ++k) acc[k] = 0.0f;
+  float offacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  const uint16_t *sv = w.stage_v + ig * s.Tmax * D;
+  int8_t *Aw = As[wave];
+
+  for (int b = b0; b < b1; ++b) {
+    const int tb = (b - b0) * BLOCK;             // chunk-local index of the block's row 0
+    if (V[b]) {
+      // FP16 values of a promoted block (rung 2): plain fp32 accumulation
+      const int n = min(BLOCK, T - b * BLOCK);
+#pragma unroll 4
+      for (int r = 0; r < n; ++r) {
+        const float p = (hl < G) ? ps[hl][tb + r] : 0.0f;
+#pragma unroll
+        for (int k = 0; k < NTW; ++k) {
+          const int c = (wave * NTW + k) * 16 + (lane & 15);
+          acc[k] = fmaf(p, h2f(sv[((size_t)b * BLOCK + r) * D + c]), acc[k]);
+        }
+      }
+      continue;
+    }
+    const int tok = b * BLOCK + lane;
+    const bool valid = tok < T;
+    float sc = 0.0f, of = 0.0f;
+    if (valid) {
+      const uint32_t meta = t.vmeta[(u * s.Tmax + tok) * (D / VGROUP) + j];
+      sc = h2f((uint16_t)(meta & 0xffffu));
+      of = h2f((uint16_t)(meta >> 16));
+    }
+    const float smax = bfly_max<64>(sc);
+    const int e = (smax > 0.0f) ? ilogb_f(smax) - 27 : 0;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const float p = (valid && h < G) ? ps[h][tb + lane] : 0.0f;
+      offacc[h] = fmaf(p, of, offacc[h]);
+      const uint32_t A = (uint32_t)rintf(ldexpf(p * sc, -e));
+      Aw[(h * 4 + 0) * AST + lane] = (int8_t)(A & 127u);
+      Aw[(h * 4 + 1) * AST + lane] = (int8_t)((A >> 7) & 127u);
+      Aw[(h * 4 + 2) * AST + lane] = (int8_t)((A >> 14) & 127u);
+      Aw[(h * 4 + 3) * AST + lane] = (int8_t)((A >> 21) & 127u);
+    }
+    wave_lds_sync();
+    const v4i Aop = *(const v4i *)&Aw[(lane & 15) * AST + 16 * (lane >> 4)];
+    const uint8_t *vc = t.vcodes + (u * s.NBmax + b) * (size_t)(32 * D);
+    const float f0 = ldexpf(1.0f, e), f1 = ldexpf(1.0f, e + 7), f2 = ldexpf(1.0f, e + 14),
+                f3 = ldexpf(1.0f, e + 21);
+#pragma unroll
+    for (int k = 0; k < NTW; ++k) {
+      const int ntile = wave * NTW + k;
+      const uint2 pk = *(const uint2 *)(vc + (size_t)(ntile * 64 + lane) * 8);
+      v4i Bop;
+      Bop[0] = (int)(pk.x & 0x0f0f0f0fu);
+      Bop[1] = (int)((pk.x >> 4) & 0x0f0f0f0fu);
+      Bop[2] = (int)(pk.y & 0x0f0f0f0fu);
+      Bop[3] = (int)((pk.y >> 4) & 0x0f0f0f0fu);
+      const v4i Dm = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aop, Bop, (v4i){0, 0, 0, 0}, 0, 0, 0);
+      float a = acc[k];
+      a = fmaf((float)Dm[0], f0, a);
+      a = fmaf((float)Dm[1], f1, a);
+      a = fmaf((float)Dm[2], f2, a);
+      a = fmaf((float)Dm[3], f3, a);
+      acc[k] = a;
+    }
+    wave_lds_sync();
+  }
+  // offset term of this wave's group, per head
+  float offh = 0.0f;
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const float sh = bfly_sum<64>(offacc[h]);
+    if (h == hl) offh = sh;
+  }
+  if (hl < G) {
+    float *part = w.part + ((ig * s.nchmax + ch) * G + hl) * (size_t)(D + 2);
+#pragma unroll
+    for (int k = 0; k < NTW; ++k) part[(wave * NTW + k) * 16 + (lane & 15)] = acc[k] + offh;
+    if ((lane & 15) == 0 && wave == 0) {
+      part[D] = sM[hl];
+      part[D + 1] = sL[hl];
+    }
+  }
+}
+
 hipError_t launch_decode(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,
                          int layer, int maxNB, bool dense, hipStream_t st) {
   dim3 grid((maxNB + DEC_CB - 1) / DEC_CB, s.Hkv, tab.n);
   if (s.d == 128) {
     if (dense)
-      hipLaunchKernelGGL((k_decode<128, true>), grid, dim3(256), 0, st, s, t, w, tab, layer);
+      hipLaunchKernelGGL(k_decode_dense<128>, grid, dim3(256), 0, st, s, t, w, tab, layer);
     else
-      hipLaunchKernelGGL((k_decode<128, false>), grid, dim3(256), 0, st, s, t, w, tab, layer);
+      hipLaunchKernelGGL(k_decode_mixed<128>, grid, dim3(256), 0, st, s, t, w, tab, layer);
   } else {
     if (dense)
-      hipLaunchKernelGGL((k_decode<64, true>), grid, dim3(256), 0, st, s, t, w, tab, layer);
+      hipLaunchKernelGGL(k_decode_dense<64>, grid, dim3(256), 0, st, s, t, w, tab, layer);
     else
-      hipLaunchKernelGGL((k_decode<64, false>), grid, dim3(256), 0, st, s, t, w, tab, layer);
+      hipLaunchKernelGGL(k_decode_mixed<64>, grid, dim3(256), 0, st, s, t, w, tab, layer);
   }
   return hipGetLastError();
 }
 
 // Merges the chunk partials of each (sequence, query head): levels 3/4 read
-// the dense partials, the others the mixed ones.
-__global__ void k_combine(Shape s, Step w, SeqTab tab, float *out) {
-  const int i = blockIdx.y, hq = blockIdx.x, c = threadIdx.x;
+// the dense partials, the others the mixed ones.  256 threads: the chunk
+// maxima and weights first, then 256/d groups of channels-threads each sum a
+// share of the chunks; the shares are added in LDS.
+__global__ __launch_bounds__(256) void k_combine(Shape s, Step w, SeqTab tab, float *out) {
+  __shared__ float fw[1024];
+  __shared__ float red[256];
+  __shared__ float sMl[2];
+  const int i = blockIdx.y, hq = blockIdx.x;
   const int D = s.d, G = s.G, g = hq / G, h = hq % G;
   const int NB = (tab.T[i] + BLOCK - 1) / BLOCK, nch = (NB + DEC_CB - 1) / DEC_CB;
   const bool dense = w.hlevel[(size_t)i * s.Hq + hq] >= 3;
   const float *part = (dense ? w.partd : w.part) + (((size_t)i * s.Hkv + g) * s.nchmax * G + h) * (D + 2);
   const size_t stride = (size_t)G * (D + 2);
-  float M = -INFINITY;
-  for (int k = 0; k < nch; ++k) M = fmaxf(M, part[k * stride + D]);
-  float l = 0.0f, acc = 0.0f;
-  for (int k = 0; k < nch; ++k) {
+  float m = -INFINITY;
+  for (int k = threadIdx.x; k < nch; k += 256) m = fmaxf(m, part[k * stride + D]);
+  m = bfly_max<64>(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float l = 0.0f;
+  for (int k = threadIdx.x; k < nch; k += 256) {
     const float f = exp2f(part[k * stride + D] - M);
+    fw[k] = f;
     l = fmaf(part[k * stride + D + 1], f, l);
-    if (c < D) acc = fmaf(part[k * stride + c], f, acc);
   }
-  if (c < D) out[((size_t)i * s.Hq + hq) * D + c] = acc / l;
+  l = bfly_sum<64>(l);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = l;
+  __syncthreads();
+  if (threadIdx.x == 0) sMl[0] = red[0] + red[1] + red[2] + red[3];
+  __syncthreads();
+  const int parts = 256 / D, c = threadIdx.x % D, pp = threadIdx.x / D;
+  float acc = 0.0f;
+#pragma unroll 4
+  for (int k = pp; k < nch; k += parts) acc = fmaf(part[k * stride + c], fw[k], acc);
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  if (threadIdx.x < D) {
+    float sum = 0.0f;
+    for (int q = 0; q < parts; ++q) sum += red[q * D + threadIdx.x];
+    out[((size_t)i * s.Hq + hq) * D + threadIdx.x] = sum / sMl[0];
+  }
 }
 
 hipError_t launch_combine(const Shape &s, const Step &w, const SeqTab &tab, float *out,
                           hipStream_t st) {
-  hipLaunchKernelGGL(k_combine, dim3(s.Hq, tab.n), dim3(s.d), 0, st, s, w, tab, out);
+  hipLaunchKernelGGL(k_combine, dim3(s.Hq, tab.n), dim3(256), 0, st, s, w, tab, out);
   return hipGetLastError();
 }
 

@@ -94,4 +94,11 @@ __device__ __forceinline__ uint32_t bfly_sum_u32(uint32_t v) {
   return v;
 }
 
+// Wave-level LDS hand-off between lanes of one wave.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
 }  // namespace kvq

@@ -21,7 +21,11 @@ constexpr int DEC_CB = 16;          // blocks per split-K chunk of the decode ke
 //                             ((ks*4 + nt)*64 + l)*16 are the codes of token
 //                             nt*16 + l%16, channels ks*64 + 16*(l/16) + 0..15
 //   kmeta  [NBmax][d]    u32  binary16 scale (low half), offset (high half)
-//   vcodes [Tmax][d/2]   u8   channel 2c in the low nibble, 2c+1 in the high
+//   vcodes [NBmax][32*d] u8   block-local MFMA operand order: for 16-channel
+//                             tile nt and lane l, 8 bytes at (nt*64 + l)*8 hold
+//                             the codes of channel nt*16 + l%16 for tokens
+//                             16*(l/16) + p, p = 0..15: byte 4*(p/8) + p%4,
+//                             high nibble when (p/4) is odd (see vnib())
 //   vmeta  [Tmax][d/32]  u32  binary16 scale (low), offset (high) per group
 //   eta    [NBmax]       f32  per-block value error annotation
 //   vmin/vmax [d]        u32  order-mapped floats, running over all tokens
@@ -79,6 +83,15 @@ struct Thresh {
 // Layout helpers (host and device).
 __host__ __device__ inline size_t unit_of(const Shape &s, int slot, int layer, int g) {
   return ((size_t)slot * s.L + layer) * s.Hkv + g;
+}
+
+// Byte (within a block's value codes) and nibble shift of (row r, channel c).
+// Unpacking a lane's 8 bytes as (x & 0x0f0f0f0f), (x >> 4) & 0x0f0f0f0f per
+// dword yields its 16 tokens in order.
+__host__ __device__ inline void vnib(int r, int c, int &byte, int &shift) {
+  const int nt = c >> 4, l = (c & 15) + 16 * (r >> 4), p = r & 15;
+  byte = (nt * 64 + l) * 8 + (p >> 3) * 4 + (p & 3);
+  shift = ((p >> 2) & 1) * 4;
 }
 
 // ---- launchers (each in its own .hip file) ---------------------------------

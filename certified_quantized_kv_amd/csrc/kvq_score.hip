@@ -50,13 +50,6 @@ hipError_t launch_qprep(const Shape &s, const Step &w, int n, const uint16_t *q,
   return hipGetLastError();
 }
 
-// Wave-level LDS hand-off between lanes of one wave.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-}
-
 constexpr int S8_BLOCKS_PER_WG = 16;   // 4 waves x 4 blocks
 
 template <int D>

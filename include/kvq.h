@@ -117,11 +117,16 @@ typedef struct kvq_step_stats {
     int32_t key_rounds;            /* evaluation rounds of the controller         */
     int32_t host_syncs;            /* host round-trips taken                      */
     int32_t level_count[5];        /* heads per ladder level                      */
-    float ms_score;                /* phase times (KVQ_FLAG_TIMING), milliseconds */
-    float ms_select;
-    float ms_promote;              /* copies + FP16 scoring + controller rounds   */
-    float ms_decode;
-    float ms_total;
+    /* kernel times (KVQ_FLAG_TIMING), milliseconds, from HIP events recorded
+       around each launch on the stream it runs on */
+    float ms_score_int8;           /* INT8 scoring pass                           */
+    float ms_select;               /* top-K* selection and promotion planning     */
+    float ms_score_fp16;           /* FP16 scoring of promoted blocks (all rounds)*/
+    float ms_control;              /* controller rounds                           */
+    float ms_copy;                 /* host->device copies (copy stream)           */
+    float ms_decode;               /* mixed split-K decode + combine              */
+    float ms_dense;                /* dense fallback decode                       */
+    float ms_total;                /* whole call, first launch to last            */
 } kvq_step_stats;
 
 /* One decode step at one layer (Méthodologie §2-§3): attends over every
