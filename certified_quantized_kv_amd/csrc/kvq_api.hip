@@ -256,7 +256,6 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out) {
   DA(w.U, B * Hkv * NBm);
   DA(w.Knew, B * Hkv * NBm);
   DA(w.V, B * Hkv * NBm);
-  DA(w.Vnew, B * Hkv * NBm);
   DA(w.gstat, B * Hkv * 4);
   DA(w.runs, B * Hkv * 2 * (size_t)s.runmax * 4);
   DA(w.nruns, B * Hkv * 2 * 4);
@@ -447,16 +446,7 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
   Timer tm{ctx, timing};
   if (timing) HIPCK(ctx, hipEventRecord(ctx->ev_t[46], st));
 
-  HIPCK(ctx, hipMemsetAsync(w.U, 0, (size_t)n * s.Hkv * NBm, st));
-  HIPCK(ctx, hipMemsetAsync(w.Knew, 0, (size_t)n * s.Hkv * NBm, st));
-  HIPCK(ctx, hipMemsetAsync(w.V, 0, (size_t)n * s.Hkv * NBm, st));
-  HIPCK(ctx, hipMemsetAsync(w.Vnew, 0, (size_t)n * s.Hkv * NBm, st));
-  HIPCK(ctx, hipMemsetAsync(w.vh, 0, (size_t)n * s.Hq * NBm, st));
-  HIPCK(ctx, hipMemsetAsync(w.gstat, 0, (size_t)n * s.Hkv * 4, st));
-  HIPCK(ctx, hipMemsetAsync(w.hflags, 0, (size_t)n * s.Hq * 4, st));
-  HIPCK(ctx, hipMemsetAsync(w.nruns, 0, (size_t)n * s.Hkv * 2 * 4, st));
-  HIPCK(ctx, hipMemsetAsync(w.ekey64, 0, (size_t)n * s.Hq * 8, st));
-  HIPCK(ctx, hipMemsetAsync(w.eval64, 0, (size_t)n * s.Hq * 8, st));
+  HIPCK(ctx, launch_reset(s, w, n, st));
   // staging may still be read by the previous step's kernels, and tier 2 was
   // written by earlier appends on this stream: copies wait for both
   HIPCK(ctx, hipEventRecord(ctx->ev_start, st));

@@ -84,6 +84,30 @@ __device__ int block_min_i32(int v, int *buf) {
   return r;
 }
 
+// Sums 8 u64 values per thread over the workgroup (result in every thread).
+__device__ void block_sum_u64_8(unsigned long long (&v)[8], CtlShared &sh) {
+  __shared__ unsigned long long buf[CTL_NT / 64][8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    unsigned long long x = v[k];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+    v[k] = x;
+  }
+  if ((threadIdx.x & 63) == 0)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) buf[threadIdx.x >> 6][k] = v[k];
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    unsigned long long r = 0ull;
+    for (int q = 0; q < CTL_NT / 64; ++q) r += buf[q][k];
+    v[k] = r;
+  }
+  __syncthreads();
+  (void)sh;
+}
+
 // Evaluates one head on the current U: mixed weights Wt, FP16 weights W16
 // over S_h, ranking verdict and E_key.
 __device__ void evaluate_head(const Shape &s, const Step &w, const Thresh &th, int i, int g, int hq,
@@ -140,7 +164,7 @@ __device__ void evaluate_head(const Shape &s, const Step &w, const Thresh &th, i
   const float M16 = block_max_f32(m16loc, sh.f32);
   for (int b = threadIdx.x; b < NB; b += CTL_NT) w.W16[base + b] = 0u;
   __syncthreads();
-  const int n2 = pow2_at_least(n);
+  const int n2 = max(64, pow2_at_least(n));
   for (int k = threadIdx.x; k < n2; k += CTL_NT) {
     unsigned long long key = 0ull;
     if (k < n) {
@@ -153,7 +177,7 @@ __device__ void evaluate_head(const Shape &s, const Step &w, const Thresh &th, i
     keys[k] = key;
   }
   __syncthreads();
-  bitonic_desc<CTL_NT>(keys, n2);
+  sort_desc_u64<CTL_NT>(keys, max(n, 1));
   unsigned long long ssd = 0ull;
   for (int j = threadIdx.x; j < n; j += CTL_NT) {
     const uint32_t b = 0xffffffffu - (uint32_t)(keys[j] & 0xffffffffull);
@@ -174,22 +198,14 @@ __device__ void evaluate_head(const Shape &s, const Step &w, const Thresh &th, i
   __syncthreads();
 }
 
-// Rung 2 for one head: greedy value promotion; returns via vh / V flags.
+// Rung 2 for one head with E_val(no value promoted) = numv / denv > v_tol:
+// greedy value promotion by contribution; sets vh / V flags.
 __device__ void value_rung(const Shape &s, const Tier1 &t, const Step &w, const Thresh &th, int i,
-                           int g, int hq, int NB, size_t unit, unsigned long long *keys,
-                           CtlShared &sh) {
+                           int g, int hq, int NB, size_t unit, unsigned long long numv,
+                           unsigned long long denv, unsigned long long *keys, CtlShared &sh) {
   const size_t base = ((size_t)i * s.Hq + hq) * s.NBmax;
   const float *eta = t.eta + unit * s.NBmax;
-  unsigned long long numv = 0ull, denv = 0ull;
-  for (int b = threadIdx.x; b < NB; b += CTL_NT) {
-    const uint32_t Wt = w.Wt[base + b];
-    numv += (unsigned long long)ceil((double)(Wt + 65u) * W_UP * (double)eta[b]);
-    denv += (unsigned long long)floor((double)Wt * W_DN);
-  }
-  numv = block_sum_u64(numv, sh.u64[0]);
-  denv = block_sum_u64(denv, sh.u64[1]);
-  if (!((double)numv / (double)denv > th.v_tol)) return;
-  const int n2 = pow2_at_least(NB);
+  const int n2 = max(64, pow2_at_least(NB));
   for (int b = threadIdx.x; b < n2; b += CTL_NT) {
     unsigned long long key = 0ull;
     if (b < NB) {
@@ -201,35 +217,24 @@ __device__ void value_rung(const Shape &s, const Tier1 &t, const Step &w, const 
     keys[b] = key;
   }
   __syncthreads();
-  bitonic_desc<CTL_NT>(keys, n2);
-  // prefix sums of the sorted contributions (4 per thread, NB <= 4096)
-  constexpr int PER = MAX_NB / CTL_NT;
-  unsigned long long loc[PER];
-  unsigned long long run = 0ull;
-  for (int k = 0; k < PER; ++k) {
-    const int p = threadIdx.x * PER + k;
-    if (p < NB) run += keys[p] >> 12;
-    loc[k] = run;
-  }
-  __shared__ unsigned long long part[CTL_NT + 1];
-  part[threadIdx.x + 1] = run;
-  if (threadIdx.x == 0) part[0] = 0ull;
-  __syncthreads();
-  for (int o = 1; o < CTL_NT; o <<= 1) {
-    unsigned long long v = 0ull;
-    if ((int)threadIdx.x >= o) v = part[threadIdx.x + 1 - o];
-    __syncthreads();
-    part[threadIdx.x + 1] += v;
-    __syncthreads();
-  }
-  const unsigned long long off = part[threadIdx.x];
+  sort_desc_u64<CTL_NT>(keys, NB);
+  // prefix sums of the sorted contributions: thread t owns [t*per, (t+1)*per)
+  const int per = (n2 + CTL_NT - 1) / CTL_NT;
+  const int p0 = threadIdx.x * per;
+  unsigned long long own = 0ull;
+  for (int k = 0; k < per; ++k)
+    if (p0 + k < NB) own += keys[p0 + k] >> 12;
+  unsigned long long total;
+  const unsigned long long incl = block_incl_scan_u64<CTL_NT>(own, sh.u64[0], &total);
+  unsigned long long pre = incl - own;
   int kmin = NB;
-  for (int k = 0; k < PER; ++k) {
-    const int p = threadIdx.x * PER + k;
+  for (int k = 0; k < per; ++k) {
+    const int p = p0 + k;
     if (p >= NB) break;
-    const unsigned long long rem = numv - (off + loc[k]);
+    pre += keys[p] >> 12;
+    const unsigned long long rem = numv - pre;
     if ((double)rem / (double)denv <= th.v_tol) {
-      kmin = min(kmin, p + 1);
+      kmin = p + 1;
       break;
     }
   }
@@ -241,118 +246,174 @@ __device__ void value_rung(const Shape &s, const Tier1 &t, const Step &w, const 
     vh[b] = 1;
     V[b] = 1;   // benign race across heads: every writer stores 1
   }
-  if (threadIdx.x == 0) w.hflags[(size_t)i * s.Hq + hq] |= 8u;   // bit3: V_h non-empty
   __syncthreads();
 }
 
-__global__ __launch_bounds__(CTL_NT) void k_control(Shape s, Tier1 t, Step w, SeqTab tab, int layer,
-                                                    Thresh th, int round) {
+// One controller round, part 1: every query head not yet at rung 3, in a
+// group not yet final, is evaluated on the group's current U (one workgroup
+// per query head).
+__global__ __launch_bounds__(CTL_NT) void k_eval(Shape s, Step w, SeqTab tab, Thresh th) {
   extern __shared__ unsigned long long keys[];
   __shared__ uint16_t pos[MAX_NB];
+  __shared__ CtlShared sh;
+  const int i = blockIdx.y, hq = blockIdx.x, g = hq / s.G;
+  if (w.gstat[(size_t)i * s.Hkv + g] & 1u) return;
+  if (w.hflags[(size_t)i * s.Hq + hq] & 4u) return;
+  const int NB = (tab.T[i] + BLOCK - 1) / BLOCK;
+  evaluate_head(s, w, th, i, g, hq, NB, keys, pos, sh);
+}
+
+// Part 2, one workgroup per (sequence, KV head): rung 1 decisions; a group
+// that widens plans its new key blocks, a group that stops takes its final
+// decisions (rung 3 for heads above eps_key, rung 2, E_val, levels) and
+// plans its value blocks.
+__global__ __launch_bounds__(CTL_NT) void k_decide(Shape s, Tier1 t, Step w, SeqTab tab, int layer,
+                                                   Thresh th, int round) {
+  extern __shared__ unsigned long long keys[];
   __shared__ CtlShared sh;
   __shared__ int tmp[17];
   const int i = blockIdx.y, g = blockIdx.x;
   uint32_t *gs = w.gstat + (size_t)i * s.Hkv + g;
+  uint32_t *nr = w.nruns + ((size_t)i * s.Hkv + g) * 2;
   if (*gs & 1u) {                             // group already final: nothing new to copy
     if (threadIdx.x == 0) {
-      w.nruns[((size_t)i * s.Hkv + g) * 2 + 0] = 0u;
-      w.nruns[((size_t)i * s.Hkv + g) * 2 + 1] = 0u;
+      nr[0] = 0u;
+      nr[1] = 0u;
     }
     return;
   }
   const int T = tab.T[i], NB = (T + BLOCK - 1) / BLOCK;
   const size_t unit = unit_of(s, tab.slot[i], layer, g);
-  if (threadIdx.x == 0) w.nruns[((size_t)i * s.Hkv + g) * 2 + 0] = 0u;
-  for (int hh = 0; hh < s.G; ++hh) {
-    const int hq = g * s.G + hh;
-    if (w.hflags[(size_t)i * s.Hq + hq] & 4u) continue;      // failed earlier
-    evaluate_head(s, w, th, i, g, hq, NB, keys, pos, sh);
+  // head state of the group, loaded in parallel (one thread per head)
+  __shared__ uint32_t hf[4];
+  __shared__ double hek[4];
+  __shared__ int hss[4];
+  if (threadIdx.x < s.G) {
+    const size_t o = (size_t)i * s.Hq + g * s.G + threadIdx.x;
+    hf[threadIdx.x] = w.hflags[o];
+    hek[threadIdx.x] = w.ekey64[o];
+    hss[threadIdx.x] = w.ssize[o];
   }
-  // rung 1
+  if (threadIdx.x == 0) nr[0] = 0u;
+  __syncthreads();
   if (threadIdx.x == 0) {
     int any = 0;
     if (round < th.R1) {
       for (int hh = 0; hh < s.G; ++hh) {
-        const size_t o = (size_t)i * s.Hq + g * s.G + hh;
-        const uint32_t f = w.hflags[o];
-        if (f & 4u) continue;
-        if (w.ekey64[o] > th.eps_key && w.ssize[o] < NB) {
-          w.ssize[o] = min(NB, 2 * w.ssize[o]);
-          w.hflags[o] = f | 2u;
+        if (hf[hh] & 4u) continue;
+        if (hek[hh] > th.eps_key && hss[hh] < NB) {
+          hss[hh] = min(NB, 2 * hss[hh]);
+          hf[hh] |= 2u;
           any = 1;
         }
       }
     }
+    if (!any)   // final round of this group: rung 3 for heads still above eps_key
+      for (int hh = 0; hh < s.G; ++hh)
+        if (!(hf[hh] & 4u) && hek[hh] > th.eps_key) hf[hh] |= 4u;
     sh.wid = any;
+  }
+  __syncthreads();
+  if (threadIdx.x < s.G) {
+    const size_t o = (size_t)i * s.Hq + g * s.G + threadIdx.x;
+    w.hflags[o] = hf[threadIdx.x];
+    w.ssize[o] = hss[threadIdx.x];
   }
   __syncthreads();
   if (sh.wid) {
     plan_group_keys(s, w, i, g, NB);
     return;
   }
-  // final round of this group: rung 3 for heads still above eps_key
-  if (threadIdx.x == 0) {
-    for (int hh = 0; hh < s.G; ++hh) {
-      const size_t o = (size_t)i * s.Hq + g * s.G + hh;
-      if (!(w.hflags[o] & 4u) && w.ekey64[o] > th.eps_key) w.hflags[o] |= 4u;
+  // E_val ingredients of every head of the group in one pass over the blocks
+  const uint8_t *V = w.V + ((size_t)i * s.Hkv + g) * s.NBmax;
+  const float *eta = t.eta + unit * s.NBmax;
+  unsigned long long sums[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) sums[k] = 0ull;
+  for (int b = threadIdx.x; b < NB; b += CTL_NT) {
+    const double eb = (double)eta[b];
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) {
+      if (hh >= s.G) continue;
+      const uint32_t Wt = w.Wt[((size_t)i * s.Hq + g * s.G + hh) * s.NBmax + b];
+      sums[2 * hh] += (unsigned long long)ceil((double)(Wt + 65u) * W_UP * eb);
+      sums[2 * hh + 1] += (unsigned long long)floor((double)Wt * W_DN);
+    }
+  }
+  block_sum_u64_8(sums, sh);
+  // rung 2
+  int anyv = 0;
+  for (int hh = 0; hh < s.G; ++hh) {
+    const int hq = g * s.G + hh;
+    if (hf[hh] & 4u) continue;
+    if ((double)sums[2 * hh] / (double)sums[2 * hh + 1] > th.v_tol) {
+      value_rung(s, t, w, th, i, g, hq, NB, unit, sums[2 * hh], sums[2 * hh + 1], keys, sh);
+      if (threadIdx.x == 0) hf[hh] |= 8u;
+      anyv = 1;
     }
   }
   __syncthreads();
-  // rung 2
-  for (int hh = 0; hh < s.G; ++hh) {
-    const int hq = g * s.G + hh;
-    if (w.hflags[(size_t)i * s.Hq + hq] & 4u) continue;
-    value_rung(s, t, w, th, i, g, hq, NB, unit, keys, sh);
+  if (anyv) {
+    // E_val on the group's V: contributions of blocks without FP16 values
+#pragma unroll
+    for (int k = 0; k < 8; k += 2) sums[k] = 0ull;
+    for (int b = threadIdx.x; b < NB; b += CTL_NT) {
+      if (V[b]) continue;
+      const double eb = (double)eta[b];
+#pragma unroll
+      for (int hh = 0; hh < 4; ++hh) {
+        if (hh >= s.G) continue;
+        const uint32_t Wt = w.Wt[((size_t)i * s.Hq + g * s.G + hh) * s.NBmax + b];
+        sums[2 * hh] += (unsigned long long)ceil((double)(Wt + 65u) * W_UP * eb);
+      }
+    }
+    unsigned long long dens[4];
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) dens[hh] = sums[2 * hh + 1];
+    block_sum_u64_8(sums, sh);
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) sums[2 * hh + 1] = dens[hh];
   }
-  __syncthreads();
-  // E_val on the group's V and the levels
-  const uint8_t *V = w.V + ((size_t)i * s.Hkv + g) * s.NBmax;
-  const float *eta = t.eta + unit * s.NBmax;
   int any3 = 0;
+  __syncthreads();
   for (int hh = 0; hh < s.G; ++hh) {
-    const int hq = g * s.G + hh;
-    const size_t o = (size_t)i * s.Hq + hq;
-    const uint32_t f = w.hflags[o];
+    const size_t o = (size_t)i * s.Hq + g * s.G + hh;
+    const uint32_t f = hf[hh];
     if (f & 4u) {
+      any3 = 1;
       if (threadIdx.x == 0) {
         w.hlevel[o] = 3;
         w.eval64[o] = 0.0;
       }
-      any3 = 1;
-      continue;
-    }
-    const size_t base = o * s.NBmax;
-    unsigned long long numv = 0ull, denv = 0ull;
-    for (int b = threadIdx.x; b < NB; b += CTL_NT) {
-      const uint32_t Wt = w.Wt[base + b];
-      if (!V[b]) numv += (unsigned long long)ceil((double)(Wt + 65u) * W_UP * (double)eta[b]);
-      denv += (unsigned long long)floor((double)Wt * W_DN);
-    }
-    numv = block_sum_u64(numv, sh.u64[0]);
-    denv = block_sum_u64(denv, sh.u64[1]);
-    if (threadIdx.x == 0) {
-      w.eval64[o] = (double)numv / (double)denv;
+    } else if (threadIdx.x == 0) {
+      w.eval64[o] = (double)sums[2 * hh] / (double)sums[2 * hh + 1];
       w.hlevel[o] = (f & 8u) ? 2 : ((f & 2u) ? 1 : 0);
     }
   }
-  // value promotions to copy
-  uint8_t *Vn = w.Vnew + ((size_t)i * s.Hkv + g) * s.NBmax;
-  for (int b = threadIdx.x; b < NB; b += CTL_NT) Vn[b] = V[b];
+  // value promotions to copy: runs of V, extracted from an LDS copy
+  __shared__ uint8_t fv[MAX_NB];
+  for (int b = threadIdx.x; b < NB; b += CTL_NT) fv[b] = anyv ? V[b] : 0;
   __syncthreads();
   uint32_t *runs = w.runs + (((size_t)i * s.Hkv + g) * 2 + 1) * s.runmax;
-  const int nr = build_runs(Vn, NB, runs, tmp);
+  const int nrv = anyv ? build_runs(fv, NB, runs, tmp) : 0;
   if (threadIdx.x == 0) {
-    w.nruns[((size_t)i * s.Hkv + g) * 2 + 1] = (uint32_t)nr;
+    nr[1] = (uint32_t)nrv;
     *gs = 1u | (any3 ? 2u : 0u);
-    uint32_t *fl = w.hflags + (size_t)i * s.Hq + g * s.G;
-    for (int hh = 0; hh < s.G; ++hh) fl[hh] = (fl[hh] & 0xffu) | ((uint32_t)round << 8);
+  }
+  if (threadIdx.x < s.G) {
+    // bit3 marks V_h non-empty; bits 8..15 the round the group stopped in
+    w.hflags[(size_t)i * s.Hq + g * s.G + threadIdx.x] = (hf[threadIdx.x] & 0xffu) | ((uint32_t)round << 8);
   }
 }
 
 hipError_t launch_control(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,
                           int layer, const Thresh &th, int round, int maxNB, hipStream_t st) {
-  const int n2 = pow2_at_least(maxNB);
-  hipLaunchKernelGGL(k_control, dim3(s.Hkv, tab.n), dim3(CTL_NT), n2 * sizeof(unsigned long long),
+  const int n2 = max(64, pow2_at_least(maxNB));
+  hipLaunchKernelGGL(k_eval, dim3(s.Hq, tab.n), dim3(CTL_NT), n2 * sizeof(unsigned long long), st,
+                     s, w, tab, th);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_decide, dim3(s.Hkv, tab.n), dim3(CTL_NT), n2 * sizeof(unsigned long long),
                      st, s, t, w, tab, layer, th, round);
   return hipGetLastError();
 }

@@ -24,8 +24,8 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 // Scores of a chunk -> per-head p = 2^(x - M_h) in LDS, M_h and l_h = sum p.
 template <int D, bool DENSE>
 __device__ __forceinline__ void chunk_softmax(const Shape &s, const Step &w, int i, int g, size_t ig,
-                                              int t0, int nt, const uint8_t *U, float (*ps)[DEC_CB * BLOCK],
-                                              float *sM, float *sL) {
+                                              int t0, int nt, unsigned long long umask,
+                                              float (*ps)[DEC_CB * BLOCK], float *sM, float *sL) {
   const int G = s.G;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   for (int idx = threadIdx.x; idx < G * nt; idx += 256) {
@@ -41,7 +41,7 @@ __device__ __forceinline__ void chunk_softmax(const Shape &s, const Step &w, int
       x = acc;
     } else {
       const size_t o = ((size_t)i * s.Hq + hq) * s.Tmax + tok;
-      x = U[tok / BLOCK] ? w.sp[o] : w.shat[o];
+      x = ((umask >> (tt / BLOCK)) & 1ull) ? w.sp[o] : w.shat[o];
     }
     ps[h][tt] = x;
   }
@@ -82,7 +82,7 @@ __global__ __launch_bounds__(256) void k_decode_dense(Shape s, Tier1 t, Step w, 
   __shared__ float ps[4][CT];
   __shared__ float red[4][4][D];
   __shared__ float sM[4], sL[4];
-  chunk_softmax<D, true>(s, w, i, g, ig, t0, nt, w.U + ig * s.NBmax, ps, sM, sL);
+  chunk_softmax<D, true>(s, w, i, g, ig, t0, nt, 0ull, ps, sM, sL);
   float o[4][CPL];
 #pragma unroll
   for (int h = 0; h < 4; ++h)
@@ -156,7 +156,10 @@ __global__ __launch_bounds__(256) void k_decode_mixed(Shape s, Tier1 t, Step w, 
   __shared__ float ps[4][CT];
   __shared__ __align__(16) int8_t As[4][16 * AST];
   __shared__ float sM[4], sL[4];
-  chunk_softmax<D, false>(s, w, i, g, ig, t0, nt, U, ps, sM, sL);
+  const int nblk = b1 - b0;
+  const unsigned long long umask = __ballot(lane < nblk && U[b0 + lane] != 0);
+  const unsigned long long vmask = __ballot(lane < nblk && V[b0 + lane] != 0);
+  chunk_softmax<D, false>(s, w, i, g, ig, t0, nt, umask, ps, sM, sL);
 
   float acc[NTW];
 #pragma unroll
@@ -165,9 +168,27 @@ __global__ __launch_bounds__(256) void k_decode_mixed(Shape s, Tier1 t, Step w, 
   const uint16_t *sv = w.stage_v + ig * s.Tmax * D;
   int8_t *Aw = As[wave];
 
+  // software pipeline: the next block's value metadata and codes are in
+  // flight while the current block is processed
+  uint32_t meta_n = 0u;
+  uint2 pk_n[NTW];
+  auto fetch = [&](int bb) {
+    const int tk = bb * BLOCK + lane;
+    meta_n = (tk < T) ? t.vmeta[(u * s.Tmax + tk) * (D / VGROUP) + j] : 0u;
+    const uint8_t *vc = t.vcodes + (u * s.NBmax + bb) * (size_t)(32 * D);
+#pragma unroll
+    for (int k = 0; k < NTW; ++k)
+      pk_n[k] = *(const uint2 *)(vc + (size_t)((wave * NTW + k) * 64 + lane) * 8);
+  };
+  fetch(b0);
   for (int b = b0; b < b1; ++b) {
     const int tb = (b - b0) * BLOCK;             // chunk-local index of the block's row 0
-    if (V[b]) {
+    const uint32_t meta = meta_n;
+    uint2 pk[NTW];
+#pragma unroll
+    for (int k = 0; k < NTW; ++k) pk[k] = pk_n[k];
+    if (b + 1 < b1) fetch(b + 1);
+    if ((vmask >> (b - b0)) & 1ull) {
       // FP16 values of a promoted block (rung 2): plain fp32 accumulation
       const int n = min(BLOCK, T - b * BLOCK);
 #pragma unroll 4
@@ -185,7 +206,6 @@ __global__ __launch_bounds__(256) void k_decode_mixed(Shape s, Tier1 t, Step w, 
     const bool valid = tok < T;
     float sc = 0.0f, of = 0.0f;
     if (valid) {
-      const uint32_t meta = t.vmeta[(u * s.Tmax + tok) * (D / VGROUP) + j];
       sc = h2f((uint16_t)(meta & 0xffffu));
       of = h2f((uint16_t)(meta >> 16));
     }
@@ -203,18 +223,15 @@ __global__ __launch_bounds__(256) void k_decode_mixed(Shape s, Tier1 t, Step w, 
     }
     wave_lds_sync();
     const v4i Aop = *(const v4i *)&Aw[(lane & 15) * AST + 16 * (lane >> 4)];
-    const uint8_t *vc = t.vcodes + (u * s.NBmax + b) * (size_t)(32 * D);
     const float f0 = ldexpf(1.0f, e), f1 = ldexpf(1.0f, e + 7), f2 = ldexpf(1.0f, e + 14),
                 f3 = ldexpf(1.0f, e + 21);
 #pragma unroll
     for (int k = 0; k < NTW; ++k) {
-      const int ntile = wave * NTW + k;
-      const uint2 pk = *(const uint2 *)(vc + (size_t)(ntile * 64 + lane) * 8);
       v4i Bop;
-      Bop[0] = (int)(pk.x & 0x0f0f0f0fu);
-      Bop[1] = (int)((pk.x >> 4) & 0x0f0f0f0fu);
-      Bop[2] = (int)(pk.y & 0x0f0f0f0fu);
-      Bop[3] = (int)((pk.y >> 4) & 0x0f0f0f0fu);
+      Bop[0] = (int)(pk[k].x & 0x0f0f0f0fu);
+      Bop[1] = (int)((pk[k].x >> 4) & 0x0f0f0f0fu);
+      Bop[2] = (int)(pk[k].y & 0x0f0f0f0fu);
+      Bop[3] = (int)((pk[k].y >> 4) & 0x0f0f0f0fu);
       const v4i Dm = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aop, Bop, (v4i){0, 0, 0, 0}, 0, 0, 0);
       float a = acc[k];
       a = fmaf((float)Dm[0], f0, a);

@@ -54,7 +54,7 @@ struct Step {
   double *ekey64, *eval64;         // [B][Hq]
   uint32_t *hflags;                // [B][Hq]
   int8_t *hlevel;                  // [B][Hq]
-  uint8_t *U, *Knew, *V, *Vnew;    // [B][Hkv][NBmax]
+  uint8_t *U, *Knew, *V;           // [B][Hkv][NBmax]
   uint32_t *gstat;                 // [B][Hkv] bit0 done, bit1 any rung 3
   uint32_t *runs;                  // [B][Hkv][2][RUNMAX] start | len << 16
   uint32_t *nruns;                 // [B][Hkv][2]
@@ -116,6 +116,7 @@ hipError_t launch_score_fp16(const Shape &s, const Step &w, const SeqTab &tab, i
 hipError_t launch_control(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,
                           int layer, const Thresh &th, int round, int maxNB, hipStream_t st);
 hipError_t launch_gather_plan(const Shape &s, const Step &w, int n, hipStream_t st);
+hipError_t launch_reset(const Shape &s, const Step &w, int n, hipStream_t st);
 hipError_t launch_finalize(const Shape &s, const Step &w, const SeqTab &tab, const Thresh &th,
                            float *e_key, float *e_val, int8_t *level, hipStream_t st);
 hipError_t launch_decode(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,

@@ -76,23 +76,40 @@ __global__ __launch_bounds__(256) void k_score_int8(Shape s, Tier1 t, Step w, Se
 
   const int b_first = blockIdx.x * S8_BLOCKS_PER_WG + wave;
   const int b_end = min(NB, (int)(blockIdx.x + 1) * S8_BLOCKS_PER_WG);
-  for (int b = b_first; b < b_end; b += 4) {
-    const int n = min(BLOCK, T - b * BLOCK);
-    const uint8_t *kc = t.kcodes + (u * s.NBmax + b) * (size_t)(BLOCK * D);
-    v4i Bv[NKS][4];
+  // software pipeline: the next block's codes and metadata are in flight
+  // while the current block is processed
+  v4i Bn[NKS][4];
+  uint32_t kmn[CW];
+  auto fetch = [&](int bb) {
+    const uint8_t *kc = t.kcodes + (u * s.NBmax + bb) * (size_t)(BLOCK * D);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
-        Bv[ks][nt] = *(const v4i *)(kc + ((size_t)((ks * 4 + nt) * 64 + lane)) * 16);
+        Bn[ks][nt] = *(const v4i *)(kc + ((size_t)((ks * 4 + nt) * 64 + lane)) * 16);
+    const uint32_t *km = t.kmeta + (u * s.NBmax + bb) * D + jc * CW;
+#pragma unroll
+    for (int k = 0; k < CW; ++k) kmn[k] = km[k];
+  };
+  if (b_first < b_end) fetch(b_first);
+  for (int b = b_first; b < b_end; b += 4) {
+    const int n = min(BLOCK, T - b * BLOCK);
+    v4i Bv[NKS][4];
+    uint32_t kmv[CW];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) Bv[ks][nt] = Bn[ks][nt];
+#pragma unroll
+    for (int k = 0; k < CW; ++k) kmv[k] = kmn[k];
+    if (b + 4 < b_end) fetch(b + 4);
 
     // ---- prologue: exponent, limbs of A, beta and Delta' per head -----------
-    const uint32_t *km = t.kmeta + (u * s.NBmax + b) * D + jc * CW;
     float sv[CW], ov[CW], a[CW];
     float am = 0.0f;
 #pragma unroll
     for (int k = 0; k < CW; ++k) {
-      const uint32_t m = km[k];
+      const uint32_t m = kmv[k];
       sv[k] = h2f((uint16_t)(m & 0xffffu));
       ov[k] = h2f((uint16_t)(m >> 16));
       a[k] = qv[k] * sv[k];
@@ -198,41 +215,46 @@ hipError_t launch_score_int8(const Shape &s, const Tier1 &t, const Step &w, cons
 
 // ---- FP16-key scores of blocks promoted this round ------------------------------
 // One workgroup per (sequence, KV head, block); wave h = query head of the
-// group, lane = token.  Each lane runs the canonical fma chain over channels.
+// group, lane = token.  The block's FP16 keys are staged with 16-byte
+// coalesced loads into LDS rows padded to d*2 + 16 bytes (conflict-free
+// 16-byte row reads); q' is read at wave-uniform addresses.  Each lane runs
+// the canonical fma chain over channels in ascending order.
 template <int D>
 __global__ __launch_bounds__(256) void k_score_fp16(Shape s, Step w, SeqTab tab) {
-  constexpr int KST = D + 2;            // LDS row stride (halves): 4-byte bank spread
+  constexpr int RST = D + 8;            // LDS row stride in halves (d*2 + 16 bytes)
   const int i = blockIdx.z, g = blockIdx.y, b = blockIdx.x;
   const int T = tab.T[i], NB = (T + BLOCK - 1) / BLOCK;
   if (b >= NB) return;
   uint8_t *flag = w.Knew + ((size_t)i * s.Hkv + g) * s.NBmax + b;
   if (*flag == 0) return;
   const int n = min(BLOCK, T - b * BLOCK);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  __shared__ __align__(16) uint16_t sk[BLOCK * KST];
-  __shared__ float sq[4][D];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  __shared__ __align__(16) uint16_t sk[BLOCK * RST];
 
   const uint16_t *src = w.stage_k + (((size_t)i * s.Hkv + g) * s.Tmax + (size_t)b * BLOCK) * D;
-  for (int idx = threadIdx.x; idx < BLOCK * D / 2; idx += 256) {
-    const int r = idx / (D / 2), c2 = (idx % (D / 2)) * 2;
-    uint32_t v = 0u;
-    if (r < n) v = *(const uint32_t *)(src + (size_t)r * D + c2);
-    *(uint32_t *)&sk[r * KST + c2] = v;
-  }
-  for (int idx = threadIdx.x; idx < s.G * D; idx += 256) {
-    const int hh = idx / D, c = idx % D;
-    sq[hh][c] = w.qp[((size_t)i * s.Hq + g * s.G + hh) * D + c];
+  for (int idx = threadIdx.x; idx < BLOCK * D / 8; idx += 256) {
+    const int r = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r < n) v = *(const uint4 *)(src + (size_t)r * D + c8);
+    *(uint4 *)&sk[r * RST + c8] = v;
   }
   __syncthreads();
   if (wave < s.G) {
     const int hq = g * s.G + wave;
+    const float *q = w.qp + ((size_t)i * s.Hq + hq) * D;
     float acc = 0.0f;
-    const uint16_t *row = &sk[lane * KST];
-#pragma unroll 8
-    for (int c = 0; c < D; c += 2) {
-      const uint32_t kk = *(const uint32_t *)&row[c];
-      acc = fmaf(sq[wave][c], h2f((uint16_t)(kk & 0xffffu)), acc);
-      acc = fmaf(sq[wave][c + 1], h2f((uint16_t)(kk >> 16)), acc);
+    const uint16_t *row = &sk[lane * RST];
+#pragma unroll 4
+    for (int c = 0; c < D; c += 8) {
+      const uint4 kk = *(const uint4 *)&row[c];
+      acc = fmaf(q[c + 0], h2f((uint16_t)(kk.x & 0xffffu)), acc);
+      acc = fmaf(q[c + 1], h2f((uint16_t)(kk.x >> 16)), acc);
+      acc = fmaf(q[c + 2], h2f((uint16_t)(kk.y & 0xffffu)), acc);
+      acc = fmaf(q[c + 3], h2f((uint16_t)(kk.y >> 16)), acc);
+      acc = fmaf(q[c + 4], h2f((uint16_t)(kk.z & 0xffffu)), acc);
+      acc = fmaf(q[c + 5], h2f((uint16_t)(kk.z >> 16)), acc);
+      acc = fmaf(q[c + 6], h2f((uint16_t)(kk.w & 0xffffu)), acc);
+      acc = fmaf(q[c + 7], h2f((uint16_t)(kk.w >> 16)), acc);
     }
     const bool valid = lane < n;
     if (valid) w.sp[((size_t)i * s.Hq + hq) * s.Tmax + (size_t)b * BLOCK + lane] = acc;

@@ -21,11 +21,10 @@ constexpr int SEL_NT = 1024;
 __global__ __launch_bounds__(SEL_NT) void k_select(Shape s, Step w, SeqTab tab, int tau_ppm) {
   extern __shared__ unsigned long long keys[];
   __shared__ float red[SEL_NT / 64];
-  __shared__ unsigned long long part[SEL_NT + 1];
+  __shared__ unsigned long long sbuf[SEL_NT / 64];
   const int i = blockIdx.y, hq = blockIdx.x;
   const int T = tab.T[i], NB = (T + BLOCK - 1) / BLOCK;
-  int n2 = 1;
-  while (n2 < NB) n2 <<= 1;
+  const int n2 = max(64, pow2_at_least(NB));
   const size_t base = ((size_t)i * s.Hq + hq) * s.NBmax;
 
   float m = -INFINITY;
@@ -34,6 +33,7 @@ __global__ __launch_bounds__(SEL_NT) void k_select(Shape s, Step w, SeqTab tab, 
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
   float M = red[0];
+#pragma unroll
   for (int k = 1; k < SEL_NT / 64; ++k) M = fmaxf(M, red[k]);
 
   for (int b = threadIdx.x; b < n2; b += SEL_NT) {
@@ -45,44 +45,31 @@ __global__ __launch_bounds__(SEL_NT) void k_select(Shape s, Step w, SeqTab tab, 
     }
     keys[b] = key;
   }
-  __syncthreads();
-  bitonic_desc<SEL_NT>(keys, n2);
+  sort_desc_u64<SEL_NT>(keys, NB);
 
-  // pi, then inclusive prefix sums of the sorted weights (4 per thread)
-  constexpr int PER = MAX_NB / SEL_NT;
-  unsigned long long loc[PER];
-  unsigned long long run = 0ull;
-  for (int k = 0; k < PER; ++k) {
-    const int p = threadIdx.x * PER + k;
-    unsigned long long W = 0ull;
+  // pi, then prefix sums of the sorted weights: thread t owns positions
+  // [t*per, (t+1)*per)
+  const int per = (n2 + SEL_NT - 1) / SEL_NT;
+  const int p0 = threadIdx.x * per;
+  unsigned long long own = 0ull;
+  for (int k = 0; k < per; ++k) {
+    const int p = p0 + k;
     if (p < NB) {
       const unsigned long long key = keys[p];
       w.pi[base + p] = 0xffffffffu - (uint32_t)(key & 0xffffffffull);
-      W = key >> 32;
+      own += key >> 32;
     }
-    run += W;
-    loc[k] = run;
   }
-  part[threadIdx.x + 1] = run;
-  if (threadIdx.x == 0) part[0] = 0ull;
-  __syncthreads();
-  for (int o = 1; o < SEL_NT; o <<= 1) {           // inclusive scan of part[1..]
-    unsigned long long v = 0ull;
-    if (threadIdx.x >= o) v = part[threadIdx.x + 1 - o];
-    __syncthreads();
-    part[threadIdx.x + 1] += v;
-    __syncthreads();
-  }
-  const unsigned long long total = part[SEL_NT];
+  unsigned long long total;
+  const unsigned long long incl = block_incl_scan_u64<SEL_NT>(own, sbuf, &total);
   const unsigned long long need = (unsigned long long)tau_ppm * total;
-  const unsigned long long off = part[threadIdx.x];
-  for (int k = 0; k < PER; ++k) {
-    const int p = threadIdx.x * PER + k;         // K* candidate p + 1
+  unsigned long long pre = incl - own;
+  for (int k = 0; k < per; ++k) {
+    const int p = p0 + k;                       // K* candidate p + 1
     if (p >= NB) break;
-    const unsigned long long pre = off + loc[k];
-    const unsigned long long prev = (k == 0) ? off : off + loc[k - 1];
+    const bool ok_prev = (p == 0) ? false : (1000000ull * pre >= need);
+    pre += keys[p] >> 32;
     const bool ok = 1000000ull * pre >= need;
-    const bool ok_prev = (p == 0) ? false : (1000000ull * prev >= need);
     if (ok && !ok_prev) {
       w.k0[(size_t)i * s.Hq + hq] = p + 1;
       w.ssize[(size_t)i * s.Hq + hq] = p + 1;
@@ -92,14 +79,13 @@ __global__ __launch_bounds__(SEL_NT) void k_select(Shape s, Step w, SeqTab tab, 
 
 hipError_t launch_select(const Shape &s, const Step &w, const SeqTab &tab, int tau_ppm, int maxNB,
                          hipStream_t st) {
-  int n2 = 1;
-  while (n2 < maxNB) n2 <<= 1;
+  const int n2 = max(64, pow2_at_least(maxNB));
   hipLaunchKernelGGL(k_select, dim3(s.Hq, tab.n), dim3(SEL_NT), n2 * sizeof(unsigned long long),
                      st, s, w, tab, tau_ppm);
   return hipGetLastError();
 }
 
-__global__ __launch_bounds__(256) void k_plan_keys(Shape s, Step w, SeqTab tab) {
+__global__ __launch_bounds__(1024) void k_plan_keys(Shape s, Step w, SeqTab tab) {
   const int i = blockIdx.y, g = blockIdx.x;
   const int NB = (tab.T[i] + BLOCK - 1) / BLOCK;
   plan_group_keys(s, w, i, g, NB);
@@ -108,7 +94,7 @@ __global__ __launch_bounds__(256) void k_plan_keys(Shape s, Step w, SeqTab tab) 
 hipError_t launch_plan_keys(const Shape &s, const Step &w, const SeqTab &tab, int maxNB,
                             hipStream_t st) {
   (void)maxNB;
-  hipLaunchKernelGGL(k_plan_keys, dim3(s.Hkv, tab.n), dim3(256), 0, st, s, w, tab);
+  hipLaunchKernelGGL(k_plan_keys, dim3(s.Hkv, tab.n), dim3(1024), 0, st, s, w, tab);
   return hipGetLastError();
 }
 
@@ -157,6 +143,34 @@ __global__ __launch_bounds__(1024) void k_gather_plan(Shape s, Step w, int n) {
     w.plan[2] = (unsigned long long)s_flags;
     w.plan[3] = 0ull;
   }
+}
+
+// Clears the per-step flags and head state of the first n call positions in
+// one launch (byte arrays [n][Hkv][NBmax] and [n][Hq][NBmax], head/group words).
+__global__ void k_reset(Shape s, Step w, int n) {
+  const size_t nb_g = (size_t)n * s.Hkv * s.NBmax, nb_h = (size_t)n * s.Hq * s.NBmax;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t k = blockIdx.x * (size_t)blockDim.x + threadIdx.x; k < nb_g; k += stride) {
+    w.U[k] = 0;
+    w.Knew[k] = 0;
+    w.V[k] = 0;
+  }
+  for (size_t k = blockIdx.x * (size_t)blockDim.x + threadIdx.x; k < nb_h; k += stride) w.vh[k] = 0;
+  for (size_t k = blockIdx.x * (size_t)blockDim.x + threadIdx.x; k < (size_t)n * s.Hq; k += stride) {
+    w.hflags[k] = 0u;
+    w.ekey64[k] = 0.0;
+    w.eval64[k] = 0.0;
+  }
+  for (size_t k = blockIdx.x * (size_t)blockDim.x + threadIdx.x; k < (size_t)n * s.Hkv; k += stride) {
+    w.gstat[k] = 0u;
+    w.nruns[2 * k] = 0u;
+    w.nruns[2 * k + 1] = 0u;
+  }
+}
+
+hipError_t launch_reset(const Shape &s, const Step &w, int n, hipStream_t st) {
+  hipLaunchKernelGGL(k_reset, dim3(64), dim3(256), 0, st, s, w, n);
+  return hipGetLastError();
 }
 
 hipError_t launch_gather_plan(const Shape &s, const Step &w, int n, hipStream_t st) {

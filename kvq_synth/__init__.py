@@ -152,9 +152,9 @@ def prefill(w, layer, seq):
             r = rng(w.cfg_id, layer, seq, TAG_HOSTILE * 64 + g)
             ng = w.d // 32
             hit = r.random((T, ng)) < w.hostile_frac
-            vals = r.uniform(-50.0, 50.0, size=(T, ng, 32)).astype(np.float32)
+            vals = r.uniform(-50.0, 50.0, size=(int(hit.sum()), 32)).astype(np.float32)
             Vg = V[:, g, :].reshape(T, ng, 32)
-            Vg[hit] = vals[hit]
+            Vg[hit] = vals
             V[:, g, :] = Vg.reshape(T, w.d)
     return to16(K), to16(V)
 
