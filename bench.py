@@ -173,8 +173,8 @@ def main():
         return sum(r[key] for r in recs) / n
 
     per_kernel = {k: avg(k) for k in ("ms_score_int8", "ms_select", "ms_score_fp16",
-                                      "ms_control", "ms_copy", "ms_decode", "ms_dense",
-                                      "ms_total")}
+                                      "ms_control", "ms_copy", "ms_decode", "ms_combine",
+                                      "ms_dense", "ms_misc", "ms_total")}
     T_avg = kv_tokens / n
     t1b = kvq.tier1_bytes_per_token(d)
     bytes_k = T_avg * Hkv * (d + 4 * d / 64)                  # INT8 codes + key meta
@@ -194,7 +194,7 @@ def main():
                 "traffic": counter_traffic(dom, shape), "avg_launch_ms": round(ms_dom, 5),
                 "algorithmic_bytes_per_launch": int(by_dom)}
     qp_ms = (per_kernel["ms_score_int8"] + per_kernel["ms_select"] + per_kernel["ms_control"] +
-             per_kernel["ms_decode"])
+             per_kernel["ms_decode"] + per_kernel["ms_combine"] + per_kernel["ms_misc"])
     qp_bytes = T_avg * Hkv * t1b
     quantized_pass = {
         "ms_per_layer": round(qp_ms, 5), "tier1_bytes_per_layer": int(qp_bytes),

@@ -42,7 +42,8 @@ class StepStats(ctypes.Structure):
                 ("ms_score_int8", ctypes.c_float), ("ms_select", ctypes.c_float),
                 ("ms_score_fp16", ctypes.c_float), ("ms_control", ctypes.c_float),
                 ("ms_copy", ctypes.c_float), ("ms_decode", ctypes.c_float),
-                ("ms_dense", ctypes.c_float), ("ms_total", ctypes.c_float)]
+                ("ms_dense", ctypes.c_float), ("ms_total", ctypes.c_float),
+                ("ms_combine", ctypes.c_float), ("ms_misc", ctypes.c_float)]
 
     def as_dict(self):
         d = {k: getattr(self, k) for k, _ in self._fields_}

@@ -27,6 +27,13 @@
 
 using namespace kvq;
 
+namespace kvq {
+KernelClock *&kernel_clock() {
+  static thread_local KernelClock *clock = nullptr;
+  return clock;
+}
+}  // namespace kvq
+
 struct kvq_ctx {
   kvq_config cfg;
   Shape s;
@@ -38,7 +45,9 @@ struct kvq_ctx {
   std::vector<void *> dallocs;
   hipStream_t cstream = nullptr;
   hipEvent_t ev_start = nullptr, ev_copy = nullptr;
-  hipEvent_t ev_t[48] = {};
+  hipEvent_t ev_k[128] = {};   // kernel timing pairs
+  hipEvent_t ev_c[32] = {};    // copy timing pairs
+  hipEvent_t ev_tot[2] = {};
   unsigned long long *plan_host = nullptr;
   size_t plan_cap = 0;
   size_t plan_words = 0;
@@ -85,7 +94,11 @@ void free_all(kvq_ctx *c) {
   if (c->cstream) (void)hipStreamDestroy(c->cstream);
   if (c->ev_start) (void)hipEventDestroy(c->ev_start);
   if (c->ev_copy) (void)hipEventDestroy(c->ev_copy);
-  for (auto &e : c->ev_t)
+  for (auto &e : c->ev_k)
+    if (e) (void)hipEventDestroy(e);
+  for (auto &e : c->ev_c)
+    if (e) (void)hipEventDestroy(e);
+  for (auto &e : c->ev_tot)
     if (e) (void)hipEventDestroy(e);
 }
 
@@ -99,32 +112,52 @@ bool valid_seqs(const kvq_ctx *c, int n, const int32_t *ids) {
   return true;
 }
 
-// Kernel timing: pairs of events around a launch, summed per category.
-enum TimeCat { TC_SCORE8, TC_SELECT, TC_SCORE16, TC_CONTROL, TC_COPY, TC_DECODE, TC_DENSE, TC_TOTAL, TC_N };
+// Step timing.  Kernels: while a category is open, each launch is stamped
+// with its own start/end events (launch_k); copies: event pairs recorded on
+// the copy stream around each batch of copies.  Sums per category.
+enum TimeCat {
+  TC_SCORE8, TC_SELECT, TC_SCORE16, TC_CONTROL, TC_COPY, TC_DECODE, TC_DENSE, TC_COMBINE,
+  TC_MISC, TC_N
+};
 struct Timer {
   kvq_ctx *c;
   bool on;
-  int used = 0;
-  int cat[24];
-  hipError_t begin(int k, hipStream_t st) {
-    if (!on || used >= 24) return hipSuccess;
-    cat[used] = k;
-    return hipEventRecord(c->ev_t[2 * used], st);
+  KernelClock kc{};
+  int ncopy = 0;
+  int ccat[16];
+  Timer(kvq_ctx *ctx, bool timing) : c(ctx), on(timing) {
+    kc.ev = c->ev_k;
+    kc.cap = 64;
+    kc.used = 0;
+    kc.open = -1;
+    if (on) kernel_clock() = &kc;
   }
-  hipError_t end(hipStream_t st) {
-    if (!on || used >= 24) return hipSuccess;
-    hipError_t e = hipEventRecord(c->ev_t[2 * used + 1], st);
-    ++used;
+  ~Timer() {
+    if (on) kernel_clock() = nullptr;
+  }
+  void open(int k) { kc.open = k; }
+  void close() { kc.open = -1; }
+  hipError_t copy_begin(int k, hipStream_t st) {
+    if (!on || ncopy >= 16) return hipSuccess;
+    ccat[ncopy] = k;
+    return hipEventRecord(c->ev_c[2 * ncopy], st);
+  }
+  hipError_t copy_end(hipStream_t st) {
+    if (!on || ncopy >= 16) return hipSuccess;
+    hipError_t e = hipEventRecord(c->ev_c[2 * ncopy + 1], st);
+    ++ncopy;
     return e;
   }
   hipError_t collect(float *ms) {
     for (int k = 0; k < TC_N; ++k) ms[k] = 0.0f;
-    for (int u = 0; u < used; ++u) {
+    for (int u = 0; u < kc.used + ncopy; ++u) {
+      const bool kern = u < kc.used;
+      hipEvent_t *ev = kern ? c->ev_k + 2 * u : c->ev_c + 2 * (u - kc.used);
       float a = 0.0f;
-      hipError_t e = hipEventSynchronize(c->ev_t[2 * u + 1]);
-      if (e == hipSuccess) e = hipEventElapsedTime(&a, c->ev_t[2 * u], c->ev_t[2 * u + 1]);
+      hipError_t e = hipEventSynchronize(ev[1]);
+      if (e == hipSuccess) e = hipEventElapsedTime(&a, ev[0], ev[1]);
       if (e != hipSuccess) return e;
-      ms[cat[u]] += a;
+      ms[kern ? kc.cat[u] : ccat[u - kc.used]] += a;
     }
     return hipSuccess;
   }
@@ -181,6 +214,7 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out) {
   if (!cfg || !out) return KVQ_EINVAL;
   const kvq_config &c = *cfg;
   if (c.n_layers < 1 || c.max_batch < 1 || c.n_q_heads < 1 || c.n_kv_heads < 1 ||
+      c.n_kv_heads > 128 ||
       c.n_q_heads % c.n_kv_heads != 0 || (c.head_dim != 64 && c.head_dim != 128) ||
       c.max_tokens < 1 || (c.max_tokens + BLOCK - 1) / BLOCK > MAX_NB)
     return KVQ_EINVAL;
@@ -207,6 +241,14 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out) {
   s.runmax = s.NBmax / 2 + 1;
   s.nchmax = (s.NBmax + DEC_CB - 1) / DEC_CB;
   s.B = c.max_batch;
+  s.ncu = 0;
+  if (hipDeviceGetAttribute(&s.ncu, hipDeviceAttributeMultiprocessorCount, x->device) !=
+          hipSuccess ||
+      s.ncu < 1) {
+    (void)hipGetLastError();
+    delete x;
+    return KVQ_EHIP;
+  }
   x->th.tau_ppm = c.tau_cov_ppm;
   x->th.rho_ppm = c.rho_min_ppm;
   x->th.R1 = c.widen_rounds;
@@ -291,7 +333,11 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out) {
   if (e == hipSuccess) e = hipStreamCreateWithFlags(&x->cstream, hipStreamNonBlocking);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&x->ev_start, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&x->ev_copy, hipEventDisableTiming);
-  for (auto &ev : x->ev_t)
+  for (auto &ev : x->ev_k)
+    if (e == hipSuccess) e = hipEventCreate(&ev);
+  for (auto &ev : x->ev_c)
+    if (e == hipSuccess) e = hipEventCreate(&ev);
+  for (auto &ev : x->ev_tot)
     if (e == hipSuccess) e = hipEventCreate(&ev);
   if (e == hipSuccess) e = hipMemsetD32(reinterpret_cast<hipDeviceptr_t>(t.vmin), 0xff800000u, NU * d);
   if (e == hipSuccess) e = hipMemsetD32(reinterpret_cast<hipDeviceptr_t>(t.vmax), 0x007fffffu, NU * d);
@@ -435,6 +481,7 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
     if (T < 1) return fail(ctx, KVQ_ESTATE, "decode on an empty sequence");
     tab.slot[i] = seq_ids[i];
     tab.T[i] = (int)T;
+    tab.nbc[i + 1] = tab.nbc[i] + (int)((T + BLOCK - 1) / BLOCK);
     maxNB = std::max(maxNB, (int)((T + BLOCK - 1) / BLOCK));
   }
   hipStream_t st = (hipStream_t)stream;
@@ -444,8 +491,9 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
   int64_t h2d = 0, kblk = 0, vblk = 0, dense_heads = 0;
   int syncs = 0, rounds = 0;
   Timer tm{ctx, timing};
-  if (timing) HIPCK(ctx, hipEventRecord(ctx->ev_t[46], st));
+  if (timing) HIPCK(ctx, hipEventRecord(ctx->ev_tot[0], st));
 
+  tm.open(TC_MISC);
   HIPCK(ctx, launch_reset(s, w, n, st));
   // staging may still be read by the previous step's kernels, and tier 2 was
   // written by earlier appends on this stream: copies wait for both
@@ -454,14 +502,13 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
 
   const float C = (float)(1.4426950408889634 / sqrt((double)s.d));
   HIPCK(ctx, launch_qprep(s, w, n, (const uint16_t *)q, C, st));
-  HIPCK(ctx, tm.begin(TC_SCORE8, st));
+  tm.open(TC_SCORE8);
   HIPCK(ctx, launch_score_int8(s, ctx->t, w, tab, layer, maxNB, st));
-  HIPCK(ctx, tm.end(st));
-  HIPCK(ctx, tm.begin(TC_SELECT, st));
+  tm.open(TC_SELECT);
   HIPCK(ctx, launch_select(s, w, tab, ctx->th.tau_ppm, maxNB, st));
   HIPCK(ctx, launch_plan_keys(s, w, tab, maxNB, st));
   HIPCK(ctx, launch_gather_plan(s, w, n, st));
-  HIPCK(ctx, tm.end(st));
+  tm.close();
   Plan plan;
   kvq_status rs = read_plan(ctx, st, plan);
   if (rs != KVQ_OK) return rs;
@@ -469,31 +516,32 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
   for (int round = 0;; ++round) {
     const bool new_keys = plan.nk > 0;
     if (!plan.ent.empty()) {
-      HIPCK(ctx, tm.begin(TC_COPY, ctx->cstream));
+      HIPCK(ctx, tm.copy_begin(TC_COPY, ctx->cstream));
       rs = issue_copies(ctx, tab, layer, plan, h2d, kblk, vblk);
       if (rs != KVQ_OK) return rs;
-      HIPCK(ctx, tm.end(ctx->cstream));
+      HIPCK(ctx, tm.copy_end(ctx->cstream));
       HIPCK(ctx, hipEventRecord(ctx->ev_copy, ctx->cstream));
       HIPCK(ctx, hipStreamWaitEvent(st, ctx->ev_copy, 0));
     }
     if (round > 0 && !(plan.flags & 1u)) break;      // every group final
     if (round > ctx->th.R1) return fail(ctx, KVQ_EHIP, "controller did not finish its rounds");
     if (new_keys) {
-      HIPCK(ctx, tm.begin(TC_SCORE16, st));
+      tm.open(TC_SCORE16);
       HIPCK(ctx, launch_score_fp16(s, w, tab, maxNB, st));
-      HIPCK(ctx, tm.end(st));
     }
-    HIPCK(ctx, tm.begin(TC_CONTROL, st));
+    tm.open(TC_CONTROL);
     HIPCK(ctx, launch_control(s, ctx->t, w, tab, layer, ctx->th, round, maxNB, st));
-    HIPCK(ctx, tm.end(st));
     HIPCK(ctx, launch_gather_plan(s, w, n, st));
+    tm.close();
     rs = read_plan(ctx, st, plan);
     if (rs != KVQ_OK) return rs;
     ++syncs;
     rounds = round + 1;
     if (!(plan.flags & 1u) && plan.ent.empty()) break;
   }
+  tm.open(TC_MISC);
   HIPCK(ctx, launch_finalize(s, w, tab, ctx->th, e_key, e_val, level, st));
+  tm.close();
   const bool maybe_dense = ctx->th.force_dense || (plan.flags & 2u);
   std::vector<uint8_t> gd;
   if (maybe_dense) {
@@ -510,27 +558,28 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
         const size_t u = unit_of(s, tab.slot[i], layer, g);
         const size_t ig = (size_t)i * s.Hkv + g;
         const size_t bytes = (size_t)((tab.T[i] + BLOCK - 1) / BLOCK) * BLOCK * s.d * 2;
-        HIPCK(ctx, tm.begin(TC_COPY, ctx->cstream));
+        HIPCK(ctx, tm.copy_begin(TC_COPY, ctx->cstream));
         HIPCK(ctx, hipMemcpyAsync(w.stage_k + ig * s.Tmax * s.d, ctx->t2k_host + u * s.Tmax * s.d,
                                   bytes, hipMemcpyHostToDevice, ctx->cstream));
         HIPCK(ctx, hipMemcpyAsync(w.stage_v + ig * s.Tmax * s.d, ctx->t2v_host + u * s.Tmax * s.d,
                                   bytes, hipMemcpyHostToDevice, ctx->cstream));
-        HIPCK(ctx, tm.end(ctx->cstream));
+        HIPCK(ctx, tm.copy_end(ctx->cstream));
         h2d += 2 * (int64_t)bytes;
       }
     if (any) {
       HIPCK(ctx, hipEventRecord(ctx->ev_copy, ctx->cstream));
       HIPCK(ctx, hipStreamWaitEvent(st, ctx->ev_copy, 0));
-      HIPCK(ctx, tm.begin(TC_DENSE, st));
+      tm.open(TC_DENSE);
       HIPCK(ctx, launch_decode(s, ctx->t, w, tab, layer, maxNB, true, st));
-      HIPCK(ctx, tm.end(st));
+      tm.close();
     }
   }
-  HIPCK(ctx, tm.begin(TC_DECODE, st));
+  tm.open(TC_DECODE);
   HIPCK(ctx, launch_decode(s, ctx->t, w, tab, layer, maxNB, false, st));
+  tm.open(TC_COMBINE);
   HIPCK(ctx, launch_combine(s, w, tab, out, st));
-  HIPCK(ctx, tm.end(st));
-  if (timing) HIPCK(ctx, hipEventRecord(ctx->ev_t[47], st));
+  tm.close();
+  if (timing) HIPCK(ctx, hipEventRecord(ctx->ev_tot[1], st));
 
   ctx->last_n = n;
   ctx->last_layer = layer;
@@ -561,9 +610,11 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
       stats->ms_copy = ms[TC_COPY];
       stats->ms_decode = ms[TC_DECODE];
       stats->ms_dense = ms[TC_DENSE];
+      stats->ms_combine = ms[TC_COMBINE];
+      stats->ms_misc = ms[TC_MISC];
       float a = 0.0f;
-      HIPCK(ctx, hipEventSynchronize(ctx->ev_t[47]));
-      HIPCK(ctx, hipEventElapsedTime(&a, ctx->ev_t[46], ctx->ev_t[47]));
+      HIPCK(ctx, hipEventSynchronize(ctx->ev_tot[1]));
+      HIPCK(ctx, hipEventElapsedTime(&a, ctx->ev_tot[0], ctx->ev_tot[1]));
       stats->ms_total = a;
     }
   }

@@ -1,6 +1,7 @@
 // kvq_blockops.h -- workgroup-level building blocks shared by the selection
-// and controller kernels: exclusive scan, run extraction, bitonic sort of
-// 64-bit keys in LDS, and the per-KV-head promotion planner.
+// and controller kernels: exclusive scan, run extraction, sort of 64-bit
+// keys (register bitonic chunks merged in LDS), and the per-KV-head
+// promotion planner.
 #pragma once
 #include "kvq_device.h"
 #include "kvq_internal.h"
@@ -70,155 +71,121 @@ __device__ inline int build_runs(const uint8_t *flags, int NB, uint32_t *runs, i
   return base_s;
 }
 
-// ---- block sort of distinct 64-bit keys into descending order -------------
-// Bitonic network on a power-of-two count n2 (64 <= n2 <= 16 * NT).  Each
-// thread keeps E = max(1, n2/NT) consecutive keys in registers: partners
-// closer than E are in the same thread, partners closer than 64*E in the same
-// wave (exchanged with compile-time lane masks), and only the wider stages go
-// through LDS with barriers.
-__device__ __forceinline__ unsigned long long cx_pick(unsigned long long a, unsigned long long b,
-                                                      bool keep_max) {
-  return keep_max ? (a > b ? a : b) : (a < b ? a : b);
+// ---- block sort of 64-bit keys into descending order -----------------------
+// Every wave sorts a chunk of 64*E keys in registers with a bitonic network
+// (E consecutive keys per lane; partners closer than E in the same lane,
+// the others exchanged across lanes with DPP / swizzle moves), then sorted
+// runs are merged pairwise in LDS: a key's position in the merged run is its
+// position in its own run plus the number of keys of the partner run ahead of
+// it (binary search; the earlier run wins ties, so positions never collide),
+// computed by every thread for its keys before any is written.
+template <int X>
+__device__ __forceinline__ unsigned long long xor_lane_u64(unsigned long long v) {
+  const int lo = xor_lane<X>((int)(uint32_t)v);
+  const int hi = xor_lane<X>((int)(uint32_t)(v >> 32));
+  return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
 }
 
-template <int E, int LJ>
-__device__ __forceinline__ void inwave_stage(unsigned long long (&v)[E], int t, int kk) {
-  constexpr int J = LJ * E;
+template <int E, int KK, int J>
+__device__ __forceinline__ void bitonic_stage(unsigned long long (&v)[E], int lane) {
+  if constexpr (J < E) {
 #pragma unroll
-  for (int k = 0; k < E; ++k) {
-    const int e = t * E + k;
-    const unsigned long long p = __shfl_xor(v[k], LJ, 64);
-    v[k] = cx_pick(v[k], p, ((e & J) == 0) == ((e & kk) == 0));
-  }
-}
-
-template <int E, int JJ>
-__device__ __forceinline__ void inthread_stage(unsigned long long (&v)[E], int t, int kk) {
+    for (int k = 0; k < E; ++k) {
+      if (k & J) continue;
+      const bool desc = ((lane * E + k) & KK) == 0;
+      const unsigned long long a = v[k], b = v[k | J];
+      const bool swap = desc ? (a < b) : (a > b);
+      v[k] = swap ? b : a;
+      v[k | J] = swap ? a : b;
+    }
+  } else {
 #pragma unroll
-  for (int k = 0; k < E; ++k) {
-    if (k & JJ) continue;
-    const int e = t * E + k;
-    const unsigned long long a = v[k], b = v[k | JJ];
-    const bool desc = (e & kk) == 0;
-    if (desc ? (a < b) : (a > b)) {
-      v[k] = b;
-      v[k | JJ] = a;
+    for (int k = 0; k < E; ++k) {
+      const int le = lane * E + k;
+      const unsigned long long p = xor_lane_u64<J / E>(v[k]);
+      const bool keep_max = ((le & J) == 0) == ((le & KK) == 0);
+      v[k] = keep_max ? (v[k] > p ? v[k] : p) : (v[k] < p ? v[k] : p);
     }
   }
+  if constexpr (J > 1) bitonic_stage<E, KK, J / 2>(v, lane);
+}
+
+template <int E, int KK, int CH>
+__device__ __forceinline__ void bitonic_chunk(unsigned long long (&v)[E], int lane) {
+  bitonic_stage<E, KK, KK / 2>(v, lane);
+  if constexpr (KK < CH) bitonic_chunk<E, KK * 2, CH>(v, lane);
+}
+
+// Number of entries of the descending run a[0..len) ahead of x: those > x
+// (ties = false) or >= x (ties = true).
+__device__ __forceinline__ int count_ahead(const unsigned long long *a, int len,
+                                           unsigned long long x, bool ties) {
+  int lo = 0, hi = len;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    const unsigned long long y = a[mid];
+    if (y > x || (ties && y == x)) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
 }
 
 template <int NT, int E>
-__device__ inline void sort_desc_pow2_e(unsigned long long *keys, int n2) {
-  const int act = n2 / E;
-  const int t = threadIdx.x;
+__device__ inline void sort_desc_merge(unsigned long long *keys, int n) {
+  constexpr int CH = 64 * E;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nch = (n + CH - 1) / CH;
+  const int cap = nch * CH;
+  const bool active = wave < nch;
   unsigned long long v[E];
-#pragma unroll
-  for (int k = 0; k < E; ++k) v[k] = 0ull;
+  int pos[E];
   __syncthreads();
-  if (t < act) {
 #pragma unroll
-    for (int k = 0; k < E; ++k) v[k] = keys[t * E + k];
+  for (int k = 0; k < E; ++k) {
+    pos[k] = wave * CH + lane * E + k;
+    v[k] = (active && pos[k] < n) ? keys[pos[k]] : 0ull;
   }
-  for (int kk = 2; kk <= n2; kk <<= 1) {
-    // stages whose partner lives in another wave: through LDS
-    for (int j = kk >> 1; j >= 64 * E; j >>= 1) {
-      __syncthreads();
-      if (t < act) {
+  if (active) bitonic_chunk<E, 2, CH>(v, lane);
+  __syncthreads();
+  if (active) {
 #pragma unroll
-        for (int k = 0; k < E; ++k) keys[t * E + k] = v[k];
-      }
-      __syncthreads();
-      if (t < act) {
+    for (int k = 0; k < E; ++k) keys[pos[k]] = v[k];
+  }
+  for (int R = CH; R < cap; R <<= 1) {
+    __syncthreads();
+    int np[E];
+    if (active) {
 #pragma unroll
-        for (int k = 0; k < E; ++k) {
-          const int e = t * E + k;
-          v[k] = cx_pick(v[k], keys[e ^ j], ((e & j) == 0) == ((e & kk) == 0));
-        }
+      for (int k = 0; k < E; ++k) {
+        const int id = pos[k] / R;
+        const int ps = (id ^ 1) * R;
+        const int plen = max(0, min(R, cap - ps));
+        const int cnt = count_ahead(keys + ps, plen, v[k], (id & 1) != 0);
+        np[k] = (id & ~1) * R + (pos[k] - id * R) + cnt;
       }
     }
-    // stages within a wave, then within a thread (partner distance j = LJ*E)
-    const int top = kk >> 1;
-    if (top >= 32 * E) inwave_stage<E, 32>(v, t, kk);
-    if (top >= 16 * E) inwave_stage<E, 16>(v, t, kk);
-    if (top >= 8 * E) inwave_stage<E, 8>(v, t, kk);
-    if (top >= 4 * E) inwave_stage<E, 4>(v, t, kk);
-    if (top >= 2 * E) inwave_stage<E, 2>(v, t, kk);
-    if (top >= E) inwave_stage<E, 1>(v, t, kk);
-    if (E >= 16 && top >= 8) inthread_stage<E, (E >= 16 ? 8 : 1)>(v, t, kk);
-    if (E >= 8 && top >= 4) inthread_stage<E, (E >= 8 ? 4 : 1)>(v, t, kk);
-    if (E >= 4 && top >= 2) inthread_stage<E, (E >= 4 ? 2 : 1)>(v, t, kk);
-    if (E >= 2 && top >= 1) inthread_stage<E, 1>(v, t, kk);
-  }
-  __syncthreads();
-  if (t < act) {
+    __syncthreads();
+    if (active) {
 #pragma unroll
-    for (int k = 0; k < E; ++k) keys[t * E + k] = v[k];
+      for (int k = 0; k < E; ++k) {
+        pos[k] = np[k];
+        keys[np[k]] = v[k];
+      }
+    }
   }
   __syncthreads();
 }
 
-template <int NT>
-__device__ inline void sort_desc_pow2(unsigned long long *keys, int n2) {
-  if (n2 <= NT)
-    sort_desc_pow2_e<NT, 1>(keys, n2);
-  else if (n2 <= 2 * NT)
-    sort_desc_pow2_e<NT, 2>(keys, n2);
-  else if (n2 <= 4 * NT)
-    sort_desc_pow2_e<NT, 4>(keys, n2);
-  else if (n2 <= 8 * NT)
-    sort_desc_pow2_e<NT, 8>(keys, n2);
-  else
-    sort_desc_pow2_e<NT, 16>(keys, n2);
-}
-
-// Sorts n distinct keys keys[0..n) into descending order (n <= 4 * NT); the
-// buffer must hold pow2(n) entries.  n = A + B with A the largest power of two
-// <= n (at least 64): A and B (zero-padded to a power of two) are sorted by
-// the network above and merged in place: every key's output position is found
-// by binary search in the other run (keys are distinct, so positions never
-// collide), kept in registers, and written after a barrier.
+// Sorts keys[0..n) into descending order (1 <= n <= 4 * NT); the buffer must
+// hold max(64, pow2(n)) entries, those past n are used as scratch.
 template <int NT>
 __device__ inline void sort_desc_u64(unsigned long long *keys, int n) {
-  int A = 64;
-  while (A * 2 <= n) A <<= 1;
-  if (n <= A) {
-    for (int k = n + threadIdx.x; k < A; k += NT) keys[k] = 0ull;
-    sort_desc_pow2<NT>(keys, A);
-    return;
-  }
-  const int B = n - A;
-  int B2 = 64;
-  while (B2 < B) B2 <<= 1;
-  unsigned long long *kb = keys + A;
-  for (int k = B + threadIdx.x; k < B2; k += NT) kb[k] = 0ull;
-  sort_desc_pow2<NT>(keys, A);
-  sort_desc_pow2<NT>(kb, B2);
-  unsigned long long kv[4];
-  int pos[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int x = threadIdx.x + r * NT;
-    pos[r] = -1;
-    kv[r] = 0ull;
-    if (x < A + B) {
-      const bool inA = x < A;
-      const int idx = inA ? x : x - A;
-      const unsigned long long key = inA ? keys[idx] : kb[idx];
-      const unsigned long long *other = inA ? kb : keys;
-      int lo = 0, hi = inA ? B : A;             // count of other keys > key
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (other[mid] > key) lo = mid + 1; else hi = mid;
-      }
-      kv[r] = key;
-      pos[r] = idx + lo;
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-    if (pos[r] >= 0) keys[pos[r]] = kv[r];
-  __syncthreads();
+  if (n <= NT)
+    sort_desc_merge<NT, 1>(keys, n);
+  else if (n <= 2 * NT)
+    sort_desc_merge<NT, 2>(keys, n);
+  else
+    sort_desc_merge<NT, 4>(keys, n);
 }
 
 // Inclusive scan of per-thread u64 values over a workgroup of NT threads

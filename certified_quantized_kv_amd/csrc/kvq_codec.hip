@@ -128,12 +128,18 @@ __global__ __launch_bounds__(256) void k_append(Shape s, Tier1 t, AppendArgs a,
   if (myerr > 0.0f) atomicMax(&s_err, __float_as_uint(myerr));
   __syncthreads();
 
-  // ---- key codes in MFMA operand order ---------------------------------------
+  // ---- key codes in MFMA operand order, stored as code ^ 0x80 (the signed
+  //      byte code - 128 that the scoring contraction multiplies) -------------
   uint8_t *kdst = t.kcodes + (u * s.NBmax + b) * (size_t)(BLOCK * D);
   for (int q = tid; q < BLOCK * D / 16; q += 256) {
     const int ks = q / 256, nt = (q / 64) % 4, l = q % 64;
     const int r = nt * 16 + (l % 16), c0 = ks * 64 + 16 * (l / 16);
-    *(uint4 *)(kdst + (size_t)q * 16) = *(const uint4 *)&cb[r][c0];
+    uint4 x = *(const uint4 *)&cb[r][c0];
+    x.x ^= 0x80808080u;
+    x.y ^= 0x80808080u;
+    x.z ^= 0x80808080u;
+    x.w ^= 0x80808080u;
+    *(uint4 *)(kdst + (size_t)q * 16) = x;
   }
   // ---- value codes in MFMA operand order (old rows' nibbles kept) --------------
   uint32_t *vdst = (uint32_t *)(t.vcodes + (u * s.NBmax + b) * (size_t)(32 * D));
@@ -177,10 +183,9 @@ hipError_t launch_append(const Shape &s, const Tier1 &t, const AppendArgs &a, co
   if (max_blk <= 0) return hipSuccess;
   dim3 grid(max_blk, s.Hkv, a.n);
   if (s.d == 128)
-    hipLaunchKernelGGL(k_append<128>, grid, dim3(256), 0, st, s, t, a, k, v);
+    return launch_k(k_append<128>, grid, dim3(256), 0, st, s, t, a, k, v);
   else
-    hipLaunchKernelGGL(k_append<64>, grid, dim3(256), 0, st, s, t, a, k, v);
-  return hipGetLastError();
+    return launch_k(k_append<64>, grid, dim3(256), 0, st, s, t, a, k, v);
 }
 
 // ---- exports to plain layouts (tests) ---------------------------------------
@@ -194,7 +199,7 @@ __global__ void k_export_kcodes(Shape s, Tier1 t, size_t u, int T, uint8_t *dst)
     const int b = tok / BLOCK, r = tok % BLOCK;
     const int ks = c / 64, nt = r / 16, l = (r % 16) + 16 * ((c % 64) / 16), jj = c % 16;
     const size_t q = (size_t)((ks * 4 + nt) * 64 + l);
-    dst[idx] = t.kcodes[(u * s.NBmax + b) * (size_t)(BLOCK * d) + q * 16 + jj];
+    dst[idx] = t.kcodes[(u * s.NBmax + b) * (size_t)(BLOCK * d) + q * 16 + jj] ^ 0x80u;
   }
 }
 
@@ -213,13 +218,11 @@ __global__ void k_export_vcodes(Shape s, Tier1 t, size_t u, int T, uint8_t *dst)
 
 hipError_t launch_export_kcodes(const Shape &s, const Tier1 &t, size_t u, int T, uint8_t *dst,
                                 hipStream_t st) {
-  hipLaunchKernelGGL(k_export_kcodes, dim3(256), dim3(256), 0, st, s, t, u, T, dst);
-  return hipGetLastError();
+  return launch_k(k_export_kcodes, dim3(256), dim3(256), 0, st, s, t, u, T, dst);
 }
 hipError_t launch_export_vcodes(const Shape &s, const Tier1 &t, size_t u, int T, uint8_t *dst,
                                 hipStream_t st) {
-  hipLaunchKernelGGL(k_export_vcodes, dim3(256), dim3(256), 0, st, s, t, u, T, dst);
-  return hipGetLastError();
+  return launch_k(k_export_vcodes, dim3(256), dim3(256), 0, st, s, t, u, T, dst);
 }
 
 }  // namespace kvq

@@ -342,12 +342,20 @@ __global__ __launch_bounds__(CTL_NT) void k_decide(Shape s, Tier1 t, Step w, Seq
   }
   block_sum_u64_8(sums, sh);
   // rung 2
+  // (the sums go through LDS so that the head loop below indexes them freely)
+  __shared__ unsigned long long ssum[8];
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) ssum[k] = sums[k];
+  }
+  __syncthreads();
   int anyv = 0;
   for (int hh = 0; hh < s.G; ++hh) {
     const int hq = g * s.G + hh;
     if (hf[hh] & 4u) continue;
-    if ((double)sums[2 * hh] / (double)sums[2 * hh + 1] > th.v_tol) {
-      value_rung(s, t, w, th, i, g, hq, NB, unit, sums[2 * hh], sums[2 * hh + 1], keys, sh);
+    const unsigned long long nv = ssum[2 * hh], dv = ssum[2 * hh + 1];
+    if ((double)nv / (double)dv > th.v_tol) {
+      value_rung(s, t, w, th, i, g, hq, NB, unit, nv, dv, keys, sh);
       if (threadIdx.x == 0) hf[hh] |= 8u;
       anyv = 1;
     }
@@ -376,7 +384,9 @@ __global__ __launch_bounds__(CTL_NT) void k_decide(Shape s, Tier1 t, Step w, Seq
   }
   int any3 = 0;
   __syncthreads();
-  for (int hh = 0; hh < s.G; ++hh) {
+#pragma unroll
+  for (int hh = 0; hh < 4; ++hh) {
+    if (hh >= s.G) continue;
     const size_t o = (size_t)i * s.Hq + g * s.G + hh;
     const uint32_t f = hf[hh];
     if (f & 4u) {
@@ -409,13 +419,11 @@ __global__ __launch_bounds__(CTL_NT) void k_decide(Shape s, Tier1 t, Step w, Seq
 hipError_t launch_control(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,
                           int layer, const Thresh &th, int round, int maxNB, hipStream_t st) {
   const int n2 = max(64, pow2_at_least(maxNB));
-  hipLaunchKernelGGL(k_eval, dim3(s.Hq, tab.n), dim3(CTL_NT), n2 * sizeof(unsigned long long), st,
-                     s, w, tab, th);
-  hipError_t e = hipGetLastError();
+  const hipError_t e = launch_k(k_eval, dim3(s.Hq, tab.n), dim3(CTL_NT),
+                                n2 * sizeof(unsigned long long), st, s, w, tab, th);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_decide, dim3(s.Hkv, tab.n), dim3(CTL_NT), n2 * sizeof(unsigned long long),
-                     st, s, t, w, tab, layer, th, round);
-  return hipGetLastError();
+  return launch_k(k_decide, dim3(s.Hkv, tab.n), dim3(CTL_NT), n2 * sizeof(unsigned long long), st,
+                  s, t, w, tab, layer, th, round);
 }
 
 // ---- rung 4 and the per-head outputs ---------------------------------------------
@@ -454,8 +462,7 @@ __global__ void k_finalize(Shape s, Step w, SeqTab tab, Thresh th, float *e_key,
 
 hipError_t launch_finalize(const Shape &s, const Step &w, const SeqTab &tab, const Thresh &th,
                            float *e_key, float *e_val, int8_t *level, hipStream_t st) {
-  hipLaunchKernelGGL(k_finalize, dim3(tab.n), dim3(64), 0, st, s, w, tab, th, e_key, e_val, level);
-  return hipGetLastError();
+  return launch_k(k_finalize, dim3(tab.n), dim3(64), 0, st, s, w, tab, th, e_key, e_val, level);
 }
 
 }  // namespace kvq

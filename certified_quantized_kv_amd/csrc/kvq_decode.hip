@@ -133,89 +133,128 @@ __global__ __launch_bounds__(256) void k_decode_dense(Shape s, Tier1 t, Step w, 
 // (k: tokens, n: 16 channels), one v_mfma_i32_16x16x64_i8 per 16 channels.
 // Wave w owns the channel tiles of one value group, so A is built by the
 // wave that uses it (p*s < 2^(e + 28), e from the block's largest scale).
+//
+// The chunk's softmax reference M_h is the largest block maximum of the
+// scores in use (FP16 on blocks of U, INT8 elsewhere), known from the
+// scoring passes, so every wave forms p = 2^(x - M_h) for its block's
+// tokens in registers as the block streams in; scores, value metadata and
+// codes run PF blocks ahead of the block being accumulated.
 template <int D>
 __global__ __launch_bounds__(256) void k_decode_mixed(Shape s, Tier1 t, Step w, SeqTab tab, int layer) {
-  constexpr int CT = DEC_CB * BLOCK;
   constexpr int NTW = D / 64;                    // 16-channel tiles per wave
   constexpr int AST = 80;                        // LDS row stride of A (bank spread)
+  constexpr int PF = 2;                          // blocks in flight ahead
   const int i = blockIdx.z, g = blockIdx.y, ch = blockIdx.x;
   const int T = tab.T[i], NB = (T + BLOCK - 1) / BLOCK;
   const int b0 = ch * DEC_CB;
   if (b0 >= NB) return;
   const size_t ig = (size_t)i * s.Hkv + g;
   const int G = s.G;
-  const int t0 = b0 * BLOCK, nt = min(T, (b0 + DEC_CB) * BLOCK) - t0;
-  const int b1 = (t0 + nt + BLOCK - 1) / BLOCK;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int b1 = min(NB, b0 + DEC_CB);
+  const int nblk = b1 - b0;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int hl = lane >> 4;                      // head of this lane in the MFMA output
   const int j = (wave * NTW * 16) / VGROUP;      // value group of this wave's tiles
   const size_t u = unit_of(s, tab.slot[i], layer, g);
   const uint8_t *U = w.U + ig * s.NBmax;
   const uint8_t *V = w.V + ig * s.NBmax;
 
-  __shared__ float ps[4][CT];
   __shared__ __align__(16) int8_t As[4][16 * AST];
-  __shared__ float sM[4], sL[4];
-  const int nblk = b1 - b0;
+  __shared__ float pv[4][4][BLOCK];              // p of an FP16-value block, per wave
   const unsigned long long umask = __ballot(lane < nblk && U[b0 + lane] != 0);
   const unsigned long long vmask = __ballot(lane < nblk && V[b0 + lane] != 0);
-  chunk_softmax<D, false>(s, w, i, g, ig, t0, nt, umask, ps, sM, sL);
+
+  // chunk reference per head: max over the chunk's blocks of the block maxima
+  float Mh[4];
+  {
+    const int k = lane & 15;
+    float bm = -INFINITY;
+    if (hl < G && k < nblk) {
+      const size_t o = ((size_t)i * s.Hq + g * G + hl) * s.NBmax + b0 + k;
+      bm = ((umask >> k) & 1ull) ? w.m16[o] : w.mhat[o];
+    }
+    bm = bfly_max<16>(bm);
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+      Mh[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bm), 16 * h));
+  }
 
   float acc[NTW];
 #pragma unroll
   for (int k = 0; k < NTW; ++k) acc[k] = 0.0f;
   float offacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   const uint16_t *sv = w.stage_v + ig * s.Tmax * D;
   int8_t *Aw = As[wave];
 
-  // software pipeline: the next block's value metadata and codes are in
-  // flight while the current block is processed
-  uint32_t meta_n = 0u;
-  uint2 pk_n[NTW];
-  auto fetch = [&](int bb) {
+  // in-flight ring: scores of the four heads, value metadata, codes
+  struct Stage {
+    float x[4];
+    uint32_t meta;
+    uint2 pk[NTW];
+  };
+  Stage ring[PF];
+  auto fetch = [&](Stage &st, int bb) {
     const int tk = bb * BLOCK + lane;
-    meta_n = (tk < T) ? t.vmeta[(u * s.Tmax + tk) * (D / VGROUP) + j] : 0u;
+    const bool ok = tk < T;
+    const bool up = (umask >> (bb - b0)) & 1ull;
+    const float *src = up ? w.sp : w.shat;
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+      st.x[h] = (ok && h < G) ? src[((size_t)i * s.Hq + g * G + h) * s.Tmax + tk] : -INFINITY;
+    st.meta = ok ? t.vmeta[(u * s.Tmax + tk) * (D / VGROUP) + j] : 0u;
     const uint8_t *vc = t.vcodes + (u * s.NBmax + bb) * (size_t)(32 * D);
 #pragma unroll
     for (int k = 0; k < NTW; ++k)
-      pk_n[k] = *(const uint2 *)(vc + (size_t)((wave * NTW + k) * 64 + lane) * 8);
+      st.pk[k] = *(const uint2 *)(vc + (size_t)((wave * NTW + k) * 64 + lane) * 8);
   };
-  fetch(b0);
-  for (int b = b0; b < b1; ++b) {
-    const int tb = (b - b0) * BLOCK;             // chunk-local index of the block's row 0
-    const uint32_t meta = meta_n;
-    uint2 pk[NTW];
 #pragma unroll
-    for (int k = 0; k < NTW; ++k) pk[k] = pk_n[k];
-    if (b + 1 < b1) fetch(b + 1);
+  for (int q = 0; q < PF; ++q)
+    if (b0 + q < b1) fetch(ring[q], b0 + q);
+
+  for (int b = b0; b < b1; ++b) {
+    const Stage cur = ring[0];
+#pragma unroll
+    for (int q = 0; q + 1 < PF; ++q) ring[q] = ring[q + 1];
+    if (b + PF < b1) fetch(ring[PF - 1], b + PF);
+
+    const int tok = b * BLOCK + lane;
+    const bool valid = tok < T;
+    float p[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      p[h] = (h < G) ? exp2f(cur.x[h] - Mh[h]) : 0.0f;   // 0 for tokens past T
+      lsum[h] += p[h];
+    }
     if ((vmask >> (b - b0)) & 1ull) {
       // FP16 values of a promoted block (rung 2): plain fp32 accumulation
+#pragma unroll
+      for (int h = 0; h < 4; ++h) pv[wave][h][lane] = p[h];
+      wave_lds_sync();
       const int n = min(BLOCK, T - b * BLOCK);
 #pragma unroll 4
       for (int r = 0; r < n; ++r) {
-        const float p = (hl < G) ? ps[hl][tb + r] : 0.0f;
+        const float pr = (hl < G) ? pv[wave][hl][r] : 0.0f;
 #pragma unroll
         for (int k = 0; k < NTW; ++k) {
           const int c = (wave * NTW + k) * 16 + (lane & 15);
-          acc[k] = fmaf(p, h2f(sv[((size_t)b * BLOCK + r) * D + c]), acc[k]);
+          acc[k] = fmaf(pr, h2f(sv[((size_t)b * BLOCK + r) * D + c]), acc[k]);
         }
       }
+      wave_lds_sync();
       continue;
     }
-    const int tok = b * BLOCK + lane;
-    const bool valid = tok < T;
     float sc = 0.0f, of = 0.0f;
     if (valid) {
-      sc = h2f((uint16_t)(meta & 0xffffu));
-      of = h2f((uint16_t)(meta >> 16));
+      sc = h2f((uint16_t)(cur.meta & 0xffffu));
+      of = h2f((uint16_t)(cur.meta >> 16));
     }
     const float smax = bfly_max<64>(sc);
     const int e = (smax > 0.0f) ? ilogb_f(smax) - 27 : 0;
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      const float p = (valid && h < G) ? ps[h][tb + lane] : 0.0f;
-      offacc[h] = fmaf(p, of, offacc[h]);
-      const uint32_t A = (uint32_t)rintf(ldexpf(p * sc, -e));
+      offacc[h] = fmaf(p[h], of, offacc[h]);
+      const uint32_t A = (uint32_t)rintf(ldexpf(p[h] * sc, -e));
       Aw[(h * 4 + 0) * AST + lane] = (int8_t)(A & 127u);
       Aw[(h * 4 + 1) * AST + lane] = (int8_t)((A >> 7) & 127u);
       Aw[(h * 4 + 2) * AST + lane] = (int8_t)((A >> 14) & 127u);
@@ -228,10 +267,10 @@ __global__ __launch_bounds__(256) void k_decode_mixed(Shape s, Tier1 t, Step w, 
 #pragma unroll
     for (int k = 0; k < NTW; ++k) {
       v4i Bop;
-      Bop[0] = (int)(pk[k].x & 0x0f0f0f0fu);
-      Bop[1] = (int)((pk[k].x >> 4) & 0x0f0f0f0fu);
-      Bop[2] = (int)(pk[k].y & 0x0f0f0f0fu);
-      Bop[3] = (int)((pk[k].y >> 4) & 0x0f0f0f0fu);
+      Bop[0] = (int)(cur.pk[k].x & 0x0f0f0f0fu);
+      Bop[1] = (int)((cur.pk[k].x >> 4) & 0x0f0f0f0fu);
+      Bop[2] = (int)(cur.pk[k].y & 0x0f0f0f0fu);
+      Bop[3] = (int)((cur.pk[k].y >> 4) & 0x0f0f0f0fu);
       const v4i Dm = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aop, Bop, (v4i){0, 0, 0, 0}, 0, 0, 0);
       float a = acc[k];
       a = fmaf((float)Dm[0], f0, a);
@@ -242,20 +281,24 @@ __global__ __launch_bounds__(256) void k_decode_mixed(Shape s, Tier1 t, Step w, 
     }
     wave_lds_sync();
   }
-  // offset term of this wave's group, per head
-  float offh = 0.0f;
+  // offset term of this wave's group and the chunk sums, per head
+  float offh = 0.0f, lh = 0.0f;
 #pragma unroll
   for (int h = 0; h < 4; ++h) {
     const float sh = bfly_sum<64>(offacc[h]);
-    if (h == hl) offh = sh;
+    const float lv = bfly_sum<64>(lsum[h]);
+    if (h == hl) {
+      offh = sh;
+      lh = lv;
+    }
   }
   if (hl < G) {
     float *part = w.part + ((ig * s.nchmax + ch) * G + hl) * (size_t)(D + 2);
 #pragma unroll
     for (int k = 0; k < NTW; ++k) part[(wave * NTW + k) * 16 + (lane & 15)] = acc[k] + offh;
     if ((lane & 15) == 0 && wave == 0) {
-      part[D] = sM[hl];
-      part[D + 1] = sL[hl];
+      part[D] = hl == 0 ? Mh[0] : hl == 1 ? Mh[1] : hl == 2 ? Mh[2] : Mh[3];
+      part[D + 1] = lh;
     }
   }
 }
@@ -265,16 +308,15 @@ hipError_t launch_decode(const Shape &s, const Tier1 &t, const Step &w, const Se
   dim3 grid((maxNB + DEC_CB - 1) / DEC_CB, s.Hkv, tab.n);
   if (s.d == 128) {
     if (dense)
-      hipLaunchKernelGGL(k_decode_dense<128>, grid, dim3(256), 0, st, s, t, w, tab, layer);
+      return launch_k(k_decode_dense<128>, grid, dim3(256), 0, st, s, t, w, tab, layer);
     else
-      hipLaunchKernelGGL(k_decode_mixed<128>, grid, dim3(256), 0, st, s, t, w, tab, layer);
+      return launch_k(k_decode_mixed<128>, grid, dim3(256), 0, st, s, t, w, tab, layer);
   } else {
     if (dense)
-      hipLaunchKernelGGL(k_decode_dense<64>, grid, dim3(256), 0, st, s, t, w, tab, layer);
+      return launch_k(k_decode_dense<64>, grid, dim3(256), 0, st, s, t, w, tab, layer);
     else
-      hipLaunchKernelGGL(k_decode_mixed<64>, grid, dim3(256), 0, st, s, t, w, tab, layer);
+      return launch_k(k_decode_mixed<64>, grid, dim3(256), 0, st, s, t, w, tab, layer);
   }
-  return hipGetLastError();
 }
 
 // Merges the chunk partials of each (sequence, query head): levels 3/4 read
@@ -324,8 +366,7 @@ __global__ __launch_bounds__(256) void k_combine(Shape s, Step w, SeqTab tab, fl
 
 hipError_t launch_combine(const Shape &s, const Step &w, const SeqTab &tab, float *out,
                           hipStream_t st) {
-  hipLaunchKernelGGL(k_combine, dim3(s.Hq, tab.n), dim3(256), 0, st, s, w, tab, out);
-  return hipGetLastError();
+  return launch_k(k_combine, dim3(s.Hq, tab.n), dim3(256), 0, st, s, w, tab, out);
 }
 
 }  // namespace kvq

@@ -32,10 +32,12 @@ __device__ __forceinline__ uint16_t ru16(float q) {
 // n, f = x - n (exact, |f| <= 1/2), 2^f by its degree-7 Taylor polynomial
 // (coefficients (ln 2)^k / k! rounded to binary32) in Horner form with fmaf,
 // scaled by 2^n.  Zero for x < -125 (results are always normal otherwise).
+// Evaluated without a branch: the argument is clamped before the polynomial
+// and the result selected afterwards (identical values for every x).
 __device__ __forceinline__ float exp2k(float x) {
-  if (!(x >= -125.0f)) return 0.0f;
-  float n = rintf(x);
-  float f = x - n;
+  const float xc = fmaxf(x, -126.0f);  // NaN -> -126, result discarded below
+  const float n = rintf(xc);
+  const float f = xc - n;
   float p = 0x1.ffcbfcp-17f;           // (ln2)^7/7!
   p = fmaf(p, f, 0x1.430912p-13f);     // (ln2)^6/6!
   p = fmaf(p, f, 0x1.5d87fep-10f);     // (ln2)^5/5!
@@ -44,7 +46,8 @@ __device__ __forceinline__ float exp2k(float x) {
   p = fmaf(p, f, 0x1.ebfbe0p-3f);      // (ln2)^2/2!
   p = fmaf(p, f, 0x1.62e430p-1f);      // ln2
   p = fmaf(p, f, 1.0f);
-  return ldexpf(p, (int)n);
+  const float r = ldexpf(p, (int)n);
+  return (x >= -125.0f) ? r : 0.0f;
 }
 
 // floor(log2 |x|) for finite nonzero x (subnormals included).
@@ -72,25 +75,59 @@ __device__ __forceinline__ float i64_to_f32(long long v) {
   return (float)(double)v;
 }
 
-// Butterfly reductions over lanes that differ in the low bits given by MASKS
-// (xor partners).  For sums this realises fold-in-half: the pair (j, j^w)
-// adds the same two values in either lane (fp32 addition is commutative).
+// Value of lane j ^ X for every lane j (X a power of two below 64).  Within a
+// row of 16 lanes the exchange is done by DPP moves (quad permutes, the
+// half-row mirror, the row rotate by 8), across rows by ds_swizzle (16) and
+// ds_bpermute (32).
+template <int X>
+__device__ __forceinline__ int xor_lane(int v) {
+  static_assert(X == 1 || X == 2 || X == 4 || X == 8 || X == 16 || X == 32, "lane xor");
+  if constexpr (X == 1) {
+    return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xf, 0xf, false);    // quad_perm [1,0,3,2]
+  } else if constexpr (X == 2) {
+    return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xf, 0xf, false);    // quad_perm [2,3,0,1]
+  } else if constexpr (X == 4) {
+    // half-row mirror (j ^ 7), then quad_perm [3,2,1,0] (j ^ 3)
+    const int t = __builtin_amdgcn_mov_dpp(v, 0x141, 0xf, 0xf, false);
+    return __builtin_amdgcn_mov_dpp(t, 0x1B, 0xf, 0xf, false);
+  } else if constexpr (X == 8) {
+    return __builtin_amdgcn_mov_dpp(v, 0x128, 0xf, 0xf, false);   // row_ror:8
+  } else if constexpr (X == 16) {
+    return __builtin_amdgcn_ds_swizzle(v, 0x401F);                // bitmask mode, xor 16
+  } else {
+    return __shfl_xor(v, 32, 64);
+  }
+}
+template <int X>
+__device__ __forceinline__ float xor_lane_f(float v) {
+  return __int_as_float(xor_lane<X>(__float_as_int(v)));
+}
+
+// Butterfly reductions over groups of W lanes (xor partners W/2, ..., 1).
+// For sums this realises fold-in-half: the pair (j, j^w) adds the same two
+// values in either lane (fp32 addition is commutative).
 template <int W>
 __device__ __forceinline__ float bfly_sum(float v) {
-#pragma unroll
-  for (int w = W / 2; w >= 1; w >>= 1) v = v + __shfl_xor(v, w, 64);
+  if constexpr (W > 1) {
+    v = v + xor_lane_f<W / 2>(v);
+    return bfly_sum<W / 2>(v);
+  }
   return v;
 }
 template <int W>
 __device__ __forceinline__ float bfly_max(float v) {
-#pragma unroll
-  for (int w = W / 2; w >= 1; w >>= 1) v = fmaxf(v, __shfl_xor(v, w, 64));
+  if constexpr (W > 1) {
+    v = fmaxf(v, xor_lane_f<W / 2>(v));
+    return bfly_max<W / 2>(v);
+  }
   return v;
 }
 template <int W>
 __device__ __forceinline__ uint32_t bfly_sum_u32(uint32_t v) {
-#pragma unroll
-  for (int w = W / 2; w >= 1; w >>= 1) v += (uint32_t)__shfl_xor((int)v, w, 64);
+  if constexpr (W > 1) {
+    v += (uint32_t)xor_lane<W / 2>((int)v);
+    return bfly_sum_u32<W / 2>(v);
+  }
   return v;
 }
 

@@ -4,9 +4,11 @@
 // per-step scratch) and of tier 2 in pinned host memory.  A "unit" is one
 // (slot, layer, KV head); u = (slot * n_layers + layer) * n_kv_heads + g.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string>
+#include <tuple>
 
 #include "../../include/kvq.h"
 
@@ -19,7 +21,9 @@ constexpr int DEC_CB = 16;          // blocks per split-K chunk of the decode ke
 // Tier 1, per unit (device memory):
 //   kcodes [NBmax][64*d] u8   block-local MFMA operand order: the 16 bytes at
 //                             ((ks*4 + nt)*64 + l)*16 are the codes of token
-//                             nt*16 + l%16, channels ks*64 + 16*(l/16) + 0..15
+//                             nt*16 + l%16, channels ks*64 + 16*(l/16) + 0..15,
+//                             each stored as code ^ 0x80 (= code - 128 as a
+//                             signed byte)
 //   kmeta  [NBmax][d]    u32  binary16 scale (low half), offset (high half)
 //   vcodes [NBmax][32*d] u8   block-local MFMA operand order: for 16-channel
 //                             tile nt and lane l, 8 bytes at (nt*64 + l)*8 hold
@@ -68,10 +72,12 @@ struct SeqTab {
   int n;
   int slot[MAX_CALL];
   int T[MAX_CALL];
+  int nbc[MAX_CALL + 1];            // nbc[i] = blocks of the sequences before i
 };
 
 struct Shape {
   int L, Hq, Hkv, G, d, Tmax, NBmax, runmax, nchmax, B;
+  int ncu;                          // compute units of the device
 };
 
 struct Thresh {
@@ -92,6 +98,40 @@ __host__ __device__ inline void vnib(int r, int c, int &byte, int &shift) {
   const int nt = c >> 4, l = (c & 15) + 16 * (r >> 4), p = r & 15;
   byte = (nt * 64 + l) * 8 + (p >> 3) * 4 + (p & 3);
   shift = ((p >> 2) & 1) * 4;
+}
+
+// ---- kernel launch with optional per-kernel timing ------------------------------
+// While a timing category is open on the calling thread, every launch gets
+// its own pair of events that the runtime stamps with the kernel's start and
+// end (hipExtLaunchKernel), so a pair's elapsed time is that one kernel's
+// duration on its stream.
+struct KernelClock {
+  hipEvent_t *ev;      // 2 * cap events
+  int cap, used;
+  int open;            // category of launches being timed, -1 when none
+  int cat[64];
+};
+KernelClock *&kernel_clock();      // thread-local; defined in kvq_api.hip
+
+template <typename... P, typename... A>
+inline hipError_t launch_k(void (*k)(P...), dim3 grid, dim3 block, uint32_t shmem,
+                           hipStream_t st, A... a) {
+  static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
+  std::tuple<P...> args{a...};
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  KernelClock *kc = kernel_clock();
+  if (kc && kc->open >= 0 && kc->used < kc->cap) {
+    e0 = kc->ev[2 * kc->used];
+    e1 = kc->ev[2 * kc->used + 1];
+    kc->cat[kc->used++] = kc->open;
+  }
+  hipError_t e = std::apply(
+      [&](auto &...x) {
+        void *ptrs[] = {(void *)&x...};
+        return hipExtLaunchKernel((const void *)k, grid, block, ptrs, shmem, st, e0, e1, 0);
+      },
+      args);
+  return e != hipSuccess ? e : hipGetLastError();
 }
 
 // ---- launchers (each in its own .hip file) ---------------------------------

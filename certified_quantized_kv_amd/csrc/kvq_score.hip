@@ -31,6 +31,9 @@
 // FP16-key score (promoted blocks): s'_t = fma chain over c ascending of
 // q'_c * k_tc from 0.  Block ingredients of any score row x:
 //   m_b = max_t x_t,   L_b = sum_t floor(2^24 exp2k(fl32(x_t - m_b)))  (exact).
+#include <algorithm>
+#include <numeric>
+
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -46,54 +49,68 @@ __global__ void k_qprep(int total, const uint16_t *__restrict__ q, float C, floa
 hipError_t launch_qprep(const Shape &s, const Step &w, int n, const uint16_t *q, float C,
                         hipStream_t st) {
   const int total = n * s.Hq * s.d;
-  hipLaunchKernelGGL(k_qprep, dim3((total + 255) / 256), dim3(256), 0, st, total, q, C, w.qp);
-  return hipGetLastError();
+  return launch_k(k_qprep, dim3((total + 255) / 256), dim3(256), 0, st, total, q, C, w.qp);
 }
 
-constexpr int S8_BLOCKS_PER_WG = 16;   // 4 waves x 4 blocks
-
+// Work split: a unit is one (sequence, block, KV head), numbered with the KV
+// head fastest; wave k of the grid (W waves, W a multiple of the KV head
+// count) takes units k, k + W, k + 2W, ...: every wave carries the same load
+// to within one unit, keeps one KV head (one query set) for a sequence, and
+// at any moment the grid streams a contiguous window of blocks per KV head.
 template <int D>
 __global__ __launch_bounds__(256) void k_score_int8(Shape s, Tier1 t, Step w, SeqTab tab, int layer) {
   constexpr int CW = D / 16;            // channels per lane-chunk
   constexpr int NKS = D / 64;           // MFMA k-steps per block
   constexpr int AST = D + 16;           // LDS row stride of the A operand (bank spread)
-  const int i = blockIdx.z, g = blockIdx.y;
-  const int T = tab.T[i], NB = (T + BLOCK - 1) / BLOCK;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int h = lane >> 4, jc = lane & 15;
   const bool hv = h < s.G;
-  const int hq = g * s.G + (hv ? h : 0);
-  const size_t u = unit_of(s, tab.slot[i], layer, g);
 
   __shared__ __align__(16) int8_t As[4][16][AST];
 
+  const int U = s.Hkv * tab.nbc[tab.n];
+  const int W = gridDim.x * 4;
+  const int u0 = blockIdx.x * 4 + wave;
+  if (u0 >= U) return;
+  auto locate = [&](int uu, int &ii, int &gg, int &bb) {
+    ii = 0;
+    while (ii + 1 < tab.n && s.Hkv * tab.nbc[ii + 1] <= uu) ++ii;
+    const int r = uu - s.Hkv * tab.nbc[ii];
+    bb = r / s.Hkv;
+    gg = r - bb * s.Hkv;
+  };
+  int i, g, b;
+  locate(u0, i, g, b);
+
   float qv[CW];
-  {
+  auto load_q = [&]() {
+    const int hq = g * s.G + (hv ? h : 0);
     const float *qsrc = w.qp + ((size_t)i * s.Hq + hq) * D + jc * CW;
 #pragma unroll
-    for (int k = 0; k < CW; ++k) qv[k] = qsrc[k];
-  }
-
-  const int b_first = blockIdx.x * S8_BLOCKS_PER_WG + wave;
-  const int b_end = min(NB, (int)(blockIdx.x + 1) * S8_BLOCKS_PER_WG);
-  // software pipeline: the next block's codes and metadata are in flight
-  // while the current block is processed
+    for (int c = 0; c < CW; ++c) qv[c] = qsrc[c];
+  };
+  // software pipeline: the next unit's codes and metadata are in flight
+  // while the current one is processed
   v4i Bn[NKS][4];
   uint32_t kmn[CW];
-  auto fetch = [&](int bb) {
-    const uint8_t *kc = t.kcodes + (u * s.NBmax + bb) * (size_t)(BLOCK * D);
+  auto fetch = [&](int ii, int gg, int bb) {
+    const size_t uu = unit_of(s, tab.slot[ii], layer, gg);
+    const uint8_t *kc = t.kcodes + (uu * s.NBmax + bb) * (size_t)(BLOCK * D);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
         Bn[ks][nt] = *(const v4i *)(kc + ((size_t)((ks * 4 + nt) * 64 + lane)) * 16);
-    const uint32_t *km = t.kmeta + (u * s.NBmax + bb) * D + jc * CW;
+    const uint32_t *km = t.kmeta + (uu * s.NBmax + bb) * D + jc * CW;
 #pragma unroll
-    for (int k = 0; k < CW; ++k) kmn[k] = km[k];
+    for (int c = 0; c < CW; ++c) kmn[c] = km[c];
   };
-  if (b_first < b_end) fetch(b_first);
-  for (int b = b_first; b < b_end; b += 4) {
+  load_q();
+  fetch(i, g, b);
+  for (int u = u0; u < U; u += W) {
+    const int T = tab.T[i];
     const int n = min(BLOCK, T - b * BLOCK);
+    const int hq = g * s.G + (hv ? h : 0);
     v4i Bv[NKS][4];
     uint32_t kmv[CW];
 #pragma unroll
@@ -101,54 +118,59 @@ __global__ __launch_bounds__(256) void k_score_int8(Shape s, Tier1 t, Step w, Se
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) Bv[ks][nt] = Bn[ks][nt];
 #pragma unroll
-    for (int k = 0; k < CW; ++k) kmv[k] = kmn[k];
-    if (b + 4 < b_end) fetch(b + 4);
+    for (int c = 0; c < CW; ++c) kmv[c] = kmn[c];
+    // successor unit
+    int i2 = i, g2 = g, b2 = b;
+    if (u + W < U) {
+      locate(u + W, i2, g2, b2);
+      fetch(i2, g2, b2);
+    }
 
     // ---- prologue: exponent, limbs of A, beta and Delta' per head -----------
     float sv[CW], ov[CW], a[CW];
     float am = 0.0f;
 #pragma unroll
-    for (int k = 0; k < CW; ++k) {
-      const uint32_t m = kmv[k];
-      sv[k] = h2f((uint16_t)(m & 0xffffu));
-      ov[k] = h2f((uint16_t)(m >> 16));
-      a[k] = qv[k] * sv[k];
-      am = fmaxf(am, fabsf(a[k]));
+    for (int c = 0; c < CW; ++c) {
+      const uint32_t m = kmv[c];
+      sv[c] = h2f((uint16_t)(m & 0xffffu));
+      ov[c] = h2f((uint16_t)(m >> 16));
+      a[c] = qv[c] * sv[c];
+      am = fmaxf(am, fabsf(a[c]));
     }
     am = bfly_max<16>(am);
     const bool zero = !(am > 0.0f);
     const int e = zero ? 0 : ilogb_f(am) - 21;
     uint32_t l0w[CW / 4], l1w[CW / 4], l2w[CW / 4];
 #pragma unroll
-    for (int k = 0; k < CW / 4; ++k) l0w[k] = l1w[k] = l2w[k] = 0u;
+    for (int c = 0; c < CW / 4; ++c) l0w[c] = l1w[c] = l2w[c] = 0u;
     float pb = 0.0f, pd = 0.0f;
 #pragma unroll
-    for (int k = 0; k < CW; ++k) {
-      const int A = (int)rintf(ldexpf(a[k], -e));
+    for (int c = 0; c < CW; ++c) {
+      const int A = (int)rintf(ldexpf(a[c], -e));
       const int L0 = ((A + 128) & 255) - 128;
       const int A1 = (A - L0) >> 8;
       const int L1 = ((A1 + 128) & 255) - 128;
       const int L2 = (A1 - L1) >> 8;
-      l0w[k / 4] |= ((uint32_t)L0 & 255u) << (8 * (k % 4));
-      l1w[k / 4] |= ((uint32_t)L1 & 255u) << (8 * (k % 4));
-      l2w[k / 4] |= ((uint32_t)L2 & 255u) << (8 * (k % 4));
-      const float uu = fmaf(128.0f, sv[k], ov[k]);
-      pb = fmaf(qv[k], uu, pb);
-      const float kp = fmaxf(fabsf(ov[k]), fabsf(fmaf(256.0f, sv[k], ov[k])));
-      const float tt = fmaf((float)D * 0x1p-22f, kp, 0.5f * sv[k]);
-      pd = fmaf(fabsf(qv[k]), tt, pd);
+      l0w[c / 4] |= ((uint32_t)L0 & 255u) << (8 * (c % 4));
+      l1w[c / 4] |= ((uint32_t)L1 & 255u) << (8 * (c % 4));
+      l2w[c / 4] |= ((uint32_t)L2 & 255u) << (8 * (c % 4));
+      const float uu = fmaf(128.0f, sv[c], ov[c]);
+      pb = fmaf(qv[c], uu, pb);
+      const float kp = fmaxf(fabsf(ov[c]), fabsf(fmaf(256.0f, sv[c], ov[c])));
+      const float tt = fmaf((float)D * 0x1p-22f, kp, 0.5f * sv[c]);
+      pd = fmaf(fabsf(qv[c]), tt, pd);
     }
     pb = bfly_sum<16>(pb);
     pd = bfly_sum<16>(pd);
     {
       int8_t *row = &As[wave][h * 4][jc * CW];
 #pragma unroll
-      for (int k = 0; k < CW / 4; ++k) {
+      for (int c = 0; c < CW / 4; ++c) {
         const uint32_t z = 0u;
-        ((uint32_t *)(row + 0 * AST))[k] = hv ? l0w[k] : z;
-        ((uint32_t *)(row + 1 * AST))[k] = hv ? l1w[k] : z;
-        ((uint32_t *)(row + 2 * AST))[k] = hv ? l2w[k] : z;
-        ((uint32_t *)(row + 3 * AST))[k] = z;
+        ((uint32_t *)(row + 0 * AST))[c] = hv ? l0w[c] : z;
+        ((uint32_t *)(row + 1 * AST))[c] = hv ? l1w[c] : z;
+        ((uint32_t *)(row + 2 * AST))[c] = hv ? l2w[c] : z;
+        ((uint32_t *)(row + 3 * AST))[c] = z;
       }
     }
     if (hv && jc == 0) {
@@ -166,9 +188,7 @@ __global__ __launch_bounds__(256) void k_score_int8(Shape s, Tier1 t, Step w, Se
       const v4i Aop = *(const v4i *)&As[wave][lane & 15][ks * 64 + 16 * (lane >> 4)];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        v4i Bop = Bv[ks][nt] ^ (v4i){(int)0x80808080, (int)0x80808080, (int)0x80808080,
-                                     (int)0x80808080};
-        acc[nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aop, Bop, acc[nt], 0, 0, 0);
+        acc[nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aop, Bv[ks][nt], acc[nt], 0, 0, 0);
       }
     }
 
@@ -182,17 +202,17 @@ __global__ __launch_bounds__(256) void k_score_int8(Shape s, Tier1 t, Step w, Se
       const long long Dv = ((long long)acc[nt][2] << 16) + ((long long)acc[nt][1] << 8) +
                            (long long)acc[nt][0];
       x[nt] = fmaf(i64_to_f32(Dv), sc, pb);
-      const int tok = nt * 16 + jc;
-      if (tok < n) {
-        mx = fmaxf(mx, x[nt]);
-        if (hv) dst[tok] = x[nt];
-      }
+      const bool ok = nt * 16 + jc < n;
+      mx = ok ? fmaxf(mx, x[nt]) : mx;
+      if (ok && hv) dst[nt * 16 + jc] = x[nt];
     }
     mx = bfly_max<16>(mx);
     uint32_t Ls = 0u;
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-      if (nt * 16 + jc < n) Ls += (uint32_t)floorf(0x1p24f * exp2k(x[nt] - mx));
+    for (int nt = 0; nt < 4; ++nt) {
+      const uint32_t l = (uint32_t)floorf(0x1p24f * exp2k(x[nt] - mx));
+      Ls += (nt * 16 + jc < n) ? l : 0u;
+    }
     Ls = bfly_sum_u32<16>(Ls);
     if (hv && jc == 0) {
       const size_t o = ((size_t)i * s.Hq + hq) * s.NBmax + b;
@@ -200,17 +220,47 @@ __global__ __launch_bounds__(256) void k_score_int8(Shape s, Tier1 t, Step w, Se
       w.Lhat[o] = Ls;
     }
     wave_lds_sync();
+    // advance
+    const bool newgroup = (i2 != i) || (g2 != g);
+    i = i2;
+    g = g2;
+    b = b2;
+    if (newgroup && u + W < U) load_q();
   }
+}
+
+template <int D>
+int grid_score_int8(const Shape &s) {
+  static int per_cu = 0;
+  if (per_cu == 0) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_score_int8<D>, 256, 0) != hipSuccess ||
+        nb < 1)
+      nb = 1;
+    per_cu = nb;
+  }
+  return per_cu * s.ncu;
+}
+
+// Workgroups: what the device holds at once, rounded down so that the wave
+// count is a multiple of the KV head count (whole workgroups of 4 waves).
+static int int8_grid(int resident, int units, int hkv) {
+  int waves = std::min(resident * 4, ((units + 3) / 4) * 4);
+  const int step = std::lcm(4, hkv);
+  if (waves >= step) waves -= waves % step;
+  return std::max(1, waves / 4);
 }
 
 hipError_t launch_score_int8(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,
                              int layer, int maxNB, hipStream_t st) {
-  dim3 grid((maxNB + S8_BLOCKS_PER_WG - 1) / S8_BLOCKS_PER_WG, s.Hkv, tab.n);
-  if (s.d == 128)
-    hipLaunchKernelGGL(k_score_int8<128>, grid, dim3(256), 0, st, s, t, w, tab, layer);
-  else
-    hipLaunchKernelGGL(k_score_int8<64>, grid, dim3(256), 0, st, s, t, w, tab, layer);
-  return hipGetLastError();
+  (void)maxNB;
+  const int units = s.Hkv * tab.nbc[tab.n];
+  if (s.d == 128) {
+    const int grid = int8_grid(grid_score_int8<128>(s), units, s.Hkv);
+    return launch_k(k_score_int8<128>, dim3(grid), dim3(256), 0, st, s, t, w, tab, layer);
+  }
+  const int grid = int8_grid(grid_score_int8<64>(s), units, s.Hkv);
+  return launch_k(k_score_int8<64>, dim3(grid), dim3(256), 0, st, s, t, w, tab, layer);
 }
 
 // ---- FP16-key scores of blocks promoted this round ------------------------------
@@ -231,12 +281,20 @@ __global__ __launch_bounds__(256) void k_score_fp16(Shape s, Step w, SeqTab tab)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   __shared__ __align__(16) uint16_t sk[BLOCK * RST];
 
+  // all 64 rows are loaded at once (rows past n of a partial block lie inside
+  // the staging buffer; their results are masked below)
+  constexpr int NL = BLOCK * D / 8 / 256;
   const uint16_t *src = w.stage_k + (((size_t)i * s.Hkv + g) * s.Tmax + (size_t)b * BLOCK) * D;
-  for (int idx = threadIdx.x; idx < BLOCK * D / 8; idx += 256) {
-    const int r = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (r < n) v = *(const uint4 *)(src + (size_t)r * D + c8);
-    *(uint4 *)&sk[r * RST + c8] = v;
+  v4i v[NL];
+#pragma unroll
+  for (int k = 0; k < NL; ++k) {
+    const int idx = threadIdx.x + 256 * k;
+    v[k] = *(const v4i *)(src + (size_t)(idx / (D / 8)) * D + (idx % (D / 8)) * 8);
+  }
+#pragma unroll
+  for (int k = 0; k < NL; ++k) {
+    const int idx = threadIdx.x + 256 * k;
+    *(v4i *)&sk[(idx / (D / 8)) * RST + (idx % (D / 8)) * 8] = v[k];
   }
   __syncthreads();
   if (wave < s.G) {
@@ -274,11 +332,8 @@ __global__ __launch_bounds__(256) void k_score_fp16(Shape s, Step w, SeqTab tab)
 hipError_t launch_score_fp16(const Shape &s, const Step &w, const SeqTab &tab, int maxNB,
                              hipStream_t st) {
   dim3 grid(maxNB, s.Hkv, tab.n);
-  if (s.d == 128)
-    hipLaunchKernelGGL(k_score_fp16<128>, grid, dim3(256), 0, st, s, w, tab);
-  else
-    hipLaunchKernelGGL(k_score_fp16<64>, grid, dim3(256), 0, st, s, w, tab);
-  return hipGetLastError();
+  if (s.d == 128) return launch_k(k_score_fp16<128>, grid, dim3(256), 0, st, s, w, tab);
+  return launch_k(k_score_fp16<64>, grid, dim3(256), 0, st, s, w, tab);
 }
 
 // ---- test hook: the decision exponential on a vector ------------------------------
@@ -288,8 +343,7 @@ __global__ void k_exp2k(const float *x, float *y, int64_t n) {
     y[idx] = exp2k(x[idx]);
 }
 hipError_t launch_exp2k(const float *x, float *y, int64_t n, hipStream_t st) {
-  hipLaunchKernelGGL(k_exp2k, dim3(1024), dim3(256), 0, st, x, y, n);
-  return hipGetLastError();
+  return launch_k(k_exp2k, dim3(1024), dim3(256), 0, st, x, y, n);
 }
 
 }  // namespace kvq

@@ -4,8 +4,9 @@
 //
 // Per query head: fixed-point INT8 block weights
 //   What_b = floor(fl32(fl32(Lhat_b) exp2k(fl32(mhat_b - max_b mhat_b))))  (< 2^31)
-// are sorted by (What descending, block index ascending) in LDS (bitonic
-// sort of 64-bit keys What << 32 | ~b), prefix-summed in 64-bit integers, and
+// are sorted by (What descending, block index ascending) as 64-bit keys
+// What << 32 | ~b (register bitonic chunks merged in LDS), prefix-summed in
+// 64-bit integers, and
 //   K* = min k >= 1 with 10^6 sum_{i<k} What_pi(i) >= tau_ppm sum_b What_b.
 // Integer sums make the result independent of reduction order.
 // Promotion is per KV head: U_g = union of the group's top-K* sets; blocks
@@ -80,9 +81,8 @@ __global__ __launch_bounds__(SEL_NT) void k_select(Shape s, Step w, SeqTab tab, 
 hipError_t launch_select(const Shape &s, const Step &w, const SeqTab &tab, int tau_ppm, int maxNB,
                          hipStream_t st) {
   const int n2 = max(64, pow2_at_least(maxNB));
-  hipLaunchKernelGGL(k_select, dim3(s.Hq, tab.n), dim3(SEL_NT), n2 * sizeof(unsigned long long),
+  return launch_k(k_select, dim3(s.Hq, tab.n), dim3(SEL_NT), n2 * sizeof(unsigned long long),
                      st, s, w, tab, tau_ppm);
-  return hipGetLastError();
 }
 
 __global__ __launch_bounds__(1024) void k_plan_keys(Shape s, Step w, SeqTab tab) {
@@ -94,8 +94,7 @@ __global__ __launch_bounds__(1024) void k_plan_keys(Shape s, Step w, SeqTab tab)
 hipError_t launch_plan_keys(const Shape &s, const Step &w, const SeqTab &tab, int maxNB,
                             hipStream_t st) {
   (void)maxNB;
-  hipLaunchKernelGGL(k_plan_keys, dim3(s.Hkv, tab.n), dim3(1024), 0, st, s, w, tab);
-  return hipGetLastError();
+  return launch_k(k_plan_keys, dim3(s.Hkv, tab.n), dim3(1024), 0, st, s, w, tab);
 }
 
 // Compacts every group's runs into plan[]: plan[0] = #K runs, plan[1] = #V
@@ -169,13 +168,11 @@ __global__ void k_reset(Shape s, Step w, int n) {
 }
 
 hipError_t launch_reset(const Shape &s, const Step &w, int n, hipStream_t st) {
-  hipLaunchKernelGGL(k_reset, dim3(64), dim3(256), 0, st, s, w, n);
-  return hipGetLastError();
+  return launch_k(k_reset, dim3(64), dim3(256), 0, st, s, w, n);
 }
 
 hipError_t launch_gather_plan(const Shape &s, const Step &w, int n, hipStream_t st) {
-  hipLaunchKernelGGL(k_gather_plan, dim3(1), dim3(1024), 0, st, s, w, n);
-  return hipGetLastError();
+  return launch_k(k_gather_plan, dim3(1), dim3(1024), 0, st, s, w, n);
 }
 
 }  // namespace kvq

@@ -32,7 +32,7 @@
  *     message of the last failing call on that context.
  *   - Block size is 64 tokens; value groups are 32 consecutive channels of a
  *     token.  head_dim must be 64 or 128; n_q_heads / n_kv_heads must be 1,
- *     2 or 4.
+ *     2 or 4; n_kv_heads at most 128.
  */
 #ifndef KVQ_H
 #define KVQ_H
@@ -117,16 +117,20 @@ typedef struct kvq_step_stats {
     int32_t key_rounds;            /* evaluation rounds of the controller         */
     int32_t host_syncs;            /* host round-trips taken                      */
     int32_t level_count[5];        /* heads per ladder level                      */
-    /* kernel times (KVQ_FLAG_TIMING), milliseconds, from HIP events recorded
-       around each launch on the stream it runs on */
-    float ms_score_int8;           /* INT8 scoring pass                           */
-    float ms_select;               /* top-K* selection and promotion planning     */
+    /* times (KVQ_FLAG_TIMING), milliseconds.  Kernel entries are sums of
+       kernel durations, each stamped by the runtime at the kernel's own
+       start and end (hipExtLaunchKernel events); copies are bracketed by
+       events on the copy stream. */
+    float ms_score_int8;           /* INT8 scoring kernel                         */
+    float ms_select;               /* top-K* selection, union planning, run lists */
     float ms_score_fp16;           /* FP16 scoring of promoted blocks (all rounds)*/
-    float ms_control;              /* controller rounds                           */
+    float ms_control;              /* controller kernels, all rounds              */
     float ms_copy;                 /* host->device copies (copy stream)           */
-    float ms_decode;               /* mixed split-K decode + combine              */
-    float ms_dense;                /* dense fallback decode                       */
+    float ms_decode;               /* mixed split-K decode kernel                 */
+    float ms_dense;                /* dense fallback decode kernel                */
     float ms_total;                /* whole call, first launch to last            */
+    float ms_combine;              /* split-K combine kernel                      */
+    float ms_misc;                 /* reset, q scaling, plan export, finalize     */
 } kvq_step_stats;
 
 /* One decode step at one layer (Méthodologie §2-§3): attends over every
