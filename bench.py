@@ -50,6 +50,8 @@ def parse():
     p.add_argument("--layers", type=int, default=32)
     p.add_argument("--ctx", type=int, default=131072)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-comparators", action="store_true",
+                   help="skip the dense FP16 (device-resident) and naive INT8/INT4 comparators")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (counter calibration)")
     return p.parse_args()
@@ -114,7 +116,9 @@ def main():
         f"{ctx.host_pinned_bytes / 2**30:.2f} GiB ({time.time() - t_setup:.1f} s)")
     gen = torch.Generator(device=dev)
     keep = not a.no_cpu_baseline
+    comp = not a.no_comparators
     host0 = None
+    dense_k, dense_v = [], []          # FP16 caches in device memory (comparator)
     for layer in range(L):
         gen.manual_seed(4_000_000 + layer)
         K = torch.randn((T0, Hkv, d), generator=gen, device=dev, dtype=torch.float32)
@@ -124,6 +128,13 @@ def main():
         V = torch.randn((T0, Hkv, d), generator=gen, device=dev, dtype=torch.float32)
         K, V = K.half(), V.half()
         ctx.append(layer, [0], [T0], K, V)
+        if comp:
+            kd = torch.zeros((1, max_tokens, Hkv, d), dtype=torch.float16, device=dev)
+            vd = torch.zeros_like(kd)
+            kd[0, :T0] = K
+            vd[0, :T0] = V
+            dense_k.append(kd)
+            dense_v.append(vd)
         if keep and layer == 0:
             host0 = (K.cpu().numpy().view(np.uint16), V.cpu().numpy().view(np.uint16))
         del K, V
@@ -147,6 +158,49 @@ def main():
     log(f"prefill {L} layers x {T0} tokens done ({time.time() - t_setup:.1f} s)")
 
     recs = []
+
+    def comparators(T_final):
+        """Dense FP16 attention over a device-resident cache and the naive
+        INT8/INT4 pass over tier 1, on the same layers, lengths and queries
+        as the timed certified steps (one untimed warm pass each)."""
+        for layer in range(L):
+            for s in range(n_total):
+                dense_k[layer][0, T0 + s] = k1s[s][layer][0]
+                dense_v[layer][0, T0 + s] = v1s[s][layer][0]
+        o_d = torch.empty((1, Hq, d), dtype=torch.float32, device=dev)
+        res = {}
+        for name in ("dense", "naive"):
+            def run(s):
+                for layer in range(L):
+                    if name == "dense":
+                        ctx.dense_decode([T_final], qs[s][layer], dense_k[layer], dense_v[layer],
+                                         out=o_d)
+                    else:
+                        ctx.decode_naive(layer, [0], qs[s][layer], out=o_d)
+            run(0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for s in range(a.warmup, n_total):
+                run(s)
+            e1.record()
+            e1.synchronize()
+            res[name] = e0.elapsed_time(e1) / (a.steps * L)
+        dense_bytes = T_final * Hkv * 4 * d
+        return {
+            "dense_fp16_vram": {
+                "what": "dense decode attention, FP16 K/V resident in device memory (same "
+                        "layers, lengths and queries)",
+                "ms_per_layer": round(res["dense"], 5),
+                "kv_tokens_per_s": round(T_final / (res["dense"] * 1e-3), 1),
+                "hbm_GBps": round(dense_bytes / (res["dense"] * 1e-3) / 1e9, 1),
+                "hbm_frac": round(dense_bytes / (res["dense"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
+            "naive_int8_int4": {
+                "what": "uncertified INT8 scores + INT4 values over tier 1 (no selection, "
+                        "promotion, bounds or ladder)",
+                "ms_per_layer": round(res["naive"], 5),
+                "kv_tokens_per_s": round(T_final / (res["naive"] * 1e-3), 1)},
+        }
 
     def step(s):
         for layer in range(L):
@@ -215,6 +269,22 @@ def main():
     levels = [sum(r["level_count"][k] for r in recs) for k in range(5)]
 
     cpu = None
+    comps = None
+    if comp:
+        T_final = ctx.seq_len(0, 0)
+        comps = comparators(T_final)
+        cert_ms = wall / a.steps * 1e3 / L
+        kern_ms = sum(per_kernel[k] for k in ("ms_score_int8", "ms_select", "ms_score_fp16",
+                                             "ms_control", "ms_decode", "ms_combine", "ms_dense",
+                                             "ms_misc"))
+        dms = comps["dense_fp16_vram"]["ms_per_layer"]
+        comps["certified_ms_per_layer"] = round(cert_ms, 5)
+        comps["certified_kernels_ms_per_layer"] = round(kern_ms, 5)
+        comps["certified_over_dense"] = round(cert_ms / dms, 2)
+        comps["certified_kernels_over_dense"] = round(kern_ms / dms, 2)
+        comps["naive_over_dense"] = round(comps["naive_int8_int4"]["ms_per_layer"] / dms, 2)
+        del dense_k[:], dense_v[:]
+
     parity = None
     if keep:
         import oracle
@@ -264,7 +334,8 @@ def main():
                    "head_dim": d, "tau_cov": 0.995},
         "roofline": roofline, "cpu_baseline": cpu,
         "quantized_pass": quantized_pass, "per_kernel_ms": {k: round(v, 5) for k, v in per_kernel.items()},
-        "promotion": promo, "level_counts": levels, "parity_sample": parity,
+        "promotion": promo, "level_counts": levels, "comparators": comps,
+        "parity_sample": parity,
         "tier1_vram_frac_of_fp16": round(t1b / (4 * d), 4),
     }
     print(json.dumps(line), flush=True)

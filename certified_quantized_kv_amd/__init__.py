@@ -68,6 +68,8 @@ _SIGS = {
     "kvq_destroy": (None, [P]),
     "kvq_append": (I32, [P, I32, I32, P, P, P, P, P]),
     "kvq_decode_step": (I32, [P, I32, I32, P, P, P, P, P, P, P, P]),
+    "kvq_decode_naive": (I32, [P, I32, I32, P, P, P, P]),
+    "kvq_dense_decode": (I32, [P, I32, P, P, P, P, P, P]),
     "kvq_reset_seq": (I32, [P, I32]),
     "kvq_seq_len": (I64, [P, I32, I32]),
     "kvq_strerror": (ctypes.c_char_p, [I32]),
@@ -215,6 +217,39 @@ class Context:
                                   ctypes.byref(ss) if ss is not None else None, _stream())
         self._check(st, "kvq_decode_step")
         return out, e_key, e_val, level, (ss.as_dict() if ss is not None else None)
+
+    def decode_naive(self, layer, seq_ids, q, out=None):
+        """Uncertified INT8/INT4 attention over tier 1 (comparator); returns out f32."""
+        import torch
+        n = len(seq_ids)
+        if q.shape != (n, self.Hq, self.d):
+            raise ValueError(f"q shape {tuple(q.shape)} != {(n, self.Hq, self.d)}")
+        out = torch.empty((n, self.Hq, self.d), dtype=torch.float32, device=q.device) \
+            if out is None else out
+        self._check(_lib.kvq_decode_naive(self._ctx, layer, n, _i32(seq_ids),
+                                          _dev(q, torch.float16, "q"),
+                                          _dev(out, torch.float32, "out"), _stream()),
+                    "kvq_decode_naive")
+        return out
+
+    def dense_decode(self, seq_lens, q, k, v, out=None):
+        """Dense FP16 attention over a device-resident cache (comparator).
+        q fp16 [n, Hq, d]; k, v fp16 [n, max_tokens, Hkv, d]; returns out f32."""
+        import torch
+        n = len(seq_lens)
+        if q.shape != (n, self.Hq, self.d):
+            raise ValueError(f"q shape {tuple(q.shape)} != {(n, self.Hq, self.d)}")
+        want = (n, self.cfg.max_tokens, self.Hkv, self.d)
+        if tuple(k.shape) != want or tuple(v.shape) != want:
+            raise ValueError(f"k/v shape must be {want}")
+        out = torch.empty((n, self.Hq, self.d), dtype=torch.float32, device=q.device) \
+            if out is None else out
+        self._check(_lib.kvq_dense_decode(self._ctx, n, _i32(seq_lens),
+                                          _dev(q, torch.float16, "q"), _dev(k, torch.float16, "k"),
+                                          _dev(v, torch.float16, "v"),
+                                          _dev(out, torch.float32, "out"), _stream()),
+                    "kvq_dense_decode")
+        return out
 
     def export_tier1(self, layer, seq, g):
         """Tier 1 of one (layer, slot, KV head) in plain layouts (numpy)."""

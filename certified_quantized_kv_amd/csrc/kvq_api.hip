@@ -577,7 +577,7 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
   tm.open(TC_DECODE);
   HIPCK(ctx, launch_decode(s, ctx->t, w, tab, layer, maxNB, false, st));
   tm.open(TC_COMBINE);
-  HIPCK(ctx, launch_combine(s, w, tab, out, st));
+  HIPCK(ctx, launch_combine(s, w, tab, out, 0, st));
   tm.close();
   if (timing) HIPCK(ctx, hipEventRecord(ctx->ev_tot[1], st));
 
@@ -618,6 +618,69 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
       stats->ms_total = a;
     }
   }
+  return KVQ_OK;
+}
+
+// ---- comparators ------------------------------------------------------------------
+
+kvq_status kvq_decode_naive(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t *seq_ids,
+                            const void *q, float *out, void *stream) {
+  if (!ctx) return KVQ_EINVAL;
+  if (layer < 0 || layer >= ctx->cfg.n_layers) return fail(ctx, KVQ_ESTATE, "bad layer");
+  if (!valid_seqs(ctx, n, seq_ids)) return fail(ctx, KVQ_EINVAL, "bad sequence list");
+  if (!q || !out) return fail(ctx, KVQ_EINVAL, "null argument");
+  const Shape &s = ctx->s;
+  SeqTab tab;
+  memset(&tab, 0, sizeof(tab));
+  tab.n = n;
+  int maxNB = 0;
+  for (int i = 0; i < n; ++i) {
+    const int64_t T = ctx->T[(size_t)seq_ids[i] * s.L + layer];
+    if (T < 1) return fail(ctx, KVQ_ESTATE, "decode on an empty sequence");
+    tab.slot[i] = seq_ids[i];
+    tab.T[i] = (int)T;
+    tab.nbc[i + 1] = tab.nbc[i] + (int)((T + BLOCK - 1) / BLOCK);
+    maxNB = std::max(maxNB, (int)((T + BLOCK - 1) / BLOCK));
+  }
+  hipStream_t st = (hipStream_t)stream;
+  Step &w = ctx->w;
+  // empty U and V: INT8 scores and INT4 values for every block
+  HIPCK(ctx, launch_reset(s, w, n, st));
+  const float C = (float)(1.4426950408889634 / sqrt((double)s.d));
+  HIPCK(ctx, launch_qprep(s, w, n, (const uint16_t *)q, C, st));
+  HIPCK(ctx, launch_score_int8(s, ctx->t, w, tab, layer, maxNB, st));
+  HIPCK(ctx, launch_decode(s, ctx->t, w, tab, layer, maxNB, false, st));
+  HIPCK(ctx, launch_combine(s, w, tab, out, 1, st));
+  return KVQ_OK;
+}
+
+kvq_status kvq_dense_decode(kvq_ctx *ctx, int32_t n, const int32_t *seq_lens, const void *q,
+                            const void *k, const void *v, float *out, void *stream) {
+  if (!ctx) return KVQ_EINVAL;
+  if (n < 1 || n > ctx->cfg.max_batch || n > MAX_CALL || !seq_lens)
+    return fail(ctx, KVQ_EINVAL, "bad sequence count");
+  if (!q || !k || !v || !out) return fail(ctx, KVQ_EINVAL, "null argument");
+  const Shape &s = ctx->s;
+  DenseArgs a;
+  memset(&a, 0, sizeof(a));
+  SeqTab tab;
+  memset(&tab, 0, sizeof(tab));
+  a.n = tab.n = n;
+  int maxNB = 0;
+  for (int i = 0; i < n; ++i) {
+    if (seq_lens[i] < 1 || seq_lens[i] > ctx->cfg.max_tokens)
+      return fail(ctx, KVQ_EINVAL, "sequence length out of range");
+    a.T[i] = tab.T[i] = seq_lens[i];
+    tab.nbc[i + 1] = tab.nbc[i] + (seq_lens[i] + BLOCK - 1) / BLOCK;
+    maxNB = std::max(maxNB, (seq_lens[i] + BLOCK - 1) / BLOCK);
+  }
+  a.tcap = ctx->cfg.max_tokens;
+  a.q = (const uint16_t *)q;
+  a.k = (const uint16_t *)k;
+  a.v = (const uint16_t *)v;
+  hipStream_t st = (hipStream_t)stream;
+  HIPCK(ctx, launch_dense_vram(s, ctx->w, a, maxNB, st));
+  HIPCK(ctx, launch_combine(s, ctx->w, tab, out, 2, st));
   return KVQ_OK;
 }
 

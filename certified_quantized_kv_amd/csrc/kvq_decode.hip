@@ -323,14 +323,14 @@ hipError_t launch_decode(const Shape &s, const Tier1 &t, const Step &w, const Se
 // the dense partials, the others the mixed ones.  256 threads: the chunk
 // maxima and weights first, then 256/d groups of channels-threads each sum a
 // share of the chunks; the shares are added in LDS.
-__global__ __launch_bounds__(256) void k_combine(Shape s, Step w, SeqTab tab, float *out) {
+__global__ __launch_bounds__(256) void k_combine(Shape s, Step w, SeqTab tab, float *out, int mode) {
   __shared__ float fw[1024];
   __shared__ float red[256];
   __shared__ float sMl[2];
   const int i = blockIdx.y, hq = blockIdx.x;
   const int D = s.d, G = s.G, g = hq / G, h = hq % G;
   const int NB = (tab.T[i] + BLOCK - 1) / BLOCK, nch = (NB + DEC_CB - 1) / DEC_CB;
-  const bool dense = w.hlevel[(size_t)i * s.Hq + hq] >= 3;
+  const bool dense = mode == 2 || (mode == 0 && w.hlevel[(size_t)i * s.Hq + hq] >= 3);
   const float *part = (dense ? w.partd : w.part) + (((size_t)i * s.Hkv + g) * s.nchmax * G + h) * (D + 2);
   const size_t stride = (size_t)G * (D + 2);
   float m = -INFINITY;
@@ -364,9 +364,9 @@ __global__ __launch_bounds__(256) void k_combine(Shape s, Step w, SeqTab tab, fl
   }
 }
 
-hipError_t launch_combine(const Shape &s, const Step &w, const SeqTab &tab, float *out,
+hipError_t launch_combine(const Shape &s, const Step &w, const SeqTab &tab, float *out, int mode,
                           hipStream_t st) {
-  return launch_k(k_combine, dim3(s.Hq, tab.n), dim3(256), 0, st, s, w, tab, out);
+  return launch_k(k_combine, dim3(s.Hq, tab.n), dim3(256), 0, st, s, w, tab, out, mode);
 }
 
 }  // namespace kvq

@@ -80,6 +80,15 @@ struct Shape {
   int ncu;                          // compute units of the device
 };
 
+// Arguments of the dense comparator: FP16 q [n][Hq][d], K and V
+// [n][tcap][Hkv][d] in device memory, T[i] tokens of sequence i.
+struct DenseArgs {
+  int n;
+  int T[MAX_CALL];
+  long long tcap;
+  const uint16_t *q, *k, *v;
+};
+
 struct Thresh {
   int tau_ppm, rho_ppm, R1, frac_ppm;
   double eps_key, v_tol;
@@ -161,8 +170,11 @@ hipError_t launch_finalize(const Shape &s, const Step &w, const SeqTab &tab, con
                            float *e_key, float *e_val, int8_t *level, hipStream_t st);
 hipError_t launch_decode(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,
                          int layer, int maxNB, bool dense, hipStream_t st);
-hipError_t launch_combine(const Shape &s, const Step &w, const SeqTab &tab, float *out,
+// mode 0: partials chosen by each head's level; 1: mixed partials; 2: dense
+hipError_t launch_combine(const Shape &s, const Step &w, const SeqTab &tab, float *out, int mode,
                           hipStream_t st);
+hipError_t launch_dense_vram(const Shape &s, const Step &w, const DenseArgs &a, int maxNB,
+                             hipStream_t st);
 hipError_t launch_exp2k(const float *x, float *y, int64_t n, hipStream_t st);
 hipError_t launch_export_kcodes(const Shape &s, const Tier1 &t, size_t u, int T, uint8_t *dst,
                                 hipStream_t st);

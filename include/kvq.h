@@ -152,6 +152,31 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n_seqs, const in
                            const void *q, float *out, float *e_key, float *e_val, int8_t *level,
                            kvq_step_stats *stats, void *stream);
 
+/* Comparators of the certified step (the two reference points of the pages'
+ * cost comparison, Résultats: the naive INT8/INT4 baseline and dense
+ * attention).  Both reuse the context's per-step scratch, so calls on one
+ * context must not overlap any other decode call of that context.
+ *
+ * kvq_decode_naive: uncertified attention over tier 1 alone -- INT8 scores
+ * and dequantized INT4 values for every token, no selection, promotion,
+ * bounds or ladder.  Arguments as in kvq_decode_step (seq_ids host, q device
+ * fp16 [n_seqs][n_q_heads][head_dim], out device f32 likewise).
+ *
+ * kvq_dense_decode: standard dense decode attention over an FP16 KV cache
+ * that the caller holds in device memory:
+ *   seq_lens (host)  [n_seqs], 1 <= seq_lens[i] <= max_tokens (of the config)
+ *   q        (device) fp16 [n_seqs][n_q_heads][head_dim]
+ *   k, v     (device) fp16 [n_seqs][max_tokens][n_kv_heads][head_dim]; token t
+ *            of sequence i at ((i * max_tokens + t) * n_kv_heads + g) * head_dim
+ *   out      (device) f32  [n_seqs][n_q_heads][head_dim]
+ * Softmax scale 1/sqrt(head_dim); fp32 accumulation.  The context supplies
+ * the shape (heads, head_dim, max_tokens, max_batch >= n_seqs) and scratch;
+ * its tiers are not read. */
+kvq_status kvq_decode_naive(kvq_ctx *ctx, int32_t layer, int32_t n_seqs, const int32_t *seq_ids,
+                            const void *q, float *out, void *stream);
+kvq_status kvq_dense_decode(kvq_ctx *ctx, int32_t n_seqs, const int32_t *seq_lens, const void *q,
+                            const void *k, const void *v, float *out, void *stream);
+
 /* Forgets every token of a slot at every layer. */
 kvq_status kvq_reset_seq(kvq_ctx *ctx, int32_t seq_id);
 

@@ -19,4 +19,4 @@ from .method import (Config, build_tier1, query, int8_scores, fp16_scores, ingre
                      weights, gfactors, attend, value_rows, exp2k, exp2k_coeffs, h2f,
                      rank_order, k_star, ranking_consistent, e_key, e_val_parts, w_bounds,
                      group_step, mixed_output, dense_output, decode_step, f32_up,
-                     BLOCK, VGROUP)
+                     naive_output, dense_attention, BLOCK, VGROUP)

@@ -422,6 +422,22 @@ def dense_output(sp, t1, v16):
     return attend(sp, val)
 
 
+def naive_output(qp, t1, v16):
+    """The uncertified quantized baseline the pages compare against (Résultats:
+    naive INT8/INT4 attention): INT8 scores and dequantized INT4 values for
+    every token, fp64 softmax; no selection, promotion, bounds or ladder."""
+    shat, _ = int8_scores(qp, t1)
+    return attend(shat, value_rows(t1, v16))
+
+
+def dense_attention(q16, k16, v16):
+    """Dense attention over FP16 keys and values (Méthodologie §1: the exact
+    computation the fallback returns): canonical FP16-key scores, fp64
+    softmax and fp64 P.V.  q16 [G][d], k16 and v16 [T][d] (uint16)."""
+    sp = fp16_scores(query(q16), k16)
+    return attend(sp, h2f(c_array(v16, np.uint16)).astype(np.float64))
+
+
 @dataclass
 class StepResult:
     out: np.ndarray          # [Hq][d] fp64

@@ -225,3 +225,50 @@ def test_needle_block_ranked_first(orc):
             assert tr.pi[i][0] == needles[i]
             W = tr.What[i].astype(np.float64)
             assert W[needles[i]] / W.sum() > 0.5
+
+
+def test_dense_attention_is_textbook_softmax(orc):
+    """The dense comparator's definition: softmax(q k^T / sqrt(d)) v over the
+    FP16 keys and values, against a plain fp64 numpy evaluation."""
+    r = np.random.default_rng(11)
+    for T, G, d in ((1, 2, 64), (333, 4, 128)):
+        q16 = r.standard_normal((G, d)).astype(np.float16).view(np.uint16)
+        k16 = (r.standard_normal((T, d)) * 2).astype(np.float16).view(np.uint16)
+        v16 = r.standard_normal((T, d)).astype(np.float16).view(np.uint16)
+        q, k, v = f16_to_f64(q16), f16_to_f64(k16), f16_to_f64(v16)
+        s = q @ k.T / math.sqrt(d)
+        p = np.exp(s - s.max(1, keepdims=True))
+        ref = (p @ v) / p.sum(1, keepdims=True)
+        assert np.abs(orc.dense_attention(q16, k16, v16) - ref).max() < 1e-5
+
+
+def test_naive_output_on_grid_equals_dense(orc):
+    """Keys on the INT8 grid of their block (scale 2^-5, offset -4, codes 0
+    and 255 present per channel) and values on the INT4 grid of their group
+    (scale 1/8, offset -1, codes 0 and 15 present): quantization is lossless,
+    so the naive INT8/INT4 output equals dense attention up to score
+    rounding; on off-grid data it does not (the naive path is uncertified)."""
+    r = np.random.default_rng(5)
+    T, G, d = 300, 4, 64
+    kc = r.integers(0, 256, size=(T, d))
+    for b in range(0, T, 64):
+        kc[b, :], kc[min(b + 1, T - 1), :] = 0, 255
+    vc = r.integers(0, 16, size=(T, d))
+    vc[:, 0::32], vc[:, 1::32] = 0, 15
+    k = -4.0 + kc / 32.0
+    v = -1.0 + vc / 8.0
+    k16 = k.astype(np.float16).view(np.uint16)
+    v16 = v.astype(np.float16).view(np.uint16)
+    assert np.array_equal(f16_to_f64(k16), k) and np.array_equal(f16_to_f64(v16), v)
+    t1 = orc.build_tier1(k16, v16)
+    assert np.array_equal(t1["kcode"], kc.astype(np.uint8))
+    assert np.all(t1["eta"] == 0)
+    q16 = r.standard_normal((G, d)).astype(np.float16).view(np.uint16)
+    naive = orc.naive_output(orc.query(q16), t1, v16)
+    dense = orc.dense_attention(q16, k16, v16)
+    assert np.abs(naive - dense).max() < 1e-5
+    # off-grid keys: the naive output moves away from dense
+    k2 = (r.standard_normal((T, d)) * 3).astype(np.float16).view(np.uint16)
+    t2 = orc.build_tier1(k2, v16)
+    gap = np.abs(orc.naive_output(orc.query(q16), t2, v16) - orc.dense_attention(q16, k2, v16)).max()
+    assert gap > 1e-4
