@@ -50,6 +50,8 @@ def parse():
     p.add_argument("--layers", type=int, default=32)
     p.add_argument("--ctx", type=int, default=131072)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-residency", action="store_true",
+                   help="skip the second run with promoted FP16 keys kept in device memory")
     p.add_argument("--no-comparators", action="store_true",
                    help="skip the dense FP16 (device-resident) and naive INT8/INT4 comparators")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -119,25 +121,29 @@ def main():
     comp = not a.no_comparators
     host0 = None
     dense_k, dense_v = [], []          # FP16 caches in device memory (comparator)
-    for layer in range(L):
-        gen.manual_seed(4_000_000 + layer)
-        K = torch.randn((T0, Hkv, d), generator=gen, device=dev, dtype=torch.float32)
-        for g in range(Hkv):
-            ch = torch.from_numpy(S.outlier_channels(w, layer, g)).to(dev)
-            K[:, g, ch] *= w.outlier_scale
-        V = torch.randn((T0, Hkv, d), generator=gen, device=dev, dtype=torch.float32)
-        K, V = K.half(), V.half()
-        ctx.append(layer, [0], [T0], K, V)
-        if comp:
-            kd = torch.zeros((1, max_tokens, Hkv, d), dtype=torch.float16, device=dev)
-            vd = torch.zeros_like(kd)
-            kd[0, :T0] = K
-            vd[0, :T0] = V
-            dense_k.append(kd)
-            dense_v.append(vd)
-        if keep and layer == 0:
-            host0 = (K.cpu().numpy().view(np.uint16), V.cpu().numpy().view(np.uint16))
-        del K, V
+    def prefill(cx, keep_dense, keep_host0):
+        nonlocal host0
+        for layer in range(L):
+            gen.manual_seed(4_000_000 + layer)
+            K = torch.randn((T0, Hkv, d), generator=gen, device=dev, dtype=torch.float32)
+            for g in range(Hkv):
+                ch = torch.from_numpy(S.outlier_channels(w, layer, g)).to(dev)
+                K[:, g, ch] *= w.outlier_scale
+            V = torch.randn((T0, Hkv, d), generator=gen, device=dev, dtype=torch.float32)
+            K, V = K.half(), V.half()
+            cx.append(layer, [0], [T0], K, V)
+            if keep_dense:
+                kd = torch.zeros((1, max_tokens, Hkv, d), dtype=torch.float16, device=dev)
+                vd = torch.zeros_like(kd)
+                kd[0, :T0] = K
+                vd[0, :T0] = V
+                dense_k.append(kd)
+                dense_v.append(vd)
+            if keep_host0 and layer == 0:
+                host0 = (K.cpu().numpy().view(np.uint16), V.cpu().numpy().view(np.uint16))
+            del K, V
+
+    prefill(ctx, comp, keep)
     # inputs of every step, resident before timing
     qs, k1s, v1s = [], [], []
     for s in range(n_total):
@@ -158,6 +164,25 @@ def main():
     log(f"prefill {L} layers x {T0} tokens done ({time.time() - t_setup:.1f} s)")
 
     recs = []
+
+    def run_steps(cx, rec):
+        def step(s):
+            for layer in range(L):
+                cx.append(layer, [0], [1], k1s[s][layer], v1s[s][layer])
+                _, _, _, _, st = cx.decode_step(layer, [0], qs[s][layer], out, ek, ev, lv,
+                                                stats=True)
+                st["T"] = cx.seq_len(layer, 0)
+                rec.append(st)
+        for s in range(a.warmup):
+            step(s)
+        torch.cuda.synchronize()
+        rec.clear()
+        t0 = time.time()
+        for s in range(a.warmup, n_total):
+            step(s)
+            log(f"step {s - a.warmup + 1}/{a.steps} done")
+        torch.cuda.synchronize()
+        return time.time() - t0
 
     def comparators(T_final):
         """Dense FP16 attention over a device-resident cache and the naive
@@ -202,23 +227,8 @@ def main():
                 "kv_tokens_per_s": round(T_final / (res["naive"] * 1e-3), 1)},
         }
 
-    def step(s):
-        for layer in range(L):
-            ctx.append(layer, [0], [1], k1s[s][layer], v1s[s][layer])
-            _, _, _, _, st = ctx.decode_step(layer, [0], qs[s][layer], out, ek, ev, lv, stats=True)
-            st["T"] = ctx.seq_len(layer, 0)
-            recs.append(st)
-
-    for s in range(a.warmup):
-        step(s)
-    torch.cuda.synchronize()
-    recs.clear()
-    t0 = time.time()
-    for s in range(a.warmup, n_total):
-        step(s)
-        log(f"step {s - a.warmup + 1}/{a.steps} done")
-    torch.cuda.synchronize()
-    wall = time.time() - t0
+    wall = run_steps(ctx, recs)
+    out_default = out.clone()
     kv_tokens = sum(r["T"] for r in recs)
     value = kv_tokens / wall
     n = len(recs)
@@ -323,6 +333,30 @@ def main():
                                                           ref.e_val.view(np.uint32))),
                   "max_abs_out_err": err, "tol": 2e-3}
 
+    resid = None
+    if not a.no_residency:
+        # the same steps on a context whose promoted FP16 keys stay in device
+        # memory across steps (copied once, again only after an append)
+        ctx.close()
+        cx2 = kvq.Context(L, 1, Hq, Hkv, d, max_tokens, timing=True, resident_keys=True)
+        prefill(cx2, False, False)
+        recs2 = []
+        wall2 = run_steps(cx2, recs2)
+        n2 = len(recs2)
+        dense_bytes = L * max_tokens * Hkv * 4 * d
+        resid = {
+            "what": "same steps with KVQ_FLAG_RESIDENT_KEYS: promoted FP16 key blocks kept in "
+                    "device memory across steps",
+            "value": round(sum(r["T"] for r in recs2) / wall2, 1), "unit": "KV tokens/s",
+            "ms_per_step": round(wall2 / a.steps * 1e3, 3),
+            "h2d_MB_per_layer": round(sum(r["h2d_bytes"] for r in recs2) / n2 / 1e6, 3),
+            "ms_copy_per_layer": round(sum(r["ms_copy"] for r in recs2) / n2, 5),
+            "device_GiB": round(cx2.device_bytes / 2**30, 2),
+            "device_frac_of_dense_fp16_cache": round(cx2.device_bytes / dense_bytes, 3),
+            "last_output_bit_equal_to_default": bool(torch.equal(out, out_default)),
+        }
+        cx2.close()
+
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "KV tokens/s", "n_gpus": 1,
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(wall / a.steps * 1e3, 3),
@@ -334,7 +368,7 @@ def main():
                    "head_dim": d, "tau_cov": 0.995},
         "roofline": roofline, "cpu_baseline": cpu,
         "quantized_pass": quantized_pass, "per_kernel_ms": {k: round(v, 5) for k, v in per_kernel.items()},
-        "promotion": promo, "level_counts": levels, "comparators": comps,
+        "promotion": promo, "level_counts": levels, "comparators": comps, "residency": resid,
         "parity_sample": parity,
         "tier1_vram_frac_of_fp16": round(t1b / (4 * d), 4),
     }

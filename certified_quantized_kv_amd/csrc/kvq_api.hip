@@ -49,6 +49,7 @@ struct kvq_ctx {
   hipEvent_t ev_c[32] = {};    // copy timing pairs
   hipEvent_t ev_tot[2] = {};
   unsigned long long *plan_host = nullptr;
+  std::vector<uint8_t> kres;  // [unit][NBmax]: FP16 keys of the block valid in staging
   size_t plan_cap = 0;
   size_t plan_words = 0;
   int last_n = 0, last_layer = -1;
@@ -241,6 +242,7 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out) {
   s.runmax = s.NBmax / 2 + 1;
   s.nchmax = (s.NBmax + DEC_CB - 1) / DEC_CB;
   s.B = c.max_batch;
+  s.kres = (c.flags & KVQ_FLAG_RESIDENT_KEYS) ? 1 : 0;
   s.ncu = 0;
   if (hipDeviceGetAttribute(&s.ncu, hipDeviceAttributeMultiprocessorCount, x->device) !=
           hipSuccess ||
@@ -259,6 +261,7 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out) {
   x->T.assign((size_t)c.max_batch * c.n_layers, 0);
 
   const size_t NU = (size_t)c.max_batch * c.n_layers * c.n_kv_heads;
+  if (s.kres) x->kres.assign(NU * s.NBmax, 0);
   const size_t d = s.d, NBm = s.NBmax, Tm = s.Tmax;
   Tier1 &t = x->t;
   Step &w = x->w;
@@ -303,7 +306,7 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out) {
   DA(w.nruns, B * Hkv * 2 * 4);
   x->plan_words = 4 + B * Hkv * 2 * (size_t)s.runmax;
   DA(w.plan, x->plan_words * 8);
-  DA(w.stage_k, B * Hkv * Tm * d * 2);
+  DA(w.stage_k, (s.kres ? NU : B * Hkv) * Tm * d * 2);
   DA(w.stage_v, B * Hkv * Tm * d * 2);
   DA(w.part, B * Hkv * (size_t)s.nchmax * G * (d + 2) * 4);
   DA(w.partd, B * Hkv * (size_t)s.nchmax * G * (d + 2) * 4);
@@ -373,6 +376,9 @@ kvq_status kvq_reset_seq(kvq_ctx *ctx, int32_t seq) {
   const Shape &s = ctx->s;
   for (int l = 0; l < s.L; ++l) {
     ctx->T[(size_t)seq * s.L + l] = 0;
+    if (s.kres)
+      std::fill(ctx->kres.begin() + unit_of(s, seq, l, 0) * s.NBmax,
+                ctx->kres.begin() + unit_of(s, seq, l, s.Hkv) * s.NBmax, (uint8_t)0);
     const size_t u0 = unit_of(s, seq, l, 0);
     HIPCK(ctx, hipMemsetD32(reinterpret_cast<hipDeviceptr_t>(ctx->t.vmin + u0 * s.d), 0xff800000u,
                             (size_t)s.Hkv * s.d));
@@ -412,7 +418,17 @@ kvq_status kvq_append(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t *seq
     HIPCK(ctx, launch_append(s, ctx->t, a, (const uint16_t *)k, (const uint16_t *)v, max_blk,
                              (hipStream_t)stream));
   }
-  for (int i = 0; i < n; ++i) ctx->T[(size_t)seq_ids[i] * s.L + layer] += n_new[i];
+  for (int i = 0; i < n; ++i) {
+    // blocks that took new tokens no longer match a resident copy
+    if (s.kres && n_new[i] > 0) {
+      const int64_t Told = ctx->T[(size_t)seq_ids[i] * s.L + layer];
+      for (int g = 0; g < s.Hkv; ++g) {
+        uint8_t *r = ctx->kres.data() + unit_of(s, seq_ids[i], layer, g) * s.NBmax;
+        for (int64_t b = Told / BLOCK; b <= (Told + n_new[i] - 1) / BLOCK; ++b) r[b] = 0;
+      }
+    }
+    ctx->T[(size_t)seq_ids[i] * s.L + layer] += n_new[i];
+  }
   return KVQ_OK;
 }
 
@@ -451,6 +467,28 @@ kvq_status issue_copies(kvq_ctx *c, const SeqTab &tab, int layer, const Plan &p,
     const int ig = (int)((e >> 32) & 0xffffu), kind = (int)((e >> 48) & 1u);
     const int i = ig / s.Hkv, g = ig % s.Hkv;
     const size_t u = unit_of(s, tab.slot[i], layer, g);
+    if (kind == 0 && s.kres) {
+      // resident keys: copy the sub-runs not already in device memory
+      uint8_t *res = c->kres.data() + u * s.NBmax;
+      uint16_t *area = c->w.stage_k + u * s.Tmax * s.d;
+      const uint16_t *src = c->t2k_host + u * s.Tmax * s.d;
+      int b = start;
+      while (b < start + len) {
+        if (res[b]) {
+          ++b;
+          continue;
+        }
+        int e = b;
+        while (e < start + len && !res[e]) res[e++] = 1;
+        const size_t off = (size_t)b * BLOCK * s.d;
+        HIPCK(c, hipMemcpyAsync(area + off, src + off, (size_t)(e - b) * blk_bytes,
+                                hipMemcpyHostToDevice, c->cstream));
+        bytes += (int64_t)(e - b) * (int64_t)blk_bytes;
+        b = e;
+      }
+      kblocks += len;
+      continue;
+    }
     const size_t srow = u * s.Tmax + (size_t)start * BLOCK;
     const size_t drow = (size_t)ig * s.Tmax + (size_t)start * BLOCK;
     uint16_t *dst = (kind ? c->w.stage_v : c->w.stage_k) + drow * s.d;
@@ -527,7 +565,7 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
     if (round > ctx->th.R1) return fail(ctx, KVQ_EHIP, "controller did not finish its rounds");
     if (new_keys) {
       tm.open(TC_SCORE16);
-      HIPCK(ctx, launch_score_fp16(s, w, tab, maxNB, st));
+      HIPCK(ctx, launch_score_fp16(s, w, tab, layer, maxNB, st));
     }
     tm.open(TC_CONTROL);
     HIPCK(ctx, launch_control(s, ctx->t, w, tab, layer, ctx->th, round, maxNB, st));
@@ -559,7 +597,13 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
         const size_t ig = (size_t)i * s.Hkv + g;
         const size_t bytes = (size_t)((tab.T[i] + BLOCK - 1) / BLOCK) * BLOCK * s.d * 2;
         HIPCK(ctx, tm.copy_begin(TC_COPY, ctx->cstream));
-        HIPCK(ctx, hipMemcpyAsync(w.stage_k + ig * s.Tmax * s.d, ctx->t2k_host + u * s.Tmax * s.d,
+        if (s.kres) {
+          const int nbk = (tab.T[i] + BLOCK - 1) / BLOCK;
+          std::fill(ctx->kres.begin() + u * s.NBmax, ctx->kres.begin() + u * s.NBmax + nbk,
+                    (uint8_t)1);
+        }
+        HIPCK(ctx, hipMemcpyAsync(w.stage_k + stage_k_area(s, i, g, tab.slot[i], layer) * s.Tmax * s.d,
+                                  ctx->t2k_host + u * s.Tmax * s.d,
                                   bytes, hipMemcpyHostToDevice, ctx->cstream));
         HIPCK(ctx, hipMemcpyAsync(w.stage_v + ig * s.Tmax * s.d, ctx->t2v_host + u * s.Tmax * s.d,
                                   bytes, hipMemcpyHostToDevice, ctx->cstream));

@@ -21,10 +21,11 @@ namespace kvq {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-// Scores of a chunk -> per-head p = 2^(x - M_h) in LDS, M_h and l_h = sum p.
-template <int D, bool DENSE>
-__device__ __forceinline__ void chunk_softmax(const Shape &s, const Step &w, int i, int g, size_t ig,
-                                              int t0, int nt, unsigned long long umask,
+// Dense chunk scores (canonical FP16-key chains from the staged keys kst) ->
+// per-head p = 2^(x - M_h) in LDS, M_h and l_h = sum p.
+template <int D>
+__device__ __forceinline__ void chunk_softmax(const Shape &s, const Step &w, int i, int g,
+                                              const uint16_t *kst, int t0, int nt,
                                               float (*ps)[DEC_CB * BLOCK], float *sM, float *sL) {
   const int G = s.G;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -32,17 +33,10 @@ __device__ __forceinline__ void chunk_softmax(const Shape &s, const Step &w, int
     const int h = idx / nt, tt = idx % nt;
     const int tok = t0 + tt;
     const int hq = g * G + h;
-    float x;
-    if (DENSE) {
-      const uint16_t *row = w.stage_k + (ig * s.Tmax + tok) * D;
-      const float *q = w.qp + ((size_t)i * s.Hq + hq) * D;
-      float acc = 0.0f;
-      for (int c = 0; c < D; ++c) acc = fmaf(q[c], h2f(row[c]), acc);
-      x = acc;
-    } else {
-      const size_t o = ((size_t)i * s.Hq + hq) * s.Tmax + tok;
-      x = ((umask >> (tt / BLOCK)) & 1ull) ? w.sp[o] : w.shat[o];
-    }
+    const uint16_t *row = kst + (size_t)tok * D;
+    const float *q = w.qp + ((size_t)i * s.Hq + hq) * D;
+    float x = 0.0f;
+    for (int c = 0; c < D; ++c) x = fmaf(q[c], h2f(row[c]), x);
     ps[h][tt] = x;
   }
   __syncthreads();
@@ -82,7 +76,8 @@ __global__ __launch_bounds__(256) void k_decode_dense(Shape s, Tier1 t, Step w, 
   __shared__ float ps[4][CT];
   __shared__ float red[4][4][D];
   __shared__ float sM[4], sL[4];
-  chunk_softmax<D, true>(s, w, i, g, ig, t0, nt, 0ull, ps, sM, sL);
+  const uint16_t *kst = w.stage_k + stage_k_area(s, i, g, tab.slot[i], layer) * s.Tmax * D;
+  chunk_softmax<D>(s, w, i, g, kst, t0, nt, ps, sM, sL);
   float o[4][CPL];
 #pragma unroll
   for (int h = 0; h < 4; ++h)

@@ -63,7 +63,7 @@ struct Step {
   uint32_t *runs;                  // [B][Hkv][2][RUNMAX] start | len << 16
   uint32_t *nruns;                 // [B][Hkv][2]
   unsigned long long *plan;        // compacted runs for the host
-  uint16_t *stage_k, *stage_v;     // [B][Hkv][Tmax][d]
+  uint16_t *stage_k, *stage_v;     // [B][Hkv][Tmax][d] ([units][Tmax][d] keys when resident)
   float *part, *partd;             // [B][Hkv][NCH][G][d + 2]
   uint8_t *gdense;                 // [B][Hkv]
 };
@@ -78,6 +78,7 @@ struct SeqTab {
 struct Shape {
   int L, Hq, Hkv, G, d, Tmax, NBmax, runmax, nchmax, B;
   int ncu;                          // compute units of the device
+  int kres;                         // 1: FP16 key staging per unit, kept across steps
 };
 
 // Arguments of the dense comparator: FP16 q [n][Hq][d], K and V
@@ -98,6 +99,13 @@ struct Thresh {
 // Layout helpers (host and device).
 __host__ __device__ inline size_t unit_of(const Shape &s, int slot, int layer, int g) {
   return ((size_t)slot * s.L + layer) * s.Hkv + g;
+}
+
+// Index (in units of Tmax rows) of the FP16 key staging of call position i,
+// KV head g: one area per call position, or, with resident keys, one per
+// unit so that promoted blocks stay valid across steps.
+__host__ __device__ inline size_t stage_k_area(const Shape &s, int i, int g, int slot, int layer) {
+  return s.kres ? unit_of(s, slot, layer, g) : (size_t)i * s.Hkv + g;
 }
 
 // Byte (within a block's value codes) and nibble shift of (row r, channel c).
@@ -160,8 +168,8 @@ hipError_t launch_select(const Shape &s, const Step &w, const SeqTab &tab, int t
                          hipStream_t st);
 hipError_t launch_plan_keys(const Shape &s, const Step &w, const SeqTab &tab, int maxNB,
                             hipStream_t st);
-hipError_t launch_score_fp16(const Shape &s, const Step &w, const SeqTab &tab, int maxNB,
-                             hipStream_t st);
+hipError_t launch_score_fp16(const Shape &s, const Step &w, const SeqTab &tab, int layer,
+                             int maxNB, hipStream_t st);
 hipError_t launch_control(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,
                           int layer, const Thresh &th, int round, int maxNB, hipStream_t st);
 hipError_t launch_gather_plan(const Shape &s, const Step &w, int n, hipStream_t st);

@@ -270,7 +270,7 @@ hipError_t launch_score_int8(const Shape &s, const Tier1 &t, const Step &w, cons
 // 16-byte row reads); q' is read at wave-uniform addresses.  Each lane runs
 // the canonical fma chain over channels in ascending order.
 template <int D>
-__global__ __launch_bounds__(256) void k_score_fp16(Shape s, Step w, SeqTab tab) {
+__global__ __launch_bounds__(256) void k_score_fp16(Shape s, Step w, SeqTab tab, int layer) {
   constexpr int RST = D + 8;            // LDS row stride in halves (d*2 + 16 bytes)
   const int i = blockIdx.z, g = blockIdx.y, b = blockIdx.x;
   const int T = tab.T[i], NB = (T + BLOCK - 1) / BLOCK;
@@ -284,7 +284,8 @@ __global__ __launch_bounds__(256) void k_score_fp16(Shape s, Step w, SeqTab tab)
   // all 64 rows are loaded at once (rows past n of a partial block lie inside
   // the staging buffer; their results are masked below)
   constexpr int NL = BLOCK * D / 8 / 256;
-  const uint16_t *src = w.stage_k + (((size_t)i * s.Hkv + g) * s.Tmax + (size_t)b * BLOCK) * D;
+  const uint16_t *src =
+      w.stage_k + (stage_k_area(s, i, g, tab.slot[i], layer) * s.Tmax + (size_t)b * BLOCK) * D;
   v4i v[NL];
 #pragma unroll
   for (int k = 0; k < NL; ++k) {
@@ -329,11 +330,11 @@ __global__ __launch_bounds__(256) void k_score_fp16(Shape s, Step w, SeqTab tab)
   if (threadIdx.x == 0) *flag = 0;
 }
 
-hipError_t launch_score_fp16(const Shape &s, const Step &w, const SeqTab &tab, int maxNB,
-                             hipStream_t st) {
+hipError_t launch_score_fp16(const Shape &s, const Step &w, const SeqTab &tab, int layer,
+                             int maxNB, hipStream_t st) {
   dim3 grid(maxNB, s.Hkv, tab.n);
-  if (s.d == 128) return launch_k(k_score_fp16<128>, grid, dim3(256), 0, st, s, w, tab);
-  return launch_k(k_score_fp16<64>, grid, dim3(256), 0, st, s, w, tab);
+  if (s.d == 128) return launch_k(k_score_fp16<128>, grid, dim3(256), 0, st, s, w, tab, layer);
+  return launch_k(k_score_fp16<64>, grid, dim3(256), 0, st, s, w, tab, layer);
 }
 
 // ---- test hook: the decision exponential on a vector ------------------------------

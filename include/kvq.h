@@ -61,6 +61,15 @@ typedef int32_t kvq_status;
 /* flags */
 #define KVQ_FLAG_FORCE_DENSE  1u  /* every head at level 4 (exact dense path) */
 #define KVQ_FLAG_TIMING       2u  /* fill kvq_step_stats phase times          */
+/* Promoted FP16 key blocks stay in device memory across steps (one staging
+ * area per (slot, layer, KV head), n_layers * max_batch * n_kv_heads *
+ * max_tokens * head_dim * 2 bytes instead of max_batch * n_kv_heads * ...):
+ * a block is copied from tier 2 the first time it is promoted and again only
+ * after an append changed it.  Decisions and outputs are unchanged; only the
+ * host-link traffic and the device footprint differ.  Not part of the pages'
+ * method (which pages keys in on demand); a device-memory-for-bandwidth
+ * trade on GPUs with large HBM. */
+#define KVQ_FLAG_RESIDENT_KEYS 4u
 
 typedef struct kvq_config {
     int32_t n_layers;        /* layers held by the context                      */
