@@ -11,14 +11,19 @@ ranking check and bounds, ladder, split-K decode).  Inputs of the timed steps
 (q, k, v) are generated and resident in device memory before timing starts.
 
 value = KV tokens attended per second over the whole job: sum over timed steps
-and layers of the context length, divided by the wall time of the timed steps.
+and layers of the context length, divided by the wall time of the timed steps
+(which read no per-call statistics back).
 
-Also reported: per-kernel times from HIP events recorded by the library on the
-stream each kernel runs on; the roofline of the dominant kernel; the
+Also reported, from the last two steps' queries run again on every layer with
+statistics on: per-kernel times stamped by the runtime at each kernel's start
+and end on the stream it runs on; the roofline of the dominant kernel; the
 quantized-tier pass (INT8 scoring + selection + controller + mixed decode)
-against the tier-1 bytes it must read; host-link throughput of promotions; and
-the CPU oracle timed on one layer-step (a bounded sample), whose output is
-also compared with the GPU's for that layer (sampled parity).
+against the tier-1 bytes it must read; host-link throughput of promotions.
+Then: the dense FP16 (device-resident cache) and naive INT8/INT4 comparators
+on the same layers; the CPU oracle timed on one layer-step (a bounded
+sample), whose output is also compared with the GPU's for that layer (sampled
+parity); and the same timed steps on a context that keeps promoted FP16 keys
+in device memory across steps.
 """
 import argparse
 import hashlib
@@ -165,24 +170,36 @@ def main():
 
     recs = []
 
-    def run_steps(cx, rec):
-        def step(s):
+    def run_steps(cx):
+        """Warm-up, then the timed steps (append + certified decode per layer,
+        no per-call stats readback); returns (wall seconds, KV tokens)."""
+        toks = [0]
+
+        def step(s, timed):
             for layer in range(L):
                 cx.append(layer, [0], [1], k1s[s][layer], v1s[s][layer])
+                cx.decode_step(layer, [0], qs[s][layer], out, ek, ev, lv, stats=False)
+                if timed:
+                    toks[0] += cx.seq_len(layer, 0)
+        for s in range(a.warmup):
+            step(s, False)
+        torch.cuda.synchronize()
+        t0 = time.time()
+        for s in range(a.warmup, n_total):
+            step(s, True)
+            log(f"step {s - a.warmup + 1}/{a.steps} done")
+        torch.cuda.synchronize()
+        return time.time() - t0, toks[0]
+
+    def instrument(cx, rec):
+        """Per-kernel times, promotions and levels: the last two timed steps'
+        queries again on every layer (same shapes), with stats."""
+        for s in range(max(a.warmup, n_total - 2), n_total):
+            for layer in range(L):
                 _, _, _, _, st = cx.decode_step(layer, [0], qs[s][layer], out, ek, ev, lv,
                                                 stats=True)
                 st["T"] = cx.seq_len(layer, 0)
                 rec.append(st)
-        for s in range(a.warmup):
-            step(s)
-        torch.cuda.synchronize()
-        rec.clear()
-        t0 = time.time()
-        for s in range(a.warmup, n_total):
-            step(s)
-            log(f"step {s - a.warmup + 1}/{a.steps} done")
-        torch.cuda.synchronize()
-        return time.time() - t0
 
     def comparators(T_final):
         """Dense FP16 attention over a device-resident cache and the naive
@@ -227,10 +244,10 @@ def main():
                 "kv_tokens_per_s": round(T_final / (res["naive"] * 1e-3), 1)},
         }
 
-    wall = run_steps(ctx, recs)
+    wall, kv_tokens = run_steps(ctx)
     out_default = out.clone()
-    kv_tokens = sum(r["T"] for r in recs)
     value = kv_tokens / wall
+    instrument(ctx, recs)
     n = len(recs)
 
     def avg(key):
@@ -239,7 +256,7 @@ def main():
     per_kernel = {k: avg(k) for k in ("ms_score_int8", "ms_select", "ms_score_fp16",
                                       "ms_control", "ms_copy", "ms_decode", "ms_combine",
                                       "ms_dense", "ms_misc", "ms_total")}
-    T_avg = kv_tokens / n
+    T_avg = sum(r["T"] for r in recs) / n
     t1b = kvq.tier1_bytes_per_token(d)
     bytes_k = T_avg * Hkv * (d + 4 * d / 64)                  # INT8 codes + key meta
     bytes_v = T_avg * Hkv * (d / 2 + 4 * d / 32 + 4 / 64)     # INT4 codes + value meta + eta
@@ -341,19 +358,21 @@ def main():
         cx2 = kvq.Context(L, 1, Hq, Hkv, d, max_tokens, timing=True, resident_keys=True)
         prefill(cx2, False, False)
         recs2 = []
-        wall2 = run_steps(cx2, recs2)
+        wall2, toks2 = run_steps(cx2)
+        last2 = out.clone()
+        instrument(cx2, recs2)
         n2 = len(recs2)
         dense_bytes = L * max_tokens * Hkv * 4 * d
         resid = {
             "what": "same steps with KVQ_FLAG_RESIDENT_KEYS: promoted FP16 key blocks kept in "
                     "device memory across steps",
-            "value": round(sum(r["T"] for r in recs2) / wall2, 1), "unit": "KV tokens/s",
+            "value": round(toks2 / wall2, 1), "unit": "KV tokens/s",
             "ms_per_step": round(wall2 / a.steps * 1e3, 3),
             "h2d_MB_per_layer": round(sum(r["h2d_bytes"] for r in recs2) / n2 / 1e6, 3),
             "ms_copy_per_layer": round(sum(r["ms_copy"] for r in recs2) / n2, 5),
             "device_GiB": round(cx2.device_bytes / 2**30, 2),
             "device_frac_of_dense_fp16_cache": round(cx2.device_bytes / dense_bytes, 3),
-            "last_output_bit_equal_to_default": bool(torch.equal(out, out_default)),
+            "last_output_bit_equal_to_default": bool(torch.equal(last2, out_default)),
         }
         cx2.close()
 

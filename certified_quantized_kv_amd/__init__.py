@@ -54,6 +54,7 @@ class StepStats(ctypes.Structure):
 FLAG_FORCE_DENSE = 1
 FLAG_TIMING = 2
 FLAG_RESIDENT_KEYS = 4
+FLAG_FP16_VALUES = 8
 
 TR = dict(shat=1, sp=2, mhat=3, Lhat=4, delta=5, m16=6, L16=7, What=8, pi=9, Wt=10, W16=11,
           k0=12, ssize=13, ssd=14, ekey64=15, eval64=16, hflags=17, U=18, V=19, vh=20)
@@ -140,7 +141,7 @@ class Context:
     def __init__(self, n_layers, max_batch, n_q_heads, n_kv_heads, head_dim, max_tokens,
                  tau_cov_ppm=995_000, eps_key=1e-3, v_tol=0.25, rho_min_ppm=900_000,
                  widen_rounds=2, layer_frac_ppm=500_000, force_dense=False, timing=False,
-                 resident_keys=False):
+                 resident_keys=False, fp16_values=False):
         cfg = Config()
         _lib.kvq_default_config(ctypes.byref(cfg), n_layers, max_batch, n_q_heads, n_kv_heads,
                                 head_dim, max_tokens)
@@ -151,7 +152,8 @@ class Context:
         cfg.widen_rounds = widen_rounds
         cfg.layer_frac_ppm = layer_frac_ppm
         cfg.flags = ((FLAG_FORCE_DENSE if force_dense else 0) | (FLAG_TIMING if timing else 0) |
-                     (FLAG_RESIDENT_KEYS if resident_keys else 0))
+                     (FLAG_RESIDENT_KEYS if resident_keys else 0) |
+                     (FLAG_FP16_VALUES if fp16_values else 0))
         self.cfg = cfg
         self._ctx = ctypes.c_void_p()
         st = _lib.kvq_create(ctypes.byref(cfg), ctypes.byref(self._ctx))

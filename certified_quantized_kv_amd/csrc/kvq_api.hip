@@ -258,6 +258,7 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out) {
   x->th.eps_key = c.eps_key;
   x->th.v_tol = c.v_tol;
   x->th.force_dense = (c.flags & KVQ_FLAG_FORCE_DENSE) ? 1 : 0;
+  x->th.fp16_values = (c.flags & KVQ_FLAG_FP16_VALUES) ? 1 : 0;
   x->T.assign((size_t)c.max_batch * c.n_layers, 0);
 
   const size_t NU = (size_t)c.max_batch * c.n_layers * c.n_kv_heads;

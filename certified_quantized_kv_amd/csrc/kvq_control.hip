@@ -20,7 +20,8 @@
 //     the last round; rung 2: a head with E_val > v_tol promotes the values of
 //     blocks by contribution ceil(W+ eta_b) (descending, index ascending)
 //     until E_val <= v_tol; V_g = union of the heads' choices;
-//   * rung 4 (k_finalize): more than layer_frac of a sequence's heads at rung 3.
+//   * rung 4 (k_finalize): more than layer_frac of a sequence's heads at rung 3;
+//   * FP16-values ablation (flag): V_g = every block, no rung 2, E_val = 0.
 // Every sum is an integer, so no reduction order can change a decision.
 #include "kvq_device.h"
 #include "kvq_internal.h"
@@ -350,7 +351,13 @@ __global__ __launch_bounds__(CTL_NT) void k_decide(Shape s, Tier1 t, Step w, Seq
   }
   __syncthreads();
   int anyv = 0;
-  for (int hh = 0; hh < s.G; ++hh) {
+  if (th.fp16_values) {
+    // FP16-values ablation: every block's values from tier 2, no rung 2
+    uint8_t *Vw = w.V + ((size_t)i * s.Hkv + g) * s.NBmax;
+    for (int b = threadIdx.x; b < NB; b += CTL_NT) Vw[b] = 1;
+    anyv = 1;
+  }
+  for (int hh = 0; hh < s.G && !th.fp16_values; ++hh) {
     const int hq = g * s.G + hh;
     if (hf[hh] & 4u) continue;
     const unsigned long long nv = ssum[2 * hh], dv = ssum[2 * hh + 1];

@@ -94,6 +94,7 @@ struct Thresh {
   int tau_ppm, rho_ppm, R1, frac_ppm;
   double eps_key, v_tol;
   int force_dense;
+  int fp16_values;                  // every block's values from tier 2 (ablation)
 };
 
 // Layout helpers (host and device).

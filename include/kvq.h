@@ -70,6 +70,11 @@ typedef int32_t kvq_status;
  * method (which pages keys in on demand); a device-memory-for-bandwidth
  * trade on GPUs with large HBM. */
 #define KVQ_FLAG_RESIDENT_KEYS 4u
+/* The pages' FP16-values ablation (Résultats): every block's values are read
+ * in FP16 from tier 2 (V_g = all blocks), so E_val = 0 and rung 2 never
+ * fires; keys keep the INT8 scoring, selection, ranking check and rungs 1,
+ * 3 and 4. */
+#define KVQ_FLAG_FP16_VALUES  8u
 
 typedef struct kvq_config {
     int32_t n_layers;        /* layers held by the context                      */

@@ -46,6 +46,7 @@ class Config:
     widen_rounds: int = 2            # R1, rounds of rung 1
     layer_frac_ppm: int = 500_000    # rung 4 when more than this share of heads is at rung 3
     force_dense: bool = False        # every head at level 4 (test hook)
+    fp16_values: bool = False        # values in FP16 for every block (the pages' ablation)
 
 
 # --------------------------------------------------------------------------
@@ -372,8 +373,10 @@ def group_step(cfg, q16, t1, k16, v16):
     for h in range(G):
         if not failed[h] and state[h]["ekey"] > cfg.eps_key:
             failed[h] = True
-    # rung 2: value promotion
-    V = np.zeros(NB, np.uint8)
+    # rung 2: value promotion.  With fp16_values (the FP16-values ablation of
+    # Résultats) every block's values come from tier 2 by configuration:
+    # V_g = all blocks, no head takes rung 2, and E_val = 0.
+    V = np.ones(NB, np.uint8) if cfg.fp16_values else np.zeros(NB, np.uint8)
     contribs = [None] * G
     for h in range(G):
         Vh = []
@@ -381,7 +384,7 @@ def group_step(cfg, q16, t1, k16, v16):
             contrib, den = e_val_parts(state[h]["Wt"], t1["eta"])
             contribs[h] = (contrib, den)
             rem = sum(contrib)
-            if float(rem) / float(den) > cfg.v_tol:
+            if not cfg.fp16_values and float(rem) / float(den) > cfg.v_tol:
                 for b in sorted(range(NB), key=lambda b: (-contrib[b], b)):
                     Vh.append(b)
                     rem -= contrib[b]

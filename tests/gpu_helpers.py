@@ -85,7 +85,8 @@ def full_seq(s):
 def run_oracle(orc, case):
     cfgkw = {}
     m = dict(tau_cov_ppm="tau_ppm", eps_key="eps_key", v_tol="v_tol", rho_min_ppm="rho_ppm",
-             widen_rounds="widen_rounds", layer_frac_ppm="layer_frac_ppm", force_dense="force_dense")
+             widen_rounds="widen_rounds", layer_frac_ppm="layer_frac_ppm", force_dense="force_dense",
+             fp16_values="fp16_values")
     for k, v in case.cfg.items():
         if k in m:
             cfgkw[m[k]] = v

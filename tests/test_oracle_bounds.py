@@ -272,3 +272,29 @@ def test_naive_output_on_grid_equals_dense(orc):
     t2 = orc.build_tier1(k2, v16)
     gap = np.abs(orc.naive_output(orc.query(q16), t2, v16) - orc.dense_attention(q16, k2, v16)).max()
     assert gap > 1e-4
+
+
+def test_fp16_values_ablation(orc):
+    """FP16-values ablation (Résultats): V_g = every block, E_val = 0, no head
+    at level 2; with full key coverage the output is the dense output.  On
+    hostile values (5 % of groups U(-50, 50)) rung 2 fires without the flag
+    and not with it, and the flag's output is closer to dense."""
+    w = S.workload(1)
+    groups = oracle_groups(orc, w, 0, 0)
+    q16 = S.query(w, 0, 0, 0)
+    dense = orc.decode_step(orc.Config(force_dense=True), q16, groups)
+    res = orc.decode_step(orc.Config(tau_ppm=1_000_000, fp16_values=True), q16, groups)
+    assert np.all(res.e_val == 0) and not np.any(res.level == 2)
+    assert all(np.all(tr.V == 1) for tr in res.groups)
+    assert np.abs(res.out - dense.out).max() < 1e-5
+
+    w5 = S.workload(5)
+    w5.ctx, w5.tied_heads, w5.max_tokens = [1500], (0,), 1500 + 64
+    g5 = oracle_groups(orc, w5, 0, 0)
+    q5 = S.query(w5, 0, 0, 0)
+    d5 = orc.decode_step(orc.Config(force_dense=True), q5, g5)
+    plain = orc.decode_step(orc.Config(), q5, g5)
+    abl = orc.decode_step(orc.Config(fp16_values=True), q5, g5)
+    assert np.any(plain.level == 2)
+    assert not np.any(abl.level == 2) and np.all(abl.e_val == 0)
+    assert np.abs(abl.out - d5.out).max() < np.abs(plain.out - d5.out).max()
