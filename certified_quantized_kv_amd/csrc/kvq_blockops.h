@@ -1,7 +1,6 @@
 // kvq_blockops.h -- workgroup-level building blocks shared by the selection
 // and controller kernels: exclusive scan, run extraction, sort of 64-bit
-// keys (register bitonic chunks merged in LDS), and the per-KV-head
-// promotion planner.
+// keys (bucket sort in LDS), and the per-KV-head promotion planner.
 #pragma once
 #include "kvq_device.h"
 #include "kvq_internal.h"
@@ -71,7 +70,7 @@ __device__ inline int build_runs(const uint8_t *flags, int NB, uint32_t *runs, i
   return base_s;
 }
 
-// ---- block sort of 64-bit keys into descending order -----------------------
+// ---- comparison sort (the bucket sort's fallback) ----------------------------
 // Every wave sorts a chunk of 64*E keys in registers with a bitonic network
 // (E consecutive keys per lane; partners closer than E in the same lane,
 // the others exchanged across lanes with DPP / swizzle moves), then sorted
@@ -131,7 +130,7 @@ __device__ __forceinline__ int count_ahead(const unsigned long long *a, int len,
 }
 
 template <int NT, int E>
-__device__ inline void sort_desc_merge(unsigned long long *keys, int n) {
+__device__ inline void sort_desc_network(unsigned long long *keys, int n) {
   constexpr int CH = 64 * E;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nch = (n + CH - 1) / CH;
@@ -176,16 +175,190 @@ __device__ inline void sort_desc_merge(unsigned long long *keys, int n) {
   __syncthreads();
 }
 
-// Sorts keys[0..n) into descending order (1 <= n <= 4 * NT); the buffer must
-// hold max(64, pow2(n)) entries, those past n are used as scratch.
+// ---- block sort of distinct 64-bit keys into descending order --------------
+// Bucket sort by a monotone image of each key: its binary32 image, cut into
+// 4096 buckets on a log-like scale (the float bits), or, if that crowds a
+// bucket, key - smallest key on a linear scale.  Keys are counted and
+// scattered into bucket order with LDS atomics, and each key takes its final
+// place inside its bucket by counting the bucket's keys ahead of it.  The
+// result does not depend on the order of the atomics.  When both images leave
+// more than SORT_MAX_BUCKET keys in some bucket (clusters of keys that differ
+// only far below their leading bits) the comparison network above sorts
+// instead.  The caller's LDS buffer `keys` holds
+// sort_lds_bytes(cap) bytes (cap >= n keys, cap a power of two >= 64).
+constexpr int SORT_BUCKETS = 4096;
+
+__host__ __device__ inline size_t sort_lds_bytes(int cap) {
+  return (size_t)cap * 16 + (size_t)(2 * SORT_BUCKETS + 2) * 4;
+}
+
+__device__ __forceinline__ uint32_t key_image(unsigned long long k) {
+  return __float_as_uint((float)k);      // round to nearest: non-decreasing in k
+}
+
+// Buckets larger than this send the whole sort to the comparison network.
+constexpr int SORT_MAX_BUCKET = 48;
+
+// Largest bucket count over the workgroup (counts in cnt[0..SB)).
 template <int NT>
-__device__ inline void sort_desc_u64(unsigned long long *keys, int n) {
-  if (n <= NT)
-    sort_desc_merge<NT, 1>(keys, n);
-  else if (n <= 2 * NT)
-    sort_desc_merge<NT, 2>(keys, n);
-  else
-    sort_desc_merge<NT, 4>(keys, n);
+__device__ inline int max_bucket(const int *cnt, int *wbuf) {
+  constexpr int PER = SORT_BUCKETS / NT;
+  int big = 0;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) big = max(big, cnt[threadIdx.x * PER + k]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) big = max(big, __shfl_xor(big, o, 64));
+  if ((threadIdx.x & 63) == 0) wbuf[threadIdx.x >> 6] = big;
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < NT / 64; ++k) big = max(big, wbuf[k]);
+  __syncthreads();
+  return big;
+}
+
+template <int NT>
+__device__ inline void sort_desc_u64(unsigned long long *keys, int n, int cap) {
+  constexpr int SB = SORT_BUCKETS;
+  constexpr int PER = SB / NT;           // counters per thread in the scan
+  static_assert(SB % NT == 0, "bucket count");
+  unsigned long long *tmp = keys + cap;
+  int *base = reinterpret_cast<int *>(keys + 2 * (size_t)cap);   // SB + 1 entries
+  int *cur = base + SB + 1;                                     // SB entries
+  __shared__ unsigned long long kred[NT / 64];
+  __shared__ uint32_t red[2][NT / 64];
+  __shared__ int wsum[NT / 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  // image 1: the key's own binary32 image, over the images' range
+  unsigned long long kmin = ~0ull;
+  uint32_t lo = 0xffffffffu, hi = 0u;
+  for (int p = threadIdx.x; p < n; p += NT) {
+    const unsigned long long k = keys[p];
+    kmin = min(kmin, k);
+    const uint32_t f = key_image(k);
+    lo = min(lo, f);
+    hi = max(hi, f);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    kmin = min(kmin, (unsigned long long)__shfl_xor(kmin, o, 64));
+    lo = min(lo, (uint32_t)__shfl_xor((int)lo, o, 64));
+    hi = max(hi, (uint32_t)__shfl_xor((int)hi, o, 64));
+  }
+  if (lane == 0) {
+    kred[wave] = kmin;
+    red[0][wave] = lo;
+    red[1][wave] = hi;
+  }
+  for (int k = threadIdx.x; k < SB; k += NT) cur[k] = 0;
+  __syncthreads();
+  kmin = kred[0];
+  lo = red[0][0];
+  hi = red[1][0];
+#pragma unroll
+  for (int k = 1; k < NT / 64; ++k) {
+    kmin = min(kmin, kred[k]);
+    lo = min(lo, red[0][k]);
+    hi = max(hi, red[1][k]);
+  }
+  // image 2 (used when image 1 crowds a bucket): key - smallest key on a
+  // linear scale, which separates keys that agree in their leading bits
+  bool rel = false;
+  int sh = 0;
+  auto bucket = [&](unsigned long long k) {
+    const int f = rel ? (int)((k - kmin) >> sh) : (int)((key_image(k) - lo) >> sh);
+    return SB - 1 - f;
+  };
+  for (int pass = 0; pass < 2; ++pass) {
+    if (pass == 0) {
+      const uint32_t span = hi - lo;
+      sh = span >= (uint32_t)SB ? (32 - __clz((int)span)) - 12 : 0;
+    } else {
+      rel = true;
+      unsigned long long kmax = 0ull;
+      for (int p = threadIdx.x; p < n; p += NT) kmax = max(kmax, keys[p]);
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1)
+        kmax = max(kmax, (unsigned long long)__shfl_xor(kmax, o, 64));
+      if (lane == 0) kred[wave] = kmax;
+      for (int k = threadIdx.x; k < SB; k += NT) cur[k] = 0;
+      __syncthreads();
+      kmax = kred[0];
+#pragma unroll
+      for (int k = 1; k < NT / 64; ++k) kmax = max(kmax, kred[k]);
+      const unsigned long long span = kmax - kmin;
+      sh = span >= (unsigned long long)SB ? (64 - __clzll((long long)span)) - 12 : 0;
+    }
+    for (int p = threadIdx.x; p < n; p += NT) atomicAdd(&cur[bucket(keys[p])], 1);
+    __syncthreads();
+    if (max_bucket<NT>(cur, wsum) <= SORT_MAX_BUCKET) break;
+    if (pass == 1) {
+      // clustered keys: comparison network instead (the keys are untouched)
+      if (n <= NT)
+        sort_desc_network<NT, 1>(keys, n);
+      else if (n <= 2 * NT)
+        sort_desc_network<NT, 2>(keys, n);
+      else
+        sort_desc_network<NT, 4>(keys, n);
+      return;
+    }
+  }
+  // exclusive scan of the counts -> base (thread t: counters [t PER, (t+1) PER))
+  int c[PER];
+  int own = 0;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    c[k] = cur[threadIdx.x * PER + k];
+    own += c[k];
+  }
+  int x = own;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  int before = 0;
+#pragma unroll
+  for (int k = 0; k < NT / 64; ++k)
+    if (k < wave) before += wsum[k];
+  int run = before + x - own;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    base[threadIdx.x * PER + k] = run;
+    cur[threadIdx.x * PER + k] = run;
+    run += c[k];
+  }
+  if (threadIdx.x == 0) base[SB] = n;
+  __syncthreads();
+  // scatter into bucket order
+  for (int p = threadIdx.x; p < n; p += NT) {
+    const unsigned long long k = keys[p];
+    tmp[atomicAdd(&cur[bucket(k)], 1)] = k;
+  }
+  __syncthreads();
+  // place inside the bucket: keys ahead = larger keys (equal keys by slot)
+  for (int p = threadIdx.x; p < n; p += NT) {
+    const unsigned long long k = tmp[p];
+    const int bk = bucket(k);
+    const int b0 = base[bk], b1 = base[bk + 1];
+    int r = 0;
+    int q = b0;
+    for (; q + 4 <= b1; q += 4) {
+      const unsigned long long y0 = tmp[q], y1 = tmp[q + 1], y2 = tmp[q + 2], y3 = tmp[q + 3];
+      r += (y0 > k || (y0 == k && q < p)) ? 1 : 0;
+      r += (y1 > k || (y1 == k && q + 1 < p)) ? 1 : 0;
+      r += (y2 > k || (y2 == k && q + 2 < p)) ? 1 : 0;
+      r += (y3 > k || (y3 == k && q + 3 < p)) ? 1 : 0;
+    }
+    for (; q < b1; ++q) {
+      const unsigned long long y = tmp[q];
+      r += (y > k || (y == k && q < p)) ? 1 : 0;
+    }
+    keys[b0 + r] = k;
+  }
+  __syncthreads();
 }
 
 // Inclusive scan of per-thread u64 values over a workgroup of NT threads

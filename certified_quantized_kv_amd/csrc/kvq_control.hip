@@ -178,7 +178,7 @@ __device__ void evaluate_head(const Shape &s, const Step &w, const Thresh &th, i
     keys[k] = key;
   }
   __syncthreads();
-  sort_desc_u64<CTL_NT>(keys, max(n, 1));
+  sort_desc_u64<CTL_NT>(keys, n, n2);
   unsigned long long ssd = 0ull;
   for (int j = threadIdx.x; j < n; j += CTL_NT) {
     const uint32_t b = 0xffffffffu - (uint32_t)(keys[j] & 0xffffffffull);
@@ -218,7 +218,7 @@ __device__ void value_rung(const Shape &s, const Tier1 &t, const Step &w, const 
     keys[b] = key;
   }
   __syncthreads();
-  sort_desc_u64<CTL_NT>(keys, NB);
+  sort_desc_u64<CTL_NT>(keys, NB, n2);
   // prefix sums of the sorted contributions: thread t owns [t*per, (t+1)*per)
   const int per = (n2 + CTL_NT - 1) / CTL_NT;
   const int p0 = threadIdx.x * per;
@@ -427,10 +427,10 @@ hipError_t launch_control(const Shape &s, const Tier1 &t, const Step &w, const S
                           int layer, const Thresh &th, int round, int maxNB, hipStream_t st) {
   const int n2 = max(64, pow2_at_least(maxNB));
   const hipError_t e = launch_k(k_eval, dim3(s.Hq, tab.n), dim3(CTL_NT),
-                                n2 * sizeof(unsigned long long), st, s, w, tab, th);
+                                (uint32_t)sort_lds_bytes(n2), st, s, w, tab, th);
   if (e != hipSuccess) return e;
-  return launch_k(k_decide, dim3(s.Hkv, tab.n), dim3(CTL_NT), n2 * sizeof(unsigned long long), st,
-                  s, t, w, tab, layer, th, round);
+  return launch_k(k_decide, dim3(s.Hkv, tab.n), dim3(CTL_NT), (uint32_t)sort_lds_bytes(n2), st, s,
+                  t, w, tab, layer, th, round);
 }
 
 // ---- rung 4 and the per-head outputs ---------------------------------------------

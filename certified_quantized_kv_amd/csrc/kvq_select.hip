@@ -5,8 +5,7 @@
 // Per query head: fixed-point INT8 block weights
 //   What_b = floor(fl32(fl32(Lhat_b) exp2k(fl32(mhat_b - max_b mhat_b))))  (< 2^31)
 // are sorted by (What descending, block index ascending) as 64-bit keys
-// What << 32 | ~b (register bitonic chunks merged in LDS), prefix-summed in
-// 64-bit integers, and
+// What << 32 | ~b (bucket sort in LDS), prefix-summed in 64-bit integers, and
 //   K* = min k >= 1 with 10^6 sum_{i<k} What_pi(i) >= tau_ppm sum_b What_b.
 // Integer sums make the result independent of reduction order.
 // Promotion is per KV head: U_g = union of the group's top-K* sets; blocks
@@ -46,7 +45,7 @@ __global__ __launch_bounds__(SEL_NT) void k_select(Shape s, Step w, SeqTab tab, 
     }
     keys[b] = key;
   }
-  sort_desc_u64<SEL_NT>(keys, NB);
+  sort_desc_u64<SEL_NT>(keys, NB, n2);
 
   // pi, then prefix sums of the sorted weights: thread t owns positions
   // [t*per, (t+1)*per)
@@ -81,8 +80,8 @@ __global__ __launch_bounds__(SEL_NT) void k_select(Shape s, Step w, SeqTab tab, 
 hipError_t launch_select(const Shape &s, const Step &w, const SeqTab &tab, int tau_ppm, int maxNB,
                          hipStream_t st) {
   const int n2 = max(64, pow2_at_least(maxNB));
-  return launch_k(k_select, dim3(s.Hq, tab.n), dim3(SEL_NT), n2 * sizeof(unsigned long long),
-                     st, s, w, tab, tau_ppm);
+  return launch_k(k_select, dim3(s.Hq, tab.n), dim3(SEL_NT), (uint32_t)sort_lds_bytes(n2), st, s,
+                  w, tab, tau_ppm);
 }
 
 __global__ __launch_bounds__(1024) void k_plan_keys(Shape s, Step w, SeqTab tab) {
