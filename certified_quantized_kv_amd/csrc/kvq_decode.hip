@@ -315,15 +315,20 @@ hipError_t launch_decode(const Shape &s, const Tier1 &t, const Step &w, const Se
 }
 
 // Merges the chunk partials of each (sequence, query head): levels 3/4 read
-// the dense partials, the others the mixed ones.  256 threads: the chunk
-// maxima and weights first, then 256/d groups of channels-threads each sum a
-// share of the chunks; the shares are added in LDS.
+// the dense partials, the others the mixed ones.  One workgroup per
+// (query head, sequence, quarter of the channels): the chunk maxima and
+// weights first (every quarter computes them), then 256 / (d/4) groups of
+// channel-threads each sum a share of the chunks with four independent
+// accumulators; the shares are added in LDS.
+constexpr int COMB_MAXCH = 1024;
+static_assert((MAX_NB + DEC_CB - 1) / DEC_CB <= COMB_MAXCH, "chunk weights fit in LDS");
+
 __global__ __launch_bounds__(256) void k_combine(Shape s, Step w, SeqTab tab, float *out, int mode) {
-  __shared__ float fw[1024];
+  __shared__ float fw[COMB_MAXCH];
   __shared__ float red[256];
-  __shared__ float sMl[2];
-  const int i = blockIdx.y, hq = blockIdx.x;
-  const int D = s.d, G = s.G, g = hq / G, h = hq % G;
+  __shared__ float wred[4];
+  const int i = blockIdx.y, hq = blockIdx.x, cq = blockIdx.z;
+  const int D = s.d, G = s.G, g = hq / G, h = hq % G, CQ = D / 4;
   const int NB = (tab.T[i] + BLOCK - 1) / BLOCK, nch = (NB + DEC_CB - 1) / DEC_CB;
   const bool dense = mode == 2 || (mode == 0 && w.hlevel[(size_t)i * s.Hq + hq] >= 3);
   const float *part = (dense ? w.partd : w.part) + (((size_t)i * s.Hkv + g) * s.nchmax * G + h) * (D + 2);
@@ -331,9 +336,10 @@ __global__ __launch_bounds__(256) void k_combine(Shape s, Step w, SeqTab tab, fl
   float m = -INFINITY;
   for (int k = threadIdx.x; k < nch; k += 256) m = fmaxf(m, part[k * stride + D]);
   m = bfly_max<64>(m);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  if ((threadIdx.x & 63) == 0) wred[threadIdx.x >> 6] = m;
   __syncthreads();
-  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float M = fmaxf(fmaxf(wred[0], wred[1]), fmaxf(wred[2], wred[3]));
+  __syncthreads();
   float l = 0.0f;
   for (int k = threadIdx.x; k < nch; k += 256) {
     const float f = exp2f(part[k * stride + D] - M);
@@ -341,27 +347,31 @@ __global__ __launch_bounds__(256) void k_combine(Shape s, Step w, SeqTab tab, fl
     l = fmaf(part[k * stride + D + 1], f, l);
   }
   l = bfly_sum<64>(l);
+  if ((threadIdx.x & 63) == 0) wred[threadIdx.x >> 6] = l;
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = l;
+  const float L = wred[0] + wred[1] + wred[2] + wred[3];
+  const int parts = 256 / CQ, c = cq * CQ + threadIdx.x % CQ, pp = threadIdx.x / CQ;
+  float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+  int k = pp;
+  for (; k + 3 * parts < nch; k += 4 * parts) {
+    a0 = fmaf(part[k * stride + c], fw[k], a0);
+    a1 = fmaf(part[(k + parts) * stride + c], fw[k + parts], a1);
+    a2 = fmaf(part[(k + 2 * parts) * stride + c], fw[k + 2 * parts], a2);
+    a3 = fmaf(part[(k + 3 * parts) * stride + c], fw[k + 3 * parts], a3);
+  }
+  for (; k < nch; k += parts) a0 = fmaf(part[k * stride + c], fw[k], a0);
+  red[threadIdx.x] = (a0 + a1) + (a2 + a3);
   __syncthreads();
-  if (threadIdx.x == 0) sMl[0] = red[0] + red[1] + red[2] + red[3];
-  __syncthreads();
-  const int parts = 256 / D, c = threadIdx.x % D, pp = threadIdx.x / D;
-  float acc = 0.0f;
-#pragma unroll 4
-  for (int k = pp; k < nch; k += parts) acc = fmaf(part[k * stride + c], fw[k], acc);
-  red[threadIdx.x] = acc;
-  __syncthreads();
-  if (threadIdx.x < D) {
+  if (threadIdx.x < CQ) {
     float sum = 0.0f;
-    for (int q = 0; q < parts; ++q) sum += red[q * D + threadIdx.x];
-    out[((size_t)i * s.Hq + hq) * D + threadIdx.x] = sum / sMl[0];
+    for (int q = 0; q < parts; ++q) sum += red[q * CQ + threadIdx.x];
+    out[((size_t)i * s.Hq + hq) * D + c] = sum / L;
   }
 }
 
 hipError_t launch_combine(const Shape &s, const Step &w, const SeqTab &tab, float *out, int mode,
                           hipStream_t st) {
-  return launch_k(k_combine, dim3(s.Hq, tab.n), dim3(256), 0, st, s, w, tab, out, mode);
+  return launch_k(k_combine, dim3(s.Hq, tab.n, 4), dim3(256), 0, st, s, w, tab, out, mode);
 }
 
 }  // namespace kvq

@@ -90,7 +90,7 @@ __global__ __launch_bounds__(256) void k_score_int8(Shape s, Tier1 t, Step w, Se
     for (int c = 0; c < CW; ++c) qv[c] = qsrc[c];
   };
   // software pipeline: the next unit's codes and metadata are in flight
-  // while the current one is processed
+  // while the current one's scores and block ingredients are formed
   v4i Bn[NKS][4];
   uint32_t kmn[CW];
   auto fetch = [&](int ii, int gg, int bb) {
@@ -111,27 +111,17 @@ __global__ __launch_bounds__(256) void k_score_int8(Shape s, Tier1 t, Step w, Se
     const int T = tab.T[i];
     const int n = min(BLOCK, T - b * BLOCK);
     const int hq = g * s.G + (hv ? h : 0);
-    v4i Bv[NKS][4];
-    uint32_t kmv[CW];
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) Bv[ks][nt] = Bn[ks][nt];
-#pragma unroll
-    for (int c = 0; c < CW; ++c) kmv[c] = kmn[c];
-    // successor unit
+    // successor unit (its codes and metadata are fetched once this unit's
+    // contraction has consumed the registers)
     int i2 = i, g2 = g, b2 = b;
-    if (u + W < U) {
-      locate(u + W, i2, g2, b2);
-      fetch(i2, g2, b2);
-    }
+    if (u + W < U) locate(u + W, i2, g2, b2);
 
     // ---- prologue: exponent, limbs of A, beta and Delta' per head -----------
     float sv[CW], ov[CW], a[CW];
     float am = 0.0f;
 #pragma unroll
     for (int c = 0; c < CW; ++c) {
-      const uint32_t m = kmv[c];
+      const uint32_t m = kmn[c];
       sv[c] = h2f((uint16_t)(m & 0xffffu));
       ov[c] = h2f((uint16_t)(m >> 16));
       a[c] = qv[c] * sv[c];
@@ -188,9 +178,10 @@ __global__ __launch_bounds__(256) void k_score_int8(Shape s, Tier1 t, Step w, Se
       const v4i Aop = *(const v4i *)&As[wave][lane & 15][ks * 64 + 16 * (lane >> 4)];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        acc[nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aop, Bv[ks][nt], acc[nt], 0, 0, 0);
+        acc[nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aop, Bn[ks][nt], acc[nt], 0, 0, 0);
       }
     }
+    if (u + W < U) fetch(i2, g2, b2);
 
     // ---- scores and block ingredients (lane: head lane/16, token lane%16) -----
     const float sc = ldexpf(1.0f, e);
