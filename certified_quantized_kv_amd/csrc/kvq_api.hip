@@ -304,8 +304,7 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out) {
   DA(w.V, B * Hkv * NBm);
   DA(w.gstat, B * Hkv * 4);
   DA(w.runs, B * Hkv * 2 * (size_t)s.runmax * 4);
-  DA(w.nruns, B * Hkv * 2 * 4);
-  x->plan_words = 4 + B * Hkv * 2 * (size_t)s.runmax;
+  x->plan_words = 4 + 2 * plan_kcap(s);
   DA(w.plan, x->plan_words * 8);
   DA(w.stage_k, (s.kres ? NU : B * Hkv) * Tm * d * 2);
   DA(w.stage_v, B * Hkv * Tm * d * 2);
@@ -442,17 +441,25 @@ struct Plan {
 };
 
 kvq_status read_plan(kvq_ctx *c, hipStream_t st, Plan &p) {
-  const size_t first = std::min(c->plan_cap, c->plan_words - 4);
+  const size_t kcap = plan_kcap(c->s);
+  const size_t first = std::min(c->plan_cap, kcap);
   HIPCK(c, hipMemcpyAsync(c->plan_host, c->w.plan, (4 + first) * 8, hipMemcpyDeviceToHost, st));
   HIPCK(c, hipStreamSynchronize(st));
   p.nk = (int64_t)c->plan_host[0];
   p.nv = (int64_t)c->plan_host[1];
   p.flags = (uint32_t)c->plan_host[2];
-  const size_t tot = (size_t)(p.nk + p.nv);
-  p.ent.assign(c->plan_host + 4, c->plan_host + 4 + std::min(tot, first));
-  if (tot > first) {
-    p.ent.resize(tot);
-    HIPCK(c, hipMemcpy(p.ent.data() + first, c->w.plan + 4 + first, (tot - first) * 8,
+  if (p.nk < 0 || (size_t)p.nk > kcap || p.nv < 0 || (size_t)p.nv > kcap)
+    return fail(c, KVQ_EHIP, "promotion plan out of range");
+  p.ent.assign(c->plan_host + 4, c->plan_host + 4 + std::min((size_t)p.nk, first));
+  if ((size_t)p.nk > first) {
+    p.ent.resize((size_t)p.nk);
+    HIPCK(c, hipMemcpy(p.ent.data() + first, c->w.plan + 4 + first, ((size_t)p.nk - first) * 8,
+                       hipMemcpyDeviceToHost));
+  }
+  if (p.nv > 0) {
+    const size_t k0 = p.ent.size();
+    p.ent.resize(k0 + (size_t)p.nv);
+    HIPCK(c, hipMemcpy(p.ent.data() + k0, c->w.plan + 4 + kcap, (size_t)p.nv * 8,
                        hipMemcpyDeviceToHost));
   }
   return KVQ_OK;
@@ -546,7 +553,6 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
   tm.open(TC_SELECT);
   HIPCK(ctx, launch_select(s, w, tab, ctx->th.tau_ppm, maxNB, st));
   HIPCK(ctx, launch_plan_keys(s, w, tab, maxNB, st));
-  HIPCK(ctx, launch_gather_plan(s, w, n, st));
   tm.close();
   Plan plan;
   kvq_status rs = read_plan(ctx, st, plan);
@@ -570,7 +576,6 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
     }
     tm.open(TC_CONTROL);
     HIPCK(ctx, launch_control(s, ctx->t, w, tab, layer, ctx->th, round, maxNB, st));
-    HIPCK(ctx, launch_gather_plan(s, w, n, st));
     tm.close();
     rs = read_plan(ctx, st, plan);
     if (rs != KVQ_OK) return rs;

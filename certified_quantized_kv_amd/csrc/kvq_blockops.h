@@ -41,33 +41,55 @@ __device__ inline int block_excl_scan(int v, int *tmp, int &total) {
 }
 
 // Runs of consecutive set flags (flags[0..NB)) -> runs[k] = start | len << 16.
-// Starts and (exclusive) ends are compacted separately, in increasing order,
-// so the k-th start pairs with the k-th end; the two halves of runs[k] are
-// written by different threads, then joined.
+// Thread t scans the flags [t E, (t+1) E); one exclusive scan of its packed
+// (starts | ends << 16) counts gives every start and every (exclusive) end its
+// rank, so the k-th start pairs with the k-th end; the two halves of runs[k]
+// are written by the threads that found them, then joined.
 __device__ inline int build_runs(const uint8_t *flags, int NB, uint32_t *runs, int *tmp) {
   uint16_t *half = reinterpret_cast<uint16_t *>(runs);
-  int base_s = 0, base_e = 0;
-  for (int c0 = 0; c0 < NB; c0 += blockDim.x) {
-    const int b = c0 + threadIdx.x;
-    const bool on = b < NB && flags[b];
-    const bool start = on && (b == 0 || !flags[b - 1]);
-    const bool end = on && (b == NB - 1 || !flags[b + 1]);
-    int ts, te;
-    const int ps = block_excl_scan(start ? 1 : 0, tmp, ts);
-    const int pe = block_excl_scan(end ? 1 : 0, tmp, te);
-    if (start) half[2 * (base_s + ps)] = (uint16_t)b;
-    if (end) half[2 * (base_e + pe) + 1] = (uint16_t)(b + 1);
-    base_s += ts;
-    base_e += te;
+  const int E = (NB + (int)blockDim.x - 1) / (int)blockDim.x;
+  const int b0 = threadIdx.x * E, b1 = min(NB, b0 + E);
+  int ns = 0, ne = 0;
+  for (int b = b0; b < b1; ++b) {
+    if (!flags[b]) continue;
+    ns += (b == 0 || !flags[b - 1]) ? 1 : 0;
+    ne += (b == NB - 1 || !flags[b + 1]) ? 1 : 0;
   }
+  int total;
+  const int pre = block_excl_scan(ns | (ne << 16), tmp, total);
+  int ps = pre & 0xffff, pe = pre >> 16;
+  for (int b = b0; b < b1; ++b) {
+    if (!flags[b]) continue;
+    if (b == 0 || !flags[b - 1]) half[2 * (ps++)] = (uint16_t)b;
+    if (b == NB - 1 || !flags[b + 1]) half[2 * (pe++) + 1] = (uint16_t)(b + 1);
+  }
+  const int nr = total & 0xffff;
   __syncthreads();
-  for (int k = threadIdx.x; k < base_s; k += blockDim.x) {
+  for (int k = threadIdx.x; k < nr; k += blockDim.x) {
     const uint32_t r = runs[k];
     const uint32_t st = r & 0xffffu, en = r >> 16;
     runs[k] = st | ((en - st) << 16);
   }
   __syncthreads();
-  return base_s;
+  return nr;
+}
+
+// Plan for the host (device words, 64-bit): [0] number of K runs, [1] number
+// of V runs, [2] flags (bit0: a group is still widening, bit1: some head is at
+// rung 3), then K entries from word 4 and V entries from word 4 + kcap, each
+// len | start << 16 | ig << 32 | kind << 48 with ig = i * Hkv + g.  Groups
+// reserve their entries with atomics (entry order is immaterial to the copies).
+__device__ inline void emit_runs(const Shape &s, const Step &w, int ig, int kind,
+                                 const uint32_t *runs, int nr, int *sbase) {
+  if (threadIdx.x == 0)
+    *sbase = nr ? (int)atomicAdd(&w.plan[kind], (unsigned long long)nr) : 0;
+  __syncthreads();
+  const size_t off = 4 + (kind ? plan_kcap(s) : 0) + (size_t)*sbase;
+  for (int k = threadIdx.x; k < nr; k += blockDim.x) {
+    const uint32_t r = runs[k];
+    w.plan[off + k] = (unsigned long long)(r >> 16) | ((unsigned long long)(r & 0xffffu) << 16) |
+                      ((unsigned long long)ig << 32) | ((unsigned long long)kind << 48);
+  }
 }
 
 // ---- comparison sort (the bucket sort's fallback) ----------------------------
@@ -390,7 +412,7 @@ __device__ inline unsigned long long block_incl_scan_u64(unsigned long long v, u
 // Union of the group's selections -> U; blocks new to U -> Knew and K runs.
 // Flags live in LDS while the group is planned; U and Knew are written back.
 __device__ inline void plan_group_keys(const Shape &s, const Step &w, int i, int g, int NB) {
-  __shared__ int tmp[17];
+  __shared__ int tmp[18];
   __shared__ uint8_t fu[MAX_NB];
   __shared__ uint8_t fk[MAX_NB];
   uint8_t *U = w.U + ((size_t)i * s.Hkv + g) * s.NBmax;
@@ -418,7 +440,7 @@ __device__ inline void plan_group_keys(const Shape &s, const Step &w, int i, int
   }
   uint32_t *runs = w.runs + (((size_t)i * s.Hkv + g) * 2 + 0) * s.runmax;
   const int nr = build_runs(fk, NB, runs, tmp);
-  if (threadIdx.x == 0) w.nruns[((size_t)i * s.Hkv + g) * 2 + 0] = (uint32_t)nr;
+  emit_runs(s, w, i * s.Hkv + g, 0, runs, nr, tmp + 17);
 }
 
 }  // namespace kvq

@@ -258,6 +258,8 @@ __global__ __launch_bounds__(CTL_NT) void k_eval(Shape s, Step w, SeqTab tab, Th
   __shared__ uint16_t pos[MAX_NB];
   __shared__ CtlShared sh;
   const int i = blockIdx.y, hq = blockIdx.x, g = hq / s.G;
+  // a new plan starts with this round (the host has read the previous one)
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 4) w.plan[threadIdx.x] = 0ull;
   if (w.gstat[(size_t)i * s.Hkv + g] & 1u) return;
   if (w.hflags[(size_t)i * s.Hq + hq] & 4u) return;
   const int NB = (tab.T[i] + BLOCK - 1) / BLOCK;
@@ -272,15 +274,11 @@ __global__ __launch_bounds__(CTL_NT) void k_decide(Shape s, Tier1 t, Step w, Seq
                                                    Thresh th, int round) {
   extern __shared__ unsigned long long keys[];
   __shared__ CtlShared sh;
-  __shared__ int tmp[17];
+  __shared__ int tmp[18];
   const int i = blockIdx.y, g = blockIdx.x;
   uint32_t *gs = w.gstat + (size_t)i * s.Hkv + g;
-  uint32_t *nr = w.nruns + ((size_t)i * s.Hkv + g) * 2;
   if (*gs & 1u) {                             // group already final: nothing new to copy
-    if (threadIdx.x == 0) {
-      nr[0] = 0u;
-      nr[1] = 0u;
-    }
+    if (threadIdx.x == 0 && (*gs & 2u)) atomicOr(&w.plan[2], 2ull);
     return;
   }
   const int T = tab.T[i], NB = (T + BLOCK - 1) / BLOCK;
@@ -295,7 +293,6 @@ __global__ __launch_bounds__(CTL_NT) void k_decide(Shape s, Tier1 t, Step w, Seq
     hek[threadIdx.x] = w.ekey64[o];
     hss[threadIdx.x] = w.ssize[o];
   }
-  if (threadIdx.x == 0) nr[0] = 0u;
   __syncthreads();
   if (threadIdx.x == 0) {
     int any = 0;
@@ -322,6 +319,7 @@ __global__ __launch_bounds__(CTL_NT) void k_decide(Shape s, Tier1 t, Step w, Seq
   }
   __syncthreads();
   if (sh.wid) {
+    if (threadIdx.x == 0) atomicOr(&w.plan[2], 1ull);
     plan_group_keys(s, w, i, g, NB);
     return;
   }
@@ -413,9 +411,10 @@ __global__ __launch_bounds__(CTL_NT) void k_decide(Shape s, Tier1 t, Step w, Seq
   __syncthreads();
   uint32_t *runs = w.runs + (((size_t)i * s.Hkv + g) * 2 + 1) * s.runmax;
   const int nrv = anyv ? build_runs(fv, NB, runs, tmp) : 0;
+  emit_runs(s, w, i * s.Hkv + g, 1, runs, nrv, tmp + 17);
   if (threadIdx.x == 0) {
-    nr[1] = (uint32_t)nrv;
     *gs = 1u | (any3 ? 2u : 0u);
+    if (any3) atomicOr(&w.plan[2], 2ull);
   }
   if (threadIdx.x < s.G) {
     // bit3 marks V_h non-empty; bits 8..15 the round the group stopped in

@@ -60,9 +60,8 @@ struct Step {
   int8_t *hlevel;                  // [B][Hq]
   uint8_t *U, *Knew, *V;           // [B][Hkv][NBmax]
   uint32_t *gstat;                 // [B][Hkv] bit0 done, bit1 any rung 3
-  uint32_t *runs;                  // [B][Hkv][2][RUNMAX] start | len << 16
-  uint32_t *nruns;                 // [B][Hkv][2]
-  unsigned long long *plan;        // compacted runs for the host
+  uint32_t *runs;                  // [B][Hkv][2][RUNMAX] start | len << 16 (scratch)
+  unsigned long long *plan;        // runs for the host (layout at emit_runs)
   uint16_t *stage_k, *stage_v;     // [B][Hkv][Tmax][d] ([units][Tmax][d] keys when resident)
   float *part, *partd;             // [B][Hkv][NCH][G][d + 2]
   uint8_t *gdense;                 // [B][Hkv]
@@ -107,6 +106,11 @@ __host__ __device__ inline size_t unit_of(const Shape &s, int slot, int layer, i
 // unit so that promoted blocks stay valid across steps.
 __host__ __device__ inline size_t stage_k_area(const Shape &s, int i, int g, int slot, int layer) {
   return s.kres ? unit_of(s, slot, layer, g) : (size_t)i * s.Hkv + g;
+}
+
+// Capacity (entries) of each of the K and V halves of the promotion plan.
+__host__ __device__ inline size_t plan_kcap(const Shape &s) {
+  return (size_t)s.B * s.Hkv * s.runmax;
 }
 
 // Byte (within a block's value codes) and nibble shift of (row r, channel c).
@@ -173,7 +177,6 @@ hipError_t launch_score_fp16(const Shape &s, const Step &w, const SeqTab &tab, i
                              int maxNB, hipStream_t st);
 hipError_t launch_control(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,
                           int layer, const Thresh &th, int round, int maxNB, hipStream_t st);
-hipError_t launch_gather_plan(const Shape &s, const Step &w, int n, hipStream_t st);
 hipError_t launch_reset(const Shape &s, const Step &w, int n, hipStream_t st);
 hipError_t launch_finalize(const Shape &s, const Step &w, const SeqTab &tab, const Thresh &th,
                            float *e_key, float *e_val, int8_t *level, hipStream_t st);

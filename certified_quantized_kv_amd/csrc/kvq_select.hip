@@ -96,53 +96,6 @@ hipError_t launch_plan_keys(const Shape &s, const Step &w, const SeqTab &tab, in
   return launch_k(k_plan_keys, dim3(s.Hkv, tab.n), dim3(1024), 0, st, s, w, tab);
 }
 
-// Compacts every group's runs into plan[]: plan[0] = #K runs, plan[1] = #V
-// runs, plan[2] = flags (bit0: a group is still widening, bit1: some head is
-// at rung 3), then the K entries followed by the V entries, each
-// len | start << 16 | ig << 32 | kind << 48 with ig = i * Hkv + g.
-__global__ __launch_bounds__(1024) void k_gather_plan(Shape s, Step w, int n) {
-  __shared__ int tmp[17];
-  __shared__ uint32_t s_flags;
-  if (threadIdx.x == 0) s_flags = 0u;
-  __syncthreads();
-  const int G2 = n * s.Hkv;
-  int base = 0, nk = 0;
-  for (int kind = 0; kind < 2; ++kind) {
-    for (int c0 = 0; c0 < G2; c0 += blockDim.x) {
-      const int ig = c0 + threadIdx.x;
-      const int cnt = (ig < G2) ? (int)w.nruns[(size_t)ig * 2 + kind] : 0;
-      int total;
-      const int pos = block_excl_scan(cnt, tmp, total);
-      if (ig < G2) {
-        const uint32_t *runs = w.runs + ((size_t)ig * 2 + kind) * s.runmax;
-        for (int k = 0; k < cnt; ++k) {
-          const uint32_t r = runs[k];
-          w.plan[4 + base + pos + k] = (unsigned long long)(r >> 16) |
-                                       ((unsigned long long)(r & 0xffffu) << 16) |
-                                       ((unsigned long long)ig << 32) |
-                                       ((unsigned long long)kind << 48);
-        }
-        if (kind == 0) {
-          const uint32_t gs = w.gstat[ig];
-          uint32_t f = 0u;
-          if (!(gs & 1u)) f |= 1u;
-          if (gs & 2u) f |= 2u;
-          if (f) atomicOr(&s_flags, f);
-        }
-      }
-      base += total;
-    }
-    if (kind == 0) nk = base;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    w.plan[0] = (unsigned long long)nk;
-    w.plan[1] = (unsigned long long)(base - nk);
-    w.plan[2] = (unsigned long long)s_flags;
-    w.plan[3] = 0ull;
-  }
-}
-
 // Clears the per-step flags and head state of the first n call positions in
 // one launch (byte arrays [n][Hkv][NBmax] and [n][Hq][NBmax], head/group words).
 __global__ void k_reset(Shape s, Step w, int n) {
@@ -159,19 +112,14 @@ __global__ void k_reset(Shape s, Step w, int n) {
     w.ekey64[k] = 0.0;
     w.eval64[k] = 0.0;
   }
-  for (size_t k = blockIdx.x * (size_t)blockDim.x + threadIdx.x; k < (size_t)n * s.Hkv; k += stride) {
+  for (size_t k = blockIdx.x * (size_t)blockDim.x + threadIdx.x; k < (size_t)n * s.Hkv; k += stride)
     w.gstat[k] = 0u;
-    w.nruns[2 * k] = 0u;
-    w.nruns[2 * k + 1] = 0u;
-  }
+  if (blockIdx.x == 0 && threadIdx.x < 4) w.plan[threadIdx.x] = 0ull;
 }
 
 hipError_t launch_reset(const Shape &s, const Step &w, int n, hipStream_t st) {
   return launch_k(k_reset, dim3(64), dim3(256), 0, st, s, w, n);
 }
 
-hipError_t launch_gather_plan(const Shape &s, const Step &w, int n, hipStream_t st) {
-  return launch_k(k_gather_plan, dim3(1), dim3(1024), 0, st, s, w, n);
-}
 
 }  // namespace kvq
