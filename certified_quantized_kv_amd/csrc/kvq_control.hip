@@ -110,18 +110,45 @@ __device__ void block_sum_u64_8(unsigned long long (&v)[8], CtlShared &sh) {
 }
 
 // Evaluates one head on the current U: mixed weights Wt, FP16 weights W16
-// over S_h, ranking verdict and E_key.
+// over S_h, ranking verdict and E_key.  Passes over the blocks: S_h
+// membership (positions in pi), both references (mixed maximum, FP16 maximum
+// over S_h), then weights, E_key sums and sort keys together.
 __device__ void evaluate_head(const Shape &s, const Step &w, const Thresh &th, int i, int g, int hq,
                               int NB, unsigned long long *keys, uint16_t *pos, CtlShared &sh) {
   const size_t base = ((size_t)i * s.Hq + hq) * s.NBmax;
   const uint8_t *U = w.U + ((size_t)i * s.Hkv + g) * s.NBmax;
-  // mixed weights
-  float mloc = -INFINITY;
-  for (int b = threadIdx.x; b < NB; b += CTL_NT)
-    mloc = fmaxf(mloc, U[b] ? w.m16[base + b] : w.mhat[base + b]);
-  const float Mt = block_max_f32(mloc, sh.f32);
-  unsigned long long den = 0ull, num = 0ull, sub = 0ull;
-  int cap = 0;
+  const int n = w.ssize[(size_t)i * s.Hq + hq];
+  const uint32_t *pi = w.pi + base;
+  __shared__ float mred[2][CTL_NT / 64];
+  __shared__ unsigned long long sred[4][CTL_NT / 64];
+  // S_h = pi[0 .. n): INT8 position of each member, 0xffff elsewhere
+  for (int b = threadIdx.x; b < NB; b += CTL_NT) pos[b] = 0xffff;
+  __syncthreads();
+  for (int k = threadIdx.x; k < n; k += CTL_NT) pos[pi[k]] = (uint16_t)k;
+  __syncthreads();
+  // references: Mt over the mixed block maxima, M16 over S_h (S_h lies in U)
+  float mloc = -INFINITY, m16loc = -INFINITY;
+  for (int b = threadIdx.x; b < NB; b += CTL_NT) {
+    const bool pr = U[b] != 0;
+    const float mb = pr ? w.m16[base + b] : w.mhat[base + b];
+    mloc = fmaxf(mloc, mb);
+    if (pos[b] != 0xffff) m16loc = fmaxf(m16loc, mb);
+  }
+  mloc = bfly_max<64>(mloc);
+  m16loc = bfly_max<64>(m16loc);
+  if ((threadIdx.x & 63) == 0) {
+    mred[0][threadIdx.x >> 6] = mloc;
+    mred[1][threadIdx.x >> 6] = m16loc;
+  }
+  __syncthreads();
+  float Mt = mred[0][0], M16 = mred[1][0];
+#pragma unroll
+  for (int k = 1; k < CTL_NT / 64; ++k) {
+    Mt = fmaxf(Mt, mred[0][k]);
+    M16 = fmaxf(M16, mred[1][k]);
+  }
+  // mixed weights and E_key sums; FP16 weights and sort keys of S_h
+  unsigned long long den = 0ull, num = 0ull, sub = 0ull, cap = 0ull;
   for (int b = threadIdx.x; b < NB; b += CTL_NT) {
     const bool pr = U[b] != 0;
     const float mb = pr ? w.m16[base + b] : w.mhat[base + b];
@@ -134,7 +161,7 @@ __device__ void evaluate_head(const Shape &s, const Step &w, const Thresh &th, i
     if (!pr) {
       const float dl = w.delta[base + b];
       if (dl > 20.0f) {
-        cap = 1;
+        cap = 1ull;
       } else {
         const float up = exp2k(dl) - 1.0f;
         const float dn = 1.0f - exp2k(-dl);
@@ -144,40 +171,41 @@ __device__ void evaluate_head(const Shape &s, const Step &w, const Thresh &th, i
         sub += (unsigned long long)ceil(Wp * gm);
       }
     }
+    uint32_t W16 = 0u;
+    const int pb = pos[b];
+    if (pb != 0xffff) {
+      W16 = (uint32_t)floorf((float)Lb * exp2k(mb - M16));
+      keys[pb] = ((unsigned long long)W16 << 32) | (unsigned long long)(0xffffffffu - (uint32_t)b);
+    }
+    w.W16[base + b] = W16;
   }
-  den = block_sum_u64(den, sh.u64[0]);
-  num = block_sum_u64(num, sh.u64[1]);
-  sub = block_sum_u64(sub, sh.u64[2]);
-  cap = block_or_i32(cap, sh.i32);
+  unsigned long long v4[4] = {den, num, sub, cap};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v4[k] += __shfl_xor(v4[k], o, 64);
+  }
+  if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) sred[k][threadIdx.x >> 6] = v4[k];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    unsigned long long r = 0ull;
+#pragma unroll
+    for (int q = 0; q < CTL_NT / 64; ++q) r += sred[k][q];
+    v4[k] = r;
+  }
   double ek;
-  if (cap) {
+  if (v4[3]) {
     ek = 1.0;
   } else {
-    const long long D = (long long)den - (long long)sub;
-    ek = (D <= 0) ? 1.0 : fmin(1.0, (double)num / (double)D);
+    const long long D = (long long)v4[0] - (long long)v4[2];
+    ek = (D <= 0) ? 1.0 : fmin(1.0, (double)v4[1] / (double)D);
   }
-
-  // ranking over S_h = pi[0 .. n)
-  const int n = w.ssize[(size_t)i * s.Hq + hq];
-  const uint32_t *pi = w.pi + base;
-  float m16loc = -INFINITY;
-  for (int k = threadIdx.x; k < n; k += CTL_NT) m16loc = fmaxf(m16loc, w.m16[base + pi[k]]);
-  const float M16 = block_max_f32(m16loc, sh.f32);
-  for (int b = threadIdx.x; b < NB; b += CTL_NT) w.W16[base + b] = 0u;
-  __syncthreads();
+  // ranking over S_h: FP16 order (W16 descending, index ascending)
   const int n2 = max(64, pow2_at_least(n));
-  for (int k = threadIdx.x; k < n2; k += CTL_NT) {
-    unsigned long long key = 0ull;
-    if (k < n) {
-      const uint32_t b = pi[k];
-      const uint32_t W16 = (uint32_t)floorf((float)w.L16[base + b] * exp2k(w.m16[base + b] - M16));
-      w.W16[base + b] = W16;
-      key = ((unsigned long long)W16 << 32) | (unsigned long long)(0xffffffffu - b);
-      pos[b] = (uint16_t)k;
-    }
-    keys[k] = key;
-  }
-  __syncthreads();
   sort_desc_u64<CTL_NT>(keys, n, n2);
   unsigned long long ssd = 0ull;
   for (int j = threadIdx.x; j < n; j += CTL_NT) {

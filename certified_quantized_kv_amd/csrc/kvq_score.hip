@@ -255,41 +255,50 @@ hipError_t launch_score_int8(const Shape &s, const Tier1 &t, const Step &w, cons
 }
 
 // ---- FP16-key scores of blocks promoted this round ------------------------------
-// One workgroup per (sequence, KV head, block); wave h = query head of the
-// group, lane = token.  The block's FP16 keys are staged with 16-byte
-// coalesced loads into LDS rows padded to d*2 + 16 bytes (conflict-free
-// 16-byte row reads); q' is read at wave-uniform addresses.  Each lane runs
-// the canonical fma chain over channels in ascending order.
+// One workgroup per (sequence, KV head, F16_BPW blocks), four waves per
+// block (one block per workgroup measured fastest); wave h = query head of
+// the group, lane = token.  A block's FP16 keys
+// are staged with 16-byte coalesced loads into LDS rows padded to d*2 + 16
+// bytes (conflict-free 16-byte row reads); q' is read at wave-uniform
+// addresses.  Each lane runs the canonical fma chain over channels in
+// ascending order.
+constexpr int F16_BPW = 1;             // blocks per workgroup (4 waves each)
+
 template <int D>
-__global__ __launch_bounds__(256) void k_score_fp16(Shape s, Step w, SeqTab tab, int layer) {
+__global__ __launch_bounds__(256 * F16_BPW) void k_score_fp16(Shape s, Step w, SeqTab tab, int layer) {
   constexpr int RST = D + 8;            // LDS row stride in halves (d*2 + 16 bytes)
-  const int i = blockIdx.z, g = blockIdx.y, b = blockIdx.x;
+  const int i = blockIdx.z, g = blockIdx.y;
   const int T = tab.T[i], NB = (T + BLOCK - 1) / BLOCK;
-  if (b >= NB) return;
+  const int part = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8);   // block of this thread
+  const int tid = threadIdx.x & 255;
+  const int wave = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) & 3), lane = threadIdx.x & 63;
+  const int b = blockIdx.x * F16_BPW + part;
   uint8_t *flag = w.Knew + ((size_t)i * s.Hkv + g) * s.NBmax + b;
-  if (*flag == 0) return;
+  const bool active = b < NB && *flag != 0;
   const int n = min(BLOCK, T - b * BLOCK);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  __shared__ __align__(16) uint16_t sk[BLOCK * RST];
+  __shared__ __align__(16) uint16_t skall[F16_BPW][BLOCK * RST];
+  uint16_t *sk = skall[part];
 
   // all 64 rows are loaded at once (rows past n of a partial block lie inside
   // the staging buffer; their results are masked below)
   constexpr int NL = BLOCK * D / 8 / 256;
-  const uint16_t *src =
-      w.stage_k + (stage_k_area(s, i, g, tab.slot[i], layer) * s.Tmax + (size_t)b * BLOCK) * D;
-  v4i v[NL];
+  if (active) {
+    const uint16_t *src =
+        w.stage_k + (stage_k_area(s, i, g, tab.slot[i], layer) * s.Tmax + (size_t)b * BLOCK) * D;
+    v4i v[NL];
 #pragma unroll
-  for (int k = 0; k < NL; ++k) {
-    const int idx = threadIdx.x + 256 * k;
-    v[k] = *(const v4i *)(src + (size_t)(idx / (D / 8)) * D + (idx % (D / 8)) * 8);
-  }
+    for (int k = 0; k < NL; ++k) {
+      const int idx = tid + 256 * k;
+      v[k] = *(const v4i *)(src + (size_t)(idx / (D / 8)) * D + (idx % (D / 8)) * 8);
+    }
 #pragma unroll
-  for (int k = 0; k < NL; ++k) {
-    const int idx = threadIdx.x + 256 * k;
-    *(v4i *)&sk[(idx / (D / 8)) * RST + (idx % (D / 8)) * 8] = v[k];
+    for (int k = 0; k < NL; ++k) {
+      const int idx = tid + 256 * k;
+      *(v4i *)&sk[(idx / (D / 8)) * RST + (idx % (D / 8)) * 8] = v[k];
+    }
   }
   __syncthreads();
-  if (wave < s.G) {
+  if (active && wave < s.G) {
     const int hq = g * s.G + wave;
     const float *q = w.qp + ((size_t)i * s.Hq + hq) * D;
     float acc = 0.0f;
@@ -318,14 +327,15 @@ __global__ __launch_bounds__(256) void k_score_fp16(Shape s, Step w, SeqTab tab,
     }
   }
   __syncthreads();
-  if (threadIdx.x == 0) *flag = 0;
+  if (active && tid == 0) *flag = 0;
 }
 
 hipError_t launch_score_fp16(const Shape &s, const Step &w, const SeqTab &tab, int layer,
                              int maxNB, hipStream_t st) {
-  dim3 grid(maxNB, s.Hkv, tab.n);
-  if (s.d == 128) return launch_k(k_score_fp16<128>, grid, dim3(256), 0, st, s, w, tab, layer);
-  return launch_k(k_score_fp16<64>, grid, dim3(256), 0, st, s, w, tab, layer);
+  dim3 grid((maxNB + F16_BPW - 1) / F16_BPW, s.Hkv, tab.n);
+  if (s.d == 128)
+    return launch_k(k_score_fp16<128>, grid, dim3(256 * F16_BPW), 0, st, s, w, tab, layer);
+  return launch_k(k_score_fp16<64>, grid, dim3(256 * F16_BPW), 0, st, s, w, tab, layer);
 }
 
 // ---- test hook: the decision exponential on a vector ------------------------------
