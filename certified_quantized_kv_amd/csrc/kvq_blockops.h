@@ -152,7 +152,7 @@ __device__ __forceinline__ int count_ahead(const unsigned long long *a, int len,
 }
 
 template <int NT, int E>
-__device__ inline void sort_desc_network(unsigned long long *keys, int n) {
+__device__ __forceinline__ void sort_desc_network(unsigned long long *keys, int n) {
   constexpr int CH = 64 * E;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nch = (n + CH - 1) / CH;
@@ -239,7 +239,7 @@ __device__ inline int max_bucket(const int *cnt, int *wbuf) {
 }
 
 template <int NT>
-__device__ inline void sort_desc_u64(unsigned long long *keys, int n, int cap) {
+__device__ __forceinline__ void sort_desc_u64(unsigned long long *keys, int n, int cap) {
   constexpr int SB = SORT_BUCKETS;
   constexpr int PER = SB / NT;           // counters per thread in the scan
   static_assert(SB % NT == 0, "bucket count");

@@ -311,39 +311,35 @@ __global__ __launch_bounds__(CTL_NT) void k_decide(Shape s, Tier1 t, Step w, Seq
   }
   const int T = tab.T[i], NB = (T + BLOCK - 1) / BLOCK;
   const size_t unit = unit_of(s, tab.slot[i], layer, g);
-  // head state of the group, loaded in parallel (one thread per head)
+  // head state and rung-1 decisions of the group: lane hh of wave 0 takes
+  // head hh; "some head widens" is the wave's ballot
   __shared__ uint32_t hf[4];
-  __shared__ double hek[4];
-  __shared__ int hss[4];
-  if (threadIdx.x < s.G) {
-    const size_t o = (size_t)i * s.Hq + g * s.G + threadIdx.x;
-    hf[threadIdx.x] = w.hflags[o];
-    hek[threadIdx.x] = w.ekey64[o];
-    hss[threadIdx.x] = w.ssize[o];
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int any = 0;
-    if (round < th.R1) {
-      for (int hh = 0; hh < s.G; ++hh) {
-        if (hf[hh] & 4u) continue;
-        if (hek[hh] > th.eps_key && hss[hh] < NB) {
-          hss[hh] = min(NB, 2 * hss[hh]);
-          hf[hh] |= 2u;
-          any = 1;
-        }
-      }
+  if (threadIdx.x < 64) {
+    const int hh = threadIdx.x;
+    const size_t o = (size_t)i * s.Hq + g * s.G + hh;
+    uint32_t f = 0u;
+    double ek = 0.0;
+    int ss = 0;
+    bool wid = false;
+    if (hh < s.G) {
+      f = w.hflags[o];
+      ek = w.ekey64[o];
+      ss = w.ssize[o];
+      wid = round < th.R1 && !(f & 4u) && ek > th.eps_key && ss < NB;
     }
-    if (!any)   // final round of this group: rung 3 for heads still above eps_key
-      for (int hh = 0; hh < s.G; ++hh)
-        if (!(hf[hh] & 4u) && hek[hh] > th.eps_key) hf[hh] |= 4u;
-    sh.wid = any;
-  }
-  __syncthreads();
-  if (threadIdx.x < s.G) {
-    const size_t o = (size_t)i * s.Hq + g * s.G + threadIdx.x;
-    w.hflags[o] = hf[threadIdx.x];
-    w.ssize[o] = hss[threadIdx.x];
+    const bool any = __ballot(wid) != 0ull;
+    if (hh < s.G) {
+      if (wid) {
+        ss = min(NB, 2 * ss);
+        f |= 2u;
+      }
+      // final round of this group: rung 3 for heads still above eps_key
+      if (!any && !(f & 4u) && ek > th.eps_key) f |= 4u;
+      hf[hh] = f;
+      w.hflags[o] = f;
+      w.ssize[o] = ss;
+    }
+    if (hh == 0) sh.wid = any ? 1 : 0;
   }
   __syncthreads();
   if (sh.wid) {
@@ -434,12 +430,14 @@ __global__ __launch_bounds__(CTL_NT) void k_decide(Shape s, Tier1 t, Step w, Seq
     }
   }
   // value promotions to copy: runs of V, extracted from an LDS copy
-  __shared__ uint8_t fv[MAX_NB];
-  for (int b = threadIdx.x; b < NB; b += CTL_NT) fv[b] = anyv ? V[b] : 0;
-  __syncthreads();
-  uint32_t *runs = w.runs + (((size_t)i * s.Hkv + g) * 2 + 1) * s.runmax;
-  const int nrv = anyv ? build_runs(fv, NB, runs, tmp) : 0;
-  emit_runs(s, w, i * s.Hkv + g, 1, runs, nrv, tmp + 17);
+  if (anyv) {
+    __shared__ uint8_t fv[MAX_NB];
+    for (int b = threadIdx.x; b < NB; b += CTL_NT) fv[b] = V[b];
+    __syncthreads();
+    uint32_t *runs = w.runs + (((size_t)i * s.Hkv + g) * 2 + 1) * s.runmax;
+    const int nrv = build_runs(fv, NB, runs, tmp);
+    emit_runs(s, w, i * s.Hkv + g, 1, runs, nrv, tmp + 17);
+  }
   if (threadIdx.x == 0) {
     *gs = 1u | (any3 ? 2u : 0u);
     if (any3) atomicOr(&w.plan[2], 2ull);
