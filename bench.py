@@ -364,8 +364,8 @@ def main():
         n2 = len(recs2)
         dense_bytes = L * max_tokens * Hkv * 4 * d
         resid = {
-            "what": "same steps with KVQ_FLAG_RESIDENT_KEYS: promoted FP16 key blocks kept in "
-                    "device memory across steps",
+            "what": "same steps with KVQ_FLAG_RESIDENT_KEYS: FP16 keys kept in device memory "
+                    "(written on append), no key page-in",
             "value": round(toks2 / wall2, 1), "unit": "KV tokens/s",
             "ms_per_step": round(wall2 / a.steps * 1e3, 3),
             "h2d_MB_per_layer": round(sum(r["h2d_bytes"] for r in recs2) / n2 / 1e6, 3),

@@ -49,7 +49,6 @@ struct kvq_ctx {
   hipEvent_t ev_c[32] = {};    // copy timing pairs
   hipEvent_t ev_tot[2] = {};
   unsigned long long *plan_host = nullptr;
-  std::vector<uint8_t> kres;  // [unit][NBmax]: FP16 keys of the block valid in staging
   size_t plan_cap = 0;
   size_t plan_words = 0;
   int last_n = 0, last_layer = -1;
@@ -262,7 +261,6 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out) {
   x->T.assign((size_t)c.max_batch * c.n_layers, 0);
 
   const size_t NU = (size_t)c.max_batch * c.n_layers * c.n_kv_heads;
-  if (s.kres) x->kres.assign(NU * s.NBmax, 0);
   const size_t d = s.d, NBm = s.NBmax, Tm = s.Tmax;
   Tier1 &t = x->t;
   Step &w = x->w;
@@ -307,6 +305,7 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out) {
   x->plan_words = 4 + 2 * plan_kcap(s);
   DA(w.plan, x->plan_words * 8);
   DA(w.stage_k, (s.kres ? NU : B * Hkv) * Tm * d * 2);
+  t.kres = s.kres ? w.stage_k : nullptr;
   DA(w.stage_v, B * Hkv * Tm * d * 2);
   DA(w.part, B * Hkv * (size_t)s.nchmax * G * (d + 2) * 4);
   DA(w.partd, B * Hkv * (size_t)s.nchmax * G * (d + 2) * 4);
@@ -376,9 +375,6 @@ kvq_status kvq_reset_seq(kvq_ctx *ctx, int32_t seq) {
   const Shape &s = ctx->s;
   for (int l = 0; l < s.L; ++l) {
     ctx->T[(size_t)seq * s.L + l] = 0;
-    if (s.kres)
-      std::fill(ctx->kres.begin() + unit_of(s, seq, l, 0) * s.NBmax,
-                ctx->kres.begin() + unit_of(s, seq, l, s.Hkv) * s.NBmax, (uint8_t)0);
     const size_t u0 = unit_of(s, seq, l, 0);
     HIPCK(ctx, hipMemsetD32(reinterpret_cast<hipDeviceptr_t>(ctx->t.vmin + u0 * s.d), 0xff800000u,
                             (size_t)s.Hkv * s.d));
@@ -419,14 +415,6 @@ kvq_status kvq_append(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t *seq
                              (hipStream_t)stream));
   }
   for (int i = 0; i < n; ++i) {
-    // blocks that took new tokens no longer match a resident copy
-    if (s.kres && n_new[i] > 0) {
-      const int64_t Told = ctx->T[(size_t)seq_ids[i] * s.L + layer];
-      for (int g = 0; g < s.Hkv; ++g) {
-        uint8_t *r = ctx->kres.data() + unit_of(s, seq_ids[i], layer, g) * s.NBmax;
-        for (int64_t b = Told / BLOCK; b <= (Told + n_new[i] - 1) / BLOCK; ++b) r[b] = 0;
-      }
-    }
     ctx->T[(size_t)seq_ids[i] * s.L + layer] += n_new[i];
   }
   return KVQ_OK;
@@ -475,25 +463,7 @@ kvq_status issue_copies(kvq_ctx *c, const SeqTab &tab, int layer, const Plan &p,
     const int ig = (int)((e >> 32) & 0xffffu), kind = (int)((e >> 48) & 1u);
     const int i = ig / s.Hkv, g = ig % s.Hkv;
     const size_t u = unit_of(s, tab.slot[i], layer, g);
-    if (kind == 0 && s.kres) {
-      // resident keys: copy the sub-runs not already in device memory
-      uint8_t *res = c->kres.data() + u * s.NBmax;
-      uint16_t *area = c->w.stage_k + u * s.Tmax * s.d;
-      const uint16_t *src = c->t2k_host + u * s.Tmax * s.d;
-      int b = start;
-      while (b < start + len) {
-        if (res[b]) {
-          ++b;
-          continue;
-        }
-        int e = b;
-        while (e < start + len && !res[e]) res[e++] = 1;
-        const size_t off = (size_t)b * BLOCK * s.d;
-        HIPCK(c, hipMemcpyAsync(area + off, src + off, (size_t)(e - b) * blk_bytes,
-                                hipMemcpyHostToDevice, c->cstream));
-        bytes += (int64_t)(e - b) * (int64_t)blk_bytes;
-        b = e;
-      }
+    if (kind == 0 && s.kres) {   // resident keys: already in device memory
       kblocks += len;
       continue;
     }
@@ -540,24 +510,30 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
   if (timing) HIPCK(ctx, hipEventRecord(ctx->ev_tot[0], st));
 
   tm.open(TC_MISC);
-  HIPCK(ctx, launch_reset(s, w, n, st));
+  const float C = (float)(1.4426950408889634 / sqrt((double)s.d));
+  HIPCK(ctx, launch_reset(s, w, n, (const uint16_t *)q, C, st));
   // staging may still be read by the previous step's kernels, and tier 2 was
   // written by earlier appends on this stream: copies wait for both
   HIPCK(ctx, hipEventRecord(ctx->ev_start, st));
   HIPCK(ctx, hipStreamWaitEvent(ctx->cstream, ctx->ev_start, 0));
 
-  const float C = (float)(1.4426950408889634 / sqrt((double)s.d));
-  HIPCK(ctx, launch_qprep(s, w, n, (const uint16_t *)q, C, st));
   tm.open(TC_SCORE8);
   HIPCK(ctx, launch_score_int8(s, ctx->t, w, tab, layer, maxNB, st));
   tm.open(TC_SELECT);
   HIPCK(ctx, launch_select(s, w, tab, ctx->th.tau_ppm, maxNB, st));
   HIPCK(ctx, launch_plan_keys(s, w, tab, maxNB, st));
   tm.close();
+  // with resident keys no copy depends on the selection, so the host reads
+  // the plan only for the statistics
   Plan plan;
-  kvq_status rs = read_plan(ctx, st, plan);
-  if (rs != KVQ_OK) return rs;
-  ++syncs;
+  kvq_status rs = KVQ_OK;
+  if (!s.kres || stats) {
+    rs = read_plan(ctx, st, plan);
+    if (rs != KVQ_OK) return rs;
+    ++syncs;
+  } else {
+    plan.nk = 1;   // score whatever the selection flagged
+  }
   for (int round = 0;; ++round) {
     const bool new_keys = plan.nk > 0;
     if (!plan.ent.empty()) {
@@ -603,18 +579,15 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
         const size_t ig = (size_t)i * s.Hkv + g;
         const size_t bytes = (size_t)((tab.T[i] + BLOCK - 1) / BLOCK) * BLOCK * s.d * 2;
         HIPCK(ctx, tm.copy_begin(TC_COPY, ctx->cstream));
-        if (s.kres) {
-          const int nbk = (tab.T[i] + BLOCK - 1) / BLOCK;
-          std::fill(ctx->kres.begin() + u * s.NBmax, ctx->kres.begin() + u * s.NBmax + nbk,
-                    (uint8_t)1);
+        if (!s.kres) {   // resident keys are in device memory already
+          HIPCK(ctx, hipMemcpyAsync(w.stage_k + ig * s.Tmax * s.d, ctx->t2k_host + u * s.Tmax * s.d,
+                                    bytes, hipMemcpyHostToDevice, ctx->cstream));
+          h2d += (int64_t)bytes;
         }
-        HIPCK(ctx, hipMemcpyAsync(w.stage_k + stage_k_area(s, i, g, tab.slot[i], layer) * s.Tmax * s.d,
-                                  ctx->t2k_host + u * s.Tmax * s.d,
-                                  bytes, hipMemcpyHostToDevice, ctx->cstream));
         HIPCK(ctx, hipMemcpyAsync(w.stage_v + ig * s.Tmax * s.d, ctx->t2v_host + u * s.Tmax * s.d,
                                   bytes, hipMemcpyHostToDevice, ctx->cstream));
         HIPCK(ctx, tm.copy_end(ctx->cstream));
-        h2d += 2 * (int64_t)bytes;
+        h2d += (int64_t)bytes;
       }
     if (any) {
       HIPCK(ctx, hipEventRecord(ctx->ev_copy, ctx->cstream));
@@ -695,9 +668,8 @@ kvq_status kvq_decode_naive(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_
   hipStream_t st = (hipStream_t)stream;
   Step &w = ctx->w;
   // empty U and V: INT8 scores and INT4 values for every block
-  HIPCK(ctx, launch_reset(s, w, n, st));
   const float C = (float)(1.4426950408889634 / sqrt((double)s.d));
-  HIPCK(ctx, launch_qprep(s, w, n, (const uint16_t *)q, C, st));
+  HIPCK(ctx, launch_reset(s, w, n, (const uint16_t *)q, C, st));
   HIPCK(ctx, launch_score_int8(s, ctx->t, w, tab, layer, maxNB, st));
   HIPCK(ctx, launch_decode(s, ctx->t, w, tab, layer, maxNB, false, st));
   HIPCK(ctx, launch_combine(s, w, tab, out, 1, st));

@@ -18,7 +18,8 @@
 // caller's buffer) and new values are staged in LDS; 64-128 threads own a
 // channel each for the key statistics, one thread per (token, value group)
 // quantizes values.  New FP16 rows go straight to tier 2 (pinned host memory
-// mapped into the device address space).
+// mapped into the device address space), and with resident keys the FP16 keys
+// also to their device copy.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -167,6 +168,7 @@ __global__ __launch_bounds__(256) void k_append(Shape s, Tier1 t, AppendArgs a,
     const size_t row = u * s.Tmax + t0 + r;
     *(uint4 *)(t.t2k + row * D + c8) = *(const uint4 *)&kb[r][c8];
     *(uint4 *)(t.t2v + row * D + c8) = *(const uint4 *)&vb[r][c8];
+    if (t.kres) *(uint4 *)(t.kres + row * D + c8) = *(const uint4 *)&kb[r][c8];
     if (n < BLOCK) *(uint4 *)(t.openk + (u * BLOCK + r) * D + c8) = *(const uint4 *)&kb[r][c8];
   }
   if (tid == 0) {

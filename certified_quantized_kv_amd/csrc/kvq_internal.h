@@ -34,6 +34,8 @@ constexpr int DEC_CB = 8;           // blocks per split-K chunk of the decode ke
 //   eta    [NBmax]       f32  per-block value error annotation
 //   vmin/vmax [d]        u32  order-mapped floats, running over all tokens
 //   openk  [64][d]       u16  FP16 keys of the open (partial) block
+//   kres   [Tmax][d]     u16  with resident keys: every FP16 key (written on
+//                             append; the FP16 key staging of the unit)
 // Tier 2, per unit (pinned host, device-mapped): t2k/t2v [Tmax][d] fp16.
 struct Tier1 {
   uint8_t *kcodes;
@@ -44,6 +46,7 @@ struct Tier1 {
   uint32_t *vmin, *vmax;
   uint16_t *openk;
   uint16_t *t2k, *t2v;     // device-mapped pointers to pinned host memory
+  uint16_t *kres;          // resident FP16 keys [unit][Tmax][d], or null
 };
 
 // Per-step scratch, indexed by the position i of a sequence in the call.
@@ -165,8 +168,6 @@ struct AppendArgs {
 hipError_t launch_append(const Shape &s, const Tier1 &t, const AppendArgs &a, const uint16_t *k,
                          const uint16_t *v, int max_blk, hipStream_t st);
 
-hipError_t launch_qprep(const Shape &s, const Step &w, int n, const uint16_t *q, float C,
-                        hipStream_t st);
 hipError_t launch_score_int8(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,
                              int layer, int maxNB, hipStream_t st);
 hipError_t launch_select(const Shape &s, const Step &w, const SeqTab &tab, int tau_ppm, int maxNB,
@@ -177,7 +178,8 @@ hipError_t launch_score_fp16(const Shape &s, const Step &w, const SeqTab &tab, i
                              int maxNB, hipStream_t st);
 hipError_t launch_control(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,
                           int layer, const Thresh &th, int round, int maxNB, hipStream_t st);
-hipError_t launch_reset(const Shape &s, const Step &w, int n, hipStream_t st);
+hipError_t launch_reset(const Shape &s, const Step &w, int n, const uint16_t *q, float C,
+                        hipStream_t st);
 hipError_t launch_finalize(const Shape &s, const Step &w, const SeqTab &tab, const Thresh &th,
                            float *e_key, float *e_val, int8_t *level, hipStream_t st);
 hipError_t launch_decode(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,

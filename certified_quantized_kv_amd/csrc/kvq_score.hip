@@ -41,17 +41,6 @@ namespace kvq {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-__global__ void k_qprep(int total, const uint16_t *__restrict__ q, float C, float *__restrict__ qp) {
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx < total) qp[idx] = h2f(q[idx]) * C;
-}
-
-hipError_t launch_qprep(const Shape &s, const Step &w, int n, const uint16_t *q, float C,
-                        hipStream_t st) {
-  const int total = n * s.Hq * s.d;
-  return launch_k(k_qprep, dim3((total + 255) / 256), dim3(256), 0, st, total, q, C, w.qp);
-}
-
 // Work split: a unit is one (sequence, block, KV head), numbered with the KV
 // head fastest; wave k of the grid (W waves, W a multiple of the KV head
 // count) takes units k, k + W, k + 2W, ...: every wave carries the same load

@@ -96,11 +96,15 @@ hipError_t launch_plan_keys(const Shape &s, const Step &w, const SeqTab &tab, in
   return launch_k(k_plan_keys, dim3(s.Hkv, tab.n), dim3(1024), 0, st, s, w, tab);
 }
 
-// Clears the per-step flags and head state of the first n call positions in
-// one launch (byte arrays [n][Hkv][NBmax] and [n][Hq][NBmax], head/group words).
-__global__ void k_reset(Shape s, Step w, int n) {
+// Step set-up in one launch: q' = fl32(q * C) (log2 units) for the n call
+// positions, and the per-step flags and head state cleared (byte arrays
+// [n][Hkv][NBmax] and [n][Hq][NBmax], head/group words, plan header).
+__global__ void k_reset(Shape s, Step w, int n, const uint16_t *__restrict__ q, float C) {
   const size_t nb_g = (size_t)n * s.Hkv * s.NBmax, nb_h = (size_t)n * s.Hq * s.NBmax;
   const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t k = blockIdx.x * (size_t)blockDim.x + threadIdx.x; k < (size_t)n * s.Hq * s.d;
+       k += stride)
+    w.qp[k] = h2f(q[k]) * C;
   for (size_t k = blockIdx.x * (size_t)blockDim.x + threadIdx.x; k < nb_g; k += stride) {
     w.U[k] = 0;
     w.Knew[k] = 0;
@@ -117,8 +121,9 @@ __global__ void k_reset(Shape s, Step w, int n) {
   if (blockIdx.x == 0 && threadIdx.x < 4) w.plan[threadIdx.x] = 0ull;
 }
 
-hipError_t launch_reset(const Shape &s, const Step &w, int n, hipStream_t st) {
-  return launch_k(k_reset, dim3(64), dim3(256), 0, st, s, w, n);
+hipError_t launch_reset(const Shape &s, const Step &w, int n, const uint16_t *q, float C,
+                        hipStream_t st) {
+  return launch_k(k_reset, dim3(64), dim3(256), 0, st, s, w, n, q, C);
 }
 
 

@@ -61,14 +61,15 @@ typedef int32_t kvq_status;
 /* flags */
 #define KVQ_FLAG_FORCE_DENSE  1u  /* every head at level 4 (exact dense path) */
 #define KVQ_FLAG_TIMING       2u  /* fill kvq_step_stats phase times          */
-/* Promoted FP16 key blocks stay in device memory across steps (one staging
- * area per (slot, layer, KV head), n_layers * max_batch * n_kv_heads *
- * max_tokens * head_dim * 2 bytes instead of max_batch * n_kv_heads * ...):
- * a block is copied from tier 2 the first time it is promoted and again only
- * after an append changed it.  Decisions and outputs are unchanged; only the
- * host-link traffic and the device footprint differ.  Not part of the pages'
- * method (which pages keys in on demand); a device-memory-for-bandwidth
- * trade on GPUs with large HBM. */
+/* FP16 keys kept in device memory (one staging area per (slot, layer, KV
+ * head), n_layers * max_batch * n_kv_heads * max_tokens * head_dim * 2 bytes
+ * instead of max_batch * n_kv_heads * ...): kvq_append writes each new key to
+ * its device copy as well as to tier 2, so promotion copies no keys and the
+ * step reads no promotion list back before the FP16 scoring.  Decisions and
+ * outputs are unchanged; only host-link traffic, host round trips and the
+ * device footprint differ.  Not part of the pages' method (which pages keys
+ * in on demand); a device-memory-for-bandwidth trade on GPUs with large
+ * HBM. */
 #define KVQ_FLAG_RESIDENT_KEYS 4u
 /* The pages' FP16-values ablation (Résultats): every block's values are read
  * in FP16 from tier 2 (V_g = all blocks), so E_val = 0 and rung 2 never
@@ -144,7 +145,7 @@ typedef struct kvq_step_stats {
     float ms_dense;                /* dense fallback decode kernel                */
     float ms_total;                /* whole call, first launch to last            */
     float ms_combine;              /* split-K combine kernel                      */
-    float ms_misc;                 /* reset, q scaling, plan export, finalize     */
+    float ms_misc;                 /* step set-up (q scaling, reset), finalize    */
 } kvq_step_stats;
 
 /* One decode step at one layer (Méthodologie §2-§3): attends over every

@@ -1,12 +1,11 @@
 """GPU tests of KVQ_FLAG_RESIDENT_KEYS (needs an MI355X; marked gpu).
 
-Keeping promoted FP16 key blocks in device memory across steps must change
+Keeping the FP16 keys in device memory (written on append) must change
 nothing but the host-link traffic: over several steps with appends in
-between (which rewrite the open block, so a stale resident copy would show
-up in the FP16 scores), every decision array and output of the resident
-context is bit-identical to the paging context's, and after the first step
-only the blocks that took new tokens are copied again.  The second case
-also checks the result against the oracle.
+between (which rewrite the open block, so a stale device copy would show up
+in the FP16 scores), every decision array and output of the resident
+context is bit-identical to the paging context's, and no key block crosses
+the host link.  The second case also checks the result against the oracle.
 """
 import numpy as np
 import pytest
@@ -71,15 +70,11 @@ def test_resident_keys_bit_identical_over_steps(env):
             assert np.array_equal(x["tr"][k], y["tr"][k]), (step, k)
         assert x["st"]["promoted_key_blocks"] == y["st"]["promoted_key_blocks"]
     blk = 64 * d * 2
-    assert b[0]["st"]["h2d_bytes"] == a[0]["st"]["h2d_bytes"]
-    # later steps: at most the blocks that took new tokens (per KV head) are copied
-    for step in range(1, len(sizes)):
-        n = sizes[step]
-        T_old = T + sum(sizes[:step])
-        touched = 0 if n == 0 else (T_old + n - 1) // 64 - T_old // 64 + 1
-        assert b[step]["st"]["h2d_bytes"] <= touched * Hkv * blk + \
-            b[step]["st"]["promoted_value_blocks"] * blk, (step, b[step]["st"])
-        assert b[step]["st"]["h2d_bytes"] < a[step]["st"]["h2d_bytes"]
+    # resident keys are never copied: only value blocks (rung 2) cross the link
+    for step in range(len(sizes)):
+        st_a, st_b = a[step]["st"], b[step]["st"]
+        assert st_b["h2d_bytes"] == st_b["promoted_value_blocks"] * blk, (step, st_b)
+        assert st_b["h2d_bytes"] < st_a["h2d_bytes"]
 
 
 def test_resident_keys_match_oracle_after_appends(env):
