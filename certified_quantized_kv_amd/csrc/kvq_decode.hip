@@ -127,7 +127,8 @@ __global__ __launch_bounds__(256) void k_decode_dense(Shape s, Tier1 t, Step w, 
 // unsigned 7-bit limbs (rows: head x limb, k: 64 tokens), B = the INT4 codes
 // (k: tokens, n: 16 channels), one v_mfma_i32_16x16x64_i8 per 16 channels.
 // Wave w owns the channel tiles of one value group, so A is built by the
-// wave that uses it (p*s < 2^(e + 28), e from the block's largest scale).
+// wave that uses it (p*s < 2^(e_h + 27), e_h per block and head from the
+// block's largest scale and its largest p).
 //
 // The chunk's softmax reference M_h is the largest block maximum of the
 // scores in use (FP16 on blocks of U, INT8 elsewhere), known from the
@@ -159,20 +160,25 @@ __global__ __launch_bounds__(256) void k_decode_mixed(Shape s, Tier1 t, Step w, 
   const unsigned long long umask = __ballot(lane < nblk && U[b0 + lane] != 0);
   const unsigned long long vmask = __ballot(lane < nblk && V[b0 + lane] != 0);
 
-  // chunk reference per head: max over the chunk's blocks of the block maxima
+  // chunk reference per head: max over the chunk's blocks of the block
+  // maxima; lane 16 h + k keeps head h's maximum of block b0 + k
   float Mh[4];
+  float bmv = -INFINITY;
   {
     const int k = lane & 15;
-    float bm = -INFINITY;
     if (hl < G && k < nblk) {
       const size_t o = ((size_t)i * s.Hq + g * G + hl) * s.NBmax + b0 + k;
-      bm = ((umask >> k) & 1ull) ? w.m16[o] : w.mhat[o];
+      bmv = ((umask >> k) & 1ull) ? w.m16[o] : w.mhat[o];
     }
-    bm = bfly_max<16>(bm);
+    const float bm = bfly_max<16>(bmv);
 #pragma unroll
     for (int h = 0; h < 4; ++h)
       Mh[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bm), 16 * h));
   }
+  // lane 16 h + k: floor(m_b - M_h) of block b0 + k (p <= 2^(m_b - M_h) there),
+  // at least -64
+  const float Ml = hl == 0 ? Mh[0] : hl == 1 ? Mh[1] : hl == 2 ? Mh[2] : Mh[3];
+  const int dmi = (int)floorf(fmaxf(bmv - Ml, -64.0f));
 
   float acc[NTW];
 #pragma unroll
@@ -244,21 +250,31 @@ __global__ __launch_bounds__(256) void k_decode_mixed(Shape s, Tier1 t, Step w, 
       sc = h2f((uint16_t)(cur.meta & 0xffffu));
       of = h2f((uint16_t)(cur.meta >> 16));
     }
+    // fixed point per (block, head): p <= 2^(m_b - M_h) on this block, so
+    // e_h = ilogb(max scale) + floor(m_b - M_h) - 25 keeps p s 2^-e_h < 2^27
+    // and every block's terms at 27 bits relative to its own largest one
     const float smax = bfly_max<64>(sc);
-    const int e = (smax > 0.0f) ? ilogb_f(smax) - 27 : 0;
+    const int il = (smax > 0.0f) ? ilogb_f(smax) : 0;
+    int eh[4];
+    float sce[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      eh[h] = il + __builtin_amdgcn_readlane(dmi, 16 * h + (b - b0)) - 25;
+      sce[h] = ldexpf(sc, -eh[h]);              // exact: a power-of-two scaling
+    }
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
       offacc[h] = fmaf(p[h], of, offacc[h]);
-      const uint32_t A = (uint32_t)rintf(ldexpf(p[h] * sc, -e));
-      Aw[(h * 4 + 0) * AST + lane] = (int8_t)(A & 127u);
-      Aw[(h * 4 + 1) * AST + lane] = (int8_t)((A >> 7) & 127u);
-      Aw[(h * 4 + 2) * AST + lane] = (int8_t)((A >> 14) & 127u);
-      Aw[(h * 4 + 3) * AST + lane] = (int8_t)((A >> 21) & 127u);
+      const uint32_t A = (uint32_t)rintf(p[h] * sce[h]);
+      Aw[(h * 4 + 0) * AST + lane] = (int8_t)__builtin_amdgcn_ubfe(A, 0, 7);
+      Aw[(h * 4 + 1) * AST + lane] = (int8_t)__builtin_amdgcn_ubfe(A, 7, 7);
+      Aw[(h * 4 + 2) * AST + lane] = (int8_t)__builtin_amdgcn_ubfe(A, 14, 7);
+      Aw[(h * 4 + 3) * AST + lane] = (int8_t)__builtin_amdgcn_ubfe(A, 21, 7);
     }
     wave_lds_sync();
     const v4i Aop = *(const v4i *)&Aw[(lane & 15) * AST + 16 * (lane >> 4)];
-    const float f0 = ldexpf(1.0f, e), f1 = ldexpf(1.0f, e + 7), f2 = ldexpf(1.0f, e + 14),
-                f3 = ldexpf(1.0f, e + 21);
+    const int el = hl == 0 ? eh[0] : hl == 1 ? eh[1] : hl == 2 ? eh[2] : eh[3];
+    const float f0 = ldexpf(1.0f, el), f2 = ldexpf(1.0f, el + 14);
 #pragma unroll
     for (int k = 0; k < NTW; ++k) {
       v4i Bop;
@@ -267,12 +283,10 @@ __global__ __launch_bounds__(256) void k_decode_mixed(Shape s, Tier1 t, Step w, 
       Bop[2] = (int)(cur.pk[k].y & 0x0f0f0f0fu);
       Bop[3] = (int)((cur.pk[k].y >> 4) & 0x0f0f0f0fu);
       const v4i Dm = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aop, Bop, (v4i){0, 0, 0, 0}, 0, 0, 0);
-      float a = acc[k];
-      a = fmaf((float)Dm[0], f0, a);
-      a = fmaf((float)Dm[1], f1, a);
-      a = fmaf((float)Dm[2], f2, a);
-      a = fmaf((float)Dm[3], f3, a);
-      acc[k] = a;
+      // limb pairs recombined in int32 (each limb sum < 2^17, so a pair is
+      // below 2^25: at most one rounding of 2^-24 relative in the conversion)
+      const int D01 = Dm[0] + (Dm[1] << 7), D23 = Dm[2] + (Dm[3] << 7);
+      acc[k] = fmaf((float)D23, f2, fmaf((float)D01, f0, acc[k]));
     }
     wave_lds_sync();
   }
