@@ -123,40 +123,45 @@ __global__ __launch_bounds__(256) void k_decode_dense(Shape s, Tier1 t, Step w, 
 
 // Mixed decode.  Per block, sum_t p_ht v_tc with v = off_tj + s_tj code_tc
 // splits into sum_t p_ht off_tj (VALU, per group) and the contraction
-// sum_t (p_ht s_tj) code_tc on the matrix cores: A = fixed-point p*s as four
-// unsigned 7-bit limbs (rows: head x limb, k: 64 tokens), B = the INT4 codes
+// sum_t (p_ht s_tj) code_tc on the matrix cores: A = fixed-point p*s as three
+// signed byte limbs (rows: head x limb, k: 64 tokens), B = the INT4 codes
 // (k: tokens, n: 16 channels), one v_mfma_i32_16x16x64_i8 per 16 channels.
-// Wave w owns the channel tiles of one value group, so A is built by the
-// wave that uses it (p*s < 2^(e_h + 27), e_h per block and head from the
-// block's largest scale and its largest p).
 //
-// The chunk's softmax reference M_h is the largest block maximum of the
-// scores in use (FP16 on blocks of U, INT8 elsewhere), known from the
-// scoring passes, so every wave forms p = 2^(x - M_h) for its block's
-// tokens in registers as the block streams in; scores, value metadata and
-// codes run PF blocks ahead of the block being accumulated.
+// Per (sequence, KV head, chunk of MIX_CB blocks) one workgroup; wave w takes
+// half w % 2 of the channels of blocks b0 + w / 2, b0 + w / 2 + 2, ..., so a
+// block's scores and exponentials are read and formed by two waves.  The
+// chunk's softmax reference M_h is the largest block maximum of the scores in
+// use (FP16 on blocks of U, INT8 elsewhere), known from the scoring passes,
+// so every wave forms p = 2^(x - M_h) in registers as its blocks stream in,
+// and the four waves' sums share that reference (they add without rescaling).
+// Scores, value metadata and codes of a wave's next block load while the
+// current one is accumulated.
 template <int D>
-__global__ __launch_bounds__(256) void k_decode_mixed(Shape s, Tier1 t, Step w, SeqTab tab, int layer) {
-  constexpr int NTW = D / 64;                    // 16-channel tiles per wave
+__global__ __launch_bounds__(256, 6) void k_decode_mixed(Shape s, Tier1 t, Step w, SeqTab tab, int layer) {
+  constexpr int NT = D / 16;                     // 16-channel tiles
+  constexpr int NG = D / VGROUP;                 // value groups (two tiles each)
+  constexpr int NTW = NT / 2, NGW = NG / 2;      // tiles and groups of one wave
   constexpr int AST = 80;                        // LDS row stride of A (bank spread)
-  constexpr int PF = 2;                          // blocks in flight ahead
+  constexpr int PW = MIX_CB / 2;                 // blocks per wave
+  static_assert(MIX_CB <= 16 && MIX_CB % 2 == 0, "block maxima sit in lanes 16 h + k");
   const int i = blockIdx.z, g = blockIdx.y, ch = blockIdx.x;
   const int T = tab.T[i], NB = (T + BLOCK - 1) / BLOCK;
-  const int b0 = ch * DEC_CB;
+  const int b0 = ch * MIX_CB;
   if (b0 >= NB) return;
   const size_t ig = (size_t)i * s.Hkv + g;
   const int G = s.G;
-  const int b1 = min(NB, b0 + DEC_CB);
+  const int b1 = min(NB, b0 + MIX_CB);
   const int nblk = b1 - b0;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int hl = lane >> 4;                      // head of this lane in the MFMA output
-  const int j = (wave * NTW * 16) / VGROUP;      // value group of this wave's tiles
+  const int half = wave & 1, pair = wave >> 1;   // channel half, block parity
   const size_t u = unit_of(s, tab.slot[i], layer, g);
   const uint8_t *U = w.U + ig * s.NBmax;
   const uint8_t *V = w.V + ig * s.NBmax;
 
-  __shared__ __align__(16) int8_t As[4][16 * AST];
+  __shared__ __align__(16) int8_t As[4][NGW][16 * AST];
   __shared__ float pv[4][4][BLOCK];              // p of an FP16-value block, per wave
+  __shared__ float sl[4][4];
   const unsigned long long umask = __ballot(lane < nblk && U[b0 + lane] != 0);
   const unsigned long long vmask = __ballot(lane < nblk && V[b0 + lane] != 0);
 
@@ -175,146 +180,203 @@ __global__ __launch_bounds__(256) void k_decode_mixed(Shape s, Tier1 t, Step w, 
     for (int h = 0; h < 4; ++h)
       Mh[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bm), 16 * h));
   }
-  // lane 16 h + k: floor(m_b - M_h) of block b0 + k (p <= 2^(m_b - M_h) there),
-  // at least -64
-  const float Ml = hl == 0 ? Mh[0] : hl == 1 ? Mh[1] : hl == 2 ? Mh[2] : Mh[3];
-  const int dmi = (int)floorf(fmaxf(bmv - Ml, -64.0f));
 
   float acc[NTW];
 #pragma unroll
   for (int k = 0; k < NTW; ++k) acc[k] = 0.0f;
-  float offacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float offacc[4][NGW];
+#pragma unroll
+  for (int h = 0; h < 4; ++h)
+#pragma unroll
+    for (int j = 0; j < NGW; ++j) offacc[h][j] = 0.0f;
   float lsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   const uint16_t *sv = w.stage_v + ig * s.Tmax * D;
-  int8_t *Aw = As[wave];
 
-  // in-flight ring: scores of the four heads, value metadata, codes
+  // A wave's block in flight: scores of the four heads, its groups' value
+  // metadata of its token, its code tiles.  Loads are unconditional at
+  // clamped indices (token T - 1, head G - 1); masks apply at use.
   struct Stage {
     float x[4];
-    uint32_t meta;
+    uint32_t meta[NGW];
     uint2 pk[NTW];
   };
-  Stage ring[PF];
   auto fetch = [&](Stage &st, int bb) {
-    const int tk = bb * BLOCK + lane;
-    const bool ok = tk < T;
+    const int tk = min(bb * BLOCK + lane, T - 1);
     const bool up = (umask >> (bb - b0)) & 1ull;
-    const float *src = up ? w.sp : w.shat;
+    const float *src = (up ? w.sp : w.shat) + ((size_t)i * s.Hq + g * G) * s.Tmax + tk;
 #pragma unroll
-    for (int h = 0; h < 4; ++h)
-      st.x[h] = (ok && h < G) ? src[((size_t)i * s.Hq + g * G + h) * s.Tmax + tk] : -INFINITY;
-    st.meta = ok ? t.vmeta[(u * s.Tmax + tk) * (D / VGROUP) + j] : 0u;
+    for (int h = 0; h < 4; ++h) st.x[h] = src[(size_t)min(h, G - 1) * s.Tmax];
+    const uint32_t *mp = t.vmeta + (u * s.Tmax + tk) * NG + half * NGW;
+    if constexpr (NGW == 2) {
+      const uint2 m = *(const uint2 *)mp;
+      st.meta[0] = m.x, st.meta[1] = m.y;
+    } else {
+      st.meta[0] = *mp;
+    }
     const uint8_t *vc = t.vcodes + (u * s.NBmax + bb) * (size_t)(32 * D);
 #pragma unroll
     for (int k = 0; k < NTW; ++k)
-      st.pk[k] = *(const uint2 *)(vc + (size_t)((wave * NTW + k) * 64 + lane) * 8);
+      st.pk[k] = *(const uint2 *)(vc + (size_t)((half * NTW + k) * 64 + lane) * 8);
   };
+  // quantized values: p*s as fixed point against the INT4 codes
+  auto body = [&](const Stage &cur, int b) {
+    const bool valid = b * BLOCK + lane < T;
+    float sc[NGW], of[NGW];
+    uint32_t ex = 0;
 #pragma unroll
-  for (int q = 0; q < PF; ++q)
-    if (b0 + q < b1) fetch(ring[q], b0 + q);
-
-  for (int b = b0; b < b1; ++b) {
-    const Stage cur = ring[0];
+    for (int j = 0; j < NGW; ++j) {
+      const uint32_t m = valid ? cur.meta[j] : 0u;
+      sc[j] = h2f((uint16_t)(m & 0xffffu));
+      of[j] = h2f((uint16_t)(m >> 16));
+      ex = max(ex, __builtin_amdgcn_ubfe(m, 10, 5));   // binary16 exponent field of the scale
+    }
+    // E = the largest exponent field in the block (this wave's groups), by
+    // bisection on ballots; every scale is below 2^(E - 14), so with
+    // e = E - 36 and p <= 1 each A = rint(p s 2^-e) is below 2^22 (22 bits
+    // relative to the block's largest scale), and 2^-e, 2^e, 2^(e + 16) are
+    // normal floats (E in [0, 30])
+    int E = 0;
 #pragma unroll
-    for (int q = 0; q + 1 < PF; ++q) ring[q] = ring[q + 1];
-    if (b + PF < b1) fetch(ring[PF - 1], b + PF);
-
-    const int tok = b * BLOCK + lane;
-    const bool valid = tok < T;
+    for (int bit = 4; bit >= 0; --bit)
+      if (__ballot(ex >= (uint32_t)(E | (1 << bit)))) E |= 1 << bit;
+    const float fm = __int_as_float((163 - E) << 23);          // 2^-e
+    const float f0 = __int_as_float((E + 91) << 23);           // 2^e
+    const float f2 = __int_as_float((E + 107) << 23);          // 2^(e + 16)
     float p[4];
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      p[h] = (h < G) ? exp2f(cur.x[h] - Mh[h]) : 0.0f;   // 0 for tokens past T
+      p[h] = (valid && h < G) ? __builtin_amdgcn_exp2f(cur.x[h] - Mh[h]) : 0.0f;
       lsum[h] += p[h];
     }
-    if ((vmask >> (b - b0)) & 1ull) {
-      // FP16 values of a promoted block (rung 2): plain fp32 accumulation
 #pragma unroll
-      for (int h = 0; h < 4; ++h) pv[wave][h][lane] = p[h];
-      wave_lds_sync();
-      const int n = min(BLOCK, T - b * BLOCK);
-#pragma unroll 4
-      for (int r = 0; r < n; ++r) {
-        const float pr = (hl < G) ? pv[wave][hl][r] : 0.0f;
+    for (int j = 0; j < NGW; ++j) {
+      int8_t *Aj = As[wave][j];
+      const float sce = sc[j] * fm;              // exact: a power-of-two scaling
 #pragma unroll
-        for (int k = 0; k < NTW; ++k) {
-          const int c = (wave * NTW + k) * 16 + (lane & 15);
-          acc[k] = fmaf(pr, h2f(sv[((size_t)b * BLOCK + r) * D + c]), acc[k]);
-        }
+      for (int h = 0; h < 4; ++h) {
+        offacc[h][j] = fmaf(p[h], of[j], offacc[h][j]);
+        // rint(p s 2^-e) + 0x808080 in one rounding (the sum stays below
+        // 2^24, where fp32 spacing is 1); the XOR leaves three signed bytes
+        // L0 + 2^8 L1 + 2^16 L2 = rint(p s 2^-e), each in [-128, 127]
+        const uint32_t Bv = (uint32_t)fmaf(p[h], sce, 8421504.0f) ^ 0x808080u;
+        Aj[(h * 4 + 0) * AST + lane] = (int8_t)Bv;
+        Aj[(h * 4 + 1) * AST + lane] = (int8_t)(Bv >> 8);
+        Aj[(h * 4 + 2) * AST + lane] = (int8_t)(Bv >> 16);
       }
-      wave_lds_sync();
-      continue;
-    }
-    float sc = 0.0f, of = 0.0f;
-    if (valid) {
-      sc = h2f((uint16_t)(cur.meta & 0xffffu));
-      of = h2f((uint16_t)(cur.meta >> 16));
-    }
-    // fixed point per (block, head): p <= 2^(m_b - M_h) on this block, so
-    // e_h = ilogb(max scale) + floor(m_b - M_h) - 25 keeps p s 2^-e_h < 2^27
-    // and every block's terms at 27 bits relative to its own largest one
-    const float smax = bfly_max<64>(sc);
-    const int il = (smax > 0.0f) ? ilogb_f(smax) : 0;
-    int eh[4];
-    float sce[4];
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      eh[h] = il + __builtin_amdgcn_readlane(dmi, 16 * h + (b - b0)) - 25;
-      sce[h] = ldexpf(sc, -eh[h]);              // exact: a power-of-two scaling
-    }
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      offacc[h] = fmaf(p[h], of, offacc[h]);
-      const uint32_t A = (uint32_t)rintf(p[h] * sce[h]);
-      Aw[(h * 4 + 0) * AST + lane] = (int8_t)__builtin_amdgcn_ubfe(A, 0, 7);
-      Aw[(h * 4 + 1) * AST + lane] = (int8_t)__builtin_amdgcn_ubfe(A, 7, 7);
-      Aw[(h * 4 + 2) * AST + lane] = (int8_t)__builtin_amdgcn_ubfe(A, 14, 7);
-      Aw[(h * 4 + 3) * AST + lane] = (int8_t)__builtin_amdgcn_ubfe(A, 21, 7);
     }
     wave_lds_sync();
-    const v4i Aop = *(const v4i *)&Aw[(lane & 15) * AST + 16 * (lane >> 4)];
-    const int el = hl == 0 ? eh[0] : hl == 1 ? eh[1] : hl == 2 ? eh[2] : eh[3];
-    const float f0 = ldexpf(1.0f, el), f2 = ldexpf(1.0f, el + 14);
 #pragma unroll
-    for (int k = 0; k < NTW; ++k) {
-      v4i Bop;
-      Bop[0] = (int)(cur.pk[k].x & 0x0f0f0f0fu);
-      Bop[1] = (int)((cur.pk[k].x >> 4) & 0x0f0f0f0fu);
-      Bop[2] = (int)(cur.pk[k].y & 0x0f0f0f0fu);
-      Bop[3] = (int)((cur.pk[k].y >> 4) & 0x0f0f0f0fu);
-      const v4i Dm = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aop, Bop, (v4i){0, 0, 0, 0}, 0, 0, 0);
-      // limb pairs recombined in int32 (each limb sum < 2^17, so a pair is
-      // below 2^25: at most one rounding of 2^-24 relative in the conversion)
-      const int D01 = Dm[0] + (Dm[1] << 7), D23 = Dm[2] + (Dm[3] << 7);
-      acc[k] = fmaf((float)D23, f2, fmaf((float)D01, f0, acc[k]));
+    for (int j = 0; j < NGW; ++j) {
+      const v4i Aop = *(const v4i *)&As[wave][j][(lane & 15) * AST + 16 * (lane >> 4)];
+#pragma unroll
+      for (int k = 2 * j; k < 2 * j + 2; ++k) {
+        v4i Bop;
+        Bop[0] = (int)(cur.pk[k].x & 0x0f0f0f0fu);
+        Bop[1] = (int)((cur.pk[k].x >> 4) & 0x0f0f0f0fu);
+        Bop[2] = (int)(cur.pk[k].y & 0x0f0f0f0fu);
+        Bop[3] = (int)((cur.pk[k].y >> 4) & 0x0f0f0f0fu);
+        const v4i Dm = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aop, Bop, (v4i){0, 0, 0, 0}, 0, 0, 0);
+        // rows 4 h + 0..2 hold head h's limb sums (each below 2^17 in
+        // magnitude), row 4 h + 3 is zero; limbs 0 and 1 recombine in int32
+        // (below 2^26: one rounding of 2^-24 relative in the conversion)
+        const int D01 = Dm[0] + (Dm[1] << 8);
+        acc[k] = fmaf((float)Dm[2], f2, fmaf((float)D01, f0, acc[k]));
+      }
     }
     wave_lds_sync();
+  };
+  // FP16 values of a promoted block (rung 2): plain fp32 accumulation
+  auto body_fp16 = [&](int b) {
+    const int tk = min(b * BLOCK + lane, T - 1);
+    const bool valid = b * BLOCK + lane < T;
+    const bool up = (umask >> (b - b0)) & 1ull;
+    const float *src = (up ? w.sp : w.shat) + ((size_t)i * s.Hq + g * G) * s.Tmax + tk;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const float x = src[(size_t)min(h, G - 1) * s.Tmax];
+      const float p = (valid && h < G) ? __builtin_amdgcn_exp2f(x - Mh[h]) : 0.0f;
+      lsum[h] += p;
+      pv[wave][h][lane] = p;
+    }
+    wave_lds_sync();
+    const int n = min(BLOCK, T - b * BLOCK);
+    for (int r = 0; r < n; ++r) {
+      const float pr = (hl < G) ? pv[wave][hl][r] : 0.0f;
+      const uint16_t *row = sv + ((size_t)b * BLOCK + r) * D + half * NTW * 16 + (lane & 15);
+#pragma unroll
+      for (int k = 0; k < NTW; ++k) acc[k] = fmaf(pr, h2f(row[16 * k]), acc[k]);
+    }
+    wave_lds_sync();
+  };
+  // rows 4 h + 3 of A stay zero (three limbs per head)
+#pragma unroll
+  for (int j = 0; j < NGW; ++j)
+#pragma unroll
+    for (int h = 0; h < 4; ++h) As[wave][j][(h * 4 + 3) * AST + lane] = 0;
+  // fully unrolled over the wave's blocks, so the two stages keep fixed
+  // registers and each wait covers only the older stage's loads; blocks with
+  // FP16 values are skipped here and accumulated afterwards
+  Stage st[2];
+  fetch(st[0], min(b0 + pair, b1 - 1));
+  if (PW > 1) fetch(st[1], min(b0 + pair + 2, b1 - 1));
+#pragma unroll
+  for (int q = 0; q < PW; ++q) {
+    const int bb = b0 + pair + 2 * q;
+    if (bb >= b1) break;
+    if (!((vmask >> (bb - b0)) & 1ull)) body(st[q & 1], bb);
+    __builtin_amdgcn_sched_barrier(0);
+    if (q + 2 < PW) fetch(st[q & 1], min(bb + 4, b1 - 1));
+    __builtin_amdgcn_sched_barrier(0);
   }
-  // offset term of this wave's group and the chunk sums, per head
-  float offh = 0.0f, lh = 0.0f;
+  if (vmask)
+    for (int bb = b0 + pair; bb < b1; bb += 2)
+      if ((vmask >> (bb - b0)) & 1ull) body_fp16(bb);
+
+  // offset terms: head h, group j summed over the wave's tokens; channel
+  // tile k belongs to group k / 2
+  float offs[4][NGW];
+#pragma unroll
+  for (int h = 0; h < 4; ++h)
+#pragma unroll
+    for (int j = 0; j < NGW; ++j) offs[h][j] = bfly_sum<64>(offacc[h][j]);
+#pragma unroll
+  for (int k = 0; k < NTW; ++k) {
+    const float o = hl == 0 ? offs[0][k / 2] : hl == 1 ? offs[1][k / 2] : hl == 2 ? offs[2][k / 2] : offs[3][k / 2];
+    acc[k] += o;
+  }
 #pragma unroll
   for (int h = 0; h < 4; ++h) {
-    const float sh = bfly_sum<64>(offacc[h]);
     const float lv = bfly_sum<64>(lsum[h]);
-    if (h == hl) {
-      offh = sh;
-      lh = lv;
+    if (lane == 0) sl[wave][h] = lv;
+  }
+  // the two block parities' sums (same reference M_h) add in LDS, in the A
+  // area; the softmax sums come from the waves of channel half 0
+  __syncthreads();
+  float *red = (float *)&As[0][0][0];            // [4 waves][NTW][64]
+  static_assert(sizeof(As) >= 4 * NTW * 64 * sizeof(float), "merge fits in the A area");
+#pragma unroll
+  for (int k = 0; k < NTW; ++k) red[(wave * NTW + k) * 64 + lane] = acc[k];
+  __syncthreads();
+  for (int e = threadIdx.x; e < NT * 64; e += 256) {
+    const int k = e / 64, ln = e % 64, h = ln >> 4;
+    const int hf = k / NTW, kk = k % NTW;        // waves hf (parity 0) and 2 + hf (parity 1)
+    if (h < G) {
+      const float v = red[(hf * NTW + kk) * 64 + ln] + red[((2 + hf) * NTW + kk) * 64 + ln];
+      float *part = w.part + ((ig * s.nchmax + ch) * G + h) * (size_t)(D + 2);
+      part[k * 16 + (ln & 15)] = v;
     }
   }
-  if (hl < G) {
-    float *part = w.part + ((ig * s.nchmax + ch) * G + hl) * (size_t)(D + 2);
-#pragma unroll
-    for (int k = 0; k < NTW; ++k) part[(wave * NTW + k) * 16 + (lane & 15)] = acc[k] + offh;
-    if ((lane & 15) == 0 && wave == 0) {
-      part[D] = hl == 0 ? Mh[0] : hl == 1 ? Mh[1] : hl == 2 ? Mh[2] : Mh[3];
-      part[D + 1] = lh;
-    }
+  if (threadIdx.x < G) {
+    const int h = threadIdx.x;
+    float *part = w.part + ((ig * s.nchmax + ch) * G + h) * (size_t)(D + 2);
+    part[D] = h == 0 ? Mh[0] : h == 1 ? Mh[1] : h == 2 ? Mh[2] : Mh[3];
+    part[D + 1] = sl[0][h] + sl[2][h];
   }
 }
 
 hipError_t launch_decode(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,
                          int layer, int maxNB, bool dense, hipStream_t st) {
-  dim3 grid((maxNB + DEC_CB - 1) / DEC_CB, s.Hkv, tab.n);
+  dim3 grid((maxNB + (dense ? DEC_CB : MIX_CB) - 1) / (dense ? DEC_CB : MIX_CB), s.Hkv, tab.n);
   if (s.d == 128) {
     if (dense)
       return launch_k(k_decode_dense<128>, grid, dim3(256), 0, st, s, t, w, tab, layer);
@@ -343,8 +405,9 @@ __global__ __launch_bounds__(256) void k_combine(Shape s, Step w, SeqTab tab, fl
   __shared__ float wred[4];
   const int i = blockIdx.y, hq = blockIdx.x, cq = blockIdx.z;
   const int D = s.d, G = s.G, g = hq / G, h = hq % G, CQ = D / 4;
-  const int NB = (tab.T[i] + BLOCK - 1) / BLOCK, nch = (NB + DEC_CB - 1) / DEC_CB;
   const bool dense = mode == 2 || (mode == 0 && w.hlevel[(size_t)i * s.Hq + hq] >= 3);
+  const int cb = dense ? DEC_CB : MIX_CB;
+  const int NB = (tab.T[i] + BLOCK - 1) / BLOCK, nch = (NB + cb - 1) / cb;
   const float *part = (dense ? w.partd : w.part) + (((size_t)i * s.Hkv + g) * s.nchmax * G + h) * (D + 2);
   const size_t stride = (size_t)G * (D + 2);
   float m = -INFINITY;
