@@ -295,6 +295,7 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out) {
   DA(w.ssd, B * Hq * 8);
   DA(w.ekey64, B * Hq * 8);
   DA(w.eval64, B * Hq * 8);
+  DA(w.evs, B * Hq * 2 * 8);
   DA(w.hflags, B * Hq * 4);
   DA(w.hlevel, B * Hq);
   DA(w.U, B * Hkv * NBm);
@@ -509,19 +510,17 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
   Timer tm{ctx, timing};
   if (timing) HIPCK(ctx, hipEventRecord(ctx->ev_tot[0], st));
 
-  tm.open(TC_MISC);
   const float C = (float)(1.4426950408889634 / sqrt((double)s.d));
-  HIPCK(ctx, launch_reset(s, w, n, (const uint16_t *)q, C, st));
   // staging may still be read by the previous step's kernels, and tier 2 was
   // written by earlier appends on this stream: copies wait for both
   HIPCK(ctx, hipEventRecord(ctx->ev_start, st));
   HIPCK(ctx, hipStreamWaitEvent(ctx->cstream, ctx->ev_start, 0));
 
-  tm.open(TC_SCORE8);
-  HIPCK(ctx, launch_score_int8(s, ctx->t, w, tab, layer, maxNB, st));
+  tm.open(TC_SCORE8);   // INT8 scores, with the step set-up (q', flags cleared)
+  HIPCK(ctx, launch_score_int8(s, ctx->t, w, tab, layer, (const uint16_t *)q, C, st));
   tm.open(TC_SELECT);
   HIPCK(ctx, launch_select(s, w, tab, ctx->th.tau_ppm, maxNB, st));
-  HIPCK(ctx, launch_plan_keys(s, w, tab, maxNB, st));
+  HIPCK(ctx, launch_plan_keys(s, w, tab, st));
   tm.close();
   // with resident keys no copy depends on the selection, so the host reads
   // the plan only for the statistics
@@ -669,8 +668,7 @@ kvq_status kvq_decode_naive(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_
   Step &w = ctx->w;
   // empty U and V: INT8 scores and INT4 values for every block
   const float C = (float)(1.4426950408889634 / sqrt((double)s.d));
-  HIPCK(ctx, launch_reset(s, w, n, (const uint16_t *)q, C, st));
-  HIPCK(ctx, launch_score_int8(s, ctx->t, w, tab, layer, maxNB, st));
+  HIPCK(ctx, launch_score_int8(s, ctx->t, w, tab, layer, (const uint16_t *)q, C, st));
   HIPCK(ctx, launch_decode(s, ctx->t, w, tab, layer, maxNB, false, st));
   HIPCK(ctx, launch_combine(s, w, tab, out, 1, st));
   return KVQ_OK;

@@ -443,4 +443,27 @@ __device__ inline void plan_group_keys(const Shape &s, const Step &w, int i, int
   emit_runs(s, w, i * s.Hkv + g, 0, runs, nr, tmp + 17);
 }
 
+// Step set-up, spread over the threads of the first kernel of a step (nt
+// threads, this one numbered tid): q' = fl32(q * C) (log2 units) for the n
+// call positions, and the per-step flags and head state cleared (byte arrays
+// [n][Hkv][NBmax] and [n][Hq][NBmax], head/group words, plan headers).
+__device__ inline void step_setup(const Shape &s, const Step &w, int n, const uint16_t *q, float C,
+                                  size_t tid, size_t nt) {
+  const size_t nb_g = (size_t)n * s.Hkv * s.NBmax, nb_h = (size_t)n * s.Hq * s.NBmax;
+  for (size_t k = tid; k < (size_t)n * s.Hq * s.d; k += nt) w.qp[k] = h2f(q[k]) * C;
+  for (size_t k = tid; k < nb_g; k += nt) {
+    w.U[k] = 0;
+    w.Knew[k] = 0;
+    w.V[k] = 0;
+  }
+  for (size_t k = tid; k < nb_h; k += nt) w.vh[k] = 0;
+  for (size_t k = tid; k < (size_t)n * s.Hq; k += nt) {
+    w.hflags[k] = 0u;
+    w.ekey64[k] = 0.0;
+    w.eval64[k] = 0.0;
+  }
+  for (size_t k = tid; k < (size_t)n * s.Hkv; k += nt) w.gstat[k] = 0u;
+  if (tid < 4) w.plan[tid] = 0ull;
+}
+
 }  // namespace kvq

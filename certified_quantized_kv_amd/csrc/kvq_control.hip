@@ -114,13 +114,14 @@ __device__ void block_sum_u64_8(unsigned long long (&v)[8], CtlShared &sh) {
 // membership (positions in pi), both references (mixed maximum, FP16 maximum
 // over S_h), then weights, E_key sums and sort keys together.
 __device__ void evaluate_head(const Shape &s, const Step &w, const Thresh &th, int i, int g, int hq,
-                              int NB, unsigned long long *keys, uint16_t *pos, CtlShared &sh) {
+                              int NB, const float *eta, unsigned long long *keys, uint16_t *pos,
+                              CtlShared &sh) {
   const size_t base = ((size_t)i * s.Hq + hq) * s.NBmax;
   const uint8_t *U = w.U + ((size_t)i * s.Hkv + g) * s.NBmax;
   const int n = w.ssize[(size_t)i * s.Hq + hq];
   const uint32_t *pi = w.pi + base;
   __shared__ float mred[2][CTL_NT / 64];
-  __shared__ unsigned long long sred[4][CTL_NT / 64];
+  __shared__ unsigned long long sred[5][CTL_NT / 64];
   // S_h = pi[0 .. n): INT8 position of each member, 0xffff elsewhere
   for (int b = threadIdx.x; b < NB; b += CTL_NT) pos[b] = 0xffff;
   __syncthreads();
@@ -147,8 +148,9 @@ __device__ void evaluate_head(const Shape &s, const Step &w, const Thresh &th, i
     Mt = fmaxf(Mt, mred[0][k]);
     M16 = fmaxf(M16, mred[1][k]);
   }
-  // mixed weights and E_key sums; FP16 weights and sort keys of S_h
-  unsigned long long den = 0ull, num = 0ull, sub = 0ull, cap = 0ull;
+  // mixed weights, E_key sums and the E_val numerator with no value
+  // promoted; FP16 weights and sort keys of S_h
+  unsigned long long den = 0ull, num = 0ull, sub = 0ull, cap = 0ull, numv = 0ull;
   for (int b = threadIdx.x; b < NB; b += CTL_NT) {
     const bool pr = U[b] != 0;
     const float mb = pr ? w.m16[base + b] : w.mhat[base + b];
@@ -158,6 +160,7 @@ __device__ void evaluate_head(const Shape &s, const Step &w, const Thresh &th, i
     const double Wp = (double)(Wt + 65u) * W_UP;
     const double Wm = (double)Wt * W_DN;
     den += (unsigned long long)floor(Wm);
+    numv += (unsigned long long)ceil(Wp * (double)eta[b]);
     if (!pr) {
       const float dl = w.delta[base + b];
       if (dl > 20.0f) {
@@ -179,19 +182,19 @@ __device__ void evaluate_head(const Shape &s, const Step &w, const Thresh &th, i
     }
     w.W16[base + b] = W16;
   }
-  unsigned long long v4[4] = {den, num, sub, cap};
+  unsigned long long v4[5] = {den, num, sub, cap, numv};
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < 5; ++k) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) v4[k] += __shfl_xor(v4[k], o, 64);
   }
   if ((threadIdx.x & 63) == 0) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) sred[k][threadIdx.x >> 6] = v4[k];
+    for (int k = 0; k < 5; ++k) sred[k][threadIdx.x >> 6] = v4[k];
   }
   __syncthreads();
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < 5; ++k) {
     unsigned long long r = 0ull;
 #pragma unroll
     for (int q = 0; q < CTL_NT / 64; ++q) r += sred[k][q];
@@ -220,6 +223,8 @@ __device__ void evaluate_head(const Shape &s, const Step &w, const Thresh &th, i
                     (6000000ull * ssd <= (unsigned long long)(1000000 - th.rho_ppm) * nn * (nn * nn - 1ull));
     w.ssd[(size_t)i * s.Hq + hq] = ssd;
     w.ekey64[(size_t)i * s.Hq + hq] = ek;
+    w.evs[2 * ((size_t)i * s.Hq + hq)] = v4[4];
+    w.evs[2 * ((size_t)i * s.Hq + hq) + 1] = v4[0];
     uint32_t f = w.hflags[(size_t)i * s.Hq + hq];
     f = ok ? (f | 1u) : ((f & ~1u) | 4u);
     w.hflags[(size_t)i * s.Hq + hq] = f;
@@ -281,7 +286,8 @@ __device__ void value_rung(const Shape &s, const Tier1 &t, const Step &w, const 
 // One controller round, part 1: every query head not yet at rung 3, in a
 // group not yet final, is evaluated on the group's current U (one workgroup
 // per query head).
-__global__ __launch_bounds__(CTL_NT) void k_eval(Shape s, Step w, SeqTab tab, Thresh th) {
+__global__ __launch_bounds__(CTL_NT) void k_eval(Shape s, Tier1 t, Step w, SeqTab tab, int layer,
+                                                 Thresh th) {
   extern __shared__ unsigned long long keys[];
   __shared__ uint16_t pos[MAX_NB];
   __shared__ CtlShared sh;
@@ -291,7 +297,8 @@ __global__ __launch_bounds__(CTL_NT) void k_eval(Shape s, Step w, SeqTab tab, Th
   if (w.gstat[(size_t)i * s.Hkv + g] & 1u) return;
   if (w.hflags[(size_t)i * s.Hq + hq] & 4u) return;
   const int NB = (tab.T[i] + BLOCK - 1) / BLOCK;
-  evaluate_head(s, w, th, i, g, hq, NB, keys, pos, sh);
+  const float *eta = t.eta + unit_of(s, tab.slot[i], layer, g) * s.NBmax;
+  evaluate_head(s, w, th, i, g, hq, NB, eta, keys, pos, sh);
 }
 
 // Part 2, one workgroup per (sequence, KV head): rung 1 decisions; a group
@@ -347,31 +354,17 @@ __global__ __launch_bounds__(CTL_NT) void k_decide(Shape s, Tier1 t, Step w, Seq
     plan_group_keys(s, w, i, g, NB);
     return;
   }
-  // E_val ingredients of every head of the group in one pass over the blocks
+  // E_val ingredients of every head of the group (from the evaluation:
+  // numerator with no value promoted, denominator), in LDS so that the head
+  // loop below indexes them freely
   const uint8_t *V = w.V + ((size_t)i * s.Hkv + g) * s.NBmax;
   const float *eta = t.eta + unit * s.NBmax;
+  __shared__ unsigned long long ssum[8];
+  if (threadIdx.x < 2 * s.G) ssum[threadIdx.x] = w.evs[2 * ((size_t)i * s.Hq + g * s.G) + threadIdx.x];
+  __syncthreads();
   unsigned long long sums[8];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) sums[k] = 0ull;
-  for (int b = threadIdx.x; b < NB; b += CTL_NT) {
-    const double eb = (double)eta[b];
-#pragma unroll
-    for (int hh = 0; hh < 4; ++hh) {
-      if (hh >= s.G) continue;
-      const uint32_t Wt = w.Wt[((size_t)i * s.Hq + g * s.G + hh) * s.NBmax + b];
-      sums[2 * hh] += (unsigned long long)ceil((double)(Wt + 65u) * W_UP * eb);
-      sums[2 * hh + 1] += (unsigned long long)floor((double)Wt * W_DN);
-    }
-  }
-  block_sum_u64_8(sums, sh);
-  // rung 2
-  // (the sums go through LDS so that the head loop below indexes them freely)
-  __shared__ unsigned long long ssum[8];
-  if (threadIdx.x == 0) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) ssum[k] = sums[k];
-  }
-  __syncthreads();
+  for (int k = 0; k < 8; ++k) sums[k] = (k < 2 * s.G) ? ssum[k] : 0ull;
   int anyv = 0;
   if (th.fp16_values) {
     // FP16-values ablation: every block's values from tier 2, no rung 2
@@ -452,7 +445,7 @@ hipError_t launch_control(const Shape &s, const Tier1 &t, const Step &w, const S
                           int layer, const Thresh &th, int round, int maxNB, hipStream_t st) {
   const int n2 = max(64, pow2_at_least(maxNB));
   const hipError_t e = launch_k(k_eval, dim3(s.Hq, tab.n), dim3(CTL_NT),
-                                (uint32_t)sort_lds_bytes(n2), st, s, w, tab, th);
+                                (uint32_t)sort_lds_bytes(n2), st, s, t, w, tab, layer, th);
   if (e != hipSuccess) return e;
   return launch_k(k_decide, dim3(s.Hkv, tab.n), dim3(CTL_NT), (uint32_t)sort_lds_bytes(n2), st, s,
                   t, w, tab, layer, th, round);

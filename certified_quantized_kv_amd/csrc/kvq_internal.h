@@ -61,6 +61,7 @@ struct Step {
   int32_t *k0, *ssize;             // [B][Hq]
   unsigned long long *ssd;         // [B][Hq]
   double *ekey64, *eval64;         // [B][Hq]
+  unsigned long long *evs;         // [B][Hq][2] E_val numerator (no value promoted), denominator
   uint32_t *hflags;                // [B][Hq]
   int8_t *hlevel;                  // [B][Hq]
   uint8_t *U, *Knew, *V;           // [B][Hkv][NBmax]
@@ -171,17 +172,14 @@ hipError_t launch_append(const Shape &s, const Tier1 &t, const AppendArgs &a, co
                          const uint16_t *v, int max_blk, hipStream_t st);
 
 hipError_t launch_score_int8(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,
-                             int layer, int maxNB, hipStream_t st);
+                             int layer, const uint16_t *q, float C, hipStream_t st);
 hipError_t launch_select(const Shape &s, const Step &w, const SeqTab &tab, int tau_ppm, int maxNB,
                          hipStream_t st);
-hipError_t launch_plan_keys(const Shape &s, const Step &w, const SeqTab &tab, int maxNB,
-                            hipStream_t st);
+hipError_t launch_plan_keys(const Shape &s, const Step &w, const SeqTab &tab, hipStream_t st);
 hipError_t launch_score_fp16(const Shape &s, const Step &w, const SeqTab &tab, int layer,
                              int maxNB, hipStream_t st);
 hipError_t launch_control(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,
                           int layer, const Thresh &th, int round, int maxNB, hipStream_t st);
-hipError_t launch_reset(const Shape &s, const Step &w, int n, const uint16_t *q, float C,
-                        hipStream_t st);
 hipError_t launch_finalize(const Shape &s, const Step &w, const SeqTab &tab, const Thresh &th,
                            float *e_key, float *e_val, int8_t *level, hipStream_t st);
 hipError_t launch_decode(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,

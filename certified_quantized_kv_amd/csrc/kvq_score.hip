@@ -36,6 +36,7 @@
 
 #include "kvq_device.h"
 #include "kvq_internal.h"
+#include "kvq_blockops.h"
 
 namespace kvq {
 
@@ -46,8 +47,11 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 // count) takes units k, k + W, k + 2W, ...: every wave carries the same load
 // to within one unit, keeps one KV head (one query set) for a sequence, and
 // at any moment the grid streams a contiguous window of blocks per KV head.
+// The kernel also carries the step set-up (q' for the later kernels, flags
+// cleared); its own waves form q' from q directly.
 template <int D>
-__global__ __launch_bounds__(256) void k_score_int8(Shape s, Tier1 t, Step w, SeqTab tab, int layer) {
+__global__ __launch_bounds__(256) void k_score_int8(Shape s, Tier1 t, Step w, SeqTab tab, int layer,
+                                                    const uint16_t *__restrict__ q16, float C) {
   constexpr int CW = D / 16;            // channels per lane-chunk
   constexpr int NKS = D / 64;           // MFMA k-steps per block
   constexpr int AST = D + 16;           // LDS row stride of the A operand (bank spread)
@@ -60,7 +64,6 @@ __global__ __launch_bounds__(256) void k_score_int8(Shape s, Tier1 t, Step w, Se
   const int U = s.Hkv * tab.nbc[tab.n];
   const int W = gridDim.x * 4;
   const int u0 = blockIdx.x * 4 + wave;
-  if (u0 >= U) return;
   auto locate = [&](int uu, int &ii, int &gg, int &bb) {
     ii = 0;
     while (ii + 1 < tab.n && s.Hkv * tab.nbc[ii + 1] <= uu) ++ii;
@@ -74,9 +77,9 @@ __global__ __launch_bounds__(256) void k_score_int8(Shape s, Tier1 t, Step w, Se
   float qv[CW];
   auto load_q = [&]() {
     const int hq = g * s.G + (hv ? h : 0);
-    const float *qsrc = w.qp + ((size_t)i * s.Hq + hq) * D + jc * CW;
+    const uint16_t *qsrc = q16 + ((size_t)i * s.Hq + hq) * D + jc * CW;
 #pragma unroll
-    for (int c = 0; c < CW; ++c) qv[c] = qsrc[c];
+    for (int c = 0; c < CW; ++c) qv[c] = h2f(qsrc[c]) * C;
   };
   // software pipeline: the next unit's codes and metadata are in flight
   // while the current one's scores and block ingredients are formed
@@ -94,8 +97,14 @@ __global__ __launch_bounds__(256) void k_score_int8(Shape s, Tier1 t, Step w, Se
 #pragma unroll
     for (int c = 0; c < CW; ++c) kmn[c] = km[c];
   };
-  load_q();
-  fetch(i, g, b);
+  if (u0 < U) {
+    load_q();
+    fetch(i, g, b);
+  }
+  // the set-up's stores go out while the first unit's loads are in flight
+  step_setup(s, w, tab.n, q16, C, blockIdx.x * (size_t)blockDim.x + threadIdx.x,
+             (size_t)gridDim.x * blockDim.x);
+  if (u0 >= U) return;
   for (int u = u0; u < U; u += W) {
     const int T = tab.T[i];
     const int n = min(BLOCK, T - b * BLOCK);
@@ -232,15 +241,14 @@ static int int8_grid(int resident, int units, int hkv) {
 }
 
 hipError_t launch_score_int8(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,
-                             int layer, int maxNB, hipStream_t st) {
-  (void)maxNB;
+                             int layer, const uint16_t *q, float C, hipStream_t st) {
   const int units = s.Hkv * tab.nbc[tab.n];
   if (s.d == 128) {
     const int grid = int8_grid(grid_score_int8<128>(s), units, s.Hkv);
-    return launch_k(k_score_int8<128>, dim3(grid), dim3(256), 0, st, s, t, w, tab, layer);
+    return launch_k(k_score_int8<128>, dim3(grid), dim3(256), 0, st, s, t, w, tab, layer, q, C);
   }
   const int grid = int8_grid(grid_score_int8<64>(s), units, s.Hkv);
-  return launch_k(k_score_int8<64>, dim3(grid), dim3(256), 0, st, s, t, w, tab, layer);
+  return launch_k(k_score_int8<64>, dim3(grid), dim3(256), 0, st, s, t, w, tab, layer, q, C);
 }
 
 // ---- FP16-key scores of blocks promoted this round ------------------------------

@@ -9,7 +9,8 @@
 //   K* = min k >= 1 with 10^6 sum_{i<k} What_pi(i) >= tau_ppm sum_b What_b.
 // Integer sums make the result independent of reduction order.
 // Promotion is per KV head: U_g = union of the group's top-K* sets; blocks
-// new to U_g are listed as runs of consecutive blocks for the host copies.
+// new to U_g (marked by each head's workgroup) are listed as runs of
+// consecutive blocks for the host copies.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 #include "kvq_blockops.h"
@@ -63,6 +64,7 @@ __global__ __launch_bounds__(SEL_NT) void k_select(Shape s, Step w, SeqTab tab, 
   unsigned long long total;
   const unsigned long long incl = block_incl_scan_u64<SEL_NT>(own, sbuf, &total);
   const unsigned long long need = (unsigned long long)tau_ppm * total;
+  __shared__ int kst;
   unsigned long long pre = incl - own;
   for (int k = 0; k < per; ++k) {
     const int p = p0 + k;                       // K* candidate p + 1
@@ -73,8 +75,42 @@ __global__ __launch_bounds__(SEL_NT) void k_select(Shape s, Step w, SeqTab tab, 
     if (ok && !ok_prev) {
       w.k0[(size_t)i * s.Hq + hq] = p + 1;
       w.ssize[(size_t)i * s.Hq + hq] = p + 1;
+      kst = p + 1;
     }
   }
+  __syncthreads();
+
+  // the head's selection joins the group's new blocks (U is empty at this
+  // point of the step, so every selected block is new)
+  const int g = hq / s.G;
+  const size_t ig = (size_t)i * s.Hkv + g;
+  uint8_t *Kn = w.Knew + ig * s.NBmax;
+  for (int p = threadIdx.x; p < kst; p += SEL_NT)
+    Kn[0xffffffffu - (uint32_t)(keys[p] & 0xffffffffull)] = 1;   // benign race: every writer stores 1
+}
+
+// The group's plan after the selection: U = the new blocks, and their runs.
+__global__ __launch_bounds__(1024) void k_plan_keys(Shape s, Step w, SeqTab tab) {
+  const int i = blockIdx.y, g = blockIdx.x;
+  const int NB = (tab.T[i] + BLOCK - 1) / BLOCK;
+  const size_t ig = (size_t)i * s.Hkv + g;
+  __shared__ int tmp[18];
+  __shared__ uint8_t fk[MAX_NB];
+  const uint8_t *Kn = w.Knew + ig * s.NBmax;
+  uint8_t *U = w.U + ig * s.NBmax;
+  for (int b = threadIdx.x; b < NB; b += blockDim.x) {
+    const uint8_t f = Kn[b];
+    fk[b] = f;
+    if (f) U[b] = 1;
+  }
+  __syncthreads();
+  uint32_t *runs = w.runs + (ig * 2 + 0) * s.runmax;
+  const int nr = build_runs(fk, NB, runs, tmp);
+  emit_runs(s, w, (int)ig, 0, runs, nr, tmp + 17);
+}
+
+hipError_t launch_plan_keys(const Shape &s, const Step &w, const SeqTab &tab, hipStream_t st) {
+  return launch_k(k_plan_keys, dim3(s.Hkv, tab.n), dim3(1024), 0, st, s, w, tab);
 }
 
 hipError_t launch_select(const Shape &s, const Step &w, const SeqTab &tab, int tau_ppm, int maxNB,
@@ -83,48 +119,5 @@ hipError_t launch_select(const Shape &s, const Step &w, const SeqTab &tab, int t
   return launch_k(k_select, dim3(s.Hq, tab.n), dim3(SEL_NT), (uint32_t)sort_lds_bytes(n2), st, s,
                   w, tab, tau_ppm);
 }
-
-__global__ __launch_bounds__(1024) void k_plan_keys(Shape s, Step w, SeqTab tab) {
-  const int i = blockIdx.y, g = blockIdx.x;
-  const int NB = (tab.T[i] + BLOCK - 1) / BLOCK;
-  plan_group_keys(s, w, i, g, NB);
-}
-
-hipError_t launch_plan_keys(const Shape &s, const Step &w, const SeqTab &tab, int maxNB,
-                            hipStream_t st) {
-  (void)maxNB;
-  return launch_k(k_plan_keys, dim3(s.Hkv, tab.n), dim3(1024), 0, st, s, w, tab);
-}
-
-// Step set-up in one launch: q' = fl32(q * C) (log2 units) for the n call
-// positions, and the per-step flags and head state cleared (byte arrays
-// [n][Hkv][NBmax] and [n][Hq][NBmax], head/group words, plan header).
-__global__ void k_reset(Shape s, Step w, int n, const uint16_t *__restrict__ q, float C) {
-  const size_t nb_g = (size_t)n * s.Hkv * s.NBmax, nb_h = (size_t)n * s.Hq * s.NBmax;
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  for (size_t k = blockIdx.x * (size_t)blockDim.x + threadIdx.x; k < (size_t)n * s.Hq * s.d;
-       k += stride)
-    w.qp[k] = h2f(q[k]) * C;
-  for (size_t k = blockIdx.x * (size_t)blockDim.x + threadIdx.x; k < nb_g; k += stride) {
-    w.U[k] = 0;
-    w.Knew[k] = 0;
-    w.V[k] = 0;
-  }
-  for (size_t k = blockIdx.x * (size_t)blockDim.x + threadIdx.x; k < nb_h; k += stride) w.vh[k] = 0;
-  for (size_t k = blockIdx.x * (size_t)blockDim.x + threadIdx.x; k < (size_t)n * s.Hq; k += stride) {
-    w.hflags[k] = 0u;
-    w.ekey64[k] = 0.0;
-    w.eval64[k] = 0.0;
-  }
-  for (size_t k = blockIdx.x * (size_t)blockDim.x + threadIdx.x; k < (size_t)n * s.Hkv; k += stride)
-    w.gstat[k] = 0u;
-  if (blockIdx.x == 0 && threadIdx.x < 4) w.plan[threadIdx.x] = 0ull;
-}
-
-hipError_t launch_reset(const Shape &s, const Step &w, int n, const uint16_t *q, float C,
-                        hipStream_t st) {
-  return launch_k(k_reset, dim3(64), dim3(256), 0, st, s, w, n, q, C);
-}
-
 
 }  // namespace kvq
