@@ -16,12 +16,7 @@ __host__ __device__ inline int pow2_at_least(int n) {
 // Block-wide exclusive scan of small counts (blockDim multiple of 64).
 __device__ inline int block_excl_scan(int v, int *tmp, int &total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  const int x = (int)wave_incl_scan_u32((uint32_t)v);
   if (lane == 63) tmp[wave] = x;
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -100,13 +95,6 @@ __device__ inline void emit_runs(const Shape &s, const Step &w, int ig, int kind
 // position in its own run plus the number of keys of the partner run ahead of
 // it (binary search; the earlier run wins ties, so positions never collide),
 // computed by every thread for its keys before any is written.
-template <int X>
-__device__ __forceinline__ unsigned long long xor_lane_u64(unsigned long long v) {
-  const int lo = xor_lane<X>((int)(uint32_t)v);
-  const int hi = xor_lane<X>((int)(uint32_t)(v >> 32));
-  return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
-}
-
 template <int E, int KK, int J>
 __device__ __forceinline__ void bitonic_stage(unsigned long long (&v)[E], int lane) {
   if constexpr (J < E) {
@@ -221,23 +209,6 @@ __device__ __forceinline__ uint32_t key_image(unsigned long long k) {
 // Buckets larger than this send the whole sort to the comparison network.
 constexpr int SORT_MAX_BUCKET = 48;
 
-// Largest bucket count over the workgroup (counts in cnt[0..SB)).
-template <int NT>
-__device__ inline int max_bucket(const int *cnt, int *wbuf) {
-  constexpr int PER = SORT_BUCKETS / NT;
-  int big = 0;
-#pragma unroll
-  for (int k = 0; k < PER; ++k) big = max(big, cnt[threadIdx.x * PER + k]);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) big = max(big, __shfl_xor(big, o, 64));
-  if ((threadIdx.x & 63) == 0) wbuf[threadIdx.x >> 6] = big;
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < NT / 64; ++k) big = max(big, wbuf[k]);
-  __syncthreads();
-  return big;
-}
-
 template <int NT>
 __device__ __forceinline__ void sort_desc_u64(unsigned long long *keys, int n, int cap) {
   constexpr int SB = SORT_BUCKETS;
@@ -246,40 +217,30 @@ __device__ __forceinline__ void sort_desc_u64(unsigned long long *keys, int n, i
   unsigned long long *tmp = keys + cap;
   int *base = reinterpret_cast<int *>(keys + 2 * (size_t)cap);   // SB + 1 entries
   int *cur = base + SB + 1;                                     // SB entries
-  __shared__ unsigned long long kred[NT / 64];
+  __shared__ unsigned long long kred[2][NT / 64];
   __shared__ uint32_t red[2][NT / 64];
-  __shared__ int wsum[NT / 64];
+  __shared__ int wsum[2][NT / 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __syncthreads();
   // image 1: the key's own binary32 image, over the images' range
-  unsigned long long kmin = ~0ull;
   uint32_t lo = 0xffffffffu, hi = 0u;
   for (int p = threadIdx.x; p < n; p += NT) {
-    const unsigned long long k = keys[p];
-    kmin = min(kmin, k);
-    const uint32_t f = key_image(k);
+    const uint32_t f = key_image(keys[p]);
     lo = min(lo, f);
     hi = max(hi, f);
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    kmin = min(kmin, (unsigned long long)__shfl_xor(kmin, o, 64));
-    lo = min(lo, (uint32_t)__shfl_xor((int)lo, o, 64));
-    hi = max(hi, (uint32_t)__shfl_xor((int)hi, o, 64));
-  }
+  lo = wave_min_u32(lo);
+  hi = wave_max_u32(hi);
   if (lane == 0) {
-    kred[wave] = kmin;
     red[0][wave] = lo;
     red[1][wave] = hi;
   }
   for (int k = threadIdx.x; k < SB; k += NT) cur[k] = 0;
   __syncthreads();
-  kmin = kred[0];
   lo = red[0][0];
   hi = red[1][0];
 #pragma unroll
   for (int k = 1; k < NT / 64; ++k) {
-    kmin = min(kmin, kred[k]);
     lo = min(lo, red[0][k]);
     hi = max(hi, red[1][k]);
   }
@@ -287,33 +248,62 @@ __device__ __forceinline__ void sort_desc_u64(unsigned long long *keys, int n, i
   // linear scale, which separates keys that agree in their leading bits
   bool rel = false;
   int sh = 0;
+  unsigned long long kmin = 0ull;
   auto bucket = [&](unsigned long long k) {
     const int f = rel ? (int)((k - kmin) >> sh) : (int)((key_image(k) - lo) >> sh);
     return SB - 1 - f;
   };
+  int c[PER];
+  int own = 0, xs = 0;
   for (int pass = 0; pass < 2; ++pass) {
     if (pass == 0) {
       const uint32_t span = hi - lo;
       sh = span >= (uint32_t)SB ? (32 - __clz((int)span)) - 12 : 0;
     } else {
       rel = true;
-      unsigned long long kmax = 0ull;
-      for (int p = threadIdx.x; p < n; p += NT) kmax = max(kmax, keys[p]);
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1)
-        kmax = max(kmax, (unsigned long long)__shfl_xor(kmax, o, 64));
-      if (lane == 0) kred[wave] = kmax;
+      unsigned long long kmn = ~0ull, kmx = 0ull;
+      for (int p = threadIdx.x; p < n; p += NT) {
+        kmn = min(kmn, keys[p]);
+        kmx = max(kmx, keys[p]);
+      }
+      kmn = wave_min_u64(kmn);
+      kmx = wave_max_u64(kmx);
+      if (lane == 0) {
+        kred[0][wave] = kmn;
+        kred[1][wave] = kmx;
+      }
       for (int k = threadIdx.x; k < SB; k += NT) cur[k] = 0;
       __syncthreads();
-      kmax = kred[0];
+      kmin = kred[0][0];
+      unsigned long long kmax = kred[1][0];
 #pragma unroll
-      for (int k = 1; k < NT / 64; ++k) kmax = max(kmax, kred[k]);
+      for (int k = 1; k < NT / 64; ++k) {
+        kmin = min(kmin, kred[0][k]);
+        kmax = max(kmax, kred[1][k]);
+      }
       const unsigned long long span = kmax - kmin;
       sh = span >= (unsigned long long)SB ? (64 - __clzll((long long)span)) - 12 : 0;
     }
     for (int p = threadIdx.x; p < n; p += NT) atomicAdd(&cur[bucket(keys[p])], 1);
     __syncthreads();
-    if (max_bucket<NT>(cur, wsum) <= SORT_MAX_BUCKET) break;
+    // this thread's counters [t PER, (t+1) PER): their sum, scanned over the
+    // wave, and the largest count, reduced over the wave
+    own = 0;
+    int big = 0;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      c[k] = cur[threadIdx.x * PER + k];
+      own += c[k];
+      big = max(big, c[k]);
+    }
+    xs = (int)wave_incl_scan_u32((uint32_t)own);
+    big = (int)wave_max_u32((uint32_t)big);
+    if (lane == 63) wsum[0][wave] = xs;
+    if (lane == 0) wsum[1][wave] = big;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NT / 64; ++k) big = max(big, wsum[1][k]);
+    if (big <= SORT_MAX_BUCKET) break;
     if (pass == 1) {
       // clustered keys: comparison network instead (the keys are untouched)
       if (n <= NT)
@@ -324,28 +314,14 @@ __device__ __forceinline__ void sort_desc_u64(unsigned long long *keys, int n, i
         sort_desc_network<NT, 4>(keys, n);
       return;
     }
+    __syncthreads();                     // wsum is written again by pass 1
   }
-  // exclusive scan of the counts -> base (thread t: counters [t PER, (t+1) PER))
-  int c[PER];
-  int own = 0;
-#pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    c[k] = cur[threadIdx.x * PER + k];
-    own += c[k];
-  }
-  int x = own;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) wsum[wave] = x;
-  __syncthreads();
+  // exclusive prefix of the counts -> base
   int before = 0;
 #pragma unroll
   for (int k = 0; k < NT / 64; ++k)
-    if (k < wave) before += wsum[k];
-  int run = before + x - own;
+    if (k < wave) before += wsum[0][k];
+  int run = before + xs - own;
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
     base[threadIdx.x * PER + k] = run;
@@ -389,12 +365,7 @@ template <int NT>
 __device__ inline unsigned long long block_incl_scan_u64(unsigned long long v, unsigned long long *buf,
                                                          unsigned long long *total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  unsigned long long x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const unsigned long long y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  const unsigned long long x = wave_incl_scan_u64(v);
   if (lane == 63) buf[wave] = x;
   __syncthreads();
   unsigned long long before = 0ull, all = 0ull;

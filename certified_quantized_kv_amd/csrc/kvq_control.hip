@@ -43,8 +43,7 @@ struct CtlShared {
 };
 
 __device__ unsigned long long block_sum_u64(unsigned long long v, unsigned long long *buf) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  v = wave_sum_u64(v);
   if ((threadIdx.x & 63) == 0) buf[threadIdx.x >> 6] = v;
   __syncthreads();
   unsigned long long r = 0ull;
@@ -64,8 +63,7 @@ __device__ float block_max_f32(float v, float *buf) {
 }
 
 __device__ int block_or_i32(int v, int *buf) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v |= __shfl_xor(v, o, 64);
+  v = wave_or_i32(v);
   if ((threadIdx.x & 63) == 0) buf[threadIdx.x >> 6] = v;
   __syncthreads();
   int r = 0;
@@ -75,8 +73,7 @@ __device__ int block_or_i32(int v, int *buf) {
 }
 
 __device__ int block_min_i32(int v, int *buf) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
+  v = wave_min_i32(v);
   if ((threadIdx.x & 63) == 0) buf[threadIdx.x >> 6] = v;
   __syncthreads();
   int r = buf[0];
@@ -90,10 +87,7 @@ __device__ void block_sum_u64_8(unsigned long long (&v)[8], CtlShared &sh) {
   __shared__ unsigned long long buf[CTL_NT / 64][8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    unsigned long long x = v[k];
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
-    v[k] = x;
+    v[k] = wave_sum_u64(v[k]);
   }
   if ((threadIdx.x & 63) == 0)
 #pragma unroll
@@ -184,10 +178,7 @@ __device__ void evaluate_head(const Shape &s, const Step &w, const Thresh &th, i
   }
   unsigned long long v4[5] = {den, num, sub, cap, numv};
 #pragma unroll
-  for (int k = 0; k < 5; ++k) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v4[k] += __shfl_xor(v4[k], o, 64);
-  }
+  for (int k = 0; k < 5; ++k) v4[k] = wave_sum_u64(v4[k]);
   if ((threadIdx.x & 63) == 0) {
 #pragma unroll
     for (int k = 0; k < 5; ++k) sred[k][threadIdx.x >> 6] = v4[k];

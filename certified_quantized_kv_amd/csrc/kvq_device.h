@@ -77,8 +77,9 @@ __device__ __forceinline__ float i64_to_f32(long long v) {
 
 // Value of lane j ^ X for every lane j (X a power of two below 64).  Within a
 // row of 16 lanes the exchange is done by DPP moves (quad permutes, the
-// half-row mirror, the row rotate by 8), across rows by ds_swizzle (16) and
-// ds_bpermute (32).
+// half-row mirror, the row rotate by 8), across rows by the CDNA4 lane swaps
+// v_permlane16_swap (rows 0 <-> 1, 2 <-> 3) and v_permlane32_swap (lanes
+// 0..31 <-> 32..63): all on the vector ALU, none through LDS.
 template <int X>
 __device__ __forceinline__ int xor_lane(int v) {
   static_assert(X == 1 || X == 2 || X == 4 || X == 8 || X == 16 || X == 32, "lane xor");
@@ -93,10 +94,117 @@ __device__ __forceinline__ int xor_lane(int v) {
   } else if constexpr (X == 8) {
     return __builtin_amdgcn_mov_dpp(v, 0x128, 0xf, 0xf, false);   // row_ror:8
   } else if constexpr (X == 16) {
-    return __builtin_amdgcn_ds_swizzle(v, 0x401F);                // bitmask mode, xor 16
+    // the swap leaves the partner's value in the first result on odd rows
+    // and in the second on even rows
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (__lane_id() & 16) ? r[0] : r[1];
   } else {
-    return __shfl_xor(v, 32, 64);
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (__lane_id() & 32) ? r[0] : r[1];
   }
+}
+template <int X>
+__device__ __forceinline__ unsigned long long xor_lane_u64(unsigned long long v) {
+  const int lo = xor_lane<X>((int)(uint32_t)v);
+  const int hi = xor_lane<X>((int)(uint32_t)(v >> 32));
+  return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4, 8
+// inside each row of 16 lanes (DPP row_shr, zero shifted in), then the last
+// lane of row 0 is added to row 1 and of row 2 to row 3 (row_bcast:15), and
+// the last lane of row 1 to rows 2 and 3 (row_bcast:31).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xf, false);
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long v) {
+  const uint32_t lo = dpp_u32<CTRL, ROWS>((uint32_t)v), hi = dpp_u32<CTRL, ROWS>((uint32_t)(v >> 32));
+  return ((unsigned long long)hi << 32) | lo;
+}
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x) {
+  x += dpp_u32<0x111, 0xf>(x);
+  x += dpp_u32<0x112, 0xf>(x);
+  x += dpp_u32<0x114, 0xf>(x);
+  x += dpp_u32<0x118, 0xf>(x);
+  x += dpp_u32<0x142, 0xa>(x);
+  x += dpp_u32<0x143, 0xc>(x);
+  return x;
+}
+__device__ __forceinline__ unsigned long long wave_incl_scan_u64(unsigned long long x) {
+  x += dpp_u64<0x111, 0xf>(x);
+  x += dpp_u64<0x112, 0xf>(x);
+  x += dpp_u64<0x114, 0xf>(x);
+  x += dpp_u64<0x118, 0xf>(x);
+  x += dpp_u64<0x142, 0xa>(x);
+  x += dpp_u64<0x143, 0xc>(x);
+  return x;
+}
+
+// Butterfly reductions of integers over the 64 lanes (result in every lane).
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
+  v += xor_lane_u64<32>(v);
+  v += xor_lane_u64<16>(v);
+  v += xor_lane_u64<8>(v);
+  v += xor_lane_u64<4>(v);
+  v += xor_lane_u64<2>(v);
+  v += xor_lane_u64<1>(v);
+  return v;
+}
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+  v = max(v, xor_lane_u64<32>(v));
+  v = max(v, xor_lane_u64<16>(v));
+  v = max(v, xor_lane_u64<8>(v));
+  v = max(v, xor_lane_u64<4>(v));
+  v = max(v, xor_lane_u64<2>(v));
+  v = max(v, xor_lane_u64<1>(v));
+  return v;
+}
+__device__ __forceinline__ unsigned long long wave_min_u64(unsigned long long v) {
+  v = min(v, xor_lane_u64<32>(v));
+  v = min(v, xor_lane_u64<16>(v));
+  v = min(v, xor_lane_u64<8>(v));
+  v = min(v, xor_lane_u64<4>(v));
+  v = min(v, xor_lane_u64<2>(v));
+  v = min(v, xor_lane_u64<1>(v));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)xor_lane<32>((int)v));
+  v = max(v, (uint32_t)xor_lane<16>((int)v));
+  v = max(v, (uint32_t)xor_lane<8>((int)v));
+  v = max(v, (uint32_t)xor_lane<4>((int)v));
+  v = max(v, (uint32_t)xor_lane<2>((int)v));
+  v = max(v, (uint32_t)xor_lane<1>((int)v));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, (uint32_t)xor_lane<32>((int)v));
+  v = min(v, (uint32_t)xor_lane<16>((int)v));
+  v = min(v, (uint32_t)xor_lane<8>((int)v));
+  v = min(v, (uint32_t)xor_lane<4>((int)v));
+  v = min(v, (uint32_t)xor_lane<2>((int)v));
+  v = min(v, (uint32_t)xor_lane<1>((int)v));
+  return v;
+}
+__device__ __forceinline__ int wave_min_i32(int v) {
+  v = min(v, xor_lane<32>(v));
+  v = min(v, xor_lane<16>(v));
+  v = min(v, xor_lane<8>(v));
+  v = min(v, xor_lane<4>(v));
+  v = min(v, xor_lane<2>(v));
+  v = min(v, xor_lane<1>(v));
+  return v;
+}
+__device__ __forceinline__ int wave_or_i32(int v) {
+  v |= xor_lane<32>(v);
+  v |= xor_lane<16>(v);
+  v |= xor_lane<8>(v);
+  v |= xor_lane<4>(v);
+  v |= xor_lane<2>(v);
+  v |= xor_lane<1>(v);
+  return v;
 }
 template <int X>
 __device__ __forceinline__ float xor_lane_f(float v) {
