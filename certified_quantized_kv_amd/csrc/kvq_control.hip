@@ -116,18 +116,45 @@ __device__ void evaluate_head(const Shape &s, const Step &w, const Thresh &th, i
   const uint32_t *pi = w.pi + base;
   __shared__ float mred[2][CTL_NT / 64];
   __shared__ unsigned long long sred[5][CTL_NT / 64];
+  // every per-block input of this thread's blocks b = t + r CTL_NT is loaded
+  // once, up front (both score kinds; the block's kind selects afterwards),
+  // so the passes below wait on no global load
+  constexpr int EB = (MAX_NB + CTL_NT - 1) / CTL_NT;
+  bool pr[EB];
+  float mb[EB], dl[EB], et[EB];
+  uint32_t Lb[EB], pk[EB];
+#pragma unroll
+  for (int r = 0; r < EB; ++r) {
+    const int b = threadIdx.x + r * CTL_NT;
+    if (b < NB) {
+      const float m16 = w.m16[base + b], mh = w.mhat[base + b];
+      const uint32_t l16 = w.L16[base + b], lh = w.Lhat[base + b];
+      pr[r] = U[b] != 0;
+      mb[r] = pr[r] ? m16 : mh;
+      Lb[r] = pr[r] ? l16 : lh;
+      dl[r] = w.delta[base + b];
+      et[r] = eta[b];
+      pk[r] = pi[b];                    // the block at INT8 position b
+    }
+  }
   // S_h = pi[0 .. n): INT8 position of each member, 0xffff elsewhere
   for (int b = threadIdx.x; b < NB; b += CTL_NT) pos[b] = 0xffff;
   __syncthreads();
-  for (int k = threadIdx.x; k < n; k += CTL_NT) pos[pi[k]] = (uint16_t)k;
+#pragma unroll
+  for (int r = 0; r < EB; ++r) {
+    const int k = threadIdx.x + r * CTL_NT;
+    if (k < n) pos[pk[r]] = (uint16_t)k;
+  }
   __syncthreads();
   // references: Mt over the mixed block maxima, M16 over S_h (S_h lies in U)
   float mloc = -INFINITY, m16loc = -INFINITY;
-  for (int b = threadIdx.x; b < NB; b += CTL_NT) {
-    const bool pr = U[b] != 0;
-    const float mb = pr ? w.m16[base + b] : w.mhat[base + b];
-    mloc = fmaxf(mloc, mb);
-    if (pos[b] != 0xffff) m16loc = fmaxf(m16loc, mb);
+#pragma unroll
+  for (int r = 0; r < EB; ++r) {
+    const int b = threadIdx.x + r * CTL_NT;
+    if (b < NB) {
+      mloc = fmaxf(mloc, mb[r]);
+      if (pos[b] != 0xffff) m16loc = fmaxf(m16loc, mb[r]);
+    }
   }
   mloc = bfly_max<64>(mloc);
   m16loc = bfly_max<64>(m16loc);
@@ -145,23 +172,22 @@ __device__ void evaluate_head(const Shape &s, const Step &w, const Thresh &th, i
   // mixed weights, E_key sums and the E_val numerator with no value
   // promoted; FP16 weights and sort keys of S_h
   unsigned long long den = 0ull, num = 0ull, sub = 0ull, cap = 0ull, numv = 0ull;
-  for (int b = threadIdx.x; b < NB; b += CTL_NT) {
-    const bool pr = U[b] != 0;
-    const float mb = pr ? w.m16[base + b] : w.mhat[base + b];
-    const uint32_t Lb = pr ? w.L16[base + b] : w.Lhat[base + b];
-    const uint32_t Wt = (uint32_t)floorf((float)Lb * exp2k(mb - Mt));
+#pragma unroll
+  for (int r = 0; r < EB; ++r) {
+    const int b = threadIdx.x + r * CTL_NT;
+    if (b >= NB) continue;
+    const uint32_t Wt = (uint32_t)floorf((float)Lb[r] * exp2k(mb[r] - Mt));
     w.Wt[base + b] = Wt;
     const double Wp = (double)(Wt + 65u) * W_UP;
     const double Wm = (double)Wt * W_DN;
     den += (unsigned long long)floor(Wm);
-    numv += (unsigned long long)ceil(Wp * (double)eta[b]);
-    if (!pr) {
-      const float dl = w.delta[base + b];
-      if (dl > 20.0f) {
+    numv += (unsigned long long)ceil(Wp * (double)et[r]);
+    if (!pr[r]) {
+      if (dl[r] > 20.0f) {
         cap = 1ull;
       } else {
-        const float up = exp2k(dl) - 1.0f;
-        const float dn = 1.0f - exp2k(-dl);
+        const float up = exp2k(dl[r]) - 1.0f;
+        const float dn = 1.0f - exp2k(-dl[r]);
         const double gp = (double)up * (1.0 + 0x1p-16) + 0x1p-20;
         const double gm = (double)dn * (1.0 + 0x1p-16) + 0x1p-20;
         num += (unsigned long long)ceil(Wp * gp);
@@ -171,7 +197,7 @@ __device__ void evaluate_head(const Shape &s, const Step &w, const Thresh &th, i
     uint32_t W16 = 0u;
     const int pb = pos[b];
     if (pb != 0xffff) {
-      W16 = (uint32_t)floorf((float)Lb * exp2k(mb - M16));
+      W16 = (uint32_t)floorf((float)Lb[r] * exp2k(mb[r] - M16));
       keys[pb] = ((unsigned long long)W16 << 32) | (unsigned long long)(0xffffffffu - (uint32_t)b);
     }
     w.W16[base + b] = W16;

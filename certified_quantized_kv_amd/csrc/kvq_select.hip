@@ -28,8 +28,20 @@ __global__ __launch_bounds__(SEL_NT) void k_select(Shape s, Step w, SeqTab tab, 
   const int n2 = max(64, pow2_at_least(NB));
   const size_t base = ((size_t)i * s.Hq + hq) * s.NBmax;
 
+  // the thread's blocks b = t + r SEL_NT, loaded once
+  constexpr int EB = (MAX_NB + SEL_NT - 1) / SEL_NT;
+  float mh[EB];
+  uint32_t lh[EB];
   float m = -INFINITY;
-  for (int b = threadIdx.x; b < NB; b += SEL_NT) m = fmaxf(m, w.mhat[base + b]);
+#pragma unroll
+  for (int r = 0; r < EB; ++r) {
+    const int b = threadIdx.x + r * SEL_NT;
+    if (b < NB) {
+      mh[r] = w.mhat[base + b];
+      lh[r] = w.Lhat[base + b];
+      m = fmaxf(m, mh[r]);
+    }
+  }
   m = bfly_max<64>(m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
@@ -37,10 +49,13 @@ __global__ __launch_bounds__(SEL_NT) void k_select(Shape s, Step w, SeqTab tab, 
 #pragma unroll
   for (int k = 1; k < SEL_NT / 64; ++k) M = fmaxf(M, red[k]);
 
-  for (int b = threadIdx.x; b < n2; b += SEL_NT) {
+#pragma unroll
+  for (int r = 0; r < EB; ++r) {
+    const int b = threadIdx.x + r * SEL_NT;
+    if (b >= n2) break;
     unsigned long long key = 0ull;
     if (b < NB) {
-      const uint32_t W = (uint32_t)floorf((float)w.Lhat[base + b] * exp2k(w.mhat[base + b] - M));
+      const uint32_t W = (uint32_t)floorf((float)lh[r] * exp2k(mh[r] - M));
       w.What[base + b] = W;
       key = ((unsigned long long)W << 32) | (unsigned long long)(0xffffffffu - (uint32_t)b);
     }
