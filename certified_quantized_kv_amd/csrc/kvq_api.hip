@@ -558,10 +558,14 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
     rounds = round + 1;
     if (!(plan.flags & 1u) && plan.ent.empty()) break;
   }
-  tm.open(TC_MISC);
-  HIPCK(ctx, launch_finalize(s, w, tab, ctx->th, e_key, e_val, level, st));
-  tm.close();
+  // rung 4 and the outputs: with no head at rung 3 (and no forced dense
+  // fallback) no level can change, and the combine kernel writes the outputs
   const bool maybe_dense = ctx->th.force_dense || (plan.flags & 2u);
+  if (maybe_dense) {
+    tm.open(TC_MISC);
+    HIPCK(ctx, launch_finalize(s, w, tab, ctx->th, e_key, e_val, level, st));
+    tm.close();
+  }
   std::vector<uint8_t> gd;
   if (maybe_dense) {
     gd.resize((size_t)n * s.Hkv);
@@ -599,7 +603,8 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
   tm.open(TC_DECODE);
   HIPCK(ctx, launch_decode(s, ctx->t, w, tab, layer, maxNB, false, st));
   tm.open(TC_COMBINE);
-  HIPCK(ctx, launch_combine(s, w, tab, out, 0, st));
+  HIPCK(ctx, launch_combine(s, w, tab, out, 0, maybe_dense ? nullptr : e_key,
+                            maybe_dense ? nullptr : e_val, maybe_dense ? nullptr : level, st));
   tm.close();
   if (timing) HIPCK(ctx, hipEventRecord(ctx->ev_tot[1], st));
 
@@ -670,7 +675,7 @@ kvq_status kvq_decode_naive(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_
   const float C = (float)(1.4426950408889634 / sqrt((double)s.d));
   HIPCK(ctx, launch_score_int8(s, ctx->t, w, tab, layer, (const uint16_t *)q, C, st));
   HIPCK(ctx, launch_decode(s, ctx->t, w, tab, layer, maxNB, false, st));
-  HIPCK(ctx, launch_combine(s, w, tab, out, 1, st));
+  HIPCK(ctx, launch_combine(s, w, tab, out, 1, nullptr, nullptr, nullptr, st));
   return KVQ_OK;
 }
 
@@ -700,7 +705,7 @@ kvq_status kvq_dense_decode(kvq_ctx *ctx, int32_t n, const int32_t *seq_lens, co
   a.v = (const uint16_t *)v;
   hipStream_t st = (hipStream_t)stream;
   HIPCK(ctx, launch_dense_vram(s, ctx->w, a, maxNB, st));
-  HIPCK(ctx, launch_combine(s, ctx->w, tab, out, 2, st));
+  HIPCK(ctx, launch_combine(s, ctx->w, tab, out, 2, nullptr, nullptr, nullptr, st));
   return KVQ_OK;
 }
 

@@ -13,26 +13,22 @@ __host__ __device__ inline int pow2_at_least(int n) {
   return p;
 }
 
-// Block-wide exclusive scan of small counts (blockDim multiple of 64).
+// Block-wide exclusive scan of small counts (blockDim multiple of 64); every
+// thread adds up the wave totals below its own.  tmp holds blockDim / 64
+// entries and is free again after the caller's next barrier.
 __device__ inline int block_excl_scan(int v, int *tmp, int &total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int x = (int)wave_incl_scan_u32((uint32_t)v);
   if (lane == 63) tmp[wave] = x;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int acc = 0;
-    for (int k = 0; k < nw; ++k) {
-      const int c = tmp[k];
-      tmp[k] = acc;
-      acc += c;
-    }
-    tmp[nw] = acc;
+  int before = 0, all = 0;
+  for (int k = 0; k < nw; ++k) {
+    const int c = tmp[k];
+    if (k < wave) before += c;
+    all += c;
   }
-  __syncthreads();
-  const int r = x - v + tmp[wave];
-  total = tmp[nw];
-  __syncthreads();
-  return r;
+  total = all;
+  return before + x - v;
 }
 
 // Runs of consecutive set flags (flags[0..NB)) -> runs[k] = start | len << 16.

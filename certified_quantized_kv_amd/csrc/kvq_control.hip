@@ -469,11 +469,6 @@ hipError_t launch_control(const Shape &s, const Tier1 &t, const Step &w, const S
 }
 
 // ---- rung 4 and the per-head outputs ---------------------------------------------
-__device__ __forceinline__ float f32_up(double x) {
-  float f = (float)x;
-  if ((double)f < x) f = __uint_as_float(__float_as_uint(f) + 1u);   // x >= 0
-  return f;
-}
 
 __global__ void k_finalize(Shape s, Step w, SeqTab tab, Thresh th, float *e_key, float *e_val,
                            int8_t *level) {

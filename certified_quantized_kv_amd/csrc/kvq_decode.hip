@@ -399,12 +399,22 @@ hipError_t launch_decode(const Shape &s, const Tier1 &t, const Step &w, const Se
 constexpr int COMB_MAXCH = 1024;
 static_assert((MAX_NB + DEC_CB - 1) / DEC_CB <= COMB_MAXCH, "chunk weights fit in LDS");
 
-__global__ __launch_bounds__(256) void k_combine(Shape s, Step w, SeqTab tab, float *out, int mode) {
+// With `level` non-null (a certified step in which no head reached rung 3, so
+// no rung 4 either) the workgroup of channel quarter 0 also writes the
+// head's outputs: level, and E_key, E_val rounded up to binary32.
+__global__ __launch_bounds__(256) void k_combine(Shape s, Step w, SeqTab tab, float *out, int mode,
+                                                 float *e_key, float *e_val, int8_t *level) {
   __shared__ float fw[COMB_MAXCH];
   __shared__ float red[256];
   __shared__ float wred[4];
   const int i = blockIdx.y, hq = blockIdx.x, cq = blockIdx.z;
   const int D = s.d, G = s.G, g = hq / G, h = hq % G, CQ = D / 4;
+  if (level && cq == 0 && threadIdx.x == 0) {
+    const size_t o = (size_t)i * s.Hq + hq;
+    level[o] = w.hlevel[o];
+    e_key[o] = f32_up(w.ekey64[o]);
+    e_val[o] = f32_up(w.eval64[o]);
+  }
   const bool dense = mode == 2 || (mode == 0 && w.hlevel[(size_t)i * s.Hq + hq] >= 3);
   const int cb = dense ? DEC_CB : MIX_CB;
   const int NB = (tab.T[i] + BLOCK - 1) / BLOCK, nch = (NB + cb - 1) / cb;
@@ -447,8 +457,9 @@ __global__ __launch_bounds__(256) void k_combine(Shape s, Step w, SeqTab tab, fl
 }
 
 hipError_t launch_combine(const Shape &s, const Step &w, const SeqTab &tab, float *out, int mode,
-                          hipStream_t st) {
-  return launch_k(k_combine, dim3(s.Hq, tab.n, 4), dim3(256), 0, st, s, w, tab, out, mode);
+                          float *e_key, float *e_val, int8_t *level, hipStream_t st) {
+  return launch_k(k_combine, dim3(s.Hq, tab.n, 4), dim3(256), 0, st, s, w, tab, out, mode, e_key,
+                  e_val, level);
 }
 
 }  // namespace kvq

@@ -70,6 +70,13 @@ __device__ __forceinline__ float nextup_pos(float x) {
   return __uint_as_float(__float_as_uint(x) + 1u);
 }
 
+// Smallest float >= x for x >= 0 (a bound rounded up to binary32).
+__device__ __forceinline__ float f32_up(double x) {
+  float f = (float)x;
+  if ((double)f < x) f = __uint_as_float(__float_as_uint(f) + 1u);
+  return f;
+}
+
 // int64 -> fp32, one rounding (|v| < 2^53 is exact in fp64 first).
 __device__ __forceinline__ float i64_to_f32(long long v) {
   return (float)(double)v;

@@ -186,7 +186,7 @@ hipError_t launch_decode(const Shape &s, const Tier1 &t, const Step &w, const Se
                          int layer, int maxNB, bool dense, hipStream_t st);
 // mode 0: partials chosen by each head's level; 1: mixed partials; 2: dense
 hipError_t launch_combine(const Shape &s, const Step &w, const SeqTab &tab, float *out, int mode,
-                          hipStream_t st);
+                          float *e_key, float *e_val, int8_t *level, hipStream_t st);
 hipError_t launch_dense_vram(const Shape &s, const Step &w, const DenseArgs &a, int maxNB,
                              hipStream_t st);
 hipError_t launch_exp2k(const float *x, float *y, int64_t n, hipStream_t st);
