@@ -22,8 +22,10 @@ against the tier-1 bytes it must read; host-link throughput of promotions.
 Then: the dense FP16 (device-resident cache) and naive INT8/INT4 comparators
 on the same layers; the CPU oracle timed on one layer-step (a bounded
 sample), whose output is also compared with the GPU's for that layer (sampled
-parity); and the same timed steps on a context that keeps promoted FP16 keys
-in device memory across steps.
+parity); the same timed steps on a context that keeps promoted FP16 keys in
+device memory across steps; and on one with a device cache of FP16 key blocks
+sized so that tier 1 plus the cache take the pages' ~56 % of the dense FP16
+cache's device memory.
 """
 import argparse
 import hashlib
@@ -57,6 +59,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-residency", action="store_true",
                    help="skip the second run with promoted FP16 keys kept in device memory")
+    p.add_argument("--no-key-cache", action="store_true",
+                   help="skip the run with a device cache of FP16 key blocks")
     p.add_argument("--no-comparators", action="store_true",
                    help="skip the dense FP16 (device-resident) and naive INT8/INT4 comparators")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -376,6 +380,42 @@ def main():
         }
         cx2.close()
 
+    kcache = None
+    if not a.no_key_cache:
+        # the same steps with a device cache of FP16 key blocks sized so that
+        # tier 1 plus the cache take the pages' ~56 % of the dense FP16
+        # cache's device memory: (0.56 * 4d - tier-1 bytes) / 2d of the key
+        # blocks (27.6 % at d = 128)
+        if resid is None:
+            ctx.close()
+        nbmax = (max_tokens + 63) // 64
+        frac = (0.56 * 4 * d - t1b) / (2 * d)
+        budget = int(frac * L * Hkv * nbmax)
+        cx3 = kvq.Context(L, 1, Hq, Hkv, d, max_tokens, timing=True, key_cache_blocks=budget)
+        prefill(cx3, False, False)
+        recs3 = []
+        wall3, toks3 = run_steps(cx3)
+        last3 = out.clone()
+        instrument(cx3, recs3)
+        n3 = len(recs3)
+        dense_bytes = L * max_tokens * Hkv * 4 * d
+        cached = sum(r["cached_key_blocks"] for r in recs3)
+        paged = sum(r["promoted_key_blocks"] for r in recs3)
+        kcache = {
+            "what": "same steps with KVQ_FLAG_KEY_CACHE: promoted FP16 key blocks kept in a "
+                    "device cache (LRU, blocks used within one pass over the layers are kept)",
+            "budget_blocks": budget, "budget_frac_of_key_blocks": round(frac, 4),
+            "value": round(toks3 / wall3, 1), "unit": "KV tokens/s",
+            "ms_per_step": round(wall3 / a.steps * 1e3, 3),
+            "cached_frac_of_promoted": round(cached / max(1, cached + paged), 4),
+            "h2d_MB_per_layer": round(sum(r["h2d_bytes"] for r in recs3) / n3 / 1e6, 3),
+            "ms_copy_per_layer": round(sum(r["ms_copy"] for r in recs3) / n3, 5),
+            "device_GiB": round(cx3.device_bytes / 2**30, 2),
+            "device_frac_of_dense_fp16_cache": round(cx3.device_bytes / dense_bytes, 3),
+            "last_output_bit_equal_to_default": bool(torch.equal(last3, out_default)),
+        }
+        cx3.close()
+
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "KV tokens/s", "n_gpus": 1,
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(wall / a.steps * 1e3, 3),
@@ -388,11 +428,13 @@ def main():
         "roofline": roofline, "cpu_baseline": cpu,
         "quantized_pass": quantized_pass, "per_kernel_ms": {k: round(v, 5) for k, v in per_kernel.items()},
         "promotion": promo, "level_counts": levels, "comparators": comps, "residency": resid,
+        "key_cache": kcache,
         "parity_sample": parity,
         "tier1_vram_frac_of_fp16": round(t1b / (4 * d), 4),
     }
     print(json.dumps(line), flush=True)
-    ctx.close()
+    if resid is None and kcache is None:
+        ctx.close()
 
 
 if __name__ == "__main__":

@@ -32,7 +32,7 @@ class Config(ctypes.Structure):
                 ("head_dim", I32), ("max_tokens", I32), ("tau_cov_ppm", I32),
                 ("rho_min_ppm", I32), ("widen_rounds", I32), ("layer_frac_ppm", I32),
                 ("eps_key", ctypes.c_double), ("v_tol", ctypes.c_double),
-                ("flags", ctypes.c_uint32)]
+                ("flags", ctypes.c_uint32), ("key_cache_blocks", I64)]
 
 
 class StepStats(ctypes.Structure):
@@ -43,7 +43,8 @@ class StepStats(ctypes.Structure):
                 ("ms_score_fp16", ctypes.c_float), ("ms_control", ctypes.c_float),
                 ("ms_copy", ctypes.c_float), ("ms_decode", ctypes.c_float),
                 ("ms_dense", ctypes.c_float), ("ms_total", ctypes.c_float),
-                ("ms_combine", ctypes.c_float), ("ms_misc", ctypes.c_float)]
+                ("ms_combine", ctypes.c_float), ("ms_misc", ctypes.c_float),
+                ("cached_key_blocks", I64)]
 
     def as_dict(self):
         d = {k: getattr(self, k) for k, _ in self._fields_}
@@ -55,6 +56,7 @@ FLAG_FORCE_DENSE = 1
 FLAG_TIMING = 2
 FLAG_RESIDENT_KEYS = 4
 FLAG_FP16_VALUES = 8
+FLAG_KEY_CACHE = 16
 
 TR = dict(shat=1, sp=2, mhat=3, Lhat=4, delta=5, m16=6, L16=7, What=8, pi=9, Wt=10, W16=11,
           k0=12, ssize=13, ssd=14, ekey64=15, eval64=16, hflags=17, U=18, V=19, vh=20)
@@ -141,7 +143,7 @@ class Context:
     def __init__(self, n_layers, max_batch, n_q_heads, n_kv_heads, head_dim, max_tokens,
                  tau_cov_ppm=995_000, eps_key=1e-3, v_tol=0.25, rho_min_ppm=900_000,
                  widen_rounds=2, layer_frac_ppm=500_000, force_dense=False, timing=False,
-                 resident_keys=False, fp16_values=False):
+                 resident_keys=False, fp16_values=False, key_cache_blocks=0):
         cfg = Config()
         _lib.kvq_default_config(ctypes.byref(cfg), n_layers, max_batch, n_q_heads, n_kv_heads,
                                 head_dim, max_tokens)
@@ -153,7 +155,9 @@ class Context:
         cfg.layer_frac_ppm = layer_frac_ppm
         cfg.flags = ((FLAG_FORCE_DENSE if force_dense else 0) | (FLAG_TIMING if timing else 0) |
                      (FLAG_RESIDENT_KEYS if resident_keys else 0) |
-                     (FLAG_FP16_VALUES if fp16_values else 0))
+                     (FLAG_FP16_VALUES if fp16_values else 0) |
+                     (FLAG_KEY_CACHE if key_cache_blocks > 0 else 0))
+        cfg.key_cache_blocks = key_cache_blocks
         self.cfg = cfg
         self._ctx = ctypes.c_void_p()
         st = _lib.kvq_create(ctypes.byref(cfg), ctypes.byref(self._ctx))

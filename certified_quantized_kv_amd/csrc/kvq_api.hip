@@ -34,8 +34,78 @@ KernelClock *&kernel_clock() {
 }
 }  // namespace kvq
 
+// Device cache of FP16 key blocks (KVQ_FLAG_KEY_CACHE), managed on the host:
+// a block (unit u, block b) has key u * NBmax + b.  Least recently used
+// replacement over an intrusive list (head = most recent); a slot used by
+// this call or within the last n_layers calls (one pass over the layers, so
+// the same layer's previous step) is not evicted, so a working set larger
+// than the cache keeps the cached part instead of cycling through it, and a
+// miss of one KV head cannot evict a block another head of the same call is
+// about to hit.
+struct KeyCache {
+  int64_t slots = 0;
+  int64_t guard = 1;
+  uint16_t *dev = nullptr;             // [slots][BLOCK][d]
+  std::vector<int32_t> of;             // [unit * NBmax + b] -> slot, or -1
+  std::vector<int64_t> owner;          // [slot] -> key, or -1
+  std::vector<int64_t> used;           // [slot] call stamp of the last use
+  std::vector<int32_t> prev, next;
+  int32_t head = -1, tail = -1;
+  std::vector<int32_t> free_slots;
+  int64_t now = 0;
+  uint32_t *list_host = nullptr;       // pinned [2][cap][2]: hits, then admissions
+  uint32_t *list_dev = nullptr;        // device copy of the lists
+  size_t cap = 0;                      // entries per list
+
+  void unlink(int32_t x) {
+    if (prev[x] >= 0) next[prev[x]] = next[x]; else head = next[x];
+    if (next[x] >= 0) prev[next[x]] = prev[x]; else tail = prev[x];
+    prev[x] = next[x] = -1;
+  }
+  void push_front(int32_t x) {
+    prev[x] = -1;
+    next[x] = head;
+    if (head >= 0) prev[head] = x;
+    head = x;
+    if (tail < 0) tail = x;
+  }
+  void touch(int32_t x) {
+    used[x] = now;
+    unlink(x);
+    push_front(x);
+  }
+  void drop(int64_t key) {
+    const int32_t x = of[key];
+    if (x < 0) return;
+    of[key] = -1;
+    owner[x] = -1;
+    unlink(x);
+    free_slots.push_back(x);
+  }
+  // a slot for `key`, or -1 when every slot is protected
+  int32_t admit(int64_t key) {
+    int32_t x = -1;
+    if (!free_slots.empty()) {
+      x = free_slots.back();
+      free_slots.pop_back();
+    } else if (tail >= 0 && used[tail] + guard <= now) {
+      x = tail;
+      of[owner[x]] = -1;
+      unlink(x);
+    } else {
+      return -1;
+    }
+    owner[x] = key;
+    of[key] = x;
+    used[x] = now;
+    push_front(x);
+    return x;
+  }
+};
+
 struct kvq_ctx {
   kvq_config cfg;
+  KeyCache kc;
   Shape s;
   Thresh th;
   Tier1 t;
@@ -91,6 +161,7 @@ void free_all(kvq_ctx *c) {
   if (c->t2k_host) (void)hipHostFree(c->t2k_host);
   if (c->t2v_host) (void)hipHostFree(c->t2v_host);
   if (c->plan_host) (void)hipHostFree(c->plan_host);
+  if (c->kc.list_host) (void)hipHostFree(c->kc.list_host);
   if (c->cstream) (void)hipStreamDestroy(c->cstream);
   if (c->ev_start) (void)hipEventDestroy(c->ev_start);
   if (c->ev_copy) (void)hipEventDestroy(c->ev_copy);
@@ -220,6 +291,13 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out) {
     return KVQ_EINVAL;
   const int G = c.n_q_heads / c.n_kv_heads;
   if (G != 1 && G != 2 && G != 4) return KVQ_EINVAL;
+  const bool kcache = (c.flags & KVQ_FLAG_KEY_CACHE) != 0;
+  // cache rows and staging rows are listed as 32-bit row numbers
+  if (kcache && ((c.flags & KVQ_FLAG_RESIDENT_KEYS) || c.key_cache_blocks < 1 ||
+                 c.key_cache_blocks > ((int64_t)1 << 25) ||
+                 (int64_t)c.max_batch * c.n_kv_heads * ((c.max_tokens + BLOCK - 1) / BLOCK) * BLOCK >=
+                     ((int64_t)1 << 32)))
+    return KVQ_EINVAL;
   if (c.tau_cov_ppm < 1 || c.tau_cov_ppm > 1000000 || c.rho_min_ppm < -1000000 ||
       c.rho_min_ppm > 1000000 || c.widen_rounds < 0 || c.widen_rounds > 12 ||
       c.layer_frac_ppm < 0 || c.layer_frac_ppm > 1000000 || !(c.eps_key >= 0.0) ||
@@ -311,6 +389,12 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out) {
   DA(w.part, B * Hkv * (size_t)s.nchmax * G * (d + 2) * 4);
   DA(w.partd, B * Hkv * (size_t)s.nchmax * G * (d + 2) * 4);
   DA(w.gdense, B * Hkv);
+  if (kcache) {
+    x->kc.slots = c.key_cache_blocks;
+    x->kc.cap = B * Hkv * NBm;
+    DA(x->kc.dev, (size_t)c.key_cache_blocks * BLOCK * d * 2);
+    DA(x->kc.list_dev, 2 * x->kc.cap * 2 * 4);
+  }
 #undef DA
   if (e != hipSuccess) {
     x->err = std::string("device allocation: ") + hipGetErrorString(e);
@@ -333,6 +417,18 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out) {
   if (e == hipSuccess) e = hipHostGetDevicePointer(&dv, x->t2v_host, 0);
   x->plan_cap = 4096;
   if (e == hipSuccess) e = hipHostMalloc((void **)&x->plan_host, (4 + x->plan_cap) * 8, 0);
+  if (e == hipSuccess && kcache) {
+    e = hipHostMalloc((void **)&x->kc.list_host, 2 * x->kc.cap * 2 * 4, 0);
+    KeyCache &kc = x->kc;
+    kc.guard = (int64_t)c.n_layers + 1;
+    kc.of.assign(NU * NBm, -1);
+    kc.owner.assign((size_t)kc.slots, -1);
+    kc.used.assign((size_t)kc.slots, 0);
+    kc.prev.assign((size_t)kc.slots, -1);
+    kc.next.assign((size_t)kc.slots, -1);
+    kc.free_slots.resize((size_t)kc.slots);
+    for (int64_t k = 0; k < kc.slots; ++k) kc.free_slots[(size_t)k] = (int32_t)(kc.slots - 1 - k);
+  }
   if (e == hipSuccess) e = hipStreamCreateWithFlags(&x->cstream, hipStreamNonBlocking);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&x->ev_start, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&x->ev_copy, hipEventDisableTiming);
@@ -375,6 +471,11 @@ kvq_status kvq_reset_seq(kvq_ctx *ctx, int32_t seq) {
   if (!ctx || seq < 0 || seq >= ctx->cfg.max_batch) return KVQ_EINVAL;
   const Shape &s = ctx->s;
   for (int l = 0; l < s.L; ++l) {
+    if (ctx->kc.slots) {
+      const int64_t nb = (ctx->T[(size_t)seq * s.L + l] + BLOCK - 1) / BLOCK;
+      for (int g = 0; g < s.Hkv; ++g)
+        for (int64_t b = 0; b < nb; ++b) ctx->kc.drop((int64_t)unit_of(s, seq, l, g) * s.NBmax + b);
+    }
     ctx->T[(size_t)seq * s.L + l] = 0;
     const size_t u0 = unit_of(s, seq, l, 0);
     HIPCK(ctx, hipMemsetD32(reinterpret_cast<hipDeviceptr_t>(ctx->t.vmin + u0 * s.d), 0xff800000u,
@@ -416,6 +517,13 @@ kvq_status kvq_append(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t *seq
                              (hipStream_t)stream));
   }
   for (int i = 0; i < n; ++i) {
+    if (ctx->kc.slots && n_new[i] > 0) {
+      // the block holding the old end (if partial) and every new block
+      const int64_t b0 = a.T_old[i] / BLOCK, b1 = (a.T_old[i] + n_new[i] - 1) / BLOCK;
+      for (int g = 0; g < s.Hkv; ++g)
+        for (int64_t b = b0; b <= b1; ++b)
+          ctx->kc.drop((int64_t)unit_of(s, seq_ids[i], layer, g) * s.NBmax + b);
+    }
     ctx->T[(size_t)seq_ids[i] * s.L + layer] += n_new[i];
   }
   return KVQ_OK;
@@ -455,10 +563,27 @@ kvq_status read_plan(kvq_ctx *c, hipStream_t st, Plan &p) {
 }
 
 // Issues the copies of a plan on the copy stream; returns bytes and blocks.
+// With the key cache, a key run splits into cached blocks (one device-side
+// gather from their slots) and runs of uncached blocks (host link), and the
+// uncached blocks that find a slot are copied into it from the staging
+// buffer once their host copies have landed.
 kvq_status issue_copies(kvq_ctx *c, const SeqTab &tab, int layer, const Plan &p, int64_t &bytes,
-                        int64_t &kblocks, int64_t &vblocks) {
+                        int64_t &kblocks, int64_t &vblocks, int64_t &kcached) {
   const Shape &s = c->s;
   const size_t blk_bytes = (size_t)BLOCK * s.d * 2;
+  KeyCache &kc = c->kc;
+  uint32_t *hits = kc.list_host, *adm = kc.list_host ? kc.list_host + 2 * kc.cap : nullptr;
+  size_t nh = 0, na = 0;
+  auto h2d = [&](int kind, size_t u, int ig, int start, int len) -> kvq_status {
+    const size_t srow = u * s.Tmax + (size_t)start * BLOCK;
+    const size_t drow = (size_t)ig * s.Tmax + (size_t)start * BLOCK;
+    uint16_t *dst = (kind ? c->w.stage_v : c->w.stage_k) + drow * s.d;
+    const uint16_t *src = (kind ? c->t2v_host : c->t2k_host) + srow * s.d;
+    HIPCK(c, hipMemcpyAsync(dst, src, (size_t)len * blk_bytes, hipMemcpyHostToDevice, c->cstream));
+    bytes += (int64_t)len * (int64_t)blk_bytes;
+    (kind ? vblocks : kblocks) += len;
+    return KVQ_OK;
+  };
   for (const unsigned long long e : p.ent) {
     const int len = (int)(e & 0xffffu), start = (int)((e >> 16) & 0xffffu);
     const int ig = (int)((e >> 32) & 0xffffu), kind = (int)((e >> 48) & 1u);
@@ -468,13 +593,52 @@ kvq_status issue_copies(kvq_ctx *c, const SeqTab &tab, int layer, const Plan &p,
       kblocks += len;
       continue;
     }
-    const size_t srow = u * s.Tmax + (size_t)start * BLOCK;
-    const size_t drow = (size_t)ig * s.Tmax + (size_t)start * BLOCK;
-    uint16_t *dst = (kind ? c->w.stage_v : c->w.stage_k) + drow * s.d;
-    const uint16_t *src = (kind ? c->t2v_host : c->t2k_host) + srow * s.d;
-    HIPCK(c, hipMemcpyAsync(dst, src, (size_t)len * blk_bytes, hipMemcpyHostToDevice, c->cstream));
-    bytes += (int64_t)len * (int64_t)blk_bytes;
-    (kind ? vblocks : kblocks) += len;
+    if (kind == 1 || !kc.slots) {
+      const kvq_status r = h2d(kind, u, ig, start, len);
+      if (r != KVQ_OK) return r;
+      continue;
+    }
+    if (start + len > s.NBmax || (size_t)ig >= (size_t)s.B * s.Hkv)
+      return fail(c, KVQ_EHIP, "promotion entry out of range");
+    const int64_t key0 = (int64_t)u * s.NBmax;
+    const uint32_t row0 = (uint32_t)((size_t)ig * s.Tmax);
+    for (int b = start; b < start + len;) {
+      const int32_t x = kc.of[(size_t)(key0 + b)];
+      if (x >= 0) {                     // cached: gather from the slot
+        kc.touch(x);
+        hits[2 * nh] = (uint32_t)x * BLOCK;
+        hits[2 * nh + 1] = row0 + (uint32_t)b * BLOCK;
+        ++nh;
+        ++kcached;
+        ++b;
+        continue;
+      }
+      int e2 = b + 1;
+      while (e2 < start + len && kc.of[(size_t)(key0 + e2)] < 0) ++e2;
+      const kvq_status r = h2d(0, u, ig, b, e2 - b);
+      if (r != KVQ_OK) return r;
+      for (int bb = b; bb < e2; ++bb) {
+        const int32_t y = kc.admit(key0 + bb);
+        if (y < 0) break;               // every slot protected: no further admission
+        adm[2 * na] = row0 + (uint32_t)bb * BLOCK;
+        adm[2 * na + 1] = (uint32_t)y * BLOCK;
+        ++na;
+      }
+      b = e2;
+    }
+  }
+  if (nh > kc.cap || na > kc.cap) return fail(c, KVQ_EHIP, "cache list overflow");
+  // the gather (slots -> staging), then the admissions (staging -> slots,
+  // after the host copies on this stream); each list goes over first
+  if (nh > 0) {
+    HIPCK(c, hipMemcpyAsync(kc.list_dev, hits, nh * 8, hipMemcpyHostToDevice, c->cstream));
+    HIPCK(c, launch_copy_blocks(kc.list_dev, (int)nh, kc.dev, c->w.stage_k, s.d, c->cstream));
+  }
+  if (na > 0) {
+    HIPCK(c, hipMemcpyAsync(kc.list_dev + 2 * kc.cap, adm, na * 8, hipMemcpyHostToDevice,
+                            c->cstream));
+    HIPCK(c, launch_copy_blocks(kc.list_dev + 2 * kc.cap, (int)na, c->w.stage_k, kc.dev, s.d,
+                                c->cstream));
   }
   return KVQ_OK;
 }
@@ -505,7 +669,8 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
   const bool timing = (ctx->cfg.flags & KVQ_FLAG_TIMING) != 0;
   Step &w = ctx->w;
   const size_t NBm = s.NBmax;
-  int64_t h2d = 0, kblk = 0, vblk = 0, dense_heads = 0;
+  int64_t h2d = 0, kblk = 0, vblk = 0, dense_heads = 0, kcached = 0;
+  ++ctx->kc.now;
   int syncs = 0, rounds = 0;
   Timer tm{ctx, timing};
   if (timing) HIPCK(ctx, hipEventRecord(ctx->ev_tot[0], st));
@@ -537,7 +702,7 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
     const bool new_keys = plan.nk > 0;
     if (!plan.ent.empty()) {
       HIPCK(ctx, tm.copy_begin(TC_COPY, ctx->cstream));
-      rs = issue_copies(ctx, tab, layer, plan, h2d, kblk, vblk);
+      rs = issue_copies(ctx, tab, layer, plan, h2d, kblk, vblk, kcached);
       if (rs != KVQ_OK) return rs;
       HIPCK(ctx, tm.copy_end(ctx->cstream));
       HIPCK(ctx, hipEventRecord(ctx->ev_copy, ctx->cstream));
@@ -617,6 +782,7 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
   if (stats) {
     memset(stats, 0, sizeof(*stats));
     stats->promoted_key_blocks = kblk;
+    stats->cached_key_blocks = kcached;
     stats->promoted_value_blocks = vblk;
     stats->dense_kv_heads = dense_heads;
     stats->h2d_bytes = h2d;

@@ -227,4 +227,24 @@ hipError_t launch_export_vcodes(const Shape &s, const Tier1 &t, size_t u, int T,
   return launch_k(k_export_vcodes, dim3(256), dim3(256), 0, st, s, t, u, T, dst);
 }
 
+// Copies whole FP16 blocks (64 rows of d halves) between device row arrays:
+// entry e of `list` is (source row, destination row) of one block; one
+// workgroup per entry, 16-byte loads and stores.  Used by the key block
+// cache: cache slot -> staging on a hit, staging -> cache slot on admission.
+__global__ __launch_bounds__(256) void k_copy_blocks(const uint32_t *__restrict__ list,
+                                                     const uint16_t *__restrict__ src,
+                                                     uint16_t *__restrict__ dst, int d) {
+  const size_t sr = list[2 * (size_t)blockIdx.x], dr = list[2 * (size_t)blockIdx.x + 1];
+  const uint4 *a = reinterpret_cast<const uint4 *>(src + sr * d);
+  uint4 *b = reinterpret_cast<uint4 *>(dst + dr * d);
+  const int n16 = BLOCK * d / 8;                 // 16-byte words per block
+  for (int k = threadIdx.x; k < n16; k += 256) b[k] = a[k];
+}
+
+hipError_t launch_copy_blocks(const uint32_t *list, int n, const uint16_t *src, uint16_t *dst,
+                              int d, hipStream_t st) {
+  if (n < 1) return hipSuccess;
+  return launch_k(k_copy_blocks, dim3(n), dim3(256), 0, st, list, src, dst, d);
+}
+
 }  // namespace kvq

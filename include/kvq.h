@@ -76,6 +76,20 @@ typedef int32_t kvq_status;
  * fires; keys keep the INT8 scoring, selection, ranking check and rungs 1,
  * 3 and 4. */
 #define KVQ_FLAG_FP16_VALUES  8u
+/* FP16 key blocks promoted in a step are kept in a device cache of
+ * key_cache_blocks slots (key_cache_blocks * 64 * head_dim * 2 bytes) shared
+ * by all (slot, layer, KV head) units, and later steps take a cached block
+ * with a device-to-device copy instead of the host link.  Replacement is least
+ * recently used, except that a block used by this call or within the last
+ * n_layers calls (one pass over the layers) is never evicted: a promoted
+ * block that finds no free slot and no older slot is copied from tier 2
+ * without being cached.  kvq_append drops the
+ * cached copies of the blocks it changes and kvq_reset_seq those of the
+ * sequence.  Decisions and outputs are unchanged.  Not part of the pages'
+ * method (a device-memory-for-bandwidth trade within a chosen budget);
+ * exclusive with KVQ_FLAG_RESIDENT_KEYS (KVQ_EINVAL if both are set, or if
+ * key_cache_blocks < 1 with this flag). */
+#define KVQ_FLAG_KEY_CACHE    16u
 
 typedef struct kvq_config {
     int32_t n_layers;        /* layers held by the context                      */
@@ -94,6 +108,8 @@ typedef struct kvq_config {
     double eps_key;          /* E_key tolerance (1e-3)                           */
     double v_tol;            /* E_val tolerance (0.25)                           */
     uint32_t flags;          /* KVQ_FLAG_*                                       */
+    int64_t key_cache_blocks;/* slots of the FP16 key block cache
+                                (KVQ_FLAG_KEY_CACHE; 0 otherwise)               */
 } kvq_config;
 
 /* Fills cfg with the defaults above for the given shape. */
@@ -145,7 +161,10 @@ typedef struct kvq_step_stats {
     float ms_dense;                /* dense fallback decode kernel                */
     float ms_total;                /* whole call, first launch to last            */
     float ms_combine;              /* split-K combine kernel                      */
-    float ms_misc;                 /* step set-up (q scaling, reset), finalize    */
+    float ms_misc;                 /* rung-4 kernel (only when a head reached
+                                      rung 3 or the dense path is forced)         */
+    int64_t cached_key_blocks;     /* key blocks taken from the device cache
+                                      (KVQ_FLAG_KEY_CACHE), not the host link     */
 } kvq_step_stats;
 
 /* One decode step at one layer (Méthodologie §2-§3): attends over every

@@ -103,6 +103,28 @@ def run_oracle(orc, case):
     return res
 
 
+def same_traces(ta, tb, Hq, Hkv, T, where):
+    """Two GPU step traces of the same call are equal everywhere the step
+    defines them: FP16 scores and FP16 block ingredients only on promoted
+    blocks (elsewhere those arrays keep whatever earlier calls left)."""
+    NB = (T + 63) // 64
+    U = ta["U"].reshape(Hkv, NB)
+    assert np.array_equal(U, tb["U"].reshape(Hkv, NB)), f"{where}: U"
+    G = Hq // Hkv
+    Uh = np.repeat(U, G, axis=0) == 1                        # [Hq][NB]
+    tokU = Uh[:, np.arange(T) // 64]                         # [Hq][T]
+    for k in ta:
+        a, b = ta[k], tb[k]
+        if k == "sp":
+            a, b = a.reshape(Hq, T)[tokU], b.reshape(Hq, T)[tokU]
+        elif k in ("m16", "L16"):
+            a, b = a.reshape(Hq, NB)[Uh], b.reshape(Hq, NB)[Uh]
+        if a.dtype.kind == "f":
+            a, b = a.view(np.uint32 if a.itemsize == 4 else np.uint64), \
+                b.view(np.uint32 if b.itemsize == 4 else np.uint64)
+        assert np.array_equal(a, b), f"{where}: {k}"
+
+
 def compare(case, gpu, ref, check_out=True):
     G = case.Hq // case.Hkv
     for i, (r, groups) in enumerate(ref):

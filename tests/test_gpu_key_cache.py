@@ -1,0 +1,103 @@
+"""GPU tests of KVQ_FLAG_KEY_CACHE (needs an MI355X; marked gpu).
+
+A device cache of FP16 key blocks must change nothing but where promoted
+keys come from: over several steps on two layers, with appends in between
+(which change the open block, so a stale cached copy would show up in the
+FP16 scores), every decision array and output is bit-identical to the
+default context's, cached blocks are counted, and only uncached key blocks
+cross the host link.
+"""
+import numpy as np
+import pytest
+
+from gpu_helpers import log, same_traces
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env(orc):
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import certified_quantized_kv_amd as kvq
+    return kvq, torch
+
+
+def _run(kvq, torch, L, K, V, appends, qs, Hq, Hkv, d, cap, cache_blocks):
+    dev = torch.device("cuda:0")
+    ctx = kvq.Context(L, 1, Hq, Hkv, d, cap, key_cache_blocks=cache_blocks)
+    for layer in range(L):
+        ctx.append(layer, [0], [K[layer].shape[0]],
+                   torch.from_numpy(K[layer].view(np.float16)).to(dev),
+                   torch.from_numpy(V[layer].view(np.float16)).to(dev))
+    res = []
+    for step, (ap, q) in enumerate(zip(appends, qs)):
+        for layer in range(L):
+            k1, v1 = ap[layer]
+            if k1.shape[0]:
+                ctx.append(layer, [0], [k1.shape[0]], torch.from_numpy(k1.view(np.float16)).to(dev),
+                           torch.from_numpy(v1.view(np.float16)).to(dev))
+            out, ek, ev, lv, st = ctx.decode_step(
+                layer, [0], torch.from_numpy(q[layer][None].view(np.float16)).to(dev), stats=True)
+            torch.cuda.synchronize()
+            res.append(dict(out=out.cpu().numpy(), ek=ek.cpu().numpy(), ev=ev.cpu().numpy(),
+                            lv=lv.cpu().numpy(), st=st, T=ctx.seq_len(layer, 0),
+                            tr={k: ctx.export_trace(k, 0) for k in kvq.TR}))
+    ctx.close()
+    return res
+
+
+def _case(seed, L, Hq, Hkv, d, T, sizes):
+    r = np.random.default_rng(seed)
+    K = [(r.standard_normal((T, Hkv, d)) * 2).astype(np.float16).view(np.uint16) for _ in range(L)]
+    V = [r.standard_normal((T, Hkv, d)).astype(np.float16).view(np.uint16) for _ in range(L)]
+    appends = [[((r.standard_normal((n, Hkv, d)) * 2).astype(np.float16).view(np.uint16),
+                 r.standard_normal((n, Hkv, d)).astype(np.float16).view(np.uint16))
+                for _ in range(L)] for n in sizes]
+    qs = [[r.standard_normal((Hq, d)).astype(np.float16).view(np.uint16) for _ in range(L)]
+          for _ in sizes]
+    return K, V, appends, qs
+
+
+@pytest.mark.parametrize("frac", [0.4, 2.0], ids=["budget-40pct", "budget-all"])
+def test_key_cache_bit_identical_over_steps(env, frac):
+    kvq, torch = env
+    L, Hq, Hkv, d, T = 2, 8, 2, 128, 1000
+    sizes = [0, 1, 30, 0, 64]           # the 30 cross a block boundary
+    K, V, appends, qs = _case(31, L, Hq, Hkv, d, T, sizes)
+    cap = T + sum(sizes) + 64
+    blocks = L * Hkv * ((cap + 63) // 64)
+    budget = max(1, int(frac * blocks))
+    log(f"[key-cache] default context ({len(sizes)} steps x {L} layers)")
+    a = _run(kvq, torch, L, K, V, appends, qs, Hq, Hkv, d, cap, 0)
+    log(f"[key-cache] cached context, {budget} slots")
+    b = _run(kvq, torch, L, K, V, appends, qs, Hq, Hkv, d, cap, budget)
+    blk = 64 * d * 2
+    cached_total = 0
+    for n, (x, y) in enumerate(zip(a, b)):
+        assert np.array_equal(x["out"].view(np.uint32), y["out"].view(np.uint32)), n
+        assert np.array_equal(x["lv"], y["lv"]), n
+        assert np.array_equal(x["ek"].view(np.uint32), y["ek"].view(np.uint32)), n
+        assert np.array_equal(x["ev"].view(np.uint32), y["ev"].view(np.uint32)), n
+        same_traces(x["tr"], y["tr"], Hq, Hkv, x["T"], f"call {n}")
+        sa, sb = x["st"], y["st"]
+        assert sa["cached_key_blocks"] == 0
+        # the same blocks are promoted; the cached ones skip the host link
+        assert sb["promoted_key_blocks"] + sb["cached_key_blocks"] == sa["promoted_key_blocks"], n
+        assert sb["h2d_bytes"] == sa["h2d_bytes"] - sb["cached_key_blocks"] * blk, n
+        if n < L:
+            assert sb["cached_key_blocks"] == 0      # first pass over the layers: cache empty
+        cached_total += sb["cached_key_blocks"]
+    assert cached_total > 0
+    if frac > 1.0:
+        # everything fits: after the first pass only blocks changed by an
+        # append (or never promoted before) come over the host link
+        last = b[-1]["st"]
+        assert last["cached_key_blocks"] >= last["promoted_key_blocks"] > 0
+
+
+def test_key_cache_rejects_residency(env):
+    kvq, torch = env
+    with pytest.raises(kvq.KvqError):
+        kvq.Context(1, 1, 8, 2, 128, 256, resident_keys=True, key_cache_blocks=16)

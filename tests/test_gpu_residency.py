@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import kvq_synth as S
-from gpu_helpers import Case, compare, log, run_oracle
+from gpu_helpers import Case, compare, log, run_oracle, same_traces
 
 pytestmark = pytest.mark.gpu
 
@@ -39,7 +39,7 @@ def _steps(kvq, torch, resident, K, V, appends, qs, Hq, Hkv, d, cap):
                                               stats=True)
         torch.cuda.synchronize()
         res.append(dict(out=out.cpu().numpy(), ek=ek.cpu().numpy(), ev=ev.cpu().numpy(),
-                        lv=lv.cpu().numpy(), st=st,
+                        lv=lv.cpu().numpy(), st=st, T=ctx.seq_len(0, 0),
                         tr={k: ctx.export_trace(k, 0) for k in kvq.TR}))
     ctx.close()
     return res
@@ -66,8 +66,7 @@ def test_resident_keys_bit_identical_over_steps(env):
         assert np.array_equal(x["lv"], y["lv"]), step
         assert np.array_equal(x["ek"].view(np.uint32), y["ek"].view(np.uint32)), step
         assert np.array_equal(x["ev"].view(np.uint32), y["ev"].view(np.uint32)), step
-        for k in x["tr"]:
-            assert np.array_equal(x["tr"][k], y["tr"][k]), (step, k)
+        same_traces(x["tr"], y["tr"], Hq, Hkv, x["T"], f"step {step}")
         assert x["st"]["promoted_key_blocks"] == y["st"]["promoted_key_blocks"]
     blk = 64 * d * 2
     # resident keys are never copied: only value blocks (rung 2) cross the link
