@@ -205,8 +205,15 @@ __device__ __forceinline__ uint32_t key_image(unsigned long long k) {
 // Buckets larger than this send the whole sort to the comparison network.
 constexpr int SORT_MAX_BUCKET = 48;
 
-template <int NT>
-__device__ __forceinline__ void sort_desc_u64(unsigned long long *keys, int n, int cap) {
+// Callable on each key's final position (bucket path); the comparison
+// network path does not call it and sort_desc_u64 then returns false.
+struct NoPlace {
+  __device__ void operator()(unsigned long long, int) const {}
+};
+
+template <int NT, class OnPlace = NoPlace>
+__device__ __forceinline__ bool sort_desc_u64(unsigned long long *keys, int n, int cap,
+                                              OnPlace on_place = OnPlace()) {
   constexpr int SB = SORT_BUCKETS;
   constexpr int PER = SB / NT;           // counters per thread in the scan
   static_assert(SB % NT == 0, "bucket count");
@@ -308,7 +315,7 @@ __device__ __forceinline__ void sort_desc_u64(unsigned long long *keys, int n, i
         sort_desc_network<NT, 2>(keys, n);
       else
         sort_desc_network<NT, 4>(keys, n);
-      return;
+      return false;
     }
     __syncthreads();                     // wsum is written again by pass 1
   }
@@ -351,8 +358,10 @@ __device__ __forceinline__ void sort_desc_u64(unsigned long long *keys, int n, i
       r += (y > k || (y == k && q < p)) ? 1 : 0;
     }
     keys[b0 + r] = k;
+    on_place(k, b0 + r);
   }
   __syncthreads();
+  return true;
 }
 
 // Inclusive scan of per-thread u64 values over a workgroup of NT threads

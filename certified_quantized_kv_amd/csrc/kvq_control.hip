@@ -115,7 +115,7 @@ __device__ void evaluate_head(const Shape &s, const Step &w, const Thresh &th, i
   const int n = w.ssize[(size_t)i * s.Hq + hq];
   const uint32_t *pi = w.pi + base;
   __shared__ float mred[2][CTL_NT / 64];
-  __shared__ unsigned long long sred[5][CTL_NT / 64];
+  __shared__ unsigned long long sred[6][CTL_NT / 64];
   // every per-block input of this thread's blocks b = t + r CTL_NT is loaded
   // once, up front (both score kinds; the block's kind selects afterwards),
   // so the passes below wait on no global load
@@ -202,16 +202,33 @@ __device__ void evaluate_head(const Shape &s, const Step &w, const Thresh &th, i
     }
     w.W16[base + b] = W16;
   }
-  unsigned long long v4[5] = {den, num, sub, cap, numv};
+  // ranking over S_h: FP16 order (W16 descending, index ascending); each
+  // member's squared rank difference is taken where the sort places it
+  const int n2 = max(64, pow2_at_least(n));
+  unsigned long long ssd = 0ull;
+  const bool placed = sort_desc_u64<CTL_NT>(keys, n, n2, [&](unsigned long long k, int j) {
+    const uint32_t b = 0xffffffffu - (uint32_t)(k & 0xffffffffull);
+    const long long dd = (long long)pos[b] - (long long)j;
+    ssd += (unsigned long long)(dd * dd);
+  });
+  if (!placed) {
+    for (int j = threadIdx.x; j < n; j += CTL_NT) {
+      const uint32_t b = 0xffffffffu - (uint32_t)(keys[j] & 0xffffffffull);
+      const long long dd = (long long)pos[b] - (long long)j;
+      ssd += (unsigned long long)(dd * dd);
+    }
+  }
+  // one reduction for the E_key sums, the E_val numerator and the ranks
+  unsigned long long v4[6] = {den, num, sub, cap, numv, ssd};
 #pragma unroll
-  for (int k = 0; k < 5; ++k) v4[k] = wave_sum_u64(v4[k]);
+  for (int k = 0; k < 6; ++k) v4[k] = wave_sum_u64(v4[k]);
   if ((threadIdx.x & 63) == 0) {
 #pragma unroll
-    for (int k = 0; k < 5; ++k) sred[k][threadIdx.x >> 6] = v4[k];
+    for (int k = 0; k < 6; ++k) sred[k][threadIdx.x >> 6] = v4[k];
   }
   __syncthreads();
 #pragma unroll
-  for (int k = 0; k < 5; ++k) {
+  for (int k = 0; k < 6; ++k) {
     unsigned long long r = 0ull;
 #pragma unroll
     for (int q = 0; q < CTL_NT / 64; ++q) r += sred[k][q];
@@ -224,16 +241,7 @@ __device__ void evaluate_head(const Shape &s, const Step &w, const Thresh &th, i
     const long long D = (long long)v4[0] - (long long)v4[2];
     ek = (D <= 0) ? 1.0 : fmin(1.0, (double)v4[1] / (double)D);
   }
-  // ranking over S_h: FP16 order (W16 descending, index ascending)
-  const int n2 = max(64, pow2_at_least(n));
-  sort_desc_u64<CTL_NT>(keys, n, n2);
-  unsigned long long ssd = 0ull;
-  for (int j = threadIdx.x; j < n; j += CTL_NT) {
-    const uint32_t b = 0xffffffffu - (uint32_t)(keys[j] & 0xffffffffull);
-    const long long dd = (long long)pos[b] - (long long)j;
-    ssd += (unsigned long long)(dd * dd);
-  }
-  ssd = block_sum_u64(ssd, sh.u64[0]);
+  ssd = v4[5];
   if (threadIdx.x == 0) {
     const unsigned long long nn = (unsigned long long)n;
     const bool ok = (n <= 1) ||
@@ -246,7 +254,6 @@ __device__ void evaluate_head(const Shape &s, const Step &w, const Thresh &th, i
     f = ok ? (f | 1u) : ((f & ~1u) | 4u);
     w.hflags[(size_t)i * s.Hq + hq] = f;
   }
-  __syncthreads();
 }
 
 // Rung 2 for one head with E_val(no value promoted) = numv / denv > v_tol:
