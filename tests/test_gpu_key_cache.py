@@ -101,3 +101,57 @@ def test_key_cache_rejects_residency(env):
     kvq, torch = env
     with pytest.raises(kvq.KvqError):
         kvq.Context(1, 1, 8, 2, 128, 256, resident_keys=True, key_cache_blocks=16)
+
+
+def test_key_cache_tiny_budget_and_reset(env):
+    """Five slots for three layers (constant eviction and bypass), then the
+    sequence is reset and refilled with other keys: the cache must serve
+    nothing stale, and the results stay bit-identical to the default context."""
+    kvq, torch = env
+    L, Hq, Hkv, d, T = 3, 8, 2, 128, 500
+    sizes = [0, 3, 0, 70]
+    cap = 2 * T + sum(sizes) + 64
+    dev = torch.device("cuda:0")
+
+    def run(cache_blocks):
+        K, V, appends, qs = _case(41, L, Hq, Hkv, d, T, sizes)
+        K2, V2, _, _ = _case(42, L, Hq, Hkv, d, T, [0])
+        ctx = kvq.Context(L, 1, Hq, Hkv, d, cap, key_cache_blocks=cache_blocks)
+        outs = []
+        for phase, (KK, VV) in enumerate(((K, V), (K2, V2))):
+            if phase == 1:
+                ctx.reset_seq(0)
+            for layer in range(L):
+                ctx.append(layer, [0], [KK[layer].shape[0]],
+                           torch.from_numpy(KK[layer].view(np.float16)).to(dev),
+                           torch.from_numpy(VV[layer].view(np.float16)).to(dev))
+            for ap, q in zip(appends, qs):
+                for layer in range(L):
+                    k1, v1 = ap[layer]
+                    if k1.shape[0]:
+                        ctx.append(layer, [0], [k1.shape[0]],
+                                   torch.from_numpy(k1.view(np.float16)).to(dev),
+                                   torch.from_numpy(v1.view(np.float16)).to(dev))
+                    out, ek, ev, lv, st = ctx.decode_step(
+                        layer, [0], torch.from_numpy(q[layer][None].view(np.float16)).to(dev),
+                        stats=True)
+                    torch.cuda.synchronize()
+                    outs.append((out.cpu().numpy(), ek.cpu().numpy(), lv.cpu().numpy(), st,
+                                 {k: ctx.export_trace(k, 0) for k in kvq.TR},
+                                 ctx.seq_len(layer, 0)))
+        ctx.close()
+        return outs
+
+    log("[key-cache] tiny budget: default context")
+    a = run(0)
+    log("[key-cache] tiny budget: 5 slots")
+    b = run(5)
+    cached = 0
+    for n, (x, y) in enumerate(zip(a, b)):
+        assert np.array_equal(x[0].view(np.uint32), y[0].view(np.uint32)), n
+        assert np.array_equal(x[1].view(np.uint32), y[1].view(np.uint32)), n
+        assert np.array_equal(x[2], y[2]), n
+        same_traces(x[4], y[4], Hq, Hkv, x[5], f"call {n}")
+        assert y[3]["promoted_key_blocks"] + y[3]["cached_key_blocks"] == x[3]["promoted_key_blocks"]
+        cached += y[3]["cached_key_blocks"]
+    assert cached > 0
