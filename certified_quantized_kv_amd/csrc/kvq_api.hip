@@ -114,7 +114,7 @@ struct kvq_ctx {
   std::vector<int64_t> T;     // [slot][layer]
   std::vector<void *> dallocs;
   hipStream_t cstream = nullptr;
-  hipEvent_t ev_start = nullptr, ev_copy = nullptr;
+  hipEvent_t ev_start = nullptr, ev_copy = nullptr, ev_plan = nullptr;
   hipEvent_t ev_k[128] = {};   // kernel timing pairs
   hipEvent_t ev_c[32] = {};    // copy timing pairs
   hipEvent_t ev_tot[2] = {};
@@ -165,6 +165,7 @@ void free_all(kvq_ctx *c) {
   if (c->cstream) (void)hipStreamDestroy(c->cstream);
   if (c->ev_start) (void)hipEventDestroy(c->ev_start);
   if (c->ev_copy) (void)hipEventDestroy(c->ev_copy);
+  if (c->ev_plan) (void)hipEventDestroy(c->ev_plan);
   for (auto &e : c->ev_k)
     if (e) (void)hipEventDestroy(e);
   for (auto &e : c->ev_c)
@@ -432,6 +433,7 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out) {
   if (e == hipSuccess) e = hipStreamCreateWithFlags(&x->cstream, hipStreamNonBlocking);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&x->ev_start, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&x->ev_copy, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&x->ev_plan, hipEventDisableTiming);
   for (auto &ev : x->ev_k)
     if (e == hipSuccess) e = hipEventCreate(&ev);
   for (auto &ev : x->ev_c)
@@ -537,11 +539,20 @@ struct Plan {
   std::vector<unsigned long long> ent;
 };
 
-kvq_status read_plan(kvq_ctx *c, hipStream_t st, Plan &p) {
+// The plan's header and first entries come back in one copy on the step's
+// stream; the host waits for that copy only (an event), so kernels enqueued
+// after it keep running meanwhile.
+kvq_status read_plan_issue(kvq_ctx *c, hipStream_t st) {
+  const size_t first = std::min(c->plan_cap, plan_kcap(c->s));
+  HIPCK(c, hipMemcpyAsync(c->plan_host, c->w.plan, (4 + first) * 8, hipMemcpyDeviceToHost, st));
+  HIPCK(c, hipEventRecord(c->ev_plan, st));
+  return KVQ_OK;
+}
+
+kvq_status read_plan_wait(kvq_ctx *c, Plan &p) {
   const size_t kcap = plan_kcap(c->s);
   const size_t first = std::min(c->plan_cap, kcap);
-  HIPCK(c, hipMemcpyAsync(c->plan_host, c->w.plan, (4 + first) * 8, hipMemcpyDeviceToHost, st));
-  HIPCK(c, hipStreamSynchronize(st));
+  HIPCK(c, hipEventSynchronize(c->ev_plan));
   p.nk = (int64_t)c->plan_host[0];
   p.nv = (int64_t)c->plan_host[1];
   p.flags = (uint32_t)c->plan_host[2];
@@ -560,6 +571,11 @@ kvq_status read_plan(kvq_ctx *c, hipStream_t st, Plan &p) {
                        hipMemcpyDeviceToHost));
   }
   return KVQ_OK;
+}
+
+kvq_status read_plan(kvq_ctx *c, hipStream_t st, Plan &p) {
+  const kvq_status r = read_plan_issue(c, st);
+  return r != KVQ_OK ? r : read_plan_wait(c, p);
 }
 
 // Issues the copies of a plan on the copy stream; returns bytes and blocks.
@@ -672,6 +688,7 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
   int64_t h2d = 0, kblk = 0, vblk = 0, dense_heads = 0, kcached = 0;
   ++ctx->kc.now;
   int syncs = 0, rounds = 0;
+  bool decoded = false;   // the decode launched behind the last round stands
   Timer tm{ctx, timing};
   if (timing) HIPCK(ctx, hipEventRecord(ctx->ev_tot[0], st));
 
@@ -716,61 +733,78 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
     }
     tm.open(TC_CONTROL);
     HIPCK(ctx, launch_control(s, ctx->t, w, tab, layer, ctx->th, round, maxNB, st));
+    rs = read_plan_issue(ctx, st);
+    if (rs != KVQ_OK) return rs;
+    // the decode and combine go in behind the plan's copy: in the common case
+    // (no group widens, no values to copy, no head at rung 3) they are the
+    // step's last kernels and run while the host reads the plan; otherwise
+    // they are launched again below and overwrite these results
+    if (!ctx->th.force_dense) {
+      tm.open(TC_DECODE);
+      HIPCK(ctx, launch_decode(s, ctx->t, w, tab, layer, maxNB, false, st));
+      tm.open(TC_COMBINE);
+      HIPCK(ctx, launch_combine(s, w, tab, out, 0, e_key, e_val, level, st));
+    }
     tm.close();
-    rs = read_plan(ctx, st, plan);
+    rs = read_plan_wait(ctx, plan);
     if (rs != KVQ_OK) return rs;
     ++syncs;
     rounds = round + 1;
-    if (!(plan.flags & 1u) && plan.ent.empty()) break;
+    if (!(plan.flags & 1u) && plan.ent.empty()) {
+      decoded = !ctx->th.force_dense && !(plan.flags & 2u);
+      break;
+    }
   }
   // rung 4 and the outputs: with no head at rung 3 (and no forced dense
   // fallback) no level can change, and the combine kernel writes the outputs
   const bool maybe_dense = ctx->th.force_dense || (plan.flags & 2u);
-  if (maybe_dense) {
-    tm.open(TC_MISC);
-    HIPCK(ctx, launch_finalize(s, w, tab, ctx->th, e_key, e_val, level, st));
-    tm.close();
-  }
-  std::vector<uint8_t> gd;
-  if (maybe_dense) {
-    gd.resize((size_t)n * s.Hkv);
-    HIPCK(ctx, hipMemcpyAsync(gd.data(), w.gdense, gd.size(), hipMemcpyDeviceToHost, st));
-    HIPCK(ctx, hipStreamSynchronize(st));
-    ++syncs;
-    bool any = false;
-    for (int i = 0; i < n; ++i)
-      for (int g = 0; g < s.Hkv; ++g) {
-        if (!gd[(size_t)i * s.Hkv + g]) continue;
-        any = true;
-        ++dense_heads;
-        const size_t u = unit_of(s, tab.slot[i], layer, g);
-        const size_t ig = (size_t)i * s.Hkv + g;
-        const size_t bytes = (size_t)((tab.T[i] + BLOCK - 1) / BLOCK) * BLOCK * s.d * 2;
-        HIPCK(ctx, tm.copy_begin(TC_COPY, ctx->cstream));
-        if (!s.kres) {   // resident keys are in device memory already
-          HIPCK(ctx, hipMemcpyAsync(w.stage_k + ig * s.Tmax * s.d, ctx->t2k_host + u * s.Tmax * s.d,
-                                    bytes, hipMemcpyHostToDevice, ctx->cstream));
-          h2d += (int64_t)bytes;
-        }
-        HIPCK(ctx, hipMemcpyAsync(w.stage_v + ig * s.Tmax * s.d, ctx->t2v_host + u * s.Tmax * s.d,
-                                  bytes, hipMemcpyHostToDevice, ctx->cstream));
-        HIPCK(ctx, tm.copy_end(ctx->cstream));
-        h2d += (int64_t)bytes;
-      }
-    if (any) {
-      HIPCK(ctx, hipEventRecord(ctx->ev_copy, ctx->cstream));
-      HIPCK(ctx, hipStreamWaitEvent(st, ctx->ev_copy, 0));
-      tm.open(TC_DENSE);
-      HIPCK(ctx, launch_decode(s, ctx->t, w, tab, layer, maxNB, true, st));
+  if (!decoded) {
+    if (maybe_dense) {
+      tm.open(TC_MISC);
+      HIPCK(ctx, launch_finalize(s, w, tab, ctx->th, e_key, e_val, level, st));
       tm.close();
     }
+    std::vector<uint8_t> gd;
+    if (maybe_dense) {
+      gd.resize((size_t)n * s.Hkv);
+      HIPCK(ctx, hipMemcpyAsync(gd.data(), w.gdense, gd.size(), hipMemcpyDeviceToHost, st));
+      HIPCK(ctx, hipStreamSynchronize(st));
+      ++syncs;
+      bool any = false;
+      for (int i = 0; i < n; ++i)
+        for (int g = 0; g < s.Hkv; ++g) {
+          if (!gd[(size_t)i * s.Hkv + g]) continue;
+          any = true;
+          ++dense_heads;
+          const size_t u = unit_of(s, tab.slot[i], layer, g);
+          const size_t ig = (size_t)i * s.Hkv + g;
+          const size_t bytes = (size_t)((tab.T[i] + BLOCK - 1) / BLOCK) * BLOCK * s.d * 2;
+          HIPCK(ctx, tm.copy_begin(TC_COPY, ctx->cstream));
+          if (!s.kres) {   // resident keys are in device memory already
+            HIPCK(ctx, hipMemcpyAsync(w.stage_k + ig * s.Tmax * s.d, ctx->t2k_host + u * s.Tmax * s.d,
+                                      bytes, hipMemcpyHostToDevice, ctx->cstream));
+            h2d += (int64_t)bytes;
+          }
+          HIPCK(ctx, hipMemcpyAsync(w.stage_v + ig * s.Tmax * s.d, ctx->t2v_host + u * s.Tmax * s.d,
+                                    bytes, hipMemcpyHostToDevice, ctx->cstream));
+          HIPCK(ctx, tm.copy_end(ctx->cstream));
+          h2d += (int64_t)bytes;
+        }
+      if (any) {
+        HIPCK(ctx, hipEventRecord(ctx->ev_copy, ctx->cstream));
+        HIPCK(ctx, hipStreamWaitEvent(st, ctx->ev_copy, 0));
+        tm.open(TC_DENSE);
+        HIPCK(ctx, launch_decode(s, ctx->t, w, tab, layer, maxNB, true, st));
+        tm.close();
+      }
+    }
+    tm.open(TC_DECODE);
+    HIPCK(ctx, launch_decode(s, ctx->t, w, tab, layer, maxNB, false, st));
+    tm.open(TC_COMBINE);
+    HIPCK(ctx, launch_combine(s, w, tab, out, 0, maybe_dense ? nullptr : e_key,
+                              maybe_dense ? nullptr : e_val, maybe_dense ? nullptr : level, st));
+    tm.close();
   }
-  tm.open(TC_DECODE);
-  HIPCK(ctx, launch_decode(s, ctx->t, w, tab, layer, maxNB, false, st));
-  tm.open(TC_COMBINE);
-  HIPCK(ctx, launch_combine(s, w, tab, out, 0, maybe_dense ? nullptr : e_key,
-                            maybe_dense ? nullptr : e_val, maybe_dense ? nullptr : level, st));
-  tm.close();
   if (timing) HIPCK(ctx, hipEventRecord(ctx->ev_tot[1], st));
 
   ctx->last_n = n;
