@@ -42,36 +42,6 @@ struct CtlShared {
   int wid;
 };
 
-__device__ unsigned long long block_sum_u64(unsigned long long v, unsigned long long *buf) {
-  v = wave_sum_u64(v);
-  if ((threadIdx.x & 63) == 0) buf[threadIdx.x >> 6] = v;
-  __syncthreads();
-  unsigned long long r = 0ull;
-  for (int k = 0; k < (int)(blockDim.x >> 6); ++k) r += buf[k];
-  __syncthreads();
-  return r;
-}
-
-__device__ float block_max_f32(float v, float *buf) {
-  v = bfly_max<64>(v);
-  if ((threadIdx.x & 63) == 0) buf[threadIdx.x >> 6] = v;
-  __syncthreads();
-  float r = buf[0];
-  for (int k = 1; k < (int)(blockDim.x >> 6); ++k) r = fmaxf(r, buf[k]);
-  __syncthreads();
-  return r;
-}
-
-__device__ int block_or_i32(int v, int *buf) {
-  v = wave_or_i32(v);
-  if ((threadIdx.x & 63) == 0) buf[threadIdx.x >> 6] = v;
-  __syncthreads();
-  int r = 0;
-  for (int k = 0; k < (int)(blockDim.x >> 6); ++k) r |= buf[k];
-  __syncthreads();
-  return r;
-}
-
 __device__ int block_min_i32(int v, int *buf) {
   v = wave_min_i32(v);
   if ((threadIdx.x & 63) == 0) buf[threadIdx.x >> 6] = v;

@@ -62,9 +62,6 @@ __device__ __forceinline__ uint32_t f_ord(float f) {
   uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
-__device__ __forceinline__ float f_unord(uint32_t u) {
-  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
-}
 
 __device__ __forceinline__ float nextup_pos(float x) {
   return __uint_as_float(__float_as_uint(x) + 1u);
@@ -202,15 +199,6 @@ __device__ __forceinline__ int wave_min_i32(int v) {
   v = min(v, xor_lane<4>(v));
   v = min(v, xor_lane<2>(v));
   v = min(v, xor_lane<1>(v));
-  return v;
-}
-__device__ __forceinline__ int wave_or_i32(int v) {
-  v |= xor_lane<32>(v);
-  v |= xor_lane<16>(v);
-  v |= xor_lane<8>(v);
-  v |= xor_lane<4>(v);
-  v |= xor_lane<2>(v);
-  v |= xor_lane<1>(v);
   return v;
 }
 template <int X>
