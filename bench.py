@@ -289,6 +289,13 @@ def main():
         "per_kernel_hbm_frac": {k: round(v[1] / (v[0] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
                                 for k, v in cand.items() if v[0] > 0},
     }
+    # the same bytes over the two kernels that stream tier 1 (INT8 scoring and
+    # the mixed decode), and the time of the latency-bound controller kernels
+    st_ms = per_kernel["ms_score_int8"] + per_kernel["ms_decode"]
+    quantized_pass["tier1_streaming_kernels"] = {
+        "ms_per_layer": round(st_ms, 5),
+        "hbm_frac": round(qp_bytes / (st_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    quantized_pass["controller_ms_per_layer"] = round(qp_ms - st_ms, 5)
     promo = {
         "key_blocks_per_layer": round(avg("promoted_key_blocks"), 1),
         "value_blocks_per_layer": round(avg("promoted_value_blocks"), 1),
