@@ -13,7 +13,8 @@
 //   P.V     on the vector units: lane (token group j, channel slice c)
 //           accumulates p_ht v_tc for its slice with fp32 fma of fp16 values.
 // The four waves' partials are merged in LDS into one (m, l, o[d]) per head
-// and chunk; the combine kernel merges the chunks.
+// and chunk; the combine kernel merges the chunks.  K and V are read once
+// (non-temporal loads).
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -79,14 +80,15 @@ __global__ __launch_bounds__(256) void k_dense_vram(Shape s, Step w, DenseArgs a
         const int tok = min(t0 + tt * 16 + (lane & 15), T - 1);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          kb[tt][ks] = *(const h8v *)(Kb + (size_t)tok * rowstride + 32 * ks + 8 * (lane >> 4));
+          kb[tt][ks] = __builtin_nontemporal_load(
+              (const h8v *)(Kb + (size_t)tok * rowstride + 32 * ks + 8 * (lane >> 4)));
       }
       typedef _Float16 hc __attribute__((ext_vector_type(CPL)));
       hc vv[STEP / 4];
 #pragma unroll
       for (int r = 0; r < STEP / 4; ++r) {
         const int tok = min(t0 + tj + 4 * r, T - 1);
-        vv[r] = *(const hc *)(Vb + (size_t)tok * rowstride + c0);
+        vv[r] = __builtin_nontemporal_load((const hc *)(Vb + (size_t)tok * rowstride + c0));
       }
       // ---- scores --------------------------------------------------------------
       float x[2][4];

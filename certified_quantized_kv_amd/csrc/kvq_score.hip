@@ -48,7 +48,10 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 // to within one unit, keeps one KV head (one query set) for a sequence, and
 // at any moment the grid streams a contiguous window of blocks per KV head.
 // The kernel also carries the step set-up (q' for the later kernels, flags
-// cleared); its own waves form q' from q directly.
+// cleared); its own waves form q' from q directly.  Codes and metadata are
+// read once per step, and the scores are read once later: both go through
+// non-temporal loads and stores, which leave the caches to the data that is
+// reused.
 template <int D>
 __global__ __launch_bounds__(256) void k_score_int8(Shape s, Tier1 t, Step w, SeqTab tab, int layer,
                                                     const uint16_t *__restrict__ q16, float C) {
@@ -92,10 +95,11 @@ __global__ __launch_bounds__(256) void k_score_int8(Shape s, Tier1 t, Step w, Se
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
-        Bn[ks][nt] = *(const v4i *)(kc + ((size_t)((ks * 4 + nt) * 64 + lane)) * 16);
+        Bn[ks][nt] = __builtin_nontemporal_load(
+            (const v4i *)(kc + ((size_t)((ks * 4 + nt) * 64 + lane)) * 16));
     const uint32_t *km = t.kmeta + (uu * s.NBmax + bb) * D + jc * CW;
 #pragma unroll
-    for (int c = 0; c < CW; ++c) kmn[c] = km[c];
+    for (int c = 0; c < CW; ++c) kmn[c] = __builtin_nontemporal_load(&km[c]);
   };
   if (u0 < U) {
     load_q();
@@ -193,7 +197,7 @@ __global__ __launch_bounds__(256) void k_score_int8(Shape s, Tier1 t, Step w, Se
       x[nt] = fmaf(i64_to_f32(Dv), sc, pb);
       const bool ok = nt * 16 + jc < n;
       mx = ok ? fmaxf(mx, x[nt]) : mx;
-      if (ok && hv) dst[nt * 16 + jc] = x[nt];
+      if (ok && hv) __builtin_nontemporal_store(x[nt], &dst[nt * 16 + jc]);
     }
     mx = bfly_max<16>(mx);
     uint32_t Ls = 0u;
@@ -258,7 +262,8 @@ hipError_t launch_score_int8(const Shape &s, const Tier1 &t, const Step &w, cons
 // are staged with 16-byte coalesced loads into LDS rows padded to d*2 + 16
 // bytes (conflict-free 16-byte row reads); q' is read at wave-uniform
 // addresses.  Each lane runs the canonical fma chain over channels in
-// ascending order.
+// ascending order.  The staged keys are read once and the scores stored
+// once (non-temporal loads and stores: no cache allocation for the stream).
 constexpr int F16_BPW = 1;             // blocks per workgroup (4 waves each)
 
 template <int D>
@@ -286,7 +291,8 @@ __global__ __launch_bounds__(256 * F16_BPW) void k_score_fp16(Shape s, Step w, S
 #pragma unroll
     for (int k = 0; k < NL; ++k) {
       const int idx = tid + 256 * k;
-      v[k] = *(const v4i *)(src + (size_t)(idx / (D / 8)) * D + (idx % (D / 8)) * 8);
+      v[k] = __builtin_nontemporal_load(
+          (const v4i *)(src + (size_t)(idx / (D / 8)) * D + (idx % (D / 8)) * 8));
     }
 #pragma unroll
     for (int k = 0; k < NL; ++k) {
@@ -313,7 +319,8 @@ __global__ __launch_bounds__(256 * F16_BPW) void k_score_fp16(Shape s, Step w, S
       acc = fmaf(q[c + 7], h2f((uint16_t)(kk.w >> 16)), acc);
     }
     const bool valid = lane < n;
-    if (valid) w.sp[((size_t)i * s.Hq + hq) * s.Tmax + (size_t)b * BLOCK + lane] = acc;
+    if (valid)
+      __builtin_nontemporal_store(acc, &w.sp[((size_t)i * s.Hq + hq) * s.Tmax + (size_t)b * BLOCK + lane]);
     const float mx = bfly_max<64>(valid ? acc : -INFINITY);
     uint32_t L = valid ? (uint32_t)floorf(0x1p24f * exp2k(acc - mx)) : 0u;
     L = bfly_sum_u32<64>(L);
