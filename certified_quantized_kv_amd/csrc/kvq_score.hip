@@ -32,7 +32,6 @@
 // q'_c * k_tc from 0.  Block ingredients of any score row x:
 //   m_b = max_t x_t,   L_b = sum_t floor(2^24 exp2k(fl32(x_t - m_b)))  (exact).
 #include <algorithm>
-#include <numeric>
 
 #include "kvq_device.h"
 #include "kvq_internal.h"
@@ -42,16 +41,17 @@ namespace kvq {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-// Work split: a unit is one (sequence, block, KV head), numbered with the KV
-// head fastest; wave k of the grid (W waves, W a multiple of the KV head
-// count) takes units k, k + W, k + 2W, ...: every wave carries the same load
-// to within one unit, keeps one KV head (one query set) for a sequence, and
-// at any moment the grid streams a contiguous window of blocks per KV head.
-// The kernel also carries the step set-up (q' for the later kernels, flags
-// cleared); its own waves form q' from q directly.  Codes and metadata are
-// read once per step, and the scores are read once later: both go through
-// non-temporal loads and stores, which leave the caches to the data that is
-// reused.
+// Work split: a unit is one (sequence, KV head, block), numbered with the
+// block fastest; wave k of the grid (W waves) takes units k, k + W, k + 2W,
+// ...: every wave carries the same load to within one unit, and at any
+// moment the grid streams one contiguous window of W blocks (measured
+// faster than a window of W / Hkv blocks in each KV head).  A wave's
+// successive units may belong to different KV heads, so each unit's query
+// slice is fetched with its codes and metadata.  The kernel also carries
+// the step set-up (q' for the later kernels, flags cleared); its own waves
+// form q' from q directly.  Codes and metadata are read once per step, and
+// the scores are read once later: both go through non-temporal loads and
+// stores, which leave the caches to the data that is reused.
 template <int D>
 __global__ __launch_bounds__(256) void k_score_int8(Shape s, Tier1 t, Step w, SeqTab tab, int layer,
                                                     const uint16_t *__restrict__ q16, float C) {
@@ -71,40 +71,37 @@ __global__ __launch_bounds__(256) void k_score_int8(Shape s, Tier1 t, Step w, Se
     ii = 0;
     while (ii + 1 < tab.n && s.Hkv * tab.nbc[ii + 1] <= uu) ++ii;
     const int r = uu - s.Hkv * tab.nbc[ii];
-    bb = r / s.Hkv;
-    gg = r - bb * s.Hkv;
+    const int nbi = tab.nbc[ii + 1] - tab.nbc[ii];
+    gg = r / nbi;
+    bb = r - gg * nbi;
   };
   int i, g, b;
   locate(u0, i, g, b);
 
-  float qv[CW];
-  auto load_q = [&]() {
-    const int hq = g * s.G + (hv ? h : 0);
-    const uint16_t *qsrc = q16 + ((size_t)i * s.Hq + hq) * D + jc * CW;
-#pragma unroll
-    for (int c = 0; c < CW; ++c) qv[c] = h2f(qsrc[c]) * C;
-  };
-  // software pipeline: the next unit's codes and metadata are in flight
-  // while the current one's scores and block ingredients are formed
+  // software pipeline: the next unit's query slice, metadata and codes are
+  // in flight while the current one's scores and block ingredients are formed
   v4i Bn[NKS][4];
   uint32_t kmn[CW];
+  uint32_t qn[CW / 2];
   auto fetch = [&](int ii, int gg, int bb) {
+    const int hq = gg * s.G + (hv ? h : 0);
+    const uint32_t *qsrc = (const uint32_t *)(q16 + ((size_t)ii * s.Hq + hq) * D + jc * CW);
+#pragma unroll
+    for (int c = 0; c < CW / 2; ++c) qn[c] = qsrc[c];
     const size_t uu = unit_of(s, tab.slot[ii], layer, gg);
     const uint8_t *kc = t.kcodes + (uu * s.NBmax + bb) * (size_t)(BLOCK * D);
+    const uint32_t *km = t.kmeta + (uu * s.NBmax + bb) * D + jc * CW;
+#pragma unroll
+    for (int c = 0; c < CW; ++c) kmn[c] = __builtin_nontemporal_load(&km[c]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
         Bn[ks][nt] = __builtin_nontemporal_load(
             (const v4i *)(kc + ((size_t)((ks * 4 + nt) * 64 + lane)) * 16));
-    const uint32_t *km = t.kmeta + (uu * s.NBmax + bb) * D + jc * CW;
-#pragma unroll
-    for (int c = 0; c < CW; ++c) kmn[c] = __builtin_nontemporal_load(&km[c]);
   };
-  if (u0 < U) {
-    load_q();
-    fetch(i, g, b);
-  }
+  if (u0 < U) fetch(i, g, b);
   // the set-up's stores go out while the first unit's loads are in flight
   step_setup(s, w, tab.n, q16, C, blockIdx.x * (size_t)blockDim.x + threadIdx.x,
              (size_t)gridDim.x * blockDim.x);
@@ -119,6 +116,9 @@ __global__ __launch_bounds__(256) void k_score_int8(Shape s, Tier1 t, Step w, Se
     if (u + W < U) locate(u + W, i2, g2, b2);
 
     // ---- prologue: exponent, limbs of A, beta and Delta' per head -----------
+    float qv[CW];
+#pragma unroll
+    for (int c = 0; c < CW; ++c) qv[c] = h2f((uint16_t)(qn[c / 2] >> (16 * (c % 2)))) * C;
     float sv[CW], ov[CW], a[CW];
     float am = 0.0f;
 #pragma unroll
@@ -165,10 +165,8 @@ __global__ __launch_bounds__(256) void k_score_int8(Shape s, Tier1 t, Step w, Se
         ((uint32_t *)(row + 3 * AST))[c] = z;
       }
     }
-    if (hv && jc == 0) {
-      const float R = zero ? 0.0f : ldexpf(64.0f * (float)D, e);
-      w.delta[((size_t)i * s.Hq + hq) * s.NBmax + b] = (pd + R) * (1.0f + 0x1p-15f);
-    }
+    // Delta' is stored with the block ingredients, after the contraction
+    const float dv = (pd + (zero ? 0.0f : ldexpf(64.0f * (float)D, e))) * (1.0f + 0x1p-15f);
     wave_lds_sync();
 
     // ---- exact integer core on the matrix cores -------------------------------
@@ -211,14 +209,13 @@ __global__ __launch_bounds__(256) void k_score_int8(Shape s, Tier1 t, Step w, Se
       const size_t o = ((size_t)i * s.Hq + hq) * s.NBmax + b;
       w.mhat[o] = mx;
       w.Lhat[o] = Ls;
+      w.delta[o] = dv;
     }
     wave_lds_sync();
     // advance
-    const bool newgroup = (i2 != i) || (g2 != g);
     i = i2;
     g = g2;
     b = b2;
-    if (newgroup && u + W < U) load_q();
   }
 }
 
@@ -235,23 +232,19 @@ int grid_score_int8(const Shape &s) {
   return per_cu * s.ncu;
 }
 
-// Workgroups: what the device holds at once, rounded down so that the wave
-// count is a multiple of the KV head count (whole workgroups of 4 waves).
-static int int8_grid(int resident, int units, int hkv) {
-  int waves = std::min(resident * 4, ((units + 3) / 4) * 4);
-  const int step = std::lcm(4, hkv);
-  if (waves >= step) waves -= waves % step;
-  return std::max(1, waves / 4);
+// Workgroups: what the device holds at once, or one wave per unit.
+static int int8_grid(int resident, int units) {
+  return std::max(1, std::min(resident, (units + 3) / 4));
 }
 
 hipError_t launch_score_int8(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,
                              int layer, const uint16_t *q, float C, hipStream_t st) {
   const int units = s.Hkv * tab.nbc[tab.n];
   if (s.d == 128) {
-    const int grid = int8_grid(grid_score_int8<128>(s), units, s.Hkv);
+    const int grid = int8_grid(grid_score_int8<128>(s), units);
     return launch_k(k_score_int8<128>, dim3(grid), dim3(256), 0, st, s, t, w, tab, layer, q, C);
   }
-  const int grid = int8_grid(grid_score_int8<64>(s), units, s.Hkv);
+  const int grid = int8_grid(grid_score_int8<64>(s), units);
   return launch_k(k_score_int8<64>, dim3(grid), dim3(256), 0, st, s, t, w, tab, layer, q, C);
 }
 
