@@ -76,10 +76,12 @@ __device__ void block_sum_u64_8(unsigned long long (&v)[8], CtlShared &sh) {
 // Evaluates one head on the current U: mixed weights Wt, FP16 weights W16
 // over S_h, ranking verdict and E_key.  Passes over the blocks: S_h
 // membership (positions in pi), both references (mixed maximum, FP16 maximum
-// over S_h), then weights, E_key sums and sort keys together.
+// over S_h), then weights, E_key sums and sort keys together.  gsp / hfp
+// point at the group's and the head's state: they are read with the block
+// arrays, and a final group or a head at rung 3 is not evaluated.
 __device__ void evaluate_head(const Shape &s, const Step &w, const Thresh &th, int i, int g, int hq,
-                              int NB, const float *eta, unsigned long long *keys, uint16_t *pos,
-                              CtlShared &sh) {
+                              int NB, const float *eta, const uint32_t *gsp, const uint32_t *hfp,
+                              unsigned long long *keys, uint16_t *pos, CtlShared &sh) {
   const size_t base = ((size_t)i * s.Hq + hq) * s.NBmax;
   const uint8_t *U = w.U + ((size_t)i * s.Hkv + g) * s.NBmax;
   const int n = w.ssize[(size_t)i * s.Hq + hq];
@@ -90,6 +92,7 @@ __device__ void evaluate_head(const Shape &s, const Step &w, const Thresh &th, i
   // once, up front (both score kinds; the block's kind selects afterwards),
   // so the passes below wait on no global load
   constexpr int EB = (MAX_NB + CTL_NT - 1) / CTL_NT;
+  const uint32_t gsv = *gsp, hfv = *hfp;
   bool pr[EB];
   float mb[EB], dl[EB], et[EB];
   uint32_t Lb[EB], pk[EB];
@@ -107,6 +110,7 @@ __device__ void evaluate_head(const Shape &s, const Step &w, const Thresh &th, i
       pk[r] = pi[b];                    // the block at INT8 position b
     }
   }
+  if ((gsv & 1u) || (hfv & 4u)) return;   // the whole workgroup leaves
   // S_h = pi[0 .. n): INT8 position of each member, 0xffff elsewhere
   for (int b = threadIdx.x; b < NB; b += CTL_NT) pos[b] = 0xffff;
   __syncthreads();
@@ -220,7 +224,7 @@ __device__ void evaluate_head(const Shape &s, const Step &w, const Thresh &th, i
     w.ekey64[(size_t)i * s.Hq + hq] = ek;
     w.evs[2 * ((size_t)i * s.Hq + hq)] = v4[4];
     w.evs[2 * ((size_t)i * s.Hq + hq) + 1] = v4[0];
-    uint32_t f = w.hflags[(size_t)i * s.Hq + hq];
+    uint32_t f = hfv;                   // written by this workgroup only
     f = ok ? (f | 1u) : ((f & ~1u) | 4u);
     w.hflags[(size_t)i * s.Hq + hq] = f;
   }
@@ -288,11 +292,10 @@ __global__ __launch_bounds__(CTL_NT) void k_eval(Shape s, Tier1 t, Step w, SeqTa
   const int i = blockIdx.y, hq = blockIdx.x, g = hq / s.G;
   // a new plan starts with this round (the host has read the previous one)
   if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 4) w.plan[threadIdx.x] = 0ull;
-  if (w.gstat[(size_t)i * s.Hkv + g] & 1u) return;
-  if (w.hflags[(size_t)i * s.Hq + hq] & 4u) return;
   const int NB = (tab.T[i] + BLOCK - 1) / BLOCK;
   const float *eta = t.eta + unit_of(s, tab.slot[i], layer, g) * s.NBmax;
-  evaluate_head(s, w, th, i, g, hq, NB, eta, keys, pos, sh);
+  evaluate_head(s, w, th, i, g, hq, NB, eta, w.gstat + (size_t)i * s.Hkv + g,
+                w.hflags + (size_t)i * s.Hq + hq, keys, pos, sh);
 }
 
 // Part 2, one workgroup per (sequence, KV head): rung 1 decisions; a group
@@ -306,28 +309,36 @@ __global__ __launch_bounds__(CTL_NT) void k_decide(Shape s, Tier1 t, Step w, Seq
   __shared__ int tmp[18];
   const int i = blockIdx.y, g = blockIdx.x;
   uint32_t *gs = w.gstat + (size_t)i * s.Hkv + g;
-  if (*gs & 1u) {                             // group already final: nothing new to copy
-    if (threadIdx.x == 0 && (*gs & 2u)) atomicOr(&w.plan[2], 2ull);
+  // the group's state, and (lane hh of wave 0) head hh's state and E_val
+  // ingredients from the evaluation (numerator with no value promoted,
+  // denominator), read together
+  const uint32_t gsv = *gs;
+  const size_t oh = (size_t)i * s.Hq + g * s.G + threadIdx.x;
+  uint32_t f = 0u;
+  double ek = 0.0;
+  int ss = 0;
+  unsigned long long evn = 0ull, evd = 0ull;
+  if (threadIdx.x < s.G) {
+    f = w.hflags[oh];
+    ek = w.ekey64[oh];
+    ss = w.ssize[oh];
+    evn = w.evs[2 * oh];
+    evd = w.evs[2 * oh + 1];
+  }
+  if (gsv & 1u) {                             // group already final: nothing new to copy
+    if (threadIdx.x == 0 && (gsv & 2u)) atomicOr(&w.plan[2], 2ull);
     return;
   }
   const int T = tab.T[i], NB = (T + BLOCK - 1) / BLOCK;
   const size_t unit = unit_of(s, tab.slot[i], layer, g);
-  // head state and rung-1 decisions of the group: lane hh of wave 0 takes
-  // head hh; "some head widens" is the wave's ballot
+  // rung-1 decisions of the group: lane hh of wave 0 takes head hh; "some
+  // head widens" is the wave's ballot.  The E_val ingredients go to LDS so
+  // that the head loop below indexes them freely.
   __shared__ uint32_t hf[4];
+  __shared__ unsigned long long ssum[8];
   if (threadIdx.x < 64) {
     const int hh = threadIdx.x;
-    const size_t o = (size_t)i * s.Hq + g * s.G + hh;
-    uint32_t f = 0u;
-    double ek = 0.0;
-    int ss = 0;
-    bool wid = false;
-    if (hh < s.G) {
-      f = w.hflags[o];
-      ek = w.ekey64[o];
-      ss = w.ssize[o];
-      wid = round < th.R1 && !(f & 4u) && ek > th.eps_key && ss < NB;
-    }
+    const bool wid = hh < s.G && round < th.R1 && !(f & 4u) && ek > th.eps_key && ss < NB;
     const bool any = __ballot(wid) != 0ull;
     if (hh < s.G) {
       if (wid) {
@@ -337,8 +348,10 @@ __global__ __launch_bounds__(CTL_NT) void k_decide(Shape s, Tier1 t, Step w, Seq
       // final round of this group: rung 3 for heads still above eps_key
       if (!any && !(f & 4u) && ek > th.eps_key) f |= 4u;
       hf[hh] = f;
-      w.hflags[o] = f;
-      w.ssize[o] = ss;
+      w.hflags[oh] = f;
+      w.ssize[oh] = ss;
+      ssum[2 * hh] = evn;
+      ssum[2 * hh + 1] = evd;
     }
     if (hh == 0) sh.wid = any ? 1 : 0;
   }
@@ -348,14 +361,8 @@ __global__ __launch_bounds__(CTL_NT) void k_decide(Shape s, Tier1 t, Step w, Seq
     plan_group_keys(s, w, i, g, NB);
     return;
   }
-  // E_val ingredients of every head of the group (from the evaluation:
-  // numerator with no value promoted, denominator), in LDS so that the head
-  // loop below indexes them freely
   const uint8_t *V = w.V + ((size_t)i * s.Hkv + g) * s.NBmax;
   const float *eta = t.eta + unit * s.NBmax;
-  __shared__ unsigned long long ssum[8];
-  if (threadIdx.x < 2 * s.G) ssum[threadIdx.x] = w.evs[2 * ((size_t)i * s.Hq + g * s.G) + threadIdx.x];
-  __syncthreads();
   unsigned long long sums[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) sums[k] = (k < 2 * s.G) ? ssum[k] : 0ull;
