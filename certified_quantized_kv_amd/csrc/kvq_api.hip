@@ -583,6 +583,32 @@ kvq_status read_plan(kvq_ctx *c, hipStream_t st, Plan &p) {
 // gather from their slots) and runs of uncached blocks (host link), and the
 // uncached blocks that find a slot are copied into it from the staging
 // buffer once their host copies have landed.
+// Plan entries with overlapping or adjacent runs of one (sequence, KV head)
+// and kind merged (the selection lists each query head's runs; later rounds
+// list each group's new blocks once), in (kind, group, start) order.
+void merge_runs(const std::vector<unsigned long long> &ent, std::vector<unsigned long long> &out) {
+  // an entry (len | start << 16 | ig << 32 | kind << 48) sorts by kind,
+  // group, start
+  std::vector<unsigned long long> v(ent);
+  std::sort(v.begin(), v.end());
+  out.clear();
+  out.reserve(v.size());
+  for (const unsigned long long e : v) {
+    const unsigned long long grp = e >> 32;
+    const unsigned long long st = (e >> 16) & 0xffffu, en = st + (e & 0xffffu);
+    if (!out.empty() && (out.back() >> 32) == grp) {
+      const unsigned long long pst = (out.back() >> 16) & 0xffffu;
+      const unsigned long long pen = pst + (out.back() & 0xffffu);
+      if (st <= pen) {
+        const unsigned long long nen = std::max(pen, en);
+        out.back() = (grp << 32) | (pst << 16) | (nen - pst);
+        continue;
+      }
+    }
+    out.push_back(e);
+  }
+}
+
 kvq_status issue_copies(kvq_ctx *c, const SeqTab &tab, int layer, const Plan &p, int64_t &bytes,
                         int64_t &kblocks, int64_t &vblocks, int64_t &kcached) {
   const Shape &s = c->s;
@@ -600,7 +626,9 @@ kvq_status issue_copies(kvq_ctx *c, const SeqTab &tab, int layer, const Plan &p,
     (kind ? vblocks : kblocks) += len;
     return KVQ_OK;
   };
-  for (const unsigned long long e : p.ent) {
+  std::vector<unsigned long long> runs;
+  merge_runs(p.ent, runs);
+  for (const unsigned long long e : runs) {
     const int len = (int)(e & 0xffffu), start = (int)((e >> 16) & 0xffffu);
     const int ig = (int)((e >> 32) & 0xffffu), kind = (int)((e >> 48) & 1u);
     const int i = ig / s.Hkv, g = ig % s.Hkv;
@@ -702,7 +730,6 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
   HIPCK(ctx, launch_score_int8(s, ctx->t, w, tab, layer, (const uint16_t *)q, C, st));
   tm.open(TC_SELECT);
   HIPCK(ctx, launch_select(s, w, tab, ctx->th.tau_ppm, maxNB, st));
-  HIPCK(ctx, launch_plan_keys(s, w, tab, st));
   tm.close();
   // with resident keys no copy depends on the selection, so the host reads
   // the plan only for the statistics

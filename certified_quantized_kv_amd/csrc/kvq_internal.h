@@ -114,9 +114,10 @@ __host__ __device__ inline size_t stage_k_area(const Shape &s, int i, int g, int
   return s.kres ? unit_of(s, slot, layer, g) : (size_t)i * s.Hkv + g;
 }
 
-// Capacity (entries) of each of the K and V halves of the promotion plan.
+// Capacity (entries) of each of the K and V halves of the promotion plan:
+// the selection lists runs per query head.
 __host__ __device__ inline size_t plan_kcap(const Shape &s) {
-  return (size_t)s.B * s.Hkv * s.runmax;
+  return (size_t)s.B * s.Hq * s.runmax;
 }
 
 // Byte (within a block's value codes) and nibble shift of (row r, channel c).
@@ -175,7 +176,6 @@ hipError_t launch_score_int8(const Shape &s, const Tier1 &t, const Step &w, cons
                              int layer, const uint16_t *q, float C, hipStream_t st);
 hipError_t launch_select(const Shape &s, const Step &w, const SeqTab &tab, int tau_ppm, int maxNB,
                          hipStream_t st);
-hipError_t launch_plan_keys(const Shape &s, const Step &w, const SeqTab &tab, hipStream_t st);
 hipError_t launch_score_fp16(const Shape &s, const Step &w, const SeqTab &tab, int layer,
                              int maxNB, hipStream_t st);
 hipError_t launch_control(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,

@@ -8,9 +8,10 @@
 // What << 32 | ~b (bucket sort in LDS), prefix-summed in 64-bit integers, and
 //   K* = min k >= 1 with 10^6 sum_{i<k} What_pi(i) >= tau_ppm sum_b What_b.
 // Integer sums make the result independent of reduction order.
-// Promotion is per KV head: U_g = union of the group's top-K* sets; blocks
-// new to U_g (marked by each head's workgroup) are listed as runs of
-// consecutive blocks for the host copies.
+// Promotion is per KV head: U_g = union of the group's top-K* sets.  Each
+// head's workgroup marks its blocks in U_g and in the group's new-block
+// flags, and lists its own selection as runs of consecutive blocks for the
+// host, which merges the runs of a group's heads before copying.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 #include "kvq_blockops.h"
@@ -23,10 +24,14 @@ __global__ __launch_bounds__(SEL_NT) void k_select(Shape s, Step w, SeqTab tab, 
   extern __shared__ unsigned long long keys[];
   __shared__ float red[SEL_NT / 64];
   __shared__ unsigned long long sbuf[SEL_NT / 64];
+  __shared__ uint8_t fk[MAX_NB];                   // this head's selection
+  __shared__ uint32_t hruns[MAX_NB / 2 + 1];
+  __shared__ int tmp[18];
   const int i = blockIdx.y, hq = blockIdx.x;
   const int T = tab.T[i], NB = (T + BLOCK - 1) / BLOCK;
   const int n2 = max(64, pow2_at_least(NB));
   const size_t base = ((size_t)i * s.Hq + hq) * s.NBmax;
+  for (int b = threadIdx.x; b < NB; b += SEL_NT) fk[b] = 0;
 
   // the thread's blocks b = t + r SEL_NT, loaded once
   constexpr int EB = (MAX_NB + SEL_NT - 1) / SEL_NT;
@@ -95,37 +100,22 @@ __global__ __launch_bounds__(SEL_NT) void k_select(Shape s, Step w, SeqTab tab, 
   }
   __syncthreads();
 
-  // the head's selection joins the group's new blocks (U is empty at this
-  // point of the step, so every selected block is new)
+  // the head's selection joins U_g and the group's new blocks (U is empty at
+  // this point of the step, so every selected block is new), and goes to the
+  // host as runs
   const int g = hq / s.G;
   const size_t ig = (size_t)i * s.Hkv + g;
   uint8_t *Kn = w.Knew + ig * s.NBmax;
-  for (int p = threadIdx.x; p < kst; p += SEL_NT)
-    Kn[0xffffffffu - (uint32_t)(keys[p] & 0xffffffffull)] = 1;   // benign race: every writer stores 1
-}
-
-// The group's plan after the selection: U = the new blocks, and their runs.
-__global__ __launch_bounds__(1024) void k_plan_keys(Shape s, Step w, SeqTab tab) {
-  const int i = blockIdx.y, g = blockIdx.x;
-  const int NB = (tab.T[i] + BLOCK - 1) / BLOCK;
-  const size_t ig = (size_t)i * s.Hkv + g;
-  __shared__ int tmp[18];
-  __shared__ uint8_t fk[MAX_NB];
-  const uint8_t *Kn = w.Knew + ig * s.NBmax;
-  uint8_t *U = w.U + ig * s.NBmax;
-  for (int b = threadIdx.x; b < NB; b += blockDim.x) {
-    const uint8_t f = Kn[b];
-    fk[b] = f;
-    if (f) U[b] = 1;
+  uint8_t *Ug = w.U + ig * s.NBmax;
+  for (int p = threadIdx.x; p < kst; p += SEL_NT) {
+    const uint32_t b = 0xffffffffu - (uint32_t)(keys[p] & 0xffffffffull);
+    fk[b] = 1;
+    Kn[b] = 1;      // benign races across the group's heads: every writer stores 1
+    Ug[b] = 1;
   }
   __syncthreads();
-  uint32_t *runs = w.runs + (ig * 2 + 0) * s.runmax;
-  const int nr = build_runs(fk, NB, runs, tmp);
-  emit_runs(s, w, (int)ig, 0, runs, nr, tmp + 17);
-}
-
-hipError_t launch_plan_keys(const Shape &s, const Step &w, const SeqTab &tab, hipStream_t st) {
-  return launch_k(k_plan_keys, dim3(s.Hkv, tab.n), dim3(1024), 0, st, s, w, tab);
+  const int nr = build_runs(fk, NB, hruns, tmp);
+  emit_runs(s, w, (int)ig, 0, hruns, nr, tmp + 17);
 }
 
 hipError_t launch_select(const Shape &s, const Step &w, const SeqTab &tab, int tau_ppm, int maxNB,
