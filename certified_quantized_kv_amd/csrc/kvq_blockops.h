@@ -184,14 +184,17 @@ __device__ __forceinline__ void sort_desc_network(unsigned long long *keys, int 
 // ---- block sort of distinct 64-bit keys into descending order --------------
 // Bucket sort by a monotone image of each key: its binary32 image, cut into
 // 4096 buckets on a log-like scale (the float bits), or, if that crowds a
-// bucket, key - smallest key on a linear scale.  Keys are counted and
-// scattered into bucket order with LDS atomics, and each key takes its final
-// place inside its bucket by counting the bucket's keys ahead of it.  The
-// result does not depend on the order of the atomics.  When both images leave
-// more than SORT_MAX_BUCKET keys in some bucket (clusters of keys that differ
-// only far below their leading bits) the comparison network above sorts
-// instead.  The caller's LDS buffer `keys` holds
-// sort_lds_bytes(cap) bytes (cap >= n keys, cap a power of two >= 64).
+// bucket, key - smallest key on a linear scale.  Each thread keeps its keys
+// in registers; counting them into buckets with LDS atomics also gives each
+// key a slot in its bucket.  A key alone in its bucket goes straight to its
+// final place (the bucket's start); the others are scattered by slot and
+// take their place inside the bucket by counting the bucket's keys ahead of
+// them.  The result does not depend on the order of the atomics.  When both
+// images leave more than SORT_MAX_BUCKET keys in some bucket (clusters of
+// keys that differ only far below their leading bits) the comparison network
+// above sorts instead.  The caller's LDS buffer `keys` holds
+// sort_lds_bytes(cap) bytes (cap >= n keys, cap a power of two >= 64,
+// n <= MAX_NB).
 constexpr int SORT_BUCKETS = 4096;
 
 __host__ __device__ inline size_t sort_lds_bytes(int cap) {
@@ -216,6 +219,7 @@ __device__ __forceinline__ bool sort_desc_u64(unsigned long long *keys, int n, i
                                               OnPlace on_place = OnPlace()) {
   constexpr int SB = SORT_BUCKETS;
   constexpr int PER = SB / NT;           // counters per thread in the scan
+  constexpr int RK = (MAX_NB + NT - 1) / NT;   // keys per thread
   static_assert(SB % NT == 0, "bucket count");
   unsigned long long *tmp = keys + cap;
   int *base = reinterpret_cast<int *>(keys + 2 * (size_t)cap);   // SB + 1 entries
@@ -225,12 +229,20 @@ __device__ __forceinline__ bool sort_desc_u64(unsigned long long *keys, int n, i
   __shared__ int wsum[2][NT / 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __syncthreads();
-  // image 1: the key's own binary32 image, over the images' range
+  // the thread's keys p = t + r NT; image 1: the key's own binary32 image,
+  // over the images' range
+  unsigned long long kv[RK];
+  int bk[RK], slot[RK];
   uint32_t lo = 0xffffffffu, hi = 0u;
-  for (int p = threadIdx.x; p < n; p += NT) {
-    const uint32_t f = key_image(keys[p]);
-    lo = min(lo, f);
-    hi = max(hi, f);
+#pragma unroll
+  for (int r = 0; r < RK; ++r) {
+    const int p = threadIdx.x + r * NT;
+    kv[r] = p < n ? keys[p] : 0ull;
+    if (p < n) {
+      const uint32_t f = key_image(kv[r]);
+      lo = min(lo, f);
+      hi = max(hi, f);
+    }
   }
   lo = wave_min_u32(lo);
   hi = wave_max_u32(hi);
@@ -257,7 +269,7 @@ __device__ __forceinline__ bool sort_desc_u64(unsigned long long *keys, int n, i
     return SB - 1 - f;
   };
   int c[PER];
-  int own = 0, xs = 0;
+  int own = 0, xs = 0, big = 0;
   for (int pass = 0; pass < 2; ++pass) {
     if (pass == 0) {
       const uint32_t span = hi - lo;
@@ -265,9 +277,12 @@ __device__ __forceinline__ bool sort_desc_u64(unsigned long long *keys, int n, i
     } else {
       rel = true;
       unsigned long long kmn = ~0ull, kmx = 0ull;
-      for (int p = threadIdx.x; p < n; p += NT) {
-        kmn = min(kmn, keys[p]);
-        kmx = max(kmx, keys[p]);
+#pragma unroll
+      for (int r = 0; r < RK; ++r) {
+        if (threadIdx.x + r * NT < n) {
+          kmn = min(kmn, kv[r]);
+          kmx = max(kmx, kv[r]);
+        }
       }
       kmn = wave_min_u64(kmn);
       kmx = wave_max_u64(kmx);
@@ -287,12 +302,18 @@ __device__ __forceinline__ bool sort_desc_u64(unsigned long long *keys, int n, i
       const unsigned long long span = kmax - kmin;
       sh = span >= (unsigned long long)SB ? (64 - __clzll((long long)span)) - 12 : 0;
     }
-    for (int p = threadIdx.x; p < n; p += NT) atomicAdd(&cur[bucket(keys[p])], 1);
+#pragma unroll
+    for (int r = 0; r < RK; ++r) {
+      if (threadIdx.x + r * NT < n) {
+        bk[r] = bucket(kv[r]);
+        slot[r] = atomicAdd(&cur[bk[r]], 1);
+      }
+    }
     __syncthreads();
     // this thread's counters [t PER, (t+1) PER): their sum, scanned over the
     // wave, and the largest count, reduced over the wave
     own = 0;
-    int big = 0;
+    big = 0;
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       c[k] = cur[threadIdx.x * PER + k];
@@ -317,7 +338,7 @@ __device__ __forceinline__ bool sort_desc_u64(unsigned long long *keys, int n, i
         sort_desc_network<NT, 4>(keys, n);
       return false;
     }
-    __syncthreads();                     // wsum is written again by pass 1
+    __syncthreads();                     // wsum and cur are written again by pass 1
   }
   // exclusive prefix of the counts -> base
   int before = 0;
@@ -328,37 +349,48 @@ __device__ __forceinline__ bool sort_desc_u64(unsigned long long *keys, int n, i
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
     base[threadIdx.x * PER + k] = run;
-    cur[threadIdx.x * PER + k] = run;
     run += c[k];
   }
   if (threadIdx.x == 0) base[SB] = n;
   __syncthreads();
-  // scatter into bucket order
-  for (int p = threadIdx.x; p < n; p += NT) {
-    const unsigned long long k = keys[p];
-    tmp[atomicAdd(&cur[bucket(k)], 1)] = k;
+  // a key alone in its bucket is placed; the others are scattered by slot
+  int b0[RK], b1[RK];
+#pragma unroll
+  for (int r = 0; r < RK; ++r) {
+    if (threadIdx.x + r * NT >= n) continue;
+    b0[r] = base[bk[r]];
+    b1[r] = base[bk[r] + 1];
+    if (b1[r] - b0[r] == 1) {
+      keys[b0[r]] = kv[r];
+      on_place(kv[r], b0[r]);
+    } else {
+      tmp[b0[r] + slot[r]] = kv[r];
+    }
   }
-  __syncthreads();
-  // place inside the bucket: keys ahead = larger keys (equal keys by slot)
-  for (int p = threadIdx.x; p < n; p += NT) {
-    const unsigned long long k = tmp[p];
-    const int bk = bucket(k);
-    const int b0 = base[bk], b1 = base[bk + 1];
-    int r = 0;
-    int q = b0;
-    for (; q + 4 <= b1; q += 4) {
-      const unsigned long long y0 = tmp[q], y1 = tmp[q + 1], y2 = tmp[q + 2], y3 = tmp[q + 3];
-      r += (y0 > k || (y0 == k && q < p)) ? 1 : 0;
-      r += (y1 > k || (y1 == k && q + 1 < p)) ? 1 : 0;
-      r += (y2 > k || (y2 == k && q + 2 < p)) ? 1 : 0;
-      r += (y3 > k || (y3 == k && q + 3 < p)) ? 1 : 0;
+  if (big > 1) {
+    __syncthreads();
+    // place inside the bucket: keys ahead = larger keys (equal keys by slot)
+#pragma unroll
+    for (int r = 0; r < RK; ++r) {
+      if (threadIdx.x + r * NT >= n || b1[r] - b0[r] == 1) continue;
+      const unsigned long long k = kv[r];
+      const int me = b0[r] + slot[r];
+      int rk = 0;
+      int q = b0[r];
+      for (; q + 4 <= b1[r]; q += 4) {
+        const unsigned long long y0 = tmp[q], y1 = tmp[q + 1], y2 = tmp[q + 2], y3 = tmp[q + 3];
+        rk += (y0 > k || (y0 == k && q < me)) ? 1 : 0;
+        rk += (y1 > k || (y1 == k && q + 1 < me)) ? 1 : 0;
+        rk += (y2 > k || (y2 == k && q + 2 < me)) ? 1 : 0;
+        rk += (y3 > k || (y3 == k && q + 3 < me)) ? 1 : 0;
+      }
+      for (; q < b1[r]; ++q) {
+        const unsigned long long y = tmp[q];
+        rk += (y > k || (y == k && q < me)) ? 1 : 0;
+      }
+      keys[b0[r] + rk] = k;
+      on_place(k, b0[r] + rk);
     }
-    for (; q < b1; ++q) {
-      const unsigned long long y = tmp[q];
-      r += (y > k || (y == k && q < p)) ? 1 : 0;
-    }
-    keys[b0 + r] = k;
-    on_place(k, b0 + r);
   }
   __syncthreads();
   return true;
