@@ -127,6 +127,12 @@ def same_traces(ta, tb, Hq, Hkv, T, where):
 
 def compare(case, gpu, ref, check_out=True):
     G = case.Hq // case.Hkv
+    # every block of every U_g crossed the host link exactly once (the host
+    # merges the selection's per-head runs of a group, later rounds add new
+    # blocks only)
+    nU = sum(int(np.sum(r.groups[g].U)) for r, _ in ref for g in range(case.Hkv))
+    assert gpu["stats"]["promoted_key_blocks"] == nU, \
+        f"{case.name}: promoted key blocks {gpu['stats']['promoted_key_blocks']} vs |U| {nU}"
     for i, (r, groups) in enumerate(ref):
         tr_g = gpu["trace"][i]
         T = groups[0][0]["T"]
