@@ -12,7 +12,8 @@ ranking check and bounds, ladder, split-K decode).  Inputs of the timed steps
 
 value = KV tokens attended per second over the whole job: sum over timed steps
 and layers of the context length, divided by the wall time of the timed steps
-(which read no per-call statistics back).
+(which read no per-call statistics back).  step_ms gives the median, 10th and
+90th percentile of the per-step times (events on the stream between steps).
 
 Also reported, from the last two steps' queries run again on every layer with
 statistics on: per-kernel times stamped by the runtime at each kernel's start
@@ -173,10 +174,13 @@ def main():
     log(f"prefill {L} layers x {T0} tokens done ({time.time() - t_setup:.1f} s)")
 
     recs = []
+    step_ms = []
 
     def run_steps(cx):
         """Warm-up, then the timed steps (append + certified decode per layer,
-        no per-call stats readback); returns (wall seconds, KV tokens)."""
+        no per-call stats readback); returns (wall seconds, KV tokens).  An
+        event on the stream after each timed step gives the per-step times
+        (no extra synchronisation)."""
         toks = [0]
 
         def step(s, timed):
@@ -188,12 +192,17 @@ def main():
         for s in range(a.warmup):
             step(s, False)
         torch.cuda.synchronize()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
         t0 = time.time()
+        evs[0].record()
         for s in range(a.warmup, n_total):
             step(s, True)
+            evs[s - a.warmup + 1].record()
             log(f"step {s - a.warmup + 1}/{a.steps} done")
         torch.cuda.synchronize()
-        return time.time() - t0, toks[0]
+        wall_s = time.time() - t0
+        step_ms[:] = [evs[k].elapsed_time(evs[k + 1]) for k in range(a.steps)]
+        return wall_s, toks[0]
 
     def instrument(cx, rec):
         """Per-kernel times, promotions and levels: the last two timed steps'
@@ -249,6 +258,7 @@ def main():
         }
 
     wall, kv_tokens = run_steps(ctx)
+    steps_main = sorted(step_ms)
     out_default = out.clone()
     value = kv_tokens / wall
     instrument(ctx, recs)
@@ -347,8 +357,14 @@ def main():
         ref = oracle.decode_step(oracle.Config(), q16, groups)
         t_step = time.time() - tq
         T_last = ks.shape[0]
+        model = ""
+        try:
+            with open("/proc/cpuinfo") as f:
+                model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+        except OSError:
+            pass
         cpu = {"value": round(T_last / t_step, 1), "unit": "KV tokens/s", "cores": 1,
-               "kind": "oracle",
+               "kind": "oracle", "host": f"{model}, {os.cpu_count()} logical CPUs visible",
                "sample": f"one certified decode step of layer 0 (32 q / 8 KV heads, d 128, "
                          f"{T_last} tokens) after the timed steps; {t_step:.2f} s per layer-step, "
                          f"tier-1 quantization of that layer {t_tier1:.2f} s (not in value)"}
@@ -426,6 +442,9 @@ def main():
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "KV tokens/s", "n_gpus": 1,
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(wall / a.steps * 1e3, 3),
+        "step_ms": {"median": round(float(np.median(steps_main)), 3),
+                    "p10": round(float(np.percentile(steps_main, 10)), 3),
+                    "p90": round(float(np.percentile(steps_main, 90)), 3)},
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "i8xi8->i32 scores, u4 values, f32 accumulate", "data": "synthetic",
         "config": {"workload": "llama3.1-8b-shaped 32-layer decode, 128K context, append + "
