@@ -710,7 +710,9 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
     maxNB = std::max(maxNB, (int)((T + BLOCK - 1) / BLOCK));
   }
   hipStream_t st = (hipStream_t)stream;
-  const bool timing = (ctx->cfg.flags & KVQ_FLAG_TIMING) != 0;
+  // kernel and copy events only when the call returns statistics: a launch
+  // with start/stop events costs several microseconds of dispatch gap
+  const bool timing = stats && (ctx->cfg.flags & KVQ_FLAG_TIMING) != 0;
   Step &w = ctx->w;
   const size_t NBm = s.NBmax;
   int64_t h2d = 0, kblk = 0, vblk = 0, dense_heads = 0, kcached = 0;

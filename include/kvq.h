@@ -151,7 +151,8 @@ typedef struct kvq_step_stats {
     /* times (KVQ_FLAG_TIMING), milliseconds.  Kernel entries are sums of
        kernel durations, each stamped by the runtime at the kernel's own
        start and end (hipExtLaunchKernel events); copies are bracketed by
-       events on the copy stream. */
+       events on the copy stream.  The events are recorded only on calls
+       that return statistics. */
     float ms_score_int8;           /* INT8 scoring kernel                         */
     float ms_select;               /* top-K* selection, union planning, run lists */
     float ms_score_fp16;           /* FP16 scoring of promoted blocks (all rounds)*/
