@@ -86,6 +86,7 @@ _SIGS = {
     "kvq_trace_bytes": (I64, [P, I32, I32]),
     "kvq_export_trace": (I32, [P, I32, I32, P, ctypes.c_size_t]),
     "kvq_selftest_exp2k": (I32, [P, P, I64, P]),
+    "kvq_selftest_merge_runs": (I32, [P, I64, P, P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -124,6 +125,20 @@ def _dev(t, dtype, name):
 def _i32(seq):
     arr = (I32 * len(seq))(*[int(x) for x in seq])
     return arr
+
+
+def merge_runs(entries):
+    """The host's merge of promotion-plan entries (test hook, no device call):
+    entries = sequence of ints len | start << 16 | group << 32 | kind << 48."""
+    n = len(entries)
+    a = np.ascontiguousarray(np.asarray(entries, dtype=np.uint64))
+    out = np.zeros(max(n, 1), np.uint64)
+    n_out = ctypes.c_int64(0)
+    st = _lib.kvq_selftest_merge_runs(a.ctypes.data_as(P), n, out.ctypes.data_as(P),
+                                      ctypes.byref(n_out))
+    if st != 0:
+        raise KvqError(st, "merge_runs")
+    return out[:n_out.value]
 
 
 def exp2k(x):

@@ -1082,4 +1082,17 @@ kvq_status kvq_selftest_exp2k(const float *x, float *y, int64_t n, void *stream)
   return launch_exp2k(x, y, n, (hipStream_t)stream) == hipSuccess ? KVQ_OK : KVQ_EHIP;
 }
 
+kvq_status kvq_selftest_merge_runs(const uint64_t *in, int64_t n, uint64_t *out, int64_t *n_out) {
+  if (n < 0 || (n > 0 && (!in || !out)) || !n_out) return KVQ_EINVAL;
+  for (int64_t k = 0; k < n; ++k)
+    if ((in[k] >> 49) != 0 || (in[k] & 0xffffu) == 0 ||
+        ((in[k] >> 16) & 0xffffu) + (in[k] & 0xffffu) > 0xffffu)
+      return KVQ_EINVAL;
+  std::vector<unsigned long long> ent(in, in + n), m;
+  merge_runs(ent, m);
+  std::copy(m.begin(), m.end(), out);
+  *n_out = (int64_t)m.size();
+  return KVQ_OK;
+}
+
 }  // extern "C"

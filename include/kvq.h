@@ -272,6 +272,15 @@ kvq_status kvq_export_trace(kvq_ctx *ctx, int32_t which, int32_t seq_id, void *h
  * device floats.  For tests. */
 kvq_status kvq_selftest_exp2k(const float *x, float *y, int64_t n, void *stream);
 
+/* Merges promotion-plan entries the way a decode step does before copying
+ * (host only, no device call).  in: n host entries, each
+ * len | start << 16 | group << 32 | kind << 48 (len >= 1, start + len < 2^16,
+ * kind 0 or 1); out: host room for n entries, receives the merged entries
+ * (overlapping or adjacent runs of one group and kind joined) in (kind,
+ * group, start) order, *n_out of them.  KVQ_EINVAL on a malformed entry.
+ * For tests. */
+kvq_status kvq_selftest_merge_runs(const uint64_t *in, int64_t n, uint64_t *out, int64_t *n_out);
+
 #ifdef __cplusplus
 }
 #endif
