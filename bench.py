@@ -21,8 +21,8 @@ and end on the stream it runs on; the roofline of the dominant kernel; the
 quantized-tier pass (INT8 scoring + selection + controller + mixed decode)
 against the tier-1 bytes it must read; host-link throughput of promotions.
 Then: the dense FP16 (device-resident cache) and naive INT8/INT4 comparators
-on the same layers; the CPU oracle timed on one layer-step (a bounded
-sample), whose output is also compared with the GPU's for that layer (sampled
+on the same layers; the CPU oracle timed on four layer-steps (a bounded
+sample), whose outputs are also compared with the GPU's for those layers (sampled
 parity); the same timed steps on a context that keeps promoted FP16 keys in
 device memory across steps; and on one with a device cache of FP16 key blocks
 sized so that tier 1 plus the cache take the pages' ~56 % of the dense FP16
@@ -129,7 +129,8 @@ def main():
     gen = torch.Generator(device=dev)
     keep = not a.no_cpu_baseline
     comp = not a.no_comparators
-    host0 = None
+    NCPU = 4                          # layers in the oracle's sample
+    host0 = {}
     dense_k, dense_v = [], []          # FP16 caches in device memory (comparator)
     def prefill(cx, keep_dense, keep_host0):
         nonlocal host0
@@ -149,8 +150,8 @@ def main():
                 vd[0, :T0] = V
                 dense_k.append(kd)
                 dense_v.append(vd)
-            if keep_host0 and layer == 0:
-                host0 = (K.cpu().numpy().view(np.uint16), V.cpu().numpy().view(np.uint16))
+            if keep_host0 and layer < NCPU:
+                host0[layer] = (K.cpu().numpy().view(np.uint16), V.cpu().numpy().view(np.uint16))
             del K, V
 
     prefill(ctx, comp, keep)
@@ -337,44 +338,53 @@ def main():
     if keep:
         import oracle
         oracle.build()
-        # the layer-0 state after the last timed step, recomputed on the GPU
-        # and on the CPU from the same fp16 inputs
-        K0, V0 = host0
-        ks = np.concatenate([K0] + [k1s[s][0].cpu().numpy().view(np.uint16) for s in range(n_total)])
-        vs = np.concatenate([V0] + [v1s[s][0].cpu().numpy().view(np.uint16) for s in range(n_total)])
-        q_last = qs[n_total - 1][0]
-        o_gpu, ek_g, ev_g, lv_g, _ = ctx.decode_step(0, [0], q_last, stats=False)
-        torch.cuda.synchronize()
-        q16 = q_last[0].cpu().numpy().view(np.uint16)
-        tq = time.time()
-        groups = []
-        for g in range(Hkv):
-            k16 = np.ascontiguousarray(ks[:, g])
-            v16 = np.ascontiguousarray(vs[:, g])
-            groups.append((oracle.build_tier1(k16, v16), k16, v16))
-        t_tier1 = time.time() - tq
-        tq = time.time()
-        ref = oracle.decode_step(oracle.Config(), q16, groups)
-        t_step = time.time() - tq
-        T_last = ks.shape[0]
+        # the state of layers 0 .. NCPU-1 after the last timed step,
+        # recomputed on the GPU and on the CPU from the same fp16 inputs
         model = ""
         try:
             with open("/proc/cpuinfo") as f:
                 model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
         except OSError:
             pass
-        cpu = {"value": round(T_last / t_step, 1), "unit": "KV tokens/s", "cores": 1,
+        t_step = t_tier1 = 0.0
+        toks_cpu = 0
+        lv_ok = ek_ok = ev_ok = True
+        err = 0.0
+        for layer in range(NCPU):
+            K0, V0 = host0[layer]
+            ks = np.concatenate([K0] + [k1s[s][layer].cpu().numpy().view(np.uint16)
+                                        for s in range(n_total)])
+            vs = np.concatenate([V0] + [v1s[s][layer].cpu().numpy().view(np.uint16)
+                                        for s in range(n_total)])
+            q_last = qs[n_total - 1][layer]
+            o_gpu, ek_g, ev_g, lv_g, _ = ctx.decode_step(layer, [0], q_last, stats=False)
+            torch.cuda.synchronize()
+            q16 = q_last[0].cpu().numpy().view(np.uint16)
+            tq = time.time()
+            groups = []
+            for g in range(Hkv):
+                k16 = np.ascontiguousarray(ks[:, g])
+                v16 = np.ascontiguousarray(vs[:, g])
+                groups.append((oracle.build_tier1(k16, v16), k16, v16))
+            t_tier1 += time.time() - tq
+            tq = time.time()
+            ref = oracle.decode_step(oracle.Config(), q16, groups)
+            t_step += time.time() - tq
+            T_last = ks.shape[0]
+            toks_cpu += T_last
+            lv_ok &= bool(np.array_equal(lv_g.cpu().numpy()[0], ref.level))
+            ek_ok &= bool(np.array_equal(ek_g.cpu().numpy()[0].view(np.uint32), ref.e_key.view(np.uint32)))
+            ev_ok &= bool(np.array_equal(ev_g.cpu().numpy()[0].view(np.uint32), ref.e_val.view(np.uint32)))
+            err = max(err, float(np.abs(o_gpu.cpu().numpy()[0].astype(np.float64) - ref.out).max()))
+            del ks, vs, groups
+            log(f"oracle layer {layer} done")
+        cpu = {"value": round(toks_cpu / t_step, 1), "unit": "KV tokens/s", "cores": 1,
                "kind": "oracle", "host": f"{model}, {os.cpu_count()} logical CPUs visible",
-               "sample": f"one certified decode step of layer 0 (32 q / 8 KV heads, d 128, "
-                         f"{T_last} tokens) after the timed steps; {t_step:.2f} s per layer-step, "
-                         f"tier-1 quantization of that layer {t_tier1:.2f} s (not in value)"}
-        err = float(np.abs(o_gpu.cpu().numpy()[0].astype(np.float64) - ref.out).max())
-        parity = {"layer": 0, "tokens": T_last,
-                  "levels_equal": bool(np.array_equal(lv_g.cpu().numpy()[0], ref.level)),
-                  "e_key_bits_equal": bool(np.array_equal(ek_g.cpu().numpy()[0].view(np.uint32),
-                                                          ref.e_key.view(np.uint32))),
-                  "e_val_bits_equal": bool(np.array_equal(ev_g.cpu().numpy()[0].view(np.uint32),
-                                                          ref.e_val.view(np.uint32))),
+               "sample": f"one certified decode step of each of layers 0-{NCPU - 1} (32 q / 8 KV heads, "
+                         f"d 128, {T_last} tokens) after the timed steps; {t_step / NCPU:.2f} s per "
+                         f"layer-step, tier-1 quantization {t_tier1 / NCPU:.2f} s per layer (not in value)"}
+        parity = {"layers": list(range(NCPU)), "tokens": T_last, "levels_equal": lv_ok,
+                  "e_key_bits_equal": ek_ok, "e_val_bits_equal": ev_ok,
                   "max_abs_out_err": err, "tol": 2e-3}
 
     resid = None
