@@ -770,7 +770,7 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
     // they are launched again below and overwrite these results
     if (!ctx->th.force_dense) {
       tm.open(TC_DECODE);
-      HIPCK(ctx, launch_decode(s, ctx->t, w, tab, layer, maxNB, false, st));
+      HIPCK(ctx, launch_decode(s, ctx->t, w, tab, layer, maxNB, st));
       tm.open(TC_COMBINE);
       HIPCK(ctx, launch_combine(s, w, tab, out, 0, e_key, e_val, level, st));
     }
@@ -823,12 +823,14 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
         HIPCK(ctx, hipEventRecord(ctx->ev_copy, ctx->cstream));
         HIPCK(ctx, hipStreamWaitEvent(st, ctx->ev_copy, 0));
         tm.open(TC_DENSE);
-        HIPCK(ctx, launch_decode(s, ctx->t, w, tab, layer, maxNB, true, st));
+        HIPCK(ctx, launch_dense_staged(s, w, tab, layer, (const uint16_t *)q, maxNB, st));
         tm.close();
       }
     }
-    tm.open(TC_DECODE);
-    HIPCK(ctx, launch_decode(s, ctx->t, w, tab, layer, maxNB, false, st));
+    if (!ctx->th.force_dense) {        // forced: every head is at level 4 (dense partials)
+      tm.open(TC_DECODE);
+      HIPCK(ctx, launch_decode(s, ctx->t, w, tab, layer, maxNB, st));
+    }
     tm.open(TC_COMBINE);
     HIPCK(ctx, launch_combine(s, w, tab, out, 0, maybe_dense ? nullptr : e_key,
                               maybe_dense ? nullptr : e_val, maybe_dense ? nullptr : level, st));
@@ -903,7 +905,7 @@ kvq_status kvq_decode_naive(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_
   // empty U and V: INT8 scores and INT4 values for every block
   const float C = (float)(1.4426950408889634 / sqrt((double)s.d));
   HIPCK(ctx, launch_score_int8(s, ctx->t, w, tab, layer, (const uint16_t *)q, C, st));
-  HIPCK(ctx, launch_decode(s, ctx->t, w, tab, layer, maxNB, false, st));
+  HIPCK(ctx, launch_decode(s, ctx->t, w, tab, layer, maxNB, st));
   HIPCK(ctx, launch_combine(s, w, tab, out, 1, nullptr, nullptr, nullptr, st));
   return KVQ_OK;
 }

@@ -11,115 +11,14 @@
 //           in registers as fmaf(scale, code, offset) elsewhere;
 //   online softmax in fp32: the chunk's max M_h and sum l_h per head, and
 //           o_h = sum_t 2^(x_t - M_h) v_t; the combine kernel merges chunks.
-// Dense mode (groups with a head at level 3/4): scores are the canonical
-// FP16-key chains recomputed from the staged keys, values FP16 throughout.
-// The four query heads of a KV head share each value load.
+// Dense mode (groups with a head at level 3/4) is the kernel of
+// kvq_dense.hip on the staged FP16 keys and values.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
 namespace kvq {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
-
-// Dense chunk scores (canonical FP16-key chains from the staged keys kst) ->
-// per-head p = 2^(x - M_h) in LDS, M_h and l_h = sum p.
-template <int D>
-__device__ __forceinline__ void chunk_softmax(const Shape &s, const Step &w, int i, int g,
-                                              const uint16_t *kst, int t0, int nt,
-                                              float (*ps)[DEC_CB * BLOCK], float *sM, float *sL) {
-  const int G = s.G;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int idx = threadIdx.x; idx < G * nt; idx += 256) {
-    const int h = idx / nt, tt = idx % nt;
-    const int tok = t0 + tt;
-    const int hq = g * G + h;
-    const uint16_t *row = kst + (size_t)tok * D;
-    const float *q = w.qp + ((size_t)i * s.Hq + hq) * D;
-    float x = 0.0f;
-    for (int c = 0; c < D; ++c) x = fmaf(q[c], h2f(row[c]), x);
-    ps[h][tt] = x;
-  }
-  __syncthreads();
-  if (wave < G) {
-    float m = -INFINITY;
-    for (int tt = lane; tt < nt; tt += 64) m = fmaxf(m, ps[wave][tt]);
-    m = bfly_max<64>(m);
-    float l = 0.0f;
-    for (int tt = lane; tt < nt; tt += 64) {
-      const float p = exp2f(ps[wave][tt] - m);
-      ps[wave][tt] = p;
-      l += p;
-    }
-    l = bfly_sum<64>(l);
-    if (lane == 0) {
-      sM[wave] = m;
-      sL[wave] = l;
-    }
-  }
-  __syncthreads();
-}
-
-// Dense fallback: FP16 keys and values throughout (VALU).
-template <int D>
-__global__ __launch_bounds__(256) void k_decode_dense(Shape s, Tier1 t, Step w, SeqTab tab, int layer) {
-  constexpr int CT = DEC_CB * BLOCK;
-  constexpr int CPL = D / 64;
-  const int i = blockIdx.z, g = blockIdx.y, ch = blockIdx.x;
-  const int T = tab.T[i], NB = (T + BLOCK - 1) / BLOCK;
-  const int b0 = ch * DEC_CB;
-  if (b0 >= NB) return;
-  const size_t ig = (size_t)i * s.Hkv + g;
-  if (!w.gdense[ig]) return;
-  const int G = s.G;
-  const int t0 = b0 * BLOCK, nt = min(T, (b0 + DEC_CB) * BLOCK) - t0;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  __shared__ float ps[4][CT];
-  __shared__ float red[4][4][D];
-  __shared__ float sM[4], sL[4];
-  const uint16_t *kst = w.stage_k + stage_k_area(s, i, g, tab.slot[i], layer) * s.Tmax * D;
-  chunk_softmax<D>(s, w, i, g, kst, t0, nt, ps, sM, sL);
-  float o[4][CPL];
-#pragma unroll
-  for (int h = 0; h < 4; ++h)
-#pragma unroll
-    for (int k = 0; k < CPL; ++k) o[h][k] = 0.0f;
-  const int per = (nt + 3) / 4;
-  const int ta = wave * per, tb = min(nt, ta + per);
-  const uint16_t *sv = w.stage_v + ig * s.Tmax * D;
-#pragma unroll 4
-  for (int tt = ta; tt < tb; ++tt) {
-    const int tok = t0 + tt;
-    float v[CPL];
-    if (CPL == 2) {
-      const uint32_t pr = *(const uint32_t *)(sv + (size_t)tok * D + 2 * lane);
-      v[0] = h2f((uint16_t)(pr & 0xffffu));
-      v[CPL - 1] = h2f((uint16_t)(pr >> 16));
-    } else {
-      v[0] = h2f(sv[(size_t)tok * D + lane]);
-    }
-#pragma unroll
-    for (int h = 0; h < 4; ++h)
-      if (h < G) {
-        const float p = ps[h][tt];
-#pragma unroll
-        for (int k = 0; k < CPL; ++k) o[h][k] = fmaf(p, v[k], o[h][k]);
-      }
-  }
-#pragma unroll
-  for (int h = 0; h < 4; ++h)
-#pragma unroll
-    for (int k = 0; k < CPL; ++k) red[wave][h][CPL * lane + k] = o[h][k];
-  __syncthreads();
-  float *part = w.partd + ((ig * s.nchmax + ch) * G) * (size_t)(D + 2);
-  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
-    const int h = idx / D, c = idx % D;
-    part[(size_t)h * (D + 2) + c] = red[0][h][c] + red[1][h][c] + red[2][h][c] + red[3][h][c];
-  }
-  if (threadIdx.x < G) {
-    part[(size_t)threadIdx.x * (D + 2) + D] = sM[threadIdx.x];
-    part[(size_t)threadIdx.x * (D + 2) + D + 1] = sL[threadIdx.x];
-  }
-}
 
 // Mixed decode.  Per block, sum_t p_ht v_tc with v = off_tj + s_tj code_tc
 // splits into sum_t p_ht off_tj (VALU, per group) and the contraction
@@ -375,19 +274,10 @@ __global__ __launch_bounds__(256, 6) void k_decode_mixed(Shape s, Tier1 t, Step 
 }
 
 hipError_t launch_decode(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,
-                         int layer, int maxNB, bool dense, hipStream_t st) {
-  dim3 grid((maxNB + (dense ? DEC_CB : MIX_CB) - 1) / (dense ? DEC_CB : MIX_CB), s.Hkv, tab.n);
-  if (s.d == 128) {
-    if (dense)
-      return launch_k(k_decode_dense<128>, grid, dim3(256), 0, st, s, t, w, tab, layer);
-    else
-      return launch_k(k_decode_mixed<128>, grid, dim3(256), 0, st, s, t, w, tab, layer);
-  } else {
-    if (dense)
-      return launch_k(k_decode_dense<64>, grid, dim3(256), 0, st, s, t, w, tab, layer);
-    else
-      return launch_k(k_decode_mixed<64>, grid, dim3(256), 0, st, s, t, w, tab, layer);
-  }
+                         int layer, int maxNB, hipStream_t st) {
+  dim3 grid((maxNB + MIX_CB - 1) / MIX_CB, s.Hkv, tab.n);
+  if (s.d == 128) return launch_k(k_decode_mixed<128>, grid, dim3(256), 0, st, s, t, w, tab, layer);
+  return launch_k(k_decode_mixed<64>, grid, dim3(256), 0, st, s, t, w, tab, layer);
 }
 
 // Merges the chunk partials of each (sequence, query head): levels 3/4 read

@@ -23,21 +23,22 @@ namespace kvq {
 typedef _Float16 h8v __attribute__((ext_vector_type(8)));
 typedef float f4v __attribute__((ext_vector_type(4)));
 
+// One chunk (DEC_CB blocks) of sequence i, KV head g: q of the group's
+// heads at qg ([G][D] fp16), K and V rows of the sequence at Kb / Vb with
+// rowstride halves between tokens; partials to w.partd.
 template <int D>
-__global__ __launch_bounds__(256) void k_dense_vram(Shape s, Step w, DenseArgs a) {
+__device__ __forceinline__ void dense_chunk(const Shape &s, const Step &w, int i, int g, int ch,
+                                            int T, const uint16_t *qg, const uint16_t *Kb,
+                                            const uint16_t *Vb, size_t rowstride) {
   constexpr int KS = D / 32;                 // MFMA k-steps over the channels
   constexpr int CPL = D / 16;                // channels per lane in P.V
   constexpr int STEP = 32;                   // tokens per step (two 16-token tiles)
-  const int i = blockIdx.z, g = blockIdx.y, ch = blockIdx.x;
-  const int T = a.T[i], NB = (T + BLOCK - 1) / BLOCK;
+  const int NB = (T + BLOCK - 1) / BLOCK;
   const int b0 = ch * DEC_CB;
   if (b0 >= NB) return;
   const int b1 = min(NB, b0 + DEC_CB);
   const int G = s.G;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const size_t rowstride = (size_t)s.Hkv * D;          // halves between tokens
-  const uint16_t *Kb = a.k + ((size_t)i * a.tcap * s.Hkv + g) * D;
-  const uint16_t *Vb = a.v + ((size_t)i * a.tcap * s.Hkv + g) * D;
   const float C = (float)(1.4426950408889634 / sqrt((double)D));
 
   __shared__ __align__(16) float ps[4][STEP][4];        // p per wave: [token][head]
@@ -53,7 +54,7 @@ __global__ __launch_bounds__(256) void k_dense_vram(Shape s, Step w, DenseArgs a
     for (int ks = 0; ks < KS; ++ks) {
       h8v x = (h8v){0, 0, 0, 0, 0, 0, 0, 0};
       if (r < G) {
-        const uint16_t *qp = a.q + ((size_t)i * s.Hq + g * G + r) * D + 32 * ks + 8 * (lane >> 4);
+        const uint16_t *qp = qg + (size_t)r * D + 32 * ks + 8 * (lane >> 4);
         x = *(const h8v *)qp;
       }
       qa[ks] = x;
@@ -184,6 +185,35 @@ __global__ __launch_bounds__(256) void k_dense_vram(Shape s, Step w, DenseArgs a
       part[D + 1] = L;
     }
   }
+}
+
+// Comparator: FP16 K and V resident in device memory, [n][tcap][Hkv][d].
+template <int D>
+__global__ __launch_bounds__(256) void k_dense_vram(Shape s, Step w, DenseArgs a) {
+  const int i = blockIdx.z, g = blockIdx.y;
+  dense_chunk<D>(s, w, i, g, blockIdx.x, a.T[i], a.q + ((size_t)i * s.Hq + g * s.G) * D,
+                 a.k + ((size_t)i * a.tcap * s.Hkv + g) * D,
+                 a.v + ((size_t)i * a.tcap * s.Hkv + g) * D, (size_t)s.Hkv * D);
+}
+
+// Rungs 3 and 4: the groups marked dense, from their staged FP16 K and V.
+template <int D>
+__global__ __launch_bounds__(256) void k_dense_staged(Shape s, Step w, SeqTab tab, int layer,
+                                                      const uint16_t *q16) {
+  const int i = blockIdx.z, g = blockIdx.y;
+  const size_t ig = (size_t)i * s.Hkv + g;
+  if (!w.gdense[ig]) return;
+  dense_chunk<D>(s, w, i, g, blockIdx.x, tab.T[i], q16 + ((size_t)i * s.Hq + g * s.G) * D,
+                 w.stage_k + stage_k_area(s, i, g, tab.slot[i], layer) * s.Tmax * D,
+                 w.stage_v + ig * s.Tmax * D, (size_t)D);
+}
+
+hipError_t launch_dense_staged(const Shape &s, const Step &w, const SeqTab &tab, int layer,
+                               const uint16_t *q16, int maxNB, hipStream_t st) {
+  dim3 grid((maxNB + DEC_CB - 1) / DEC_CB, s.Hkv, tab.n);
+  if (s.d == 128)
+    return launch_k(k_dense_staged<128>, grid, dim3(256), 0, st, s, w, tab, layer, q16);
+  return launch_k(k_dense_staged<64>, grid, dim3(256), 0, st, s, w, tab, layer, q16);
 }
 
 hipError_t launch_dense_vram(const Shape &s, const Step &w, const DenseArgs &a, int maxNB,
