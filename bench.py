@@ -26,7 +26,8 @@ sample), whose outputs are also compared with the GPU's for those layers (sample
 parity); the same timed steps on a context that keeps promoted FP16 keys in
 device memory across steps; and on one with a device cache of FP16 key blocks
 sized so that tier 1 plus the cache take the pages' ~56 % of the dense FP16
-cache's device memory.
+cache's device memory; and one layer with every head forced to the dense
+fallback (rungs 3/4).
 """
 import argparse
 import hashlib
@@ -64,6 +65,8 @@ def parse():
                    help="skip the run with a device cache of FP16 key blocks")
     p.add_argument("--no-comparators", action="store_true",
                    help="skip the dense FP16 (device-resident) and naive INT8/INT4 comparators")
+    p.add_argument("--no-dense-fallback", action="store_true",
+                   help="skip the one-layer run with every head forced to the dense fallback")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (counter calibration)")
     return p.parse_args()
@@ -449,6 +452,44 @@ def main():
         }
         cx3.close()
 
+    dense_fb = None
+    if not a.no_dense_fallback:
+        # rungs 3/4 on one layer of the same shape: every head forced dense,
+        # so the step copies the layer's FP16 K and V in and runs the dense
+        # kernel on them
+        if resid is None and kcache is None:
+            ctx.close()
+        cx4 = kvq.Context(1, 1, Hq, Hkv, d, max_tokens, timing=True, force_dense=True)
+        gen.manual_seed(4_000_000)
+        K = torch.randn((T0, Hkv, d), generator=gen, device=dev, dtype=torch.float32)
+        for g in range(Hkv):
+            ch = torch.from_numpy(S.outlier_channels(w, 0, g)).to(dev)
+            K[:, g, ch] *= w.outlier_scale
+        V = torch.randn((T0, Hkv, d), generator=gen, device=dev, dtype=torch.float32)
+        cx4.append(0, [0], [T0], K.half(), V.half())
+        del K, V
+        recs4 = []
+        for s in range(4):
+            st = cx4.decode_step(0, [0], qs[s][0], out, ek, ev, lv, stats=True)[4]
+            if s > 0:
+                recs4.append(st)
+        torch.cuda.synchronize()
+        med = lambda k: float(np.median([r[k] for r in recs4]))
+        kb = T0 * Hkv * 4 * d
+        dense_fb = {
+            "what": "one layer (128K tokens, 8 KV heads) with every head forced to level 4: whole-layer "
+                    "FP16 K/V over the host link, dense decode on the staged copy",
+            "levels": sorted(set(lv.cpu().numpy().ravel().tolist())),
+            "kernel": "k_dense_staged", "ms_kernel": round(med("ms_dense"), 5),
+            "algorithmic_bytes": kb, "GBps": round(kb / (med("ms_dense") * 1e-3) / 1e9, 1),
+            "hbm_frac": round(kb / (med("ms_dense") * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "ms_copy": round(med("ms_copy"), 4),
+            "h2d_GBps": round(med("h2d_bytes") / (med("ms_copy") * 1e-3) / 1e9, 2),
+            "ms_step": round(med("ms_total"), 4),
+        }
+        cx4.close()
+        log("dense fallback run done")
+
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "KV tokens/s", "n_gpus": 1,
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(wall / a.steps * 1e3, 3),
@@ -464,12 +505,12 @@ def main():
         "roofline": roofline, "cpu_baseline": cpu,
         "quantized_pass": quantized_pass, "per_kernel_ms": {k: round(v, 5) for k, v in per_kernel.items()},
         "promotion": promo, "level_counts": levels, "comparators": comps, "residency": resid,
-        "key_cache": kcache,
+        "key_cache": kcache, "dense_fallback": dense_fb,
         "parity_sample": parity,
         "tier1_vram_frac_of_fp16": round(t1b / (4 * d), 4),
     }
     print(json.dumps(line), flush=True)
-    if resid is None and kcache is None:
+    if resid is None and kcache is None and dense_fb is None:
         ctx.close()
 
 
