@@ -470,7 +470,7 @@ def main():
         del K, V
         recs4 = []
         for s in range(4):
-            st = cx4.decode_step(0, [0], qs[s][0], out, ek, ev, lv, stats=True)[4]
+            st = cx4.decode_step(0, [0], qs[s % n_total][0], out, ek, ev, lv, stats=True)[4]
             if s > 0:
                 recs4.append(st)
         torch.cuda.synchronize()
