@@ -188,11 +188,13 @@ def main():
         toks = [0]
 
         def step(s, timed):
+            # after this step's append every layer holds T0 + s + 1 tokens
+            # (checked against the library once the steps are done)
             for layer in range(L):
                 cx.append(layer, [0], [1], k1s[s][layer], v1s[s][layer])
                 cx.decode_step(layer, [0], qs[s][layer], out, ek, ev, lv, stats=False)
-                if timed:
-                    toks[0] += cx.seq_len(layer, 0)
+            if timed:
+                toks[0] += L * (T0 + s + 1)
         for s in range(a.warmup):
             step(s, False)
         torch.cuda.synchronize()
@@ -205,6 +207,7 @@ def main():
             log(f"step {s - a.warmup + 1}/{a.steps} done")
         torch.cuda.synchronize()
         wall_s = time.time() - t0
+        assert all(cx.seq_len(layer, 0) == T0 + n_total for layer in range(L))
         step_ms[:] = [evs[k].elapsed_time(evs[k + 1]) for k in range(a.steps)]
         return wall_s, toks[0]
 
