@@ -135,6 +135,8 @@ def main():
     NCPU = 4                          # layers in the oracle's sample
     host0 = {}
     dense_k, dense_v = [], []          # FP16 caches in device memory (comparator)
+    prefill_ms = []                    # bulk append of each layer (main context)
+
     def prefill(cx, keep_dense, keep_host0):
         nonlocal host0
         for layer in range(L):
@@ -145,7 +147,13 @@ def main():
                 K[:, g, ch] *= w.outlier_scale
             V = torch.randn((T0, Hkv, d), generator=gen, device=dev, dtype=torch.float32)
             K, V = K.half(), V.half()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
             cx.append(layer, [0], [T0], K, V)
+            e1.record()
+            if cx is ctx:
+                e1.synchronize()
+                prefill_ms.append(e0.elapsed_time(e1))
             if keep_dense:
                 kd = torch.zeros((1, max_tokens, Hkv, d), dtype=torch.float16, device=dev)
                 vd = torch.zeros_like(kd)
@@ -493,6 +501,18 @@ def main():
         cx4.close()
         log("dense fallback run done")
 
+    t1_bytes = t1b * T0 * Hkv
+    t2_bytes = T0 * Hkv * 4 * d
+    pm = float(np.median(prefill_ms))
+    append = {
+        "what": "quantize-on-append of a layer's 131072-token prefill (tier-1 codes, metadata and "
+                "eta written to device memory, FP16 K/V written to pinned host memory through the "
+                "device mapping), median over the 32 layers",
+        "ms_per_layer": round(pm, 3), "tier1_bytes": int(t1_bytes), "tier2_bytes": int(t2_bytes),
+        "tier2_host_GBps": round(t2_bytes / (pm * 1e-3) / 1e9, 2),
+        "tier1_GBps": round(t1_bytes / (pm * 1e-3) / 1e9, 1),
+    }
+
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "KV tokens/s", "n_gpus": 1,
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(wall / a.steps * 1e3, 3),
@@ -508,7 +528,7 @@ def main():
         "roofline": roofline, "cpu_baseline": cpu,
         "quantized_pass": quantized_pass, "per_kernel_ms": {k: round(v, 5) for k, v in per_kernel.items()},
         "promotion": promo, "level_counts": levels, "comparators": comps, "residency": resid,
-        "key_cache": kcache, "dense_fallback": dense_fb,
+        "key_cache": kcache, "dense_fallback": dense_fb, "append": append,
         "parity_sample": parity,
         "tier1_vram_frac_of_fp16": round(t1b / (4 * d), 4),
     }
