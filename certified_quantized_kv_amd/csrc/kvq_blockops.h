@@ -221,6 +221,7 @@ __device__ __forceinline__ bool sort_desc_u64(unsigned long long *keys, int n, i
   constexpr int PER = SB / NT;           // counters per thread in the scan
   constexpr int RK = (MAX_NB + NT - 1) / NT;   // keys per thread
   static_assert(SB % NT == 0, "bucket count");
+  static_assert(4 * NT >= MAX_NB, "the comparison network's chunks (4 keys per lane) cover MAX_NB keys");
   unsigned long long *tmp = keys + cap;
   int *base = reinterpret_cast<int *>(keys + 2 * (size_t)cap);   // SB + 1 entries
   int *cur = base + SB + 1;                                     // SB entries
