@@ -87,6 +87,7 @@ _SIGS = {
     "kvq_export_trace": (I32, [P, I32, I32, P, ctypes.c_size_t]),
     "kvq_selftest_exp2k": (I32, [P, P, I64, P]),
     "kvq_selftest_merge_runs": (I32, [P, I64, P, P]),
+    "kvq_selftest_sort": (I32, [P, I64, P, P, P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -150,6 +151,22 @@ def exp2k(x):
     if st != 0:
         raise KvqError(st, "exp2k")
     return y
+
+
+def sort_desc(keys):
+    """The library's workgroup sort of block keys (test hook): keys = int64 CUDA
+    tensor of n distinct nonzero keys read as unsigned, 1 <= n <= 4096.
+    Returns (the keys in descending unsigned order, int32 CUDA tensor holding 0
+    if the bucket sort placed them, 1 if the comparison network sorted them)."""
+    import torch
+    out = torch.empty_like(keys)
+    path = torch.full((1,), -1, dtype=torch.int32, device=keys.device)
+    st = _lib.kvq_selftest_sort(_dev(keys, torch.int64, "keys"), keys.numel(),
+                                _dev(out, torch.int64, "out"), _dev(path, torch.int32, "path"),
+                                _stream())
+    if st != 0:
+        raise KvqError(st, "sort_desc")
+    return out, path
 
 
 class Context:

@@ -1084,6 +1084,14 @@ kvq_status kvq_selftest_exp2k(const float *x, float *y, int64_t n, void *stream)
   return launch_exp2k(x, y, n, (hipStream_t)stream) == hipSuccess ? KVQ_OK : KVQ_EHIP;
 }
 
+kvq_status kvq_selftest_sort(const uint64_t *keys, int64_t n, uint64_t *out, int32_t *path, void *stream) {
+  if (!keys || !out || !path || n < 1 || n > MAX_NB) return KVQ_EINVAL;
+  return launch_selftest_sort((const unsigned long long *)keys, (int)n, (unsigned long long *)out, path,
+                              (hipStream_t)stream) == hipSuccess
+             ? KVQ_OK
+             : KVQ_EHIP;
+}
+
 kvq_status kvq_selftest_merge_runs(const uint64_t *in, int64_t n, uint64_t *out, int64_t *n_out) {
   if (n < 0 || (n > 0 && (!in || !out)) || !n_out) return KVQ_EINVAL;
   for (int64_t k = 0; k < n; ++k)

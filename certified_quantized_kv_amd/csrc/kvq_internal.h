@@ -192,6 +192,8 @@ hipError_t launch_combine(const Shape &s, const Step &w, const SeqTab &tab, floa
 hipError_t launch_dense_vram(const Shape &s, const Step &w, const DenseArgs &a, int maxNB,
                              hipStream_t st);
 hipError_t launch_exp2k(const float *x, float *y, int64_t n, hipStream_t st);
+hipError_t launch_selftest_sort(const unsigned long long *in, int n, unsigned long long *out, int *path,
+                                hipStream_t st);
 hipError_t launch_export_kcodes(const Shape &s, const Tier1 &t, size_t u, int T, uint8_t *dst,
                                 hipStream_t st);
 hipError_t launch_export_vcodes(const Shape &s, const Tier1 &t, size_t u, int T, uint8_t *dst,

@@ -125,4 +125,24 @@ hipError_t launch_select(const Shape &s, const Step &w, const SeqTab &tab, int t
                   w, tab, tau_ppm);
 }
 
+// The workgroup sort of the selection and controller kernels on n distinct
+// nonzero keys (cap = max(64, next power of two >= n), unused slots zero);
+// *path = 0 when the bucket sort placed the keys, 1 when the comparison
+// network sorted them.
+__global__ __launch_bounds__(SEL_NT) void k_selftest_sort(const unsigned long long *in, int n, int cap,
+                                                          unsigned long long *out, int *path) {
+  extern __shared__ unsigned long long keys[];
+  for (int p = threadIdx.x; p < cap; p += SEL_NT) keys[p] = p < n ? in[p] : 0ull;
+  const bool placed = sort_desc_u64<SEL_NT>(keys, n, cap);
+  for (int p = threadIdx.x; p < n; p += SEL_NT) out[p] = keys[p];
+  if (threadIdx.x == 0) *path = placed ? 0 : 1;
+}
+
+hipError_t launch_selftest_sort(const unsigned long long *in, int n, unsigned long long *out, int *path,
+                                hipStream_t st) {
+  const int cap = max(64, pow2_at_least(n));
+  return launch_k(k_selftest_sort, dim3(1), dim3(SEL_NT), (uint32_t)sort_lds_bytes(cap), st, in, n,
+                  cap, out, path);
+}
+
 }  // namespace kvq

@@ -272,6 +272,17 @@ kvq_status kvq_export_trace(kvq_ctx *ctx, int32_t which, int32_t seq_id, void *h
  * device floats.  For tests. */
 kvq_status kvq_selftest_exp2k(const float *x, float *y, int64_t n, void *stream);
 
+/* Sorts n distinct nonzero 64-bit keys into descending order with the
+ * workgroup sort that orders the blocks for top-K* selection (weight << 32 |
+ * ~block) and for the ranking check (Méthodologie §3): keys and out are
+ * device arrays of n entries (1 <= n <= 4096, the blocks of one sequence at
+ * most), *path (device int32) receives 0 when the bucket sort placed the keys
+ * and 1 when the comparison network (its fallback for clustered keys) sorted
+ * them.  Stream-ordered on stream; KVQ_EINVAL on a bad size or null pointer.
+ * Duplicate or zero keys are outside the contract.  For tests. */
+kvq_status kvq_selftest_sort(const uint64_t *keys, int64_t n, uint64_t *out, int32_t *path,
+                             void *stream);
+
 /* Merges promotion-plan entries the way a decode step does before copying
  * (host only, no device call).  in: n host entries, each
  * len | start << 16 | group << 32 | kind << 48 (len >= 1, start + len < 2^16,

@@ -6,6 +6,9 @@
 * the adversarial ladder workload: 16 sequences with ragged 4K-64K contexts,
   near-tied key blocks in 0/2/4/8 KV heads per sequence and hostile values in
   5 % of value groups (rungs 2, 3 and 4 all fire).
+* the largest context one sequence may hold, 262144 tokens (4096 full blocks
+  of 64), on one KV head with its four query heads: the selection and
+  controller sorts at their largest size and 256 split-K decode chunks.
 
 Every decision-side array is compared bit for bit with the oracle (scores,
 Delta', weights, orders, K*, unions, verdicts, E_key, E_val, V sets, levels)
@@ -85,3 +88,12 @@ def test_adversarial_ladder_16_sequences(env):
     assert (lv == 2).any() and (lv == 3).any() and (lv == 4).any()
     rates = [float((lv == k).mean()) for k in range(5)]
     log(f"[fullsize] ladder level rates {rates}")
+
+
+def test_max_context_262144_tokens(env):
+    w = S.Workload(6, "max-context-256k-4q1kv", 1, 4, 1, 128, [64 * 4096], 3, 10.0,
+                   max_tokens=64 * 4096)
+    gpu = _run(env, _case(w, [0], w.name))
+    tr = gpu["trace"][0]
+    assert tr["pi"].size == 4 * 4096
+    assert sorted(tr["pi"].reshape(4, -1)[0].tolist()) == list(range(4096))
