@@ -772,7 +772,9 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
       tm.open(TC_DECODE);
       HIPCK(ctx, launch_decode(s, ctx->t, w, tab, layer, maxNB, st));
       tm.open(TC_COMBINE);
-      HIPCK(ctx, launch_combine(s, w, tab, out, 0, e_key, e_val, level, st));
+      // mixed partials for every head: the result is kept only if no head
+      // reached rung 3
+      HIPCK(ctx, launch_combine(s, w, tab, out, 1, e_key, e_val, level, st));
     }
     tm.close();
     rs = read_plan_wait(ctx, plan);

@@ -280,8 +280,9 @@ hipError_t launch_decode(const Shape &s, const Tier1 &t, const Step &w, const Se
   return launch_k(k_decode_mixed<64>, grid, dim3(256), 0, st, s, t, w, tab, layer);
 }
 
-// Merges the chunk partials of each (sequence, query head): levels 3/4 read
-// the dense partials, the others the mixed ones.  One workgroup per
+// Merges the chunk partials of each (sequence, query head): mode 0 reads the
+// dense partials for heads at level 3/4 and the mixed ones for the others,
+// mode 1 the mixed ones and mode 2 the dense ones for every head.  One workgroup per
 // (query head, sequence, quarter of the channels): the chunk maxima and
 // weights first (every quarter computes them), then 256 / (d/4) groups of
 // channel-threads each sum a share of the chunks with four independent
@@ -310,33 +311,67 @@ __global__ __launch_bounds__(256) void k_combine(Shape s, Step w, SeqTab tab, fl
   const int NB = (tab.T[i] + BLOCK - 1) / BLOCK, nch = (NB + cb - 1) / cb;
   const float *part = (dense ? w.partd : w.part) + (((size_t)i * s.Hkv + g) * s.nchmax * G + h) * (D + 2);
   const size_t stride = (size_t)G * (D + 2);
+  const int parts = 256 / CQ, c = cq * CQ + threadIdx.x % CQ, pp = threadIdx.x / CQ;
+  // every load of the workgroup goes out at once: the chunk maxima and sums
+  // of this thread's chunks t + 256 j, and the first PF partial outputs of its
+  // channel (chunks pp + parts j); the rest of the partials stream later
+  constexpr int MJ = COMB_MAXCH / 256, PF = 16;
+  float mk[MJ], lk[MJ], pv[PF];
+#pragma unroll
+  for (int j = 0; j < MJ; ++j) {
+    const int k = threadIdx.x + 256 * j;
+    mk[j] = k < nch ? part[k * stride + D] : -INFINITY;
+    lk[j] = k < nch ? part[k * stride + D + 1] : 0.0f;
+  }
+#pragma unroll
+  for (int j = 0; j < PF; ++j) {
+    const int k = pp + parts * j;
+    pv[j] = k < nch ? part[k * stride + c] : 0.0f;
+  }
   float m = -INFINITY;
-  for (int k = threadIdx.x; k < nch; k += 256) m = fmaxf(m, part[k * stride + D]);
+#pragma unroll
+  for (int j = 0; j < MJ; ++j) m = fmaxf(m, mk[j]);
   m = bfly_max<64>(m);
   if ((threadIdx.x & 63) == 0) wred[threadIdx.x >> 6] = m;
   __syncthreads();
   const float M = fmaxf(fmaxf(wred[0], wred[1]), fmaxf(wred[2], wred[3]));
   __syncthreads();
   float l = 0.0f;
-  for (int k = threadIdx.x; k < nch; k += 256) {
-    const float f = exp2f(part[k * stride + D] - M);
-    fw[k] = f;
-    l = fmaf(part[k * stride + D + 1], f, l);
+#pragma unroll
+  for (int j = 0; j < MJ; ++j) {
+    const int k = threadIdx.x + 256 * j;
+    if (k < nch) {
+      const float f = exp2f(mk[j] - M);
+      fw[k] = f;
+      l = fmaf(lk[j], f, l);
+    }
   }
   l = bfly_sum<64>(l);
   if ((threadIdx.x & 63) == 0) wred[threadIdx.x >> 6] = l;
   __syncthreads();
   const float L = wred[0] + wred[1] + wred[2] + wred[3];
-  const int parts = 256 / CQ, c = cq * CQ + threadIdx.x % CQ, pp = threadIdx.x / CQ;
-  float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
-  int k = pp;
-  for (; k + 3 * parts < nch; k += 4 * parts) {
-    a0 = fmaf(part[k * stride + c], fw[k], a0);
-    a1 = fmaf(part[(k + parts) * stride + c], fw[k + parts], a1);
-    a2 = fmaf(part[(k + 2 * parts) * stride + c], fw[k + 2 * parts], a2);
-    a3 = fmaf(part[(k + 3 * parts) * stride + c], fw[k + 3 * parts], a3);
+  // accumulators: chunk j of this thread goes to a[j % 4] when its group of
+  // four chunks is complete, to a[0] otherwise (the tail), in increasing j
+  float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int j = 0; j < PF; ++j) {
+    const int k = pp + parts * j;
+    if (k < nch) {
+      const bool full = pp + parts * ((j & ~3) + 3) < nch;
+      const float f = fw[k];
+      if (full) a[j & 3] = fmaf(pv[j], f, a[j & 3]);
+      else a[0] = fmaf(pv[j], f, a[0]);
+    }
   }
-  for (; k < nch; k += parts) a0 = fmaf(part[k * stride + c], fw[k], a0);
+  int k = pp + parts * PF;
+  for (; k + 3 * parts < nch; k += 4 * parts) {
+    a[0] = fmaf(part[k * stride + c], fw[k], a[0]);
+    a[1] = fmaf(part[(k + parts) * stride + c], fw[k + parts], a[1]);
+    a[2] = fmaf(part[(k + 2 * parts) * stride + c], fw[k + 2 * parts], a[2]);
+    a[3] = fmaf(part[(k + 3 * parts) * stride + c], fw[k + 3 * parts], a[3]);
+  }
+  for (; k < nch; k += parts) a[0] = fmaf(part[k * stride + c], fw[k], a[0]);
+  const float a0 = a[0], a1 = a[1], a2 = a[2], a3 = a[3];
   red[threadIdx.x] = (a0 + a1) + (a2 + a3);
   __syncthreads();
   if (threadIdx.x < CQ) {
