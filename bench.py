@@ -364,6 +364,7 @@ def main():
         toks_cpu = 0
         lv_ok = ek_ok = ev_ok = True
         err = 0.0
+        kept = []                      # (q, groups, reference levels) of each sampled layer
         for layer in range(NCPU):
             K0, V0 = host0[layer]
             ks = np.concatenate([K0] + [k1s[s][layer].cpu().numpy().view(np.uint16)
@@ -390,13 +391,33 @@ def main():
             ek_ok &= bool(np.array_equal(ek_g.cpu().numpy()[0].view(np.uint32), ref.e_key.view(np.uint32)))
             ev_ok &= bool(np.array_equal(ev_g.cpu().numpy()[0].view(np.uint32), ref.e_val.view(np.uint32)))
             err = max(err, float(np.abs(o_gpu.cpu().numpy()[0].astype(np.float64) - ref.out).max()))
-            del ks, vs, groups
+            kept.append((q16, groups, ref.level))
+            del ks, vs
             log(f"oracle layer {layer} done")
+        # the same layer-steps again, one host thread each (the oracle's C
+        # routines release the interpreter lock while they run)
+        import threading
+        par = [None] * NCPU
+
+        def _par(j):
+            par[j] = oracle.decode_step(oracle.Config(), kept[j][0], kept[j][1])
+        ths = [threading.Thread(target=_par, args=(j,)) for j in range(NCPU)]
+        tq = time.time()
+        for x in ths:
+            x.start()
+        for x in ths:
+            x.join()
+        t_par = time.time() - tq
+        par_same = all(np.array_equal(par[j].level, kept[j][2]) for j in range(NCPU))
+        del kept, par
         cpu = {"value": round(toks_cpu / t_step, 1), "unit": "KV tokens/s", "cores": 1,
                "kind": "oracle", "host": f"{model}, {os.cpu_count()} logical CPUs visible",
                "sample": f"one certified decode step of each of layers 0-{NCPU - 1} (32 q / 8 KV heads, "
                          f"d 128, {T_last} tokens) after the timed steps; {t_step / NCPU:.2f} s per "
-                         f"layer-step, tier-1 quantization {t_tier1 / NCPU:.2f} s per layer (not in value)"}
+                         f"layer-step, tier-1 quantization {t_tier1 / NCPU:.2f} s per layer (not in value)",
+               "threads": {"value": round(toks_cpu / t_par, 1), "cores": NCPU,
+                           "how": f"the same {NCPU} layer-steps at once, one host thread each",
+                           "levels_equal_to_single_thread": par_same}}
         parity = {"layers": list(range(NCPU)), "tokens": T_last, "levels_equal": lv_ok,
                   "e_key_bits_equal": ek_ok, "e_val_bits_equal": ev_ok,
                   "max_abs_out_err": err, "tol": 2e-3}
