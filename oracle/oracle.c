@@ -248,23 +248,17 @@ void orc_query(int G, int d, const uint16_t *q, float *qp)
     for (int i = 0; i < G * d; ++i) qp[i] = orc_h2f(q[i]) * C;
 }
 
-/* Canonical reduction order for per-block dot products over channels:
- * 16 chunks of d/16 consecutive channels, each an fma chain from 0 in
- * ascending channel order, then fold-in-half over the 16 partial sums
- * (P_j += P_{j+8}, then +4, +2, +1). */
-static float chunk_fold(int d, const float *x, const float *y, int absx)
+/* Per-block dot products over channels (beta and the Delta' sum): one fma
+ * chain from 0 over the channels in ascending order,
+ *   acc <- fmaf(x_c, y_c, acc)   (x_c replaced by |x_c| when absx is set).
+ * Both sides evaluate the chain in exactly this order, so the rounded value
+ * is fixed by the definition alone. */
+static float chain_dot(int d, const float *x, const float *y, int absx)
 {
-    float P[16];
-    int w = d / 16;
-    for (int j = 0; j < 16; ++j) {
-        float acc = 0.0f;
-        for (int c = j * w; c < (j + 1) * w; ++c)
-            acc = fmaf(absx ? fabsf(x[c]) : x[c], y[c], acc);
-        P[j] = acc;
-    }
-    for (int h = 8; h >= 1; h >>= 1)
-        for (int j = 0; j < h; ++j) P[j] = P[j] + P[j + h];
-    return P[0];
+    float acc = 0.0f;
+    for (int c = 0; c < d; ++c)
+        acc = fmaf(absx ? fabsf(x[c]) : x[c], y[c], acc);
+    return acc;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -276,13 +270,13 @@ static float chunk_fold(int d, const float *x, const float *y, int absx)
 /*   a_c = fl32(q'_c s_c);  e = ilogb(max|a_c|) - 21  (0 if all a_c = 0)      */
 /*   A_c = rint(a_c 2^-e)   (|A_c| <= 2^22, an exact integer)                 */
 /*   D_t = sum_c A_c (code_tc - 128)        exact integer, any order          */
-/*   beta = chunk_fold(q', fl32(off + 128 s))                                 */
+/*   beta = chain_dot(q', fl32(off + 128 s))   (c ascending, from 0)          */
 /*   shat_t = fmaf(fl32(D_t), 2^e, beta)                                      */
 /* Delta'_b (log2 units) bounds |shat_t - s'_t| for every valid t, s' being  */
 /* the canonical FP16-key score below:                                       */
 /*   K'_c = max(|off_c|, |fmaf(256, s_c, off_c)|)                             */
 /*   t_c  = fmaf(d 2^-22, K'_c, s_c / 2)                                      */
-/*   Delta' = fl32(fl32(chunk_fold(|q'|, t) + R) * (1 + 2^-15)),              */
+/*   Delta' = fl32(fl32(chain_dot(|q'|, t) + R) * (1 + 2^-15)),               */
 /*   R = 64 d 2^e (0 if all a_c = 0)                                          */
 /* s_c/2 is the quantization half-step (Hölder with |q'|), the d 2^-22 K'    */
 /* term covers fp32 evaluation error of both score chains, R covers the     */
@@ -311,7 +305,7 @@ void orc_int8_block(int G, int d, int n, const float *qp, const uint8_t *code,
         int zero = (amax == 0.0f);
         int e = zero ? 0 : ilogbf(amax) - 21;
         for (int c = 0; c < d; ++c) A[c] = (int64_t)rintf(ldexpf(a[c], -e));
-        float beta = chunk_fold(d, q, u, 0);
+        float beta = chain_dot(d, q, u, 0);
         float sc = ldexpf(1.0f, e);
         for (int t = 0; t < n; ++t) {
             int64_t D = 0;
@@ -319,7 +313,7 @@ void orc_int8_block(int G, int d, int n, const float *qp, const uint8_t *code,
                 D += A[c] * ((int64_t)code[(int64_t)t * d + c] - 128);
             shat[(int64_t)h * ld_shat + t] = fmaf((float)D, sc, beta);
         }
-        float P = chunk_fold(d, q, tt, 1);
+        float P = chain_dot(d, q, tt, 1);
         float R = zero ? 0.0f : ldexpf(64.0f * (float)d, e);
         delta[h] = (P + R) * (1.0f + 0x1p-15f);
     }

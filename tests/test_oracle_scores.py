@@ -182,3 +182,70 @@ def test_spearman_integer_verdict_matches_library(orc):
         if abs(rho - rho_ppm / 1e6) > 1e-12:
             assert ok == (rho >= rho_ppm / 1e6)
     assert orc.ranking_consistent([5], np.ones(6, np.int64), 999_999)[0]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_channel_sums_are_ascending_fma_chains(orc, d):
+    """beta and the Delta' sum are fma chains over the channels in ascending
+    order from 0 (Méthodologie §2/§3 readings; the order fixes the rounding).
+    Closed form by absorption: keys constant per channel (scale 0, offset =
+    the value), channel 0 holds 1024, every other channel 2^-15, q = 1, so
+    q' = C = fl32(log2(e)/sqrt(d)).  In the ascending chain the first term
+    C*1024 is exact and every later term C*2^-15 is below half an ulp of it,
+    so beta = C*1024 exactly; any order that adds the small terms first (a
+    tree, a reversed chain, the exact sum) lands at least one ulp higher.
+    The same holds for Delta': t_0 = d 2^-22 1024, t_c = d 2^-22 2^-15, so
+    the chain is C*t_0 and Delta' = fl32(C t_0 (1 + 2^-15))."""
+    from fractions import Fraction as Fr
+    T = 64
+    k = np.full((T, d), 2.0 ** -15, np.float32)
+    k[:, 0] = 1024.0
+    k16 = k.astype(np.float16).view(np.uint16)
+    assert np.array_equal(k16.view(np.float16).astype(np.float32), k)
+    v16 = np.zeros((T, d), np.float16).view(np.uint16)
+    q16 = np.ones((1, d), np.float16).view(np.uint16)
+    t1 = orc.build_tier1(k16, v16)
+    assert not t1["kscale"].any()
+    qp = orc.query(q16)
+    C = np.float32(orc.lib().orc_query_scale(d))
+    assert np.all(qp == C)
+    shat, delta = orc.int8_scores(qp, t1)
+
+    def half_ulp(x):
+        return Fr(2) ** (int(np.floor(np.log2(float(x)))) - 24)
+    big, small = Fr(float(C)) * 1024, Fr(float(C)) * Fr(2) ** -15
+    assert small < half_ulp(big)                       # each later term absorbed
+    assert (d - 1) * small > 2 * half_ulp(big)         # but not their sum
+    beta = np.float32(C) * np.float32(1024.0)           # exact: a power-of-two scaling
+    assert np.all(shat.view(np.uint32) == beta.view(np.uint32))
+    exact = np.float32(float(big + (d - 1) * small))
+    assert exact != beta                               # the case tells the orders apart
+
+    t0, ts = Fr(d) * Fr(2) ** -22 * 1024, Fr(d) * Fr(2) ** -22 * Fr(2) ** -15
+    p_big, p_small = Fr(float(C)) * t0, Fr(float(C)) * ts
+    assert p_small < half_ulp(p_big) and (d - 1) * p_small > 2 * half_ulp(p_big)
+    P = np.float32(float(p_big))
+    assert Fr(float(P)) == p_big                        # C t_0 is exact
+    want = np.float32(P * np.float32(1.0 + 2.0 ** -15))
+    assert delta.view(np.uint32)[0, 0] == want.view(np.uint32)
+
+
+def test_f32_up_is_smallest_float_at_or_above(orc):
+    """The fp64 -> binary32 rounding of every reported bound goes up: the
+    result is >= x and its binary32 predecessor is < x (so it is the least
+    such float), on random values, exact floats, ties and edge cases."""
+    from fractions import Fraction as Fr
+    r = np.random.default_rng(11)
+    xs = list(r.random(2000)) + list(10.0 ** r.uniform(-45, 38, 2000))
+    fl = r.random(500).astype(np.float32)
+    xs += [float(f) for f in fl]                                   # exactly representable
+    xs += [float(f) + float(np.spacing(f)) / 2 for f in fl]        # exact ties
+    xs += [float(f) + float(np.spacing(f)) * 1e-6 for f in fl]     # just above a float
+    xs += [0.0, 2.0 ** -149, 2.0 ** -150, 3 * 2.0 ** -150, 2.0 ** -126, 1.0, 1.0 - 2.0 ** -60,
+           1.0 + 2.0 ** -60, float(np.finfo(np.float32).max)]
+    for x in xs:
+        f = orc.f32_up(x)
+        assert isinstance(f, np.float32)
+        assert Fr(float(f)) >= Fr(x), x
+        prev = np.nextafter(f, np.float32(-np.inf))
+        assert Fr(float(prev)) < Fr(x) or (x == 0.0 and f == 0.0), x
