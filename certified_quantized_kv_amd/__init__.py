@@ -123,6 +123,19 @@ def _dev(t, dtype, name):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _out(t, shape, dtype, device, name):
+    """A caller-supplied output: the library writes shape-many elements of
+    dtype on device through its pointer, so all three must match exactly."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} shape {tuple(t.shape)} != {tuple(shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the call runs on {device}")
+    return _dev(t, dtype, name)
+
+
 def _i32(seq):
     arr = (I32 * len(seq))(*[int(x) for x in seq])
     return arr
@@ -235,6 +248,8 @@ class Context:
         if k.shape != v.shape or k.dim() != 3 or k.shape[0] != sum(n_new) or \
                 k.shape[1] != self.Hkv or k.shape[2] != self.d:
             raise ValueError(f"k/v shape {tuple(k.shape)} does not match the call")
+        if k.device != v.device:
+            raise ValueError("k and v must be on one device")
         self._check(_lib.kvq_append(self._ctx, layer, n, _i32(seq_ids), _i32(n_new), kp, vp,
                                     _stream()), "kvq_append")
 
@@ -253,8 +268,10 @@ class Context:
         level = torch.empty((n, self.Hq), dtype=torch.int8, device=dev) if level is None else level
         ss = StepStats() if stats else None
         st = _lib.kvq_decode_step(self._ctx, layer, n, _i32(seq_ids), _dev(q, torch.float16, "q"),
-                                  _dev(out, torch.float32, "out"), _dev(e_key, torch.float32, "e_key"),
-                                  _dev(e_val, torch.float32, "e_val"), _dev(level, torch.int8, "level"),
+                                  _out(out, (n, self.Hq, self.d), torch.float32, dev, "out"),
+                                  _out(e_key, (n, self.Hq), torch.float32, dev, "e_key"),
+                                  _out(e_val, (n, self.Hq), torch.float32, dev, "e_val"),
+                                  _out(level, (n, self.Hq), torch.int8, dev, "level"),
                                   ctypes.byref(ss) if ss is not None else None, _stream())
         self._check(st, "kvq_decode_step")
         return out, e_key, e_val, level, (ss.as_dict() if ss is not None else None)
@@ -269,7 +286,8 @@ class Context:
             if out is None else out
         self._check(_lib.kvq_decode_naive(self._ctx, layer, n, _i32(seq_ids),
                                           _dev(q, torch.float16, "q"),
-                                          _dev(out, torch.float32, "out"), _stream()),
+                                          _out(out, (n, self.Hq, self.d), torch.float32, q.device,
+                                               "out"), _stream()),
                     "kvq_decode_naive")
         return out
 
@@ -285,10 +303,13 @@ class Context:
             raise ValueError(f"k/v shape must be {want}")
         out = torch.empty((n, self.Hq, self.d), dtype=torch.float32, device=q.device) \
             if out is None else out
+        if k.device != q.device or v.device != q.device:
+            raise ValueError("q, k and v must be on one device")
         self._check(_lib.kvq_dense_decode(self._ctx, n, _i32(seq_lens),
                                           _dev(q, torch.float16, "q"), _dev(k, torch.float16, "k"),
                                           _dev(v, torch.float16, "v"),
-                                          _dev(out, torch.float32, "out"), _stream()),
+                                          _out(out, (n, self.Hq, self.d), torch.float32, q.device,
+                                               "out"), _stream()),
                     "kvq_dense_decode")
         return out
 

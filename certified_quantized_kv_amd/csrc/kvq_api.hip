@@ -112,9 +112,10 @@ struct kvq_ctx {
   Step w;
   uint16_t *t2k_host = nullptr, *t2v_host = nullptr;
   std::vector<int64_t> T;     // [slot][layer]
+  std::vector<uint8_t> opar;  // [slot][layer] half of openk holding the open block
   std::vector<void *> dallocs;
   hipStream_t cstream = nullptr;
-  hipEvent_t ev_start = nullptr, ev_copy = nullptr, ev_plan = nullptr;
+  hipEvent_t ev_start = nullptr, ev_copy = nullptr, ev_plan = nullptr, ev_spec = nullptr;
   hipEvent_t ev_k[128] = {};   // kernel timing pairs
   hipEvent_t ev_c[32] = {};    // copy timing pairs
   hipEvent_t ev_tot[2] = {};
@@ -166,6 +167,7 @@ void free_all(kvq_ctx *c) {
   if (c->ev_start) (void)hipEventDestroy(c->ev_start);
   if (c->ev_copy) (void)hipEventDestroy(c->ev_copy);
   if (c->ev_plan) (void)hipEventDestroy(c->ev_plan);
+  if (c->ev_spec) (void)hipEventDestroy(c->ev_spec);
   for (auto &e : c->ev_k)
     if (e) (void)hipEventDestroy(e);
   for (auto &e : c->ev_c)
@@ -338,6 +340,7 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out) {
   x->th.force_dense = (c.flags & KVQ_FLAG_FORCE_DENSE) ? 1 : 0;
   x->th.fp16_values = (c.flags & KVQ_FLAG_FP16_VALUES) ? 1 : 0;
   x->T.assign((size_t)c.max_batch * c.n_layers, 0);
+  x->opar.assign((size_t)c.max_batch * c.n_layers, 0);
 
   const size_t NU = (size_t)c.max_batch * c.n_layers * c.n_kv_heads;
   const size_t d = s.d, NBm = s.NBmax, Tm = s.Tmax;
@@ -355,7 +358,7 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out) {
   DA(t.eta, NU * NBm * 4);
   DA(t.vmin, NU * d * 4);
   DA(t.vmax, NU * d * 4);
-  DA(t.openk, NU * BLOCK * d * 2);
+  DA(t.openk, NU * 2 * BLOCK * d * 2);
   DA(w.qp, B * Hq * d * 4);
   DA(w.shat, B * Hq * Tm * 4);
   DA(w.sp, B * Hq * Tm * 4);
@@ -434,6 +437,7 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out) {
   if (e == hipSuccess) e = hipEventCreateWithFlags(&x->ev_start, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&x->ev_copy, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&x->ev_plan, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&x->ev_spec, hipEventDisableTiming);
   for (auto &ev : x->ev_k)
     if (e == hipSuccess) e = hipEventCreate(&ev);
   for (auto &ev : x->ev_c)
@@ -472,6 +476,9 @@ int64_t kvq_seq_len(const kvq_ctx *ctx, int32_t layer, int32_t seq) {
 kvq_status kvq_reset_seq(kvq_ctx *ctx, int32_t seq) {
   if (!ctx || seq < 0 || seq >= ctx->cfg.max_batch) return KVQ_EINVAL;
   const Shape &s = ctx->s;
+  // appends to this slot may still run on any stream: their value-range
+  // atomics must land before the ranges are cleared
+  HIPCK(ctx, hipDeviceSynchronize());
   for (int l = 0; l < s.L; ++l) {
     if (ctx->kc.slots) {
       const int64_t nb = (ctx->T[(size_t)seq * s.L + l] + BLOCK - 1) / BLOCK;
@@ -479,6 +486,7 @@ kvq_status kvq_reset_seq(kvq_ctx *ctx, int32_t seq) {
         for (int64_t b = 0; b < nb; ++b) ctx->kc.drop((int64_t)unit_of(s, seq, l, g) * s.NBmax + b);
     }
     ctx->T[(size_t)seq * s.L + l] = 0;
+    ctx->opar[(size_t)seq * s.L + l] = 0;
     const size_t u0 = unit_of(s, seq, l, 0);
     HIPCK(ctx, hipMemsetD32(reinterpret_cast<hipDeviceptr_t>(ctx->t.vmin + u0 * s.d), 0xff800000u,
                             (size_t)s.Hkv * s.d));
@@ -509,6 +517,7 @@ kvq_status kvq_append(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t *seq
     a.T_old[i] = (int)Told;
     a.n_new[i] = n_new[i];
     a.in_off[i] = (int)off;
+    a.par[i] = ctx->opar[(size_t)seq_ids[i] * s.L + layer];
     a.n_blk[i] = n_new[i] > 0 ? (int)((Told + n_new[i] - 1) / BLOCK - Told / BLOCK + 1) : 0;
     max_blk = std::max(max_blk, a.n_blk[i]);
     off += n_new[i];
@@ -527,6 +536,7 @@ kvq_status kvq_append(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t *seq
           ctx->kc.drop((int64_t)unit_of(s, seq_ids[i], layer, g) * s.NBmax + b);
     }
     ctx->T[(size_t)seq_ids[i] * s.L + layer] += n_new[i];
+    if (n_new[i] > 0) ctx->opar[(size_t)seq_ids[i] * s.L + layer] ^= 1;
   }
   return KVQ_OK;
 }
@@ -719,6 +729,7 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
   ++ctx->kc.now;
   int syncs = 0, rounds = 0;
   bool decoded = false;   // the decode launched behind the last round stands
+  bool spec = false;      // a speculative decode was enqueued (ev_spec recorded)
   Timer tm{ctx, timing};
   if (timing) HIPCK(ctx, hipEventRecord(ctx->ev_tot[0], st));
 
@@ -747,6 +758,7 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
   for (int round = 0;; ++round) {
     const bool new_keys = plan.nk > 0;
     if (!plan.ent.empty()) {
+      if (spec) HIPCK(ctx, hipStreamWaitEvent(ctx->cstream, ctx->ev_spec, 0));
       HIPCK(ctx, tm.copy_begin(TC_COPY, ctx->cstream));
       rs = issue_copies(ctx, tab, layer, plan, h2d, kblk, vblk, kcached);
       if (rs != KVQ_OK) return rs;
@@ -767,7 +779,10 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
     // the decode and combine go in behind the plan's copy: in the common case
     // (no group widens, no values to copy, no head at rung 3) they are the
     // step's last kernels and run while the host reads the plan; otherwise
-    // they are launched again below and overwrite these results
+    // they are launched again below and overwrite these results.  They read
+    // the value staging of blocks this round may have flagged for rung 2,
+    // whose copies are issued only after the plan is read: every later copy
+    // waits for them (ev_spec), so no copy writes a buffer they still read.
     if (!ctx->th.force_dense) {
       tm.open(TC_DECODE);
       HIPCK(ctx, launch_decode(s, ctx->t, w, tab, layer, maxNB, st));
@@ -775,6 +790,8 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
       // mixed partials for every head: the result is kept only if no head
       // reached rung 3
       HIPCK(ctx, launch_combine(s, w, tab, out, 1, e_key, e_val, level, st));
+      HIPCK(ctx, hipEventRecord(ctx->ev_spec, st));
+      spec = true;
     }
     tm.close();
     rs = read_plan_wait(ctx, plan);
@@ -802,6 +819,7 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
       HIPCK(ctx, hipStreamSynchronize(st));
       ++syncs;
       bool any = false;
+      if (spec) HIPCK(ctx, hipStreamWaitEvent(ctx->cstream, ctx->ev_spec, 0));
       for (int i = 0; i < n; ++i)
         for (int g = 0; g < s.Hkv; ++g) {
           if (!gd[(size_t)i * s.Hkv + g]) continue;

@@ -20,6 +20,14 @@
 // quantizes values.  New FP16 rows go straight to tier 2 (pinned host memory
 // mapped into the device address space), and with resident keys the FP16 keys
 // also to their device copy.
+//
+// The device copy of the open block has two halves.  An append that starts
+// inside a partial block reads that block's old rows from half par (the
+// workgroup of the first touched block), and the workgroup of the last
+// touched block, if it stays partial, writes all of its valid rows to half
+// par ^ 1; the host flips par after every append that adds tokens.  When an
+// append spans several blocks the two workgroups are different and run in no
+// fixed order, so they never touch the same half.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -51,7 +59,7 @@ __global__ __launch_bounds__(256) void k_append(Shape s, Tier1 t, AppendArgs a,
     uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
     if (r < n) {
       if (r < r_new) {
-        kv = *(const uint4 *)(t.openk + (u * BLOCK + r) * D + c8);
+        kv = *(const uint4 *)(t.openk + ((u * 2 + a.par[i]) * BLOCK + r) * D + c8);
       } else {
         const size_t src = (size_t)(a.in_off[i] + t0 + r - Told) * in_row + (size_t)g * D + c8;
         kv = *(const uint4 *)(kin + src);
@@ -169,7 +177,13 @@ __global__ __launch_bounds__(256) void k_append(Shape s, Tier1 t, AppendArgs a,
     *(uint4 *)(t.t2k + row * D + c8) = *(const uint4 *)&kb[r][c8];
     *(uint4 *)(t.t2v + row * D + c8) = *(const uint4 *)&vb[r][c8];
     if (t.kres) *(uint4 *)(t.kres + row * D + c8) = *(const uint4 *)&kb[r][c8];
-    if (n < BLOCK) *(uint4 *)(t.openk + (u * BLOCK + r) * D + c8) = *(const uint4 *)&kb[r][c8];
+  }
+  if (n < BLOCK) {                     // the last touched block stays open
+    uint16_t *dst = t.openk + (u * 2 + (a.par[i] ^ 1)) * BLOCK * D;
+    for (int idx = tid; idx < n * (D / 8); idx += 256) {
+      const int r = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
+      *(uint4 *)(dst + r * D + c8) = *(const uint4 *)&kb[r][c8];
+    }
   }
   if (tid == 0) {
     const float me = __uint_as_float(s_err);

@@ -35,7 +35,9 @@ static_assert(MIX_CB >= DEC_CB, "chunk partials are sized for DEC_CB");
 //   vmeta  [Tmax][d/32]  u32  binary16 scale (low), offset (high) per group
 //   eta    [NBmax]       f32  per-block value error annotation
 //   vmin/vmax [d]        u32  order-mapped floats, running over all tokens
-//   openk  [64][d]       u16  FP16 keys of the open (partial) block
+//   openk  [2][64][d]    u16  FP16 keys of the open (partial) block, two
+//                             halves: an append reads the half its parity
+//                             names and writes the other (see k_append)
 //   kres   [Tmax][d]     u16  with resident keys: every FP16 key (written on
 //                             append; the FP16 key staging of the unit)
 // Tier 2, per unit (pinned host, device-mapped): t2k/t2v [Tmax][d] fp16.
@@ -168,6 +170,7 @@ inline hipError_t launch_k(void (*k)(P...), dim3 grid, dim3 block, uint32_t shme
 struct AppendArgs {
   int n, layer;
   int slot[MAX_CALL], T_old[MAX_CALL], n_new[MAX_CALL], in_off[MAX_CALL], n_blk[MAX_CALL];
+  int par[MAX_CALL];                // half of openk holding the open block's keys
 };
 hipError_t launch_append(const Shape &s, const Tier1 &t, const AppendArgs &a, const uint16_t *k,
                          const uint16_t *v, int max_blk, hipStream_t st);

@@ -17,9 +17,11 @@
 // A = L2 2^16 + L1 2^8 + L0 with L0, L1 in [-128, 127]; each limb's dot
 // product is exact in int32, and D_t is recombined in int64.
 //
-// Fixed order of per-block channel sums (beta and Delta'): lane (h, j) of a
-// wave owns channels [j d/16, (j+1) d/16) of head h, runs an fma chain over
-// them from 0, then the 16 lanes of the head fold in half (xor 8, 4, 2, 1).
+// Per-block channel sums (beta and the Delta' sum): one fma chain from 0
+// over the channels in ascending order, acc <- fmaf(x_c, y_c, acc).  A chain
+// is sequential, so the wave runs its chains in batches: lane 4 h + k takes
+// query head h of the batch's unit k (four units of the wave's own list),
+// with the units' (off + 128 s, t_c) pairs staged in LDS.
 //
 // Delta'_b (bound on |shat_t - s'_t|, s' the FP16-key score below):
 //   K'_c = max(|off_c|, |fmaf(256, s_c, off_c)|)
@@ -47,22 +49,28 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 // moment the grid streams one contiguous window of W blocks (measured
 // faster than a window of W / Hkv blocks in each KV head).  A wave's
 // successive units may belong to different KV heads, so each unit's query
-// slice is fetched with its codes and metadata.  The kernel also carries
+// slice is fetched with its codes; the metadata of four consecutive units of
+// the wave's list (a batch) is fetched together, one batch ahead, for the
+// channel-sum chains, and kept in LDS for the units' prologues.  The kernel also carries
 // the step set-up (q' for the later kernels, flags cleared); its own waves
 // form q' from q directly.  Codes and metadata are read once per step, and
 // the scores are read once later: both go through non-temporal loads and
 // stores, which leave the caches to the data that is reused.
 template <int D>
-__global__ __launch_bounds__(256) void k_score_int8(Shape s, Tier1 t, Step w, SeqTab tab, int layer,
+__global__ __launch_bounds__(256, 4) void k_score_int8(Shape s, Tier1 t, Step w, SeqTab tab, int layer,
                                                     const uint16_t *__restrict__ q16, float C) {
   constexpr int CW = D / 16;            // channels per lane-chunk
   constexpr int NKS = D / 64;           // MFMA k-steps per block
   constexpr int AST = D + 16;           // LDS row stride of the A operand (bank spread)
+  constexpr int NBT = 4;                // units per batch of channel-sum chains
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int h = lane >> 4, jc = lane & 15;
   const bool hv = h < s.G;
 
   __shared__ __align__(16) int8_t As[4][16][AST];
+  __shared__ __align__(16) uint32_t Ms[4][NBT][D];   // the batch's key metadata
+  __shared__ __align__(16) float UTs[4][NBT][2 * D]; // (off + 128 s, t_c) per channel
+  __shared__ float2 Bs[4][NBT][4];                   // (beta, Delta' sum) per (unit, head)
 
   const int U = s.Hkv * tab.nbc[tab.n];
   const int W = gridDim.x * 4;
@@ -78,11 +86,12 @@ __global__ __launch_bounds__(256) void k_score_int8(Shape s, Tier1 t, Step w, Se
   int i, g, b;
   locate(u0, i, g, b);
 
-  // software pipeline: the next unit's query slice, metadata and codes are
-  // in flight while the current one's scores and block ingredients are formed
+  // software pipeline: the next unit's query slice and codes are in flight
+  // while the current one's scores and block ingredients are formed; the next
+  // batch's metadata while the current batch's units are processed
   v4i Bn[NKS][4];
-  uint32_t kmn[CW];
   uint32_t qn[CW / 2];
+  uint32_t kb[CW];                      // lane (k, jc): unit k of a batch, channels jc CW ..
   auto fetch = [&](int ii, int gg, int bb) {
     const int hq = gg * s.G + (hv ? h : 0);
     const uint32_t *qsrc = (const uint32_t *)(q16 + ((size_t)ii * s.Hq + hq) * D + jc * CW);
@@ -90,9 +99,6 @@ __global__ __launch_bounds__(256) void k_score_int8(Shape s, Tier1 t, Step w, Se
     for (int c = 0; c < CW / 2; ++c) qn[c] = qsrc[c];
     const size_t uu = unit_of(s, tab.slot[ii], layer, gg);
     const uint8_t *kc = t.kcodes + (uu * s.NBmax + bb) * (size_t)(BLOCK * D);
-    const uint32_t *km = t.kmeta + (uu * s.NBmax + bb) * D + jc * CW;
-#pragma unroll
-    for (int c = 0; c < CW; ++c) kmn[c] = __builtin_nontemporal_load(&km[c]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
@@ -101,121 +107,189 @@ __global__ __launch_bounds__(256) void k_score_int8(Shape s, Tier1 t, Step w, Se
         Bn[ks][nt] = __builtin_nontemporal_load(
             (const v4i *)(kc + ((size_t)((ks * 4 + nt) * 64 + lane)) * 16));
   };
-  if (u0 < U) fetch(i, g, b);
+  auto fetch_meta = [&](int ub) {
+    const int uk = ub + h * W;          // row h of the wave loads unit h of the batch
+    if (uk < U) {
+      int ii, gg, bb;
+      locate(uk, ii, gg, bb);
+      const size_t uu = unit_of(s, tab.slot[ii], layer, gg);
+      const uint32_t *km = t.kmeta + (uu * s.NBmax + bb) * D + jc * CW;
+#pragma unroll
+      for (int c = 0; c < CW; ++c) kb[c] = __builtin_nontemporal_load(&km[c]);
+    } else {
+#pragma unroll
+      for (int c = 0; c < CW; ++c) kb[c] = 0u;
+    }
+  };
+  if (u0 < U) {
+    fetch_meta(u0);
+    fetch(i, g, b);
+  }
   // the set-up's stores go out while the first unit's loads are in flight
   step_setup(s, w, tab.n, q16, C, blockIdx.x * (size_t)blockDim.x + threadIdx.x,
              (size_t)gridDim.x * blockDim.x);
   if (u0 >= U) return;
-  for (int u = u0; u < U; u += W) {
-    const int T = tab.T[i];
-    const int n = min(BLOCK, T - b * BLOCK);
-    const int hq = g * s.G + (hv ? h : 0);
-    // successor unit (its codes and metadata are fetched once this unit's
-    // contraction has consumed the registers)
-    int i2 = i, g2 = g, b2 = b;
-    if (u + W < U) locate(u + W, i2, g2, b2);
-
-    // ---- prologue: exponent, limbs of A, beta and Delta' per head -----------
-    float qv[CW];
-#pragma unroll
-    for (int c = 0; c < CW; ++c) qv[c] = h2f((uint16_t)(qn[c / 2] >> (16 * (c % 2)))) * C;
-    float sv[CW], ov[CW], a[CW];
-    float am = 0.0f;
-#pragma unroll
-    for (int c = 0; c < CW; ++c) {
-      const uint32_t m = kmn[c];
-      sv[c] = h2f((uint16_t)(m & 0xffffu));
-      ov[c] = h2f((uint16_t)(m >> 16));
-      a[c] = qv[c] * sv[c];
-      am = fmaxf(am, fabsf(a[c]));
-    }
-    am = bfly_max<16>(am);
-    const bool zero = !(am > 0.0f);
-    const int e = zero ? 0 : ilogb_f(am) - 21;
-    uint32_t l0w[CW / 4], l1w[CW / 4], l2w[CW / 4];
-#pragma unroll
-    for (int c = 0; c < CW / 4; ++c) l0w[c] = l1w[c] = l2w[c] = 0u;
-    float pb = 0.0f, pd = 0.0f;
-#pragma unroll
-    for (int c = 0; c < CW; ++c) {
-      const int A = (int)rintf(ldexpf(a[c], -e));
-      const int L0 = ((A + 128) & 255) - 128;
-      const int A1 = (A - L0) >> 8;
-      const int L1 = ((A1 + 128) & 255) - 128;
-      const int L2 = (A1 - L1) >> 8;
-      l0w[c / 4] |= ((uint32_t)L0 & 255u) << (8 * (c % 4));
-      l1w[c / 4] |= ((uint32_t)L1 & 255u) << (8 * (c % 4));
-      l2w[c / 4] |= ((uint32_t)L2 & 255u) << (8 * (c % 4));
-      const float uu = fmaf(128.0f, sv[c], ov[c]);
-      pb = fmaf(qv[c], uu, pb);
-      const float kp = fmaxf(fabsf(ov[c]), fabsf(fmaf(256.0f, sv[c], ov[c])));
-      const float tt = fmaf((float)D * 0x1p-22f, kp, 0.5f * sv[c]);
-      pd = fmaf(fabsf(qv[c]), tt, pd);
-    }
-    pb = bfly_sum<16>(pb);
-    pd = bfly_sum<16>(pd);
+  for (int ub = u0; ub < U; ub += NBT * W) {
+    const int nbt = min(NBT, (U - ub + W - 1) / W);
+    // ---- channel terms of the batch's units (lane (k, jc)), then the chains --
     {
-      int8_t *row = &As[wave][h * 4][jc * CW];
+      uint32_t *mrow = &Ms[wave][h][jc * CW];
+      float *urow = &UTs[wave][h][2 * jc * CW];
 #pragma unroll
-      for (int c = 0; c < CW / 4; ++c) {
-        const uint32_t z = 0u;
-        ((uint32_t *)(row + 0 * AST))[c] = hv ? l0w[c] : z;
-        ((uint32_t *)(row + 1 * AST))[c] = hv ? l1w[c] : z;
-        ((uint32_t *)(row + 2 * AST))[c] = hv ? l2w[c] : z;
-        ((uint32_t *)(row + 3 * AST))[c] = z;
+      for (int c = 0; c < CW; c += 4)
+        *(uint4 *)&mrow[c] = make_uint4(kb[c], kb[c + 1], kb[c + 2], kb[c + 3]);
+#pragma unroll
+      for (int c = 0; c < CW; c += 2) {
+        float4 ut;
+        float *e = (float *)&ut;
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const uint32_t m = kb[c + x];
+          const float sv = h2f((uint16_t)(m & 0xffffu)), ov = h2f((uint16_t)(m >> 16));
+          const float kp = fmaxf(fabsf(ov), fabsf(fmaf(256.0f, sv, ov)));
+          e[2 * x] = fmaf(128.0f, sv, ov);
+          e[2 * x + 1] = fmaf((float)D * 0x1p-22f, kp, 0.5f * sv);
+        }
+        *(float4 *)&urow[2 * c] = ut;
       }
+      if (ub + NBT * W < U) fetch_meta(ub + NBT * W);
+      wave_lds_sync();
+      if (lane < 4 * NBT) {
+        const int kk = lane & (NBT - 1), hh = lane / NBT;
+        int ik, gk, bk;
+        locate(ub + kk * W < U ? ub + kk * W : ub, ik, gk, bk);
+        const uint16_t *qrow = q16 + ((size_t)ik * s.Hq + gk * s.G + min(hh, s.G - 1)) * D;
+        const float *ut = &UTs[wave][kk][0];
+        float beta = 0.0f, sd = 0.0f;
+#pragma unroll 2
+        for (int c8 = 0; c8 < D; c8 += 8) {
+          const uint4 qq = *(const uint4 *)(qrow + c8);
+          const uint32_t qw[4] = {qq.x, qq.y, qq.z, qq.w};
+          float4 p[4];
+#pragma unroll
+          for (int x = 0; x < 4; ++x) p[x] = *(const float4 *)&ut[2 * c8 + 4 * x];
+#pragma unroll
+          for (int x = 0; x < 8; ++x) {
+            const float qf = h2f((uint16_t)(qw[x / 2] >> (16 * (x % 2)))) * C;
+            const float uc = (x % 2) ? p[x / 2].z : p[x / 2].x;
+            const float tc = (x % 2) ? p[x / 2].w : p[x / 2].y;
+            beta = fmaf(qf, uc, beta);
+            sd = fmaf(fabsf(qf), tc, sd);
+          }
+        }
+        Bs[wave][kk][hh] = make_float2(beta, sd);
+      }
+      wave_lds_sync();
     }
-    // Delta' is stored with the block ingredients, after the contraction
-    const float dv = (pd + (zero ? 0.0f : ldexpf(64.0f * (float)D, e))) * (1.0f + 0x1p-15f);
-    wave_lds_sync();
+    for (int k = 0; k < nbt; ++k) {
+      const int u = ub + k * W;
+      const int T = tab.T[i];
+      const int n = min(BLOCK, T - b * BLOCK);
+      const int hq = g * s.G + (hv ? h : 0);
+      // successor unit (its codes and query slice are fetched once this
+      // unit's contraction has consumed the registers)
+      int i2 = i, g2 = g, b2 = b;
+      if (u + W < U) locate(u + W, i2, g2, b2);
 
-    // ---- exact integer core on the matrix cores -------------------------------
-    v4i acc[4];
+      // ---- prologue: exponent and limbs of A per head ---------------------------
+      float qv[CW];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) acc[nt] = (v4i){0, 0, 0, 0};
+      for (int c = 0; c < CW; ++c) qv[c] = h2f((uint16_t)(qn[c / 2] >> (16 * (c % 2)))) * C;
+      uint32_t kmn[CW];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const v4i Aop = *(const v4i *)&As[wave][lane & 15][ks * 64 + 16 * (lane >> 4)];
+      for (int c = 0; c < CW; c += 4) {
+        const uint4 m4 = *(const uint4 *)&Ms[wave][k][jc * CW + c];
+        kmn[c] = m4.x, kmn[c + 1] = m4.y, kmn[c + 2] = m4.z, kmn[c + 3] = m4.w;
+      }
+      const float2 bd = Bs[wave][k][h];
+      float a[CW];
+      float am = 0.0f;
+#pragma unroll
+      for (int c = 0; c < CW; ++c) {
+        a[c] = qv[c] * h2f((uint16_t)(kmn[c] & 0xffffu));
+        am = fmaxf(am, fabsf(a[c]));
+      }
+      am = bfly_max<16>(am);
+      const bool zero = !(am > 0.0f);
+      const int e = zero ? 0 : ilogb_f(am) - 21;
+      uint32_t l0w[CW / 4], l1w[CW / 4], l2w[CW / 4];
+#pragma unroll
+      for (int c = 0; c < CW / 4; ++c) l0w[c] = l1w[c] = l2w[c] = 0u;
+#pragma unroll
+      for (int c = 0; c < CW; ++c) {
+        const int A = (int)rintf(ldexpf(a[c], -e));
+        const int L0 = ((A + 128) & 255) - 128;
+        const int A1 = (A - L0) >> 8;
+        const int L1 = ((A1 + 128) & 255) - 128;
+        const int L2 = (A1 - L1) >> 8;
+        l0w[c / 4] |= ((uint32_t)L0 & 255u) << (8 * (c % 4));
+        l1w[c / 4] |= ((uint32_t)L1 & 255u) << (8 * (c % 4));
+        l2w[c / 4] |= ((uint32_t)L2 & 255u) << (8 * (c % 4));
+      }
+      {
+        int8_t *row = &As[wave][h * 4][jc * CW];
+#pragma unroll
+        for (int c = 0; c < CW / 4; ++c) {
+          const uint32_t z = 0u;
+          ((uint32_t *)(row + 0 * AST))[c] = hv ? l0w[c] : z;
+          ((uint32_t *)(row + 1 * AST))[c] = hv ? l1w[c] : z;
+          ((uint32_t *)(row + 2 * AST))[c] = hv ? l2w[c] : z;
+          ((uint32_t *)(row + 3 * AST))[c] = z;
+        }
+      }
+      const float pb = bd.x;
+      // Delta' is stored with the block ingredients, after the contraction
+      const float dv = (bd.y + (zero ? 0.0f : ldexpf(64.0f * (float)D, e))) * (1.0f + 0x1p-15f);
+      wave_lds_sync();
+
+      // ---- exact integer core on the matrix cores -------------------------------
+      v4i acc[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) acc[nt] = (v4i){0, 0, 0, 0};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const v4i Aop = *(const v4i *)&As[wave][lane & 15][ks * 64 + 16 * (lane >> 4)];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          acc[nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aop, Bn[ks][nt], acc[nt], 0, 0, 0);
+        }
+      }
+      if (u + W < U) fetch(i2, g2, b2);
+
+      // ---- scores and block ingredients (lane: head lane/16, token lane%16) -----
+      const float sc = ldexpf(1.0f, e);
+      float x[4];
+      float mx = -INFINITY;
+      float *dst = w.shat + ((size_t)i * s.Hq + hq) * s.Tmax + (size_t)b * BLOCK;
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        acc[nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aop, Bn[ks][nt], acc[nt], 0, 0, 0);
+        const long long Dv = ((long long)acc[nt][2] << 16) + ((long long)acc[nt][1] << 8) +
+                             (long long)acc[nt][0];
+        x[nt] = fmaf(i64_to_f32(Dv), sc, pb);
+        const bool ok = nt * 16 + jc < n;
+        mx = ok ? fmaxf(mx, x[nt]) : mx;
+        if (ok && hv) __builtin_nontemporal_store(x[nt], &dst[nt * 16 + jc]);
       }
-    }
-    if (u + W < U) fetch(i2, g2, b2);
-
-    // ---- scores and block ingredients (lane: head lane/16, token lane%16) -----
-    const float sc = ldexpf(1.0f, e);
-    float x[4];
-    float mx = -INFINITY;
-    float *dst = w.shat + ((size_t)i * s.Hq + hq) * s.Tmax + (size_t)b * BLOCK;
+      mx = bfly_max<16>(mx);
+      uint32_t Ls = 0u;
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const long long Dv = ((long long)acc[nt][2] << 16) + ((long long)acc[nt][1] << 8) +
-                           (long long)acc[nt][0];
-      x[nt] = fmaf(i64_to_f32(Dv), sc, pb);
-      const bool ok = nt * 16 + jc < n;
-      mx = ok ? fmaxf(mx, x[nt]) : mx;
-      if (ok && hv) __builtin_nontemporal_store(x[nt], &dst[nt * 16 + jc]);
+      for (int nt = 0; nt < 4; ++nt) {
+        const uint32_t l = (uint32_t)floorf(0x1p24f * exp2k(x[nt] - mx));
+        Ls += (nt * 16 + jc < n) ? l : 0u;
+      }
+      Ls = bfly_sum_u32<16>(Ls);
+      if (hv && jc == 0) {
+        const size_t o = ((size_t)i * s.Hq + hq) * s.NBmax + b;
+        w.mhat[o] = mx;
+        w.Lhat[o] = Ls;
+        w.delta[o] = dv;
+      }
+      wave_lds_sync();
+      // advance
+      i = i2;
+      g = g2;
+      b = b2;
     }
-    mx = bfly_max<16>(mx);
-    uint32_t Ls = 0u;
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const uint32_t l = (uint32_t)floorf(0x1p24f * exp2k(x[nt] - mx));
-      Ls += (nt * 16 + jc < n) ? l : 0u;
-    }
-    Ls = bfly_sum_u32<16>(Ls);
-    if (hv && jc == 0) {
-      const size_t o = ((size_t)i * s.Hq + hq) * s.NBmax + b;
-      w.mhat[o] = mx;
-      w.Lhat[o] = Ls;
-      w.delta[o] = dv;
-    }
-    wave_lds_sync();
-    // advance
-    i = i2;
-    g = g2;
-    b = b2;
   }
 }
 

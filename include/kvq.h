@@ -212,7 +212,9 @@ kvq_status kvq_decode_naive(kvq_ctx *ctx, int32_t layer, int32_t n_seqs, const i
 kvq_status kvq_dense_decode(kvq_ctx *ctx, int32_t n_seqs, const int32_t *seq_lens, const void *q,
                             const void *k, const void *v, float *out, void *stream);
 
-/* Forgets every token of a slot at every layer. */
+/* Forgets every token of a slot at every layer.  Synchronises the device
+ * first (appends to the slot on any stream complete before its state is
+ * cleared) and again before returning. */
 kvq_status kvq_reset_seq(kvq_ctx *ctx, int32_t seq_id);
 
 /* Tokens currently held by (slot, layer), or a negative status. */

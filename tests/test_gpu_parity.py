@@ -84,6 +84,61 @@ def test_tier1_matches_oracle(env, chunks):
     gpu["ctx"].close()
 
 
+def test_tier1_multi_sequence_appends_spanning_blocks(env):
+    """Appends that start inside an open block and end in another partial
+    block, for several sequences in one call whose open-block parities
+    differ (each has had a different number of appends): tier 1 equals the
+    oracle's for every sequence and KV head."""
+    kvq, torch, orc = env
+    dev = torch.device("cuda:0")
+    r = np.random.default_rng(21)
+    T = [300, 257, 190]
+    Hkv, d = 2, 128
+    K = [S.to16(r.standard_normal((t, Hkv, d)).astype(np.float32) * 3) for t in T]
+    V = [S.to16(r.standard_normal((t, Hkv, d)).astype(np.float32)) for t in T]
+    sched = [{0: 37, 1: 100, 2: 1}, {0: 90}, {0: 70, 1: 64, 2: 129}, {1: 5, 2: 30},
+             {0: 103, 1: 88, 2: 30}]
+    ctx = kvq.Context(1, 3, 8, Hkv, d, 320)
+    pos = [0, 0, 0]
+    for step in sched + [{i: T[i] - sum(x.get(i, 0) for x in sched) for i in range(3)}]:
+        ids = [i for i in sorted(step) if step[i] > 0]
+        if not ids:
+            continue
+        log(f"[parity] multi-seq append {[(i, pos[i], step[i]) for i in ids]}")
+        kk = np.concatenate([K[i][pos[i]:pos[i] + step[i]] for i in ids])
+        vv = np.concatenate([V[i][pos[i]:pos[i] + step[i]] for i in ids])
+        ctx.append(0, ids, [step[i] for i in ids], torch.from_numpy(kk.view(np.float16)).to(dev),
+                   torch.from_numpy(vv.view(np.float16)).to(dev))
+        for i in ids:
+            pos[i] += step[i]
+    torch.cuda.synchronize()
+    assert pos == T
+    for i in range(3):
+        for g in range(Hkv):
+            t1 = orc.build_tier1(np.ascontiguousarray(K[i][:, g]), np.ascontiguousarray(V[i][:, g]))
+            compare_tier1(ctx, t1, 0, i, g, f"seq {i} kv {g}")
+    ctx.close()
+
+
+def test_channel_sums_absorption_case(env):
+    """Keys constant per channel (1024 on channel 0, 2^-15 elsewhere) and
+    q = 1: the ascending fma chains absorb every later term, so every INT8
+    score equals fl32(C * 1024) exactly (see the oracle's pin); the whole
+    step is compared with the oracle."""
+    kvq, torch, orc = env
+    d, T, Hkv, Hq = 128, 200, 2, 8
+    k = np.full((T, Hkv, d), 2.0 ** -15, np.float32)
+    k[:, :, 0] = 1024.0
+    v = np.random.default_rng(5).standard_normal((T, Hkv, d)).astype(np.float32)
+    q = np.ones((Hq, d), np.float32)
+    case = Case("absorption", Hq, Hkv, d, [(S.to16(k), S.to16(v), S.to16(q), None)])
+    gpu, ref = _check(env, case)
+    C = np.float32(orc.lib().orc_query_scale(d))
+    want = (np.float32(C) * np.float32(1024.0)).view(np.uint32)
+    assert np.all(f32bits(gpu["trace"][0]["shat"]) == want)
+    gpu["ctx"].close()
+
+
 def test_tier1_d64_and_config1(env):
     kvq, torch, orc = env
     w = S.workload(1)
