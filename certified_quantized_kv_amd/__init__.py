@@ -88,6 +88,7 @@ _SIGS = {
     "kvq_selftest_exp2k": (I32, [P, P, I64, P]),
     "kvq_selftest_merge_runs": (I32, [P, I64, P, P]),
     "kvq_selftest_sort": (I32, [P, I64, P, P, P]),
+    "kvq_dense_decode_noalloc": (I32, [I32, I32, I32, I32, I32, P, P, P, P, P, P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -164,6 +165,34 @@ def exp2k(x):
     if st != 0:
         raise KvqError(st, "exp2k")
     return y
+
+
+def dense_decode_noalloc(seq_lens, q, k, v, out=None):
+    """Dense FP16 decode attention with no device allocation in the library
+    (kvq_dense_decode_noalloc): q fp16 [n, Hq, d]; k, v fp16 [n, max_tokens,
+    Hkv, d]; out f32 [n, Hq, d] (allocated here by torch when not given).
+    Its partials use the library's fixed per-device scratch array."""
+    import torch
+    n = len(seq_lens)
+    if q.dim() != 3 or q.shape[0] != n:
+        raise ValueError(f"q shape {tuple(q.shape)} does not match {n} sequences")
+    Hq, d = q.shape[1], q.shape[2]
+    if k.dim() != 4 or tuple(k.shape) != tuple(v.shape) or k.shape[0] != n or k.shape[3] != d:
+        raise ValueError(f"k/v shape {tuple(k.shape)} / {tuple(v.shape)} does not match q")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k and v must be on one device")
+    out = torch.empty((n, Hq, d), dtype=torch.float32, device=q.device) if out is None else out
+    st = _lib.kvq_dense_decode_noalloc(n, Hq, k.shape[2], d, k.shape[1], _i32(seq_lens),
+                                       _dev(q, torch.float16, "q"), _dev(k, torch.float16, "k"),
+                                       _dev(v, torch.float16, "v"),
+                                       _out(out, (n, Hq, d), torch.float32, q.device, "out"),
+                                       _stream())
+    if st != 0:
+        raise KvqError(st, f"kvq_dense_decode_noalloc: {_lib.kvq_last_error(None).decode()}")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 def sort_desc(keys):

@@ -18,7 +18,7 @@ LIB = os.path.join(HERE, "libkvq.so")
 OBJ = os.path.join(HERE, "_build")
 
 SOURCES = ["kvq_codec.hip", "kvq_score.hip", "kvq_select.hip", "kvq_control.hip",
-           "kvq_decode.hip", "kvq_dense.hip", "kvq_api.hip"]
+           "kvq_decode.hip", "kvq_dense.hip", "kvq_api.hip", "kvq_noalloc.hip"]
 
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
          "-fno-gpu-flush-denormals-to-zero", "-Xclang", "-target-feature", "-Xclang",

@@ -274,7 +274,9 @@ const char *kvq_strerror(kvq_status s) {
   }
 }
 
-const char *kvq_last_error(const kvq_ctx *ctx) { return ctx ? ctx->err.c_str() : ""; }
+const char *kvq_last_error(const kvq_ctx *ctx) {
+  return ctx ? ctx->err.c_str() : noalloc_last_error();
+}
 
 double kvq_tier1_bytes_per_token(int32_t d) {
   // K codes d + K meta 4d/64 + V codes d/2 + V meta 4d/32 + eta 4/64

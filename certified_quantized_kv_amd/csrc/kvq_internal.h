@@ -201,6 +201,7 @@ hipError_t launch_export_kcodes(const Shape &s, const Tier1 &t, size_t u, int T,
                                 hipStream_t st);
 hipError_t launch_export_vcodes(const Shape &s, const Tier1 &t, size_t u, int T, uint8_t *dst,
                                 hipStream_t st);
+const char *noalloc_last_error();   // kvq_noalloc.hip
 hipError_t launch_copy_blocks(const uint32_t *list, int n, const uint16_t *src, uint16_t *dst,
                               int d, hipStream_t st);
 

@@ -212,6 +212,31 @@ kvq_status kvq_decode_naive(kvq_ctx *ctx, int32_t layer, int32_t n_seqs, const i
 kvq_status kvq_dense_decode(kvq_ctx *ctx, int32_t n_seqs, const int32_t *seq_lens, const void *q,
                             const void *k, const void *v, float *out, void *stream);
 
+/* Dense FP16 decode attention that allocates nothing, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same computation and kernels as
+ * kvq_dense_decode, without a context:
+ *   n_q_heads, n_kv_heads, head_dim   as in kvq_config (head_dim 64 or 128,
+ *           n_q_heads / n_kv_heads in {1, 2, 4}, n_kv_heads <= 128)
+ *   max_tokens  row capacity of each sequence in k and v
+ *   seq_lens (host)  [n_seqs], 1 <= seq_lens[i] <= max_tokens, n_seqs <= 64
+ *   q, k, v, out     as in kvq_dense_decode (device; fp16 / f32)
+ * The split-K partials live in one fixed device array per GPU of
+ * KVQ_NOALLOC_SCRATCH_BYTES, held until the process ends; a call needs
+ * n_seqs * n_kv_heads * ceil(ceil(max seq_len / 64) / 8) * (n_q_heads /
+ * n_kv_heads) * (head_dim + 2) * 4 bytes of it (at 131072 tokens and 8 KV
+ * heads of d = 128: 4.26 MB per sequence) and returns KVQ_ECAPACITY, launching
+ * nothing, when that exceeds the array.  The first call on each device
+ * resolves the array's address (make it outside graph capture).  Calls whose
+ * work overlaps on one device share the array and race.  Stream-ordered on
+ * stream.  Errors: the status, and a message in kvq_last_error(NULL) for the
+ * calling thread. */
+#define KVQ_NOALLOC_SCRATCH_BYTES (16u << 20)
+kvq_status kvq_dense_decode_noalloc(int32_t n_seqs, int32_t n_q_heads, int32_t n_kv_heads,
+                                    int32_t head_dim, int32_t max_tokens, const int32_t *seq_lens,
+                                    const void *q, const void *k, const void *v, float *out,
+                                    void *stream);
+
 /* Forgets every token of a slot at every layer.  Synchronises the device
  * first (appends to the slot on any stream complete before its state is
  * cleared) and again before returning. */
@@ -221,6 +246,8 @@ kvq_status kvq_reset_seq(kvq_ctx *ctx, int32_t seq_id);
 int64_t kvq_seq_len(const kvq_ctx *ctx, int32_t layer, int32_t seq_id);
 
 const char *kvq_strerror(kvq_status s);
+/* Message of the last failing call on ctx; with ctx NULL, of the last
+ * failing context-free call (kvq_dense_decode_noalloc) on this thread. */
 const char *kvq_last_error(const kvq_ctx *ctx);
 
 /* Device bytes of tier 1 per (token, KV head), and the context's totals. */
