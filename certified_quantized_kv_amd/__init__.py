@@ -89,6 +89,7 @@ _SIGS = {
     "kvq_selftest_merge_runs": (I32, [P, I64, P, P]),
     "kvq_selftest_sort": (I32, [P, I64, P, P, P]),
     "kvq_dense_decode_noalloc": (I32, [I32, I32, I32, I32, I32, P, P, P, P, P, P]),
+    "kvq_selftest_launch_shape": (I32, [I32, I32]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -193,6 +194,14 @@ def dense_decode_noalloc(seq_lens, q, k, v, out=None):
 
 
 NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def set_launch_shape(score_wgs=0, mix_blocks=0):
+    """Test hook (kvq_selftest_launch_shape): cap the INT8 scoring grid and
+    choose the mixed decode's chunk size for later calls; (0, 0) = defaults."""
+    st = _lib.kvq_selftest_launch_shape(int(score_wgs), int(mix_blocks))
+    if st != 0:
+        raise KvqError(st, "kvq_selftest_launch_shape")
 
 
 def sort_desc(keys):

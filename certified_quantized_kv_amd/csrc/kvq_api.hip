@@ -1114,6 +1114,14 @@ kvq_status kvq_selftest_sort(const uint64_t *keys, int64_t n, uint64_t *out, int
              : KVQ_EHIP;
 }
 
+kvq_status kvq_selftest_launch_shape(int32_t score_wgs, int32_t mix_blocks) {
+  if (score_wgs < 0 || (mix_blocks != 0 && mix_blocks != DEC_CB && mix_blocks != MIX_CB))
+    return KVQ_EINVAL;
+  set_score_grid_cap(score_wgs);
+  set_mix_chunk_blocks(mix_blocks == 0 ? MIX_CB : mix_blocks);
+  return KVQ_OK;
+}
+
 kvq_status kvq_selftest_merge_runs(const uint64_t *in, int64_t n, uint64_t *out, int64_t *n_out) {
   if (n < 0 || (n > 0 && (!in || !out)) || !n_out) return KVQ_EINVAL;
   for (int64_t k = 0; k < n; ++k)

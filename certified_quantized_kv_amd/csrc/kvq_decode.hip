@@ -35,7 +35,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 // and the four waves' sums share that reference (they add without rescaling).
 // Scores, value metadata and codes of a wave's next block load while the
 // current one is accumulated.
-template <int D>
+template <int D, int MIX_CB>
 __global__ __launch_bounds__(256, 6) void k_decode_mixed(Shape s, Tier1 t, Step w, SeqTab tab, int layer) {
   constexpr int NT = D / 16;                     // 16-channel tiles
   constexpr int NG = D / VGROUP;                 // value groups (two tiles each)
@@ -273,11 +273,25 @@ __global__ __launch_bounds__(256, 6) void k_decode_mixed(Shape s, Tier1 t, Step 
   }
 }
 
+// Blocks per chunk of the mixed decode: MIX_CB, or DEC_CB while a test has
+// selected the smaller chunks (kvq_selftest_launch_shape).  Outputs round
+// differently with the chunking; no decision depends on it.
+static int g_mix_cb = MIX_CB;
+void set_mix_chunk_blocks(int cb) { g_mix_cb = (cb == DEC_CB) ? DEC_CB : MIX_CB; }
+int mix_chunk_blocks() { return g_mix_cb; }
+
 hipError_t launch_decode(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,
                          int layer, int maxNB, hipStream_t st) {
-  dim3 grid((maxNB + MIX_CB - 1) / MIX_CB, s.Hkv, tab.n);
-  if (s.d == 128) return launch_k(k_decode_mixed<128>, grid, dim3(256), 0, st, s, t, w, tab, layer);
-  return launch_k(k_decode_mixed<64>, grid, dim3(256), 0, st, s, t, w, tab, layer);
+  const int cb = g_mix_cb;
+  dim3 grid((maxNB + cb - 1) / cb, s.Hkv, tab.n);
+  if (cb == DEC_CB) {
+    if (s.d == 128)
+      return launch_k(k_decode_mixed<128, DEC_CB>, grid, dim3(256), 0, st, s, t, w, tab, layer);
+    return launch_k(k_decode_mixed<64, DEC_CB>, grid, dim3(256), 0, st, s, t, w, tab, layer);
+  }
+  if (s.d == 128)
+    return launch_k(k_decode_mixed<128, MIX_CB>, grid, dim3(256), 0, st, s, t, w, tab, layer);
+  return launch_k(k_decode_mixed<64, MIX_CB>, grid, dim3(256), 0, st, s, t, w, tab, layer);
 }
 
 // Merges the chunk partials of each (sequence, query head): mode 0 reads the
@@ -294,7 +308,8 @@ static_assert((MAX_NB + DEC_CB - 1) / DEC_CB <= COMB_MAXCH, "chunk weights fit i
 // no rung 4 either) the workgroup of channel quarter 0 also writes the
 // head's outputs: level, and E_key, E_val rounded up to binary32.
 __global__ __launch_bounds__(256) void k_combine(Shape s, Step w, SeqTab tab, float *out, int mode,
-                                                 float *e_key, float *e_val, int8_t *level) {
+                                                 float *e_key, float *e_val, int8_t *level,
+                                                 int mix_cb) {
   __shared__ float fw[COMB_MAXCH];
   __shared__ float red[256];
   __shared__ float wred[4];
@@ -307,7 +322,7 @@ __global__ __launch_bounds__(256) void k_combine(Shape s, Step w, SeqTab tab, fl
     e_val[o] = f32_up(w.eval64[o]);
   }
   const bool dense = mode == 2 || (mode == 0 && w.hlevel[(size_t)i * s.Hq + hq] >= 3);
-  const int cb = dense ? DEC_CB : MIX_CB;
+  const int cb = dense ? DEC_CB : mix_cb;
   const int NB = (tab.T[i] + BLOCK - 1) / BLOCK, nch = (NB + cb - 1) / cb;
   const float *part = (dense ? w.partd : w.part) + (((size_t)i * s.Hkv + g) * s.nchmax * G + h) * (D + 2);
   const size_t stride = (size_t)G * (D + 2);
@@ -384,7 +399,7 @@ __global__ __launch_bounds__(256) void k_combine(Shape s, Step w, SeqTab tab, fl
 hipError_t launch_combine(const Shape &s, const Step &w, const SeqTab &tab, float *out, int mode,
                           float *e_key, float *e_val, int8_t *level, hipStream_t st) {
   return launch_k(k_combine, dim3(s.Hq, tab.n, 4), dim3(256), 0, st, s, w, tab, out, mode, e_key,
-                  e_val, level);
+                  e_val, level, g_mix_cb);
 }
 
 }  // namespace kvq

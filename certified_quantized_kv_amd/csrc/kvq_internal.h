@@ -202,6 +202,9 @@ hipError_t launch_export_kcodes(const Shape &s, const Tier1 &t, size_t u, int T,
 hipError_t launch_export_vcodes(const Shape &s, const Tier1 &t, size_t u, int T, uint8_t *dst,
                                 hipStream_t st);
 const char *noalloc_last_error();   // kvq_noalloc.hip
+void set_score_grid_cap(int wgs);   // kvq_score.hip (test hook)
+void set_mix_chunk_blocks(int cb);  // kvq_decode.hip (test hook)
+int mix_chunk_blocks();
 hipError_t launch_copy_blocks(const uint32_t *list, int n, const uint16_t *src, uint16_t *dst,
                               int d, hipStream_t st);
 

@@ -306,9 +306,16 @@ int grid_score_int8(const Shape &s) {
   return per_cu * s.ncu;
 }
 
-// Workgroups: what the device holds at once, or one wave per unit.
+// Workgroups: what the device holds at once, or one wave per unit, or fewer
+// while a test has capped the grid (kvq_selftest_launch_shape): the grid
+// decides which wave scores which block and which blocks share a batch of
+// channel-sum chains, never a result.
+static int g_score_cap = 0;
+void set_score_grid_cap(int wgs) { g_score_cap = wgs > 0 ? wgs : 0; }
+
 static int int8_grid(int resident, int units) {
-  return std::max(1, std::min(resident, (units + 3) / 4));
+  const int g = std::max(1, std::min(resident, (units + 3) / 4));
+  return g_score_cap ? std::min(g, g_score_cap) : g;
 }
 
 hipError_t launch_score_int8(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,

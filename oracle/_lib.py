@@ -58,8 +58,9 @@ _SIGS = {
 def lib():
     global _lib
     if _lib is None:
-        build()
-        L = ctypes.CDLL(LIB)
+        # a sanitizer build of the same source (tests/test_oracle_asan.py)
+        path = os.environ.get("KVQ_ORACLE_LIB") or build()
+        L = ctypes.CDLL(path)
         for name, (res, args) in _SIGS.items():
             fn = getattr(L, name)
             fn.restype = res
