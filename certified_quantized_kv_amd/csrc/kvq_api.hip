@@ -548,6 +548,7 @@ namespace {
 struct Plan {
   int64_t nk = 0, nv = 0;
   uint32_t flags = 0;
+  bool flagged = false;   // the first controller round flagged a head
   std::vector<unsigned long long> ent;
 };
 
@@ -568,6 +569,7 @@ kvq_status read_plan_wait(kvq_ctx *c, Plan &p) {
   p.nk = (int64_t)c->plan_host[0];
   p.nv = (int64_t)c->plan_host[1];
   p.flags = (uint32_t)c->plan_host[2];
+  p.flagged = c->plan_host[3] != 0ull;
   if (p.nk < 0 || (size_t)p.nk > kcap || p.nv < 0 || (size_t)p.nv > kcap)
     return fail(c, KVQ_EHIP, "promotion plan out of range");
   p.ent.assign(c->plan_host + 4, c->plan_host + 4 + std::min((size_t)p.nk, first));
@@ -774,8 +776,18 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
       tm.open(TC_SCORE16);
       HIPCK(ctx, launch_score_fp16(s, w, tab, layer, maxNB, st));
     }
+    // The first round evaluates every head (k_eval) and flags the heads the
+    // group decisions would act on (ranking failure, E_key > eps_key, E_val
+    // > v_tol).  In the common case none is flagged: every level is 0 and the
+    // speculative combine below writes the outputs, so the group pass
+    // (k_decide) does not run.  Otherwise k_decide runs for this round and
+    // the rounds go on as below.
+    const bool first = round == 0 && !ctx->th.force_dense && !ctx->th.fp16_values;
     tm.open(TC_CONTROL);
-    HIPCK(ctx, launch_control(s, ctx->t, w, tab, layer, ctx->th, round, maxNB, st));
+    if (first)
+      HIPCK(ctx, launch_eval(s, ctx->t, w, tab, layer, ctx->th, maxNB, st));
+    else
+      HIPCK(ctx, launch_control(s, ctx->t, w, tab, layer, ctx->th, round, maxNB, st));
     rs = read_plan_issue(ctx, st);
     if (rs != KVQ_OK) return rs;
     // the decode and combine go in behind the plan's copy: in the common case
@@ -791,7 +803,7 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
       tm.open(TC_COMBINE);
       // mixed partials for every head: the result is kept only if no head
       // reached rung 3
-      HIPCK(ctx, launch_combine(s, w, tab, out, 1, e_key, e_val, level, st));
+      HIPCK(ctx, launch_combine(s, w, tab, out, first ? 3 : 1, e_key, e_val, level, st));
       HIPCK(ctx, hipEventRecord(ctx->ev_spec, st));
       spec = true;
     }
@@ -800,8 +812,23 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
     if (rs != KVQ_OK) return rs;
     ++syncs;
     rounds = round + 1;
+    if (first && !plan.flagged) {
+      decoded = true;
+      break;
+    }
+    if (first) {
+      // a flagged head: the group decisions of this round, and a new plan
+      tm.open(TC_CONTROL);
+      HIPCK(ctx, launch_decide(s, ctx->t, w, tab, layer, ctx->th, round, maxNB, st));
+      tm.close();
+      rs = read_plan(ctx, st, plan);
+      if (rs != KVQ_OK) return rs;
+      ++syncs;
+    }
     if (!(plan.flags & 1u) && plan.ent.empty()) {
-      decoded = !ctx->th.force_dense && !(plan.flags & 2u);
+      // outputs of the speculative combine stand unless a head is at rung 3;
+      // after a flagged first round they came from the first round's sums
+      decoded = !first && !ctx->th.force_dense && !(plan.flags & 2u);
       break;
     }
   }

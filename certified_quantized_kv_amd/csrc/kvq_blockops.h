@@ -67,7 +67,8 @@ __device__ inline int build_runs(const uint8_t *flags, int NB, uint32_t *runs, i
 
 // Plan for the host (device words, 64-bit): [0] number of K runs, [1] number
 // of V runs, [2] flags (bit0: a group is still widening, bit1: some head is at
-// rung 3), then K entries from word 4 and V entries from word 4 + kcap, each
+// rung 3), [3] nonzero when the first controller round flagged a head for the
+// group decisions, then K entries from word 4 and V entries from word 4 + kcap, each
 // len | start << 16 | ig << 32 | kind << 48 with ig = i * Hkv + g.  Groups
 // reserve their entries with atomics (entry order is immaterial to the copies).
 __device__ inline void emit_runs(const Shape &s, const Step &w, int ig, int kind,

@@ -227,6 +227,12 @@ __device__ void evaluate_head(const Shape &s, const Step &w, const Thresh &th, i
     uint32_t f = hfv;                   // written by this workgroup only
     f = ok ? (f | 1u) : ((f & ~1u) | 4u);
     w.hflags[(size_t)i * s.Hq + hq] = f;
+    // a head the group decisions would act on: a ranking failure (rung 3),
+    // E_key above eps_key (rung 1 or 3) or E_val above v_tol (rung 2).  When
+    // no head of the first round is flagged, the decisions are known without
+    // the group pass: level 0, E_val from these sums (see k_combine)
+    const bool acts = !ok || ek > th.eps_key || (double)v4[4] / (double)v4[0] > th.v_tol;
+    if (acts) atomicOr(&w.plan[3], 1ull);
   }
 }
 
@@ -290,8 +296,10 @@ __global__ __launch_bounds__(CTL_NT) void k_eval(Shape s, Tier1 t, Step w, SeqTa
   __shared__ uint16_t pos[MAX_NB];
   __shared__ CtlShared sh;
   const int i = blockIdx.y, hq = blockIdx.x, g = hq / s.G;
-  // a new plan starts with this round (the host has read the previous one)
-  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 4) w.plan[threadIdx.x] = 0ull;
+  // a new plan starts with this round (the host has read the previous one);
+  // word 3 (heads flagged for the group decisions) is cleared at the start of
+  // the step and only read after the first round
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 3) w.plan[threadIdx.x] = 0ull;
   const int NB = (tab.T[i] + BLOCK - 1) / BLOCK;
   const float *eta = t.eta + unit_of(s, tab.slot[i], layer, g) * s.NBmax;
   evaluate_head(s, w, th, i, g, hq, NB, eta, w.gstat + (size_t)i * s.Hkv + g,
@@ -442,14 +450,25 @@ __global__ __launch_bounds__(CTL_NT) void k_decide(Shape s, Tier1 t, Step w, Seq
   }
 }
 
-hipError_t launch_control(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,
-                          int layer, const Thresh &th, int round, int maxNB, hipStream_t st) {
+hipError_t launch_eval(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab, int layer,
+                       const Thresh &th, int maxNB, hipStream_t st) {
   const int n2 = max(64, pow2_at_least(maxNB));
-  const hipError_t e = launch_k(k_eval, dim3(s.Hq, tab.n), dim3(CTL_NT),
-                                (uint32_t)sort_lds_bytes(n2), st, s, t, w, tab, layer, th);
-  if (e != hipSuccess) return e;
+  return launch_k(k_eval, dim3(s.Hq, tab.n), dim3(CTL_NT), (uint32_t)sort_lds_bytes(n2), st, s, t,
+                  w, tab, layer, th);
+}
+
+hipError_t launch_decide(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,
+                         int layer, const Thresh &th, int round, int maxNB, hipStream_t st) {
+  const int n2 = max(64, pow2_at_least(maxNB));
   return launch_k(k_decide, dim3(s.Hkv, tab.n), dim3(CTL_NT), (uint32_t)sort_lds_bytes(n2), st, s,
                   t, w, tab, layer, th, round);
+}
+
+hipError_t launch_control(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,
+                          int layer, const Thresh &th, int round, int maxNB, hipStream_t st) {
+  const hipError_t e = launch_eval(s, t, w, tab, layer, th, maxNB, st);
+  if (e != hipSuccess) return e;
+  return launch_decide(s, t, w, tab, layer, th, round, maxNB, st);
 }
 
 // ---- rung 4 and the per-head outputs ---------------------------------------------

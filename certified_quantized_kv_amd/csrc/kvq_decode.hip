@@ -306,7 +306,8 @@ static_assert((MAX_NB + DEC_CB - 1) / DEC_CB <= COMB_MAXCH, "chunk weights fit i
 
 // With `level` non-null (a certified step in which no head reached rung 3, so
 // no rung 4 either) the workgroup of channel quarter 0 also writes the
-// head's outputs: level, and E_key, E_val rounded up to binary32.
+// head's outputs: level, and E_key, E_val rounded up to binary32 (mode 3:
+// from the first round's evaluation sums, the group decisions not having run).
 __global__ __launch_bounds__(256) void k_combine(Shape s, Step w, SeqTab tab, float *out, int mode,
                                                  float *e_key, float *e_val, int8_t *level,
                                                  int mix_cb) {
@@ -317,9 +318,20 @@ __global__ __launch_bounds__(256) void k_combine(Shape s, Step w, SeqTab tab, fl
   const int D = s.d, G = s.G, g = hq / G, h = hq % G, CQ = D / 4;
   if (level && cq == 0 && threadIdx.x == 0) {
     const size_t o = (size_t)i * s.Hq + hq;
-    level[o] = w.hlevel[o];
-    e_key[o] = f32_up(w.ekey64[o]);
-    e_val[o] = f32_up(w.eval64[o]);
+    if (mode == 3) {
+      // first round, no head flagged: consistent, E_key <= eps_key, no value
+      // promoted (E_val <= v_tol), nothing widened -> level 0
+      const double ev = (double)w.evs[2 * o] / (double)w.evs[2 * o + 1];
+      w.eval64[o] = ev;
+      w.hlevel[o] = 0;
+      level[o] = 0;
+      e_key[o] = f32_up(w.ekey64[o]);
+      e_val[o] = f32_up(ev);
+    } else {
+      level[o] = w.hlevel[o];
+      e_key[o] = f32_up(w.ekey64[o]);
+      e_val[o] = f32_up(w.eval64[o]);
+    }
   }
   const bool dense = mode == 2 || (mode == 0 && w.hlevel[(size_t)i * s.Hq + hq] >= 3);
   const int cb = dense ? DEC_CB : mix_cb;

@@ -183,13 +183,18 @@ hipError_t launch_score_fp16(const Shape &s, const Step &w, const SeqTab &tab, i
                              int maxNB, hipStream_t st);
 hipError_t launch_control(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,
                           int layer, const Thresh &th, int round, int maxNB, hipStream_t st);
+hipError_t launch_eval(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab, int layer,
+                       const Thresh &th, int maxNB, hipStream_t st);
+hipError_t launch_decide(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,
+                         int layer, const Thresh &th, int round, int maxNB, hipStream_t st);
 hipError_t launch_finalize(const Shape &s, const Step &w, const SeqTab &tab, const Thresh &th,
                            float *e_key, float *e_val, int8_t *level, hipStream_t st);
 hipError_t launch_decode(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,
                          int layer, int maxNB, hipStream_t st);
 hipError_t launch_dense_staged(const Shape &s, const Step &w, const SeqTab &tab, int layer,
                                const uint16_t *q16, int maxNB, hipStream_t st);
-// mode 0: partials chosen by each head's level; 1: mixed partials; 2: dense
+// mode 0: partials chosen by each head's level; 1: mixed partials; 2: dense;
+// 3: mixed partials, and the outputs of a first round that flagged no head
 hipError_t launch_combine(const Shape &s, const Step &w, const SeqTab &tab, float *out, int mode,
                           float *e_key, float *e_val, int8_t *level, hipStream_t st);
 hipError_t launch_dense_vram(const Shape &s, const Step &w, const DenseArgs &a, int maxNB,
