@@ -3,7 +3,7 @@
 // cost of certification ("Runtime-Certified Bounded-Error Quantized
 // Attention", Résultats: slowdown versus dense attention at 8K-128K).
 //
-// Per (sequence, KV head, chunk of 16 blocks) one workgroup; wave w takes
+// Per (sequence, KV head, chunk of DEC_CB = 8 blocks) one workgroup; wave w takes
 // blocks b0 + w, b0 + w + 4, ... of the chunk, 32 tokens at a time:
 //   scores  s_ht = q_h . k_t on the matrix cores: v_mfma_f32_16x16x32_f16
 //           with rows = the group's query heads (zero rows above G),

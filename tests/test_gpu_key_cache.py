@@ -80,7 +80,10 @@ def _case(seed, L, Hq, Hkv, d, T, sizes):
     return K, V, appends, qs
 
 
-@pytest.mark.parametrize("frac", [0.4, 2.0], ids=["budget-40pct", "budget-all"])
+# 0.596: the "asymmetric cache configuration" as read here (device memory at
+# 72 % of the dense FP16 cache: (0.72 * 4d - 216.06) / 2d of the key blocks)
+@pytest.mark.parametrize("frac", [0.4, (0.72 * 512 - 216.0625) / 256, 2.0],
+                         ids=["budget-40pct", "budget-asymmetric-59.6pct", "budget-all"])
 def test_key_cache_bit_identical_over_steps(env, frac):
     kvq, torch, orc = env
     L, Hq, Hkv, d, T = 2, 8, 2, 128, 1000
