@@ -215,12 +215,12 @@ struct NoPlace {
   __device__ void operator()(unsigned long long, int) const {}
 };
 
-template <int NT, class OnPlace = NoPlace>
+// RK = keys per thread: the caller guarantees n <= RK * NT.
+template <int NT, int RK = (MAX_NB + NT - 1) / NT, class OnPlace = NoPlace>
 __device__ __forceinline__ bool sort_desc_u64(unsigned long long *keys, int n, int cap,
                                               OnPlace on_place = OnPlace()) {
   constexpr int SB = SORT_BUCKETS;
   constexpr int PER = SB / NT;           // counters per thread in the scan
-  constexpr int RK = (MAX_NB + NT - 1) / NT;   // keys per thread
   static_assert(SB % NT == 0, "bucket count");
   static_assert(4 * NT >= MAX_NB, "the comparison network's chunks (4 keys per lane) cover MAX_NB keys");
   unsigned long long *tmp = keys + cap;

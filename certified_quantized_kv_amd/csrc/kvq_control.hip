@@ -79,6 +79,7 @@ __device__ void block_sum_u64_8(unsigned long long (&v)[8], CtlShared &sh) {
 // over S_h), then weights, E_key sums and sort keys together.  gsp / hfp
 // point at the group's and the head's state: they are read with the block
 // arrays, and a final group or a head at rung 3 is not evaluated.
+template <int EB>
 __device__ void evaluate_head(const Shape &s, const Step &w, const Thresh &th, int i, int g, int hq,
                               int NB, const float *eta, const uint32_t *gsp, const uint32_t *hfp,
                               unsigned long long *keys, uint16_t *pos, CtlShared &sh) {
@@ -88,10 +89,9 @@ __device__ void evaluate_head(const Shape &s, const Step &w, const Thresh &th, i
   const uint32_t *pi = w.pi + base;
   __shared__ float mred[2][CTL_NT / 64];
   __shared__ unsigned long long sred[6][CTL_NT / 64];
-  // every per-block input of this thread's blocks b = t + r CTL_NT is loaded
-  // once, up front (both score kinds; the block's kind selects afterwards),
-  // so the passes below wait on no global load
-  constexpr int EB = (MAX_NB + CTL_NT - 1) / CTL_NT;
+  // every per-block input of this thread's blocks b = t + r CTL_NT (EB of
+  // them) is loaded once, up front (both score kinds; the block's kind
+  // selects afterwards), so the passes below wait on no global load
   const uint32_t gsv = *gsp, hfv = *hfp;
   bool pr[EB];
   float mb[EB], dl[EB], et[EB];
@@ -180,7 +180,7 @@ __device__ void evaluate_head(const Shape &s, const Step &w, const Thresh &th, i
   // member's squared rank difference is taken where the sort places it
   const int n2 = max(64, pow2_at_least(n));
   unsigned long long ssd = 0ull;
-  const bool placed = sort_desc_u64<CTL_NT>(keys, n, n2, [&](unsigned long long k, int j) {
+  const bool placed = sort_desc_u64<CTL_NT, EB>(keys, n, n2, [&](unsigned long long k, int j) {
     const uint32_t b = 0xffffffffu - (uint32_t)(k & 0xffffffffull);
     const long long dd = (long long)pos[b] - (long long)j;
     ssd += (unsigned long long)(dd * dd);
@@ -290,6 +290,7 @@ __device__ void value_rung(const Shape &s, const Tier1 &t, const Step &w, const 
 // One controller round, part 1: every query head not yet at rung 3, in a
 // group not yet final, is evaluated on the group's current U (one workgroup
 // per query head).
+template <int EB>
 __global__ __launch_bounds__(CTL_NT) void k_eval(Shape s, Tier1 t, Step w, SeqTab tab, int layer,
                                                  Thresh th) {
   extern __shared__ unsigned long long keys[];
@@ -302,7 +303,7 @@ __global__ __launch_bounds__(CTL_NT) void k_eval(Shape s, Tier1 t, Step w, SeqTa
   if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 3) w.plan[threadIdx.x] = 0ull;
   const int NB = (tab.T[i] + BLOCK - 1) / BLOCK;
   const float *eta = t.eta + unit_of(s, tab.slot[i], layer, g) * s.NBmax;
-  evaluate_head(s, w, th, i, g, hq, NB, eta, w.gstat + (size_t)i * s.Hkv + g,
+  evaluate_head<EB>(s, w, th, i, g, hq, NB, eta, w.gstat + (size_t)i * s.Hkv + g,
                 w.hflags + (size_t)i * s.Hq + hq, keys, pos, sh);
 }
 
@@ -453,8 +454,14 @@ __global__ __launch_bounds__(CTL_NT) void k_decide(Shape s, Tier1 t, Step w, Seq
 hipError_t launch_eval(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab, int layer,
                        const Thresh &th, int maxNB, hipStream_t st) {
   const int n2 = max(64, pow2_at_least(maxNB));
-  return launch_k(k_eval, dim3(s.Hq, tab.n), dim3(CTL_NT), (uint32_t)sort_lds_bytes(n2), st, s, t,
-                  w, tab, layer, th);
+  const dim3 grid(s.Hq, tab.n), block(CTL_NT);
+  const uint32_t lds = (uint32_t)sort_lds_bytes(n2);
+  switch ((maxNB + CTL_NT - 1) / CTL_NT) {   // blocks per thread
+    case 1: return launch_k(k_eval<1>, grid, block, lds, st, s, t, w, tab, layer, th);
+    case 2: return launch_k(k_eval<2>, grid, block, lds, st, s, t, w, tab, layer, th);
+    case 3: return launch_k(k_eval<3>, grid, block, lds, st, s, t, w, tab, layer, th);
+    default: return launch_k(k_eval<4>, grid, block, lds, st, s, t, w, tab, layer, th);
+  }
 }
 
 hipError_t launch_decide(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,

@@ -20,6 +20,9 @@ namespace kvq {
 
 constexpr int SEL_NT = 1024;
 
+// EB = blocks per thread (the launch picks the least that covers the
+// longest sequence of the call).
+template <int EB>
 __global__ __launch_bounds__(SEL_NT) void k_select(Shape s, Step w, SeqTab tab, int tau_ppm) {
   extern __shared__ unsigned long long keys[];
   __shared__ float red[SEL_NT / 64];
@@ -34,7 +37,6 @@ __global__ __launch_bounds__(SEL_NT) void k_select(Shape s, Step w, SeqTab tab, 
   for (int b = threadIdx.x; b < NB; b += SEL_NT) fk[b] = 0;
 
   // the thread's blocks b = t + r SEL_NT, loaded once
-  constexpr int EB = (MAX_NB + SEL_NT - 1) / SEL_NT;
   float mh[EB];
   uint32_t lh[EB];
   float m = -INFINITY;
@@ -66,7 +68,7 @@ __global__ __launch_bounds__(SEL_NT) void k_select(Shape s, Step w, SeqTab tab, 
     }
     keys[b] = key;
   }
-  sort_desc_u64<SEL_NT>(keys, NB, n2);
+  sort_desc_u64<SEL_NT, EB>(keys, NB, n2);
 
   // pi, then prefix sums of the sorted weights: thread t owns positions
   // [t*per, (t+1)*per)
@@ -121,8 +123,14 @@ __global__ __launch_bounds__(SEL_NT) void k_select(Shape s, Step w, SeqTab tab, 
 hipError_t launch_select(const Shape &s, const Step &w, const SeqTab &tab, int tau_ppm, int maxNB,
                          hipStream_t st) {
   const int n2 = max(64, pow2_at_least(maxNB));
-  return launch_k(k_select, dim3(s.Hq, tab.n), dim3(SEL_NT), (uint32_t)sort_lds_bytes(n2), st, s,
-                  w, tab, tau_ppm);
+  const dim3 grid(s.Hq, tab.n), block(SEL_NT);
+  const uint32_t lds = (uint32_t)sort_lds_bytes(n2);
+  switch ((maxNB + SEL_NT - 1) / SEL_NT) {
+    case 1: return launch_k(k_select<1>, grid, block, lds, st, s, w, tab, tau_ppm);
+    case 2: return launch_k(k_select<2>, grid, block, lds, st, s, w, tab, tau_ppm);
+    case 3: return launch_k(k_select<3>, grid, block, lds, st, s, w, tab, tau_ppm);
+    default: return launch_k(k_select<4>, grid, block, lds, st, s, w, tab, tau_ppm);
+  }
 }
 
 // The workgroup sort of the selection and controller kernels on n distinct
