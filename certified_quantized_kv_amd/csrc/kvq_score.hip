@@ -15,13 +15,15 @@
 // a real contraction: 16 rows (4 heads x 3 signed-byte limbs of A, + 1 zero
 // row each) x 64 channels x 16 tokens per v_mfma_i32_16x16x64_i8.  Limbs:
 // A = L2 2^16 + L1 2^8 + L0 with L0, L1 in [-128, 127]; each limb's dot
-// product is exact in int32, and D_t is recombined in int64.
+// product is exact in int32, and D_t is recombined exactly (in fp64, where
+// it is below 2^38) before its one rounding to fp32.
 //
 // Per-block channel sums (beta and the Delta' sum): one fma chain from 0
 // over the channels in ascending order, acc <- fmaf(x_c, y_c, acc).  A chain
 // is sequential, so the wave runs its chains in batches: lane 4 h + k takes
-// query head h of the batch's unit k (four units of the wave's own list),
-// with the units' (off + 128 s, t_c) pairs staged in LDS.
+// query head h of the batch's unit k (four consecutive blocks of one KV
+// head), with the units' (off + 128 s, t_c) pairs and the group's q rows
+// staged in LDS.
 //
 // Delta'_b (bound on |shat_t - s'_t|, s' the FP16-key score below):
 //   K'_c = max(|off_c|, |fmaf(256, s_c, off_c)|)
@@ -43,63 +45,66 @@ namespace kvq {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-// Work split: a unit is one (sequence, KV head, block), numbered with the
-// block fastest; wave k of the grid (W waves) takes units k, k + W, k + 2W,
-// ...: every wave carries the same load to within one unit, and at any
-// moment the grid streams one contiguous window of W blocks (measured
-// faster than a window of W / Hkv blocks in each KV head).  A wave's
-// successive units may belong to different KV heads, so each unit's query
-// slice is fetched with its codes; the metadata of four consecutive units of
-// the wave's list (a batch) is fetched together, one batch ahead, for the
-// channel-sum chains, and kept in LDS for the units' prologues.  The kernel also carries
-// the step set-up (q' for the later kernels, flags cleared); its own waves
-// form q' from q directly.  Codes and metadata are read once per step, and
-// the scores are read once later: both go through non-temporal loads and
-// stores, which leave the caches to the data that is reused.
+// Work split: a batch is up to four consecutive blocks of one (sequence, KV
+// head), numbered sequence-major, then KV head, then block; wave k of the
+// grid (W waves) takes batches k, k + W, k + 2W, ...  At any moment the grid
+// streams one window of W consecutive batches, which keeps the HBM channels
+// evenly loaded (measured faster than each wave sweeping a contiguous run
+// of its own).  A batch's units share one query group: the group's q rows
+// and the units' key metadata (contiguous in memory) are fetched together
+// one batch ahead, a unit's codes one unit ahead.  Rows of the score tile
+// above G repeat head 0, so every lane computes a value that is written
+// somewhere valid: the stores carry no lane conditions, and the compiler's
+// wait counts stay exact (a store under a lane condition makes it assume
+// the store was skipped and wait for every older load).  The kernel also
+// carries the step set-up (q' for the later kernels, flags cleared).  Codes
+// and metadata are read once per step and the scores read once later: both
+// go through non-temporal loads and stores, which leave the caches to the
+// data that is reused.
 template <int D>
 __global__ __launch_bounds__(256, 4) void k_score_int8(Shape s, Tier1 t, Step w, SeqTab tab, int layer,
                                                     const uint16_t *__restrict__ q16, float C) {
   constexpr int CW = D / 16;            // channels per lane-chunk
   constexpr int NKS = D / 64;           // MFMA k-steps per block
   constexpr int AST = D + 16;           // LDS row stride of the A operand (bank spread)
-  constexpr int NBT = 4;                // units per batch of channel-sum chains
+  constexpr int NBT = 4;                // units per batch
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int h = lane >> 4, jc = lane & 15;
-  const bool hv = h < s.G;
+  const int G = s.G;
+  const int hs = h < G ? h : 0;         // head slot of the lane's row
 
   __shared__ __align__(16) int8_t As[4][16][AST];
-  __shared__ __align__(16) uint32_t Ms[4][NBT][D];   // the batch's key metadata
+  __shared__ __align__(16) uint16_t Ss[4][NBT][D];   // scales of the batch's units
   __shared__ __align__(16) float UTs[4][NBT][2 * D]; // (off + 128 s, t_c) per channel
-  __shared__ float2 Bs[4][NBT][4];                   // (beta, Delta' sum) per (unit, head)
+  __shared__ __align__(16) uint16_t Qs[4][4][D];     // q rows of the batch's group (head slots)
+  __shared__ float2 Bs[4][NBT][4];                   // (beta, Delta' sum) per (unit, head slot)
 
-  const int U = s.Hkv * tab.nbc[tab.n];
+  int NBA = 0;                          // batches of the call
+  for (int ii = 0; ii < tab.n; ++ii) NBA += s.Hkv * ((tab.nbc[ii + 1] - tab.nbc[ii] + NBT - 1) / NBT);
   const int W = gridDim.x * 4;
-  const int u0 = blockIdx.x * 4 + wave;
-  auto locate = [&](int uu, int &ii, int &gg, int &bb) {
+  const int wid = blockIdx.x * 4 + wave;
+  // batch -> (sequence, KV head, first block, units); wave-uniform
+  auto locate = [&](int bi, int &ii, int &gg, int &bb, int &nn) {
     ii = 0;
-    while (ii + 1 < tab.n && s.Hkv * tab.nbc[ii + 1] <= uu) ++ii;
-    const int r = uu - s.Hkv * tab.nbc[ii];
-    const int nbi = tab.nbc[ii + 1] - tab.nbc[ii];
-    gg = r / nbi;
-    bb = r - gg * nbi;
+    int nbi = tab.nbc[1] - tab.nbc[0];
+    int per = (nbi + NBT - 1) / NBT;
+    while (bi >= s.Hkv * per) {
+      bi -= s.Hkv * per;
+      ++ii;
+      nbi = tab.nbc[ii + 1] - tab.nbc[ii];
+      per = (nbi + NBT - 1) / NBT;
+    }
+    gg = bi / per;
+    bb = (bi - gg * per) * NBT;
+    nn = min(NBT, nbi - bb);
   };
-  int i, g, b;
-  locate(u0, i, g, b);
 
-  // software pipeline: the next unit's query slice and codes are in flight
-  // while the current one's scores and block ingredients are formed; the next
-  // batch's metadata while the current batch's units are processed
-  v4i Bn[NKS][4];
-  uint32_t qn[CW / 2];
-  uint32_t kb[CW];                      // lane (k, jc): unit k of a batch, channels jc CW ..
+  v4i Bn[NKS][4];                       // codes of the unit in flight
+  uint32_t kb[CW];                      // metadata of the batch in flight (row h: unit h)
+  uint32_t qb[CW / 2];                  // q slice (head slot h) of the batch in flight
   auto fetch = [&](int ii, int gg, int bb) {
-    const int hq = gg * s.G + (hv ? h : 0);
-    const uint32_t *qsrc = (const uint32_t *)(q16 + ((size_t)ii * s.Hq + hq) * D + jc * CW);
-#pragma unroll
-    for (int c = 0; c < CW / 2; ++c) qn[c] = qsrc[c];
     const size_t uu = unit_of(s, tab.slot[ii], layer, gg);
     const uint8_t *kc = t.kcodes + (uu * s.NBmax + bb) * (size_t)(BLOCK * D);
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
@@ -107,37 +112,51 @@ __global__ __launch_bounds__(256, 4) void k_score_int8(Shape s, Tier1 t, Step w,
         Bn[ks][nt] = __builtin_nontemporal_load(
             (const v4i *)(kc + ((size_t)((ks * 4 + nt) * 64 + lane)) * 16));
   };
-  auto fetch_meta = [&](int ub) {
-    const int uk = ub + h * W;          // row h of the wave loads unit h of the batch
-    if (uk < U) {
-      int ii, gg, bb;
-      locate(uk, ii, gg, bb);
-      const size_t uu = unit_of(s, tab.slot[ii], layer, gg);
-      const uint32_t *km = t.kmeta + (uu * s.NBmax + bb) * D + jc * CW;
+  auto fetch_meta = [&](int ii, int gg, int bb, int nn) {
+    const size_t uu = unit_of(s, tab.slot[ii], layer, gg);
+    const uint32_t *km = t.kmeta + (uu * s.NBmax + bb + min(h, nn - 1)) * D + jc * CW;
 #pragma unroll
-      for (int c = 0; c < CW; ++c) kb[c] = __builtin_nontemporal_load(&km[c]);
-    } else {
+    for (int c = 0; c < CW; ++c) kb[c] = __builtin_nontemporal_load(&km[c]);
+    const uint32_t *qs = (const uint32_t *)(q16 + ((size_t)ii * s.Hq + gg * G + hs) * D + jc * CW);
 #pragma unroll
-      for (int c = 0; c < CW; ++c) kb[c] = 0u;
-    }
+    for (int c = 0; c < CW / 2; ++c) qb[c] = qs[c];
   };
-  if (u0 < U) {
-    fetch_meta(u0);
-    fetch(i, g, b);
+
+  float qv[CW];                         // q' of the lane's slice (head slot h)
+  if (wid >= NBA) {
+    step_setup(s, w, tab.n, q16, C, blockIdx.x * (size_t)blockDim.x + threadIdx.x,
+               (size_t)gridDim.x * blockDim.x);
+    return;
   }
-  // the set-up's stores go out while the first unit's loads are in flight
+  // the set-up's stores first, then the first batch's metadata and first
+  // unit's codes, waited for in full: no wait count inside the loop has to
+  // allow for a path from here
   step_setup(s, w, tab.n, q16, C, blockIdx.x * (size_t)blockDim.x + threadIdx.x,
              (size_t)gridDim.x * blockDim.x);
-  if (u0 >= U) return;
-  for (int ub = u0; ub < U; ub += NBT * W) {
-    const int nbt = min(NBT, (U - ub + W - 1) / W);
-    // ---- channel terms of the batch's units (lane (k, jc)), then the chains --
+  int i, g, b, nbt;
+  locate(wid, i, g, b, nbt);
+  fetch_meta(i, g, b, nbt);
+  fetch(i, g, b);
+  __builtin_amdgcn_s_waitcnt(0);
+
+  for (int bi = wid;;) {
+    const bool more = bi + W < NBA;
+    int ni = i, ng = g, nb = b, nn = nbt;
+    if (more) locate(bi + W, ni, ng, nb, nn);
+    // ---- the batch's set-up: scales, channel terms and q rows into LDS; the
+    // next batch's metadata and q, and (past the first batch, whose codes
+    // came with its metadata) the first unit's codes go out; then the
+    // channel-sum chains (lane 4 h + k: head slot h of unit k)
     {
-      uint32_t *mrow = &Ms[wave][h][jc * CW];
+      uint32_t *srow = (uint32_t *)&Ss[wave][h][jc * CW];
       float *urow = &UTs[wave][h][2 * jc * CW];
+      uint32_t *qrow = (uint32_t *)&Qs[wave][h][jc * CW];
 #pragma unroll
-      for (int c = 0; c < CW; c += 4)
-        *(uint4 *)&mrow[c] = make_uint4(kb[c], kb[c + 1], kb[c + 2], kb[c + 3]);
+      for (int c = 0; c < CW; c += 2) srow[c / 2] = (kb[c] & 0xffffu) | (kb[c + 1] << 16);
+#pragma unroll
+      for (int c = 0; c < CW / 2; ++c) qrow[c] = qb[c];
+#pragma unroll
+      for (int c = 0; c < CW; ++c) qv[c] = h2f((uint16_t)(qb[c / 2] >> (16 * (c % 2)))) * C;
 #pragma unroll
       for (int c = 0; c < CW; c += 2) {
         float4 ut;
@@ -152,61 +171,65 @@ __global__ __launch_bounds__(256, 4) void k_score_int8(Shape s, Tier1 t, Step w,
         }
         *(float4 *)&urow[2 * c] = ut;
       }
-      if (ub + NBT * W < U) fetch_meta(ub + NBT * W);
-      wave_lds_sync();
-      if (lane < 4 * NBT) {
-        const int kk = lane & (NBT - 1), hh = lane / NBT;
-        int ik, gk, bk;
-        locate(ub + kk * W < U ? ub + kk * W : ub, ik, gk, bk);
-        const uint16_t *qrow = q16 + ((size_t)ik * s.Hq + gk * s.G + min(hh, s.G - 1)) * D;
-        const float *ut = &UTs[wave][kk][0];
-        float beta = 0.0f, sd = 0.0f;
-#pragma unroll 2
-        for (int c8 = 0; c8 < D; c8 += 8) {
-          const uint4 qq = *(const uint4 *)(qrow + c8);
-          const uint32_t qw[4] = {qq.x, qq.y, qq.z, qq.w};
-          float4 p[4];
-#pragma unroll
-          for (int x = 0; x < 4; ++x) p[x] = *(const float4 *)&ut[2 * c8 + 4 * x];
-#pragma unroll
-          for (int x = 0; x < 8; ++x) {
-            const float qf = h2f((uint16_t)(qw[x / 2] >> (16 * (x % 2)))) * C;
-            const float uc = (x % 2) ? p[x / 2].z : p[x / 2].x;
-            const float tc = (x % 2) ? p[x / 2].w : p[x / 2].y;
-            beta = fmaf(qf, uc, beta);
-            sd = fmaf(fabsf(qf), tc, sd);
-          }
-        }
-        Bs[wave][kk][hh] = make_float2(beta, sd);
-      }
-      wave_lds_sync();
     }
-    for (int k = 0; k < nbt; ++k) {
-      const int u = ub + k * W;
-      const int T = tab.T[i];
-      const int n = min(BLOCK, T - b * BLOCK);
-      const int hq = g * s.G + (hv ? h : 0);
-      // successor unit (its codes and query slice are fetched once this
-      // unit's contraction has consumed the registers)
-      int i2 = i, g2 = g, b2 = b;
-      if (u + W < U) locate(u + W, i2, g2, b2);
+    if (more) fetch_meta(ni, ng, nb, nn);
+    if (bi != wid) fetch(i, g, b);
+    wave_lds_sync();
+    if (lane < 4 * NBT) {
+      const int kk = lane & (NBT - 1), hh = lane / NBT;
+      const uint16_t *qrow = &Qs[wave][hh][0];
+      const float *ut = &UTs[wave][kk][0];
+      float beta = 0.0f, sd = 0.0f;
+#pragma unroll 2
+      for (int c8 = 0; c8 < D; c8 += 8) {
+        const uint4 qq = *(const uint4 *)(qrow + c8);
+        const uint32_t qw[4] = {qq.x, qq.y, qq.z, qq.w};
+        float4 p[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) p[x] = *(const float4 *)&ut[2 * c8 + 4 * x];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          const float qf = h2f((uint16_t)(qw[x / 2] >> (16 * (x % 2)))) * C;
+          const float uc = (x % 2) ? p[x / 2].z : p[x / 2].x;
+          const float tc = (x % 2) ? p[x / 2].w : p[x / 2].y;
+          beta = fmaf(qf, uc, beta);
+          sd = fmaf(fabsf(qf), tc, sd);
+        }
+      }
+      Bs[wave][kk][hh] = make_float2(beta, sd);
+    }
+    wave_lds_sync();
+
+    const int T = tab.T[i];
+    const int hq = g * G + hs;
+    // one unit of the batch; the first is a copy of its own, so that the
+    // loop's wait counts allow for the stores of the previous unit between a
+    // unit's codes and their use
+    auto unit = [&](const int k) {
+      const int bk = b + k;
+      const int n = min(BLOCK, T - bk * BLOCK);
 
       // ---- prologue: exponent and limbs of A per head ---------------------------
-      float qv[CW];
+      float sc4[CW];
+      {
+        const uint32_t *sp4 = (const uint32_t *)&Ss[wave][k][jc * CW];
+        uint32_t sw[CW / 2];
+        if constexpr (CW == 8) {
+          const uint4 v = *(const uint4 *)sp4;
+          sw[0] = v.x, sw[1] = v.y, sw[2] = v.z, sw[3] = v.w;
+        } else {
+          const uint2 v = *(const uint2 *)sp4;
+          sw[0] = v.x, sw[1] = v.y;
+        }
 #pragma unroll
-      for (int c = 0; c < CW; ++c) qv[c] = h2f((uint16_t)(qn[c / 2] >> (16 * (c % 2)))) * C;
-      uint32_t kmn[CW];
-#pragma unroll
-      for (int c = 0; c < CW; c += 4) {
-        const uint4 m4 = *(const uint4 *)&Ms[wave][k][jc * CW + c];
-        kmn[c] = m4.x, kmn[c + 1] = m4.y, kmn[c + 2] = m4.z, kmn[c + 3] = m4.w;
+        for (int c = 0; c < CW; ++c) sc4[c] = h2f((uint16_t)(sw[c / 2] >> (16 * (c % 2))));
       }
       const float2 bd = Bs[wave][k][h];
       float a[CW];
       float am = 0.0f;
 #pragma unroll
       for (int c = 0; c < CW; ++c) {
-        a[c] = qv[c] * h2f((uint16_t)(kmn[c] & 0xffffu));
+        a[c] = qv[c] * sc4[c];
         am = fmaxf(am, fabsf(a[c]));
       }
       am = bfly_max<16>(am);
@@ -230,11 +253,10 @@ __global__ __launch_bounds__(256, 4) void k_score_int8(Shape s, Tier1 t, Step w,
         int8_t *row = &As[wave][h * 4][jc * CW];
 #pragma unroll
         for (int c = 0; c < CW / 4; ++c) {
-          const uint32_t z = 0u;
-          ((uint32_t *)(row + 0 * AST))[c] = hv ? l0w[c] : z;
-          ((uint32_t *)(row + 1 * AST))[c] = hv ? l1w[c] : z;
-          ((uint32_t *)(row + 2 * AST))[c] = hv ? l2w[c] : z;
-          ((uint32_t *)(row + 3 * AST))[c] = z;
+          ((uint32_t *)(row + 0 * AST))[c] = l0w[c];
+          ((uint32_t *)(row + 1 * AST))[c] = l1w[c];
+          ((uint32_t *)(row + 2 * AST))[c] = l2w[c];
+          ((uint32_t *)(row + 3 * AST))[c] = 0u;
         }
       }
       const float pb = bd.x;
@@ -254,21 +276,24 @@ __global__ __launch_bounds__(256, 4) void k_score_int8(Shape s, Tier1 t, Step w,
           acc[nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aop, Bn[ks][nt], acc[nt], 0, 0, 0);
         }
       }
-      if (u + W < U) fetch(i2, g2, b2);
+      if (k + 1 < nbt) fetch(i, g, bk + 1);
 
-      // ---- scores and block ingredients (lane: head lane/16, token lane%16) -----
+      // ---- scores and block ingredients (lane: head slot lane/16, token lane%16)
+      // D_t = 2^16 L2-sum + 2^8 L1-sum + L0-sum is exact in fp64 (below 2^38)
       const float sc = ldexpf(1.0f, e);
       float x[4];
       float mx = -INFINITY;
-      float *dst = w.shat + ((size_t)i * s.Hq + hq) * s.Tmax + (size_t)b * BLOCK;
+      float *dst = w.shat + ((size_t)i * s.Hq + hq) * s.Tmax + (size_t)bk * BLOCK;
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        const long long Dv = ((long long)acc[nt][2] << 16) + ((long long)acc[nt][1] << 8) +
-                             (long long)acc[nt][0];
-        x[nt] = fmaf(i64_to_f32(Dv), sc, pb);
+        const double Dd = fma((double)acc[nt][2], 65536.0, fma((double)acc[nt][1], 256.0,
+                                                               (double)acc[nt][0]));
+        x[nt] = fmaf((float)Dd, sc, pb);
         const bool ok = nt * 16 + jc < n;
         mx = ok ? fmaxf(mx, x[nt]) : mx;
-        if (ok && hv) __builtin_nontemporal_store(x[nt], &dst[nt * 16 + jc]);
+        // tokens past T land inside the row's last block, which no reader
+        // takes past T; rows above G write head 0's values again
+        __builtin_nontemporal_store(x[nt], &dst[nt * 16 + jc]);
       }
       mx = bfly_max<16>(mx);
       uint32_t Ls = 0u;
@@ -278,18 +303,20 @@ __global__ __launch_bounds__(256, 4) void k_score_int8(Shape s, Tier1 t, Step w,
         Ls += (nt * 16 + jc < n) ? l : 0u;
       }
       Ls = bfly_sum_u32<16>(Ls);
-      if (hv && jc == 0) {
-        const size_t o = ((size_t)i * s.Hq + hq) * s.NBmax + b;
+      {
+        // every lane of a row holds its head's values: all store them
+        const size_t o = ((size_t)i * s.Hq + hq) * s.NBmax + bk;
         w.mhat[o] = mx;
         w.Lhat[o] = Ls;
         w.delta[o] = dv;
       }
       wave_lds_sync();
-      // advance
-      i = i2;
-      g = g2;
-      b = b2;
-    }
+    };
+    unit(0);
+    for (int k = 1; k < nbt; ++k) unit(k);
+    if (!more) break;
+    bi += W;
+    i = ni, g = ng, b = nb, nbt = nn;
   }
 }
 
@@ -306,26 +333,27 @@ int grid_score_int8(const Shape &s) {
   return per_cu * s.ncu;
 }
 
-// Workgroups: what the device holds at once, or one wave per unit, or fewer
+// Workgroups: what the device holds at once, or one wave per batch, or fewer
 // while a test has capped the grid (kvq_selftest_launch_shape): the grid
 // decides which wave scores which block and which blocks share a batch of
 // channel-sum chains, never a result.
 static int g_score_cap = 0;
 void set_score_grid_cap(int wgs) { g_score_cap = wgs > 0 ? wgs : 0; }
 
-static int int8_grid(int resident, int units) {
-  const int g = std::max(1, std::min(resident, (units + 3) / 4));
+static int int8_grid(int resident, int batches) {
+  const int g = std::max(1, std::min(resident, (batches + 3) / 4));
   return g_score_cap ? std::min(g, g_score_cap) : g;
 }
 
 hipError_t launch_score_int8(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,
                              int layer, const uint16_t *q, float C, hipStream_t st) {
-  const int units = s.Hkv * tab.nbc[tab.n];
+  int batches = 0;                      // four blocks of one (sequence, KV head) each
+  for (int i = 0; i < tab.n; ++i) batches += s.Hkv * ((tab.nbc[i + 1] - tab.nbc[i] + 3) / 4);
   if (s.d == 128) {
-    const int grid = int8_grid(grid_score_int8<128>(s), units);
+    const int grid = int8_grid(grid_score_int8<128>(s), batches);
     return launch_k(k_score_int8<128>, dim3(grid), dim3(256), 0, st, s, t, w, tab, layer, q, C);
   }
-  const int grid = int8_grid(grid_score_int8<64>(s), units);
+  const int grid = int8_grid(grid_score_int8<64>(s), batches);
   return launch_k(k_score_int8<64>, dim3(grid), dim3(256), 0, st, s, t, w, tab, layer, q, C);
 }
 
