@@ -61,25 +61,18 @@ __global__ __launch_bounds__(256, 6) void k_decode_mixed(Shape s, Tier1 t, Step 
   __shared__ __align__(16) int8_t As[4][NGW][16 * AST];
   __shared__ float pv[4][4][BLOCK];              // p of an FP16-value block, per wave
   __shared__ float sl[4][4];
-  const unsigned long long umask = __ballot(lane < nblk && U[b0 + lane] != 0);
-  const unsigned long long vmask = __ballot(lane < nblk && V[b0 + lane] != 0);
-
-  // chunk reference per head: max over the chunk's blocks of the block
-  // maxima; lane 16 h + k keeps head h's maximum of block b0 + k
+  // the chunk's block flags and both kinds of block maxima load at once
+  // (no load waits on another); the first blocks' value metadata and codes
+  // go out before the flags are used
+  const int k16 = lane & 15;
+  const size_t om = ((size_t)i * s.Hq + g * G + min(hl, G - 1)) * s.NBmax + b0 + min(k16, nblk - 1);
+  const float m16v = w.m16[om], mhv = w.mhat[om];
+  const uint8_t uf = U[b0 + min(lane, nblk - 1)], vf = V[b0 + min(lane, nblk - 1)];
+  // set once the flags are in: the chunk's U and V masks, and the chunk
+  // reference per head (max over the chunk's blocks of the block maxima in
+  // use; lane 16 h + k holds head h's maximum of block b0 + k)
+  unsigned long long umask = 0ull, vmask = 0ull;
   float Mh[4];
-  float bmv = -INFINITY;
-  {
-    const int k = lane & 15;
-    if (hl < G && k < nblk) {
-      const size_t o = ((size_t)i * s.Hq + g * G + hl) * s.NBmax + b0 + k;
-      bmv = ((umask >> k) & 1ull) ? w.m16[o] : w.mhat[o];
-    }
-    const float bm = bfly_max<16>(bmv);
-#pragma unroll
-    for (int h = 0; h < 4; ++h)
-      Mh[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bm), 16 * h));
-  }
-
   float acc[NTW];
 #pragma unroll
   for (int k = 0; k < NTW; ++k) acc[k] = 0.0f;
@@ -99,12 +92,10 @@ __global__ __launch_bounds__(256, 6) void k_decode_mixed(Shape s, Tier1 t, Step 
     uint32_t meta[NGW];
     uint2 pk[NTW];
   };
-  auto fetch = [&](Stage &st, int bb) {
+  // value metadata and codes (no flag needed), then the scores (FP16 keys'
+  // on blocks of U, INT8 keys' elsewhere)
+  auto fetch_vm = [&](Stage &st, int bb) {
     const int tk = min(bb * BLOCK + lane, T - 1);
-    const bool up = (umask >> (bb - b0)) & 1ull;
-    const float *src = (up ? w.sp : w.shat) + ((size_t)i * s.Hq + g * G) * s.Tmax + tk;
-#pragma unroll
-    for (int h = 0; h < 4; ++h) st.x[h] = src[(size_t)min(h, G - 1) * s.Tmax];
     const uint32_t *mp = t.vmeta + (u * s.Tmax + tk) * NG + half * NGW;
     if constexpr (NGW == 2) {
       const uint2 m = *(const uint2 *)mp;
@@ -116,6 +107,13 @@ __global__ __launch_bounds__(256, 6) void k_decode_mixed(Shape s, Tier1 t, Step 
 #pragma unroll
     for (int k = 0; k < NTW; ++k)
       st.pk[k] = *(const uint2 *)(vc + (size_t)((half * NTW + k) * 64 + lane) * 8);
+  };
+  auto fetch_sc = [&](Stage &st, int bb, unsigned long long umask) {
+    const int tk = min(bb * BLOCK + lane, T - 1);
+    const bool up = (umask >> (bb - b0)) & 1ull;
+    const float *src = (up ? w.sp : w.shat) + ((size_t)i * s.Hq + g * G) * s.Tmax + tk;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) st.x[h] = src[(size_t)min(h, G - 1) * s.Tmax];
   };
   // quantized values: p*s as fixed point against the INT4 codes
   auto body = [&](const Stage &cur, int b) {
@@ -216,15 +214,29 @@ __global__ __launch_bounds__(256, 6) void k_decode_mixed(Shape s, Tier1 t, Step 
   // registers and each wait covers only the older stage's loads; blocks with
   // FP16 values are skipped here and accumulated afterwards
   Stage st[2];
-  fetch(st[0], min(b0 + pair, b1 - 1));
-  if (PW > 1) fetch(st[1], min(b0 + pair + 2, b1 - 1));
+  fetch_vm(st[0], min(b0 + pair, b1 - 1));
+  if (PW > 1) fetch_vm(st[1], min(b0 + pair + 2, b1 - 1));
+  umask = __ballot(lane < nblk && uf != 0);
+  vmask = __ballot(lane < nblk && vf != 0);
+  {
+    const float bmv = (hl < G && k16 < nblk) ? (((umask >> k16) & 1ull) ? m16v : mhv) : -INFINITY;
+    const float bm = bfly_max<16>(bmv);
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+      Mh[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bm), 16 * h));
+  }
+  fetch_sc(st[0], min(b0 + pair, b1 - 1), umask);
+  if (PW > 1) fetch_sc(st[1], min(b0 + pair + 2, b1 - 1), umask);
 #pragma unroll
   for (int q = 0; q < PW; ++q) {
     const int bb = b0 + pair + 2 * q;
     if (bb >= b1) break;
     if (!((vmask >> (bb - b0)) & 1ull)) body(st[q & 1], bb);
     __builtin_amdgcn_sched_barrier(0);
-    if (q + 2 < PW) fetch(st[q & 1], min(bb + 4, b1 - 1));
+    if (q + 2 < PW) {
+      fetch_vm(st[q & 1], min(bb + 4, b1 - 1));
+      fetch_sc(st[q & 1], min(bb + 4, b1 - 1), umask);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
   if (vmask)
