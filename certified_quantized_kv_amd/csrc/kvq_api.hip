@@ -120,6 +120,7 @@ struct kvq_ctx {
   hipEvent_t ev_c[32] = {};    // copy timing pairs
   hipEvent_t ev_tot[2] = {};
   unsigned long long *plan_host = nullptr;
+  uint8_t *u_host = nullptr;   // the call's group unions U after the selection
   size_t plan_cap = 0;
   size_t plan_words = 0;
   int last_n = 0, last_layer = -1;
@@ -162,6 +163,7 @@ void free_all(kvq_ctx *c) {
   if (c->t2k_host) (void)hipHostFree(c->t2k_host);
   if (c->t2v_host) (void)hipHostFree(c->t2v_host);
   if (c->plan_host) (void)hipHostFree(c->plan_host);
+  if (c->u_host) (void)hipHostFree(c->u_host);
   if (c->kc.list_host) (void)hipHostFree(c->kc.list_host);
   if (c->cstream) (void)hipStreamDestroy(c->cstream);
   if (c->ev_start) (void)hipEventDestroy(c->ev_start);
@@ -423,6 +425,7 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out) {
   if (e == hipSuccess) e = hipHostGetDevicePointer(&dv, x->t2v_host, 0);
   x->plan_cap = 4096;
   if (e == hipSuccess) e = hipHostMalloc((void **)&x->plan_host, (4 + x->plan_cap) * 8, 0);
+  if (e == hipSuccess) e = hipHostMalloc((void **)&x->u_host, (size_t)c.max_batch * c.n_kv_heads * NBm, 0);
   if (e == hipSuccess && kcache) {
     e = hipHostMalloc((void **)&x->kc.list_host, 2 * x->kc.cap * 2 * 4, 0);
     KeyCache &kc = x->kc;
@@ -592,6 +595,54 @@ kvq_status read_plan(kvq_ctx *c, hipStream_t st, Plan &p) {
   return r != KVQ_OK ? r : read_plan_wait(c, p);
 }
 
+// After the selection: the group unions U of the call's sequences come back
+// (one copy on the step's stream), and the plan's key entries are their runs
+// of consecutive blocks, one entry per run (the layout of the device plan).
+kvq_status read_union(kvq_ctx *c, hipStream_t st, const SeqTab &tab, Plan &p) {
+  const Shape &s = c->s;
+  const size_t rows = (size_t)tab.n * s.Hkv;
+  HIPCK(c, hipMemcpyAsync(c->u_host, c->w.U, rows * s.NBmax, hipMemcpyDeviceToHost, st));
+  HIPCK(c, hipEventRecord(c->ev_plan, st));
+  HIPCK(c, hipEventSynchronize(c->ev_plan));
+  p = Plan();
+  for (int i = 0; i < tab.n; ++i) {
+    const int NB = tab.nbc[i + 1] - tab.nbc[i];
+    for (int g = 0; g < s.Hkv; ++g) {
+      const size_t ig = (size_t)i * s.Hkv + g;
+      const uint8_t *u = c->u_host + ig * s.NBmax;
+      int b = 0;
+      while (b < NB) {
+        // eight flags at a time while they are all clear or all set
+        if (b + 8 <= NB) {
+          uint64_t x;
+          memcpy(&x, u + b, 8);
+          if (x == 0ull) {
+            b += 8;
+            continue;
+          }
+        }
+        if (!u[b]) {
+          ++b;
+          continue;
+        }
+        int e = b + 1;
+        while (e + 8 <= NB) {
+          uint64_t x;
+          memcpy(&x, u + e, 8);
+          if (x != 0x0101010101010101ull) break;
+          e += 8;
+        }
+        while (e < NB && u[e]) ++e;
+        p.ent.push_back((unsigned long long)(e - b) | ((unsigned long long)b << 16) |
+                        ((unsigned long long)ig << 32));
+        b = e;
+      }
+    }
+  }
+  p.nk = (int64_t)p.ent.size();
+  return KVQ_OK;
+}
+
 // Issues the copies of a plan on the copy stream; returns bytes and blocks.
 // With the key cache, a key run splits into cached blocks (one device-side
 // gather from their slots) and runs of uncached blocks (host link), and the
@@ -749,11 +800,11 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
   HIPCK(ctx, launch_select(s, w, tab, ctx->th.tau_ppm, maxNB, st));
   tm.close();
   // with resident keys no copy depends on the selection, so the host reads
-  // the plan only for the statistics
+  // the unions only for the statistics
   Plan plan;
   kvq_status rs = KVQ_OK;
   if (!s.kres || stats) {
-    rs = read_plan(ctx, st, plan);
+    rs = read_union(ctx, st, tab, plan);
     if (rs != KVQ_OK) return rs;
     ++syncs;
   } else {

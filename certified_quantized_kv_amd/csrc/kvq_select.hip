@@ -10,8 +10,7 @@
 // Integer sums make the result independent of reduction order.
 // Promotion is per KV head: U_g = union of the group's top-K* sets.  Each
 // head's workgroup marks its blocks in U_g and in the group's new-block
-// flags, and lists its own selection as runs of consecutive blocks for the
-// host, which merges the runs of a group's heads before copying.
+// flags; the host reads U back and copies its runs of consecutive blocks.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 #include "kvq_blockops.h"
@@ -27,14 +26,10 @@ __global__ __launch_bounds__(SEL_NT) void k_select(Shape s, Step w, SeqTab tab, 
   extern __shared__ unsigned long long keys[];
   __shared__ float red[SEL_NT / 64];
   __shared__ unsigned long long sbuf[SEL_NT / 64];
-  __shared__ uint8_t fk[MAX_NB];                   // this head's selection
-  __shared__ uint32_t hruns[MAX_NB / 2 + 1];
-  __shared__ int tmp[18];
   const int i = blockIdx.y, hq = blockIdx.x;
   const int T = tab.T[i], NB = (T + BLOCK - 1) / BLOCK;
   const int n2 = max(64, pow2_at_least(NB));
   const size_t base = ((size_t)i * s.Hq + hq) * s.NBmax;
-  for (int b = threadIdx.x; b < NB; b += SEL_NT) fk[b] = 0;
 
   // the thread's blocks b = t + r SEL_NT, loaded once
   float mh[EB];
@@ -103,21 +98,16 @@ __global__ __launch_bounds__(SEL_NT) void k_select(Shape s, Step w, SeqTab tab, 
   __syncthreads();
 
   // the head's selection joins U_g and the group's new blocks (U is empty at
-  // this point of the step, so every selected block is new), and goes to the
-  // host as runs
+  // this point of the step, so every selected block is new)
   const int g = hq / s.G;
   const size_t ig = (size_t)i * s.Hkv + g;
   uint8_t *Kn = w.Knew + ig * s.NBmax;
   uint8_t *Ug = w.U + ig * s.NBmax;
   for (int p = threadIdx.x; p < kst; p += SEL_NT) {
     const uint32_t b = 0xffffffffu - (uint32_t)(keys[p] & 0xffffffffull);
-    fk[b] = 1;
     Kn[b] = 1;      // benign races across the group's heads: every writer stores 1
     Ug[b] = 1;
   }
-  __syncthreads();
-  const int nr = build_runs(fk, NB, hruns, tmp);
-  emit_runs(s, w, (int)ig, 0, hruns, nr, tmp + 17);
 }
 
 hipError_t launch_select(const Shape &s, const Step &w, const SeqTab &tab, int tau_ppm, int maxNB,
