@@ -1193,7 +1193,7 @@ kvq_status kvq_selftest_sort(const uint64_t *keys, int64_t n, uint64_t *out, int
 }
 
 kvq_status kvq_selftest_launch_shape(int32_t score_wgs, int32_t mix_blocks) {
-  if (score_wgs < 0 || (mix_blocks != 0 && mix_blocks != DEC_CB && mix_blocks != MIX_CB))
+  if (score_wgs < 0 || (mix_blocks != 0 && mix_blocks != 8 && mix_blocks != 16 && mix_blocks != MIX_CB))
     return KVQ_EINVAL;
   set_score_grid_cap(score_wgs);
   set_mix_chunk_blocks(mix_blocks == 0 ? MIX_CB : mix_blocks);

@@ -26,51 +26,58 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 // signed byte limbs (rows: head x limb, k: 64 tokens), B = the INT4 codes
 // (k: tokens, n: 16 channels), one v_mfma_i32_16x16x64_i8 per 16 channels.
 //
-// Per (sequence, KV head, chunk of MIX_CB blocks) one workgroup; wave w takes
-// half w % 2 of the channels of blocks b0 + w / 2, b0 + w / 2 + 2, ..., so a
-// block's scores and exponentials are read and formed by two waves.  The
+// Per (sequence, KV head, chunk of CB blocks) one workgroup of 2 NP waves;
+// wave w takes half w % 2 of the channels of blocks b0 + w / 2,
+// b0 + w / 2 + NP, ..., so a block's scores and exponentials are read and
+// formed by two waves.  The
 // chunk's softmax reference M_h is the largest block maximum of the scores in
 // use (FP16 on blocks of U, INT8 elsewhere), known from the scoring passes,
 // so every wave forms p = 2^(x - M_h) in registers as its blocks stream in,
 // and the four waves' sums share that reference (they add without rescaling).
 // Scores, value metadata and codes of a wave's next block load while the
 // current one is accumulated.
-template <int D, int MIX_CB>
-__global__ __launch_bounds__(256, 6) void k_decode_mixed(Shape s, Tier1 t, Step w, SeqTab tab, int layer) {
+template <int D, int CB, int NP>
+__global__ __launch_bounds__(128 * NP) void k_decode_mixed(Shape s, Tier1 t, Step w, SeqTab tab, int layer) {
   constexpr int NT = D / 16;                     // 16-channel tiles
   constexpr int NG = D / VGROUP;                 // value groups (two tiles each)
   constexpr int NTW = NT / 2, NGW = NG / 2;      // tiles and groups of one wave
   constexpr int AST = 80;                        // LDS row stride of A (bank spread)
-  constexpr int PW = MIX_CB / 2;                 // blocks per wave
-  static_assert(MIX_CB <= 16 && MIX_CB % 2 == 0, "block maxima sit in lanes 16 h + k");
+  constexpr int NW = 2 * NP;                     // waves
+  constexpr int PW = CB / NP;                    // blocks per wave
+  static_assert(CB <= 32 && CB % NP == 0, "block maxima sit in lanes 16 h + k, two per lane");
   const int i = blockIdx.z, g = blockIdx.y, ch = blockIdx.x;
   const int T = tab.T[i], NB = (T + BLOCK - 1) / BLOCK;
-  const int b0 = ch * MIX_CB;
+  const int b0 = ch * CB;
   if (b0 >= NB) return;
   const size_t ig = (size_t)i * s.Hkv + g;
   const int G = s.G;
-  const int b1 = min(NB, b0 + MIX_CB);
+  const int b1 = min(NB, b0 + CB);
   const int nblk = b1 - b0;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int hl = lane >> 4;                      // head of this lane in the MFMA output
-  const int half = wave & 1, pair = wave >> 1;   // channel half, block parity
+  const int half = wave & 1, pair = wave >> 1;   // channel half, block residue mod NP
   const size_t u = unit_of(s, tab.slot[i], layer, g);
   const uint8_t *U = w.U + ig * s.NBmax;
   const uint8_t *V = w.V + ig * s.NBmax;
 
-  __shared__ __align__(16) int8_t As[4][NGW][16 * AST];
-  __shared__ float pv[4][4][BLOCK];              // p of an FP16-value block, per wave
-  __shared__ float sl[4][4];
+  __shared__ __align__(16) int8_t As[NW][NGW][16 * AST];
+  __shared__ float pv[NW][4][BLOCK];             // p of an FP16-value block, per wave
+  __shared__ float sl[NW][4];
   // the chunk's block flags and both kinds of block maxima load at once
   // (no load waits on another); the first blocks' value metadata and codes
   // go out before the flags are used
   const int k16 = lane & 15;
-  const size_t om = ((size_t)i * s.Hq + g * G + min(hl, G - 1)) * s.NBmax + b0 + min(k16, nblk - 1);
-  const float m16v = w.m16[om], mhv = w.mhat[om];
+  const size_t om = ((size_t)i * s.Hq + g * G + min(hl, G - 1)) * s.NBmax + b0;
+  const float m16v = w.m16[om + min(k16, nblk - 1)], mhv = w.mhat[om + min(k16, nblk - 1)];
+  float m16w = -INFINITY, mhw = -INFINITY;       // blocks 16 + k of a 32-block chunk
+  if constexpr (CB > 16) {
+    m16w = w.m16[om + min(k16 + 16, nblk - 1)];
+    mhw = w.mhat[om + min(k16 + 16, nblk - 1)];
+  }
   const uint8_t uf = U[b0 + min(lane, nblk - 1)], vf = V[b0 + min(lane, nblk - 1)];
   // set once the flags are in: the chunk's U and V masks, and the chunk
   // reference per head (max over the chunk's blocks of the block maxima in
-  // use; lane 16 h + k holds head h's maximum of block b0 + k)
+  // use; lane 16 h + k holds head h's maxima of blocks b0 + k, b0 + 16 + k)
   unsigned long long umask = 0ull, vmask = 0ull;
   float Mh[4];
   float acc[NTW];
@@ -215,32 +222,34 @@ __global__ __launch_bounds__(256, 6) void k_decode_mixed(Shape s, Tier1 t, Step 
   // FP16 values are skipped here and accumulated afterwards
   Stage st[2];
   fetch_vm(st[0], min(b0 + pair, b1 - 1));
-  if (PW > 1) fetch_vm(st[1], min(b0 + pair + 2, b1 - 1));
+  if (PW > 1) fetch_vm(st[1], min(b0 + pair + NP, b1 - 1));
   umask = __ballot(lane < nblk && uf != 0);
   vmask = __ballot(lane < nblk && vf != 0);
   {
-    const float bmv = (hl < G && k16 < nblk) ? (((umask >> k16) & 1ull) ? m16v : mhv) : -INFINITY;
+    float bmv = (hl < G && k16 < nblk) ? (((umask >> k16) & 1ull) ? m16v : mhv) : -INFINITY;
+    if (CB > 16 && hl < G && k16 + 16 < nblk)
+      bmv = fmaxf(bmv, ((umask >> (k16 + 16)) & 1ull) ? m16w : mhw);
     const float bm = bfly_max<16>(bmv);
 #pragma unroll
     for (int h = 0; h < 4; ++h)
       Mh[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bm), 16 * h));
   }
   fetch_sc(st[0], min(b0 + pair, b1 - 1), umask);
-  if (PW > 1) fetch_sc(st[1], min(b0 + pair + 2, b1 - 1), umask);
+  if (PW > 1) fetch_sc(st[1], min(b0 + pair + NP, b1 - 1), umask);
 #pragma unroll
   for (int q = 0; q < PW; ++q) {
-    const int bb = b0 + pair + 2 * q;
+    const int bb = b0 + pair + NP * q;
     if (bb >= b1) break;
     if (!((vmask >> (bb - b0)) & 1ull)) body(st[q & 1], bb);
     __builtin_amdgcn_sched_barrier(0);
     if (q + 2 < PW) {
-      fetch_vm(st[q & 1], min(bb + 4, b1 - 1));
-      fetch_sc(st[q & 1], min(bb + 4, b1 - 1), umask);
+      fetch_vm(st[q & 1], min(bb + 2 * NP, b1 - 1));
+      fetch_sc(st[q & 1], min(bb + 2 * NP, b1 - 1), umask);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
   if (vmask)
-    for (int bb = b0 + pair; bb < b1; bb += 2)
+    for (int bb = b0 + pair; bb < b1; bb += NP)
       if ((vmask >> (bb - b0)) & 1ull) body_fp16(bb);
 
   // offset terms: head h, group j summed over the wave's tokens; channel
@@ -260,19 +269,22 @@ __global__ __launch_bounds__(256, 6) void k_decode_mixed(Shape s, Tier1 t, Step 
     const float lv = bfly_sum<64>(lsum[h]);
     if (lane == 0) sl[wave][h] = lv;
   }
-  // the two block parities' sums (same reference M_h) add in LDS, in the A
-  // area; the softmax sums come from the waves of channel half 0
+  // the NP block residues' sums (same reference M_h) add in LDS, in the A
+  // area, in residue order; the softmax sums come from the waves of channel
+  // half 0
   __syncthreads();
-  float *red = (float *)&As[0][0][0];            // [4 waves][NTW][64]
-  static_assert(sizeof(As) >= 4 * NTW * 64 * sizeof(float), "merge fits in the A area");
+  float *red = (float *)&As[0][0][0];            // [NW waves][NTW][64]
+  static_assert(sizeof(As) >= NW * NTW * 64 * sizeof(float), "merge fits in the A area");
 #pragma unroll
   for (int k = 0; k < NTW; ++k) red[(wave * NTW + k) * 64 + lane] = acc[k];
   __syncthreads();
-  for (int e = threadIdx.x; e < NT * 64; e += 256) {
+  for (int e = threadIdx.x; e < NT * 64; e += 128 * NP) {
     const int k = e / 64, ln = e % 64, h = ln >> 4;
-    const int hf = k / NTW, kk = k % NTW;        // waves hf (parity 0) and 2 + hf (parity 1)
+    const int hf = k / NTW, kk = k % NTW;        // waves 2 p + hf, residue p
     if (h < G) {
-      const float v = red[(hf * NTW + kk) * 64 + ln] + red[((2 + hf) * NTW + kk) * 64 + ln];
+      float v = red[(hf * NTW + kk) * 64 + ln];
+#pragma unroll
+      for (int p = 1; p < NP; ++p) v += red[((2 * p + hf) * NTW + kk) * 64 + ln];
       float *part = w.part + ((ig * s.nchmax + ch) * G + h) * (size_t)(D + 2);
       part[k * 16 + (ln & 15)] = v;
     }
@@ -281,29 +293,38 @@ __global__ __launch_bounds__(256, 6) void k_decode_mixed(Shape s, Tier1 t, Step 
     const int h = threadIdx.x;
     float *part = w.part + ((ig * s.nchmax + ch) * G + h) * (size_t)(D + 2);
     part[D] = h == 0 ? Mh[0] : h == 1 ? Mh[1] : h == 2 ? Mh[2] : Mh[3];
-    part[D + 1] = sl[0][h] + sl[2][h];
+    float l = sl[0][h];
+#pragma unroll
+    for (int p = 1; p < NP; ++p) l += sl[2 * p][h];
+    part[D + 1] = l;
   }
 }
 
-// Blocks per chunk of the mixed decode: MIX_CB, or DEC_CB while a test has
-// selected the smaller chunks (kvq_selftest_launch_shape).  Outputs round
-// differently with the chunking; no decision depends on it.
+// Blocks per chunk of the mixed decode: MIX_CB (32, eight waves), or 8 or 16
+// (four waves) while a test has selected them (kvq_selftest_launch_shape).
+// Outputs round differently with the chunking; no decision depends on it.
 static int g_mix_cb = MIX_CB;
-void set_mix_chunk_blocks(int cb) { g_mix_cb = (cb == DEC_CB) ? DEC_CB : MIX_CB; }
+void set_mix_chunk_blocks(int cb) { g_mix_cb = (cb == 8 || cb == 16) ? cb : MIX_CB; }
 int mix_chunk_blocks() { return g_mix_cb; }
 
 hipError_t launch_decode(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,
                          int layer, int maxNB, hipStream_t st) {
   const int cb = g_mix_cb;
   dim3 grid((maxNB + cb - 1) / cb, s.Hkv, tab.n);
-  if (cb == DEC_CB) {
+  if (cb == 8) {
     if (s.d == 128)
-      return launch_k(k_decode_mixed<128, DEC_CB>, grid, dim3(256), 0, st, s, t, w, tab, layer);
-    return launch_k(k_decode_mixed<64, DEC_CB>, grid, dim3(256), 0, st, s, t, w, tab, layer);
+      return launch_k(k_decode_mixed<128, 8, 2>, grid, dim3(256), 0, st, s, t, w, tab, layer);
+    return launch_k(k_decode_mixed<64, 8, 2>, grid, dim3(256), 0, st, s, t, w, tab, layer);
   }
+  if (cb == 16) {
+    if (s.d == 128)
+      return launch_k(k_decode_mixed<128, 16, 2>, grid, dim3(256), 0, st, s, t, w, tab, layer);
+    return launch_k(k_decode_mixed<64, 16, 2>, grid, dim3(256), 0, st, s, t, w, tab, layer);
+  }
+  static_assert(MIX_CB == 32, "the default chunk is the eight-wave kernel");
   if (s.d == 128)
-    return launch_k(k_decode_mixed<128, MIX_CB>, grid, dim3(256), 0, st, s, t, w, tab, layer);
-  return launch_k(k_decode_mixed<64, MIX_CB>, grid, dim3(256), 0, st, s, t, w, tab, layer);
+    return launch_k(k_decode_mixed<128, 32, 4>, grid, dim3(512), 0, st, s, t, w, tab, layer);
+  return launch_k(k_decode_mixed<64, 32, 4>, grid, dim3(512), 0, st, s, t, w, tab, layer);
 }
 
 // Merges the chunk partials of each (sequence, query head): mode 0 reads the

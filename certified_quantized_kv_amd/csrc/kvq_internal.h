@@ -17,7 +17,7 @@ namespace kvq {
 constexpr int MAX_CALL = KVQ_MAX_CALL_SEQS;
 constexpr int MAX_NB = 4096;        // blocks per sequence (262144 tokens)
 constexpr int DEC_CB = 8;           // blocks per split-K chunk of the dense decode kernels
-constexpr int MIX_CB = 16;          // blocks per split-K chunk of the mixed decode
+constexpr int MIX_CB = 32;          // blocks per split-K chunk of the mixed decode
 static_assert(MIX_CB >= DEC_CB, "chunk partials are sized for DEC_CB");
 
 // Tier 1, per unit (device memory):
