@@ -22,7 +22,7 @@
 // over the channels in ascending order, acc <- fmaf(x_c, y_c, acc).  A chain
 // is sequential, so the wave runs its chains in batches: lane 4 h + k takes
 // query head h of the batch's unit k (four consecutive blocks of one KV
-// head), with the units' (off + 128 s, t_c) pairs and the group's q rows
+// head), with the units' (off + 128 s, t_c) pairs and the group's q' rows
 // staged in LDS.
 //
 // Delta'_b (bound on |shat_t - s'_t|, s' the FP16-key score below):
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256, 4) void k_score_int8(Shape s, Tier1 t, Step w,
   __shared__ __align__(16) int8_t As[4][16][AST];
   __shared__ __align__(16) uint16_t Ss[4][NBT][D];   // scales of the batch's units
   __shared__ __align__(16) float UTs[4][NBT][2 * D]; // (off + 128 s, t_c) per channel
-  __shared__ __align__(16) uint16_t Qs[4][4][D];     // q rows of the batch's group (head slots)
+  __shared__ __align__(16) float Qs[4][4][D];        // q' rows of the batch's group (head slots)
   __shared__ float2 Bs[4][NBT][4];                   // (beta, Delta' sum) per (unit, head slot)
 
   int NBA = 0;                          // batches of the call
@@ -150,13 +150,13 @@ __global__ __launch_bounds__(256, 4) void k_score_int8(Shape s, Tier1 t, Step w,
     {
       uint32_t *srow = (uint32_t *)&Ss[wave][h][jc * CW];
       float *urow = &UTs[wave][h][2 * jc * CW];
-      uint32_t *qrow = (uint32_t *)&Qs[wave][h][jc * CW];
+      float *qrow = &Qs[wave][h][jc * CW];
 #pragma unroll
       for (int c = 0; c < CW; c += 2) srow[c / 2] = (kb[c] & 0xffffu) | (kb[c + 1] << 16);
 #pragma unroll
-      for (int c = 0; c < CW / 2; ++c) qrow[c] = qb[c];
-#pragma unroll
       for (int c = 0; c < CW; ++c) qv[c] = h2f((uint16_t)(qb[c / 2] >> (16 * (c % 2)))) * C;
+#pragma unroll
+      for (int c = 0; c < CW; c += 4) *(float4 *)&qrow[c] = make_float4(qv[c], qv[c + 1], qv[c + 2], qv[c + 3]);
 #pragma unroll
       for (int c = 0; c < CW; c += 2) {
         float4 ut;
@@ -177,19 +177,19 @@ __global__ __launch_bounds__(256, 4) void k_score_int8(Shape s, Tier1 t, Step w,
     wave_lds_sync();
     if (lane < 4 * NBT) {
       const int kk = lane & (NBT - 1), hh = lane / NBT;
-      const uint16_t *qrow = &Qs[wave][hh][0];
+      const float *qrow = &Qs[wave][hh][0];
       const float *ut = &UTs[wave][kk][0];
       float beta = 0.0f, sd = 0.0f;
 #pragma unroll 2
-      for (int c8 = 0; c8 < D; c8 += 8) {
-        const uint4 qq = *(const uint4 *)(qrow + c8);
-        const uint32_t qw[4] = {qq.x, qq.y, qq.z, qq.w};
-        float4 p[4];
+      for (int c4 = 0; c4 < D; c4 += 4) {
+        const float4 qq = *(const float4 *)(qrow + c4);
+        const float qw[4] = {qq.x, qq.y, qq.z, qq.w};
+        float4 p[2];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) p[x] = *(const float4 *)&ut[2 * c8 + 4 * x];
+        for (int x = 0; x < 2; ++x) p[x] = *(const float4 *)&ut[2 * c4 + 4 * x];
 #pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          const float qf = h2f((uint16_t)(qw[x / 2] >> (16 * (x % 2)))) * C;
+        for (int x = 0; x < 4; ++x) {
+          const float qf = qw[x];
           const float uc = (x % 2) ? p[x / 2].z : p[x / 2].x;
           const float tc = (x % 2) ? p[x / 2].w : p[x / 2].y;
           beta = fmaf(qf, uc, beta);
