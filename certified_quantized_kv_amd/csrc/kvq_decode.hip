@@ -19,6 +19,7 @@
 namespace kvq {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Mixed decode.  Per block, sum_t p_ht v_tc with v = off_tj + s_tj code_tc
 // splits into sum_t p_ht off_tj (VALU, per group) and the contraction
@@ -35,7 +36,8 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 // so every wave forms p = 2^(x - M_h) in registers as its blocks stream in,
 // and the four waves' sums share that reference (they add without rescaling).
 // Scores, value metadata and codes of a wave's next block load while the
-// current one is accumulated.
+// current one is accumulated; the value tiles are read once per step, through
+// non-temporal loads.
 template <int D, int CB, int NP>
 __global__ __launch_bounds__(128 * NP) void k_decode_mixed(Shape s, Tier1 t, Step w, SeqTab tab, int layer) {
   constexpr int NT = D / 16;                     // 16-channel tiles
@@ -97,7 +99,7 @@ __global__ __launch_bounds__(128 * NP) void k_decode_mixed(Shape s, Tier1 t, Ste
   struct Stage {
     float x[4];
     uint32_t meta[NGW];
-    uint2 pk[NTW];
+    u32x2 pk[NTW];
   };
   // value metadata and codes (no flag needed), then the scores (FP16 keys'
   // on blocks of U, INT8 keys' elsewhere)
@@ -105,15 +107,15 @@ __global__ __launch_bounds__(128 * NP) void k_decode_mixed(Shape s, Tier1 t, Ste
     const int tk = min(bb * BLOCK + lane, T - 1);
     const uint32_t *mp = t.vmeta + (u * s.Tmax + tk) * NG + half * NGW;
     if constexpr (NGW == 2) {
-      const uint2 m = *(const uint2 *)mp;
+      const u32x2 m = __builtin_nontemporal_load((const u32x2 *)mp);
       st.meta[0] = m.x, st.meta[1] = m.y;
     } else {
-      st.meta[0] = *mp;
+      st.meta[0] = __builtin_nontemporal_load(mp);
     }
     const uint8_t *vc = t.vcodes + (u * s.NBmax + bb) * (size_t)(32 * D);
 #pragma unroll
     for (int k = 0; k < NTW; ++k)
-      st.pk[k] = *(const uint2 *)(vc + (size_t)((half * NTW + k) * 64 + lane) * 8);
+      st.pk[k] = __builtin_nontemporal_load((const u32x2 *)(vc + (size_t)((half * NTW + k) * 64 + lane) * 8));
   };
   auto fetch_sc = [&](Stage &st, int bb, unsigned long long umask) {
     const int tk = min(bb * BLOCK + lane, T - 1);
