@@ -13,6 +13,8 @@
 //           o_h = sum_t 2^(x_t - M_h) v_t; the combine kernel merges chunks.
 // Dense mode (groups with a head at level 3/4) is the kernel of
 // kvq_dense.hip on the staged FP16 keys and values.
+#include <algorithm>
+
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -46,14 +48,17 @@ __global__ __launch_bounds__(128 * NP) void k_decode_mixed(Shape s, Tier1 t, Ste
   constexpr int AST = 80;                        // LDS row stride of A (bank spread)
   constexpr int NW = 2 * NP;                     // waves
   constexpr int PW = CB / NP;                    // blocks per wave
-  static_assert(CB <= 32 && CB % NP == 0, "block maxima sit in lanes 16 h + k, two per lane");
+  constexpr int MR = (CB + 15) / 16;             // block maxima per lane
+  static_assert(CB <= 64 && CB % NP == 0, "block flags sit in one 64-lane ballot");
   const int i = blockIdx.z, g = blockIdx.y, ch = blockIdx.x;
   const int T = tab.T[i], NB = (T + BLOCK - 1) / BLOCK;
-  const int b0 = ch * CB;
-  if (b0 >= NB) return;
+  // chunk ch of nch: blocks [ch NB / nch, (ch + 1) NB / nch), at most CB
+  const int nch = tab.nch[i];
+  if (ch >= nch) return;
+  const int b0 = (int)((long long)ch * NB / nch);
   const size_t ig = (size_t)i * s.Hkv + g;
   const int G = s.G;
-  const int b1 = min(NB, b0 + CB);
+  const int b1 = (int)((long long)(ch + 1) * NB / nch);
   const int nblk = b1 - b0;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int hl = lane >> 4;                      // head of this lane in the MFMA output
@@ -70,16 +75,16 @@ __global__ __launch_bounds__(128 * NP) void k_decode_mixed(Shape s, Tier1 t, Ste
   // go out before the flags are used
   const int k16 = lane & 15;
   const size_t om = ((size_t)i * s.Hq + g * G + min(hl, G - 1)) * s.NBmax + b0;
-  const float m16v = w.m16[om + min(k16, nblk - 1)], mhv = w.mhat[om + min(k16, nblk - 1)];
-  float m16w = -INFINITY, mhw = -INFINITY;       // blocks 16 + k of a 32-block chunk
-  if constexpr (CB > 16) {
-    m16w = w.m16[om + min(k16 + 16, nblk - 1)];
-    mhw = w.mhat[om + min(k16 + 16, nblk - 1)];
+  float m16v[MR], mhv[MR];                       // blocks 16 r + k of the chunk
+#pragma unroll
+  for (int r = 0; r < MR; ++r) {
+    m16v[r] = w.m16[om + min(16 * r + k16, nblk - 1)];
+    mhv[r] = w.mhat[om + min(16 * r + k16, nblk - 1)];
   }
   const uint8_t uf = U[b0 + min(lane, nblk - 1)], vf = V[b0 + min(lane, nblk - 1)];
   // set once the flags are in: the chunk's U and V masks, and the chunk
   // reference per head (max over the chunk's blocks of the block maxima in
-  // use; lane 16 h + k holds head h's maxima of blocks b0 + k, b0 + 16 + k)
+  // use; lane 16 h + k holds head h's maxima of blocks b0 + 16 r + k)
   unsigned long long umask = 0ull, vmask = 0ull;
   float Mh[4];
   float acc[NTW];
@@ -228,9 +233,12 @@ __global__ __launch_bounds__(128 * NP) void k_decode_mixed(Shape s, Tier1 t, Ste
   umask = __ballot(lane < nblk && uf != 0);
   vmask = __ballot(lane < nblk && vf != 0);
   {
-    float bmv = (hl < G && k16 < nblk) ? (((umask >> k16) & 1ull) ? m16v : mhv) : -INFINITY;
-    if (CB > 16 && hl < G && k16 + 16 < nblk)
-      bmv = fmaxf(bmv, ((umask >> (k16 + 16)) & 1ull) ? m16w : mhw);
+    float bmv = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < MR; ++r) {
+      const int k = 16 * r + k16;
+      if (hl < G && k < nblk) bmv = fmaxf(bmv, ((umask >> k) & 1ull) ? m16v[r] : mhv[r]);
+    }
     const float bm = bfly_max<16>(bmv);
 #pragma unroll
     for (int h = 0; h < 4; ++h)
@@ -244,9 +252,9 @@ __global__ __launch_bounds__(128 * NP) void k_decode_mixed(Shape s, Tier1 t, Ste
     if (bb >= b1) break;
     if (!((vmask >> (bb - b0)) & 1ull)) body(st[q & 1], bb);
     __builtin_amdgcn_sched_barrier(0);
-    if (q + 2 < PW) {
-      fetch_vm(st[q & 1], min(bb + 2 * NP, b1 - 1));
-      fetch_sc(st[q & 1], min(bb + 2 * NP, b1 - 1), umask);
+    if (q + 2 < PW && bb + 2 * NP < b1) {       // (a shorter chunk loads nothing twice)
+      fetch_vm(st[q & 1], bb + 2 * NP);
+      fetch_sc(st[q & 1], bb + 2 * NP, umask);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -302,17 +310,47 @@ __global__ __launch_bounds__(128 * NP) void k_decode_mixed(Shape s, Tier1 t, Ste
   }
 }
 
-// Blocks per chunk of the mixed decode: MIX_CB (32, eight waves), or 8 or 16
-// (four waves) while a test has selected them (kvq_selftest_launch_shape).
-// Outputs round differently with the chunking; no decision depends on it.
+// Blocks per chunk of the mixed decode: at most MIX_CB (48, eight waves), or
+// 8 or 16 (four waves) while a test has selected them
+// (kvq_selftest_launch_shape).  Outputs round differently with the chunking;
+// no decision depends on it.
 static int g_mix_cb = MIX_CB;
 void set_mix_chunk_blocks(int cb) { g_mix_cb = (cb == 8 || cb == 16) ? cb : MIX_CB; }
 int mix_chunk_blocks() { return g_mix_cb; }
 
-hipError_t launch_decode(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,
+// Chunks per sequence: at least ceil(NB / cb) (a chunk holds at most cb
+// blocks), cut smaller until the call's workgroups are a multiple of the
+// compute units, so that every unit gets the same number of equal chunks
+// (with a few more workgroups than a multiple, some units run one chunk more
+// than the others: measured 26.4 us against 22.4 us for 2049 against 2048
+// blocks at batch 1 with 32-block chunks); at most one chunk per DEC_CB
+// blocks (the partials buffer).  A pure function of the call, so the combine
+// finds the same chunks.
+static void mix_chunk_counts(const Shape &s, SeqTab &tab, int cb) {
+  const long long ncu = std::max(s.ncu, 1);
+  long long total = 0;
+  for (int i = 0; i < tab.n; ++i)
+    total += (long long)s.Hkv * ((tab.nbc[i + 1] - tab.nbc[i] + cb - 1) / cb);
+  const long long want = (total + ncu - 1) / ncu * ncu;
+  for (int i = 0; i < tab.n; ++i) {
+    const int NB = tab.nbc[i + 1] - tab.nbc[i];
+    const long long base = (NB + cb - 1) / cb;
+    const long long hi = std::max(1, (NB + DEC_CB - 1) / DEC_CB);
+    long long n = total > 0 ? base * want / total : base;
+    n = std::min(std::max(n, base), std::max(hi, base));
+    tab.nch[i] = (int)n;
+  }
+}
+
+hipError_t launch_decode(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab0,
                          int layer, int maxNB, hipStream_t st) {
+  (void)maxNB;
   const int cb = g_mix_cb;
-  dim3 grid((maxNB + cb - 1) / cb, s.Hkv, tab.n);
+  SeqTab tab = tab0;
+  mix_chunk_counts(s, tab, cb);
+  int xmax = 1;
+  for (int i = 0; i < tab.n; ++i) xmax = std::max(xmax, tab.nch[i]);
+  dim3 grid(xmax, s.Hkv, tab.n);
   if (cb == 8) {
     if (s.d == 128)
       return launch_k(k_decode_mixed<128, 8, 2>, grid, dim3(256), 0, st, s, t, w, tab, layer);
@@ -323,10 +361,22 @@ hipError_t launch_decode(const Shape &s, const Tier1 &t, const Step &w, const Se
       return launch_k(k_decode_mixed<128, 16, 2>, grid, dim3(256), 0, st, s, t, w, tab, layer);
     return launch_k(k_decode_mixed<64, 16, 2>, grid, dim3(256), 0, st, s, t, w, tab, layer);
   }
-  static_assert(MIX_CB == 32, "the default chunk is the eight-wave kernel");
+  // eight waves; the 32-block build when every chunk fits it (its fully
+  // unrolled block loop is shorter: 22.2 against 24.2 us at batch 1, 128K)
+  static_assert(MIX_CB == 48, "the default chunk is the eight-wave kernel");
+  int most = 0;
+  for (int i = 0; i < tab.n; ++i) {
+    const int NB = tab.nbc[i + 1] - tab.nbc[i];
+    most = std::max(most, (NB + tab.nch[i] - 1) / tab.nch[i]);
+  }
+  if (most <= 32) {
+    if (s.d == 128)
+      return launch_k(k_decode_mixed<128, 32, 4>, grid, dim3(512), 0, st, s, t, w, tab, layer);
+    return launch_k(k_decode_mixed<64, 32, 4>, grid, dim3(512), 0, st, s, t, w, tab, layer);
+  }
   if (s.d == 128)
-    return launch_k(k_decode_mixed<128, 32, 4>, grid, dim3(512), 0, st, s, t, w, tab, layer);
-  return launch_k(k_decode_mixed<64, 32, 4>, grid, dim3(512), 0, st, s, t, w, tab, layer);
+    return launch_k(k_decode_mixed<128, 48, 4>, grid, dim3(512), 0, st, s, t, w, tab, layer);
+  return launch_k(k_decode_mixed<64, 48, 4>, grid, dim3(512), 0, st, s, t, w, tab, layer);
 }
 
 // Merges the chunk partials of each (sequence, query head): mode 0 reads the
@@ -370,7 +420,7 @@ __global__ __launch_bounds__(256) void k_combine(Shape s, Step w, SeqTab tab, fl
   }
   const bool dense = mode == 2 || (mode == 0 && w.hlevel[(size_t)i * s.Hq + hq] >= 3);
   const int cb = dense ? DEC_CB : mix_cb;
-  const int NB = (tab.T[i] + BLOCK - 1) / BLOCK, nch = (NB + cb - 1) / cb;
+  const int NB = (tab.T[i] + BLOCK - 1) / BLOCK, nch = dense ? (NB + cb - 1) / cb : tab.nch[i];
   const float *part = (dense ? w.partd : w.part) + (((size_t)i * s.Hkv + g) * s.nchmax * G + h) * (D + 2);
   const size_t stride = (size_t)G * (D + 2);
   const int parts = 256 / CQ, c = cq * CQ + threadIdx.x % CQ, pp = threadIdx.x / CQ;
@@ -443,8 +493,10 @@ __global__ __launch_bounds__(256) void k_combine(Shape s, Step w, SeqTab tab, fl
   }
 }
 
-hipError_t launch_combine(const Shape &s, const Step &w, const SeqTab &tab, float *out, int mode,
+hipError_t launch_combine(const Shape &s, const Step &w, const SeqTab &tab0, float *out, int mode,
                           float *e_key, float *e_val, int8_t *level, hipStream_t st) {
+  SeqTab tab = tab0;
+  if (mode != 2) mix_chunk_counts(s, tab, g_mix_cb);
   return launch_k(k_combine, dim3(s.Hq, tab.n, 4), dim3(256), 0, st, s, w, tab, out, mode, e_key,
                   e_val, level, g_mix_cb);
 }

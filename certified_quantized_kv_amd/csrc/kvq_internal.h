@@ -17,7 +17,7 @@ namespace kvq {
 constexpr int MAX_CALL = KVQ_MAX_CALL_SEQS;
 constexpr int MAX_NB = 4096;        // blocks per sequence (262144 tokens)
 constexpr int DEC_CB = 8;           // blocks per split-K chunk of the dense decode kernels
-constexpr int MIX_CB = 32;          // blocks per split-K chunk of the mixed decode
+constexpr int MIX_CB = 48;          // most blocks per split-K chunk of the mixed decode
 static_assert(MIX_CB >= DEC_CB, "chunk partials are sized for DEC_CB");
 
 // Tier 1, per unit (device memory):
@@ -80,6 +80,7 @@ struct SeqTab {
   int slot[MAX_CALL];
   int T[MAX_CALL];
   int nbc[MAX_CALL + 1];            // nbc[i] = blocks of the sequences before i
+  int nch[MAX_CALL];                // split-K chunks of sequence i in the mixed decode
 };
 
 struct Shape {

@@ -315,8 +315,10 @@ kvq_status kvq_selftest_sort(const uint64_t *keys, int64_t n, uint64_t *out, int
 /* Launch shapes of later calls in this process, for determinism tests:
  * score_wgs > 0 caps the workgroups of the INT8 scoring pass (which changes
  * which wave scores which block and which blocks share a batch of channel
- * sums), 0 restores the default; mix_blocks = 8, 16 or 32 sets the blocks
- * per split-K chunk of the mixed decode (0 = default 32).  Decisions must not
+ * sums), 0 restores the default; mix_blocks = 8, 16 or 48 sets the most
+ * blocks per split-K chunk of the mixed decode (0 = default 48; chunks are
+ * cut smaller until the workgroups are a multiple of the compute units).
+ * Decisions must not
  * change; outputs differ only by rounding.  Not thread-safe; KVQ_EINVAL on
  * other values.  For tests. */
 kvq_status kvq_selftest_launch_shape(int32_t score_wgs, int32_t mix_blocks);

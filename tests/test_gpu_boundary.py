@@ -108,13 +108,13 @@ def test_launch_shapes_do_not_change_decisions(env):
         rows.append((K, V, S.query(w, 0, s, 0), None))
     case = Case("launch-shapes", w.Hq, w.Hkv, w.d, rows, max_tokens=w.max_tokens)
     ref = run_oracle(orc, case)
-    shapes = [(0, 0), (3, 8), (1, 16), (17, 8), (5, 32)]
+    shapes = [(0, 0), (3, 8), (1, 16), (17, 8), (5, 48)]
     runs = []
     try:
         for sw, mb in shapes:
             kvq.set_launch_shape(sw, mb)
             log(f"[boundary] launch shape: scoring workgroups {sw or 'default'}, "
-                f"mixed chunk {mb or 32} blocks")
+                f"mixed chunk {mb or 48} blocks")
             g = run_gpu(kvq, torch, case)
             compare(case, g, ref)
             runs.append(g)
