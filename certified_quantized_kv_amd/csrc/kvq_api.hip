@@ -850,7 +850,8 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
     // waits for them (ev_spec), so no copy writes a buffer they still read.
     if (!ctx->th.force_dense) {
       tm.open(TC_DECODE);
-      HIPCK(ctx, launch_decode(s, ctx->t, w, tab, layer, maxNB, st));
+      // (the first round only evaluates: no value is promoted yet)
+      HIPCK(ctx, launch_decode(s, ctx->t, w, tab, layer, !first, st));
       tm.open(TC_COMBINE);
       // mixed partials for every head: the result is kept only if no head
       // reached rung 3
@@ -929,7 +930,7 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
     }
     if (!ctx->th.force_dense) {        // forced: every head is at level 4 (dense partials)
       tm.open(TC_DECODE);
-      HIPCK(ctx, launch_decode(s, ctx->t, w, tab, layer, maxNB, st));
+      HIPCK(ctx, launch_decode(s, ctx->t, w, tab, layer, true, st));
     }
     tm.open(TC_COMBINE);
     HIPCK(ctx, launch_combine(s, w, tab, out, 0, maybe_dense ? nullptr : e_key,
@@ -1005,7 +1006,7 @@ kvq_status kvq_decode_naive(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_
   // empty U and V: INT8 scores and INT4 values for every block
   const float C = (float)(1.4426950408889634 / sqrt((double)s.d));
   HIPCK(ctx, launch_score_int8(s, ctx->t, w, tab, layer, (const uint16_t *)q, C, st));
-  HIPCK(ctx, launch_decode(s, ctx->t, w, tab, layer, maxNB, st));
+  HIPCK(ctx, launch_decode(s, ctx->t, w, tab, layer, false, st));
   HIPCK(ctx, launch_combine(s, w, tab, out, 1, nullptr, nullptr, nullptr, st));
   return KVQ_OK;
 }

@@ -40,7 +40,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // Scores, value metadata and codes of a wave's next block load while the
 // current one is accumulated; the value tiles are read once per step, through
 // non-temporal loads.
-template <int D, int CB, int NP>
+// FV: blocks with FP16 values may occur (a step whose controller promoted
+// values); without it the kernel has no FP16-value path and none of its LDS.
+template <int D, int CB, int NP, bool FV>
 __global__ __launch_bounds__(128 * NP) void k_decode_mixed(Shape s, Tier1 t, Step w, SeqTab tab, int layer) {
   constexpr int NT = D / 16;                     // 16-channel tiles
   constexpr int NG = D / VGROUP;                 // value groups (two tiles each)
@@ -68,7 +70,8 @@ __global__ __launch_bounds__(128 * NP) void k_decode_mixed(Shape s, Tier1 t, Ste
   const uint8_t *V = w.V + ig * s.NBmax;
 
   __shared__ __align__(16) int8_t As[NW][NGW][16 * AST];
-  __shared__ float pv[NW][4][BLOCK];             // p of an FP16-value block, per wave
+  __shared__ __align__(16) float pt[FV ? NW : 1][FV ? BLOCK : 1][4]; // p of an FP16-value block per token
+  __shared__ float fsum[FV ? NW : 1][4][FV ? D : 1];                  // the FP16-value blocks' sums per wave
   __shared__ float sl[NW][4];
   // the chunk's block flags and both kinds of block maxima load at once
   // (no load waits on another); the first blocks' value metadata and codes
@@ -196,26 +199,55 @@ __global__ __launch_bounds__(128 * NP) void k_decode_mixed(Shape s, Tier1 t, Ste
     }
     wave_lds_sync();
   };
-  // FP16 values of a promoted block (rung 2): plain fp32 accumulation
+  // FP16 values of a promoted block (rung 2): plain fp32 accumulation.  The
+  // wave forms p for the block's 64 tokens (lane = token) like the quantized
+  // path, then takes its half of the tokens with lane = CPL consecutive
+  // channels, so each token's values are one coalesced row load, and keeps
+  // per-head sums of its own (added to the chunk's sums at the end)
+  constexpr int CPL = D / 64;                    // channels per lane on this path
+  float fa[4][CPL];
+#pragma unroll
+  for (int h = 0; h < 4; ++h)
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) fa[h][c] = 0.0f;
   auto body_fp16 = [&](int b) {
+    if constexpr (!FV) return;
     const int tk = min(b * BLOCK + lane, T - 1);
     const bool valid = b * BLOCK + lane < T;
     const bool up = (umask >> (b - b0)) & 1ull;
     const float *src = (up ? w.sp : w.shat) + ((size_t)i * s.Hq + g * G) * s.Tmax + tk;
+    float p4[4];
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
       const float x = src[(size_t)min(h, G - 1) * s.Tmax];
-      const float p = (valid && h < G) ? __builtin_amdgcn_exp2f(x - Mh[h]) : 0.0f;
-      lsum[h] += p;
-      pv[wave][h][lane] = p;
+      p4[h] = (valid && h < G) ? __builtin_amdgcn_exp2f(x - Mh[h]) : 0.0f;
+      lsum[h] += p4[h];
     }
+    *(float4 *)&pt[wave][lane][0] = make_float4(p4[0], p4[1], p4[2], p4[3]);
     wave_lds_sync();
-    const int n = min(BLOCK, T - b * BLOCK);
-    for (int r = 0; r < n; ++r) {
-      const float pr = (hl < G) ? pv[wave][hl][r] : 0.0f;
-      const uint16_t *row = sv + ((size_t)b * BLOCK + r) * D + half * NTW * 16 + (lane & 15);
+    // rows past T carry p = 0 and load row T - 1 (the staging past T is not
+    // written); sixteen rows' loads go out together
+    const int nlast = min(BLOCK, T - b * BLOCK) - 1;
+    const uint16_t *col = sv + (size_t)b * BLOCK * D + CPL * lane;
+    for (int r0 = BLOCK / 2 * half; r0 < BLOCK / 2 * (half + 1); r0 += 16) {
+      uint32_t xr[16];
 #pragma unroll
-      for (int k = 0; k < NTW; ++k) acc[k] = fmaf(pr, h2f(row[16 * k]), acc[k]);
+      for (int j = 0; j < 16; ++j) {
+        const uint16_t *e = col + (size_t)min(r0 + j, nlast) * D;
+        xr[j] = CPL == 2 ? *(const uint32_t *)e : (uint32_t)*e;
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float4 pr = *(const float4 *)&pt[wave][r0 + j][0];
+        const float pq[4] = {pr.x, pr.y, pr.z, pr.w};
+        float v[CPL];
+        v[0] = h2f((uint16_t)(xr[j] & 0xffffu));
+        if constexpr (CPL == 2) v[CPL - 1] = h2f((uint16_t)(xr[j] >> 16));
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) fa[h][c] = fmaf(pq[h], v[c], fa[h][c]);
+      }
     }
     wave_lds_sync();
   };
@@ -231,7 +263,7 @@ __global__ __launch_bounds__(128 * NP) void k_decode_mixed(Shape s, Tier1 t, Ste
   fetch_vm(st[0], min(b0 + pair, b1 - 1));
   if (PW > 1) fetch_vm(st[1], min(b0 + pair + NP, b1 - 1));
   umask = __ballot(lane < nblk && uf != 0);
-  vmask = __ballot(lane < nblk && vf != 0);
+  vmask = FV ? __ballot(lane < nblk && vf != 0) : 0ull;
   {
     float bmv = -INFINITY;
 #pragma unroll
@@ -258,9 +290,16 @@ __global__ __launch_bounds__(128 * NP) void k_decode_mixed(Shape s, Tier1 t, Ste
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  if (vmask)
+  if (FV && vmask) {
     for (int bb = b0 + pair; bb < b1; bb += NP)
       if ((vmask >> (bb - b0)) & 1ull) body_fp16(bb);
+    if constexpr (FV) {
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) fsum[wave][h][CPL * lane + c] = fa[h][c];
+    }
+  }
 
   // offset terms: head h, group j summed over the wave's tokens; channel
   // tile k belongs to group k / 2
@@ -295,6 +334,12 @@ __global__ __launch_bounds__(128 * NP) void k_decode_mixed(Shape s, Tier1 t, Ste
       float v = red[(hf * NTW + kk) * 64 + ln];
 #pragma unroll
       for (int p = 1; p < NP; ++p) v += red[((2 * p + hf) * NTW + kk) * 64 + ln];
+      if (FV && vmask) {                         // and every wave's FP16-value sums
+        if constexpr (FV) {
+#pragma unroll
+          for (int q = 0; q < NW; ++q) v += fsum[q][h][k * 16 + (ln & 15)];
+        }
+      }
       float *part = w.part + ((ig * s.nchmax + ch) * G + h) * (size_t)(D + 2);
       part[k * 16 + (ln & 15)] = v;
     }
@@ -342,41 +387,46 @@ static void mix_chunk_counts(const Shape &s, SeqTab &tab, int cb) {
   }
 }
 
-hipError_t launch_decode(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab0,
-                         int layer, int maxNB, hipStream_t st) {
-  (void)maxNB;
-  const int cb = g_mix_cb;
-  SeqTab tab = tab0;
-  mix_chunk_counts(s, tab, cb);
-  int xmax = 1;
-  for (int i = 0; i < tab.n; ++i) xmax = std::max(xmax, tab.nch[i]);
-  dim3 grid(xmax, s.Hkv, tab.n);
+template <bool FV>
+static hipError_t launch_decode_fv(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,
+                                   dim3 grid, int cb, int most, int layer, hipStream_t st) {
   if (cb == 8) {
     if (s.d == 128)
-      return launch_k(k_decode_mixed<128, 8, 2>, grid, dim3(256), 0, st, s, t, w, tab, layer);
-    return launch_k(k_decode_mixed<64, 8, 2>, grid, dim3(256), 0, st, s, t, w, tab, layer);
+      return launch_k(k_decode_mixed<128, 8, 2, FV>, grid, dim3(256), 0, st, s, t, w, tab, layer);
+    return launch_k(k_decode_mixed<64, 8, 2, FV>, grid, dim3(256), 0, st, s, t, w, tab, layer);
   }
   if (cb == 16) {
     if (s.d == 128)
-      return launch_k(k_decode_mixed<128, 16, 2>, grid, dim3(256), 0, st, s, t, w, tab, layer);
-    return launch_k(k_decode_mixed<64, 16, 2>, grid, dim3(256), 0, st, s, t, w, tab, layer);
+      return launch_k(k_decode_mixed<128, 16, 2, FV>, grid, dim3(256), 0, st, s, t, w, tab, layer);
+    return launch_k(k_decode_mixed<64, 16, 2, FV>, grid, dim3(256), 0, st, s, t, w, tab, layer);
   }
   // eight waves; the 32-block build when every chunk fits it (its fully
   // unrolled block loop is shorter: 22.2 against 24.2 us at batch 1, 128K)
   static_assert(MIX_CB == 48, "the default chunk is the eight-wave kernel");
-  int most = 0;
-  for (int i = 0; i < tab.n; ++i) {
-    const int NB = tab.nbc[i + 1] - tab.nbc[i];
-    most = std::max(most, (NB + tab.nch[i] - 1) / tab.nch[i]);
-  }
   if (most <= 32) {
     if (s.d == 128)
-      return launch_k(k_decode_mixed<128, 32, 4>, grid, dim3(512), 0, st, s, t, w, tab, layer);
-    return launch_k(k_decode_mixed<64, 32, 4>, grid, dim3(512), 0, st, s, t, w, tab, layer);
+      return launch_k(k_decode_mixed<128, 32, 4, FV>, grid, dim3(512), 0, st, s, t, w, tab, layer);
+    return launch_k(k_decode_mixed<64, 32, 4, FV>, grid, dim3(512), 0, st, s, t, w, tab, layer);
   }
   if (s.d == 128)
-    return launch_k(k_decode_mixed<128, 48, 4>, grid, dim3(512), 0, st, s, t, w, tab, layer);
-  return launch_k(k_decode_mixed<64, 48, 4>, grid, dim3(512), 0, st, s, t, w, tab, layer);
+    return launch_k(k_decode_mixed<128, 48, 4, FV>, grid, dim3(512), 0, st, s, t, w, tab, layer);
+  return launch_k(k_decode_mixed<64, 48, 4, FV>, grid, dim3(512), 0, st, s, t, w, tab, layer);
+}
+
+hipError_t launch_decode(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab0,
+                         int layer, bool values, hipStream_t st) {
+  const int cb = g_mix_cb;
+  SeqTab tab = tab0;
+  mix_chunk_counts(s, tab, cb);
+  int xmax = 1, most = 0;
+  for (int i = 0; i < tab.n; ++i) {
+    const int NB = tab.nbc[i + 1] - tab.nbc[i];
+    xmax = std::max(xmax, tab.nch[i]);
+    most = std::max(most, (NB + tab.nch[i] - 1) / tab.nch[i]);
+  }
+  const dim3 grid(xmax, s.Hkv, tab.n);
+  return values ? launch_decode_fv<true>(s, t, w, tab, grid, cb, most, layer, st)
+                : launch_decode_fv<false>(s, t, w, tab, grid, cb, most, layer, st);
 }
 
 // Merges the chunk partials of each (sequence, query head): mode 0 reads the

@@ -191,7 +191,7 @@ hipError_t launch_decide(const Shape &s, const Tier1 &t, const Step &w, const Se
 hipError_t launch_finalize(const Shape &s, const Step &w, const SeqTab &tab, const Thresh &th,
                            float *e_key, float *e_val, int8_t *level, hipStream_t st);
 hipError_t launch_decode(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,
-                         int layer, int maxNB, hipStream_t st);
+                         int layer, bool values, hipStream_t st);
 hipError_t launch_dense_staged(const Shape &s, const Step &w, const SeqTab &tab, int layer,
                                const uint16_t *q16, int maxNB, hipStream_t st);
 // mode 0: partials chosen by each head's level; 1: mixed partials; 2: dense;
