@@ -133,6 +133,11 @@ __global__ __launch_bounds__(128 * NP) void k_decode_mixed(Shape s, Tier1 t, Ste
     for (int h = 0; h < 4; ++h) st.x[h] = src[(size_t)min(h, G - 1) * s.Tmax];
   };
   // quantized values: p*s as fixed point against the INT4 codes
+  // byte selectors of the quad transpose (v_perm: bytes 0-3 from the second
+  // operand, 4-7 from the first): lanes with bit 0 clear take [x0 y0 x2 y2],
+  // set [y1 x1 y3 x3]; then bit 1 clear [x0 x1 z0 z1], set [z2 z3 x2 x3]
+  const uint32_t qsel1 = (lane & 1) ? 0x03070105u : 0x06020400u;
+  const uint32_t qsel2 = (lane & 2) ? 0x03020706u : 0x05040100u;
   auto body = [&](const Stage &cur, int b) {
     const bool valid = b * BLOCK + lane < T;
     float sc[NGW], of[NGW];
@@ -171,11 +176,17 @@ __global__ __launch_bounds__(128 * NP) void k_decode_mixed(Shape s, Tier1 t, Ste
         offacc[h][j] = fmaf(p[h], of[j], offacc[h][j]);
         // rint(p s 2^-e) + 0x808080 in one rounding (the sum stays below
         // 2^24, where fp32 spacing is 1); the XOR leaves three signed bytes
-        // L0 + 2^8 L1 + 2^16 L2 = rint(p s 2^-e), each in [-128, 127]
+        // L0 + 2^8 L1 + 2^16 L2 = rint(p s 2^-e), each in [-128, 127], and a
+        // zero fourth byte
         const uint32_t Bv = (uint32_t)fmaf(p[h], sce, 8421504.0f) ^ 0x808080u;
-        Aj[(h * 4 + 0) * AST + lane] = (int8_t)Bv;
-        Aj[(h * 4 + 1) * AST + lane] = (int8_t)(Bv >> 8);
-        Aj[(h * 4 + 2) * AST + lane] = (int8_t)(Bv >> 16);
+        // 4 x 4 byte transpose inside each quad of lanes (tokens 4 m .. 4 m + 3):
+        // lane 4 m + l then holds limb l of the four tokens, one dword of row
+        // 4 h + l (row 4 h + 3 gets the zero bytes)
+        const uint32_t y1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)Bv, 0xB1, 0xf, 0xf, false);
+        const uint32_t x1 = __builtin_amdgcn_perm(y1, Bv, qsel1);
+        const uint32_t y2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)x1, 0x4E, 0xf, 0xf, false);
+        const uint32_t x2 = __builtin_amdgcn_perm(y2, x1, qsel2);
+        *(uint32_t *)&Aj[(h * 4 + (lane & 3)) * AST + (lane & ~3)] = x2;
       }
     }
     wave_lds_sync();
@@ -251,11 +262,6 @@ __global__ __launch_bounds__(128 * NP) void k_decode_mixed(Shape s, Tier1 t, Ste
     }
     wave_lds_sync();
   };
-  // rows 4 h + 3 of A stay zero (three limbs per head)
-#pragma unroll
-  for (int j = 0; j < NGW; ++j)
-#pragma unroll
-    for (int h = 0; h < 4; ++h) As[wave][j][(h * 4 + 3) * AST + lane] = 0;
   // fully unrolled over the wave's blocks, so the two stages keep fixed
   // registers and each wait covers only the older stage's loads; blocks with
   // FP16 values are skipped here and accumulated afterwards
