@@ -257,7 +257,7 @@ __device__ void value_rung(const Shape &s, const Tier1 &t, const Step &w, const 
   __syncthreads();
   sort_desc_u64<CTL_NT>(keys, NB, n2);
   // prefix sums of the sorted contributions: thread t owns [t*per, (t+1)*per)
-  const int per = (n2 + CTL_NT - 1) / CTL_NT;
+  const int per = (NB + CTL_NT - 1) / CTL_NT;
   const int p0 = threadIdx.x * per;
   unsigned long long own = 0ull;
   for (int k = 0; k < per; ++k)

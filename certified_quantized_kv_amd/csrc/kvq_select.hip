@@ -67,7 +67,7 @@ __global__ __launch_bounds__(SEL_NT) void k_select(Shape s, Step w, SeqTab tab, 
 
   // pi, then prefix sums of the sorted weights: thread t owns positions
   // [t*per, (t+1)*per)
-  const int per = (n2 + SEL_NT - 1) / SEL_NT;
+  const int per = (NB + SEL_NT - 1) / SEL_NT;
   const int p0 = threadIdx.x * per;
   unsigned long long own = 0ull;
   for (int k = 0; k < per; ++k) {
