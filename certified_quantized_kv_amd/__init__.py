@@ -44,7 +44,7 @@ class StepStats(ctypes.Structure):
                 ("ms_copy", ctypes.c_float), ("ms_decode", ctypes.c_float),
                 ("ms_dense", ctypes.c_float), ("ms_total", ctypes.c_float),
                 ("ms_combine", ctypes.c_float), ("ms_misc", ctypes.c_float),
-                ("cached_key_blocks", I64)]
+                ("cached_key_blocks", I64), ("scores_deferred", I32)]
 
     def as_dict(self):
         d = {k: getattr(self, k) for k, _ in self._fields_}
@@ -57,6 +57,7 @@ FLAG_TIMING = 2
 FLAG_RESIDENT_KEYS = 4
 FLAG_FP16_VALUES = 8
 FLAG_KEY_CACHE = 16
+FLAG_ALL_SCORES = 32
 
 TR = dict(shat=1, sp=2, mhat=3, Lhat=4, delta=5, m16=6, L16=7, What=8, pi=9, Wt=10, W16=11,
           k0=12, ssize=13, ssd=14, ekey64=15, eval64=16, hflags=17, U=18, V=19, vh=20)
@@ -90,6 +91,7 @@ _SIGS = {
     "kvq_selftest_sort": (I32, [P, I64, P, P, P]),
     "kvq_dense_decode_noalloc": (I32, [I32, I32, I32, I32, I32, P, P, P, P, P, P]),
     "kvq_selftest_launch_shape": (I32, [I32, I32]),
+    "kvq_selftest_defer_scores": (I32, [I32]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -204,6 +206,15 @@ def set_launch_shape(score_wgs=0, mix_blocks=0):
         raise KvqError(st, "kvq_selftest_launch_shape")
 
 
+def set_defer_scores(ppm=-1):
+    """Test hook (kvq_selftest_defer_scores): the U fraction (ppm) of a
+    layer's last step from which a step stores the INT8 scores of the blocks
+    outside U only; 0 = every step that reads its unions back, -1 = default."""
+    st = _lib.kvq_selftest_defer_scores(int(ppm))
+    if st != 0:
+        raise KvqError(st, "kvq_selftest_defer_scores")
+
+
 def sort_desc(keys):
     """The library's workgroup sort of block keys (test hook): keys = int64 CUDA
     tensor of n distinct nonzero keys read as unsigned, 1 <= n <= 4096.
@@ -226,7 +237,7 @@ class Context:
     def __init__(self, n_layers, max_batch, n_q_heads, n_kv_heads, head_dim, max_tokens,
                  tau_cov_ppm=995_000, eps_key=1e-3, v_tol=0.25, rho_min_ppm=900_000,
                  widen_rounds=2, layer_frac_ppm=500_000, force_dense=False, timing=False,
-                 resident_keys=False, fp16_values=False, key_cache_blocks=0):
+                 resident_keys=False, fp16_values=False, key_cache_blocks=0, all_scores=False):
         cfg = Config()
         _lib.kvq_default_config(ctypes.byref(cfg), n_layers, max_batch, n_q_heads, n_kv_heads,
                                 head_dim, max_tokens)
@@ -239,7 +250,8 @@ class Context:
         cfg.flags = ((FLAG_FORCE_DENSE if force_dense else 0) | (FLAG_TIMING if timing else 0) |
                      (FLAG_RESIDENT_KEYS if resident_keys else 0) |
                      (FLAG_FP16_VALUES if fp16_values else 0) |
-                     (FLAG_KEY_CACHE if key_cache_blocks > 0 else 0))
+                     (FLAG_KEY_CACHE if key_cache_blocks > 0 else 0) |
+                     (FLAG_ALL_SCORES if all_scores else 0))
         cfg.key_cache_blocks = key_cache_blocks
         self.cfg = cfg
         self._ctx = ctypes.c_void_p()

@@ -121,6 +121,8 @@ struct kvq_ctx {
   hipEvent_t ev_tot[2] = {};
   unsigned long long *plan_host = nullptr;
   uint8_t *u_host = nullptr;   // the call's group unions U after the selection
+  uint32_t *rlist_host = nullptr;  // units outside U whose ŝ′ a deferred step rescores
+  std::vector<int32_t> uppm;   // [layer] blocks in U at the last read, parts per million
   size_t plan_cap = 0;
   size_t plan_words = 0;
   int last_n = 0, last_layer = -1;
@@ -164,6 +166,7 @@ void free_all(kvq_ctx *c) {
   if (c->t2v_host) (void)hipHostFree(c->t2v_host);
   if (c->plan_host) (void)hipHostFree(c->plan_host);
   if (c->u_host) (void)hipHostFree(c->u_host);
+  if (c->rlist_host) (void)hipHostFree(c->rlist_host);
   if (c->kc.list_host) (void)hipHostFree(c->kc.list_host);
   if (c->cstream) (void)hipStreamDestroy(c->cstream);
   if (c->ev_start) (void)hipEventDestroy(c->ev_start);
@@ -365,6 +368,7 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out) {
   DA(t.openk, NU * 2 * BLOCK * d * 2);
   DA(w.qp, B * Hq * d * 4);
   DA(w.shat, B * Hq * Tm * 4);
+  DA(w.rlist, B * Hkv * NBm * 4);
   DA(w.sp, B * Hq * Tm * 4);
   DA(w.mhat, B * Hq * NBm * 4);
   DA(w.delta, B * Hq * NBm * 4);
@@ -426,6 +430,9 @@ kvq_status kvq_create(const kvq_config *cfg, kvq_ctx **out) {
   x->plan_cap = 4096;
   if (e == hipSuccess) e = hipHostMalloc((void **)&x->plan_host, (4 + x->plan_cap) * 8, 0);
   if (e == hipSuccess) e = hipHostMalloc((void **)&x->u_host, (size_t)c.max_batch * c.n_kv_heads * NBm, 0);
+  if (e == hipSuccess)
+    e = hipHostMalloc((void **)&x->rlist_host, (size_t)c.max_batch * c.n_kv_heads * NBm * 4, 0);
+  x->uppm.assign((size_t)c.n_layers, 0);
   if (e == hipSuccess && kcache) {
     e = hipHostMalloc((void **)&x->kc.list_host, 2 * x->kc.cap * 2 * 4, 0);
     KeyCache &kc = x->kc;
@@ -598,7 +605,7 @@ kvq_status read_plan(kvq_ctx *c, hipStream_t st, Plan &p) {
 // After the selection: the group unions U of the call's sequences come back
 // (one copy on the step's stream), and the plan's key entries are their runs
 // of consecutive blocks, one entry per run (the layout of the device plan).
-kvq_status read_union(kvq_ctx *c, hipStream_t st, const SeqTab &tab, Plan &p) {
+kvq_status read_union(kvq_ctx *c, hipStream_t st, const SeqTab &tab, Plan &p, int64_t &ublocks) {
   const Shape &s = c->s;
   const size_t rows = (size_t)tab.n * s.Hkv;
   HIPCK(c, hipMemcpyAsync(c->u_host, c->w.U, rows * s.NBmax, hipMemcpyDeviceToHost, st));
@@ -640,7 +647,40 @@ kvq_status read_union(kvq_ctx *c, hipStream_t st, const SeqTab &tab, Plan &p) {
     }
   }
   p.nk = (int64_t)p.ent.size();
+  ublocks = 0;
+  for (const unsigned long long e : p.ent) ublocks += (int64_t)(e & 0xffffu);
   return KVQ_OK;
+}
+
+// U fraction (ppm) of a layer's last step from which the next step defers
+// the INT8 scores (kvq_selftest_defer_scores changes it).
+constexpr int32_t DEFER_PPM = 750000;
+static int32_t g_defer_ppm = DEFER_PPM;
+static_assert((int64_t)MAX_CALL * 128 <= 65536 && MAX_NB <= 65536, "rescore entries are ig << 16 | block");
+
+// The call's units outside U (ig << 16 | block), from the unions read back.
+int outside_union(kvq_ctx *c, const SeqTab &tab) {
+  const Shape &s = c->s;
+  int n = 0;
+  for (int i = 0; i < tab.n; ++i) {
+    const int NB = tab.nbc[i + 1] - tab.nbc[i];
+    for (int g = 0; g < s.Hkv; ++g) {
+      const size_t ig = (size_t)i * s.Hkv + g;
+      const uint8_t *u = c->u_host + ig * s.NBmax;
+      for (int b = 0; b < NB; ++b) {
+        if (b + 8 <= NB && (b & 7) == 0) {
+          uint64_t x;
+          memcpy(&x, u + b, 8);
+          if (x == 0x0101010101010101ull) {
+            b += 7;
+            continue;
+          }
+        }
+        if (!u[b]) c->rlist_host[n++] = (uint32_t)(ig << 16) | (uint32_t)b;
+      }
+    }
+  }
+  return n;
 }
 
 // Issues the copies of a plan on the copy stream; returns bytes and blocks.
@@ -794,19 +834,39 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
   HIPCK(ctx, hipEventRecord(ctx->ev_start, st));
   HIPCK(ctx, hipStreamWaitEvent(ctx->cstream, ctx->ev_start, 0));
 
+  // with resident keys no copy depends on the selection, so the host reads
+  // the unions only for the statistics
+  const bool read_u = !s.kres || stats;
+  // The INT8 scores ŝ′ are read later only for blocks outside U.  When the
+  // last step at this layer put at least three quarters of the blocks in U,
+  // the pass stores none and the blocks outside U are rescored after the
+  // selection (a written byte costs about four read bytes here); otherwise,
+  // or when the unions are not read back, the pass stores them all.
+  const bool defer = read_u && !(ctx->cfg.flags & KVQ_FLAG_ALL_SCORES) &&
+                     ctx->uppm[(size_t)layer] >= g_defer_ppm;
   tm.open(TC_SCORE8);   // INT8 scores, with the step set-up (q', flags cleared)
-  HIPCK(ctx, launch_score_int8(s, ctx->t, w, tab, layer, (const uint16_t *)q, C, st));
+  HIPCK(ctx, launch_score_int8(s, ctx->t, w, tab, layer, (const uint16_t *)q, C, !defer, st));
   tm.open(TC_SELECT);
   HIPCK(ctx, launch_select(s, w, tab, ctx->th.tau_ppm, maxNB, st));
   tm.close();
-  // with resident keys no copy depends on the selection, so the host reads
-  // the unions only for the statistics
   Plan plan;
   kvq_status rs = KVQ_OK;
-  if (!s.kres || stats) {
-    rs = read_union(ctx, st, tab, plan);
+  if (read_u) {
+    int64_t ublocks = 0;
+    rs = read_union(ctx, st, tab, plan, ublocks);
     if (rs != KVQ_OK) return rs;
     ++syncs;
+    const int64_t all = (int64_t)tab.nbc[n] * s.Hkv;
+    ctx->uppm[(size_t)layer] = all > 0 ? (int32_t)(ublocks * 1000000 / all) : 0;
+    if (defer) {
+      const int nr = outside_union(ctx, tab);
+      if (nr > 0) {
+        HIPCK(ctx, hipMemcpyAsync(w.rlist, ctx->rlist_host, (size_t)nr * 4, hipMemcpyHostToDevice, st));
+        tm.open(TC_SCORE8);
+        HIPCK(ctx, launch_rescore_int8(s, ctx->t, w, tab, layer, (const uint16_t *)q, C, w.rlist, nr, st));
+        tm.close();
+      }
+    }
   } else {
     plan.nk = 1;   // score whatever the selection flagged
   }
@@ -949,6 +1009,7 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
     memset(stats, 0, sizeof(*stats));
     stats->promoted_key_blocks = kblk;
     stats->cached_key_blocks = kcached;
+    stats->scores_deferred = defer ? 1 : 0;
     stats->promoted_value_blocks = vblk;
     stats->dense_kv_heads = dense_heads;
     stats->h2d_bytes = h2d;
@@ -1005,7 +1066,7 @@ kvq_status kvq_decode_naive(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_
   Step &w = ctx->w;
   // empty U and V: INT8 scores and INT4 values for every block
   const float C = (float)(1.4426950408889634 / sqrt((double)s.d));
-  HIPCK(ctx, launch_score_int8(s, ctx->t, w, tab, layer, (const uint16_t *)q, C, st));
+  HIPCK(ctx, launch_score_int8(s, ctx->t, w, tab, layer, (const uint16_t *)q, C, true, st));
   HIPCK(ctx, launch_decode(s, ctx->t, w, tab, layer, false, st));
   HIPCK(ctx, launch_combine(s, w, tab, out, 1, nullptr, nullptr, nullptr, st));
   return KVQ_OK;
@@ -1198,6 +1259,12 @@ kvq_status kvq_selftest_launch_shape(int32_t score_wgs, int32_t mix_blocks) {
     return KVQ_EINVAL;
   set_score_grid_cap(score_wgs);
   set_mix_chunk_blocks(mix_blocks == 0 ? MIX_CB : mix_blocks);
+  return KVQ_OK;
+}
+
+kvq_status kvq_selftest_defer_scores(int32_t ppm) {
+  if (ppm < -1 || ppm > 1000001) return KVQ_EINVAL;
+  g_defer_ppm = ppm < 0 ? DEFER_PPM : ppm;
   return KVQ_OK;
 }
 

@@ -73,6 +73,7 @@ struct Step {
   uint16_t *stage_k, *stage_v;     // [B][Hkv][Tmax][d] ([units][Tmax][d] keys when resident)
   float *part, *partd;             // [B][Hkv][NCH][G][d + 2]
   uint8_t *gdense;                 // [B][Hkv]
+  uint32_t *rlist;                 // [B * Hkv * NBmax] units whose ŝ′ a step rescores
 };
 
 struct SeqTab {
@@ -177,7 +178,11 @@ hipError_t launch_append(const Shape &s, const Tier1 &t, const AppendArgs &a, co
                          const uint16_t *v, int max_blk, hipStream_t st);
 
 hipError_t launch_score_int8(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,
-                             int layer, const uint16_t *q, float C, hipStream_t st);
+                             int layer, const uint16_t *q, float C, bool store, hipStream_t st);
+// ŝ′ of the listed units (ig << 16 | block), after a pass that stored none.
+hipError_t launch_rescore_int8(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,
+                               int layer, const uint16_t *q, float C, const uint32_t *list, int count,
+                               hipStream_t st);
 hipError_t launch_select(const Shape &s, const Step &w, const SeqTab &tab, int tau_ppm, int maxNB,
                          hipStream_t st);
 hipError_t launch_score_fp16(const Shape &s, const Step &w, const SeqTab &tab, int layer,

@@ -90,6 +90,14 @@ typedef int32_t kvq_status;
  * exclusive with KVQ_FLAG_RESIDENT_KEYS (KVQ_EINVAL if both are set, or if
  * key_cache_blocks < 1 with this flag). */
 #define KVQ_FLAG_KEY_CACHE    16u
+/* KVQ_FLAG_ALL_SCORES: every step's INT8 pass stores the INT8 scores of every
+ * block (the trace KVQ_TR_SHAT then holds them all).  Without it, a step at a
+ * layer whose previous step put at least three quarters of the blocks in U
+ * stores none in the pass and rescores only the blocks outside U after the
+ * selection (the only ones the decode reads); the trace then holds them for
+ * those blocks only, and kvq_step_stats.scores_deferred is 1.  Decisions and
+ * outputs are the same either way. */
+#define KVQ_FLAG_ALL_SCORES   32u
 
 typedef struct kvq_config {
     int32_t n_layers;        /* layers held by the context                      */
@@ -166,6 +174,8 @@ typedef struct kvq_step_stats {
                                       rung 3 or the dense path is forced)         */
     int64_t cached_key_blocks;     /* key blocks taken from the device cache
                                       (KVQ_FLAG_KEY_CACHE), not the host link     */
+    int32_t scores_deferred;       /* 1: the INT8 scores were stored for the
+                                      blocks outside U only (KVQ_FLAG_ALL_SCORES) */
 } kvq_step_stats;
 
 /* One decode step at one layer (Méthodologie §2-§3): attends over every
@@ -322,6 +332,14 @@ kvq_status kvq_selftest_sort(const uint64_t *keys, int64_t n, uint64_t *out, int
  * change; outputs differ only by rounding.  Not thread-safe; KVQ_EINVAL on
  * other values.  For tests. */
 kvq_status kvq_selftest_launch_shape(int32_t score_wgs, int32_t mix_blocks);
+
+/* When a step stores the INT8 scores only for the blocks outside U
+ * (KVQ_FLAG_ALL_SCORES): a step defers them when the previous step at its
+ * layer, with its unions read back, had at least ppm parts per million of the
+ * call's blocks in U.  ppm = 0 defers every step whose unions are read back,
+ * 1000001 none; -1 restores the default 750000.  Decisions and outputs must
+ * not change.  Not thread-safe; KVQ_EINVAL on other values.  For tests. */
+kvq_status kvq_selftest_defer_scores(int32_t ppm);
 
 /* Merges promotion-plan entries the way a decode step does before copying
  * (host only, no device call).  in: n host entries, each

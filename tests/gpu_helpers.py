@@ -106,7 +106,9 @@ def run_oracle(orc, case):
 def same_traces(ta, tb, Hq, Hkv, T, where):
     """Two GPU step traces of the same call are equal everywhere the step
     defines them: FP16 scores and FP16 block ingredients only on promoted
-    blocks (elsewhere those arrays keep whatever earlier calls left)."""
+    blocks (elsewhere those arrays keep whatever earlier calls left), INT8
+    scores outside them (a step that defers its INT8 scores stores them
+    there only)."""
     NB = (T + 63) // 64
     U = ta["U"].reshape(Hkv, NB)
     assert np.array_equal(U, tb["U"].reshape(Hkv, NB)), f"{where}: U"
@@ -117,6 +119,8 @@ def same_traces(ta, tb, Hq, Hkv, T, where):
         a, b = ta[k], tb[k]
         if k == "sp":
             a, b = a.reshape(Hq, T)[tokU], b.reshape(Hq, T)[tokU]
+        elif k == "shat":
+            a, b = a.reshape(Hq, T)[~tokU], b.reshape(Hq, T)[~tokU]
         elif k in ("m16", "L16"):
             a, b = a.reshape(Hq, NB)[Uh], b.reshape(Hq, NB)[Uh]
         if a.dtype.kind == "f":
@@ -131,6 +135,8 @@ def compare(case, gpu, ref, check_out=True):
     # merges the selection's per-head runs of a group, later rounds add new
     # blocks only)
     nU = sum(int(np.sum(r.groups[g].U)) for r, _ in ref for g in range(case.Hkv))
+    # a step that deferred its INT8 scores stored them outside U only
+    deferred = bool(gpu["stats"]["scores_deferred"])
     assert gpu["stats"]["promoted_key_blocks"] == nU, \
         f"{case.name}: promoted key blocks {gpu['stats']['promoted_key_blocks']} vs |U| {nU}"
     for i, (r, groups) in enumerate(ref):
@@ -153,7 +159,8 @@ def compare(case, gpu, ref, check_out=True):
             for hh in range(G):
                 hq = g * G + hh
                 w = f"{where} head {hq}"
-                assert np.array_equal(f32bits(shat[hq]), f32bits(tr.shat[hh])), f"{w}: shat"
+                sel = ~tokU if deferred else slice(None)
+                assert np.array_equal(f32bits(shat[hq][sel]), f32bits(tr.shat[hh][sel])), f"{w}: shat"
                 assert np.array_equal(f32bits(blk["delta"][hq]), f32bits(tr.delta[hh])), f"{w}: delta"
                 assert np.array_equal(f32bits(blk["mhat"][hq]), f32bits(tr.mhat[hh])), f"{w}: mhat"
                 assert np.array_equal(blk["Lhat"][hq], tr.Lhat[hh]), f"{w}: Lhat"
