@@ -851,6 +851,7 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
   tm.close();
   Plan plan;
   kvq_status rs = KVQ_OK;
+  int nres = 0;   // blocks outside U whose ŝ′ the first controller round computes
   if (read_u) {
     int64_t ublocks = 0;
     rs = read_union(ctx, st, tab, plan, ublocks);
@@ -859,12 +860,16 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
     const int64_t all = (int64_t)tab.nbc[n] * s.Hkv;
     ctx->uppm[(size_t)layer] = all > 0 ? (int32_t)(ublocks * 1000000 / all) : 0;
     if (defer) {
-      const int nr = outside_union(ctx, tab);
-      if (nr > 0) {
-        HIPCK(ctx, hipMemcpyAsync(w.rlist, ctx->rlist_host, (size_t)nr * 4, hipMemcpyHostToDevice, st));
+      nres = outside_union(ctx, tab);
+      if (nres > 0)
+        HIPCK(ctx, hipMemcpyAsync(w.rlist, ctx->rlist_host, (size_t)nres * 4, hipMemcpyHostToDevice, st));
+      // the first controller round (k_eval) computes them beside the heads'
+      // evaluation; a step that starts with the group pass has its own launch
+      if (nres > 0 && (ctx->th.force_dense || ctx->th.fp16_values)) {
         tm.open(TC_SCORE8);
-        HIPCK(ctx, launch_rescore_int8(s, ctx->t, w, tab, layer, (const uint16_t *)q, C, w.rlist, nr, st));
+        HIPCK(ctx, launch_rescore_int8(s, ctx->t, w, tab, layer, (const uint16_t *)q, C, w.rlist, nres, st));
         tm.close();
+        nres = 0;
       }
     }
   } else {
@@ -896,7 +901,8 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
     const bool first = round == 0 && !ctx->th.force_dense && !ctx->th.fp16_values;
     tm.open(TC_CONTROL);
     if (first)
-      HIPCK(ctx, launch_eval(s, ctx->t, w, tab, layer, ctx->th, maxNB, st));
+      HIPCK(ctx, launch_eval(s, ctx->t, w, tab, layer, ctx->th, maxNB, (const uint16_t *)q, C, w.rlist,
+                             nres, st));
     else
       HIPCK(ctx, launch_control(s, ctx->t, w, tab, layer, ctx->th, round, maxNB, st));
     rs = read_plan_issue(ctx, st);

@@ -23,9 +23,12 @@
 //   * rung 4 (k_finalize): more than layer_frac of a sequence's heads at rung 3;
 //   * FP16-values ablation (flag): V_g = every block, no rung 2, E_val = 0.
 // Every sum is an integer, so no reduction order can change a decision.
+#include <algorithm>
+
 #include "kvq_device.h"
 #include "kvq_internal.h"
 #include "kvq_blockops.h"
+#include "kvq_rescore.h"
 
 namespace kvq {
 
@@ -289,13 +292,30 @@ __device__ void value_rung(const Shape &s, const Tier1 &t, const Step &w, const 
 
 // One controller round, part 1: every query head not yet at rung 3, in a
 // group not yet final, is evaluated on the group's current U (one workgroup
-// per query head).
+// per query head).  Workgroups past the heads (x >= Hq, sequence slot 0)
+// compute the INT8 scores of the listed blocks outside U for a step whose
+// scoring pass stored none: nothing here reads them, and these short-lived
+// workgroups run beside the heads' longer chains of phases.
 template <int EB>
 __global__ __launch_bounds__(CTL_NT) void k_eval(Shape s, Tier1 t, Step w, SeqTab tab, int layer,
-                                                 Thresh th) {
-  extern __shared__ unsigned long long keys[];
+                                                 Thresh th, const uint16_t *q16, float C,
+                                                 const uint32_t *rlist, int rcount) {
+  extern __shared__ __align__(16) unsigned long long keys[];
   __shared__ uint16_t pos[MAX_NB];
   __shared__ CtlShared sh;
+  if ((int)blockIdx.x >= s.Hq) {
+    if (blockIdx.y != 0) return;
+    constexpr int NWV = CTL_NT / 64;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int k0 = ((int)blockIdx.x - s.Hq) * NWV + wave, ks = ((int)gridDim.x - s.Hq) * NWV;
+    if (s.d == 128)
+      rescore_units<128>(s, t, w, tab, layer, q16, C, rlist, rcount, k0, ks,
+                         reinterpret_cast<RescoreLds<128> *>(keys)[wave]);
+    else
+      rescore_units<64>(s, t, w, tab, layer, q16, C, rlist, rcount, k0, ks,
+                        reinterpret_cast<RescoreLds<64> *>(keys)[wave]);
+    return;
+  }
   const int i = blockIdx.y, hq = blockIdx.x, g = hq / s.G;
   // a new plan starts with this round (the host has read the previous one);
   // word 3 (heads flagged for the group decisions) is cleared at the start of
@@ -452,15 +472,19 @@ __global__ __launch_bounds__(CTL_NT) void k_decide(Shape s, Tier1 t, Step w, Seq
 }
 
 hipError_t launch_eval(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab, int layer,
-                       const Thresh &th, int maxNB, hipStream_t st) {
+                       const Thresh &th, int maxNB, const uint16_t *q, float C, const uint32_t *rlist,
+                       int rcount, hipStream_t st) {
   const int n2 = max(64, pow2_at_least(maxNB));
-  const dim3 grid(s.Hq, tab.n), block(CTL_NT);
-  const uint32_t lds = (uint32_t)sort_lds_bytes(n2);
+  // rescoring workgroups: one wave per listed block, at most two per CU
+  const int R = rcount > 0 ? std::min((rcount + CTL_NT / 64 - 1) / (CTL_NT / 64), 2 * std::max(s.ncu, 1)) : 0;
+  const dim3 grid(s.Hq + R, tab.n), block(CTL_NT);
+  const size_t rl = R ? (CTL_NT / 64) * (s.d == 128 ? sizeof(RescoreLds<128>) : sizeof(RescoreLds<64>)) : 0;
+  const uint32_t lds = (uint32_t)std::max(sort_lds_bytes(n2), rl);
   switch ((maxNB + CTL_NT - 1) / CTL_NT) {   // blocks per thread
-    case 1: return launch_k(k_eval<1>, grid, block, lds, st, s, t, w, tab, layer, th);
-    case 2: return launch_k(k_eval<2>, grid, block, lds, st, s, t, w, tab, layer, th);
-    case 3: return launch_k(k_eval<3>, grid, block, lds, st, s, t, w, tab, layer, th);
-    default: return launch_k(k_eval<4>, grid, block, lds, st, s, t, w, tab, layer, th);
+    case 1: return launch_k(k_eval<1>, grid, block, lds, st, s, t, w, tab, layer, th, q, C, rlist, rcount);
+    case 2: return launch_k(k_eval<2>, grid, block, lds, st, s, t, w, tab, layer, th, q, C, rlist, rcount);
+    case 3: return launch_k(k_eval<3>, grid, block, lds, st, s, t, w, tab, layer, th, q, C, rlist, rcount);
+    default: return launch_k(k_eval<4>, grid, block, lds, st, s, t, w, tab, layer, th, q, C, rlist, rcount);
   }
 }
 
@@ -473,7 +497,7 @@ hipError_t launch_decide(const Shape &s, const Tier1 &t, const Step &w, const Se
 
 hipError_t launch_control(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,
                           int layer, const Thresh &th, int round, int maxNB, hipStream_t st) {
-  const hipError_t e = launch_eval(s, t, w, tab, layer, th, maxNB, st);
+  const hipError_t e = launch_eval(s, t, w, tab, layer, th, maxNB, nullptr, 0.0f, nullptr, 0, st);
   if (e != hipSuccess) return e;
   return launch_decide(s, t, w, tab, layer, th, round, maxNB, st);
 }

@@ -189,8 +189,11 @@ hipError_t launch_score_fp16(const Shape &s, const Step &w, const SeqTab &tab, i
                              int maxNB, hipStream_t st);
 hipError_t launch_control(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,
                           int layer, const Thresh &th, int round, int maxNB, hipStream_t st);
+// rcount > 0: extra workgroups compute ŝ′ of rlist's blocks (as
+// launch_rescore_int8) beside the evaluation
 hipError_t launch_eval(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab, int layer,
-                       const Thresh &th, int maxNB, hipStream_t st);
+                       const Thresh &th, int maxNB, const uint16_t *q, float C, const uint32_t *rlist,
+                       int rcount, hipStream_t st);
 hipError_t launch_decide(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,
                          int layer, const Thresh &th, int round, int maxNB, hipStream_t st);
 hipError_t launch_finalize(const Shape &s, const Step &w, const SeqTab &tab, const Thresh &th,

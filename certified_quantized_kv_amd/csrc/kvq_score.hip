@@ -39,6 +39,7 @@
 
 #include "kvq_device.h"
 #include "kvq_internal.h"
+#include "kvq_rescore.h"
 #include "kvq_blockops.h"
 
 namespace kvq {
@@ -367,115 +368,15 @@ hipError_t launch_score_int8(const Shape &s, const Tier1 &t, const Step &w, cons
                : launch_k(k_score_int8<64, false>, dim3(grid), dim3(256), 0, st, s, t, w, tab, layer, q, C);
 }
 
-// ---- ŝ′ of listed blocks (after a pass that stored none) ------------------------
-// One wave per listed unit (entry ig << 16 | b, ig = i Hkv + g), the same
-// arithmetic as the pass: q′ and the limbs of A per head, the exact integer
-// core on the matrix cores, D_t rounded once from fp64, β as the fma chain
-// over the channels in ascending order; ŝ′ of the unit's 64 tokens stored.
-// No wave waits on another; a unit's loads all go out before its first use.
+// ---- ŝ′ of listed blocks (after a pass that stored none): kvq_rescore.h -------
 template <int D>
 __global__ __launch_bounds__(256) void k_rescore_int8(Shape s, Tier1 t, Step w, SeqTab tab, int layer,
                                                    const uint16_t *__restrict__ q16, float C,
                                                    const uint32_t *__restrict__ list, int count) {
-  constexpr int CW = D / 16;
-  constexpr int NKS = D / 64;
-  constexpr int AST = D + 16;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int h = lane >> 4, jc = lane & 15;
-  const int G = s.G;
-  const int hs = h < G ? h : 0;
-  __shared__ __align__(16) int8_t As[4][16][AST];
-  __shared__ __align__(16) float Qs[4][4][D];        // q′ rows (head slots)
-  __shared__ __align__(16) float Us[4][D];           // off + 128 s per channel
-  __shared__ float Bs[4][4];                         // β per head slot
-  for (int k = blockIdx.x * 4 + wave; k < count; k += gridDim.x * 4) {
-    const uint32_t ent = list[k];
-    const int ig = (int)(ent >> 16), b = (int)(ent & 0xffffu);
-    const int i = ig / s.Hkv, g = ig - i * s.Hkv;
-    const size_t uu = unit_of(s, tab.slot[i], layer, g);
-    // every load of the unit at once: codes, metadata, q slice
-    v4i Bn[NKS][4];
-    const uint8_t *kc = t.kcodes + (uu * s.NBmax + b) * (size_t)(BLOCK * D);
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-        Bn[ks][nt] = __builtin_nontemporal_load((const v4i *)(kc + ((size_t)((ks * 4 + nt) * 64 + lane)) * 16));
-    uint32_t kb[CW];
-    const uint32_t *km = t.kmeta + (uu * s.NBmax + b) * D + jc * CW;
-#pragma unroll
-    for (int c = 0; c < CW; ++c) kb[c] = km[c];
-    uint32_t qb[CW / 2];
-    const uint32_t *qs = (const uint32_t *)(q16 + ((size_t)i * s.Hq + g * G + hs) * D + jc * CW);
-#pragma unroll
-    for (int c = 0; c < CW / 2; ++c) qb[c] = qs[c];
-    // q′, a = q′ s, the exponent and the limbs (lane (h, jc): head slot h,
-    // channels jc CW ..); q′ rows and off + 128 s into LDS for the chains
-    float qv[CW], a[CW];
-    float am = 0.0f;
-#pragma unroll
-    for (int c = 0; c < CW; ++c) {
-      qv[c] = h2f((uint16_t)(qb[c / 2] >> (16 * (c % 2)))) * C;
-      const float sv = h2f((uint16_t)(kb[c] & 0xffffu));
-      a[c] = qv[c] * sv;
-      am = fmaxf(am, fabsf(a[c]));
-      Qs[wave][h][jc * CW + c] = qv[c];
-      if (h == 0) Us[wave][jc * CW + c] = fmaf(128.0f, sv, h2f((uint16_t)(kb[c] >> 16)));
-    }
-    am = bfly_max<16>(am);
-    const bool zero = !(am > 0.0f);
-    const int e = zero ? 0 : ilogb_f(am) - 21;
-    uint32_t l0w[CW / 4], l1w[CW / 4], l2w[CW / 4];
-#pragma unroll
-    for (int c = 0; c < CW / 4; ++c) l0w[c] = l1w[c] = l2w[c] = 0u;
-#pragma unroll
-    for (int c = 0; c < CW; ++c) {
-      const int A = (int)rintf(ldexpf(a[c], -e));
-      const int L0 = ((A + 128) & 255) - 128;
-      const int A1 = (A - L0) >> 8;
-      const int L1 = ((A1 + 128) & 255) - 128;
-      const int L2 = (A1 - L1) >> 8;
-      l0w[c / 4] |= ((uint32_t)L0 & 255u) << (8 * (c % 4));
-      l1w[c / 4] |= ((uint32_t)L1 & 255u) << (8 * (c % 4));
-      l2w[c / 4] |= ((uint32_t)L2 & 255u) << (8 * (c % 4));
-    }
-    {
-      int8_t *row = &As[wave][h * 4][jc * CW];
-#pragma unroll
-      for (int c = 0; c < CW / 4; ++c) {
-        ((uint32_t *)(row + 0 * AST))[c] = l0w[c];
-        ((uint32_t *)(row + 1 * AST))[c] = l1w[c];
-        ((uint32_t *)(row + 2 * AST))[c] = l2w[c];
-        ((uint32_t *)(row + 3 * AST))[c] = 0u;
-      }
-    }
-    wave_lds_sync();
-    if (lane < 4) {                               // β of head slot lane
-      float beta = 0.0f;
-      for (int c = 0; c < D; ++c) beta = fmaf(Qs[wave][lane][c], Us[wave][c], beta);
-      Bs[wave][lane] = beta;
-    }
-    v4i acc[4];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) acc[nt] = (v4i){0, 0, 0, 0};
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const v4i Aop = *(const v4i *)&As[wave][lane & 15][ks * 64 + 16 * (lane >> 4)];
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-        acc[nt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aop, Bn[ks][nt], acc[nt], 0, 0, 0);
-    }
-    wave_lds_sync();
-    const float pb = Bs[wave][h];
-    const float sc = ldexpf(1.0f, e);
-    float *dst = w.shat + ((size_t)i * s.Hq + g * G + hs) * s.Tmax + (size_t)b * BLOCK;
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const double Dd = fma((double)acc[nt][2], 65536.0, fma((double)acc[nt][1], 256.0, (double)acc[nt][0]));
-      __builtin_nontemporal_store(fmaf((float)Dd, sc, pb), &dst[nt * 16 + jc]);
-    }
-    wave_lds_sync();
-  }
+  __shared__ RescoreLds<D> L[4];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  rescore_units<D>(s, t, w, tab, layer, q16, C, list, count, blockIdx.x * 4 + wave, gridDim.x * 4,
+                   L[wave]);
 }
 
 hipError_t launch_rescore_int8(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,

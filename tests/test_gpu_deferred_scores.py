@@ -43,22 +43,25 @@ def _seq(cid, T, Hq, Hkv, d):
     return K, V, S.query(w, 0, 0, 0), None
 
 
+# the first controller round computes the rescored blocks beside the heads'
+# evaluation; with FP16 values (no such round) they have a launch of their own
 @pytest.mark.parametrize("shape", [
-    ("700x8x2x128", [(90, 700)], 8, 2, 128),
-    ("1500x4x4x64", [(92, 1500)], 4, 4, 64),
-    ("ragged-3seq", [(94, 700), (95, 130), (96, 1000)], 8, 2, 128),
+    ("700x8x2x128", [(90, 700)], 8, 2, 128, {}),
+    ("1500x4x4x64", [(92, 1500)], 4, 4, 64, {}),
+    ("ragged-3seq", [(94, 700), (95, 130), (96, 1000)], 8, 2, 128, {}),
+    ("700x8x2x128-fp16-values", [(90, 700)], 8, 2, 128, {"fp16_values": True}),
 ])
 def test_deferred_step_matches_oracle(env, defer_all, shape):
     kvq, torch, orc = env
-    name, seqs, Hq, Hkv, d = shape
-    case = Case(f"deferred {name}", Hq, Hkv, d, [_seq(c, T, Hq, Hkv, d) for c, T in seqs], **LOOSE)
+    name, seqs, Hq, Hkv, d, extra = shape
+    case = Case(f"deferred {name}", Hq, Hkv, d, [_seq(c, T, Hq, Hkv, d) for c, T in seqs], **LOOSE, **extra)
     log(f"[deferred] {case.name}")
     gpu = run_gpu(kvq, torch, case)
     assert gpu["stats"]["scores_deferred"] == 1
     ref = run_oracle(orc, case)
     outside = sum(int(np.sum(r.groups[g].U == 0)) for r, _ in ref for g in range(Hkv))
     log(f"[deferred] {case.name}: {outside} blocks rescored")
-    if name != "ragged-3seq":
+    if not name.startswith("ragged"):
         assert outside > 0, "the case should leave blocks outside U"
     compare(case, gpu, ref)
     gpu["ctx"].close()
