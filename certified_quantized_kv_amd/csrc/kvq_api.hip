@@ -863,9 +863,12 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
       nres = outside_union(ctx, tab);
       if (nres > 0)
         HIPCK(ctx, hipMemcpyAsync(w.rlist, ctx->rlist_host, (size_t)nres * 4, hipMemcpyHostToDevice, st));
-      // the first controller round (k_eval) computes them beside the heads'
-      // evaluation; a step that starts with the group pass has its own launch
-      if (nres > 0 && (ctx->th.force_dense || ctx->th.fp16_values)) {
+      // the first controller round computes them beside the heads'
+      // evaluation when it runs on its own; a round fused with the decode
+      // (which reads them) or a step that starts with the group pass has a
+      // launch of its own for them, here
+      const bool own_round = !ctx->th.force_dense && !ctx->th.fp16_values && !eval_decode_fits(s, tab);
+      if (nres > 0 && !own_round) {
         tm.open(TC_SCORE8);
         HIPCK(ctx, launch_rescore_int8(s, ctx->t, w, tab, layer, (const uint16_t *)q, C, w.rlist, nres, st));
         tm.close();
@@ -899,12 +902,24 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
     // (k_decide) does not run.  Otherwise k_decide runs for this round and
     // the rounds go on as below.
     const bool first = round == 0 && !ctx->th.force_dense && !ctx->th.fp16_values;
-    tm.open(TC_CONTROL);
-    if (first)
-      HIPCK(ctx, launch_eval(s, ctx->t, w, tab, layer, ctx->th, maxNB, (const uint16_t *)q, C, w.rlist,
-                             nres, st));
-    else
+    // The first round's evaluation and the speculative decode (which reads
+    // only U, the scores and the block maxima) share one launch, the decode's
+    // chunks filling the compute units the heads leave idle; fused_extra is
+    // that launch's count of workgroups beside the decode's (for the
+    // combine), or -1 when they run as separate launches.
+    int fused_extra = -1;
+    if (first) {
+      tm.open(TC_DECODE);
+      HIPCK(ctx, launch_eval_decode(s, ctx->t, w, tab, layer, ctx->th, maxNB, &fused_extra, st));
+      if (fused_extra < 0) {
+        tm.open(TC_CONTROL);
+        HIPCK(ctx, launch_eval(s, ctx->t, w, tab, layer, ctx->th, maxNB, (const uint16_t *)q, C, w.rlist,
+                               nres, st));
+      }
+    } else {
+      tm.open(TC_CONTROL);
       HIPCK(ctx, launch_control(s, ctx->t, w, tab, layer, ctx->th, round, maxNB, st));
+    }
     rs = read_plan_issue(ctx, st);
     if (rs != KVQ_OK) return rs;
     // the decode and combine go in behind the plan's copy: in the common case
@@ -915,13 +930,15 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
     // whose copies are issued only after the plan is read: every later copy
     // waits for them (ev_spec), so no copy writes a buffer they still read.
     if (!ctx->th.force_dense) {
-      tm.open(TC_DECODE);
-      // (the first round only evaluates: no value is promoted yet)
-      HIPCK(ctx, launch_decode(s, ctx->t, w, tab, layer, !first, st));
+      if (fused_extra < 0) {
+        tm.open(TC_DECODE);
+        // (the first round only evaluates: no value is promoted yet)
+        HIPCK(ctx, launch_decode(s, ctx->t, w, tab, layer, !first, st));
+      }
       tm.open(TC_COMBINE);
       // mixed partials for every head: the result is kept only if no head
       // reached rung 3
-      HIPCK(ctx, launch_combine(s, w, tab, out, first ? 3 : 1, e_key, e_val, level, st));
+      HIPCK(ctx, launch_combine(s, w, tab, out, first ? 3 : 1, e_key, e_val, level, fused_extra, st));
       HIPCK(ctx, hipEventRecord(ctx->ev_spec, st));
       spec = true;
     }
@@ -1000,7 +1017,7 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
     }
     tm.open(TC_COMBINE);
     HIPCK(ctx, launch_combine(s, w, tab, out, 0, maybe_dense ? nullptr : e_key,
-                              maybe_dense ? nullptr : e_val, maybe_dense ? nullptr : level, st));
+                              maybe_dense ? nullptr : e_val, maybe_dense ? nullptr : level, -1, st));
     tm.close();
   }
   if (timing) HIPCK(ctx, hipEventRecord(ctx->ev_tot[1], st));
@@ -1074,7 +1091,7 @@ kvq_status kvq_decode_naive(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_
   const float C = (float)(1.4426950408889634 / sqrt((double)s.d));
   HIPCK(ctx, launch_score_int8(s, ctx->t, w, tab, layer, (const uint16_t *)q, C, true, st));
   HIPCK(ctx, launch_decode(s, ctx->t, w, tab, layer, false, st));
-  HIPCK(ctx, launch_combine(s, w, tab, out, 1, nullptr, nullptr, nullptr, st));
+  HIPCK(ctx, launch_combine(s, w, tab, out, 1, nullptr, nullptr, nullptr, -1, st));
   return KVQ_OK;
 }
 
@@ -1104,7 +1121,7 @@ kvq_status kvq_dense_decode(kvq_ctx *ctx, int32_t n, const int32_t *seq_lens, co
   a.v = (const uint16_t *)v;
   hipStream_t st = (hipStream_t)stream;
   HIPCK(ctx, launch_dense_vram(s, ctx->w, a, maxNB, st));
-  HIPCK(ctx, launch_combine(s, ctx->w, tab, out, 2, nullptr, nullptr, nullptr, st));
+  HIPCK(ctx, launch_combine(s, ctx->w, tab, out, 2, nullptr, nullptr, nullptr, -1, st));
   return KVQ_OK;
 }
 

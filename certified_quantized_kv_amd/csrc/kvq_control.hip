@@ -28,6 +28,7 @@
 #include "kvq_device.h"
 #include "kvq_internal.h"
 #include "kvq_blockops.h"
+#include "kvq_mixed.h"
 #include "kvq_rescore.h"
 
 namespace kvq {
@@ -292,10 +293,27 @@ __device__ void value_rung(const Shape &s, const Tier1 &t, const Step &w, const 
 
 // One controller round, part 1: every query head not yet at rung 3, in a
 // group not yet final, is evaluated on the group's current U (one workgroup
-// per query head).  Workgroups past the heads (x >= Hq, sequence slot 0)
-// compute the INT8 scores of the listed blocks outside U for a step whose
-// scoring pass stored none: nothing here reads them, and these short-lived
-// workgroups run beside the heads' longer chains of phases.
+// per query head).
+template <int EB>
+__device__ inline void eval_wg(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,
+                               int layer, const Thresh &th, int i, int hq, unsigned long long *keys,
+                               uint16_t *pos, CtlShared &sh) {
+  const int g = hq / s.G;
+  // a new plan starts with this round (the host has read the previous one);
+  // word 3 (heads flagged for the group decisions) is cleared at the start of
+  // the step and only read after the first round
+  if (i == 0 && hq == 0 && threadIdx.x < 3) w.plan[threadIdx.x] = 0ull;
+  const int NB = (tab.T[i] + BLOCK - 1) / BLOCK;
+  const float *eta = t.eta + unit_of(s, tab.slot[i], layer, g) * s.NBmax;
+  evaluate_head<EB>(s, w, th, i, g, hq, NB, eta, w.gstat + (size_t)i * s.Hkv + g,
+                    w.hflags + (size_t)i * s.Hq + hq, keys, pos, sh);
+}
+
+// Grid (Hq + R, n): the heads, then (sequence slot 0 only) R workgroups that
+// compute the INT8 scores of rlist's blocks outside U for a step whose
+// scoring pass stored none, one wave per block.  Nothing in the round reads
+// them, and these short-lived workgroups run beside the heads' longer chains
+// of phases.
 template <int EB>
 __global__ __launch_bounds__(CTL_NT) void k_eval(Shape s, Tier1 t, Step w, SeqTab tab, int layer,
                                                  Thresh th, const uint16_t *q16, float C,
@@ -316,15 +334,46 @@ __global__ __launch_bounds__(CTL_NT) void k_eval(Shape s, Tier1 t, Step w, SeqTa
                         reinterpret_cast<RescoreLds<64> *>(keys)[wave]);
     return;
   }
-  const int i = blockIdx.y, hq = blockIdx.x, g = hq / s.G;
-  // a new plan starts with this round (the host has read the previous one);
-  // word 3 (heads flagged for the group decisions) is cleared at the start of
-  // the step and only read after the first round
-  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 3) w.plan[threadIdx.x] = 0ull;
-  const int NB = (tab.T[i] + BLOCK - 1) / BLOCK;
-  const float *eta = t.eta + unit_of(s, tab.slot[i], layer, g) * s.NBmax;
-  evaluate_head<EB>(s, w, th, i, g, hq, NB, eta, w.gstat + (size_t)i * s.Hkv + g,
-                w.hflags + (size_t)i * s.Hq + hq, keys, pos, sh);
+  eval_wg<EB>(s, t, w, tab, layer, th, blockIdx.y, blockIdx.x, keys, pos, sh);
+}
+
+// The first controller round (nothing flagged, no value promoted yet) and the
+// speculative mixed decode in one launch: workgroups [0, Hq n) evaluate the
+// heads, the rest run two decode chunks each (threads [0, 512) and [512,
+// 1024): the call's chunks in (sequence, KV head, chunk) order, a chunk past
+// the last computed and not stored).  The decode reads only U, the scores
+// and the block maxima, all final before this launch (a deferred step's
+// rescoring included), so the heads' latency-bound chains of phases run
+// beside its streaming work.
+template <int EB, int D, int CB>
+__global__ __launch_bounds__(CTL_NT) void k_eval_decode(Shape s, Tier1 t, Step w, SeqTab tab, int layer,
+                                                        Thresh th) {
+  extern __shared__ __align__(16) unsigned long long keys[];
+  __shared__ uint16_t pos[MAX_NB];
+  __shared__ CtlShared sh;
+  const int nev = s.Hq * tab.n, x = blockIdx.x;
+  if (x < nev) {
+    eval_wg<EB>(s, t, w, tab, layer, th, x / s.Hq, x % s.Hq, keys, pos, sh);
+    return;
+  }
+  static_assert(CTL_NT == 2 * 512, "two eight-wave decode chunks per workgroup");
+  const int sub = threadIdx.x >> 9;
+  int rem = 2 * (x - nev) + sub, i = 0;
+  bool live = true;
+  for (;; ++i) {
+    if (i >= tab.n) {                   // past the last chunk: chunk 0 again, not stored
+      live = false;
+      i = 0;
+      rem = 0;
+      break;
+    }
+    const int cnt = s.Hkv * tab.nch[i];
+    if (rem < cnt) break;
+    rem -= cnt;
+  }
+  const int g = rem / tab.nch[i], ch = rem - g * tab.nch[i];
+  decode_chunk<D, CB, 4, false>(s, t, w, tab, layer, i, g, ch, live, threadIdx.x & 511,
+                                reinterpret_cast<DecLds<D, CB, 4, false> *>(keys)[sub]);
 }
 
 // Part 2, one workgroup per (sequence, KV head): rung 1 decisions; a group
@@ -486,6 +535,62 @@ hipError_t launch_eval(const Shape &s, const Tier1 &t, const Step &w, const SeqT
     case 3: return launch_k(k_eval<3>, grid, block, lds, st, s, t, w, tab, layer, th, q, C, rlist, rcount);
     default: return launch_k(k_eval<4>, grid, block, lds, st, s, t, w, tab, layer, th, q, C, rlist, rcount);
   }
+}
+
+// One workgroup of k_eval_decode fits a CU at a time (two thirds of the
+// standalone decode's waves), so it pays while the call needs at most two
+// rounds of workgroups: at 128K tokens, batch 1 (evaluation + decode 36.9 ->
+// 24.7 us) and batch 2 (53.1 -> 48.4 us), not batch 4 (88.7 -> 94.1 us).
+// The test hook's chunk shapes (8 or 16 blocks) keep separate launches.
+bool eval_decode_fits(const Shape &s, const SeqTab &tab) {
+  if (mix_chunk_blocks() != MIX_CB) return false;
+  long long base = 0;
+  for (int i = 0; i < tab.n; ++i) base += (long long)s.Hkv * ((tab.nbc[i + 1] - tab.nbc[i] + MIX_CB - 1) / MIX_CB);
+  return (long long)s.Hq * tab.n + (base + 1) / 2 <= 2LL * std::max(s.ncu, 1);
+}
+
+hipError_t launch_eval_decode(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab0,
+                              int layer, const Thresh &th, int maxNB, int *extra, hipStream_t st) {
+  *extra = -1;
+  if (!eval_decode_fits(s, tab0)) return hipSuccess;
+  const int n2 = max(64, pow2_at_least(maxNB));
+  const int nev = s.Hq * tab0.n;
+  SeqTab tab = tab0;
+  mix_chunk_counts(s, tab, MIX_CB, 2, nev);
+  int total = 0, most = 0;
+  for (int i = 0; i < tab.n; ++i) {
+    const int NB = tab.nbc[i + 1] - tab.nbc[i];
+    total += s.Hkv * tab.nch[i];
+    most = std::max(most, (NB + tab.nch[i] - 1) / tab.nch[i]);
+  }
+  const dim3 grid(nev + (total + 1) / 2), block(CTL_NT);
+  const bool c32 = most <= 32;
+  size_t lds = sort_lds_bytes(n2);
+  const size_t dl = s.d == 128 ? (c32 ? sizeof(DecLds<128, 32, 4, false>) : sizeof(DecLds<128, 48, 4, false>))
+                               : (c32 ? sizeof(DecLds<64, 32, 4, false>) : sizeof(DecLds<64, 48, 4, false>));
+  lds = std::max(lds, 2 * dl);
+  const int eb = (maxNB + CTL_NT - 1) / CTL_NT;   // blocks per thread of the evaluation
+  hipError_t e;
+#define KVQ_ED(EB_, D_, CB_)                                                                        \
+  e = launch_k(k_eval_decode<EB_, D_, CB_>, grid, block, (uint32_t)lds, st, s, t, w, tab, layer, th)
+#define KVQ_ED_D(EB_)                          \
+  if (s.d == 128) {                            \
+    if (c32) KVQ_ED(EB_, 128, 32);             \
+    else KVQ_ED(EB_, 128, 48);                 \
+  } else {                                     \
+    if (c32) KVQ_ED(EB_, 64, 32);              \
+    else KVQ_ED(EB_, 64, 48);                  \
+  }
+  switch (eb) {
+    case 1: KVQ_ED_D(1) break;
+    case 2: KVQ_ED_D(2) break;
+    case 3: KVQ_ED_D(3) break;
+    default: KVQ_ED_D(4) break;
+  }
+#undef KVQ_ED_D
+#undef KVQ_ED
+  if (e == hipSuccess) *extra = nev;
+  return e;
 }
 
 hipError_t launch_decide(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,

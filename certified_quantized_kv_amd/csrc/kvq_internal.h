@@ -203,9 +203,23 @@ hipError_t launch_decode(const Shape &s, const Tier1 &t, const Step &w, const Se
 hipError_t launch_dense_staged(const Shape &s, const Step &w, const SeqTab &tab, int layer,
                                const uint16_t *q16, int maxNB, hipStream_t st);
 // mode 0: partials chosen by each head's level; 1: mixed partials; 2: dense;
-// 3: mixed partials, and the outputs of a first round that flagged no head
+// 3: mixed partials, and the outputs of a first round that flagged no head.
+// fused_extra >= 0: the mixed partials came from k_eval_decode launched with
+// that many workgroups beside its decode workgroups (its chunking), else -1.
 hipError_t launch_combine(const Shape &s, const Step &w, const SeqTab &tab, float *out, int mode,
-                          float *e_key, float *e_val, int8_t *level, hipStream_t st);
+                          float *e_key, float *e_val, int8_t *level, int fused_extra, hipStream_t st);
+// Split-K chunks per sequence of the mixed decode (tab.nch), for workgroups of
+// per_wg chunks beside `extra` other workgroups of the same launch.
+void mix_chunk_counts(const Shape &s, SeqTab &tab, int cb, int per_wg, int extra);
+// The first controller round and the speculative mixed decode in one launch
+// (k_eval_decode): the heads' evaluation beside the decode's chunks, two per
+// workgroup.  Sets *extra to the number of evaluation workgroups (for
+// launch_combine), or to -1 when the launch shape does not allow the fused
+// launch (then nothing was launched).
+hipError_t launch_eval_decode(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,
+                              int layer, const Thresh &th, int maxNB, int *extra, hipStream_t st);
+// Whether launch_eval_decode takes this call (else it launches nothing).
+bool eval_decode_fits(const Shape &s, const SeqTab &tab);
 hipError_t launch_dense_vram(const Shape &s, const Step &w, const DenseArgs &a, int maxNB,
                              hipStream_t st);
 hipError_t launch_exp2k(const float *x, float *y, int64_t n, hipStream_t st);

@@ -115,7 +115,7 @@ extern "C" kvq_status kvq_dense_decode_noalloc(int32_t n, int32_t Hq, int32_t Hk
   a.v = (const uint16_t *)v;
   const hipStream_t st = (hipStream_t)stream;
   hipError_t e = launch_dense_vram(s, w, a, maxNB, st);
-  if (e == hipSuccess) e = launch_combine(s, w, tab, out, 2, nullptr, nullptr, nullptr, st);
+  if (e == hipSuccess) e = launch_combine(s, w, tab, out, 2, nullptr, nullptr, nullptr, -1, st);
   if (e != hipSuccess) return noalloc_fail(KVQ_EHIP, hipGetErrorString(e));
   return KVQ_OK;
 }

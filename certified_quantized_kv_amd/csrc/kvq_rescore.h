@@ -8,8 +8,7 @@
 // the exact integer core on the matrix cores, D_t rounded once from fp64, β
 // as the fma chain over the channels in ascending order; ŝ′ of the unit's 64
 // tokens stored.  No wave waits on another; a unit's loads all go out before
-// their first use.  Used by k_rescore_int8 and by the extra workgroups of the
-// first controller round (k_eval), which runs beside them.
+// their first use.  Run by k_rescore_int8 (kvq_score.hip).
 #pragma once
 #include "kvq_device.h"
 #include "kvq_internal.h"

@@ -43,8 +43,8 @@ def _seq(cid, T, Hq, Hkv, d):
     return K, V, S.query(w, 0, 0, 0), None
 
 
-# the first controller round computes the rescored blocks beside the heads'
-# evaluation; with FP16 values (no such round) they have a launch of their own
+# with FP16 values the step has no first evaluation round of its own (the
+# group pass runs from the start), so its decode is not fused with it
 @pytest.mark.parametrize("shape", [
     ("700x8x2x128", [(90, 700)], 8, 2, 128, {}),
     ("1500x4x4x64", [(92, 1500)], 4, 4, 64, {}),
@@ -65,6 +65,25 @@ def test_deferred_step_matches_oracle(env, defer_all, shape):
         assert outside > 0, "the case should leave blocks outside U"
     compare(case, gpu, ref)
     gpu["ctx"].close()
+
+
+def test_deferred_separate_launches_match_oracle(env, defer_all):
+    """16-block decode chunks keep the evaluation and the decode in separate
+    launches; the evaluation's launch then computes the rescored blocks in
+    workgroups of its own, beside the heads."""
+    kvq, torch, orc = env
+    kvq.set_launch_shape(0, 16)
+    try:
+        case = Case("deferred separate 700x8x2x128", 8, 2, 128, [_seq(90, 700, 8, 2, 128)], **LOOSE)
+        log(f"[deferred] {case.name}")
+        gpu = run_gpu(kvq, torch, case)
+        assert gpu["stats"]["scores_deferred"] == 1
+        ref = run_oracle(orc, case)
+        assert sum(int(np.sum(r.groups[g].U == 0)) for r, _ in ref for g in range(2)) > 0
+        compare(case, gpu, ref)
+        gpu["ctx"].close()
+    finally:
+        kvq.set_launch_shape(0, 0)
 
 
 def _run_steps(kvq, torch, K, V, appends, qs, Hq, Hkv, d, cap, layers, **cfg):
