@@ -563,7 +563,10 @@ def main():
                    "kv_tokens_per_s_per_layer": round(T_avg / (qp_ms * 1e-3), 1),
                    "streaming_kernels_ms": round(st_ms, 5),
                    "streaming_kernels_hbm_frac": round(qp_bytes / (st_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                   "controller_ms": round(qp_ms - st_ms, 5)},
+                   "controller_ms": round(qp_ms - st_ms, 5),
+                   "note": ("the first controller round runs inside the decode launch (k_eval_decode): "
+                            "streaming_kernels_ms includes it, controller_ms is selection + combine"
+                            if fused else "streaming = k_score_int8 + k_decode_mixed")},
         "per_kernel_hbm_frac": {k: round(v[1] / (v[0] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
                                 for k, v in cand.items() if v[0] > 0},
     }

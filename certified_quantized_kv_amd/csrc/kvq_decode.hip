@@ -4,7 +4,7 @@
 // INT8; rung 2 promotes values; rungs 3/4 recompute with full FP16 K and V,
 // Méthodologie §1).
 //
-// Mixed mode, per (sequence, KV head, chunk of 16 blocks):
+// Mixed mode, per (sequence, KV head, chunk of up to 48 blocks):
 //   scores: FP16-key score on blocks of U_g, INT8 score elsewhere (both
 //           already computed, log2 units);
 //   values: FP16 from the staging buffer on blocks of V_g, INT4 dequantized
