@@ -161,12 +161,16 @@ typedef struct kvq_step_stats {
        start and end (hipExtLaunchKernel events); copies are bracketed by
        events on the copy stream.  The events are recorded only on calls
        that return statistics. */
-    float ms_score_int8;           /* INT8 scoring kernel                         */
+    float ms_score_int8;           /* INT8 scoring kernel (and the rescoring of a
+                                      deferring step, when it has its own launch) */
     float ms_select;               /* top-K* selection, union planning, run lists */
     float ms_score_fp16;           /* FP16 scoring of promoted blocks (all rounds)*/
-    float ms_control;              /* controller kernels, all rounds              */
+    float ms_control;              /* controller kernels, all rounds (the first
+                                      round is in ms_decode when it shares the
+                                      decode's launch, k_eval_decode)             */
     float ms_copy;                 /* host->device copies (copy stream)           */
-    float ms_decode;               /* mixed split-K decode kernel                 */
+    float ms_decode;               /* mixed split-K decode kernel (with the first
+                                      controller round when they share a launch)  */
     float ms_dense;                /* dense fallback decode kernel                */
     float ms_total;                /* whole call, first launch to last            */
     float ms_combine;              /* split-K combine kernel                      */
