@@ -9,7 +9,10 @@
 * Launch shapes: the INT8 scoring grid (which wave scores which block, which
   blocks share a batch of channel sums) and the mixed decode's chunk size
   change no decision: every decision array is bit-identical across shapes,
-  and the outputs of each shape match the oracle within 2e-3.
+  and the outputs of each shape match the oracle within 2e-3.  With the
+  default 48-block chunks the first controller round shares the decode's
+  launch (k_eval_decode); 8- and 16-block chunks keep them apart, so both
+  routes meet here on the same calls (heads at every rung among them).
 """
 import numpy as np
 import pytest
