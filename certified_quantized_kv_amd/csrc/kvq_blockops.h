@@ -399,8 +399,10 @@ __device__ __forceinline__ bool sort_desc_u64(unsigned long long *keys, int n, i
 }
 
 // Inclusive scan of per-thread u64 values over a workgroup of NT threads
-// (NT = 64 * waves); returns the inclusive prefix, total in *total.
-template <int NT>
+// (NT = 64 * waves); returns the inclusive prefix, total in *total.  With
+// REUSE false the caller writes buf again only after a barrier of its own,
+// so the scan ends without one.
+template <int NT, bool REUSE = true>
 __device__ inline unsigned long long block_incl_scan_u64(unsigned long long v, unsigned long long *buf,
                                                          unsigned long long *total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -414,7 +416,7 @@ __device__ inline unsigned long long block_incl_scan_u64(unsigned long long v, u
     if (k < wave) before += c;
     all += c;
   }
-  __syncthreads();
+  if (REUSE) __syncthreads();
   *total = all;
   return x + before;
 }

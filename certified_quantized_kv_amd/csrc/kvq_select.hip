@@ -67,27 +67,34 @@ __global__ __launch_bounds__(SEL_NT) void k_select(Shape s, Step w, SeqTab tab, 
 
   // pi, then prefix sums of the sorted weights: thread t owns positions
   // [t*per, (t+1)*per)
+  constexpr int PMAX = (MAX_NB + SEL_NT - 1) / SEL_NT;
   const int per = (NB + SEL_NT - 1) / SEL_NT;
   const int p0 = threadIdx.x * per;
   unsigned long long own = 0ull;
-  for (int k = 0; k < per; ++k) {
+  uint32_t wk[PMAX];                            // the weights at the thread's positions
+#pragma unroll
+  for (int k = 0; k < PMAX; ++k) {
     const int p = p0 + k;
-    if (p < NB) {
+    wk[k] = 0u;
+    if (k < per && p < NB) {
       const unsigned long long key = keys[p];
       w.pi[base + p] = 0xffffffffu - (uint32_t)(key & 0xffffffffull);
-      own += key >> 32;
+      wk[k] = (uint32_t)(key >> 32);
+      own += wk[k];
     }
   }
   unsigned long long total;
-  const unsigned long long incl = block_incl_scan_u64<SEL_NT>(own, sbuf, &total);
+  // (sbuf is not written again: no barrier after the scan)
+  const unsigned long long incl = block_incl_scan_u64<SEL_NT, false>(own, sbuf, &total);
   const unsigned long long need = (unsigned long long)tau_ppm * total;
   __shared__ int kst;
   unsigned long long pre = incl - own;
-  for (int k = 0; k < per; ++k) {
+#pragma unroll
+  for (int k = 0; k < PMAX; ++k) {
     const int p = p0 + k;                       // K* candidate p + 1
-    if (p >= NB) break;
+    if (k >= per || p >= NB) break;
     const bool ok_prev = (p == 0) ? false : (1000000ull * pre >= need);
-    pre += keys[p] >> 32;
+    pre += wk[k];
     const bool ok = 1000000ull * pre >= need;
     if (ok && !ok_prev) {
       w.k0[(size_t)i * s.Hq + hq] = p + 1;
