@@ -115,13 +115,12 @@ __device__ void evaluate_head(const Shape &s, const Step &w, const Thresh &th, i
     }
   }
   if ((gsv & 1u) || (hfv & 4u)) return;   // the whole workgroup leaves
-  // S_h = pi[0 .. n): INT8 position of each member, 0xffff elsewhere
-  for (int b = threadIdx.x; b < NB; b += CTL_NT) pos[b] = 0xffff;
-  __syncthreads();
+  // S_h = pi[0 .. n): INT8 position of each member, 0xffff elsewhere (pi is
+  // a permutation of the blocks, so one scatter writes every entry)
 #pragma unroll
   for (int r = 0; r < EB; ++r) {
     const int k = threadIdx.x + r * CTL_NT;
-    if (k < n) pos[pk[r]] = (uint16_t)k;
+    if (k < NB) pos[pk[r]] = k < n ? (uint16_t)k : (uint16_t)0xffff;
   }
   __syncthreads();
   // references: Mt over the mixed block maxima, M16 over S_h (S_h lies in U)
