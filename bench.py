@@ -56,7 +56,7 @@ PASS_KERNELS = {
     "k_score_int8": ("kvq_score.hip",), "k_rescore_int8": ("kvq_score.hip", "kvq_rescore.h"),
     "k_select": ("kvq_select.hip", "kvq_blockops.h"),
     "k_eval": ("kvq_control.hip", "kvq_blockops.h", "kvq_rescore.h"),
-    "k_eval_decode": ("kvq_control.hip", "kvq_blockops.h", "kvq_mixed.h"),
+    "k_eval_decode": ("kvq_control.hip", "kvq_blockops.h", "kvq_mixed.h", "kvq_rescore.h"),
     "k_decide": ("kvq_control.hip", "kvq_blockops.h"), "k_decode_mixed": ("kvq_decode.hip", "kvq_mixed.h"),
     "k_combine": ("kvq_decode.hip",),
 }
@@ -531,7 +531,8 @@ def main():
         ["k_eval_decode"] if fused else ["k_eval", "k_decode_mixed"])
     roofline = {
         "bound": "hbm", "kernel": "quantized-tier pass: k_score_int8 (+ k_rescore_int8 when a step that "
-                                  "deferred its INT8 scores leaves blocks outside U) + k_select + "
+                                  "deferred its INT8 scores and starts with the group pass leaves "
+                                  "blocks outside U) + k_select + "
                                   + ("k_eval_decode (first controller round and mixed decode in one launch)"
                                      if fused else "k_eval + k_decode_mixed")
                                   + " (+ k_decide when a head is flagged) + k_combine",

@@ -852,6 +852,7 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
   Plan plan;
   kvq_status rs = KVQ_OK;
   int nres = 0;   // blocks outside U whose ŝ′ the first controller round computes
+  bool fused_resc = false;   // ... or the fused first round's decode waves, each for its own
   if (read_u) {
     int64_t ublocks = 0;
     rs = read_union(ctx, st, tab, plan, ublocks);
@@ -861,18 +862,23 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
     ctx->uppm[(size_t)layer] = all > 0 ? (int32_t)(ublocks * 1000000 / all) : 0;
     if (defer) {
       nres = outside_union(ctx, tab);
-      if (nres > 0)
-        HIPCK(ctx, hipMemcpyAsync(w.rlist, ctx->rlist_host, (size_t)nres * 4, hipMemcpyHostToDevice, st));
-      // the first controller round computes them beside the heads'
-      // evaluation when it runs on its own; a round fused with the decode
-      // (which reads them) or a step that starts with the group pass has a
-      // launch of its own for them, here
-      const bool own_round = !ctx->th.force_dense && !ctx->th.fp16_values && !eval_decode_fits(s, tab);
-      if (nres > 0 && !own_round) {
-        tm.open(TC_SCORE8);
-        HIPCK(ctx, launch_rescore_int8(s, ctx->t, w, tab, layer, (const uint16_t *)q, C, w.rlist, nres, st));
-        tm.close();
+      // Who computes them: in a first round fused with the decode (the one
+      // kernel that reads them), each decode wave for its own blocks; in a
+      // first round with a launch of its own, extra workgroups beside the
+      // heads' evaluation (from the list); in a step that starts with the
+      // group pass (FP16 values, forced dense), a launch of their own, here
+      const bool ctl = !ctx->th.force_dense && !ctx->th.fp16_values;
+      fused_resc = nres > 0 && ctl && eval_decode_fits(s, tab);
+      if (fused_resc) {
         nres = 0;
+      } else if (nres > 0) {
+        HIPCK(ctx, hipMemcpyAsync(w.rlist, ctx->rlist_host, (size_t)nres * 4, hipMemcpyHostToDevice, st));
+        if (!ctl) {
+          tm.open(TC_SCORE8);
+          HIPCK(ctx, launch_rescore_int8(s, ctx->t, w, tab, layer, (const uint16_t *)q, C, w.rlist, nres, st));
+          tm.close();
+          nres = 0;
+        }
       }
     }
   } else {
@@ -910,7 +916,9 @@ kvq_status kvq_decode_step(kvq_ctx *ctx, int32_t layer, int32_t n, const int32_t
     int fused_extra = -1;
     if (first) {
       tm.open(TC_DECODE);
-      HIPCK(ctx, launch_eval_decode(s, ctx->t, w, tab, layer, ctx->th, maxNB, &fused_extra, st));
+      HIPCK(ctx, launch_eval_decode(s, ctx->t, w, tab, layer, ctx->th, maxNB, (const uint16_t *)q, C,
+                                    fused_resc, &fused_extra, st));
+      if (fused_resc && fused_extra < 0) return fail(ctx, KVQ_EHIP, "fused first round not launched");
       if (fused_extra < 0) {
         tm.open(TC_CONTROL);
         HIPCK(ctx, launch_eval(s, ctx->t, w, tab, layer, ctx->th, maxNB, (const uint16_t *)q, C, w.rlist,

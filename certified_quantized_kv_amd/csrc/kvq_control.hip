@@ -341,12 +341,14 @@ __global__ __launch_bounds__(CTL_NT) void k_eval(Shape s, Tier1 t, Step w, SeqTa
 // heads, the rest run two decode chunks each (threads [0, 512) and [512,
 // 1024): the call's chunks in (sequence, KV head, chunk) order, a chunk past
 // the last computed and not stored).  The decode reads only U, the scores
-// and the block maxima, all final before this launch (a deferred step's
-// rescoring included), so the heads' latency-bound chains of phases run
-// beside its streaming work.
+// and the block maxima, all final before this launch except a deferring
+// step's ŝ′ outside U (resc != 0), which each decode wave computes for its
+// own blocks before reading them; the evaluation reads no ŝ′.  So the
+// heads' latency-bound chains of phases run beside the decode's streaming
+// work.
 template <int EB, int D, int CB>
 __global__ __launch_bounds__(CTL_NT) void k_eval_decode(Shape s, Tier1 t, Step w, SeqTab tab, int layer,
-                                                        Thresh th) {
+                                                        Thresh th, const uint16_t *q16, float C, int resc) {
   extern __shared__ __align__(16) unsigned long long keys[];
   __shared__ uint16_t pos[MAX_NB];
   __shared__ CtlShared sh;
@@ -371,8 +373,13 @@ __global__ __launch_bounds__(CTL_NT) void k_eval_decode(Shape s, Tier1 t, Step w
     rem -= cnt;
   }
   const int g = rem / tab.nch[i], ch = rem - g * tab.nch[i];
+  typedef DecLds<D, CB, 4, false> DL;
+  // a deferring step: each chunk's eight waves have a rescoring area each,
+  // after the two chunks' decode areas
+  RescoreLds<D> *rl = resc ? reinterpret_cast<RescoreLds<D> *>(reinterpret_cast<char *>(keys) + 2 * sizeof(DL)) + 8 * sub
+                           : nullptr;
   decode_chunk<D, CB, 4, false>(s, t, w, tab, layer, i, g, ch, live, threadIdx.x & 511,
-                                reinterpret_cast<DecLds<D, CB, 4, false> *>(keys)[sub]);
+                                reinterpret_cast<DL *>(keys)[sub], q16, C, rl);
 }
 
 // Part 2, one workgroup per (sequence, KV head): rung 1 decisions; a group
@@ -549,7 +556,8 @@ bool eval_decode_fits(const Shape &s, const SeqTab &tab) {
 }
 
 hipError_t launch_eval_decode(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab0,
-                              int layer, const Thresh &th, int maxNB, int *extra, hipStream_t st) {
+                              int layer, const Thresh &th, int maxNB, const uint16_t *q, float C,
+                              bool resc, int *extra, hipStream_t st) {
   *extra = -1;
   if (!eval_decode_fits(s, tab0)) return hipSuccess;
   const int n2 = max(64, pow2_at_least(maxNB));
@@ -567,11 +575,13 @@ hipError_t launch_eval_decode(const Shape &s, const Tier1 &t, const Step &w, con
   size_t lds = sort_lds_bytes(n2);
   const size_t dl = s.d == 128 ? (c32 ? sizeof(DecLds<128, 32, 4, false>) : sizeof(DecLds<128, 48, 4, false>))
                                : (c32 ? sizeof(DecLds<64, 32, 4, false>) : sizeof(DecLds<64, 48, 4, false>));
-  lds = std::max(lds, 2 * dl);
+  const size_t rl = resc ? 16 * (s.d == 128 ? sizeof(RescoreLds<128>) : sizeof(RescoreLds<64>)) : 0;
+  lds = std::max(lds, 2 * dl + rl);
   const int eb = (maxNB + CTL_NT - 1) / CTL_NT;   // blocks per thread of the evaluation
   hipError_t e;
 #define KVQ_ED(EB_, D_, CB_)                                                                        \
-  e = launch_k(k_eval_decode<EB_, D_, CB_>, grid, block, (uint32_t)lds, st, s, t, w, tab, layer, th)
+  e = launch_k(k_eval_decode<EB_, D_, CB_>, grid, block, (uint32_t)lds, st, s, t, w, tab, layer, th, q, C, \
+               resc ? 1 : 0)
 #define KVQ_ED_D(EB_)                          \
   if (s.d == 128) {                            \
     if (c32) KVQ_ED(EB_, 128, 32);             \

@@ -213,11 +213,14 @@ hipError_t launch_combine(const Shape &s, const Step &w, const SeqTab &tab, floa
 void mix_chunk_counts(const Shape &s, SeqTab &tab, int cb, int per_wg, int extra);
 // The first controller round and the speculative mixed decode in one launch
 // (k_eval_decode): the heads' evaluation beside the decode's chunks, two per
-// workgroup.  Sets *extra to the number of evaluation workgroups (for
-// launch_combine), or to -1 when the launch shape does not allow the fused
-// launch (then nothing was launched).
+// workgroup.  resc: the step's INT8 pass stored no ŝ′; the decode computes
+// those of the blocks outside U itself (q, C: the query and its scale).
+// Sets *extra to the number of evaluation workgroups (for launch_combine),
+// or to -1 when the launch shape does not allow the fused launch (then
+// nothing was launched).
 hipError_t launch_eval_decode(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,
-                              int layer, const Thresh &th, int maxNB, int *extra, hipStream_t st);
+                              int layer, const Thresh &th, int maxNB, const uint16_t *q, float C,
+                              bool resc, int *extra, hipStream_t st);
 // Whether launch_eval_decode takes this call (else it launches nothing).
 bool eval_decode_fits(const Shape &s, const SeqTab &tab);
 hipError_t launch_dense_vram(const Shape &s, const Step &w, const DenseArgs &a, int maxNB,

@@ -7,6 +7,7 @@
 #pragma once
 #include "kvq_device.h"
 #include "kvq_internal.h"
+#include "kvq_rescore.h"
 
 namespace kvq {
 
@@ -43,11 +44,15 @@ struct alignas(16) DecLds {
 // One chunk (sequence i, KV head g, chunk ch) on 2 NP waves: tid = the
 // thread's index among them.  Every thread of the workgroup reaches the same
 // two barriers (a workgroup of two such thread sets runs two chunks); a set
-// with live = false computes its chunk and stores nothing.
+// with live = false computes its chunk and stores nothing.  RL != nullptr (a
+// step whose INT8 pass stored no ŝ′): each wave first computes ŝ′ of its own
+// blocks outside U (q16, C: the query and its scale, as the pass), so the
+// scores it reads next are its own stores (RL: one area per wave).
 template <int D, int CB, int NP, bool FV>
 __device__ inline void decode_chunk(const Shape &s, const Tier1 &t, const Step &w, const SeqTab &tab,
                                     int layer, int i, int g, int ch, bool live, int tid,
-                                    DecLds<D, CB, NP, FV> &L) {
+                                    DecLds<D, CB, NP, FV> &L, const uint16_t *q16 = nullptr,
+                                    float C = 0.0f, RescoreLds<D> *RL = nullptr) {
   constexpr int NT = D / 16;                     // 16-channel tiles
   constexpr int NG = D / VGROUP;                 // value groups (two tiles each)
   constexpr int NTW = NT / 2, NGW = NG / 2;      // tiles and groups of one wave
@@ -268,6 +273,15 @@ __device__ inline void decode_chunk(const Shape &s, const Tier1 &t, const Step &
   // registers and each wait covers only the older stage's loads; blocks with
   // FP16 values are skipped here and accumulated afterwards
   Stage st[2];
+  if (RL != nullptr && live) {
+    // this wave's blocks outside U, before any stage register is taken (so
+    // the value loads wait for the flags here); both channel halves of a
+    // block compute the same bits, and no wave reads another's stores
+    const unsigned long long outside = ~__ballot(lane < nblk && uf != 0) & (nblk >= 64 ? ~0ull : (1ull << nblk) - 1ull);
+    if (outside)
+      for (int k = pair; k < nblk; k += NP)
+        if ((outside >> k) & 1ull) rescore_block<D, false>(s, t, w, tab, layer, q16, C, i, g, b0 + k, RL[wave]);
+  }
   fetch_vm(st[0], min(b0 + pair, b1 - 1));
   if (PW > 1) fetch_vm(st[1], min(b0 + pair + NP, b1 - 1));
   umask = __ballot(lane < nblk && uf != 0);

@@ -7,7 +7,10 @@ selection; the scores are the same canonical arithmetic either way, so every
 decision and output must be bit-identical to a step that stored them all
 (KVQ_FLAG_ALL_SCORES), and equal to the oracle's wherever the step defines
 them.  The cases lower the coverage target and loosen the tolerances so that
-U leaves blocks out and the rescoring kernel has work.
+U leaves blocks out and the rescoring has work, on each of its three routes:
+the decode waves of a first round fused with the decode (each for its own
+blocks), extra workgroups of the evaluation's launch (separate launches), and
+a launch of its own (FP16 values: the step starts with the group pass).
 """
 import numpy as np
 import pytest
