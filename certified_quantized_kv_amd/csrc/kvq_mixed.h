@@ -118,26 +118,36 @@ __device__ inline void decode_chunk(const Shape &s, const Tier1 &t, const Step &
   };
   // value metadata and codes (no flag needed), then the scores (FP16 keys'
   // on blocks of U, INT8 keys' elsewhere)
+  // addresses: a wave-uniform base per block (and head) plus a 32-bit lane
+  // offset, so the loads take their base from scalar registers
   auto fetch_vm = [&](Stage &st, int bb) {
-    const int tk = min(bb * BLOCK + lane, T - 1);
-    const uint32_t *mp = t.vmeta + (u * s.Tmax + tk) * NG + half * NGW;
+    // the lane's token, clamped (bb is a block of the sequence: in [0, 64))
+    const uint32_t tl = (uint32_t)min(lane, T - 1 - bb * BLOCK) & (BLOCK - 1);
+    const uint32_t *mp = t.vmeta + (u * s.Tmax + (size_t)bb * BLOCK) * NG + half * NGW;
     if constexpr (NGW == 2) {
-      const u32x2 m = __builtin_nontemporal_load((const u32x2 *)mp);
+      const u32x2 m = __builtin_nontemporal_load((const u32x2 *)(mp + tl * (uint32_t)NG));
       st.meta[0] = m.x, st.meta[1] = m.y;
     } else {
-      st.meta[0] = __builtin_nontemporal_load(mp);
+      st.meta[0] = __builtin_nontemporal_load(mp + tl * (uint32_t)NG);
     }
-    const uint8_t *vc = t.vcodes + (u * s.NBmax + bb) * (size_t)(32 * D);
+    const u32x2 *vc = (const u32x2 *)(t.vcodes + (u * s.NBmax + bb) * (size_t)(32 * D)) + half * NTW * 64;
 #pragma unroll
-    for (int k = 0; k < NTW; ++k)
-      st.pk[k] = __builtin_nontemporal_load((const u32x2 *)(vc + (size_t)((half * NTW + k) * 64 + lane) * 8));
+    for (int k = 0; k < NTW; ++k) st.pk[k] = __builtin_nontemporal_load(vc + (uint32_t)(k * 64 + lane));
   };
   auto fetch_sc = [&](Stage &st, int bb, unsigned long long umask) {
-    const int tk = min(bb * BLOCK + lane, T - 1);
-    const bool up = (umask >> (bb - b0)) & 1ull;
-    const float *src = (up ? w.sp : w.shat) + ((size_t)i * s.Hq + g * G) * s.Tmax + tk;
+    const uint32_t tl = (uint32_t)min(lane, T - 1 - bb * BLOCK) & (BLOCK - 1);
+    const bool up = __builtin_amdgcn_readfirstlane((int)((umask >> (bb - b0)) & 1ull)) != 0;
+    const float *src = (up ? w.sp : w.shat) + ((size_t)i * s.Hq + g * G) * s.Tmax + (size_t)bb * BLOCK;
 #pragma unroll
-    for (int h = 0; h < 4; ++h) st.x[h] = src[(size_t)min(h, G - 1) * s.Tmax];
+    for (int h = 0; h < 4; ++h) {
+      // the head's row base pinned to scalar registers (without it the
+      // compiler adds the head offsets to the per-lane address in 64 bits)
+      const uint64_t a = (uint64_t)(src + (size_t)min(h, G - 1) * s.Tmax);
+      typedef const __attribute__((address_space(1))) float gfloat;
+      gfloat *sh = (gfloat *)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(a >> 32)) << 32) |
+                              (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a));
+      st.x[h] = sh[tl];
+    }
   };
   // quantized values: p*s as fixed point against the INT4 codes
   // byte selectors of the quad transpose (v_perm: bytes 0-3 from the second
@@ -181,11 +191,12 @@ __device__ inline void decode_chunk(const Shape &s, const Tier1 &t, const Step &
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
         offacc[h][j] = fmaf(p[h], of[j], offacc[h][j]);
-        // rint(p s 2^-e) + 0x808080 in one rounding (the sum stays below
-        // 2^24, where fp32 spacing is 1); the XOR leaves three signed bytes
-        // L0 + 2^8 L1 + 2^16 L2 = rint(p s 2^-e), each in [-128, 127], and a
-        // zero fourth byte
-        const uint32_t Bv = (uint32_t)fmaf(p[h], sce, 8421504.0f) ^ 0x808080u;
+        // A + 0x808080 with A = rint(p s 2^-e) in [0, 2^22) (p, s >= 0), in
+        // one rounding: a float in [2^23, 2^24), where the spacing is 1, so
+        // its bits are 0x4B000000 | (A + 0x8080).  One XOR then leaves three
+        // signed bytes L0 + 2^8 L1 + 2^16 L2 = A, each in [-128, 127], and a
+        // zero fourth byte (the same bytes as (A + 0x808080) ^ 0x808080)
+        const uint32_t Bv = __float_as_uint(fmaf(p[h], sce, 8421504.0f)) ^ 0x4B008080u;
         // 4 x 4 byte transpose inside each quad of lanes (tokens 4 m .. 4 m + 3):
         // lane 4 m + l then holds limb l of the four tokens, one dword of row
         // 4 h + l (row 4 h + 3 gets the zero bytes)
