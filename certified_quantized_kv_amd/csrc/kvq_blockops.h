@@ -215,10 +215,15 @@ struct NoPlace {
   __device__ void operator()(unsigned long long, int) const {}
 };
 
-// RK = keys per thread: the caller guarantees n <= RK * NT.
-template <int NT, int RK = (MAX_NB + NT - 1) / NT, class OnPlace = NoPlace>
-__device__ __forceinline__ bool sort_desc_u64(unsigned long long *keys, int n, int cap,
-                                              OnPlace on_place = OnPlace()) {
+// The sort with the keys already in the callers' registers: kv[r] is the key
+// at position t + r NT of keys[0 .. n) (thread t), and keys[] holds them too
+// (the comparison network reads them there), written by the caller before the
+// call; the sort's own LDS (tmp, the bucket counters) is not touched by the
+// caller before it, so the sort starts without a barrier.  RK = keys per
+// thread: the caller guarantees n <= RK * NT.
+template <int NT, int RK, class OnPlace = NoPlace>
+__device__ __forceinline__ bool sort_desc_u64_regs(const unsigned long long (&kv)[RK], unsigned long long *keys,
+                                                   int n, int cap, OnPlace on_place = OnPlace()) {
   constexpr int SB = SORT_BUCKETS;
   constexpr int PER = SB / NT;           // counters per thread in the scan
   static_assert(SB % NT == 0, "bucket count");
@@ -230,16 +235,12 @@ __device__ __forceinline__ bool sort_desc_u64(unsigned long long *keys, int n, i
   __shared__ uint32_t red[2][NT / 64];
   __shared__ int wsum[2][NT / 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  __syncthreads();
-  // the thread's keys p = t + r NT; image 1: the key's own binary32 image,
-  // over the images' range
-  unsigned long long kv[RK];
+  // image 1: the key's own binary32 image, over the images' range
   int bk[RK], slot[RK];
   uint32_t lo = 0xffffffffu, hi = 0u;
 #pragma unroll
   for (int r = 0; r < RK; ++r) {
     const int p = threadIdx.x + r * NT;
-    kv[r] = p < n ? keys[p] : 0ull;
     if (p < n) {
       const uint32_t f = key_image(kv[r]);
       lo = min(lo, f);
@@ -396,6 +397,20 @@ __device__ __forceinline__ bool sort_desc_u64(unsigned long long *keys, int n, i
   }
   __syncthreads();
   return true;
+}
+
+// The sort of keys[0 .. n) in LDS (written by the caller before the call).
+template <int NT, int RK = (MAX_NB + NT - 1) / NT, class OnPlace = NoPlace>
+__device__ __forceinline__ bool sort_desc_u64(unsigned long long *keys, int n, int cap,
+                                              OnPlace on_place = OnPlace()) {
+  __syncthreads();
+  unsigned long long kv[RK];
+#pragma unroll
+  for (int r = 0; r < RK; ++r) {
+    const int p = threadIdx.x + r * NT;
+    kv[r] = p < n ? keys[p] : 0ull;
+  }
+  return sort_desc_u64_regs<NT, RK>(kv, keys, n, cap, on_place);
 }
 
 // Inclusive scan of per-thread u64 values over a workgroup of NT threads

@@ -51,19 +51,21 @@ __global__ __launch_bounds__(SEL_NT) void k_select(Shape s, Step w, SeqTab tab, 
 #pragma unroll
   for (int k = 1; k < SEL_NT / 64; ++k) M = fmaxf(M, red[k]);
 
+  // the keys stay in registers for the sort (and go to LDS for its
+  // comparison-network fallback)
+  unsigned long long kv[EB];
 #pragma unroll
   for (int r = 0; r < EB; ++r) {
     const int b = threadIdx.x + r * SEL_NT;
-    if (b >= n2) break;
-    unsigned long long key = 0ull;
+    kv[r] = 0ull;
     if (b < NB) {
       const uint32_t W = (uint32_t)floorf((float)lh[r] * exp2k(mh[r] - M));
       w.What[base + b] = W;
-      key = ((unsigned long long)W << 32) | (unsigned long long)(0xffffffffu - (uint32_t)b);
+      kv[r] = ((unsigned long long)W << 32) | (unsigned long long)(0xffffffffu - (uint32_t)b);
     }
-    keys[b] = key;
+    if (b < n2) keys[b] = kv[r];
   }
-  sort_desc_u64<SEL_NT, EB>(keys, NB, n2);
+  sort_desc_u64_regs<SEL_NT, EB>(kv, keys, NB, n2);
 
   // pi, then prefix sums of the sorted weights: thread t owns positions
   // [t*per, (t+1)*per)
