@@ -64,7 +64,9 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 // data that is reused.
 // ST: the pass stores every block's INT8 scores ŝ′; without it only the
 // block ingredients are stored, and the blocks that end up outside U get
-// their ŝ′ from k_rescore_int8 after the selection.
+// their ŝ′ after the selection (rescore_block, kvq_rescore.h: in the decode
+// waves of a fused first round, in workgroups beside the heads' evaluation,
+// or in k_rescore_int8).
 template <int D, bool ST>
 __global__ __launch_bounds__(256, 4) void k_score_int8(Shape s, Tier1 t, Step w, SeqTab tab, int layer,
                                                     const uint16_t *__restrict__ q16, float C) {
