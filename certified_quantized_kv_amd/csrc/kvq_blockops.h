@@ -215,7 +215,7 @@ struct NoPlace {
   __device__ void operator()(unsigned long long, int) const {}
 };
 
-// The sort with the keys already in the callers' registers: kv[r] is the key
+// The sort with the keys already in the caller's registers: kv[r] is the key
 // at position t + r NT of keys[0 .. n) (thread t), and keys[] holds them too
 // (the comparison network reads them there), written by the caller before the
 // call; the sort's own LDS (tmp, the bucket counters) is not touched by the

@@ -286,8 +286,10 @@ __device__ inline void decode_chunk(const Shape &s, const Tier1 &t, const Step &
   Stage st[2];
   if (RL != nullptr && live) {
     // this wave's blocks outside U, before any stage register is taken (so
-    // the value loads wait for the flags here); both channel halves of a
-    // block compute the same bits, and no wave reads another's stores
+    // the value loads wait for the flags here).  Both channel halves of a
+    // block compute and store the same bits, and each reads the scores only
+    // after its own stores: whichever store lands last, the bits it reads
+    // are its own results
     const unsigned long long outside = ~__ballot(lane < nblk && uf != 0) & (nblk >= 64 ? ~0ull : (1ull << nblk) - 1ull);
     if (outside)
       for (int k = pair; k < nblk; k += NP)
