@@ -8,7 +8,11 @@ so K* ranges from a few blocks to all of them) and the controller's
 thresholds (coverage, eps_key, v_tol, rho_min, widening rounds), so that the
 ladder's paths (widening, value promotion, rung 3, rung 4) all occur across
 the sweep.  Every decision-side array is compared bit for bit with the
-oracle and every output within max-abs 2e-3 (the shared compare())."""
+oracle and every output within max-abs 2e-3 (the shared compare()).  Each
+case runs twice: with the INT8 scores stored by the scoring pass, and with
+them deferred (the pass stores none; the blocks outside U are rescored after
+the selection, in the decode waves of a fused first round or beside the
+heads' evaluation, and later rounds read those scores)."""
 import numpy as np
 import pytest
 
@@ -57,13 +61,19 @@ def _sweep_case(seed):
     return Case(name, Hq, Hkv, d, rows, **cfg)
 
 
+@pytest.mark.parametrize("deferred", [False, True], ids=["stored", "deferred"])
 @pytest.mark.parametrize("seed", range(16))
-def test_random_sweep(env, seed):
+def test_random_sweep(env, seed, deferred):
     kvq, torch, orc = env
     case = _sweep_case(seed)
     lens = [s[0].shape[0] + (0 if s[3] is None else s[3][0].shape[0]) for s in case.seqs]
-    log(f"[sweep] {case.name} lengths {lens} cfg {case.cfg}")
-    gpu = run_gpu(kvq, torch, case)
+    log(f"[sweep] {case.name} lengths {lens} cfg {case.cfg} deferred {deferred}")
+    kvq.set_defer_scores(0 if deferred else 1000001)
+    try:
+        gpu = run_gpu(kvq, torch, case)
+    finally:
+        kvq.set_defer_scores(-1)
+    assert gpu["stats"]["scores_deferred"] == int(deferred)
     ref = run_oracle(orc, case)
     compare(case, gpu, ref)
     levels = np.concatenate([r.level for r, _ in ref])
