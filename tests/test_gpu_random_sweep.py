@@ -21,7 +21,7 @@ from gpu_helpers import Case, compare, log, run_gpu, run_oracle
 
 pytestmark = pytest.mark.gpu
 
-LAYOUTS = [(4, 1), (8, 2), (8, 4), (16, 4), (32, 8)]
+LAYOUTS = [(4, 1), (8, 2), (8, 4), (16, 4), (32, 8), (8, 8), (16, 16)]
 
 
 @pytest.fixture(scope="module")
