@@ -35,6 +35,9 @@ namespace kvq {
 
 
 constexpr int CTL_NT = 1024;
+// the evaluation's per-thread sums in LDS, six per thread (its dynamic LDS
+// holds at least this much)
+constexpr size_t EVAL_TOT_BYTES = 6 * CTL_NT * sizeof(unsigned long long);
 constexpr double W_UP = 1.0 + 0x1p-12;
 constexpr double W_DN = 1.0 - 0x1p-12;
 
@@ -194,32 +197,43 @@ __device__ void evaluate_head(const Shape &s, const Step &w, const Thresh &th, i
       const long long dd = (long long)pos[b] - (long long)j;
       ssd += (unsigned long long)(dd * dd);
     }
+    __syncthreads();                      // keys[] is read; its LDS is reused below
   }
-  // one reduction for the E_key sums, the E_val numerator and the ranks
-  unsigned long long v4[6] = {den, num, sub, cap, numv, ssd};
+  // one reduction for the E_key sums, the E_val numerator and the ranks:
+  // every thread's six sums go through LDS (the sort's area, free again),
+  // wave k < 6 adds quantity k over the threads, thread 0 takes the totals
+  // (integers: exact in any order; far fewer cross-lane steps than six
+  // reductions in each of the sixteen waves)
+  unsigned long long *tot = keys;         // [6][CTL_NT]
+  {
+    const unsigned long long v[6] = {den, num, sub, cap, numv, ssd};
 #pragma unroll
-  for (int k = 0; k < 6; ++k) v4[k] = wave_sum_u64(v4[k]);
-  if ((threadIdx.x & 63) == 0) {
-#pragma unroll
-    for (int k = 0; k < 6; ++k) sred[k][threadIdx.x >> 6] = v4[k];
+    for (int k = 0; k < 6; ++k) tot[k * CTL_NT + threadIdx.x] = v[k];
   }
   __syncthreads();
+  {
+    const int wv = threadIdx.x >> 6, ln = threadIdx.x & 63;
+    if (wv < 6) {
+      unsigned long long r = 0ull;
 #pragma unroll
-  for (int k = 0; k < 6; ++k) {
-    unsigned long long r = 0ull;
-#pragma unroll
-    for (int q = 0; q < CTL_NT / 64; ++q) r += sred[k][q];
-    v4[k] = r;
+      for (int j = 0; j < CTL_NT / 64; ++j) r += tot[wv * CTL_NT + ln + 64 * j];
+      r = wave_sum_u64(r);
+      if (ln == 0) sred[wv][0] = r;
+    }
   }
-  double ek;
-  if (v4[3]) {
-    ek = 1.0;
-  } else {
-    const long long D = (long long)v4[0] - (long long)v4[2];
-    ek = (D <= 0) ? 1.0 : fmin(1.0, (double)v4[1] / (double)D);
-  }
-  ssd = v4[5];
+  __syncthreads();
+  unsigned long long v4[6];
   if (threadIdx.x == 0) {
+#pragma unroll
+    for (int k = 0; k < 6; ++k) v4[k] = sred[k][0];
+    double ek;
+    if (v4[3]) {
+      ek = 1.0;
+    } else {
+      const long long D = (long long)v4[0] - (long long)v4[2];
+      ek = (D <= 0) ? 1.0 : fmin(1.0, (double)v4[1] / (double)D);
+    }
+    ssd = v4[5];
     const unsigned long long nn = (unsigned long long)n;
     const bool ok = (n <= 1) ||
                     (6000000ull * ssd <= (unsigned long long)(1000000 - th.rho_ppm) * nn * (nn * nn - 1ull));
@@ -534,7 +548,7 @@ hipError_t launch_eval(const Shape &s, const Tier1 &t, const Step &w, const SeqT
   const int R = rcount > 0 ? std::min((rcount + CTL_NT / 64 - 1) / (CTL_NT / 64), 2 * std::max(s.ncu, 1)) : 0;
   const dim3 grid(s.Hq + R, tab.n), block(CTL_NT);
   const size_t rl = R ? (CTL_NT / 64) * (s.d == 128 ? sizeof(RescoreLds<128>) : sizeof(RescoreLds<64>)) : 0;
-  const uint32_t lds = (uint32_t)std::max(sort_lds_bytes(n2), rl);
+  const uint32_t lds = (uint32_t)std::max({sort_lds_bytes(n2), rl, EVAL_TOT_BYTES});
   switch ((maxNB + CTL_NT - 1) / CTL_NT) {   // blocks per thread
     case 1: return launch_k(k_eval<1>, grid, block, lds, st, s, t, w, tab, layer, th, q, C, rlist, rcount);
     case 2: return launch_k(k_eval<2>, grid, block, lds, st, s, t, w, tab, layer, th, q, C, rlist, rcount);
@@ -576,7 +590,7 @@ hipError_t launch_eval_decode(const Shape &s, const Tier1 &t, const Step &w, con
   const size_t dl = s.d == 128 ? (c32 ? sizeof(DecLds<128, 32, 4, false>) : sizeof(DecLds<128, 48, 4, false>))
                                : (c32 ? sizeof(DecLds<64, 32, 4, false>) : sizeof(DecLds<64, 48, 4, false>));
   const size_t rl = resc ? 16 * (s.d == 128 ? sizeof(RescoreLds<128>) : sizeof(RescoreLds<64>)) : 0;
-  lds = std::max(lds, 2 * dl + rl);
+  lds = std::max({lds, 2 * dl + rl, EVAL_TOT_BYTES});
   const int eb = (maxNB + CTL_NT - 1) / CTL_NT;   // blocks per thread of the evaluation
   hipError_t e;
 #define KVQ_ED(EB_, D_, CB_)                                                                        \
