@@ -88,16 +88,18 @@ __global__ __launch_bounds__(SEL_NT) void k_select(Shape s, Step w, SeqTab tab, 
   unsigned long long total;
   // (sbuf is not written again: no barrier after the scan)
   const unsigned long long incl = block_incl_scan_u64<SEL_NT, false>(own, sbuf, &total);
-  const unsigned long long need = (unsigned long long)tau_ppm * total;
+  // 10^6 pre >= tau_ppm total  <=>  pre >= ceil(tau_ppm total / 10^6)
+  // (integers below 2^63), so each candidate costs one 64-bit compare
+  const unsigned long long need = ((unsigned long long)tau_ppm * total + 999999ull) / 1000000ull;
   __shared__ int kst;
   unsigned long long pre = incl - own;
 #pragma unroll
   for (int k = 0; k < PMAX; ++k) {
     const int p = p0 + k;                       // K* candidate p + 1
     if (k >= per || p >= NB) break;
-    const bool ok_prev = (p == 0) ? false : (1000000ull * pre >= need);
+    const bool ok_prev = (p == 0) ? false : (pre >= need);
     pre += wk[k];
-    const bool ok = 1000000ull * pre >= need;
+    const bool ok = pre >= need;
     if (ok && !ok_prev) {
       w.k0[(size_t)i * s.Hq + hq] = p + 1;
       w.ssize[(size_t)i * s.Hq + hq] = p + 1;
