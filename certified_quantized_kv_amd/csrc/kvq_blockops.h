@@ -13,6 +13,64 @@ __host__ __device__ inline int pow2_at_least(int n) {
   return p;
 }
 
+// Combining the partials of a workgroup's waves (at most 16, written to LDS
+// by one lane each and read after a barrier): lane k < nw of every wave
+// reads partial k and a scan over the first row of 16 lanes (DPP row shifts,
+// zero shifted in) does the adds, so each wave spends a few vector steps
+// instead of one add per partial in every one of its lanes.  Results from
+// lanes of that row (readlane: wave-uniform).  The whole wave must be active.
+__device__ __forceinline__ unsigned long long row0_scan_u64(unsigned long long x) {
+  x += dpp_u64<0x111, 0xf>(x);
+  x += dpp_u64<0x112, 0xf>(x);
+  x += dpp_u64<0x114, 0xf>(x);
+  x += dpp_u64<0x118, 0xf>(x);
+  return x;
+}
+__device__ __forceinline__ unsigned long long readlane_u64(unsigned long long x, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), l);
+  return ((unsigned long long)hi << 32) | lo;
+}
+// sum of partials [0, wave) and of all nw partials
+__device__ __forceinline__ void wave_partials_u64(const unsigned long long *buf, int nw, int wave,
+                                                  unsigned long long &before, unsigned long long &all) {
+  const int lane = threadIdx.x & 63;
+  const unsigned long long x = row0_scan_u64(lane < nw ? buf[lane] : 0ull);
+  all = readlane_u64(x, nw - 1);
+  before = wave > 0 ? readlane_u64(x, wave - 1) : 0ull;
+}
+__device__ __forceinline__ int wave_partials_before_i32(const int *buf, int nw, int wave) {
+  const int lane = threadIdx.x & 63;
+  uint32_t x = lane < nw ? (uint32_t)buf[lane] : 0u;
+  x += dpp_u32<0x111, 0xf>(x);
+  x += dpp_u32<0x112, 0xf>(x);
+  x += dpp_u32<0x114, 0xf>(x);
+  x += dpp_u32<0x118, 0xf>(x);
+  return wave > 0 ? __builtin_amdgcn_readlane((int)x, wave - 1) : 0;
+}
+// largest of nw non-negative partials (the others read as 0)
+__device__ __forceinline__ int wave_partials_max_i32(const int *buf, int nw) {
+  const int lane = threadIdx.x & 63;
+  int x = lane < nw ? buf[lane] : 0;
+  x = max(x, (int)dpp_u32<0x111, 0xf>((uint32_t)x));
+  x = max(x, (int)dpp_u32<0x112, 0xf>((uint32_t)x));
+  x = max(x, (int)dpp_u32<0x114, 0xf>((uint32_t)x));
+  x = max(x, (int)dpp_u32<0x118, 0xf>((uint32_t)x));
+  return __builtin_amdgcn_readlane(x, nw - 1);
+}
+
+// largest of nw float partials (-inf shifted in)
+__device__ __forceinline__ float wave_partials_max_f32(const float *buf, int nw) {
+  const int lane = threadIdx.x & 63;
+  constexpr int NEG = (int)0xff800000u;   // -inf
+  float x = lane < nw ? buf[lane] : -INFINITY;
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(NEG, __float_as_int(x), 0x111, 0xf, 0xf, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(NEG, __float_as_int(x), 0x112, 0xf, 0xf, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(NEG, __float_as_int(x), 0x114, 0xf, 0xf, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(NEG, __float_as_int(x), 0x118, 0xf, 0xf, false)));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), nw - 1));
+}
+
 // Block-wide exclusive scan of small counts (blockDim multiple of 64); every
 // thread adds up the wave totals below its own.  tmp holds blockDim / 64
 // entries and is free again after the caller's next barrier.
@@ -234,7 +292,7 @@ __device__ __forceinline__ bool sort_desc_u64_regs(const unsigned long long (&kv
   __shared__ unsigned long long kred[2][NT / 64];
   __shared__ uint32_t red[2][NT / 64];
   __shared__ int wsum[2][NT / 64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // image 1: the key's own binary32 image, over the images' range
   int bk[RK], slot[RK];
   uint32_t lo = 0xffffffffu, hi = 0u;
@@ -328,8 +386,7 @@ __device__ __forceinline__ bool sort_desc_u64_regs(const unsigned long long (&kv
     if (lane == 63) wsum[0][wave] = xs;
     if (lane == 0) wsum[1][wave] = big;
     __syncthreads();
-#pragma unroll
-    for (int k = 0; k < NT / 64; ++k) big = max(big, wsum[1][k]);
+    big = wave_partials_max_i32(wsum[1], NT / 64);
     if (big <= SORT_MAX_BUCKET) break;
     if (pass == 1) {
       // clustered keys: comparison network instead (the keys are untouched)
@@ -344,10 +401,7 @@ __device__ __forceinline__ bool sort_desc_u64_regs(const unsigned long long (&kv
     __syncthreads();                     // wsum and cur are written again by pass 1
   }
   // exclusive prefix of the counts -> base
-  int before = 0;
-#pragma unroll
-  for (int k = 0; k < NT / 64; ++k)
-    if (k < wave) before += wsum[0][k];
+  const int before = wave_partials_before_i32(wsum[0], NT / 64, wave);
   int run = before + xs - own;
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
@@ -420,17 +474,13 @@ __device__ __forceinline__ bool sort_desc_u64(unsigned long long *keys, int n, i
 template <int NT, bool REUSE = true>
 __device__ inline unsigned long long block_incl_scan_u64(unsigned long long v, unsigned long long *buf,
                                                          unsigned long long *total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  static_assert(NT / 64 <= 16, "one partial per lane of a row");
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const unsigned long long x = wave_incl_scan_u64(v);
   if (lane == 63) buf[wave] = x;
   __syncthreads();
-  unsigned long long before = 0ull, all = 0ull;
-#pragma unroll
-  for (int k = 0; k < NT / 64; ++k) {
-    const unsigned long long c = buf[k];
-    if (k < wave) before += c;
-    all += c;
-  }
+  unsigned long long before, all;
+  wave_partials_u64(buf, NT / 64, wave, before, all);
   if (REUSE) __syncthreads();
   *total = all;
   return x + before;

@@ -143,12 +143,8 @@ __device__ void evaluate_head(const Shape &s, const Step &w, const Thresh &th, i
     mred[1][threadIdx.x >> 6] = m16loc;
   }
   __syncthreads();
-  float Mt = mred[0][0], M16 = mred[1][0];
-#pragma unroll
-  for (int k = 1; k < CTL_NT / 64; ++k) {
-    Mt = fmaxf(Mt, mred[0][k]);
-    M16 = fmaxf(M16, mred[1][k]);
-  }
+  const float Mt = wave_partials_max_f32(mred[0], CTL_NT / 64);
+  const float M16 = wave_partials_max_f32(mred[1], CTL_NT / 64);
   // mixed weights, E_key sums and the E_val numerator with no value
   // promoted; FP16 weights and sort keys of S_h
   unsigned long long den = 0ull, num = 0ull, sub = 0ull, cap = 0ull, numv = 0ull;

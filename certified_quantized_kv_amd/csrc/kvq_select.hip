@@ -47,9 +47,7 @@ __global__ __launch_bounds__(SEL_NT) void k_select(Shape s, Step w, SeqTab tab, 
   m = bfly_max<64>(m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
-  float M = red[0];
-#pragma unroll
-  for (int k = 1; k < SEL_NT / 64; ++k) M = fmaxf(M, red[k]);
+  const float M = wave_partials_max_f32(red, SEL_NT / 64);
 
   // the keys stay in registers for the sort (and go to LDS for its
   // comparison-network fallback)
