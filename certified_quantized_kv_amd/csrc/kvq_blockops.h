@@ -59,6 +59,26 @@ __device__ __forceinline__ int wave_partials_max_i32(const int *buf, int nw) {
   return __builtin_amdgcn_readlane(x, nw - 1);
 }
 
+// smallest and largest of nw u32 partials (the identities shifted in)
+__device__ __forceinline__ uint32_t wave_partials_min_u32(const uint32_t *buf, int nw) {
+  const int lane = threadIdx.x & 63;
+  constexpr int ALL = -1;
+  uint32_t x = lane < nw ? buf[lane] : 0xffffffffu;
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(ALL, (int)x, 0x111, 0xf, 0xf, false));
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(ALL, (int)x, 0x112, 0xf, 0xf, false));
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(ALL, (int)x, 0x114, 0xf, 0xf, false));
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(ALL, (int)x, 0x118, 0xf, 0xf, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, nw - 1);
+}
+__device__ __forceinline__ uint32_t wave_partials_max_u32(const uint32_t *buf, int nw) {
+  const int lane = threadIdx.x & 63;
+  uint32_t x = lane < nw ? buf[lane] : 0u;
+  x = max(x, dpp_u32<0x111, 0xf>(x));
+  x = max(x, dpp_u32<0x112, 0xf>(x));
+  x = max(x, dpp_u32<0x114, 0xf>(x));
+  x = max(x, dpp_u32<0x118, 0xf>(x));
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, nw - 1);
+}
 // largest of nw float partials (-inf shifted in)
 __device__ __forceinline__ float wave_partials_max_f32(const float *buf, int nw) {
   const int lane = threadIdx.x & 63;
@@ -313,13 +333,8 @@ __device__ __forceinline__ bool sort_desc_u64_regs(const unsigned long long (&kv
   }
   for (int k = threadIdx.x; k < SB; k += NT) cur[k] = 0;
   __syncthreads();
-  lo = red[0][0];
-  hi = red[1][0];
-#pragma unroll
-  for (int k = 1; k < NT / 64; ++k) {
-    lo = min(lo, red[0][k]);
-    hi = max(hi, red[1][k]);
-  }
+  lo = wave_partials_min_u32(red[0], NT / 64);
+  hi = wave_partials_max_u32(red[1], NT / 64);
   // image 2 (used when image 1 crowds a bucket): key - smallest key on a
   // linear scale, which separates keys that agree in their leading bits
   bool rel = false;
