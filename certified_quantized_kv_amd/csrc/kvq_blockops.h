@@ -441,25 +441,19 @@ __device__ __forceinline__ bool sort_desc_u64_regs(const unsigned long long (&kv
   }
   if (big > 1) {
     __syncthreads();
-    // place inside the bucket: keys ahead = larger keys (equal keys by slot)
+    // place inside the bucket: keys ahead = larger keys (the keys are
+    // distinct, so that count is the rank)
 #pragma unroll
     for (int r = 0; r < RK; ++r) {
       if (threadIdx.x + r * NT >= n || b1[r] - b0[r] == 1) continue;
       const unsigned long long k = kv[r];
-      const int me = b0[r] + slot[r];
       int rk = 0;
       int q = b0[r];
       for (; q + 4 <= b1[r]; q += 4) {
         const unsigned long long y0 = tmp[q], y1 = tmp[q + 1], y2 = tmp[q + 2], y3 = tmp[q + 3];
-        rk += (y0 > k || (y0 == k && q < me)) ? 1 : 0;
-        rk += (y1 > k || (y1 == k && q + 1 < me)) ? 1 : 0;
-        rk += (y2 > k || (y2 == k && q + 2 < me)) ? 1 : 0;
-        rk += (y3 > k || (y3 == k && q + 3 < me)) ? 1 : 0;
+        rk += (y0 > k ? 1 : 0) + (y1 > k ? 1 : 0) + (y2 > k ? 1 : 0) + (y3 > k ? 1 : 0);
       }
-      for (; q < b1[r]; ++q) {
-        const unsigned long long y = tmp[q];
-        rk += (y > k || (y == k && q < me)) ? 1 : 0;
-      }
+      for (; q < b1[r]; ++q) rk += tmp[q] > k ? 1 : 0;
       keys[b0[r] + rk] = k;
       on_place(k, b0[r] + rk);
     }
