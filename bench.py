@@ -848,6 +848,16 @@ def other_workloads(a, kvq, S, np, torch, gen, dev, pass_summary):
     Hq, Hkv, d = w4.Hq, w4.Hkv, w4.d
     t1b = kvq.tier1_bytes_per_token(d)
 
+    def streaming_fracs(med, n_tok):
+        # the two streaming kernels against their own algorithmic bytes: INT8
+        # codes + key metadata, and INT4 codes + value metadata + eta (the
+        # decode's launch also holds the first controller round when
+        # ms_control is zero)
+        dec = "k_eval_decode" if med["ms_control"] == 0.0 else "k_decode_mixed"
+        by = {"k_score_int8": (med["ms_score_int8"], n_tok * Hkv * (d + 4 * d / 64)),
+              dec: (med["ms_decode"], n_tok * Hkv * (d / 2 + 4 * d / 32 + 4 / 64))}
+        return {k: round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4) for k, (ms, b) in by.items() if ms > 0}
+
     def run(name, cx, lens, qfn, steps, layers, extra=None):
         recs = []
         for s in range(steps):
@@ -866,7 +876,8 @@ def other_workloads(a, kvq, S, np, torch, gen, dev, pass_summary):
              "kv_tokens_per_s": round(n_tok / (med["ms_total"] * 1e-3), 1),
              "quantized_pass": {"ms": round(qp_ms, 5), "tier1_bytes": int(byt),
                                 "hbm_frac": round(byt / (qp_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                                "per_kernel_ms": {k[3:]: round(med[k], 5) for k in PASS_STATS}},
+                                "per_kernel_ms": {k[3:]: round(med[k], 5) for k in PASS_STATS},
+                                "per_kernel_hbm_frac": streaming_fracs(med, n_tok)},
              "ms_score_fp16": round(med["ms_score_fp16"], 5), "ms_copy": round(med["ms_copy"], 4),
              "ms_dense": round(med["ms_dense"], 5),
              "level_rates": [round(x / tot, 4) for x in lv_counts]}
