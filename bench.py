@@ -336,8 +336,8 @@ def main():
         summarize_profile(a.summarize_profile, a.cmd)
         return
     if a.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported (every box here has "
-              "one GPU, and this path does not shard across GPUs)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported (the path runs on one "
+              "GPU and does not shard across GPUs)", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
@@ -747,7 +747,7 @@ def cpu_baseline(a, ctx, qs, k1s, v1s, host0, NCPU, n_threads, n_total, np, torc
     """The oracle on the state of layers 0 .. NCPU-1 after the timed steps
     (the same fp16 inputs the GPU saw), timed on one host thread (layers
     0-3) and with one host thread per layer-step on every host thread the
-    box offers (the oracle unchanged: its C routines release the interpreter
+    process may use (the oracle unchanged: its C routines release the interpreter
     lock while they run); every sampled layer's levels, bound bits and
     outputs are compared with the GPU's."""
     import threading
