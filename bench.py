@@ -63,6 +63,7 @@ PASS_KERNELS = {
 OTHER_KERNELS = {"k_score_fp16": ("kvq_score.hip",), "k_dense_vram": ("kvq_dense.hip",),
                  "k_dense_staged": ("kvq_dense.hip",), "k_append": ("kvq_codec.hip",)}
 PASS_STATS = ("ms_score_int8", "ms_select", "ms_control", "ms_decode", "ms_combine", "ms_misc")
+WORKLOADS = ("batch2_128k", "batch4_128k", "needle_4x32k", "ladder_16seq_4k_64k")
 
 
 def log(*a):
@@ -87,6 +88,10 @@ def parse():
                    help="skip the one-layer run with every head forced to the dense fallback")
     p.add_argument("--no-workloads", action="store_true",
                    help="skip the batch-2/4, needle and adversarial-ladder workloads")
+    p.add_argument("--only-workload", choices=WORKLOADS, default=None,
+                   help="run only this workload and print its record as one JSON line "
+                        "(profiling of the batch-2/4 pass, whose decode has a launch of its own "
+                        "at batch 4)")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (counter calibration)")
     p.add_argument("--summarize-profile", nargs="+", metavar="ARG",
@@ -228,8 +233,19 @@ def summarize_profile(args, cmd):
         f_fac = cal / (sum(cf[copy]) / len(cf[copy]) * 1024)
         w_fac = cal / (sum(cw[[k for k in cw if "copyBuffer" in k[0]][0]]) /
                        len(cw[[k for k in cw if "copyBuffer" in k[0]][0]]) * 1024)
-        db = {"_calibration": {"copy_bytes": cal, "fetch_factor": round(f_fac, 4),
-                               "write_factor": round(w_fac, 4), "command": cmd}}
+        # the records of other workload shapes stay; this shape's are replaced
+        path = os.path.join(ROOT, "profiles", "counters.json")
+        try:
+            old = json.load(open(path))
+        except (OSError, ValueError):
+            old = {}
+        db = {name: {key: r for key, r in recs.items() if isinstance(r, dict) and r.get("shape") != shape}
+              for name, recs in old.items() if not name.startswith("_") and isinstance(recs, dict)}
+        db = {name: recs for name, recs in db.items() if recs}
+        cals = {k: v for k, v in old.get("_calibration", {}).items() if isinstance(v, dict)}
+        cals[shape] = {"copy_bytes": cal, "fetch_factor": round(f_fac, 4),
+                       "write_factor": round(w_fac, 4), "command": cmd}
+        db["_calibration"] = cals
         lines = head + [f"# calibration: a plain device copy of {cal} bytes reads FETCH_SIZE "
                         f"{sum(cf[copy]) / len(cf[copy]):.1f} KiB per dispatch: fetched bytes = "
                         f"FETCH_SIZE x 1024 x {f_fac:.4f}, written bytes = WRITE_SIZE x 1024 x {w_fac:.4f}",
@@ -245,12 +261,12 @@ def summarize_profile(args, cmd):
                 continue
             wk = sum(wv) / len(wv)
             fb, wb = fk * 1024 * f_fac, wk * 1024 * w_fac
-            db.setdefault(name, {})[f"{full} {g}"] = {
+            db.setdefault(name, {})[f"{full} {g} {shape}"] = {
                 "source_sha": source_sha(name), "shape": shape, "fetch_kib": round(fk, 1),
                 "write_kib": round(wk, 1), "hbm_bytes_per_launch": int(fb + wb), "launches": len(v)}
             lines.append(f"{k:40s} grid {g:>12s} FETCH {fk:11.1f} KiB WRITE {wk:10.1f} KiB -> "
                          f"read {fb / 1e6:8.2f} MB + write {wb / 1e6:7.2f} MB = {(fb + wb) / 1e6:8.2f} MB")
-        json.dump(db, open(os.path.join(ROOT, "profiles", "counters.json"), "w"), indent=1)
+        json.dump(db, open(path, "w"), indent=1)
         open(out, "w").write("\n".join(lines) + "\n")
     else:
         raise SystemExit(f"unknown profile summary kind {kind}")
@@ -300,6 +316,16 @@ def calibrate_copy(mib):
 # ---------------------------------------------------------------------------------
 # synthetic inputs on the device (the recipes of kvq_synth, drawn with torch)
 # ---------------------------------------------------------------------------------
+
+def pass_summary_of(recs, n_tok_kvh, t1b):
+    """Quantized-tier pass from per-call stats: median per kernel class and
+    the tier-1 bytes of n_tok_kvh (token, KV head) pairs."""
+    import numpy as np
+    med = {k: float(np.median([r[k] for r in recs])) for k in
+           PASS_STATS + ("ms_score_fp16", "ms_copy", "ms_dense", "ms_total")}
+    qp_ms = sum(med[k] for k in PASS_STATS)
+    return med, qp_ms, t1b * n_tok_kvh
+
 
 def gen_kv(torch, gen, dev, w, layer, T, tied=0, hostile=0.0):
     """K, V fp16 [T][Hkv][d]: N(0,1) keys with the layer's outlier channels
@@ -355,6 +381,11 @@ def main():
     n_total = a.warmup + a.steps
     max_tokens = T0 + n_total + 1
     t1b = kvq.tier1_bytes_per_token(d)
+    if a.only_workload:
+        res = other_workloads(a, kvq, S, np, torch, torch.Generator(device=dev), dev,
+                              lambda recs, n: pass_summary_of(recs, n, t1b), only=a.only_workload)
+        print(json.dumps({"workload": a.only_workload, **res[a.only_workload]}), flush=True)
+        return
     t_setup = time.time()
     ctx = kvq.Context(L, 1, Hq, Hkv, d, max_tokens, timing=True)
     log(f"context: device {ctx.device_bytes / 2**30:.2f} GiB, pinned host "
@@ -497,13 +528,7 @@ def main():
         }
 
     def pass_summary(recs, n_tok_kvh):
-        """Quantized-tier pass from per-call stats: median per kernel class and
-        the tier-1 bytes of n_tok_kvh (token, KV head) pairs."""
-        med = {k: float(np.median([r[k] for r in recs])) for k in
-               PASS_STATS + ("ms_score_fp16", "ms_copy", "ms_dense", "ms_total")}
-        qp_ms = sum(med[k] for k in PASS_STATS)
-        byt = t1b * n_tok_kvh
-        return med, qp_ms, byt
+        return pass_summary_of(recs, n_tok_kvh, t1b)
 
     wall, kv_tokens = run_steps(ctx)
     steps_main = sorted(step_ms)
@@ -839,10 +864,11 @@ def cpu_baseline(a, ctx, qs, k1s, v1s, host0, NCPU, n_threads, n_total, np, torc
     return cpu, parity
 
 
-def other_workloads(a, kvq, S, np, torch, gen, dev, pass_summary):
+def other_workloads(a, kvq, S, np, torch, gen, dev, pass_summary, only=None):
     """The quantized-tier pass at batch 2 and 4 (128K each, two layers taken in
     turn so tier 1 does not stay in the 256 MB last-level cache), the 4 x 32K
-    needle workload and the 16-sequence adversarial ladder workload."""
+    needle workload and the 16-sequence adversarial ladder workload (only the
+    one named `only`, when given)."""
     res = {}
     w4 = S.workload(4)
     Hq, Hkv, d = w4.Hq, w4.Hkv, w4.d
@@ -857,6 +883,16 @@ def other_workloads(a, kvq, S, np, torch, gen, dev, pass_summary):
         by = {"k_score_int8": (med["ms_score_int8"], n_tok * Hkv * (d + 4 * d / 64)),
               dec: (med["ms_decode"], n_tok * Hkv * (d / 2 + 4 * d / 32 + 4 / 64))}
         return {k: round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4) for k, (ms, b) in by.items() if ms > 0}
+
+    def pass_traffic(med, lens):
+        # HBM bytes of one pass from the committed counters of this shape (a
+        # batch of equal 128K contexts), or None where none were taken
+        if len(set(lens)) != 1 or lens[0] != 131072:
+            return None
+        names = ["k_score_int8", "k_select", "k_combine"] + (
+            ["k_eval_decode"] if med["ms_control"] == 0.0 else ["k_eval", "k_decode_mixed"])
+        return counter_traffic(names, f"B{len(lens)}-Hq{Hq}-Hkv{Hkv}-d{d}-T131072",
+                               optional=("k_rescore_int8",))
 
     def run(name, cx, lens, qfn, steps, layers, extra=None):
         recs = []
@@ -877,7 +913,8 @@ def other_workloads(a, kvq, S, np, torch, gen, dev, pass_summary):
              "quantized_pass": {"ms": round(qp_ms, 5), "tier1_bytes": int(byt),
                                 "hbm_frac": round(byt / (qp_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                                 "per_kernel_ms": {k[3:]: round(med[k], 5) for k in PASS_STATS},
-                                "per_kernel_hbm_frac": streaming_fracs(med, n_tok)},
+                                "per_kernel_hbm_frac": streaming_fracs(med, n_tok),
+                                "traffic": pass_traffic(med, lens)},
              "ms_score_fp16": round(med["ms_score_fp16"], 5), "ms_copy": round(med["ms_copy"], 4),
              "ms_dense": round(med["ms_dense"], 5),
              "level_rates": [round(x / tot, 4) for x in lv_counts]}
@@ -889,6 +926,8 @@ def other_workloads(a, kvq, S, np, torch, gen, dev, pass_summary):
 
     # batch 2 and 4 at 128K
     for B in (2, 4):
+        if only not in (None, f"batch{B}_128k"):
+            continue
         T = 131072
         cx = kvq.Context(2, B, Hq, Hkv, d, T + 64, timing=True)
         for layer in range(2):
@@ -902,54 +941,56 @@ def other_workloads(a, kvq, S, np, torch, gen, dev, pass_summary):
         run(f"batch{B}_128k", cx, [T] * B, lambda s, l: qb[s], 8, 2)
         cx.close()
 
-    # 4 x 32K with a planted needle per query head: that head's query
-    # direction scaled to 0.8 sqrt(d), plus 0.1 N(0,1), in one block of its KV
-    # head (distinct blocks within a KV head)
-    w3 = S.workload(3)
-    T, B, G = 32768, 4, Hq // Hkv
-    cx = kvq.Context(1, B, Hq, Hkv, d, T + 64, timing=True)
-    gen.manual_seed(6_700_000)
-    q3 = torch.randn((B, Hq, d), generator=gen, device=dev).half()
-    needles = {}
-    for i in range(B):
-        gen.manual_seed(6_710_000 + i)
-        K, V = gen_kv(torch, gen, dev, w3, 0, T)
-        K = K.float()
-        for g in range(Hkv):
-            blocks = torch.randperm(T // 64, generator=gen, device=dev)[:G].tolist()
-            for hh in range(G):
-                qh = q3[i, g * G + hh].float()
-                b = blocks[hh]
-                K[b * 64:(b + 1) * 64, g, :] = (0.8 * (d ** 0.5) * qh / qh.norm() +
-                                                0.1 * torch.randn((64, d), generator=gen, device=dev))
-                needles[(i, g * G + hh)] = b
-        cx.append(0, [i], [T], K.half(), V)
-        del K, V
-
-    def needle_check(cx):
-        first = 0
+    if only in (None, "needle_4x32k"):
+        # 4 x 32K with a planted needle per query head: that head's query
+        # direction scaled to 0.8 sqrt(d), plus 0.1 N(0,1), in one block of its KV
+        # head (distinct blocks within a KV head)
+        w3 = S.workload(3)
+        T, B, G = 32768, 4, Hq // Hkv
+        cx = kvq.Context(1, B, Hq, Hkv, d, T + 64, timing=True)
+        gen.manual_seed(6_700_000)
+        q3 = torch.randn((B, Hq, d), generator=gen, device=dev).half()
+        needles = {}
         for i in range(B):
-            pi = cx.export_trace("pi", i).reshape(Hq, -1)
-            first += sum(int(pi[h][0]) == needles[(i, h)] for h in range(Hq))
-        return {"needle_ranked_first_frac": round(first / (B * Hq), 4)}
-    run("needle_4x32k", cx, [T] * B, lambda s, l: q3, 6, 1, needle_check)
-    cx.close()
+            gen.manual_seed(6_710_000 + i)
+            K, V = gen_kv(torch, gen, dev, w3, 0, T)
+            K = K.float()
+            for g in range(Hkv):
+                blocks = torch.randperm(T // 64, generator=gen, device=dev)[:G].tolist()
+                for hh in range(G):
+                    qh = q3[i, g * G + hh].float()
+                    b = blocks[hh]
+                    K[b * 64:(b + 1) * 64, g, :] = (0.8 * (d ** 0.5) * qh / qh.norm() +
+                                                    0.1 * torch.randn((64, d), generator=gen, device=dev))
+                    needles[(i, g * G + hh)] = b
+            cx.append(0, [i], [T], K.half(), V)
+            del K, V
 
-    # adversarial ladder stress: 16 sequences, contexts 4K-64K, near-tied key
-    # blocks in (0, 2, 4, 8)[i mod 4] KV heads of sequence i, 5 % hostile
-    # value cells
-    w5 = S.workload(5)
-    lens = list(w5.ctx)
-    cx = kvq.Context(1, len(lens), Hq, Hkv, d, max(lens) + 64, timing=True)
-    for i, T in enumerate(lens):
-        gen.manual_seed(6_900_000 + i)
-        K, V = gen_kv(torch, gen, dev, w5, 0, T, tied=w5.tied_heads[i], hostile=w5.hostile_frac)
-        cx.append(0, [i], [T], K, V)
-        del K, V
-    gen.manual_seed(6_950_000)
-    q5 = torch.randn((len(lens), Hq, d), generator=gen, device=dev).half()
-    run("ladder_16seq_4k_64k", cx, lens, lambda s, l: q5, 4, 1)
-    cx.close()
+        def needle_check(cx):
+            first = 0
+            for i in range(B):
+                pi = cx.export_trace("pi", i).reshape(Hq, -1)
+                first += sum(int(pi[h][0]) == needles[(i, h)] for h in range(Hq))
+            return {"needle_ranked_first_frac": round(first / (B * Hq), 4)}
+        run("needle_4x32k", cx, [T] * B, lambda s, l: q3, 6, 1, needle_check)
+        cx.close()
+
+    if only in (None, "ladder_16seq_4k_64k"):
+        # adversarial ladder stress: 16 sequences, contexts 4K-64K, near-tied key
+        # blocks in (0, 2, 4, 8)[i mod 4] KV heads of sequence i, 5 % hostile
+        # value cells
+        w5 = S.workload(5)
+        lens = list(w5.ctx)
+        cx = kvq.Context(1, len(lens), Hq, Hkv, d, max(lens) + 64, timing=True)
+        for i, T in enumerate(lens):
+            gen.manual_seed(6_900_000 + i)
+            K, V = gen_kv(torch, gen, dev, w5, 0, T, tied=w5.tied_heads[i], hostile=w5.hostile_frac)
+            cx.append(0, [i], [T], K, V)
+            del K, V
+        gen.manual_seed(6_950_000)
+        q5 = torch.randn((len(lens), Hq, d), generator=gen, device=dev).half()
+        run("ladder_16seq_4k_64k", cx, lens, lambda s, l: q5, 4, 1)
+        cx.close()
     return res
 
 
