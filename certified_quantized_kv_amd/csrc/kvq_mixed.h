@@ -30,7 +30,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // and the four waves' sums share that reference (they add without rescaling).
 // Scores, value metadata and codes of a wave's next block load while the
 // current one is accumulated; the value tiles are read once per step, through
-// non-temporal loads.
+// non-temporal loads (the metadata rows, shared by the two channel halves,
+// through ordinary ones).
 // FV: blocks with FP16 values may occur (a step whose controller promoted
 // values); without it the kernel has no FP16-value path and none of its LDS.
 template <int D, int CB, int NP, bool FV>
@@ -123,12 +124,15 @@ __device__ inline void decode_chunk(const Shape &s, const Tier1 &t, const Step &
   auto fetch_vm = [&](Stage &st, int bb) {
     // the lane's token, clamped (bb is a block of the sequence: in [0, 64))
     const uint32_t tl = (uint32_t)min(lane, T - 1 - bb * BLOCK) & (BLOCK - 1);
+    // the two channel halves' waves read the two halves of each token's
+    // metadata row: ordinary loads, so that the second reader finds the
+    // lines in L2 (non-temporal loads fetched them from HBM twice)
     const uint32_t *mp = t.vmeta + (u * s.Tmax + (size_t)bb * BLOCK) * NG + half * NGW;
     if constexpr (NGW == 2) {
-      const u32x2 m = __builtin_nontemporal_load((const u32x2 *)(mp + tl * (uint32_t)NG));
+      const u32x2 m = *(const u32x2 *)(mp + tl * (uint32_t)NG);
       st.meta[0] = m.x, st.meta[1] = m.y;
     } else {
-      st.meta[0] = __builtin_nontemporal_load(mp + tl * (uint32_t)NG);
+      st.meta[0] = mp[tl * (uint32_t)NG];
     }
     const u32x2 *vc = (const u32x2 *)(t.vcodes + (u * s.NBmax + bb) * (size_t)(32 * D)) + half * NTW * 64;
 #pragma unroll
